@@ -1,0 +1,348 @@
+/*
+ * kivi_oracle.c -- plain, slow, single-threaded CPU oracle for the KIVI
+ * quantized KV cache hot path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * loads this file.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark use it.  It shares no code, header, table or helper
+ * with the HIP library: it re-derives everything from the method's
+ * description.
+ *
+ * Sources (web pages about the method):
+ *   [KIVI-abs]  "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV
+ *               Cache", mlsanity paper page, section "Abstract (arXiv)".
+ *   [KIVI-sum]  study.space summary page of the same paper (one summary
+ *               paragraph, no headings).
+ *   [KIVI-quo]  scholarfeed.org "KIVI" quote page (one-line quotes from other
+ *               papers about the method).
+ *
+ * What the pages fix, restated:
+ *   - keys are quantized per channel: one group is one channel over a run
+ *     of consecutive tokens; values are quantized per token: one group is a
+ *     run of consecutive channels of one token [KIVI-abs]; the key groups
+ *     span tokens, so tokens are grouped before keys are quantized [KIVI-sum];
+ *   - the quantizer is asymmetric, low-bit (2-bit; 4-bit and 1-bit are also
+ *     named) and tuning-free, i.e. uses no calibration [KIVI-abs title,
+ *     KIVI-quo];
+ *   - the cache is split into a quantized "grouped" part and a
+ *     full-precision "residual" part of recent tokens; new tokens are
+ *     appended along the token axis [KIVI-sum, KIVI-quo];
+ *   - decode attention computes scores on the grouped part and combines the
+ *     residual part with it [KIVI-sum].
+ *
+ * Readings where the pages are silent (the pages print no formula):
+ *   - quantizer: z = min of the group, s = (max - min) / (2^b - 1),
+ *     code = round-half-even((x - z) / s) clamped to [0, 2^b - 1];
+ *     dequantized value = code * s + z.  Every codec step is one IEEE
+ *     binary32 operation rounded to nearest-even, in the order written in
+ *     quantize_group() below; divisions are true divisions.
+ *   - a group whose max equals its min stores s = 0, z = that value and
+ *     all-zero codes, so it dequantizes exactly;
+ *   - attention: softmax(scale * q . k_t) over every cached token, no mask,
+ *     in binary64 on the dequantized keys and values; a GQA query head hq
+ *     reads KV head hq / r.
+ *
+ * Packed layout (the library's documented storage contract, re-implemented
+ * here independently from its description):
+ *   E = 32 / bits codes per 32-bit word, little-endian bit order.
+ *   K codes : [B][H][cap][D/E] words; channel d of token t sits in word d/E
+ *             at bit offset bits*(d%E).
+ *   V codes : [B][H][cap/64][D][64/E] words; token t, channel d sits in
+ *             tile t/64, word (t%64)/E of channel d, bit offset
+ *             bits*((t%64)%E).
+ *   K scale/zero : [B][H][cap/G][D] binary32.
+ *   V scale/zero : [B][H][cap][D/G] binary32.
+ *   residual K/V : [B][H][R][D] binary16.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -shared -fPIC (x86-64 SSE
+ * arithmetic, no excess precision).
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#define KIVIO_OK 0
+#define KIVIO_EINVAL 1
+#define KIVIO_ESHAPE 2
+#define KIVIO_ECAPACITY 3
+
+/* ---- binary16 -> binary32, exact (every half is a float) ---------------- */
+float kivio_half_to_float(uint16_t h) {
+  uint32_t sign = (uint32_t)(h >> 15) << 31;
+  uint32_t exp = (h >> 10) & 0x1fu;
+  uint32_t man = h & 0x3ffu;
+  uint32_t bits;
+  if (exp == 0) {
+    if (man == 0) {
+      bits = sign;
+    } else {
+      /* subnormal half: man * 2^-24, renormalise */
+      int e = -1;
+      do {
+        man <<= 1;
+        e++;
+      } while ((man & 0x400u) == 0);
+      man &= 0x3ffu;
+      bits = sign | ((uint32_t)(127 - 15 - e) << 23) | (man << 13);
+    }
+  } else if (exp == 31) {
+    bits = sign | 0x7f800000u | (man << 13);
+  } else {
+    bits = sign | ((exp - 15 + 127) << 23) | (man << 13);
+  }
+  float f;
+  memcpy(&f, &bits, sizeof f);
+  return f;
+}
+
+static int words_per_row(int D, int bits) { return D * bits / 32; }
+
+/* Quantize one group of n binary32 values (already widened from binary16).
+ * Writes n codes and the group's scale and zero.  The order of operations is
+ * the reading stated in the file header. */
+static void quantize_group(const float* xs, int n, int bits, uint8_t* codes,
+                           float* scale_out, float* zero_out) {
+  float mn = xs[0], mx = xs[0];
+  for (int i = 1; i < n; i++) {
+    if (xs[i] < mn) mn = xs[i];
+    if (xs[i] > mx) mx = xs[i];
+  }
+  const float qmax = (float)((1 << bits) - 1);
+  if (mx == mn) { /* constant group: exact */
+    *scale_out = 0.0f;
+    *zero_out = mn;
+    for (int i = 0; i < n; i++) codes[i] = 0;
+    return;
+  }
+  float range = mx - mn;      /* one binary32 rounding */
+  float s = range / qmax;     /* one binary32 rounding */
+  float z = mn;
+  for (int i = 0; i < n; i++) {
+    float u = xs[i] - z;      /* one rounding, u >= 0 */
+    float v = u / s;          /* one rounding */
+    float c = rintf(v);       /* round half to even (default mode) */
+    if (c > qmax) c = qmax;
+    codes[i] = (uint8_t)c;
+  }
+  *scale_out = s;
+  *zero_out = z;
+}
+
+static int check_common(int B, int H, int D, int bits, int G, int cap) {
+  if (B < 1 || H < 1 || D < 1 || G < 1 || cap < 0) return KIVIO_EINVAL;
+  if (bits != 2 && bits != 4) return KIVIO_EINVAL;
+  if (D % G != 0) return KIVIO_ESHAPE;
+  if ((D * bits) % 32 != 0) return KIVIO_ESHAPE;
+  if (cap % 64 != 0 || cap % G != 0) return KIVIO_ESHAPE;
+  return KIVIO_OK;
+}
+
+/* Key quantization, per channel over groups of G consecutive tokens
+ * [KIVI-abs, KIVI-sum].  Source tokens [0, ntok) of k ([B][H][in_stride][D]
+ * binary16) go to cache tokens [dst_off, dst_off + ntok). */
+int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap,
+                     const uint16_t* k, int in_stride, int ntok, int dst_off,
+                     uint32_t* codes, float* scale, float* zero) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
+    return KIVIO_ESHAPE;
+  if (dst_off + ntok > cap) return KIVIO_ECAPACITY;
+  const int E = 32 / bits, W = words_per_row(D, bits);
+  float xs[1024];
+  uint8_t cs[1024];
+  if (G > 1024) return KIVIO_ESHAPE;
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < H; h++) {
+      const uint16_t* src = k + ((size_t)b * H + h) * (size_t)in_stride * D;
+      uint32_t* cw = codes + ((size_t)b * H + h) * (size_t)cap * W;
+      float* sc = scale + ((size_t)b * H + h) * (size_t)(cap / G) * D;
+      float* zr = zero + ((size_t)b * H + h) * (size_t)(cap / G) * D;
+      /* clear the destination rows, then OR codes in */
+      for (int t = 0; t < ntok; t++)
+        for (int w = 0; w < W; w++) cw[(size_t)(dst_off + t) * W + w] = 0;
+      for (int g = 0; g < ntok / G; g++)
+        for (int d = 0; d < D; d++) {
+          for (int i = 0; i < G; i++)
+            xs[i] = kivio_half_to_float(src[(size_t)(g * G + i) * D + d]);
+          float s, z;
+          quantize_group(xs, G, bits, cs, &s, &z);
+          int gg = (dst_off / G) + g;
+          sc[(size_t)gg * D + d] = s;
+          zr[(size_t)gg * D + d] = z;
+          for (int i = 0; i < G; i++) {
+            int t = dst_off + g * G + i;
+            cw[(size_t)t * W + d / E] |= (uint32_t)cs[i] << (bits * (d % E));
+          }
+        }
+    }
+  return KIVIO_OK;
+}
+
+/* word index (within one (b, h) plane) of value-cache token t, channel d */
+static size_t v_word_index(int D, int bits, int t, int d) {
+  const int E = 32 / bits, WPC = 64 / E; /* words per channel per tile */
+  return ((size_t)(t / 64) * D + d) * WPC + (t % 64) / E;
+}
+
+/* Value quantization, per token over groups of G consecutive channels
+ * [KIVI-abs]; quantized tokens are appended along the token axis
+ * [KIVI-sum]. */
+int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap,
+                     const uint16_t* v, int in_stride, int ntok, int dst_off,
+                     uint32_t* codes, float* scale, float* zero) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
+    return KIVIO_ESHAPE;
+  if (dst_off + ntok > cap) return KIVIO_ECAPACITY;
+  const int E = 32 / bits, NG = D / G;
+  const size_t plane_words = (size_t)cap * D / E;
+  float xs[1024];
+  uint8_t cs[1024];
+  if (G > 1024) return KIVIO_ESHAPE;
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < H; h++) {
+      const uint16_t* src = v + ((size_t)b * H + h) * (size_t)in_stride * D;
+      uint32_t* cw = codes + ((size_t)b * H + h) * plane_words;
+      float* sc = scale + ((size_t)b * H + h) * (size_t)cap * NG;
+      float* zr = zero + ((size_t)b * H + h) * (size_t)cap * NG;
+      for (int t = 0; t < ntok; t++)
+        for (int d = 0; d < D; d++) cw[v_word_index(D, bits, dst_off + t, d)] = 0;
+      for (int t = 0; t < ntok; t++)
+        for (int j = 0; j < NG; j++) {
+          for (int i = 0; i < G; i++)
+            xs[i] = kivio_half_to_float(src[(size_t)t * D + j * G + i]);
+          float s, z;
+          quantize_group(xs, G, bits, cs, &s, &z);
+          int tt = dst_off + t;
+          sc[(size_t)tt * NG + j] = s;
+          zr[(size_t)tt * NG + j] = z;
+          for (int i = 0; i < G; i++) {
+            int d = j * G + i;
+            cw[v_word_index(D, bits, tt, d)] |= (uint32_t)cs[i]
+                                                << (bits * ((tt % 64) % E));
+          }
+        }
+    }
+  return KIVIO_OK;
+}
+
+/* Streaming append of one decode token per (b, h) [KIVI-sum: the residual
+ * part is kept in full precision and new tokens are appended; KIVI-quo: a
+ * fixed-length residual of recent tokens].  Reading: when a token arrives
+ * and the residual already holds R tokens, all R are quantized into the
+ * grouped part first (keys and values alike), then the new token is stored
+ * in the residual.  *tq, *tr are updated only on success. */
+int kivio_append(int B, int H, int D, int bits, int G, int R, int cap,
+                 uint32_t* k_codes, float* ks, float* kz, uint32_t* v_codes,
+                 float* vs, float* vz, uint16_t* k_res, uint16_t* v_res,
+                 const uint16_t* k_new, const uint16_t* v_new, int* tq,
+                 int* tr) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (R < G || R % G) return KIVIO_ESHAPE;
+  int q = *tq, r = *tr;
+  if (q < 0 || q % G || r < 0 || r > R) return KIVIO_ESHAPE;
+  if (r == R) {
+    if (q + R > cap) return KIVIO_ECAPACITY;
+    rc = kivio_quantize_k(B, H, D, bits, G, cap, k_res, R, R, q, k_codes, ks, kz);
+    if (rc) return rc;
+    rc = kivio_quantize_v(B, H, D, bits, G, cap, v_res, R, R, q, v_codes, vs, vz);
+    if (rc) return rc;
+    q += R;
+    r = 0;
+  }
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < H; h++)
+      for (int d = 0; d < D; d++) {
+        size_t src = ((size_t)b * H + h) * D + d;
+        size_t dst = (((size_t)b * H + h) * R + r) * D + d;
+        k_res[dst] = k_new[src];
+        v_res[dst] = v_new[src];
+      }
+  *tq = q;
+  *tr = r + 1;
+  return KIVIO_OK;
+}
+
+/* dequantized key / value of cache token t (< tq), channel d, in binary64 */
+static double dequant_k(const uint32_t* cw, const float* sc, const float* zr,
+                        int D, int bits, int G, int t, int d) {
+  const int E = 32 / bits, W = words_per_row(D, bits);
+  uint32_t c = (cw[(size_t)t * W + d / E] >> (bits * (d % E))) & ((1u << bits) - 1);
+  size_t m = (size_t)(t / G) * D + d;
+  return (double)c * (double)sc[m] + (double)zr[m];
+}
+
+static double dequant_v(const uint32_t* cw, const float* sc, const float* zr,
+                        int D, int bits, int G, int t, int d) {
+  const int E = 32 / bits;
+  uint32_t c = (cw[v_word_index(D, bits, t, d)] >> (bits * ((t % 64) % E))) &
+               ((1u << bits) - 1);
+  size_t m = (size_t)t * (D / G) + d / G;
+  return (double)c * (double)sc[m] + (double)zr[m];
+}
+
+/* Decode attention over the mixed cache [KIVI-sum: scores on the grouped
+ * part, then the residual part is combined with it], binary64 throughout.
+ * q, out: [B][H*r][D].  Work space: 2*(tq+tr) doubles in `scratch`. */
+int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
+                      int cap, const uint32_t* k_codes, const float* ks,
+                      const float* kz, const uint32_t* v_codes,
+                      const float* vs, const float* vz, const uint16_t* k_res,
+                      const uint16_t* v_res, int tq, int tr, const uint16_t* q,
+                      float softmax_scale, double* out, double* scratch) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (r < 1) return KIVIO_EINVAL;
+  if (tq < 0 || tq % G || tq > cap || tr < 0 || tr > R || tq + tr < 1)
+    return KIVIO_ESHAPE;
+  const int Hq = H * r, W = words_per_row(D, bits), E = 32 / bits;
+  const int L = tq + tr;
+  double* logit = scratch;
+  double* p = scratch + L;
+  for (int b = 0; b < B; b++)
+    for (int hq = 0; hq < Hq; hq++) {
+      const int h = hq / r;
+      const size_t bh = (size_t)b * H + h;
+      const uint32_t* kc = k_codes + bh * (size_t)cap * W;
+      const float* ksp = ks + bh * (size_t)(cap / G) * D;
+      const float* kzp = kz + bh * (size_t)(cap / G) * D;
+      const uint32_t* vc = v_codes + bh * (size_t)cap * D / E;
+      const float* vsp = vs + bh * (size_t)cap * (D / G);
+      const float* vzp = vz + bh * (size_t)cap * (D / G);
+      const uint16_t* kr = k_res + bh * (size_t)R * D;
+      const uint16_t* vr = v_res + bh * (size_t)R * D;
+      const uint16_t* qv = q + ((size_t)b * Hq + hq) * D;
+      for (int t = 0; t < L; t++) {
+        double dot = 0.0;
+        for (int d = 0; d < D; d++) {
+          double kv = (t < tq) ? dequant_k(kc, ksp, kzp, D, bits, G, t, d)
+                               : (double)kivio_half_to_float(kr[(size_t)(t - tq) * D + d]);
+          dot += (double)kivio_half_to_float(qv[d]) * kv;
+        }
+        logit[t] = (double)softmax_scale * dot;
+      }
+      double m = logit[0];
+      for (int t = 1; t < L; t++)
+        if (logit[t] > m) m = logit[t];
+      double l = 0.0;
+      for (int t = 0; t < L; t++) {
+        p[t] = exp(logit[t] - m);
+        l += p[t];
+      }
+      double* o = out + ((size_t)b * Hq + hq) * D;
+      for (int d = 0; d < D; d++) {
+        double acc = 0.0;
+        for (int t = 0; t < L; t++) {
+          double vv = (t < tq) ? dequant_v(vc, vsp, vzp, D, bits, G, t, d)
+                               : (double)kivio_half_to_float(vr[(size_t)(t - tq) * D + d]);
+          acc += p[t] * vv;
+        }
+        o[d] = acc / l;
+      }
+    }
+  return KIVIO_OK;
+}

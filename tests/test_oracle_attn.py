@@ -1,0 +1,148 @@
+"""Pins of the oracle's decode attention.
+
+Pages: study.space summary of "KIVI: A Tuning-Free Asymmetric 2bit
+Quantization for KV Cache" -- scores are computed on the quantized grouped
+part and the full-precision residual part is combined with it.  Reading:
+softmax(scale * q.k) over all cached tokens, no mask, binary64, GQA query
+head h reads KV head h // r.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import synth
+from tests.helpers import attention_f64, dequant_k, dequant_v
+
+
+def _cache(B, H, r, D, bits, G, R, cap, k, v, tq):
+    c = oracle.OracleCache(B, H, r, D, bits, G, R, cap)
+    c.prefill(k, v, tq)
+    return c
+
+
+@pytest.mark.parametrize("r", [1, 4])
+@pytest.mark.parametrize("L", [1, 17, 128])
+def test_all_residual_equals_sdpa(oracle_lib, r, L):
+    """With every token in the residual the method is plain softmax
+    attention on the binary16 keys/values: compare with torch's
+    scaled_dot_product_attention in float64 on the CPU."""
+    B, H, D, R = 2, 2, 64, 128
+    k = synth.random_fp16(1, (B, H, L, D))
+    v = synth.random_fp16(2, (B, H, L, D))
+    q = synth.random_fp16(3, (B, H * r, D))
+    scale = float(np.float32(0.125))
+    c = _cache(B, H, r, D, 2, 32, R, 128, k, v, tq=0)
+    got = c.decode(q, scale)
+    qt = torch.from_numpy(q.astype(np.float64))[:, :, None, :]
+    kt = torch.from_numpy(k.astype(np.float64)).repeat_interleave(r, dim=1)
+    vt = torch.from_numpy(v.astype(np.float64)).repeat_interleave(r, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[:, :, 0]
+    np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("r", [1, 2, 4])
+@pytest.mark.parametrize("tq,tr", [(64, 0), (32, 1), (64, 31), (0, 5), (96, 32)])
+def test_tiny_brute_force(oracle_lib, bits, r, tq, tr):
+    """Independent NumPy binary64 attention on explicitly dequantized arrays
+    (dequantized by the test's own unpacker)."""
+    B, H, D, G, R = 2, 2, 32, 32, 32
+    L = tq + tr
+    k = synth.random_fp16(10 + bits, (B, H, L, D), scale=2.0)
+    k[..., 3] *= np.float16(10)
+    v = synth.random_fp16(20 + bits, (B, H, L, D))
+    q = synth.random_fp16(30 + r, (B, H * r, D))
+    c = _cache(B, H, r, D, bits, G, R, 128, k, v, tq)
+    got = c.decode(q, 0.2)
+    kh = np.concatenate([dequant_k(c.k_codes, c.ks, c.kz, bits, G, tq, D),
+                         k[:, :, tq:].astype(np.float64)], axis=2)
+    vh = np.concatenate([dequant_v(c.v_codes, c.vs, c.vz, bits, G, tq, D),
+                         v[:, :, tq:].astype(np.float64)], axis=2)
+    ref = attention_f64(q, kh, vh, np.float32(0.2))
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_zero_query_is_mean(oracle_lib):
+    """q = 0 gives uniform weights: the output is the mean dequantized value."""
+    B, H, D, G, R, tq, tr = 1, 2, 64, 32, 32, 128, 7
+    k = synth.random_fp16(5, (B, H, tq + tr, D))
+    v = synth.random_fp16(6, (B, H, tq + tr, D))
+    c = _cache(B, H, 1, D, 2, G, R, 256, k, v, tq)
+    got = c.decode(np.zeros((B, H, D), np.float16), 0.1)
+    vh = np.concatenate([dequant_v(c.v_codes, c.vs, c.vz, 2, G, tq, D),
+                         v[:, :, tq:].astype(np.float64)], axis=2)
+    np.testing.assert_allclose(got, vh.mean(axis=2), rtol=1e-12, atol=1e-14)
+
+
+def test_gqa_equals_repeated_mha(oracle_lib):
+    """A GQA cache with r query heads per KV head gives the same output as an
+    MHA cache whose KV heads are the GQA heads repeated r times."""
+    B, H, r, D, G, R, tq, tr = 2, 2, 4, 64, 32, 64, 192, 40
+    k = synth.random_fp16(7, (B, H, tq + tr, D))
+    v = synth.random_fp16(8, (B, H, tq + tr, D))
+    q = synth.random_fp16(9, (B, H * r, D))
+    g = _cache(B, H, r, D, 2, G, R, 256, k, v, tq).decode(q, 0.125)
+    m = _cache(B, H * r, 1, D, 2, G, R, 256, np.repeat(k, r, axis=1), np.repeat(v, r, axis=1),
+               tq).decode(q, 0.125)
+    assert np.array_equal(g, m)
+
+
+def test_group_permutation_invariance(oracle_lib):
+    """Permuting whole key groups (G tokens, with their values) permutes the
+    softmax terms only: the output is unchanged up to summation order."""
+    B, H, D, G, R, tq, tr = 1, 2, 64, 32, 32, 256, 9
+    k = synth.random_fp16(11, (B, H, tq + tr, D))
+    v = synth.random_fp16(12, (B, H, tq + tr, D))
+    q = synth.random_fp16(13, (B, H, D))
+    perm = np.random.default_rng(0).permutation(tq // G)
+    idx = np.concatenate([np.arange(p * G, (p + 1) * G) for p in perm] + [np.arange(tq, tq + tr)])
+    a = _cache(B, H, 1, D, 2, G, R, 256, k, v, tq).decode(q, 0.1)
+    b = _cache(B, H, 1, D, 2, G, R, 256, k[:, :, idx], v[:, :, idx], tq).decode(q, 0.1)
+    np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-15)
+
+
+def test_value_scaling_exact(oracle_lib):
+    """V -> 2V doubles every code-scale, zero and residual value exactly, so
+    the binary64 output doubles exactly."""
+    B, H, D, G, R, tq, tr = 1, 2, 64, 32, 32, 128, 12
+    k = synth.random_fp16(14, (B, H, tq + tr, D))
+    v = synth.random_fp16(15, (B, H, tq + tr, D))
+    q = synth.random_fp16(16, (B, H, D))
+    a = _cache(B, H, 1, D, 4, G, R, 128, k, v, tq).decode(q, 0.1)
+    b = _cache(B, H, 1, D, 4, G, R, 128, k, (v.astype(np.float32) * 2).astype(np.float16),
+               tq).decode(q, 0.1)
+    assert np.array_equal(b, 2 * a)
+
+
+def test_dominant_token(oracle_lib):
+    """One token whose key is aligned with a large query takes all the
+    weight: the output is that token's dequantized value."""
+    B, H, D, G, R, tq, tr = 1, 1, 64, 32, 32, 128, 4
+    k = synth.random_fp16(17, (B, H, tq + tr, D), scale=0.01)
+    v = synth.random_fp16(18, (B, H, tq + tr, D))
+    q = np.zeros((B, H, D), np.float16)
+    q[..., 0] = 100
+    k[:, :, 70, 0] = 60   # quantized token 70 dominates: logits differ by ~6000
+    c = _cache(B, H, 1, D, 2, G, R, 128, k, v, tq)
+    got = c.decode(q, 1.0)
+    vh = dequant_v(c.v_codes, c.vs, c.vz, 2, G, tq, D)
+    np.testing.assert_allclose(got[0, 0], vh[0, 0, 70], rtol=0, atol=1e-12)
+
+
+def test_workload_shapes_small(oracle_lib):
+    """The single-head 512-token workload (all tokens quantized) runs and
+    matches the brute force on the test-side dequantization."""
+    w = synth.WORKLOADS["single_head_512"]
+    k, v = synth.kv(w)
+    q = synth.query(w)
+    c = _cache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual,
+               w.capacity(), k, v, w.tq)
+    got = c.decode(q, w.softmax_scale)
+    kh = dequant_k(c.k_codes, c.ks, c.kz, w.bits, w.group, w.tq, w.head_dim)
+    vh = dequant_v(c.v_codes, c.vs, c.vz, w.bits, w.group, w.tq, w.head_dim)
+    ref = attention_f64(q, kh, vh, w.softmax_scale)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+    # and the quantized attention stays close to full-precision attention
+    full = attention_f64(q, k, v, w.softmax_scale)
+    assert np.abs(got - full).max() < 0.5
