@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized-KV decode hot path on one MI355X.
+
+A step is one decode step of one attention layer of the Llama-2-7B-shaped
+workload (batch 8, 32 heads, head_dim 128, 2-bit codes, G = 32, R = 128,
+context 4096 at the start of the timed region): append the new token's K/V
+(quantizing the full residual into the grouped part when it is full), then
+decode attention for every query head.  Steps rotate over `--layers`
+independent layer caches (8 by default, 1.2 GB in total) so that no step finds
+its cache resident in the 256 MB Infinity Cache left by the previous step;
+each layer starts with a full residual, so with 1024 steps every layer flushes
+once per 128 appends, the method's own rate.
+
+Prints one JSON line: whole-step algorithmic HBM GB/s (value), query-heads/s,
+the roofline of the dominant kernel (decode attention, timed with HIP events
+on the launch stream) and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
+
+
+def decode_bytes(B, H, r, D, bits, G, tq, tr):
+    """Algorithmic bytes of one decode call: packed K/V codes, fp32 scale and
+    zero of both, fp16 residual K/V, fp16 q and out."""
+    per = (2 * tq * D * bits // 8 + (tq // G) * D * 8 + tq * (D // G) * 8 + 4 * tr * D
+           + 4 * r * D)
+    return B * H * per
+
+
+def append_bytes(B, H, D, bits, G, R, flush):
+    """Algorithmic bytes of one append: read the new K/V token, write it to
+    the residual; a flush reads R residual tokens of K and V and writes their
+    codes, scales and zeros."""
+    b = B * H * D * 2 * 2 * 2
+    if flush:
+        b += B * H * (2 * R * D * 2 + 2 * R * D * bits // 8 + (R // G) * D * 8 + R * (D // G) * 8)
+    return b
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from committed rocprofv3 PMC summaries,
+    only if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
+    """The C oracle (single thread) on a bounded sample of the same workload:
+    whole decode steps (append with its flush, then attention for all 256
+    query heads) repeated until about `min_seconds` of CPU work."""
+    import numpy as np
+
+    import oracle
+    from kv_cache_bit_kivi_amd import synth
+
+    k, v = synth.kv(w)
+    cap = w.capacity(64)
+    oc = oracle.OracleCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
+                            w.residual, cap)
+    oc.prefill(k, v, w.tq)
+    del k, v
+    nbytes, steps, t_total = 0, 0, 0.0
+    while t_total < min_seconds and steps < 64:
+        kn, vn = synth.new_token(w, steps + 1)
+        q = synth.query(w, steps + 1)
+        flush = oc.tr == w.residual
+        t0 = time.perf_counter()
+        oc.append(kn, vn)
+        oc.decode(q, w.softmax_scale)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        nbytes += append_bytes(w.batch, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
+                               flush)
+        nbytes += decode_bytes(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
+                               oc.tr)
+        steps += 1
+        if t_total > max_seconds:
+            break
+    return {
+        "value": round(nbytes / t_total / 1e9, 4),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{steps} whole decode steps of the same workload (one layer: append incl. "
+                  f"flush, then attention for all {w.batch * w.q_heads} query heads), "
+                  f"{t_total:.1f} s single-threaded",
+        "seconds_per_step": round(t_total / steps, 4),
+        "query_heads_per_s": round(steps * w.batch * w.q_heads / t_total, 2),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="llama2_7b_b8_ctx4096")
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard across GPUs by (batch, KV head) with no exchange, but this "
+              "build measures one GPU only).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from kv_cache_bit_kivi_amd import synth
+    from kv_cache_bit_kivi_amd._lib import lib
+    from kv_cache_bit_kivi_amd.cache import KiviCache
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    lib()  # fails loudly if the HIP library is missing
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
+                              w.residual)
+    NL = args.layers
+    total_steps = args.warmup + args.steps
+    per_layer_appends = (total_steps + NL - 1) // NL
+    cap = w.capacity(per_layer_appends + R)
+
+    k, v = synth.kv(w)
+    kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
+    del k, v
+    caches = []
+    for _ in range(NL):
+        c = KiviCache(B, H, r, D, bits, G, R, cap)
+        c.prefill(kd, vd, w.tq)
+        caches.append(c)
+    del kd, vd
+    # distinct synthetic tokens / queries for every step, resident on the GPU
+    n_tok = min(total_steps, 256)
+    knew, vnew, qs = [], [], []
+    for s in range(n_tok):
+        kn, vn = synth.new_token(w, s + 1)
+        knew.append(torch.from_numpy(kn).cuda())
+        vnew.append(torch.from_numpy(vn).cuda())
+        qs.append(torch.from_numpy(synth.query(w, s + 1)).cuda())
+    outs = [torch.empty((B, H * r, D), dtype=torch.float16, device="cuda") for _ in range(NL)]
+    for c in caches:
+        c.workspace_for(args.splits)
+    torch.cuda.synchronize()
+
+    def step(i, ev=None):
+        c = caches[i % NL]
+        j = i % n_tok
+        flush = c.tr == R
+        c.append(knew[j], vnew[j])
+        tq, tr = c.tq, c.tr
+        if ev is not None:
+            ev[0].record()
+        c.decode(qs[j], w.softmax_scale, out=outs[i % NL], num_splits=args.splits)
+        if ev is not None:
+            ev[1].record()
+        return flush, tq, tr
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for c in caches:       # back to the workload's starting lengths (full residual)
+        c.set_lengths(w.tq, w.tr)
+    splits_used = caches[0].auto_splits() if args.splits == 0 else args.splits
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    meta = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        meta.append(step(i, events[i]))
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    dec_bytes = [decode_bytes(B, H, r, D, bits, G, tq, tr) for _, tq, tr in meta]
+    app_bytes = [append_bytes(B, H, D, bits, G, R, f) for f, _, _ in meta]
+    total_bytes = sum(dec_bytes) + sum(app_bytes)
+    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
+    value = total_bytes / elapsed / 1e9
+    achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_ms.mean() * 1e-3) / 1e9
+    n_flush = sum(1 for f, _, _ in meta if f)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "q_heads": H * r, "kv_heads": H, "head_dim": D,
+            "context_at_start": w.context, "bits": bits, "group": G, "residual": R,
+            "layers_rotated": NL, "decode_splits": splits_used,
+            "flushes_in_timed_region": n_flush,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "query_heads_per_s": round(args.steps * B * H * r / elapsed, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "kivi decode attention (one kivi_decode_attn call)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": measured_traffic(w.name),
+            "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
+            "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 3),
+            "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+            "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
+        },
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

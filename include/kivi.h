@@ -1,0 +1,186 @@
+/*
+ * kivi.h -- C ABI of the KIVI low-bit KV-cache library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The method ("KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV
+ * Cache"; mlsanity paper page, Abstract; study.space summary page):
+ *   - keys are quantized per channel, values per token, with asymmetric
+ *     low-bit codes (2-bit; 4-bit also supported here);
+ *   - the cache is a quantized "grouped" part plus a full-precision
+ *     "residual" part of the most recent tokens; tokens are appended along
+ *     the token axis, and key groups span G consecutive tokens;
+ *   - decode attention scores the grouped part with a tiled product and
+ *     combines the residual part with it.
+ * The pages print no formula.  This library uses, for every group of G
+ * values x: z = min(x), s = (max(x) - min(x)) / (2^b - 1),
+ * code = round-half-even((x - z) / s) clamped to 2^b - 1, each step one IEEE
+ * binary32 operation in that order (true division, no fused multiply-add);
+ * a group with max == min stores s = 0, z = that value and zero codes.
+ *
+ * Conventions for every function below:
+ *   - All buffer pointers are DEVICE pointers (hipMalloc'd or torch CUDA
+ *     tensors), owned by the caller; the library never allocates, frees,
+ *     reads back or synchronizes.  fp16 is IEEE binary16 bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream); all work
+ *     is enqueued asynchronously on it, in order.
+ *   - Return value: KIVI_OK or one of the error codes below.  Arguments are
+ *     validated before any HIP call; on error nothing is enqueued and no
+ *     output (including *cache) is modified.  Faults inside kernels surface
+ *     at the caller's next synchronization, as for any HIP launch.
+ *   - Every buffer pointer must be 16-byte aligned (KIVI_EALIGN otherwise).
+ *   - Functions are reentrant; one kivi_cache must not be used from two host
+ *     threads at once.
+ *
+ * Storage layout (E = 32 / bits codes per 32-bit word, little-endian bits):
+ *   k_codes : uint32 [B][Hkv][cap][D/E]; channel d of token t is in word d/E
+ *             at bits [bits*(d%E), +bits).
+ *   k_scale, k_zero : float [B][Hkv][cap/G][D]   (one pair per channel per
+ *             group of G tokens).
+ *   v_codes : uint32 [B][Hkv][cap/64][D][64/E]; 64-token tiles, channel-major
+ *             inside a tile: token t, channel d is in tile t/64, word
+ *             (t%64)/E of channel d, bits [bits*((t%64)%E), +bits).
+ *   v_scale, v_zero : float [B][Hkv][cap][D/G]   (one pair per token per
+ *             group of G channels).
+ *   k_res, v_res : fp16 [B][Hkv][R][D]; residual slot i holds cache token
+ *             tq + i.
+ *   queries / outputs : fp16 [B][Hkv*r][D]; query head h reads KV head h/r.
+ */
+#ifndef KIVI_H
+#define KIVI_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kivi_status {
+  KIVI_OK = 0,
+  KIVI_EINVAL = 1,       /* null pointer, bits not in {2,4}, a count < 1    */
+  KIVI_ESHAPE = 2,       /* sizes inconsistent (see each function)          */
+  KIVI_EALIGN = 3,       /* a buffer pointer not 16-byte aligned            */
+  KIVI_ECAPACITY = 4,    /* the quantized store would overflow `capacity`   */
+  KIVI_EWORKSPACE = 5,   /* decode workspace smaller than required          */
+  KIVI_EUNSUPPORTED = 6, /* a (head_dim, group, bits) with no kernel here   */
+  KIVI_EHIP = 7          /* a HIP launch or runtime call failed             */
+};
+
+/* Static configuration of one cache (one attention layer).
+ * Constraints (KIVI_ESHAPE unless noted):
+ *   batch, num_kv_heads, gqa_ratio >= 1 (KIVI_EINVAL);
+ *   bits in {2, 4} (KIVI_EINVAL);
+ *   head_dim in {32, 64, 128, 256}, group in {32, 64, 128}, group divides
+ *     head_dim (KIVI_EUNSUPPORTED for other head_dim/group values);
+ *   residual >= group and a multiple of group;
+ *   capacity >= 0, a multiple of 64 and of group;
+ *   gqa_ratio <= 16. */
+typedef struct {
+  int32_t batch;
+  int32_t num_kv_heads;
+  int32_t gqa_ratio;
+  int32_t head_dim;
+  int32_t bits;
+  int32_t group;
+  int32_t residual;
+  int32_t capacity;
+} kivi_shape;
+
+/* One mixed-precision cache: device buffers (layouts above) plus the host-side
+ * lengths: tq quantized tokens (a multiple of group, <= capacity) and tr
+ * residual tokens (0 <= tr <= residual), equal for every sequence. */
+typedef struct {
+  kivi_shape shape;
+  uint32_t* k_codes;
+  float* k_scale;
+  float* k_zero;
+  uint32_t* v_codes;
+  float* v_scale;
+  float* v_zero;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  int32_t tq;
+  int32_t tr;
+} kivi_cache;
+
+/* Bytes of each cache buffer for a shape (host arithmetic only, no HIP call).
+ * Returns KIVI_OK and fills the six sizes, or a shape error. */
+int kivi_cache_bytes(const kivi_shape* shape, size_t* k_codes, size_t* k_meta,
+                     size_t* v_codes, size_t* v_meta, size_t* residual,
+                     size_t* query);
+
+/* Per-channel key quantization ("KIVI...", Abstract: keys are grouped along
+ * the channel dimension; study.space summary: the key groups span tokens).
+ * Quantizes source tokens [0, ntok) of `k` (fp16 [B][Hkv][in_tok_stride][D])
+ * into cache tokens [dst_tok_offset, dst_tok_offset + ntok) of `codes`,
+ * `scale`, `zero` (layouts above).  Each (channel, group of G tokens) gets
+ * its own scale and zero; results are bit-exact to the formula above.
+ * ntok >= 1, ntok and dst_tok_offset multiples of group, in_tok_stride >=
+ * ntok; dst_tok_offset + ntok > capacity gives KIVI_ECAPACITY. */
+int kivi_quantize_k(const kivi_shape* shape, const uint16_t* k,
+                    int32_t in_tok_stride, int32_t ntok,
+                    int32_t dst_tok_offset, uint32_t* codes, float* scale,
+                    float* zero, void* stream);
+
+/* Per-token value quantization ("KIVI...", Abstract: values are quantized
+ * per token).  Same arguments and rules as kivi_quantize_k; each (token,
+ * group of G channels) gets its own scale and zero. */
+int kivi_quantize_v(const kivi_shape* shape, const uint16_t* v,
+                    int32_t in_tok_stride, int32_t ntok,
+                    int32_t dst_tok_offset, uint32_t* codes, float* scale,
+                    float* zero, void* stream);
+
+/* Fill an empty cache from a prompt (study.space summary: the cache is split
+ * into grouped and residual parts).  k, v: fp16 [B][Hkv][ntok][D].  Tokens
+ * [0, tq) are quantized, tokens [tq, ntok) are copied into the residual.
+ * Requires tq a multiple of group, 0 <= ntok - tq <= residual, tq <=
+ * capacity.  On success sets cache->tq = tq, cache->tr = ntok - tq. */
+int kivi_prefill(kivi_cache* cache, const uint16_t* k, const uint16_t* v,
+                 int32_t ntok, int32_t tq, void* stream);
+
+/* Append one decode token per (sequence, KV head) (study.space summary: new
+ * tokens are appended along the token axis; scholarfeed "KIVI" quote page: a
+ * fixed-length residual of recent full-precision key/value pairs).
+ * k_new, v_new: fp16 [B][Hkv][D].  If the residual already holds `residual`
+ * tokens, all of them are first quantized into tokens [tq, tq + residual) of
+ * the grouped part (KIVI_ECAPACITY if that exceeds capacity), tq grows by
+ * `residual` and tr becomes 0; then the token is stored in residual slot tr
+ * and tr grows by 1.  cache->tq / tr change only on success. */
+int kivi_append(kivi_cache* cache, const uint16_t* k_new,
+                const uint16_t* v_new, void* stream);
+
+/* Split count the decode call uses when num_splits == 0, for the current
+ * cache lengths and the current device (queries the device's compute-unit
+ * count once per device).  Returns >= 1, or a negative error code. */
+int kivi_decode_auto_splits(const kivi_cache* cache);
+
+/* Workspace bytes kivi_decode_attn needs for `num_splits` splits of the
+ * context; num_splits == 0 returns a bound valid for the automatic split
+ * count at every context length of this shape.  Host arithmetic only. */
+size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
+                                   int32_t num_splits);
+
+/* Decode attention on the mixed cache (study.space summary: scores on the
+ * grouped part by a tiled product, the residual part combined with it).
+ * For every sequence b and query head h (KV head h/r):
+ *   o = softmax_t(softmax_scale * q . k_t) . v_t over the tq dequantized and
+ *   tr residual tokens (no mask), accumulated in binary32, written as fp16
+ *   (round to nearest even).  q, out: fp16 [B][Hkv*r][D].
+ * num_splits: number of context chunks per (b, KV head) reduced at the end
+ *   (0 = automatic); workspace: device scratch of at least
+ *   kivi_decode_workspace_bytes(shape, num_splits) bytes (may be NULL when
+ *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  Results are
+ *   deterministic for a fixed split count (no floating-point atomics). */
+int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q,
+                     float softmax_scale, uint16_t* out, void* workspace,
+                     size_t workspace_bytes, int32_t num_splits,
+                     void* stream);
+
+/* Short static description of a status code. */
+const char* kivi_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KIVI_H */

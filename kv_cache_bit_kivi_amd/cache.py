@@ -1,0 +1,121 @@
+"""KiviCache: device buffers for one layer's mixed-precision KV cache.
+
+PyTorch only allocates the buffers and supplies the current HIP stream; all
+computation goes through the C ABI (``_lib``) into the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import check, kivi_cache, kivi_shape
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity) -> kivi_shape:
+    return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity)
+
+
+class KiviCache:
+    """One layer's cache: packed K/V codes, fp32 scale/zero, fp16 residual.
+
+    Layouts are those of include/kivi.h; the host keeps (tq, tr)."""
+
+    def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                 device="cuda"):
+        self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity)
+        sizes = [ctypes.c_size_t() for _ in range(6)]
+        check(_lib.kivi_cache_bytes(ctypes.byref(self.shape), *[ctypes.byref(s) for s in sizes]),
+              "kivi_cache_bytes")
+        B, H, D, G, R, cap = batch, kv_heads, head_dim, group, residual, capacity
+        E = 32 // bits
+        dev = torch.device(device)
+        self.k_codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device=dev)
+        self.k_scale = torch.zeros((B, H, cap // G, D), dtype=torch.float32, device=dev)
+        self.k_zero = torch.zeros((B, H, cap // G, D), dtype=torch.float32, device=dev)
+        self.v_codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device=dev)
+        self.v_scale = torch.zeros((B, H, cap, D // G), dtype=torch.float32, device=dev)
+        self.v_zero = torch.zeros((B, H, cap, D // G), dtype=torch.float32, device=dev)
+        self.k_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
+        self.v_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
+        assert self.k_codes.numel() * 4 == sizes[0].value
+        assert self.k_scale.numel() * 4 == sizes[1].value
+        assert self.v_codes.numel() * 4 == sizes[2].value
+        assert self.v_scale.numel() * 4 == sizes[3].value
+        assert self.k_res.numel() * 2 == sizes[4].value
+        self.c = kivi_cache(self.shape, *[t.data_ptr() for t in (
+            self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
+            self.k_res, self.v_res)], 0, 0)
+        self.workspace = None
+
+    # lengths live on the host, inside the C struct
+    @property
+    def tq(self) -> int:
+        return self.c.tq
+
+    @property
+    def tr(self) -> int:
+        return self.c.tr
+
+    def set_lengths(self, tq: int, tr: int) -> None:
+        self.c.tq, self.c.tr = tq, tr
+
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, tq: int) -> None:
+        """k, v: fp16 [B][Hkv][T][D] contiguous device tensors."""
+        assert k.dtype == torch.float16 and k.is_contiguous() and v.is_contiguous()
+        check(_lib.kivi_prefill(ctypes.byref(self.c), k.data_ptr(), v.data_ptr(), k.shape[2], tq,
+                                _stream()), "kivi_prefill")
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        """k_new, v_new: fp16 [B][Hkv][D]."""
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        check(_lib.kivi_append(ctypes.byref(self.c), k_new.data_ptr(), v_new.data_ptr(),
+                               _stream()), "kivi_append")
+
+    def workspace_for(self, num_splits: int = 0) -> torch.Tensor | None:
+        nbytes = _lib.kivi_decode_workspace_bytes(ctypes.byref(self.shape), num_splits)
+        if nbytes == 0:
+            return None
+        if self.workspace is None or self.workspace.numel() < nbytes:
+            self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.k_codes.device)
+        return self.workspace
+
+    def decode(self, q: torch.Tensor, softmax_scale: float, out: torch.Tensor | None = None,
+               num_splits: int = 0) -> torch.Tensor:
+        """q: fp16 [B][Hkv*r][D] -> fp16 output of the same shape."""
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_decode_attn(ctypes.byref(self.c), q.data_ptr(), float(softmax_scale),
+                                    out.data_ptr(), _ptr(ws), nb, num_splits, _stream()),
+              "kivi_decode_attn")
+        return out
+
+    def auto_splits(self) -> int:
+        s = _lib.kivi_decode_auto_splits(ctypes.byref(self.c))
+        if s < 0:
+            check(-s, "kivi_decode_auto_splits")
+        return s
+
+
+def quantize_k(shape: kivi_shape, k: torch.Tensor, ntok: int, dst_off: int, codes, scale, zero):
+    check(_lib.kivi_quantize_k(ctypes.byref(shape), k.data_ptr(), k.shape[2], ntok, dst_off,
+                               codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()),
+          "kivi_quantize_k")
+
+
+def quantize_v(shape: kivi_shape, v: torch.Tensor, ntok: int, dst_off: int, codes, scale, zero):
+    check(_lib.kivi_quantize_v(ctypes.byref(shape), v.data_ptr(), v.shape[2], ntok, dst_off,
+                               codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()),
+          "kivi_quantize_v")

@@ -1,0 +1,253 @@
+// Generic decode attention on the mixed cache (any supported shape), plus the
+// split-combine kernel shared by every decode path.
+//
+// Method (study.space summary of "KIVI: A Tuning-Free Asymmetric 2bit
+// Quantization for KV Cache"): scores are computed against the quantized
+// grouped part and the full-precision residual part is combined with them.
+// Here: o = softmax(scale * q.k) . v over the tq quantized tokens (keys and
+// values dequantized in registers as code*scale + zero) and the tr residual
+// fp16 tokens, binary32 accumulation.
+//
+// One block of 256 threads per (split, b*Hkv + h).  The block owns a
+// contiguous token chunk and all r query heads of its KV head:
+//   pass 1: one thread per token computes its r scores into LDS;
+//   pass 2: block max / exp / sum per head;
+//   pass 3: threads own (channel, token phase) and accumulate p * v.
+// With one split the block writes fp16 output; otherwise it writes its
+// (max, sum, unnormalised o) partial and the combine kernel merges them.
+#include <math.h>
+
+#include "kivi_internal.h"
+
+namespace kivi {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+__device__ __forceinline__ uint16_t f2h(float x) {
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+__device__ float block_reduce(float v, bool is_max, float* scratch) {
+  for (int off = 32; off > 0; off >>= 1) {
+    float o = __shfl_xor(v, off, 64);
+    v = is_max ? fmaxf(v, o) : v + o;
+  }
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  float r = scratch[0];
+  for (int i = 1; i < kThreads / 64; i++) r = is_max ? fmaxf(r, scratch[i]) : r + scratch[i];
+  return r;
+}
+
+// tokens scored per LDS round: the score buffer stays at 4-8 KB per head group
+template <int RR>
+constexpr int sub_tokens() { return RR <= 2 ? 1024 : 2048 / RR; }
+
+template <int RR>
+__global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, int chunk) {
+  constexpr int kSub = sub_tokens<RR>();
+  extern __shared__ __align__(16) float sm[];
+  const int r = a.r, D = a.D, G = a.G, bits = a.bits;
+  float* sq = sm;                    // [r][D]   scale * q
+  float* sp = sq + r * D;            // [r][kSub] scores, then weights
+  float* so = sp + r * kSub;         // [kThreads/D][RR][D] pass-3 partials
+  float* red = so + RR * kThreads;   // reduction scratch
+  float* stat = red + 8;             // [RR] running max, [RR] running sum, [RR] rescale
+
+  const int split = blockIdx.x;
+  const int u = blockIdx.y;          // b * H + h
+  const int b = u / a.H, h = u % a.H;
+  const int L = a.tq + a.tr;
+  const int t0 = split * chunk;
+  const int t1 = min(L, t0 + chunk);
+  const int E = 32 / bits, W = D / E, WPC = 64 / E, NG = D / G;
+  const uint32_t mask = (1u << bits) - 1u;
+
+  const size_t kvp = (size_t)u;                   // plane index
+  const uint32_t* kc = a.k_codes + kvp * (size_t)a.cap * W;
+  const float* ks = a.k_scale + kvp * (size_t)(a.cap / G) * D;
+  const float* kz = a.k_zero + kvp * (size_t)(a.cap / G) * D;
+  const uint32_t* vc = a.v_codes + kvp * (size_t)a.cap * D / E;
+  const float* vs = a.v_scale + kvp * (size_t)a.cap * NG;
+  const float* vz = a.v_zero + kvp * (size_t)a.cap * NG;
+  const uint16_t* kr = a.k_res + kvp * (size_t)a.R * D;
+  const uint16_t* vr = a.v_res + kvp * (size_t)a.R * D;
+  const size_t qrow0 = (size_t)b * a.H * r + (size_t)h * r;   // first query row
+
+  for (int i = threadIdx.x; i < r * D; i += kThreads) sq[i] = a.scale * h2f(a.q[qrow0 * D + i]);
+  if (threadIdx.x < RR) {
+    stat[threadIdx.x] = -INFINITY;
+    stat[RR + threadIdx.x] = 0.f;
+  }
+  __syncthreads();
+
+  const int nsub = kThreads / D;
+  const int d = threadIdx.x % D, sub = threadIdx.x / D;
+  float o[RR];
+#pragma unroll
+  for (int i = 0; i < RR; i++) o[i] = 0.f;
+
+  for (int c0 = t0; c0 < t1; c0 += kSub) {
+    const int c1 = min(t1, c0 + kSub);
+    const int nn = c1 - c0;
+    // pass 1: scores of tokens [c0, c1)
+    for (int t = c0 + threadIdx.x; t < c1; t += kThreads) {
+      float acc[RR];
+#pragma unroll
+      for (int i = 0; i < RR; i++) acc[i] = 0.f;
+      if (t < a.tq) {
+        const uint32_t* row = kc + (size_t)t * W;
+        const float* s_row = ks + (size_t)(t / G) * D;
+        const float* z_row = kz + (size_t)(t / G) * D;
+        for (int w = 0; w < W; w++) {
+          const uint32_t word = row[w];
+          for (int e = 0; e < E; e++) {
+            const int dd = w * E + e;
+            const float kh = (float)((word >> (bits * e)) & mask) * s_row[dd] + z_row[dd];
+#pragma unroll
+            for (int i = 0; i < RR; i++)
+              if (i < r) acc[i] += sq[i * D + dd] * kh;
+          }
+        }
+      } else {
+        const uint16_t* row = kr + (size_t)(t - a.tq) * D;
+        for (int dd = 0; dd < D; dd++) {
+          const float kh = h2f(row[dd]);
+#pragma unroll
+          for (int i = 0; i < RR; i++)
+            if (i < r) acc[i] += sq[i * D + dd] * kh;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RR; i++)
+        if (i < r) sp[i * kSub + (t - c0)] = acc[i];
+    }
+    __syncthreads();
+
+    // pass 2: online softmax statistics per head
+    for (int i = 0; i < r; i++) {
+      float m = -INFINITY;
+      for (int j = threadIdx.x; j < nn; j += kThreads) m = fmaxf(m, sp[i * kSub + j]);
+      m = block_reduce(m, true, red);
+      const float m_old = stat[i];
+      const float m_new = fmaxf(m_old, m);
+      float l = 0.f;
+      for (int j = threadIdx.x; j < nn; j += kThreads) {
+        const float p = __expf(sp[i * kSub + j] - m_new);
+        sp[i * kSub + j] = p;
+        l += p;
+      }
+      l = block_reduce(l, false, red);
+      if (threadIdx.x == 0) {
+        const float alpha = __expf(m_old - m_new);   // 0 on the first sub-chunk
+        stat[i] = m_new;
+        stat[RR + i] = stat[RR + i] * alpha + l;
+        stat[2 * RR + i] = alpha;
+      }
+      __syncthreads();
+    }
+
+    // pass 3: weighted values
+    if (sub < nsub) {
+#pragma unroll
+      for (int i = 0; i < RR; i++)
+        if (i < r) o[i] *= stat[2 * RR + i];
+      for (int t = c0 + sub; t < c1; t += nsub) {
+        float vh;
+        if (t < a.tq) {
+          const uint32_t word = vc[((size_t)(t / 64) * D + d) * WPC + (t % 64) / E];
+          const int j = d / G;
+          vh = (float)((word >> (bits * ((t % 64) % E))) & mask) * vs[(size_t)t * NG + j] +
+               vz[(size_t)t * NG + j];
+        } else {
+          vh = h2f(vr[(size_t)(t - a.tq) * D + d]);
+        }
+#pragma unroll
+        for (int i = 0; i < RR; i++)
+          if (i < r) o[i] += sp[i * kSub + (t - c0)] * vh;
+      }
+    }
+    __syncthreads();
+  }
+
+  // reduce the token phases: so[sub][i][d]
+  for (int i = 0; i < RR; i++)
+    if (i < r && sub < nsub) so[(sub * RR + i) * D + d] = o[i];
+  __syncthreads();
+  const bool empty = t1 <= t0;
+  for (int idx = threadIdx.x; idx < r * D; idx += kThreads) {
+    const int i = idx / D, dd = idx % D;
+    float acc = 0.f;
+    for (int s = 0; s < nsub; s++) acc += so[(s * RR + i) * D + dd];
+    const size_t row = qrow0 + i;
+    if (a.S == 1) {
+      a.out[row * D + dd] = f2h(acc / stat[RR + i]);
+    } else {
+      const size_t rows = (size_t)a.B * a.H * r;
+      if (dd == 0) {
+        a.ws[row * a.S + split] = empty ? -INFINITY : stat[i];
+        a.ws[rows * a.S + row * a.S + split] = empty ? 0.f : stat[RR + i];
+      }
+      a.ws[2 * rows * a.S + (row * a.S + split) * D + dd] = empty ? 0.f : acc;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ ws,
+                                                      uint16_t* __restrict__ out, int rows,
+                                                      int S, int D) {
+  const int row = blockIdx.x;
+  const float* m = ws + (size_t)row * S;
+  const float* l = ws + (size_t)rows * S + (size_t)row * S;
+  const float* o = ws + 2 * (size_t)rows * S + (size_t)row * S * D;
+  float M = -INFINITY;
+  for (int s = 0; s < S; s++) M = fmaxf(M, m[s]);
+  float Ls = 0.f;
+  for (int s = 0; s < S; s++) Ls += l[s] * __expf(m[s] - M);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < S; s++) acc += o[(size_t)s * D + d] * __expf(m[s] - M);
+    out[(size_t)row * D + d] = f2h(acc / Ls);
+  }
+}
+
+}  // namespace
+
+size_t decode_generic_lds_bytes(int r, int D) {
+  int rr = 1;
+  while (rr < r) rr *= 2;
+  const int sub = rr <= 2 ? 1024 : 2048 / rr;
+  return sizeof(float) * ((size_t)r * D + (size_t)r * sub + (size_t)rr * kThreads + 8 + 3 * rr);
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+  const int L = a.tq + a.tr;
+  const int chunk = (L + a.S - 1) / a.S;
+  dim3 grid(a.S, a.B * a.H);
+  const size_t lds = decode_generic_lds_bytes(a.r, a.D);
+  if (a.r == 1)
+    decode_generic_kernel<1><<<grid, kThreads, lds, st>>>(a, chunk);
+  else if (a.r == 2)
+    decode_generic_kernel<2><<<grid, kThreads, lds, st>>>(a, chunk);
+  else if (a.r <= 4)
+    decode_generic_kernel<4><<<grid, kThreads, lds, st>>>(a, chunk);
+  else if (a.r <= 8)
+    decode_generic_kernel<8><<<grid, kThreads, lds, st>>>(a, chunk);
+  else
+    decode_generic_kernel<16><<<grid, kThreads, lds, st>>>(a, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
+  const int rows = a.B * a.H * a.r;
+  combine_kernel<<<rows, 128, 0, st>>>(a.ws, a.out, rows, a.S, a.D);
+  return hipGetLastError();
+}
+
+}  // namespace kivi

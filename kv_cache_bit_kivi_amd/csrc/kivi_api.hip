@@ -1,0 +1,294 @@
+// C ABI entry points: argument validation (before any HIP call), launch
+// configuration and the host-side cache lengths.  See include/kivi.h.
+#include "kivi.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+
+#include "kivi_internal.h"
+
+namespace {
+
+using kivi::DecodeArgs;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const kivi_shape* s) {
+  if (!s) return KIVI_EINVAL;
+  if (s->batch < 1 || s->num_kv_heads < 1 || s->gqa_ratio < 1) return KIVI_EINVAL;
+  if (s->bits != 2 && s->bits != 4) return KIVI_EINVAL;
+  const int D = s->head_dim, G = s->group;
+  if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
+  if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
+  if (s->gqa_ratio > 16) return KIVI_EUNSUPPORTED;
+  if (D % G != 0) return KIVI_ESHAPE;
+  if (s->residual < G || s->residual % G != 0) return KIVI_ESHAPE;
+  if (s->capacity < 0 || s->capacity % 64 != 0 || s->capacity % G != 0) return KIVI_ESHAPE;
+  // 32-bit index arithmetic bound on one (b, h) plane of codes
+  if ((int64_t)s->capacity * D > (int64_t)1 << 31) return KIVI_ESHAPE;
+  return KIVI_OK;
+}
+
+int check_cache(const kivi_cache* c) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  const void* ptrs[] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
+                        c->v_scale, c->v_zero,  c->k_res,  c->v_res};
+  for (const void* p : ptrs)
+    if (!p) return KIVI_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  if (c->tq < 0 || c->tq % s.group != 0 || c->tr < 0 || c->tr > s.residual)
+    return KIVI_ESHAPE;
+  if (c->tq > s.capacity) return KIVI_ECAPACITY;
+  return KIVI_OK;
+}
+
+int check_quantize(const kivi_shape* s, const uint16_t* x, int32_t in_stride, int32_t ntok,
+                   int32_t dst, const uint32_t* codes, const float* scale, const float* zero) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!x || !codes || !scale || !zero) return KIVI_EINVAL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scale) || !aligned16(zero))
+    return KIVI_EALIGN;
+  if (ntok < 1 || ntok % s->group != 0 || dst < 0 || dst % s->group != 0 || in_stride < ntok)
+    return KIVI_ESHAPE;
+  if ((int64_t)dst + ntok > s->capacity) return KIVI_ECAPACITY;
+  return KIVI_OK;
+}
+
+std::atomic<int> g_cu_count[64];
+
+int device_cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -KIVI_EHIP;
+  if (dev < 64) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return -KIVI_EHIP;
+  if (dev < 64) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Largest split count the automatic choice can return for a shape: a split
+// count beyond 2048 (b, h) blocks buys nothing on a 256-CU device.
+int max_auto_splits(const kivi_shape& s) {
+  const int units = s.batch * s.num_kv_heads;
+  return units >= 2048 ? 1 : (2048 + units - 1) / units;
+}
+
+int auto_splits(const kivi_shape& s, int L, int cus) {
+  const int units = s.batch * s.num_kv_heads;
+  // aim for about two blocks per compute unit, at least 256 tokens a split
+  int want = (2 * cus + units - 1) / units;
+  int by_len = (L + 255) / 256;
+  int S = want < by_len ? want : by_len;
+  if (S < 1) S = 1;
+  const int cap = max_auto_splits(s);
+  return S > cap ? cap : S;
+}
+
+size_t ws_bytes(const kivi_shape& s, int S) {
+  if (S <= 1) return 0;
+  const size_t rows = (size_t)s.batch * s.num_kv_heads * s.gqa_ratio;
+  return rows * (size_t)S * (size_t)(s.head_dim + 2) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kivi_strerror(int status) {
+  switch (status) {
+    case KIVI_OK: return "ok";
+    case KIVI_EINVAL: return "invalid argument (null pointer, bits, or count)";
+    case KIVI_ESHAPE: return "inconsistent sizes";
+    case KIVI_EALIGN: return "buffer not 16-byte aligned";
+    case KIVI_ECAPACITY: return "quantized store capacity exceeded";
+    case KIVI_EWORKSPACE: return "decode workspace too small";
+    case KIVI_EUNSUPPORTED: return "unsupported head_dim / group / gqa_ratio";
+    case KIVI_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int kivi_cache_bytes(const kivi_shape* s, size_t* k_codes, size_t* k_meta, size_t* v_codes,
+                     size_t* v_meta, size_t* residual, size_t* query) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  const size_t planes = (size_t)s->batch * s->num_kv_heads;
+  const size_t cap = s->capacity, D = s->head_dim, G = s->group;
+  const size_t codes = planes * cap * D * s->bits / 8;
+  if (k_codes) *k_codes = codes;
+  if (v_codes) *v_codes = codes;
+  if (k_meta) *k_meta = planes * (cap / G) * D * sizeof(float);
+  if (v_meta) *v_meta = planes * cap * (D / G) * sizeof(float);
+  if (residual) *residual = planes * (size_t)s->residual * D * 2;
+  if (query) *query = planes * (size_t)s->gqa_ratio * D * 2;
+  return KIVI_OK;
+}
+
+int kivi_quantize_k(const kivi_shape* s, const uint16_t* k, int32_t in_tok_stride, int32_t ntok,
+                    int32_t dst, uint32_t* codes, float* scale, float* zero, void* stream) {
+  int rc = check_quantize(s, k, in_tok_stride, ntok, dst, codes, scale, zero);
+  if (rc) return rc;
+  hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
+                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
+                                         scale, zero, (hipStream_t)stream);
+  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+}
+
+int kivi_quantize_v(const kivi_shape* s, const uint16_t* v, int32_t in_tok_stride, int32_t ntok,
+                    int32_t dst, uint32_t* codes, float* scale, float* zero, void* stream) {
+  int rc = check_quantize(s, v, in_tok_stride, ntok, dst, codes, scale, zero);
+  if (rc) return rc;
+  hipError_t e = kivi::launch_quantize_v(v, s->batch, s->num_kv_heads, s->head_dim, s->bits,
+                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
+                                         scale, zero, (hipStream_t)stream);
+  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+}
+
+int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t ntok, int32_t tq,
+                 void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!k || !v) return KIVI_EINVAL;
+  if (!aligned16(k) || !aligned16(v)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  if (ntok < 1 || tq < 0 || tq % s.group != 0 || ntok - tq < 0 || ntok - tq > s.residual)
+    return KIVI_ESHAPE;
+  if (tq > s.capacity) return KIVI_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  if (tq > 0) {
+    hipError_t e = kivi::launch_quantize_k(k, s.batch, s.num_kv_heads, s.head_dim, s.bits,
+                                           s.group, s.capacity, ntok, tq, 0, c->k_codes,
+                                           c->k_scale, c->k_zero, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+    e = kivi::launch_quantize_v(v, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
+                                s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+  }
+  if (ntok > tq) {
+    hipError_t e = kivi::launch_copy_tokens(k, v, ntok, tq, c->k_res, c->v_res, s.residual, 0,
+                                            ntok - tq, s.batch, s.num_kv_heads, s.head_dim, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+  }
+  c->tq = tq;
+  c->tr = ntok - tq;
+  return KIVI_OK;
+}
+
+int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  hipStream_t st = (hipStream_t)stream;
+  int tq = c->tq, tr = c->tr;
+  if (tr == s.residual) {
+    if ((int64_t)tq + s.residual > s.capacity) return KIVI_ECAPACITY;
+    // flush: the full residual becomes the next quantized tokens; the copy
+    // below is enqueued after, so slot 0 is read before it is overwritten
+    hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
+                                           s.bits, s.group, s.capacity, s.residual, s.residual,
+                                           tq, c->k_codes, c->k_scale, c->k_zero, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+    e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
+                                s.capacity, s.residual, s.residual, tq, c->v_codes, c->v_scale,
+                                c->v_zero, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+    tq += s.residual;
+    tr = 0;
+  }
+  hipError_t e = kivi::launch_copy_tokens(k_new, v_new, 1, 0, c->k_res, c->v_res, s.residual,
+                                          tr, 1, s.batch, s.num_kv_heads, s.head_dim, st);
+  if (e != hipSuccess) return KIVI_EHIP;
+  c->tq = tq;
+  c->tr = tr + 1;
+  return KIVI_OK;
+}
+
+int kivi_decode_auto_splits(const kivi_cache* c) {
+  int rc = check_cache(c);
+  if (rc) return -rc;
+  const int cus = device_cu_count();
+  if (cus < 0) return cus;
+  return auto_splits(c->shape, c->tq + c->tr, cus);
+}
+
+size_t kivi_decode_workspace_bytes(const kivi_shape* s, int32_t num_splits) {
+  if (check_shape(s) != KIVI_OK || num_splits < 0) return 0;
+  return ws_bytes(*s, num_splits == 0 ? max_auto_splits(*s) : num_splits);
+}
+
+int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, float softmax_scale, uint16_t* out,
+                     void* workspace, size_t workspace_bytes, int32_t num_splits,
+                     void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!q || !out) return KIVI_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
+  if (num_splits < 0) return KIVI_EINVAL;
+  const kivi_shape& s = c->shape;
+  const int L = c->tq + c->tr;
+  if (L < 1) return KIVI_ESHAPE;
+  if (num_splits > 0 && num_splits > L) return KIVI_ESHAPE;
+  if (num_splits > 1) {
+    if (workspace_bytes < ws_bytes(s, num_splits)) return KIVI_EWORKSPACE;
+    if (!workspace) return KIVI_EINVAL;
+    if (!aligned16(workspace)) return KIVI_EALIGN;
+  }
+  int S = num_splits;
+  if (S == 0) {
+    const int cus = device_cu_count();
+    if (cus < 0) return KIVI_EHIP;
+    S = auto_splits(s, L, cus);
+    if (S > 1) {
+      if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
+      if (!workspace) return KIVI_EINVAL;
+      if (!aligned16(workspace)) return KIVI_EALIGN;
+    }
+  }
+  DecodeArgs a;
+  a.k_codes = c->k_codes;
+  a.k_scale = c->k_scale;
+  a.k_zero = c->k_zero;
+  a.v_codes = c->v_codes;
+  a.v_scale = c->v_scale;
+  a.v_zero = c->v_zero;
+  a.k_res = c->k_res;
+  a.v_res = c->v_res;
+  a.q = q;
+  a.out = out;
+  a.ws = static_cast<float*>(workspace);
+  a.B = s.batch;
+  a.H = s.num_kv_heads;
+  a.r = s.gqa_ratio;
+  a.D = s.head_dim;
+  a.bits = s.bits;
+  a.G = s.group;
+  a.R = s.residual;
+  a.cap = s.capacity;
+  a.tq = c->tq;
+  a.tr = c->tr;
+  a.S = S;
+  a.scale = softmax_scale;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = kivi::launch_decode_generic(a, st);
+  if (e != hipSuccess) return KIVI_EHIP;
+  if (S > 1) {
+    e = kivi::launch_combine(a, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+  }
+  return KIVI_OK;
+}
+
+}  // extern "C"

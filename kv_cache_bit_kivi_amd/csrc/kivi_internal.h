@@ -1,0 +1,47 @@
+// Internal declarations shared by the library's translation units.
+// Not part of the public ABI (see include/kivi.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kivi {
+
+// Device pointers and lengths of one decode call.
+struct DecodeArgs {
+  const uint32_t* k_codes;
+  const float* k_scale;
+  const float* k_zero;
+  const uint32_t* v_codes;
+  const float* v_scale;
+  const float* v_zero;
+  const uint16_t* k_res;
+  const uint16_t* v_res;
+  const uint16_t* q;
+  uint16_t* out;
+  float* ws;          // split partials: m, l [rows][S], o [rows][S][D]
+  int B, H, r, D, bits, G, R, cap, tq, tr, S;
+  float scale;
+};
+
+// Launchers: validate nothing (the C ABI layer did), return hipError_t of the
+// launch.
+hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G,
+                             int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
+                             float* scale, float* zero, hipStream_t st);
+hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G,
+                             int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
+                             float* scale, float* zero, hipStream_t st);
+// Copies tokens [t0, t0 + n) of src ([B][H][src_stride][D]) into slots
+// [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once.
+hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
+                              int t0, uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
+                              int slot0, int n, int B, int H, int D, hipStream_t st);
+
+// Generic decode kernel (any supported shape) + split combine.
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+size_t decode_generic_lds_bytes(int r, int D);
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace kivi

@@ -1,0 +1,213 @@
+// Quantize kernels: per-channel keys, per-token values, and token copies.
+//
+// Method: "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
+// (mlsanity paper page, Abstract): keys are quantized per channel, values per
+// token, with asymmetric low-bit codes; study.space summary: key groups span
+// consecutive tokens and new tokens are appended along the token axis.
+//
+// Codec, per group of G values (bit-exact contract, IEEE binary32, built with
+// -ffp-contract=off and correctly rounded division):
+//   mn, mx   : strict-comparison scan in index order (first extremum wins);
+//   mx == mn : scale 0, zero mn, codes 0 (the group dequantizes exactly);
+//   else     : range = mx - mn; s = range / (2^b - 1); z = mn;
+//              code = min(rint((x - z) / s), 2^b - 1), rint = half-to-even.
+// Each block stages its fp16 tile in LDS with 16-byte loads, computes the
+// group statistics from LDS, then writes whole 32-bit code words, so any
+// number of blocks can run concurrently without read-modify-write.
+#include "kivi_internal.h"
+
+namespace kivi {
+namespace {
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+template <int BITS>
+__device__ __forceinline__ void group_stats(float mn, float mx, float* s_out) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  if (mx == mn) {
+    *s_out = 0.0f;
+  } else {
+    float range = mx - mn;
+    *s_out = range / qmax;
+  }
+}
+
+template <int BITS>
+__device__ __forceinline__ uint32_t encode(float x, float s, float z) {
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  if (s == 0.0f) return 0u;
+  float u = x - z;
+  float v = u / s;
+  float c = rintf(v);
+  if (c > qmax) c = qmax;
+  return (uint32_t)c;
+}
+
+// One block per (group of G source tokens, b*H + h).
+template <int BITS>
+__global__ void __launch_bounds__(256)
+quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
+                  int dst_off, uint32_t* __restrict__ codes, float* __restrict__ scale,
+                  float* __restrict__ zero) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
+  float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
+  float* s_zr = s_sc + D;                                    // [D]
+  const int g = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const uint4* src = reinterpret_cast<const uint4*>(k + (bh * in_stride + (size_t)g * G) * D);
+  for (int i = threadIdx.x; i < G * D / 8; i += blockDim.x)
+    reinterpret_cast<uint4*>(tile)[i] = src[i];
+  __syncthreads();
+
+  const size_t gg = (size_t)(dst_off / G + g);
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float mn = h2f(tile[d]), mx = mn;
+    for (int i = 1; i < G; i++) {
+      float x = h2f(tile[i * D + d]);
+      if (x < mn) mn = x;
+      if (x > mx) mx = x;
+    }
+    float s;
+    group_stats<BITS>(mn, mx, &s);
+    s_sc[d] = s;
+    s_zr[d] = mn;
+    size_t m = (bh * (cap / G) + gg) * D + d;
+    scale[m] = s;
+    zero[m] = mn;
+  }
+  __syncthreads();
+
+  constexpr int E = 32 / BITS;
+  const int W = D / E;
+  uint32_t* dst = codes + (bh * cap + dst_off + (size_t)g * G) * W;
+  for (int it = threadIdx.x; it < G * W; it += blockDim.x) {
+    const int i = it / W, w = it % W;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      const int d = w * E + e;
+      word |= encode<BITS>(h2f(tile[i * D + d]), s_sc[d], s_zr[d]) << (BITS * e);
+    }
+    dst[it] = word;
+  }
+}
+
+// One block per (32 source tokens, b*H + h).  Value codes are stored in
+// 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E) + (t%64)/E.
+template <int BITS>
+__global__ void __launch_bounds__(256)
+quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_stride,
+                  int dst_off, uint32_t* __restrict__ codes, float* __restrict__ scale,
+                  float* __restrict__ zero) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [32][D]
+  const int NG = D / G;
+  float* s_sc = reinterpret_cast<float*>(tile + 32 * D);     // [32][NG]
+  float* s_zr = s_sc + 32 * NG;
+  const int blk = blockIdx.x;
+  const size_t bh = blockIdx.y;
+  const uint4* src = reinterpret_cast<const uint4*>(v + (bh * in_stride + (size_t)blk * 32) * D);
+  for (int i = threadIdx.x; i < 32 * D / 8; i += blockDim.x)
+    reinterpret_cast<uint4*>(tile)[i] = src[i];
+  __syncthreads();
+
+  const int t_base = dst_off + blk * 32;  // cache token of local token 0
+  for (int it = threadIdx.x; it < 32 * NG; it += blockDim.x) {
+    const int t = it / NG, j = it % NG;
+    const uint16_t* row = tile + t * D + j * G;
+    float mn = h2f(row[0]), mx = mn;
+    for (int i = 1; i < G; i++) {
+      float x = h2f(row[i]);
+      if (x < mn) mn = x;
+      if (x > mx) mx = x;
+    }
+    float s;
+    group_stats<BITS>(mn, mx, &s);
+    s_sc[it] = s;
+    s_zr[it] = mn;
+    size_t m = (bh * cap + t_base + t) * NG + j;
+    scale[m] = s;
+    zero[m] = mn;
+  }
+  __syncthreads();
+
+  constexpr int E = 32 / BITS;
+  constexpr int WPB = 32 / E;   // words per channel in this 32-token block
+  constexpr int WPC = 64 / E;   // words per channel per 64-token tile
+  uint32_t* plane = codes + bh * ((size_t)cap * D / E);
+  const size_t tile_idx = (size_t)(t_base / 64);
+  const int word0 = (t_base % 64) / E;
+  for (int it = threadIdx.x; it < D * WPB; it += blockDim.x) {
+    const int d = it / WPB, qw = it % WPB;
+    const int j = d / G;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < E; e++) {
+      const int t = qw * E + e;
+      word |= encode<BITS>(h2f(tile[t * D + d]), s_sc[t * NG + j], s_zr[t * NG + j])
+              << (BITS * e);
+    }
+    plane[(tile_idx * D + d) * WPC + word0 + qw] = word;
+  }
+}
+
+__global__ void __launch_bounds__(256)
+copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
+                   int src_stride, int t0, uint16_t* __restrict__ k_dst,
+                   uint16_t* __restrict__ v_dst, int dst_stride, int slot0, int n, int D) {
+  const size_t bh = blockIdx.y;
+  const int per_tok = D / 8;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n * per_tok;
+       i += gridDim.x * blockDim.x) {
+    const int t = i / per_tok, c = i % per_tok;
+    const size_t so = ((bh * src_stride + t0 + t) * D) / 8 + c;
+    const size_t dd = ((bh * dst_stride + slot0 + t) * D) / 8 + c;
+    reinterpret_cast<uint4*>(k_dst)[dd] = reinterpret_cast<const uint4*>(k_src)[so];
+    reinterpret_cast<uint4*>(v_dst)[dd] = reinterpret_cast<const uint4*>(v_src)[so];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G, int cap,
+                             int in_stride, int ntok, int dst_off, uint32_t* codes,
+                             float* scale, float* zero, hipStream_t st) {
+  dim3 grid(ntok / G, B * H);
+  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
+  if (bits == 2)
+    quantize_k_kernel<2><<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes,
+                                                 scale, zero);
+  else
+    quantize_k_kernel<4><<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes,
+                                                 scale, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G, int cap,
+                             int in_stride, int ntok, int dst_off, uint32_t* codes,
+                             float* scale, float* zero, hipStream_t st) {
+  dim3 grid(ntok / 32, B * H);
+  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
+  if (bits == 2)
+    quantize_v_kernel<2><<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes,
+                                                 scale, zero);
+  else
+    quantize_v_kernel<4><<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes,
+                                                 scale, zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
+                              int t0, uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
+                              int slot0, int n, int B, int H, int D, hipStream_t st) {
+  const int items = n * D / 8;
+  dim3 grid((items + 255) / 256, B * H);
+  copy_tokens_kernel<<<grid, 256, 0, st>>>(k_src, v_src, src_stride, t0, k_dst, v_dst,
+                                           dst_stride, slot0, n, D);
+  return hipGetLastError();
+}
+
+}  // namespace kivi

@@ -1,0 +1,162 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+include/kivi.h declares, and rejects bad arguments before any HIP call
+(nothing is enqueued and the cache lengths stay unchanged)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_bit_kivi_amd import _lib
+from kv_cache_bit_kivi_amd._lib import (KIVI_EALIGN, KIVI_ECAPACITY, KIVI_EINVAL, KIVI_ESHAPE,
+                                        KIVI_EUNSUPPORTED, KIVI_EWORKSPACE, KIVI_OK, kivi_cache,
+                                        kivi_shape)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "kivi.h")
+P = 4096  # fake 16-byte aligned "device" address: never dereferenced on error paths
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kivi_\w+)\s*\(", text)))
+
+
+def test_exports_match_header():
+    names = declared()
+    assert len(names) >= 9
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(_lib.PROTOTYPES) == names
+
+
+def test_strerror():
+    for code in range(8):
+        assert _lib.kivi_strerror(code)
+    assert _lib.kivi_strerror(99) == b"unknown status"
+
+
+def shape(**kw):
+    d = dict(batch=2, num_kv_heads=4, gqa_ratio=2, head_dim=128, bits=2, group=32,
+             residual=128, capacity=512)
+    d.update(kw)
+    return kivi_shape(*[d[n] for n, _ in kivi_shape._fields_])
+
+
+def sizes(s):
+    out = [ctypes.c_size_t() for _ in range(6)]
+    rc = _lib.kivi_cache_bytes(ctypes.byref(s), *[ctypes.byref(x) for x in out])
+    return rc, [x.value for x in out]
+
+
+def test_cache_bytes():
+    rc, sz = sizes(shape())
+    assert rc == KIVI_OK
+    planes, cap, D = 8, 512, 128
+    assert sz == [planes * cap * D // 4, planes * cap // 32 * D * 4, planes * cap * D // 4,
+                  planes * cap * 4 * 4, planes * 128 * D * 2, planes * 2 * D * 2]
+    rc, sz = sizes(shape(bits=4))
+    assert sz[0] == planes * cap * D // 2
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=0), KIVI_EINVAL), (dict(num_kv_heads=0), KIVI_EINVAL),
+    (dict(gqa_ratio=0), KIVI_EINVAL), (dict(bits=3), KIVI_EINVAL), (dict(bits=8), KIVI_EINVAL),
+    (dict(head_dim=48), KIVI_EUNSUPPORTED), (dict(group=16), KIVI_EUNSUPPORTED),
+    (dict(gqa_ratio=17), KIVI_EUNSUPPORTED), (dict(head_dim=32, group=64), KIVI_ESHAPE),
+    (dict(residual=48), KIVI_ESHAPE), (dict(residual=16, group=32), KIVI_ESHAPE),
+    (dict(capacity=96), KIVI_ESHAPE), (dict(capacity=-64), KIVI_ESHAPE),
+    (dict(group=128, capacity=192), KIVI_ESHAPE),
+])
+def test_shape_errors(kw, code):
+    assert sizes(shape(**kw))[0] == code
+
+
+def qk(s, x=P, stride=256, ntok=64, dst=0, codes=P, sc=P, zr=P):
+    return _lib.kivi_quantize_k(ctypes.byref(s), x, stride, ntok, dst, codes, sc, zr, None)
+
+
+def qv(s, x=P, stride=256, ntok=64, dst=0, codes=P, sc=P, zr=P):
+    return _lib.kivi_quantize_v(ctypes.byref(s), x, stride, ntok, dst, codes, sc, zr, None)
+
+
+@pytest.mark.parametrize("fn", [qk, qv])
+def test_quantize_errors(fn):
+    s = shape()
+    assert fn(s, x=None) == KIVI_EINVAL
+    assert fn(s, codes=None) == KIVI_EINVAL
+    assert fn(s, x=P + 2) == KIVI_EALIGN
+    assert fn(s, zr=P + 8) == KIVI_EALIGN
+    assert fn(s, ntok=0) == KIVI_ESHAPE
+    assert fn(s, ntok=48) == KIVI_ESHAPE
+    assert fn(s, dst=16) == KIVI_ESHAPE
+    assert fn(s, dst=-32) == KIVI_ESHAPE
+    assert fn(s, stride=32, ntok=64) == KIVI_ESHAPE
+    assert fn(s, ntok=64, dst=480) == KIVI_ECAPACITY
+    assert fn(shape(bits=3)) == KIVI_EINVAL
+
+
+def cache(**kw):
+    tq = kw.pop("tq", 0)
+    tr = kw.pop("tr", 0)
+    ptrs = kw.pop("ptrs", [P] * 8)
+    return kivi_cache(shape(**kw), *ptrs, tq, tr)
+
+
+def test_append_errors_leave_state():
+    c = cache(tq=416, tr=128)          # the flush would end at 544 > capacity 512
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    assert (c.tq, c.tr) == (416, 128)
+    c = cache(tq=32 + 1, tr=0)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_ESHAPE
+    c = cache(tq=0, tr=129)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_ESHAPE
+    assert (c.tq, c.tr) == (0, 129)
+    c = cache()
+    assert _lib.kivi_append(ctypes.byref(c), None, P, None) == KIVI_EINVAL
+    assert _lib.kivi_append(ctypes.byref(c), P + 4, P, None) == KIVI_EALIGN
+    c = cache(ptrs=[P] * 7 + [0])
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_EINVAL
+    c = cache(ptrs=[P] * 3 + [P + 8] + [P] * 4)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_EALIGN
+    c = cache(tq=1024, tr=0)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    assert (c.tq, c.tr) == (1024, 0)
+
+
+def test_prefill_errors():
+    c = cache()
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 300, 128, None) == KIVI_ESHAPE  # tr > R
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 100, 48, None) == KIVI_ESHAPE   # tq % G
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 0, 0, None) == KIVI_ESHAPE
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 600, 544, None) == KIVI_ECAPACITY
+    assert _lib.kivi_prefill(ctypes.byref(c), None, P, 64, 64, None) == KIVI_EINVAL
+    assert (c.tq, c.tr) == (0, 0)
+
+
+def test_decode_errors():
+    c = cache(tq=0, tr=0)
+    dec = _lib.kivi_decode_attn
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE   # empty cache
+    c = cache(tq=64, tr=3)
+    assert dec(ctypes.byref(c), None, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert dec(ctypes.byref(c), P, 0.1, P + 2, None, 0, 1, None) == KIVI_EALIGN
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, -1, None) == KIVI_EINVAL
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 68, None) == KIVI_ESHAPE  # splits > tokens
+    need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4)
+    assert dec(ctypes.byref(c), P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
+    assert dec(ctypes.byref(c), P, 0.1, P, None, need, 4, None) == KIVI_EINVAL
+    assert dec(ctypes.byref(c), P, 0.1, P, P + 4, need, 4, None) == KIVI_EALIGN
+    c = cache(tq=64, tr=200)
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+
+
+def test_workspace_bytes():
+    s = shape()
+    ws = _lib.kivi_decode_workspace_bytes
+    assert ws(ctypes.byref(s), 1) == 0
+    rows = 2 * 4 * 2
+    assert ws(ctypes.byref(s), 4) == rows * 4 * (128 + 2) * 4
+    assert ws(ctypes.byref(s), 0) >= ws(ctypes.byref(s), 4)
+    assert ws(ctypes.byref(shape(bits=5)), 4) == 0
