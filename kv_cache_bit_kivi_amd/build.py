@@ -30,7 +30,7 @@ COMMON = [
 EXTRA = {
     "quantize.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["kivi_api.hip", "quantize.hip", "decode_generic.hip"]
+SOURCES = ["kivi_api.hip", "quantize.hip", "decode_generic.hip", "decode_mfma.hip"]
 
 
 def _compile(src: str) -> str:

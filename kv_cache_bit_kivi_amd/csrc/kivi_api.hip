@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cstdlib>
 
 #include "kivi_internal.h"
 
@@ -84,12 +85,38 @@ int max_auto_splits(const kivi_shape& s) {
   return units >= 2048 ? 1 : (2048 + units - 1) / units;
 }
 
-int auto_splits(const kivi_shape& s, int L, int cus) {
+bool use_mfma(const kivi_shape& s) {
+  return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio);
+}
+
+// waves per block of the matrix-core decode kernel
+int mfma_waves() {
+  static const int nw = [] {
+    const char* e = getenv("KIVI_DECODE_WAVES");   // tuning override: 4, 8 or 16
+    int v = e ? atoi(e) : 8;
+    return (v == 8 || v == 16) ? v : 4;
+  }();
+  return nw;
+}
+
+int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
   const int units = s.batch * s.num_kv_heads;
-  // aim for about two blocks per compute unit, at least 256 tokens a split
-  int want = (2 * cus + units - 1) / units;
-  int by_len = (L + 255) / 256;
-  int S = want < by_len ? want : by_len;
+  const int L = tq + tr;
+  int S;
+  if (use_mfma(s)) {
+    // about 16 waves per compute unit in total, and at least two 64-token
+    // tiles per wave
+    const int nw = kivi::decode_mfma_block_waves(s.gqa_ratio, mfma_waves());
+    const int target = 16 * cus;
+    S = (target + units * nw - 1) / (units * nw);
+    const int by_work = ((tq + 63) / 64) / (2 * nw);
+    if (S > by_work) S = by_work;
+  } else {
+    // about two blocks per compute unit, at least 256 tokens a split
+    const int want = (2 * cus + units - 1) / units;
+    const int by_len = (L + 255) / 256;
+    S = want < by_len ? want : by_len;
+  }
   if (S < 1) S = 1;
   const int cap = max_auto_splits(s);
   return S > cap ? cap : S;
@@ -221,7 +248,7 @@ int kivi_decode_auto_splits(const kivi_cache* c) {
   if (rc) return -rc;
   const int cus = device_cu_count();
   if (cus < 0) return cus;
-  return auto_splits(c->shape, c->tq + c->tr, cus);
+  return auto_splits(c->shape, c->tq, c->tr, cus);
 }
 
 size_t kivi_decode_workspace_bytes(const kivi_shape* s, int32_t num_splits) {
@@ -250,7 +277,7 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, float softmax_scale
   if (S == 0) {
     const int cus = device_cu_count();
     if (cus < 0) return KIVI_EHIP;
-    S = auto_splits(s, L, cus);
+    S = auto_splits(s, c->tq, c->tr, cus);
     if (S > 1) {
       if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
       if (!workspace) return KIVI_EINVAL;
@@ -282,7 +309,8 @@ int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, float softmax_scale
   a.S = S;
   a.scale = softmax_scale;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = kivi::launch_decode_generic(a, st);
+  hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
+                             : kivi::launch_decode_generic(a, st);
   if (e != hipSuccess) return KIVI_EHIP;
   if (S > 1) {
     e = kivi::launch_combine(a, st);

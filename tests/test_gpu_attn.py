@@ -44,6 +44,11 @@ SHAPES = [
     (1, 2, 4, 256, 4, 128, 128, 768, 20),
     (1, 2, 1, 128, 2, 32, 128, 0, 97),        # residual only
     (1, 1, 16, 128, 2, 32, 128, 160, 3),
+    (1, 2, 8, 128, 2, 32, 128, 512, 40),       # matrix-core path, r = 8
+    (2, 1, 3, 128, 4, 32, 128, 640, 128),      # r = 3 (padded head rows)
+    (1, 2, 2, 128, 2, 32, 32, 1984, 32),
+    (1, 1, 1, 128, 2, 32, 128, 8192, 5),       # several chunks per wave
+    (1, 1, 4, 128, 4, 32, 128, 4096, 128),
 ]
 
 
