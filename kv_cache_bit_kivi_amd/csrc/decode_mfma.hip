@@ -29,6 +29,8 @@
 // splits write (max, sum, o) partials for the combine kernel.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -253,154 +255,207 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  for (int c0 = t_begin; c0 < t_end; c0 += CT) {
-    const int nt = min(CT, t_end - c0);
+  // Everything one 64-token tile needs from memory, held in registers so the
+  // next tile's loads are in flight while the current tile is computed.
+  using KCode = typename std::conditional<BITS == 2, uint2, uint4>::type;
+  using VCode = typename std::conditional<BITS == 2, uint32_t, uint2>::type;
+  struct KTile {
+    KCode c[4];        // codes of 4 x 16 tokens, 32 channels of this lane group
+    float2 s[2], z[2]; // key scale / zero of channels 2*lane, 2*lane+1, 2 groups
+  };
+  struct VTile {
+    VCode c[8];        // codes of 16 tokens of channel 16*nb + n16, nb = 0..7
+    float4 s, z;       // value scale / zero of token lane, 4 groups
+  };
+  auto load_k = [&](int tile, KTile& kt) {
+    const int tok0 = tile * 64;
+    const bool half_tile = tok0 + 64 > tq;
+#pragma unroll
+    for (int mb = 0; mb < 4; mb++) {
+      if (mb < 2 || !half_tile) {
+        const size_t row = (size_t)tok0 + 16 * mb + n16;
+        kt.c[mb] = *reinterpret_cast<const KCode*>(kc + row * W + (BITS == 2 ? 2 : 4) * kg);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; kb++) {
+      if (kb == 0 || !half_tile) {
+        const size_t g = (size_t)(tok0 >> 5) + kb;
+        kt.s[kb] = *reinterpret_cast<const float2*>(ksc + g * kD + 2 * lane);
+        kt.z[kb] = *reinterpret_cast<const float2*>(kzr + g * kD + 2 * lane);
+      }
+    }
+  };
+  auto load_v = [&](int tile, VTile& vt) {
+    const uint32_t* base = vc + (size_t)tile * kD * WPC;
+#pragma unroll
+    for (int nb = 0; nb < 8; nb++)
+      vt.c[nb] = *reinterpret_cast<const VCode*>(base + (16 * nb + n16) * WPC +
+                                                 (BITS == 2 ? 1 : 2) * kg);
+    const size_t t = (size_t)tile * 64 + lane;
+    vt.s = *reinterpret_cast<const float4*>(vsc + t * kNG);
+    vt.z = *reinterpret_cast<const float4*>(vzr + t * kNG);
+  };
 
-    // ---------------- key pass: scores of the chunk's tiles -> LDS
-    for (int i = 0; i < nt; i++) {
-      const int tile = c0 + i;
-      const int tok0 = tile * 64;
-      const bool half_tile = tok0 + 64 > tq;   // only the first 32 tokens exist
+  // scores of one tile -> lds_sc[h][i*64 + token]
+  auto do_k = [&](int tile, int i, const KTile& kt) {
+    const int tok0 = tile * 64;
+    const bool half_tile = tok0 + 64 > tq;   // only the first 32 tokens exist
 #pragma unroll
-      for (int kb = 0; kb < 2; kb++) {
-        if (kb == 1 && half_tile) {
+    for (int kb = 0; kb < 2; kb++) {
+      if (kb == 1 && half_tile) {
 #pragma unroll
-          for (int h = 0; h < RR; h++)
-            if (h < r && lane < 32) lds_sc[h * CH + i * 64 + 32 + lane] = -INFINITY;
-          continue;
-        }
-        const int g = (tok0 >> 5) + kb;           // key group (32 tokens)
-        const float2 s2 = *reinterpret_cast<const float2*>(ksc + (size_t)g * kD + 2 * lane);
-        const float2 z2 = *reinterpret_cast<const float2*>(kzr + (size_t)g * kD + 2 * lane);
-        float qa[RR], qb[RR], bpart[RR], beta[RR];
-        float qmax = 0.f;
+        for (int h = 0; h < RR; h++)
+          if (h < r && lane < 32) lds_sc[h * CH + i * 64 + 32 + lane] = -INFINITY;
+        continue;
+      }
+      const float2 s2 = kt.s[kb], z2 = kt.z[kb];
+      float qa[RR], qb[RR], bpart[RR], beta[RR];
+      float qmax = 0.f;
+#pragma unroll
+      for (int h = 0; h < RR; h++) {
+        qa[h] = sq0[h] * s2.x;
+        qb[h] = sq1[h] * s2.y;
+        bpart[h] = sq0[h] * z2.x + sq1[h] * z2.y;
+        qmax = fmaxf(qmax, fmaxf(fabsf(qa[h]), fabsf(qb[h])));
+      }
+      // power-of-two prescale keeps the fp16 hi part finite for any input
+      qmax = wave_max(qmax);
+      const int ex = max(0, (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xFF) - 127 - 13);
+      const float down = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
+      const float up = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
+      {
+        int m0, s0, m1, s1;
+        const int cp = (2 * lane) & 31;
+        k_pos<BITS>(cp, m0, s0);
+        k_pos<BITS>(cp + 1, m1, s1);
+        const int kgc = (2 * lane) >> 5;
 #pragma unroll
         for (int h = 0; h < RR; h++) {
-          qa[h] = sq0[h] * s2.x;
-          qb[h] = sq1[h] * s2.y;
-          bpart[h] = sq0[h] * z2.x + sq1[h] * z2.y;
-          qmax = fmaxf(qmax, fmaxf(fabsf(qa[h]), fabsf(qb[h])));
-        }
-        // power-of-two prescale keeps the fp16 hi part finite for any input
-        qmax = wave_max(qmax);
-        const int ex = max(0, (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xFF) - 127 - 13);
-        const float down = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
-        const float up = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
-        {
-          int m0, s0, m1, s1;
-          const int cp = (2 * lane) & 31;
-          k_pos<BITS>(cp, m0, s0);
-          k_pos<BITS>(cp + 1, m1, s1);
-          const int kgc = (2 * lane) >> 5;
-#pragma unroll
-          for (int h = 0; h < RR; h++) {
-            if (h < r) {
-              const float x0 = qa[h] * down, x1 = qb[h] * down;
-              const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-              const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-              lds_a[((m0 * ROWS + 2 * h) * 4 + kgc) * 8 + s0] = h0;
-              lds_a[((m0 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s0] = l0;
-              lds_a[((m1 * ROWS + 2 * h) * 4 + kgc) * 8 + s1] = h1;
-              lds_a[((m1 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s1] = l1;
-            }
+          if (h < r) {
+            const float x0 = qa[h] * down, x1 = qb[h] * down;
+            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+            const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
+            lds_a[((m0 * ROWS + 2 * h) * 4 + kgc) * 8 + s0] = h0;
+            lds_a[((m0 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s0] = l0;
+            lds_a[((m1 * ROWS + 2 * h) * 4 + kgc) * 8 + s1] = h1;
+            lds_a[((m1 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s1] = l1;
           }
         }
+      }
 #pragma unroll
-        for (int h = 0; h < RR; h++) beta[h] = h < r ? wave_sum(bpart[h]) : 0.f;
-        __builtin_amdgcn_wave_barrier();
-        half8 af[4];
+      for (int h = 0; h < RR; h++) beta[h] = h < r ? wave_sum(bpart[h]) : 0.f;
+      __builtin_amdgcn_wave_barrier();
+      half8 af[4];
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-          af[m] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-          if (a_row_ok)
-            af[m] = *reinterpret_cast<const half8*>(lds_a + ((m * ROWS + n16) * 4 + kg) * 8);
-        }
-        __builtin_amdgcn_wave_barrier();
-        const float b0 = pick<RR>(beta, kg, 0), b1 = pick<RR>(beta, kg, 1);
+      for (int m = 0; m < 4; m++) {
+        af[m] = half8{0, 0, 0, 0, 0, 0, 0, 0};
+        if (a_row_ok)
+          af[m] = *reinterpret_cast<const half8*>(lds_a + ((m * ROWS + n16) * 4 + kg) * 8);
+      }
+      __builtin_amdgcn_wave_barrier();
+      const float b0 = pick<RR>(beta, kg, 0), b1 = pick<RR>(beta, kg, 1);
 #pragma unroll
-        for (int mb2 = 0; mb2 < 2; mb2++) {
-          const int mb = 2 * kb + mb2;
-          const size_t row = (size_t)tok0 + 16 * mb + n16;
-          float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-          if (BITS == 2) {
-            const uint2 w = *reinterpret_cast<const uint2*>(kc + row * W + 2 * kg);
+      for (int mb2 = 0; mb2 < 2; mb2++) {
+        const int mb = 2 * kb + mb2;
+        float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+        if constexpr (BITS == 2) {
+          const uint2 w = kt.c[mb];
 #pragma unroll
-            for (int wp = 0; wp < 2; wp++) {
-              const uint32_t x = wp ? w.y : w.x;
-              acc = mfma(af[2 * wp], cvt_nib2(x & 0x33333333u), acc);
-              acc = mfma(af[2 * wp + 1], cvt_nib2((x >> 2) & 0x33333333u), acc);
-            }
-          } else {
-            const uint4 w = *reinterpret_cast<const uint4*>(kc + row * W + 4 * kg);
-            acc = mfma(af[0], cvt_word4(w.x), acc);
-            acc = mfma(af[1], cvt_word4(w.y), acc);
-            acc = mfma(af[2], cvt_word4(w.z), acc);
-            acc = mfma(af[3], cvt_word4(w.w), acc);
+          for (int wp = 0; wp < 2; wp++) {
+            const uint32_t x = wp ? w.y : w.x;
+            acc = mfma(af[2 * wp], cvt_nib2(x & 0x33333333u), acc);
+            acc = mfma(af[2 * wp + 1], cvt_nib2((x >> 2) & 0x33333333u), acc);
           }
-          const int k = i * 64 + 16 * mb + n16;
-          const int h0 = 2 * kg, h1 = 2 * kg + 1;
-          if (h0 < r) lds_sc[h0 * CH + k] = (acc[0] + acc[1]) * up + b0;
-          if (h1 < r) lds_sc[h1 * CH + k] = (acc[2] + acc[3]) * up + b1;
+        } else {
+          const uint4 w = kt.c[mb];
+          acc = mfma(af[0], cvt_word4(w.x), acc);
+          acc = mfma(af[1], cvt_word4(w.y), acc);
+          acc = mfma(af[2], cvt_word4(w.z), acc);
+          acc = mfma(af[3], cvt_word4(w.w), acc);
+        }
+        const int k = i * 64 + 16 * mb + n16;
+        const int h0 = 2 * kg, h1 = 2 * kg + 1;
+        if (h0 < r) lds_sc[h0 * CH + k] = (acc[0] + acc[1]) * up + b0;
+        if (h1 < r) lds_sc[h1 * CH + k] = (acc[2] + acc[3]) * up + b1;
+      }
+    }
+  };
+
+  // P.V of one tile into the cv accumulators
+  auto do_v = [&](int tile, int i, const VTile& vt) {
+    const int t = tile * 64 + lane;              // this lane's token
+    const bool valid = t < tq;
+    const float sj[4] = {vt.s.x, vt.s.y, vt.s.z, vt.s.w};
+    const float zj[4] = {valid ? vt.z.x : 0.f, valid ? vt.z.y : 0.f, valid ? vt.z.z : 0.f,
+                         valid ? vt.z.w : 0.f};
+    int mt, st;
+    v_pos<BITS>(lane & 15, mt, st);
+    const int kgt = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < RR; h++) {
+      if (h < r) {
+        const float p = valid ? fast_exp2(lds_sc[h * CH + i * 64 + lane] - m_run[h]) : 0.f;
+        l_acc[h] += p;
+#pragma unroll
+        for (int j = 0; j < kNG; j++) {
+          gam[h][j] += p * zj[j];
+          const float x = valid ? p * sj[j] : 0.f;
+          const _Float16 hi = (_Float16)x;
+          const _Float16 lo = (_Float16)(x - (float)hi);
+          lds_a[((((j * 2 + mt) * ROWS) + 2 * h) * 4 + kgt) * 8 + st] = hi;
+          lds_a[((((j * 2 + mt) * ROWS) + 2 * h + 1) * 4 + kgt) * 8 + st] = lo;
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    rescale(nt * 64);
+#pragma unroll
+    for (int j = 0; j < kNG; j++) {
+      half8 av0 = half8{0, 0, 0, 0, 0, 0, 0, 0}, av1 = av0;
+      if (a_row_ok) {
+        av0 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 0) * ROWS + n16) * 4 + kg) * 8);
+        av1 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 1) * ROWS + n16) * 4 + kg) * 8);
+      }
+#pragma unroll
+      for (int nbj = 0; nbj < 2; nbj++) {
+        const int nb = 2 * j + nbj;
+        if constexpr (BITS == 2) {
+          const uint32_t x = vt.c[nb];
+          cv[nb] = mfma(av0, cvt_nib2(x & 0x33333333u), cv[nb]);
+          cv[nb] = mfma(av1, cvt_nib2((x >> 2) & 0x33333333u), cv[nb]);
+        } else {
+          const uint2 x = vt.c[nb];
+          cv[nb] = mfma(av0, cvt_word4(x.x), cv[nb]);
+          cv[nb] = mfma(av1, cvt_word4(x.y), cv[nb]);
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
 
-    // ---------------- value pass
+  // software pipeline: the loads of step n+1 are issued before step n runs
+  KTile kt;
+  VTile vt;
+  if (t_begin < t_end) load_k(t_begin, kt);
+  for (int c0 = t_begin; c0 < t_end; c0 += CT) {
+    const int nt = min(CT, t_end - c0);
     for (int i = 0; i < nt; i++) {
-      const int tile = c0 + i;
-      const int t = tile * 64 + lane;              // this lane's token
-      const bool valid = t < tq;
-      const float4 s4 = *reinterpret_cast<const float4*>(vsc + (size_t)t * kNG);
-      const float4 z4 = *reinterpret_cast<const float4*>(vzr + (size_t)t * kNG);
-      const float sj[4] = {s4.x, s4.y, s4.z, s4.w};
-      const float zj[4] = {valid ? z4.x : 0.f, valid ? z4.y : 0.f, valid ? z4.z : 0.f,
-                           valid ? z4.w : 0.f};
-      int mt, st;
-      v_pos<BITS>(lane & 15, mt, st);
-      const int kgt = lane >> 4;
-#pragma unroll
-      for (int h = 0; h < RR; h++) {
-        if (h < r) {
-          const float p = valid ? fast_exp2(lds_sc[h * CH + i * 64 + lane] - m_run[h]) : 0.f;
-          l_acc[h] += p;
-#pragma unroll
-          for (int j = 0; j < kNG; j++) {
-            gam[h][j] += p * zj[j];
-            const float x = valid ? p * sj[j] : 0.f;
-            const _Float16 hi = (_Float16)x;
-            const _Float16 lo = (_Float16)(x - (float)hi);
-            lds_a[((((j * 2 + mt) * ROWS) + 2 * h) * 4 + kgt) * 8 + st] = hi;
-            lds_a[((((j * 2 + mt) * ROWS) + 2 * h + 1) * 4 + kgt) * 8 + st] = lo;
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      const uint32_t* vt = vc + (size_t)tile * kD * WPC;
-#pragma unroll
-      for (int j = 0; j < kNG; j++) {
-        half8 av0 = half8{0, 0, 0, 0, 0, 0, 0, 0}, av1 = av0;
-        if (a_row_ok) {
-          av0 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 0) * ROWS + n16) * 4 + kg) * 8);
-          av1 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 1) * ROWS + n16) * 4 + kg) * 8);
-        }
-#pragma unroll
-        for (int nbj = 0; nbj < 2; nbj++) {
-          const int nb = 2 * j + nbj;
-          const uint32_t* cw = vt + (size_t)(16 * nb + n16) * WPC;
-          if (BITS == 2) {
-            const uint32_t x = cw[kg];
-            cv[nb] = mfma(av0, cvt_nib2(x & 0x33333333u), cv[nb]);
-            cv[nb] = mfma(av1, cvt_nib2((x >> 2) & 0x33333333u), cv[nb]);
-          } else {
-            const uint2 x = *reinterpret_cast<const uint2*>(cw + 2 * kg);
-            cv[nb] = mfma(av0, cvt_word4(x.x), cv[nb]);
-            cv[nb] = mfma(av1, cvt_word4(x.y), cv[nb]);
-          }
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
+      const KTile cur = kt;
+      if (i + 1 < nt)
+        load_k(c0 + i + 1, kt);
+      else
+        load_v(c0, vt);
+      do_k(c0 + i, i, cur);
+    }
+    __builtin_amdgcn_wave_barrier();
+    rescale(nt * 64);
+    for (int i = 0; i < nt; i++) {
+      const VTile cur = vt;
+      if (i + 1 < nt)
+        load_v(c0 + i + 1, vt);
+      else if (c0 + nt < t_end)
+        load_k(c0 + nt, kt);
+      do_v(c0 + i, i, cur);
     }
   }
 
