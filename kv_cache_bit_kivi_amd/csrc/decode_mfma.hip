@@ -1,5 +1,5 @@
 // Decode attention on the mixed cache with matrix-core (MFMA) contractions,
-// for head_dim 128, group 32, 2- or 4-bit codes and GQA ratio r <= 8.
+// for head_dim 128, group 32, 2- or 4-bit codes and GQA ratio r in {1,2,4,8}.
 //
 // Method (study.space summary of "KIVI: A Tuning-Free Asymmetric 2bit
 // Quantization for KV Cache"): the scores of the quantized grouped part are a
@@ -12,23 +12,33 @@
 //                                       Gamma = sum_t p_t * z_t
 // (sc = softmax scale * log2(e): scores live in the log2 domain, p = 2^(s-m)).
 //
-// Both contractions run on v_mfma_f32_16x16x32_f16 with the dense operand
-// B = the codes, converted exactly to fp16 (2-bit nibbles via the e2m1
-// convert with scale 2, 4-bit nibbles via the e4m3 convert with scale 2^9),
-// and the operand A = the per-group factors q' (or p') split into fp16 hi +
-// lo rows so the products keep ~22 significant bits:
-//   keys:   A rows (head, hi|lo) x K=32 channels, B = 32 channels x 16 tokens
-//   values: A rows (head, hi|lo) x K=32 tokens,   B = 32 tokens x 16 channels
-// The K=32 slots a lane supplies map to code positions in the order the
-// converts produce them (see k_pos / v_pos); A is written to LDS in that order.
+// Both contractions run on v_mfma_f32_16x16x32_f16.  Operand B is the codes,
+// converted exactly to fp16 (2-bit codes via the e2m1 convert with scale 2,
+// 4-bit codes via the e4m3 convert with scale 2^9).  Operand A is the factor
+// q' (or p'), split into fp16 hi + lo rows (round toward zero, then the
+// remainder) so the products keep about 20 significant bits:
+//   keys:   A = rows (head, hi|lo) x 32 channels, B = 32 channels x 16 tokens
+//   values: A = rows (head, hi|lo) x 32 tokens,   B = 32 tokens x 16 channels
+// The 8 K-slots a lane supplies map to code positions in the order the
+// converts produce them (k_pos / v_pos); A is written to LDS in that order.
+// The query is normalised per wave by a power of two so that |q'| < 2^16 and
+// the fp16 hi part never overflows; scores are scaled back after the MFMA.
+// Residual keys (fp16) feed the MFMA directly; residual values use the VALU.
 //
-// Work: one block of NW waves per (b*Hkv + h, split); every wave owns a
-// contiguous run of 64-token value tiles plus a slice of the residual, walks
-// it in chunks (scores of the chunk to LDS, chunk max, rescale, then P.V), and
-// the block merges its waves in LDS.  One split writes fp16 output; more
-// splits write (max, sum, o) partials for the combine kernel.
+// Work: one block of NW waves per (b*Hkv + h, split).  Each wave owns a
+// contiguous run of 64-token value tiles plus a slice of the residual.  Per
+// tile it computes the key scores into LDS, updates the running maximum
+// (online softmax; accumulators are rescaled only when the maximum grows) and
+// accumulates P.V.  Codes and metadata arrive through raw buffer loads, 16
+// bytes per lane, one or two tiles ahead of the compute; absent tiles and
+// tokens are loaded out of range (zeros, no memory access) instead of being
+// branched around, so the completion counter never forces a full drain.
+// Codes are staged through LDS and re-read in the MFMA operand layout.  The
+// block merges its waves in LDS; one split writes fp16 output, more splits
+// write (max, sum, o) partials for the combine kernel.
 #include <math.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "kivi_internal.h"
@@ -38,6 +48,7 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __fp16 hrtz2 __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 
 constexpr int kD = 128;
@@ -101,14 +112,50 @@ __device__ __forceinline__ half8 cvt_word4(uint32_t w) {
 __device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+// (hi, lo) fp16 pairs of two binary32 values: hi = x rounded toward zero,
+// lo = the remainder rounded toward zero; hi + lo = x within 2^-20 |x|
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const hrtz2 h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
+  const hrtz2 l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h.x, x1 - (float)h.y);
+  hi = __builtin_bit_cast(uint32_t, h);
+  lo = __builtin_bit_cast(uint32_t, l);
+}
+
+// Raw buffer loads: a resource covers one plane; an offset at or past its end
+// returns zeros and touches no memory.  Absent tiles and tokens are loaded at
+// kOut instead of being branched around, so every wave issues one fixed load
+// sequence and the in-order completion counter stays exact.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOut = 0x80000000u;   // past every plane (planes stay < 2^31 bytes)
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return uint4{v.x, v.y, v.z, v.w};
+}
+// (bit-cast the whole vector: clang bit-casts an ext-vector element access
+// from the vector's first element)
+__device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t off) {
+  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  return float4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return uint2{v.x, v.y};
+}
 
 // slot of position q (0..7) inside a 4-bit word's half8
 __device__ __forceinline__ int slot4(int q) { return (q & 1) ? 4 + (q >> 1) : (q >> 1); }
 
-// Key side: channel c' (0..31 inside the lane group's 32 channels) -> (mfma m, slot s)
+// Key side: channel c' (0..31 inside a lane group's 32 channels) -> (mfma m, slot s)
 template <int BITS>
 __device__ __forceinline__ void k_pos(int cp, int& m, int& s) {
-  if (BITS == 2) {  // word (cp/16), even/odd nibble plane, nibble index
+  if (BITS == 2) {  // word cp/16, even/odd nibble plane, nibble index
     m = 2 * (cp >> 4) + (cp & 1);
     s = (cp & 15) >> 1;
   } else {          // word cp/8
@@ -116,7 +163,7 @@ __device__ __forceinline__ void k_pos(int cp, int& m, int& s) {
     s = slot4(cp & 7);
   }
 }
-// Value side: token position p (0..15 inside the lane group's 16 tokens)
+// Value side: token position p (0..15 inside a lane group's 16 tokens)
 template <int BITS>
 __device__ __forceinline__ void v_pos(int p, int& m, int& s) {
   if (BITS == 2) {
@@ -129,58 +176,87 @@ __device__ __forceinline__ void v_pos(int p, int& m, int& s) {
 }
 
 // value arr[2*g + hh] for lane group g without dynamic register indexing
-template <int RR>
-__device__ __forceinline__ float pick(const float (&arr)[RR], int g, int hh) {
-  float v = arr[hh < RR ? hh : 0];
+template <int R>
+__device__ __forceinline__ float pick(const float (&arr)[R], int g, int hh) {
+  float v = arr[hh < R ? hh : 0];
 #pragma unroll
-  for (int i = 1; i < (RR + 1) / 2; i++)
-    if (g == i && 2 * i + hh < RR) v = arr[2 * i + hh];
+  for (int i = 1; i < (R + 1) / 2; i++)
+    if (g == i && 2 * i + hh < R) v = arr[2 * i + hh];
   return v;
 }
 
-template <int RR>
+template <int BITS, int R>
 struct Cfg {
-  static constexpr int ROWS = 2 * RR;                       // A rows: (head, hi|lo)
-  static constexpr int CH = RR <= 2 ? 512 : (RR == 4 ? 256 : 128);   // tokens / chunk
-  static constexpr int CT = CH / 64;                        // tiles / chunk
-  static constexpr int A_HALVES = kNG * 2 * ROWS * 32;      // value A (key A is smaller)
-  static constexpr int LDS_A = A_HALVES / 2;                // floats
-  static constexpr int LDS_SC = RR * CH;
-  static constexpr int LDS_O = RR * kD + 2 * RR;
-  static constexpr int LDS_WAVE = LDS_A + LDS_SC + LDS_O;   // floats per wave
+  static constexpr int ROWS = 2 * R;                    // A rows: (head, hi|lo)
+  static constexpr int CH = 64;                         // score slots: one tile
+  static constexpr int KC_BYTES = 64 * kD * BITS / 8;   // key codes of one tile
+  static constexpr int VC_BYTES = 64 * kD * BITS / 8;   // value codes of one tile
+  static constexpr int A_BYTES = kNG * 2 * ROWS * 64;   // value A (two key groups: same)
+  static constexpr int RES_BYTES = 4 * ROWS * 64;       // residual key A
+  static constexpr int SC_BYTES = R * CH * 4;
+  static constexpr int O_BYTES = ((R * kD + 2 * R) * 4 + 15) / 16 * 16;  // keeps stg 16-aligned
+  static constexpr int DUMMY_BYTES = 64;                // sink for writes of absent heads
+  static constexpr int STG_BYTES = KC_BYTES + VC_BYTES; // staged codes of one tile
+  static constexpr int WAVE_BYTES =
+      A_BYTES + RES_BYTES + SC_BYTES + O_BYTES + DUMMY_BYTES + STG_BYTES;
+  static constexpr int ZERO_BYTES = ROWS < 16 ? A_BYTES : 0;  // all-zero rows, per block
+  static_assert(WAVE_BYTES % 16 == 0 && A_BYTES % 16 == 0, "b128 LDS accesses need 16-byte alignment");
 };
 
-template <int BITS, int RR, int NW>
-__global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
-  using C = Cfg<RR>;
-  constexpr int ROWS = C::ROWS, CH = C::CH, CT = C::CT;
+// occupancy target: exactly two waves per SIMD (one for 8 heads), so the
+// register allocator keeps the in-flight tile in registers instead of spilling
+template <int BITS, int R>
+constexpr int waves_per_eu() { return R >= 8 ? 1 : 2; }
+
+// tiles of loads in flight per wave: two where the register budget of the
+// occupancy target holds a second set, else one
+template <int BITS, int R>
+constexpr int prefetch_depth() {
+  return (R >= 8 || (BITS == 2 && R <= 2) || (BITS == 4 && R == 1)) ? 2 : 1;
+}
+
+template <int BITS, int R, int NW>
+__global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
+decode_mfma_kernel(DecodeArgs a) {
+  using C = Cfg<BITS, R>;
+  constexpr int ROWS = C::ROWS, CH = C::CH;
   constexpr int E = 32 / BITS;
   constexpr int W = kD / E;        // words per key row
   constexpr int WPC = 64 / E;      // words per channel per value tile
-  __shared__ __align__(16) float smem[NW * C::LDS_WAVE];
+  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
-  const int S = a.S, H = a.H, r = a.r;
+  const int S = a.S, H = a.H;
   const int u = blockIdx.x / S, split = blockIdx.x % S;
   const int b = u / H;
   const int tq = a.tq, tr = a.tr;
 
-  float* my = smem + wv * C::LDS_WAVE;
-  _Float16* lds_a = reinterpret_cast<_Float16*>(my);
-  float* lds_sc = my + C::LDS_A;
-  float* lds_o = lds_sc + C::LDS_SC;      // [RR][D], then m[RR], l[RR]
+  char* zero = smem;
+  char* my = smem + C::ZERO_BYTES + wv * C::WAVE_BYTES;
+  char* lds_a = my;                                     // key / value A tiles
+  char* lds_res = my + C::A_BYTES;                      // residual key A tile
+  float* lds_sc = reinterpret_cast<float*>(lds_res + C::RES_BYTES);   // [R][CH]
+  float* lds_o = reinterpret_cast<float*>(lds_res + C::RES_BYTES + C::SC_BYTES);
+  float* lds_dummy = reinterpret_cast<float*>(reinterpret_cast<char*>(lds_o) + C::O_BYTES);
+  char* stg = reinterpret_cast<char*>(lds_dummy) + C::DUMMY_BYTES;   // staged tile codes
+  for (int i = threadIdx.x; i < C::ZERO_BYTES / 16; i += NW * 64)
+    reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
+  __syncthreads();
 
-  const size_t plane = (size_t)u;
-  const uint32_t* kc = a.k_codes + plane * (size_t)a.cap * W;
-  const float* ksc = a.k_scale + plane * (size_t)(a.cap / kG) * kD;
-  const float* kzr = a.k_zero + plane * (size_t)(a.cap / kG) * kD;
-  const uint32_t* vc = a.v_codes + plane * (size_t)a.cap * (kD / E);
-  const float* vsc = a.v_scale + plane * (size_t)a.cap * kNG;
-  const float* vzr = a.v_zero + plane * (size_t)a.cap * kNG;
-  const uint16_t* kr = a.k_res + plane * (size_t)a.R * kD;
-  const uint16_t* vr = a.v_res + plane * (size_t)a.R * kD;
-  const size_t qrow0 = (size_t)b * H * r + (size_t)(u % H) * r;
+  // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
+  const size_t plane = (size_t)u, cap = (size_t)a.cap;
+  const rsrc_t r_kc = make_rsrc(a.k_codes + plane * cap * W, (uint32_t)(cap * W * 4));
+  const rsrc_t r_ks = make_rsrc(a.k_scale + plane * (cap / kG) * kD, (uint32_t)(cap / kG * kD * 4));
+  const rsrc_t r_kz = make_rsrc(a.k_zero + plane * (cap / kG) * kD, (uint32_t)(cap / kG * kD * 4));
+  const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD / E), (uint32_t)(cap * (kD / E) * 4));
+  const rsrc_t r_vs = make_rsrc(a.v_scale + plane * cap * kNG, (uint32_t)(cap * kNG * 4));
+  const rsrc_t r_vz = make_rsrc(a.v_zero + plane * cap * kNG, (uint32_t)(cap * kNG * 4));
+  const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
+  const rsrc_t r_vr = make_rsrc(a.v_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
+  const size_t qrow0 = (size_t)b * H * R + (size_t)(u % H) * R;
+  const rsrc_t r_q = make_rsrc(a.q + qrow0 * kD, (uint32_t)(R * kD * 2));
 
   // this wave's share: value tiles [t_begin, t_end) and residual [r_begin, r_end)
   const int NWT = S * NW, gw = split * NW + wv;
@@ -188,63 +264,208 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   const int t_begin = (int)((int64_t)gw * nT / NWT), t_end = (int)((int64_t)(gw + 1) * nT / NWT);
   const int r_begin = (int)((int64_t)gw * tr / NWT), r_end = (int)((int64_t)(gw + 1) * tr / NWT);
 
-  // scaled query (log2 domain) for channels 2*lane, 2*lane+1
-  const float qs = a.scale * kLog2e;
-  float sq0[RR], sq1[RR];
+  // Lane roles.  Every global load is 16 bytes per lane over 1 KB contiguous.
+  //  key factors: lane -> key group kgrp = lane/32 of the tile and channels
+  //    cq..cq+3 (cq = 4*(lane%32)), i.e. exactly its own 16-byte scale / zero
+  //    load; channels cq, cq+2 (and cq+1, cq+3) sit in adjacent A slots, so
+  //    hi/lo pairs are written as 32-bit words;
+  //  value factors: lane -> token lane of the tile, its own 16-byte scale /
+  //    zero load (4 value groups);
+  //  codes: staged through LDS and re-read in the MFMA operand layout.
+  const int kgrp = lane >> 5, cq = 4 * (lane & 31);
+  uint32_t kwr[2];      // A offsets of channel pairs (cq, cq+2), (cq+1, cq+3)
 #pragma unroll
-  for (int h = 0; h < RR; h++) {
-    sq0[h] = 0.f;
-    sq1[h] = 0.f;
-    if (h < r) {
-      const uint32_t qq = *reinterpret_cast<const uint32_t*>(a.q + (qrow0 + h) * kD + 2 * lane);
-      sq0[h] = qs * h2f((uint16_t)(qq & 0xFFFFu));
-      sq1[h] = qs * h2f((uint16_t)(qq >> 16));
-    }
+  for (int e = 0; e < 2; e++) {
+    const int c = cq + e;
+    int m, s;
+    k_pos<BITS>(c & 31, m, s);
+    kwr[e] = (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
   }
+  int vm, vs0;
+  v_pos<BITS>(lane & 15, vm, vs0);
+  const uint32_t vwr = (uint32_t)(((vm * ROWS) * 4 + kg) * 16 + 2 * vs0);
+  // A read base: lanes of absent rows read the all-zero region instead
+  const bool row_ok = n16 < ROWS;
+  const char* a_rd = row_ok ? lds_a + (n16 * 4 + kg) * 16 : zero + kg * 16;
+  const char* res_rd = row_ok ? lds_res + (n16 * 4 + kg) * 16 : zero + kg * 16;
 
-  float m_run[RR], l_acc[RR], l_res[RR], ores0[RR], ores1[RR];
-  float gam[RR][kNG];
+  // Issue order matters: vector-memory loads complete in order, so the query
+  // goes first, then the first residual batch, then the tile prefetch; waiting
+  // for an earlier group never waits for a later one.
+  uint2 q4r[R];
 #pragma unroll
-  for (int h = 0; h < RR; h++) {
+  for (int h = 0; h < R; h++) q4r[h] = ld8(r_q, (uint32_t)((h * kD + cq) * 2));
+  __builtin_amdgcn_sched_barrier(0);
+
+  // registers of a tile in flight: codes (2-bit uses x0..x3: key codes, then
+  // value codes; 4-bit x0..x7), key scale / zero of key group kgrp, channels
+  // cq..cq+3, value scale / zero of the token lane
+  const uint32_t l16 = (uint32_t)lane * 16;
+  // codes / metadata of tile `tile` of this wave, or zeros (no memory access)
+  // when it is past the wave's last tile.  Codes are reloaded as soon as they
+  // are staged, metadata once the tile's compute has consumed them, so that
+  // no register holds two generations at once (that would need copies, and a
+  // copy waits for its load).
+  auto load_codes = [&](int tile, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& x4,
+                        uint4& x5, uint4& x6, uint4& x7) __attribute__((always_inline)) {
+    const uint32_t co = tile < t_end ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
+    if constexpr (BITS == 2) {
+      x0 = ld16(r_kc, co);
+      x1 = ld16(r_kc, co + 1024);
+      x2 = ld16(r_vc, co);
+      x3 = ld16(r_vc, co + 1024);
+    } else {
+      x0 = ld16(r_kc, co);
+      x1 = ld16(r_kc, co + 1024);
+      x2 = ld16(r_kc, co + 2048);
+      x3 = ld16(r_kc, co + 3072);
+      x4 = ld16(r_vc, co);
+      x5 = ld16(r_vc, co + 1024);
+      x6 = ld16(r_vc, co + 2048);
+      x7 = ld16(r_vc, co + 3072);
+    }
+  };
+  auto load_meta = [&](int tile, float4& ks, float4& kz, float4& vs, float4& vz)
+      __attribute__((always_inline)) {
+    // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 1 KB each
+    const uint32_t mo = tile < t_end ? (uint32_t)tile * 1024 + l16 : kOut;
+    ks = ld16f(r_ks, mo);
+    kz = ld16f(r_kz, mo);
+    vs = ld16f(r_vs, mo);
+    vz = ld16f(r_vz, mo);
+  };
+  auto stage = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
+                   const uint4& x4, const uint4& x5, const uint4& x6, const uint4& x7)
+      __attribute__((always_inline)) {
+    uint4* d = reinterpret_cast<uint4*>(stg + l16);
+    d[0] = x0;
+    d[64] = x1;
+    d[128] = x2;
+    d[192] = x3;
+    if constexpr (BITS == 4) {
+      d[256] = x4;
+      d[320] = x5;
+      d[384] = x6;
+      d[448] = x7;
+    }
+  };
+
+  // residual slice, 16 tokens per batch.  Key lanes: token n16 of the batch,
+  // channels 8*kg + 32*i .. +7 (MFMA B operand); value lanes: token group
+  // tg = lane/16 (tokens tg, tg+4, tg+8, tg+12), channels 8*c8 .. 8*c8+7.
+  // Tokens past the slice read zeros and weigh zero.
+  const int tg = lane >> 4, c8 = lane & 15;
+  half8 rk0, rk1, rk2, rk3;
+  uint4 rv0, rv1, rv2, rv3;
+  auto load_res = [&](int t16) __attribute__((always_inline)) {
+    const int tk = t16 + n16;
+    const uint32_t ko = tk < r_end ? (uint32_t)(tk * kD * 2 + kg * 16) : kOut;
+    rk0 = __builtin_bit_cast(half8, ld16(r_kr, ko));
+    rk1 = __builtin_bit_cast(half8, ld16(r_kr, ko + 64));
+    rk2 = __builtin_bit_cast(half8, ld16(r_kr, ko + 128));
+    rk3 = __builtin_bit_cast(half8, ld16(r_kr, ko + 192));
+    auto vo = [&](int ti) {
+      const int tv = t16 + ti;
+      return tv < r_end ? (uint32_t)(tv * kD * 2 + c8 * 16) : kOut;
+    };
+    rv0 = ld16(r_vr, vo(tg));
+    rv1 = ld16(r_vr, vo(tg + 4));
+    rv2 = ld16(r_vr, vo(tg + 8));
+    rv3 = ld16(r_vr, vo(tg + 12));
+  };
+  load_res(r_begin);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Loads run DEPTH tiles ahead of the compute, in DEPTH register sets used
+  // round robin.  They are issued before the residual slice so that it
+  // overlaps them.
+  constexpr int DEPTH = prefetch_depth<BITS, R>();
+  uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
+  float4 a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
+  // (the same issue order as the loop: codes A, meta A, codes B, meta B)
+  load_codes(t_begin, a0, a1, a2, a3, a4, a5, a6, a7);
+  __builtin_amdgcn_sched_barrier(0);
+  load_meta(t_begin, a_ks, a_kz, a_vs, a_vz);
+  if constexpr (DEPTH == 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_codes(t_begin + 1, b0, b1, b2, b3, b4, b5, b6, b7);
+    __builtin_amdgcn_sched_barrier(0);
+    load_meta(t_begin + 1, b_ks, b_kz, b_vs, b_vz);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // scaled query (log2 domain) of channels cq..cq+3, and its power-of-two
+  // normalisation qn so that |q * qn| < 1 (then |q' * qn| < 65536 / 1.5)
+  const float qs = a.scale * kLog2e;
+  float sq[R][4];
+  float qabs = 0.f;
+#pragma unroll
+  for (int h = 0; h < R; h++) {
+    const uint2 q4 = q4r[h];
+    sq[h][0] = qs * h2f((uint16_t)(q4.x & 0xFFFFu));
+    sq[h][1] = qs * h2f((uint16_t)(q4.x >> 16));
+    sq[h][2] = qs * h2f((uint16_t)(q4.y & 0xFFFFu));
+    sq[h][3] = qs * h2f((uint16_t)(q4.y >> 16));
+#pragma unroll
+    for (int e = 0; e < 4; e++) qabs = fmaxf(qabs, fabsf(sq[h][e]));
+  }
+  qabs = wave_max(qabs);
+  int qe = (int)((__builtin_bit_cast(uint32_t, qabs) >> 23) & 0xFF) - 126;  // qabs < 2^qe
+  qe = qe < -100 ? -100 : (qe > 100 ? 100 : qe);
+  const float qn = __builtin_bit_cast(float, (uint32_t)(127 - qe) << 23);
+  const float qup = __builtin_bit_cast(float, (uint32_t)(127 + qe) << 23);
+  float sqn[R][4];
+#pragma unroll
+  for (int h = 0; h < R; h++)
+#pragma unroll
+    for (int e = 0; e < 4; e++) sqn[h][e] = sq[h][e] * qn;
+
+  float m_run[R], l_acc[R], l_res[R];
+  float gam[R][kNG];
+  float ores[R][8];
+#pragma unroll
+  for (int h = 0; h < R; h++) {
     m_run[h] = -INFINITY;
-    l_acc[h] = l_res[h] = ores0[h] = ores1[h] = 0.f;
+    l_acc[h] = l_res[h] = 0.f;
 #pragma unroll
     for (int j = 0; j < kNG; j++) gam[h][j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) ores[h][e] = 0.f;
   }
   float4v cv[8];
 #pragma unroll
   for (int nb = 0; nb < 8; nb++) cv[nb] = float4v{0.f, 0.f, 0.f, 0.f};
 
-  const bool a_row_ok = n16 < 2 * r;    // A rows beyond 2r stay zero
+  // score slot of head 2*kg + hh for token index k (absent heads go to a sink)
+  auto sc_addr = [&](int hh, int k) __attribute__((always_inline)) -> float* {
+    const int h = 2 * kg + hh;
+    return h < R ? lds_sc + h * CH + k : lds_dummy + n16;
+  };
 
-  // new chunk maximum -> rescale every running quantity
-  auto rescale = [&](int ntok) {
-    float alpha[RR];
+  // new maximum over the ntok scores in LDS -> rescale every running quantity
+  auto rescale = [&](int ntok) __attribute__((always_inline)) {
+    float alpha[R];
     bool any = false;
 #pragma unroll
-    for (int h = 0; h < RR; h++) {
-      alpha[h] = 1.f;
-      if (h < r) {
-        float mx = -INFINITY;
-        for (int k = lane; k < ntok; k += 64) mx = fmaxf(mx, lds_sc[h * CH + k]);
-        mx = wave_max(mx);
-        const float m_new = fmaxf(m_run[h], mx);
-        alpha[h] = fast_exp2(m_run[h] - m_new);
-        any |= m_new != m_run[h];
-        m_run[h] = m_new;
-      }
+    for (int h = 0; h < R; h++) {
+      const float mx = wave_max(lane < ntok ? lds_sc[h * CH + lane] : -INFINITY);
+      const float m_new = fmaxf(m_run[h], mx);
+      // a head still without any finite score keeps factor 1 (-inf - -inf)
+      alpha[h] = m_new == -INFINITY ? 1.f : fast_exp2(m_run[h] - m_new);
+      any |= m_new != m_run[h];
+      m_run[h] = m_new;
     }
     if (any) {
 #pragma unroll
-      for (int h = 0; h < RR; h++) {
+      for (int h = 0; h < R; h++) {
         l_acc[h] *= alpha[h];
         l_res[h] *= alpha[h];
-        ores0[h] *= alpha[h];
-        ores1[h] *= alpha[h];
 #pragma unroll
         for (int j = 0; j < kNG; j++) gam[h][j] *= alpha[h];
+#pragma unroll
+        for (int e = 0; e < 8; e++) ores[h][e] *= alpha[h];
       }
-      const float a0 = pick<RR>(alpha, kg, 0), a1 = pick<RR>(alpha, kg, 1);
+      const float a0 = pick<R>(alpha, kg, 0), a1 = pick<R>(alpha, kg, 1);
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
         cv[nb][0] *= a0;
@@ -255,176 +476,106 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     }
   };
 
-  // Everything one 64-token tile needs from memory, held in registers so the
-  // next tile's loads are in flight while the current tile is computed.
-  using KCode = typename std::conditional<BITS == 2, uint2, uint4>::type;
-  using VCode = typename std::conditional<BITS == 2, uint32_t, uint2>::type;
-  struct KTile {
-    KCode c[4];        // codes of 4 x 16 tokens, 32 channels of this lane group
-    float2 s[2], z[2]; // key scale / zero of channels 2*lane, 2*lane+1, 2 groups
-  };
-  struct VTile {
-    VCode c[8];        // codes of 16 tokens of channel 16*nb + n16, nb = 0..7
-    float4 s, z;       // value scale / zero of token lane, 4 groups
-  };
-  auto load_k = [&](int tile, KTile& kt) {
-    const int tok0 = tile * 64;
-    const bool half_tile = tok0 + 64 > tq;
+  // ---------------- tile loads: NLD code loads + 4 metadata loads, 16 B each
+  // one tile (codes already staged in LDS): key scores -> LDS, online-softmax
+  // rescale, P.V
+  auto do_tile = [&](int tile, float4 ks4, float4 kz4, float4 vs4, float4 vz4) __attribute__((always_inline)) {
+    const bool half_tile = tile * 64 + 64 > tq;   // only the first 32 tokens exist
+    // key factors (both groups at once: lanes 0-31 group 0, 32-63 group 1)
+    const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
+    const float kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
+    float beta0[R], beta1[R];
 #pragma unroll
-    for (int mb = 0; mb < 4; mb++) {
-      if (mb < 2 || !half_tile) {
-        const size_t row = (size_t)tok0 + 16 * mb + n16;
-        kt.c[mb] = *reinterpret_cast<const KCode*>(kc + row * W + (BITS == 2 ? 2 : 4) * kg);
+    for (int h = 0; h < R; h++) {
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        uint32_t hi, lo;
+        split2(sqn[h][e] * ksv[e], sqn[h][e + 2] * ksv[e + 2], hi, lo);
+        *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h) * 64) = hi;
+        *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h + 1) * 64) = lo;
       }
+      float bp = sq[h][0] * kzv[0] + sq[h][1] * kzv[1] + sq[h][2] * kzv[2] + sq[h][3] * kzv[3];
+      bp += dpp<0x128>(bp);
+      bp += dpp<0x124>(bp);
+      bp += dpp<0x122>(bp);
+      bp += dpp<0x121>(bp);
+      beta0[h] = lane_read(bp, 0) + lane_read(bp, 16);
+      beta1[h] = lane_read(bp, 32) + lane_read(bp, 48);
     }
+    if (half_tile && lane < 32) {
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      if (kb == 0 || !half_tile) {
-        const size_t g = (size_t)(tok0 >> 5) + kb;
-        kt.s[kb] = *reinterpret_cast<const float2*>(ksc + g * kD + 2 * lane);
-        kt.z[kb] = *reinterpret_cast<const float2*>(kzr + g * kD + 2 * lane);
-      }
+      for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
     }
-  };
-  auto load_v = [&](int tile, VTile& vt) {
-    const uint32_t* base = vc + (size_t)tile * kD * WPC;
+    __builtin_amdgcn_wave_barrier();
+    const int ngr = half_tile ? 1 : 2;
 #pragma unroll
-    for (int nb = 0; nb < 8; nb++)
-      vt.c[nb] = *reinterpret_cast<const VCode*>(base + (16 * nb + n16) * WPC +
-                                                 (BITS == 2 ? 1 : 2) * kg);
-    const size_t t = (size_t)tile * 64 + lane;
-    vt.s = *reinterpret_cast<const float4*>(vsc + t * kNG);
-    vt.z = *reinterpret_cast<const float4*>(vzr + t * kNG);
-  };
-
-  // scores of one tile -> lds_sc[h][i*64 + token]
-  auto do_k = [&](int tile, int i, const KTile& kt) {
-    const int tok0 = tile * 64;
-    const bool half_tile = tok0 + 64 > tq;   // only the first 32 tokens exist
+    for (int g = 0; g < 2; g++) {
+      if (g < ngr) {
+        half8 af[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; kb++) {
-      if (kb == 1 && half_tile) {
+        for (int m = 0; m < 4; m++)
+          af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
+        const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
 #pragma unroll
-        for (int h = 0; h < RR; h++)
-          if (h < r && lane < 32) lds_sc[h * CH + i * 64 + 32 + lane] = -INFINITY;
-        continue;
-      }
-      const float2 s2 = kt.s[kb], z2 = kt.z[kb];
-      float qa[RR], qb[RR], bpart[RR], beta[RR];
-      float qmax = 0.f;
-#pragma unroll
-      for (int h = 0; h < RR; h++) {
-        qa[h] = sq0[h] * s2.x;
-        qb[h] = sq1[h] * s2.y;
-        bpart[h] = sq0[h] * z2.x + sq1[h] * z2.y;
-        qmax = fmaxf(qmax, fmaxf(fabsf(qa[h]), fabsf(qb[h])));
-      }
-      // power-of-two prescale keeps the fp16 hi part finite for any input
-      qmax = wave_max(qmax);
-      const int ex = max(0, (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xFF) - 127 - 13);
-      const float down = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
-      const float up = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
-      {
-        int m0, s0, m1, s1;
-        const int cp = (2 * lane) & 31;
-        k_pos<BITS>(cp, m0, s0);
-        k_pos<BITS>(cp + 1, m1, s1);
-        const int kgc = (2 * lane) >> 5;
-#pragma unroll
-        for (int h = 0; h < RR; h++) {
-          if (h < r) {
-            const float x0 = qa[h] * down, x1 = qb[h] * down;
-            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-            const _Float16 l0 = (_Float16)(x0 - (float)h0), l1 = (_Float16)(x1 - (float)h1);
-            lds_a[((m0 * ROWS + 2 * h) * 4 + kgc) * 8 + s0] = h0;
-            lds_a[((m0 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s0] = l0;
-            lds_a[((m1 * ROWS + 2 * h) * 4 + kgc) * 8 + s1] = h1;
-            lds_a[((m1 * ROWS + 2 * h + 1) * 4 + kgc) * 8 + s1] = l1;
+        for (int mb2 = 0; mb2 < 2; mb2++) {
+          const int mb = 2 * g + mb2;
+          float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+          if constexpr (BITS == 2) {
+            const uint2 x = *reinterpret_cast<const uint2*>(stg + (16 * mb + n16) * W * 4 + kg * 8);
+            acc = mfma(af[0], cvt_nib2(x.x & 0x33333333u), acc);
+            acc = mfma(af[1], cvt_nib2((x.x >> 2) & 0x33333333u), acc);
+            acc = mfma(af[2], cvt_nib2(x.y & 0x33333333u), acc);
+            acc = mfma(af[3], cvt_nib2((x.y >> 2) & 0x33333333u), acc);
+          } else {
+            const uint4 x = *reinterpret_cast<const uint4*>(stg + (16 * mb + n16) * W * 4 + kg * 16);
+            acc = mfma(af[0], cvt_word4(x.x), acc);
+            acc = mfma(af[1], cvt_word4(x.y), acc);
+            acc = mfma(af[2], cvt_word4(x.z), acc);
+            acc = mfma(af[3], cvt_word4(x.w), acc);
           }
-        }
-      }
-#pragma unroll
-      for (int h = 0; h < RR; h++) beta[h] = h < r ? wave_sum(bpart[h]) : 0.f;
-      __builtin_amdgcn_wave_barrier();
-      half8 af[4];
-#pragma unroll
-      for (int m = 0; m < 4; m++) {
-        af[m] = half8{0, 0, 0, 0, 0, 0, 0, 0};
-        if (a_row_ok)
-          af[m] = *reinterpret_cast<const half8*>(lds_a + ((m * ROWS + n16) * 4 + kg) * 8);
-      }
-      __builtin_amdgcn_wave_barrier();
-      const float b0 = pick<RR>(beta, kg, 0), b1 = pick<RR>(beta, kg, 1);
-#pragma unroll
-      for (int mb2 = 0; mb2 < 2; mb2++) {
-        const int mb = 2 * kb + mb2;
-        float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-        if constexpr (BITS == 2) {
-          const uint2 w = kt.c[mb];
-#pragma unroll
-          for (int wp = 0; wp < 2; wp++) {
-            const uint32_t x = wp ? w.y : w.x;
-            acc = mfma(af[2 * wp], cvt_nib2(x & 0x33333333u), acc);
-            acc = mfma(af[2 * wp + 1], cvt_nib2((x >> 2) & 0x33333333u), acc);
-          }
-        } else {
-          const uint4 w = kt.c[mb];
-          acc = mfma(af[0], cvt_word4(w.x), acc);
-          acc = mfma(af[1], cvt_word4(w.y), acc);
-          acc = mfma(af[2], cvt_word4(w.z), acc);
-          acc = mfma(af[3], cvt_word4(w.w), acc);
-        }
-        const int k = i * 64 + 16 * mb + n16;
-        const int h0 = 2 * kg, h1 = 2 * kg + 1;
-        if (h0 < r) lds_sc[h0 * CH + k] = (acc[0] + acc[1]) * up + b0;
-        if (h1 < r) lds_sc[h1 * CH + k] = (acc[2] + acc[3]) * up + b1;
-      }
-    }
-  };
-
-  // P.V of one tile into the cv accumulators
-  auto do_v = [&](int tile, int i, const VTile& vt) {
-    const int t = tile * 64 + lane;              // this lane's token
-    const bool valid = t < tq;
-    const float sj[4] = {vt.s.x, vt.s.y, vt.s.z, vt.s.w};
-    const float zj[4] = {valid ? vt.z.x : 0.f, valid ? vt.z.y : 0.f, valid ? vt.z.z : 0.f,
-                         valid ? vt.z.w : 0.f};
-    int mt, st;
-    v_pos<BITS>(lane & 15, mt, st);
-    const int kgt = lane >> 4;
-#pragma unroll
-    for (int h = 0; h < RR; h++) {
-      if (h < r) {
-        const float p = valid ? fast_exp2(lds_sc[h * CH + i * 64 + lane] - m_run[h]) : 0.f;
-        l_acc[h] += p;
-#pragma unroll
-        for (int j = 0; j < kNG; j++) {
-          gam[h][j] += p * zj[j];
-          const float x = valid ? p * sj[j] : 0.f;
-          const _Float16 hi = (_Float16)x;
-          const _Float16 lo = (_Float16)(x - (float)hi);
-          lds_a[((((j * 2 + mt) * ROWS) + 2 * h) * 4 + kgt) * 8 + st] = hi;
-          lds_a[((((j * 2 + mt) * ROWS) + 2 * h + 1) * 4 + kgt) * 8 + st] = lo;
+          const int k = 16 * mb + n16;
+          *sc_addr(0, k) = (acc[0] + acc[1]) * qup + b0;
+          *sc_addr(1, k) = (acc[2] + acc[3]) * qup + b1;
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
+    rescale(64);
+    // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
+    const bool valid = tile * 64 + lane < tq;
+    const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
+    const float vzv[4] = {valid ? vz4.x : 0.f, valid ? vz4.y : 0.f, valid ? vz4.z : 0.f,
+                          valid ? vz4.w : 0.f};
+#pragma unroll
+    for (int h = 0; h < R; h++) {
+      const float p = valid ? fast_exp2(lds_sc[h * CH + lane] - m_run[h]) : 0.f;
+      l_acc[h] += p;
+#pragma unroll
+      for (int j = 0; j < kNG; j++) {
+        gam[h][j] += p * vzv[j];
+        const float x = valid ? p * vsv[j] : 0.f;
+        const _Float16 hi = (_Float16)x;
+        const _Float16 lo = (_Float16)(x - (float)hi);
+        char* dst = lds_a + vwr + (uint32_t)(j * 2 * ROWS * 64);
+        *reinterpret_cast<_Float16*>(dst + (2 * h) * 64) = hi;
+        *reinterpret_cast<_Float16*>(dst + (2 * h + 1) * 64) = lo;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const char* vstg = stg + C::KC_BYTES;
 #pragma unroll
     for (int j = 0; j < kNG; j++) {
-      half8 av0 = half8{0, 0, 0, 0, 0, 0, 0, 0}, av1 = av0;
-      if (a_row_ok) {
-        av0 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 0) * ROWS + n16) * 4 + kg) * 8);
-        av1 = *reinterpret_cast<const half8*>(lds_a + (((j * 2 + 1) * ROWS + n16) * 4 + kg) * 8);
-      }
+      const half8 av0 = *reinterpret_cast<const half8*>(a_rd + (j * 2 + 0) * ROWS * 64);
+      const half8 av1 = *reinterpret_cast<const half8*>(a_rd + (j * 2 + 1) * ROWS * 64);
 #pragma unroll
       for (int nbj = 0; nbj < 2; nbj++) {
         const int nb = 2 * j + nbj;
         if constexpr (BITS == 2) {
-          const uint32_t x = vt.c[nb];
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 4);
           cv[nb] = mfma(av0, cvt_nib2(x & 0x33333333u), cv[nb]);
           cv[nb] = mfma(av1, cvt_nib2((x >> 2) & 0x33333333u), cv[nb]);
         } else {
-          const uint2 x = vt.c[nb];
+          const uint2 x = *reinterpret_cast<const uint2*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 8);
           cv[nb] = mfma(av0, cvt_word4(x.x), cv[nb]);
           cv[nb] = mfma(av1, cvt_word4(x.y), cv[nb]);
         }
@@ -433,62 +584,109 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // software pipeline: the loads of step n+1 are issued before step n runs
-  KTile kt;
-  VTile vt;
-  if (t_begin < t_end) load_k(t_begin, kt);
-  for (int c0 = t_begin; c0 < t_end; c0 += CT) {
-    const int nt = min(CT, t_end - c0);
-    for (int i = 0; i < nt; i++) {
-      const KTile cur = kt;
-      if (i + 1 < nt)
-        load_k(c0 + i + 1, kt);
-      else
-        load_v(c0, vt);
-      do_k(c0 + i, i, cur);
+  // ---------------- residual slice (full precision), overlapping the tile loads
+  // one batch of 16 tokens from rk*/rv*: scores by MFMA, values on the VALU
+  half8 ar[4];
+  auto res_batch = [&](int t16) __attribute__((always_inline)) {
+    const int n = min(16, r_end - t16);
+    float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
+    acc = mfma(ar[0], rk0, acc);
+    acc = mfma(ar[1], rk1, acc);
+    acc = mfma(ar[2], rk2, acc);
+    acc = mfma(ar[3], rk3, acc);
+    {
+      const bool ok = n16 < n;
+      float* p0 = ok ? sc_addr(0, n16) : lds_dummy + n16;
+      float* p1 = ok ? sc_addr(1, n16) : lds_dummy + n16;
+      *p0 = (acc[0] + acc[1]) * qup;
+      *p1 = (acc[2] + acc[3]) * qup;
     }
     __builtin_amdgcn_wave_barrier();
-    rescale(nt * 64);
-    for (int i = 0; i < nt; i++) {
-      const VTile cur = vt;
-      if (i + 1 < nt)
-        load_v(c0 + i + 1, vt);
-      else if (c0 + nt < t_end)
-        load_k(c0 + nt, kt);
-      do_v(c0 + i, i, cur);
+    rescale(n);
+    const uint4 vv[4] = {rv0, rv1, rv2, rv3};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int ti = tg + 4 * i;
+      const bool ok = ti < n;
+      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        v[2 * e] = h2f((uint16_t)(w4[e] & 0xFFFFu));
+        v[2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
+      }
+#pragma unroll
+      for (int h = 0; h < R; h++) {
+        const float p = ok ? fast_exp2(lds_sc[h * CH + (ok ? ti : 0)] - m_run[h]) : 0.f;
+        if (c8 == 0) l_res[h] += p;     // each token counted once
+#pragma unroll
+        for (int e = 0; e < 8; e++) ores[h][e] += p * v[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  };
+  // The first batch runs in every wave (an empty slice weighs zero), so that
+  // its loads stay ahead of the tile loads instead of sinking into a branch.
+  // Residual key A: row (h, hi|lo), MFMA i, lane group kgr, slot s <->
+  // channel 32 i + 8 kgr + s.  Lanes 0-31 write channel pairs (cq, cq+1),
+  // (cq+2, cq+3) from the scaled query already in registers.
+  if (lane < 32) {
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      const int ch = cq + 2 * e;
+      const uint32_t off =
+          (uint32_t)((((ch >> 5) * ROWS) * 4 + ((ch & 31) >> 3)) * 16 + 2 * (ch & 7));
+#pragma unroll
+      for (int h = 0; h < R; h++) {
+        uint32_t hi, lo;
+        split2(sqn[h][2 * e], sqn[h][2 * e + 1], hi, lo);
+        *reinterpret_cast<uint32_t*>(lds_res + off + (2 * h) * 64) = hi;
+        *reinterpret_cast<uint32_t*>(lds_res + off + (2 * h + 1) * 64) = lo;
+      }
     }
   }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; i++) ar[i] = *reinterpret_cast<const half8*>(res_rd + i * ROWS * 64);
+  res_batch(r_begin);
+  // slices longer than one batch (short contexts, few splits) load the rest here
+  for (int t16 = r_begin + 16; t16 < r_end; t16 += 16) {
+    load_res(t16);
+    res_batch(t16);
+  }
 
-  // ---------------- residual slice (full precision), VALU
-  for (int c0 = r_begin; c0 < r_end; c0 += CH) {
-    const int c1 = min(r_end, c0 + CH);
-    for (int t = c0; t < c1; t++) {
-      const uint32_t kk = *reinterpret_cast<const uint32_t*>(kr + (size_t)t * kD + 2 * lane);
-      const float k0 = h2f((uint16_t)(kk & 0xFFFFu)), k1 = h2f((uint16_t)(kk >> 16));
-#pragma unroll
-      for (int h = 0; h < RR; h++) {
-        if (h < r) {
-          const float sc = wave_sum(sq0[h] * k0 + sq1[h] * k1);
-          if (lane == 0) lds_sc[h * CH + (t - c0)] = sc;
-        }
-      }
+  // ---------------- quantized tiles, DEPTH tiles of loads in flight
+  // the scheduling barriers keep "stage tile t, issue loads of t+DEPTH,
+  // compute t" in that order, so no wait for a later tile lands before the
+  // compute of tile t.  Loads past the wave's last tile read zeros; the only
+  // branch in the loop (an odd tile count under DEPTH 2) holds no load.
+  if constexpr (DEPTH == 2) {
+    for (int t = t_begin; t < t_end; t += 2) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(a0, a1, a2, a3, a4, a5, a6, a7);
+      load_codes(t + 2, a0, a1, a2, a3, a4, a5, a6, a7);
+      __builtin_amdgcn_sched_barrier(0);
+      do_tile(t, a_ks, a_kz, a_vs, a_vz);
+      __builtin_amdgcn_sched_barrier(0);
+      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz);
+      __builtin_amdgcn_sched_barrier(0);
+      stage(b0, b1, b2, b3, b4, b5, b6, b7);
+      load_codes(t + 3, b0, b1, b2, b3, b4, b5, b6, b7);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz);
+      __builtin_amdgcn_sched_barrier(0);
+      load_meta(t + 3, b_ks, b_kz, b_vs, b_vz);
     }
-    __builtin_amdgcn_wave_barrier();
-    rescale(c1 - c0);
-    for (int t = c0; t < c1; t++) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vr + (size_t)t * kD + 2 * lane);
-      const float v0 = h2f((uint16_t)(vv & 0xFFFFu)), v1 = h2f((uint16_t)(vv >> 16));
-#pragma unroll
-      for (int h = 0; h < RR; h++) {
-        if (h < r) {
-          const float p = fast_exp2(lds_sc[h * CH + (t - c0)] - m_run[h]);
-          l_res[h] += p;
-          ores0[h] += p * v0;
-          ores1[h] += p * v1;
-        }
-      }
+  } else {
+    for (int t = t_begin; t < t_end; t++) {
+      __builtin_amdgcn_sched_barrier(0);
+      stage(a0, a1, a2, a3, a4, a5, a6, a7);
+      load_codes(t + 1, a0, a1, a2, a3, a4, a5, a6, a7);
+      __builtin_amdgcn_sched_barrier(0);
+      do_tile(t, a_ks, a_kz, a_vs, a_vz);
+      __builtin_amdgcn_sched_barrier(0);
+      load_meta(t + 1, a_ks, a_kz, a_vs, a_vz);
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
   // ---------------- wave result -> LDS: o[h][d], m[h], l[h]
@@ -496,54 +694,77 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     const int h0 = 2 * kg, h1 = 2 * kg + 1;
 #pragma unroll
     for (int nb = 0; nb < 8; nb++) {
-      if (h0 < r) lds_o[h0 * kD + 16 * nb + n16] = cv[nb][0] + cv[nb][1];
-      if (h1 < r) lds_o[h1 * kD + 16 * nb + n16] = cv[nb][2] + cv[nb][3];
+      float* o0 = h0 < R ? lds_o + h0 * kD + 16 * nb + n16 : lds_dummy + n16;
+      float* o1 = h1 < R ? lds_o + h1 * kD + 16 * nb + n16 : lds_dummy + n16;
+      *o0 = cv[nb][0] + cv[nb][1];
+      *o1 = cv[nb][2] + cv[nb][3];
     }
   }
+  // residual P.V partials: lanes c8, c8+16, c8+32, c8+48 (the 4 token groups)
+  // hold channels 8*c8..8*c8+7; sum them across lanes, then lane (tg, c8) adds
+  // channels 8*c8+2*tg, 8*c8+2*tg+1 (value group c8/4) together with the Gamma
+  // term of that group
   __builtin_amdgcn_wave_barrier();
+  {
+    const int tg = lane >> 4, c8 = lane & 15, grp = c8 >> 2;
 #pragma unroll
-  for (int h = 0; h < RR; h++) {
-    if (h < r) {
-      float gsum[kNG];
+    for (int h = 0; h < R; h++) {
+      float g[kNG];
 #pragma unroll
-      for (int j = 0; j < kNG; j++) gsum[j] = wave_sum(gam[h][j]);
-      const float lsum = wave_sum(l_acc[h]) + l_res[h];
-      // channels 2*lane, 2*lane+1 lie in value group (2*lane)/32 = lane/16
-      float gj = gsum[0];
+      for (int j = 0; j < kNG; j++) g[j] = wave_sum(gam[h][j]);
+      const float lsum = wave_sum(l_acc[h]) + wave_sum(l_res[h]);
+      float gj = g[0];
 #pragma unroll
       for (int j = 1; j < kNG; j++)
-        if (kg == j) gj = gsum[j];
-      lds_o[h * kD + 2 * lane] += gj + ores0[h];
-      lds_o[h * kD + 2 * lane + 1] += gj + ores1[h];
+        if (grp == j) gj = g[j];
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        float x = ores[h][e];
+        x += __shfl_xor(x, 16);
+        x += __shfl_xor(x, 32);
+        if (e == 2 * tg) rs0 = x;
+        if (e == 2 * tg + 1) rs1 = x;
+      }
+      float2* op = reinterpret_cast<float2*>(lds_o + h * kD + 8 * c8 + 2 * tg);
+      float2 o2 = *op;
+      o2.x += gj + rs0;
+      o2.y += gj + rs1;
+      *op = o2;
       if (lane == 0) {
-        lds_o[RR * kD + h] = m_run[h];
-        lds_o[RR * kD + RR + h] = lsum;
+        lds_o[R * kD + h] = m_run[h];
+        lds_o[R * kD + R + h] = lsum;
       }
     }
   }
   __syncthreads();
 
   // ---------------- merge the block's waves
-  for (int idx = threadIdx.x; idx < r * kD; idx += NW * 64) {
+  for (int idx = threadIdx.x; idx < R * kD; idx += NW * 64) {
     const int h = idx / kD, d = idx % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; w++) M = fmaxf(M, smem[w * C::LDS_WAVE + C::LDS_A + C::LDS_SC + RR * kD + h]);
+    for (int w = 0; w < NW; w++) {
+      const float* ow = reinterpret_cast<const float*>(smem + C::ZERO_BYTES + w * C::WAVE_BYTES +
+                                                       C::A_BYTES + C::RES_BYTES + C::SC_BYTES);
+      M = fmaxf(M, ow[R * kD + h]);
+    }
     float O = 0.f, L = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < NW; w++) {
-        const float* o = smem + w * C::LDS_WAVE + C::LDS_A + C::LDS_SC;
-        const float f = fast_exp2(o[RR * kD + h] - M);
-        O += o[h * kD + d] * f;
-        L += o[RR * kD + RR + h] * f;
+        const float* ow = reinterpret_cast<const float*>(
+            smem + C::ZERO_BYTES + w * C::WAVE_BYTES + C::A_BYTES + C::RES_BYTES + C::SC_BYTES);
+        const float f = fast_exp2(ow[R * kD + h] - M);
+        O += ow[h * kD + d] * f;
+        L += ow[R * kD + R + h] * f;
       }
     }
     const size_t row = qrow0 + h;
     if (S == 1) {
       a.out[row * kD + d] = f2h(O / L);
     } else {
-      const size_t rows = (size_t)a.B * H * r;
+      const size_t rows = (size_t)a.B * H * R;
       if (d == 0) {
         a.ws[row * S + split] = M * kLn2;          // natural-log units for the combine
         a.ws[rows * S + row * S + split] = L;
@@ -553,39 +774,85 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   }
 }
 
-// blocks of 16 waves only where their LDS fits (r <= 2)
-template <int BITS, int RR>
-hipError_t launch_rr(const DecodeArgs& a, int nw, hipStream_t st) {
+template <int R>
+constexpr int block_waves(int nw) {
+  return (R >= 8 || nw < 8) ? 4 : 8;
+}
+
+template <int BITS, int R>
+hipError_t launch_r(const DecodeArgs& a, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
-  if (nw == 16 && RR <= 2)
-    decode_mfma_kernel<BITS, RR, (RR <= 2 ? 16 : 8)><<<grid, (RR <= 2 ? 16 : 8) * 64, 0, st>>>(a);
-  else if (nw >= 8)
-    decode_mfma_kernel<BITS, RR, 8><<<grid, 8 * 64, 0, st>>>(a);
+  if (block_waves<R>(nw) == 8)
+    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4)><<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a);
   else
-    decode_mfma_kernel<BITS, RR, 4><<<grid, 4 * 64, 0, st>>>(a);
+    decode_mfma_kernel<BITS, R, 4><<<grid, 4 * 64, 0, st>>>(a);
   return hipGetLastError();
 }
 
+template <int BITS>
+hipError_t launch_bits(const DecodeArgs& a, int nw, hipStream_t st) {
+  switch (a.r) {
+    case 1: return launch_r<BITS, 1>(a, nw, st);
+    case 2: return launch_r<BITS, 2>(a, nw, st);
+    case 4: return launch_r<BITS, 4>(a, nw, st);
+    default: return launch_r<BITS, 8>(a, nw, st);
+  }
+}
+
 }  // namespace
 
-int decode_mfma_block_waves(int r, int nw) {
-  if (nw == 16 && r <= 2) return 16;
-  return nw >= 8 ? 8 : 4;
+bool decode_mfma_supported(int D, int G, int r) {
+  return D == kD && G == kG && (r == 1 || r == 2 || r == 4 || r == 8);
 }
 
 namespace {
-
-template <int BITS>
-hipError_t launch_bits(const DecodeArgs& a, int nw, hipStream_t st) {
-  if (a.r == 1) return launch_rr<BITS, 1>(a, nw, st);
-  if (a.r == 2) return launch_rr<BITS, 2>(a, nw, st);
-  if (a.r <= 4) return launch_rr<BITS, 4>(a, nw, st);
-  return launch_rr<BITS, 8>(a, nw, st);
+template <int BITS, int R, int NW>
+int occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW>), NW * 64, 0) !=
+      hipSuccess)
+    return 1;
+  return n > 0 ? n : 1;
 }
-
+template <int BITS, int R>
+int occupancy_r(int nw) {
+  return block_waves<R>(nw) == 8 ? occupancy_of<BITS, R, (R < 8 ? 8 : 4)>()
+                                 : occupancy_of<BITS, R, 4>();
+}
+template <int BITS>
+int occupancy_bits(int r, int nw) {
+  switch (r) {
+    case 1: return occupancy_r<BITS, 1>(nw);
+    case 2: return occupancy_r<BITS, 2>(nw);
+    case 4: return occupancy_r<BITS, 4>(nw);
+    default: return occupancy_r<BITS, 8>(nw);
+  }
+}
 }  // namespace
 
-bool decode_mfma_supported(int D, int G, int r) { return D == kD && G == kG && r >= 1 && r <= 8; }
+int decode_mfma_blocks_per_cu(int bits, int r, int nw) {
+  // cached per (bits, r, requested waves): queried once per process
+  static std::atomic<int> cache[2][4][3];
+  const int bi = bits == 2 ? 0 : 1;
+  const int ri = r == 1 ? 0 : (r == 2 ? 1 : (r == 4 ? 2 : 3));
+  const int wi = nw >= 8 ? 1 : 0;
+  int c = cache[bi][ri][wi].load(std::memory_order_relaxed);
+  if (c == 0) {
+    c = bits == 2 ? occupancy_bits<2>(r, nw) : occupancy_bits<4>(r, nw);
+    cache[bi][ri][wi].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+int decode_mfma_block_waves(int r, int nw) {
+  switch (r) {
+    case 1: return block_waves<1>(nw);
+    case 2: return block_waves<2>(nw);
+    case 4: return block_waves<4>(nw);
+    default: return block_waves<8>(nw);
+  }
+}
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
   return a.bits == 2 ? launch_bits<2>(a, nw, st) : launch_bits<4>(a, nw, st);

@@ -92,9 +92,9 @@ bool use_mfma(const kivi_shape& s) {
 // waves per block of the matrix-core decode kernel
 int mfma_waves() {
   static const int nw = [] {
-    const char* e = getenv("KIVI_DECODE_WAVES");   // tuning override: 4, 8 or 16
+    const char* e = getenv("KIVI_DECODE_WAVES");   // tuning override: 4 or 8
     int v = e ? atoi(e) : 8;
-    return (v == 8 || v == 16) ? v : 4;
+    return v >= 8 ? 8 : 4;
   }();
   return nw;
 }
@@ -104,11 +104,11 @@ int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
   const int L = tq + tr;
   int S;
   if (use_mfma(s)) {
-    // about 16 waves per compute unit in total, and at least two 64-token
-    // tiles per wave
+    // one round of blocks: as many splits as fill the resident block slots,
+    // keeping at least two 64-token tiles per wave
     const int nw = kivi::decode_mfma_block_waves(s.gqa_ratio, mfma_waves());
-    const int target = 16 * cus;
-    S = (target + units * nw - 1) / (units * nw);
+    const int slots = cus * kivi::decode_mfma_blocks_per_cu(s.bits, s.gqa_ratio, mfma_waves());
+    S = slots / units;
     const int by_work = ((tq + 63) / 64) / (2 * nw);
     if (S > by_work) S = by_work;
   } else {

@@ -46,9 +46,11 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
 
 // Matrix-core decode kernel: head_dim 128, group 32, gqa ratio 1..8.
 bool decode_mfma_supported(int D, int G, int r);
-// nw: requested waves per block (4, 8 or 16); the block size actually used
+// nw: requested waves per block (4 or 8); the block size actually used
 // for a gqa ratio r is decode_mfma_block_waves(r, nw)
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st);
 int decode_mfma_block_waves(int r, int nw);
+// resident blocks per compute unit of that kernel variant (occupancy query)
+int decode_mfma_blocks_per_cu(int bits, int r, int nw);
 
 }  // namespace kivi
