@@ -57,9 +57,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+DECODE_KERNEL = "decode_mfma_kernel"
+# PMC calibration kernel: torch's elementwise bitwise_not over N bytes, a plain
+# copy-shaped kernel (reads N bytes, writes N bytes) with a recognisable name
+COPY_KERNEL_HINT = "bitwise_not"
+
+
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from committed rocprofv3 PMC summaries,
-    only if they were taken on the current kernel sources."""
+    """HBM bytes per decode launch from the committed rocprofv3 PMC summary,
+    only if it was taken on the current kernel sources."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
@@ -70,6 +76,58 @@ def measured_traffic(workload: str):
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, command: str):
+    """Calibrated HBM traffic of the decode kernel from two rocprofv3 --pmc
+    runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is
+    scaled by bytes / counter of the plain copy kernel that the same run
+    timed first (--copy-calibration: reads and writes `copy_bytes`)."""
+    import csv
+
+    def per_kernel(path, counter):
+        dec, cpy = [], []
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            v = float(row["Counter_Value"])
+            name = row["Kernel_Name"]
+            if DECODE_KERNEL in name:
+                dec.append(v)
+            elif COPY_KERNEL_HINT in name:
+                cpy.append(v)
+        if not dec or not cpy:
+            raise SystemExit(f"{path}: no {counter} rows for the decode or copy kernel")
+        return sum(dec) / len(dec), sum(cpy) / len(cpy), len(dec), len(cpy)
+
+    f_dec, f_cpy, nf, ncf = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_dec, w_cpy, nw, ncw = per_kernel(write_csv, "WRITE_SIZE")
+    k_fetch = copy_bytes / (f_cpy * 1024.0)
+    k_write = copy_bytes / (w_cpy * 1024.0)
+    read_b = f_dec * 1024.0 * k_fetch
+    write_b = w_dec * 1024.0 * k_write
+    out = {
+        "kernel": DECODE_KERNEL,
+        "workload": workload,
+        "command": command,
+        "fetch_size_kib_per_dispatch": round(f_dec, 1),
+        "write_size_kib_per_dispatch": round(w_dec, 1),
+        "dispatches": [nf, nw],
+        "copy_bytes": copy_bytes,
+        "copy_fetch_size_kib": round(f_cpy, 1),
+        "copy_write_size_kib": round(w_cpy, 1),
+        "fetch_scale": round(k_fetch, 4),
+        "write_scale": round(k_write, 4),
+        "hbm_read_bytes_per_launch": int(read_b),
+        "hbm_write_bytes_per_launch": int(write_b),
+        "hbm_bytes_per_launch": int(read_b + write_b),
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
@@ -127,7 +185,16 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run a plain device copy of MIB MiB (PMC calibration)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB", "CMD"),
+                    help="write the calibrated traffic summary from two PMC runs and exit")
     args = ap.parse_args()
+
+    if args.pmc_summary:
+        fcsv, wcsv, mib, cmd = args.pmc_summary
+        pmc_summary(fcsv, wcsv, int(mib) << 20, args.workload, cmd)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -173,21 +240,52 @@ def main():
         vnew.append(torch.from_numpy(vn).cuda())
         qs.append(torch.from_numpy(synth.query(w, s + 1)).cuda())
     outs = [torch.empty((B, H * r, D), dtype=torch.float16, device="cuda") for _ in range(NL)]
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for c in caches:
         c.workspace_for(args.splits)
     torch.cuda.synchronize()
 
+    # The step loop calls the C ABI directly with pointers bound once, so the
+    # host enqueues faster than the GPU drains and the events around each
+    # decode bracket queued work, not host-side gaps.
+    import ctypes
+
+    L = lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    crefs = [ctypes.byref(c.c) for c in caches]
+    kptr = [t.data_ptr() for t in knew]
+    vptr = [t.data_ptr() for t in vnew]
+    qptr = [t.data_ptr() for t in qs]
+    optr = [t.data_ptr() for t in outs]
+    wsp = [(c.workspace.data_ptr(), c.workspace.numel()) if c.workspace is not None else (None, 0)
+           for c in caches]
+    scale = float(w.softmax_scale)
+    append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
+
     def step(i, ev=None):
-        c = caches[i % NL]
+        li = i % NL
+        c = caches[li].c
         j = i % n_tok
         flush = c.tr == R
-        c.append(knew[j], vnew[j])
+        rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
+        if rc:
+            raise RuntimeError(f"kivi_append failed: {rc}")
         tq, tr = c.tq, c.tr
         if ev is not None:
             ev[0].record()
-        c.decode(qs[j], w.softmax_scale, out=outs[i % NL], num_splits=args.splits)
+        rc = decode_fn(crefs[li], qptr[j], scale, optr[li], wsp[li][0], wsp[li][1], args.splits,
+                       stream)
         if ev is not None:
             ev[1].record()
+        if rc:
+            raise RuntimeError(f"kivi_decode_attn failed: {rc}")
         return flush, tq, tr
 
     for i in range(args.warmup):
