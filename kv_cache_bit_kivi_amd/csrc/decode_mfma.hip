@@ -130,18 +130,23 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOut = 0x80000000u;   // past every plane (planes stay < 2^31 bytes)
+// Cache policy of the streamed cache reads: non-temporal.  Every cache byte is
+// read once per call, so keeping it out of the normal cache-allocation path
+// costs nothing and measurably raises the achieved read bandwidth.
+constexpr int kStream = 2;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
 __device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream);
   return uint4{v.x, v.y, v.z, v.w};
 }
 // (bit-cast the whole vector: clang bit-casts an ext-vector element access
 // from the vector's first element)
 __device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t off) {
-  const f32x4 v = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+  const f32x4 v =
+      __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream));
   return float4{v[0], v[1], v[2], v[3]};
 }
 __device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t off) {
@@ -203,16 +208,18 @@ struct Cfg {
   static_assert(WAVE_BYTES % 16 == 0 && A_BYTES % 16 == 0, "b128 LDS accesses need 16-byte alignment");
 };
 
-// occupancy target: exactly two waves per SIMD (one for 8 heads), so the
-// register allocator keeps the in-flight tile in registers instead of spilling
+// register budget of the occupancy target: one wave per SIMD for 8 heads, the
+// three-wave budget for one head at 2 bits (it fits without spilling and
+// measured fastest), two waves otherwise.  Blocks of 8 waves still place two
+// per SIMD.
 template <int BITS, int R>
-constexpr int waves_per_eu() { return R >= 8 ? 1 : 2; }
+constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS == 2 && R == 1) ? 3 : 2); }
 
-// tiles of loads in flight per wave: two where the register budget of the
-// occupancy target holds a second set, else one
+// tiles of loads in flight per wave: one (a second register set measured no
+// faster at two waves per SIMD), two for 8 heads at one wave per SIMD
 template <int BITS, int R>
 constexpr int prefetch_depth() {
-  return (R >= 8 || (BITS == 2 && R <= 2) || (BITS == 4 && R == 1)) ? 2 : 1;
+  return R >= 8 ? 2 : 1;
 }
 
 template <int BITS, int R, int NW>
