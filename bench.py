@@ -5,15 +5,18 @@ A step is one decode step of one attention layer of the Llama-2-7B-shaped
 workload (batch 8, 32 heads, head_dim 128, 2-bit codes, G = 32, R = 128,
 context 4096 at the start of the timed region): append the new token's K/V
 (quantizing the full residual into the grouped part when it is full), then
-decode attention for every query head.  Steps rotate over `--layers`
+decode attention for every query head, as one kivi_append_decode_attn call
+(the append is folded into the decode launch; `--separate` times
+kivi_append + kivi_decode_attn instead).  Steps rotate over `--layers`
 independent layer caches (8 by default, 1.2 GB in total) so that no step finds
 its cache resident in the 256 MB Infinity Cache left by the previous step;
 each layer starts with a full residual, so with 1024 steps every layer flushes
 once per 128 appends, the method's own rate.
 
 Prints one JSON line: whole-step algorithmic HBM GB/s (value), query-heads/s,
-the roofline of the dominant kernel (decode attention, timed with HIP events
-on the launch stream) and the CPU oracle timed on a bounded sample.
+the roofline of the dominant kernel (decode attention with the folded append,
+timed with HIP events on the launch stream around each call) and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -183,6 +186,8 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_b8_ctx4096")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--separate", action="store_true",
+                    help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -268,25 +273,31 @@ def main():
            for c in caches]
     scale = float(w.softmax_scale)
     append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
+    fused_fn = L.kivi_append_decode_attn
 
     def step(i, ev=None):
         li = i % NL
         c = caches[li].c
         j = i % n_tok
         flush = c.tr == R
-        rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
-        if rc:
-            raise RuntimeError(f"kivi_append failed: {rc}")
-        tq, tr = c.tq, c.tr
-        if ev is not None:
-            ev[0].record()
-        rc = decode_fn(crefs[li], qptr[j], scale, optr[li], wsp[li][0], wsp[li][1], args.splits,
-                       stream)
+        if args.separate:
+            rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
+            if rc:
+                raise RuntimeError(f"kivi_append failed: {rc}")
+            if ev is not None:
+                ev[0].record()
+            rc = decode_fn(crefs[li], qptr[j], scale, optr[li], wsp[li][0], wsp[li][1],
+                           args.splits, stream)
+        else:
+            if ev is not None:
+                ev[0].record()
+            rc = fused_fn(crefs[li], kptr[j], vptr[j], qptr[j], scale, optr[li], wsp[li][0],
+                          wsp[li][1], args.splits, stream)
         if ev is not None:
             ev[1].record()
         if rc:
-            raise RuntimeError(f"kivi_decode_attn failed: {rc}")
-        return flush, tq, tr
+            raise RuntimeError(f"decode step failed: {rc}")
+        return flush, c.tq, c.tr
 
     for i in range(args.warmup):
         step(i)
@@ -308,9 +319,16 @@ def main():
     dec_bytes = [decode_bytes(B, H, r, D, bits, G, tq, tr) for _, tq, tr in meta]
     app_bytes = [append_bytes(B, H, D, bits, G, R, f) for f, _, _ in meta]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
-    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
+    # The timed call is the decode launch, carrying the new token's append when
+    # fused.  Flush steps (a full residual quantized first: 1 in R steps per
+    # layer) also run the quantize launches inside the timed interval, so the
+    # roofline of the decode kernel averages the other steps only.
+    plain = [not f for f, _, _ in meta]
+    new_tok = append_bytes(B, H, D, bits, G, R, False)
+    call_bytes = np.array([d + (0 if args.separate else new_tok) for d in dec_bytes])[plain]
+    dec_ms = np.array([a.elapsed_time(b) for a, b in events])[plain]
     value = total_bytes / elapsed / 1e9
-    achieved = (sum(dec_bytes) / len(dec_bytes)) / (dec_ms.mean() * 1e-3) / 1e9
+    achieved = call_bytes.mean() / (dec_ms.mean() * 1e-3) / 1e9
     n_flush = sum(1 for f, _, _ in meta if f)
 
     result = {
@@ -330,19 +348,24 @@ def main():
             "workload": w.name, "batch": B, "q_heads": H * r, "kv_heads": H, "head_dim": D,
             "context_at_start": w.context, "bits": bits, "group": G, "residual": R,
             "layers_rotated": NL, "decode_splits": splits_used,
+            "step_call": "kivi_append + kivi_decode_attn" if args.separate else
+                         "kivi_append_decode_attn",
             "flushes_in_timed_region": n_flush,
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "query_heads_per_s": round(args.steps * B * H * r / elapsed, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "kivi decode attention (one kivi_decode_attn call)",
+            "kernel": ("kivi decode attention (one kivi_decode_attn call)" if args.separate else
+                       "kivi decode attention with the append folded in (one "
+                       "kivi_append_decode_attn call); flush steps excluded"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(w.name),
-            "bytes_per_launch": int(sum(dec_bytes) / len(dec_bytes)),
+            "bytes_per_launch": int(call_bytes.mean()),
+            "launches_averaged": int(len(call_bytes)),
             "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 3),
             "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
             "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),

@@ -176,6 +176,23 @@ int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q,
                      size_t workspace_bytes, int32_t num_splits,
                      void* stream);
 
+/* One decode step of a layer in one call: exactly kivi_append(cache, k_new,
+ * v_new) followed by kivi_decode_attn(cache, q, ...) (study.space summary:
+ * tokens are appended along the token axis, then attention reads the grouped
+ * and residual parts), with the same results, bit for bit, and the same
+ * errors, all checked before anything is enqueued (on error nothing is
+ * enqueued and *cache is unchanged).  Where the matrix-core decode kernel
+ * applies (head_dim 128, group 32, gqa_ratio 1, 2, 4 or 8) the append is
+ * folded into that kernel: the new token is read from k_new / v_new directly
+ * and written into its residual slot by the same launch, saving the separate
+ * copy launch.  A full residual is still flushed first, as by kivi_append.
+ * The workspace must cover the split count of the post-append lengths. */
+int kivi_append_decode_attn(kivi_cache* cache, const uint16_t* k_new,
+                            const uint16_t* v_new, const uint16_t* q,
+                            float softmax_scale, uint16_t* out,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream);
+
 /* Short static description of a status code. */
 const char* kivi_strerror(int status);
 

@@ -57,6 +57,8 @@ PROTOTYPES = {
     "kivi_decode_auto_splits": (ctypes.c_int, [_CP]),
     "kivi_decode_workspace_bytes": (ctypes.c_size_t, [_SHP, _i32]),
     "kivi_decode_attn": (ctypes.c_int, [_CP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
+    "kivi_append_decode_attn": (ctypes.c_int, [_CP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz,
+                                               _i32, _vp]),
     "kivi_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -108,4 +110,5 @@ kivi_append = _fn("kivi_append")
 kivi_decode_auto_splits = _fn("kivi_decode_auto_splits")
 kivi_decode_workspace_bytes = _fn("kivi_decode_workspace_bytes")
 kivi_decode_attn = _fn("kivi_decode_attn")
+kivi_append_decode_attn = _fn("kivi_append_decode_attn")
 kivi_strerror = _fn("kivi_strerror")

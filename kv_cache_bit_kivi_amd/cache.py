@@ -102,6 +102,23 @@ class KiviCache:
               "kivi_decode_attn")
         return out
 
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      softmax_scale: float, out: torch.Tensor | None = None,
+                      num_splits: int = 0) -> torch.Tensor:
+        """append(k_new, v_new) then decode(q) in one C call (one launch where
+        the matrix-core kernel applies)."""
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_append_decode_attn(ctypes.byref(self.c), k_new.data_ptr(),
+                                           v_new.data_ptr(), q.data_ptr(), float(softmax_scale),
+                                           out.data_ptr(), _ptr(ws), nb, num_splits, _stream()),
+              "kivi_append_decode_attn")
+        return out
+
     def auto_splits(self) -> int:
         s = _lib.kivi_decode_auto_splits(ctypes.byref(self.c))
         if s < 0:

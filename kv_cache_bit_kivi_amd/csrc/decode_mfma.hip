@@ -149,6 +149,24 @@ __device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t off) {
       __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream));
   return float4{v[0], v[1], v[2], v[3]};
 }
+__device__ __forceinline__ u32x4 ld16v(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream);
+}
+// one 16-byte slice of residual token t: from the residual plane (zeros past
+// the slice), or from the new-token row when t is the freshly appended token.
+// The two arms are exec-masked loads into one register: one load per lane.
+__device__ __forceinline__ u32x4 ld_res(rsrc_t res, rsrc_t nw, int t, int t_end, int t_new,
+                                        uint32_t row_bytes, uint32_t col) {
+  u32x4 v;
+  if (t != t_new)
+    v = ld16v(res, t < t_end ? (uint32_t)t * row_bytes + col : kOut);
+  else
+    v = ld16v(nw, col);
+  return v;
+}
+__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 __device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t off) {
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
   return uint2{v.x, v.y};
@@ -262,6 +280,11 @@ decode_mfma_kernel(DecodeArgs a) {
   const rsrc_t r_vz = make_rsrc(a.v_zero + plane * cap * kNG, (uint32_t)(cap * kNG * 4));
   const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
   const rsrc_t r_vr = make_rsrc(a.v_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
+  // fused append: the new token (residual slot t_new) comes from its input row
+  const bool fused = a.k_new != nullptr;
+  const int t_new = fused ? tr - 1 : -1;
+  const rsrc_t r_kn = make_rsrc(fused ? a.k_new + plane * kD : a.k_res, fused ? kD * 2 : 0);
+  const rsrc_t r_vn = make_rsrc(fused ? a.v_new + plane * kD : a.v_res, fused ? kD * 2 : 0);
   const size_t qrow0 = (size_t)b * H * R + (size_t)(u % H) * R;
   const rsrc_t r_q = make_rsrc(a.q + qrow0 * kD, (uint32_t)(R * kD * 2));
 
@@ -360,25 +383,22 @@ decode_mfma_kernel(DecodeArgs a) {
   // residual slice, 16 tokens per batch.  Key lanes: token n16 of the batch,
   // channels 8*kg + 32*i .. +7 (MFMA B operand); value lanes: token group
   // tg = lane/16 (tokens tg, tg+4, tg+8, tg+12), channels 8*c8 .. 8*c8+7.
-  // Tokens past the slice read zeros and weigh zero.
+  // Tokens past the slice read zeros and weigh zero.  Under a fused append
+  // every lane loads from both the residual and the new-token row, one of the
+  // two offsets out of range, and ORs the results (no per-lane branch).
   const int tg = lane >> 4, c8 = lane & 15;
-  half8 rk0, rk1, rk2, rk3;
-  uint4 rv0, rv1, rv2, rv3;
+  u32x4 rk0, rk1, rk2, rk3;   // key rows (8 fp16 each, MFMA B operand)
+  u32x4 rv0, rv1, rv2, rv3;   // value rows (8 fp16 each)
   auto load_res = [&](int t16) __attribute__((always_inline)) {
-    const int tk = t16 + n16;
-    const uint32_t ko = tk < r_end ? (uint32_t)(tk * kD * 2 + kg * 16) : kOut;
-    rk0 = __builtin_bit_cast(half8, ld16(r_kr, ko));
-    rk1 = __builtin_bit_cast(half8, ld16(r_kr, ko + 64));
-    rk2 = __builtin_bit_cast(half8, ld16(r_kr, ko + 128));
-    rk3 = __builtin_bit_cast(half8, ld16(r_kr, ko + 192));
-    auto vo = [&](int ti) {
-      const int tv = t16 + ti;
-      return tv < r_end ? (uint32_t)(tv * kD * 2 + c8 * 16) : kOut;
-    };
-    rv0 = ld16(r_vr, vo(tg));
-    rv1 = ld16(r_vr, vo(tg + 4));
-    rv2 = ld16(r_vr, vo(tg + 8));
-    rv3 = ld16(r_vr, vo(tg + 12));
+    const uint32_t rb = kD * 2;
+    rk0 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16);
+    rk1 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 64);
+    rk2 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 128);
+    rk3 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 192);
+    rv0 = ld_res(r_vr, r_vn, t16 + tg, r_end, t_new, rb, c8 * 16);
+    rv1 = ld_res(r_vr, r_vn, t16 + tg + 4, r_end, t_new, rb, c8 * 16);
+    rv2 = ld_res(r_vr, r_vn, t16 + tg + 8, r_end, t_new, rb, c8 * 16);
+    rv3 = ld_res(r_vr, r_vn, t16 + tg + 12, r_end, t_new, rb, c8 * 16);
   };
   load_res(r_begin);
   __builtin_amdgcn_sched_barrier(0);
@@ -597,10 +617,10 @@ decode_mfma_kernel(DecodeArgs a) {
   auto res_batch = [&](int t16) __attribute__((always_inline)) {
     const int n = min(16, r_end - t16);
     float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-    acc = mfma(ar[0], rk0, acc);
-    acc = mfma(ar[1], rk1, acc);
-    acc = mfma(ar[2], rk2, acc);
-    acc = mfma(ar[3], rk3, acc);
+    acc = mfma(ar[0], __builtin_bit_cast(half8, rk0), acc);
+    acc = mfma(ar[1], __builtin_bit_cast(half8, rk1), acc);
+    acc = mfma(ar[2], __builtin_bit_cast(half8, rk2), acc);
+    acc = mfma(ar[3], __builtin_bit_cast(half8, rk3), acc);
     {
       const bool ok = n16 < n;
       float* p0 = ok ? sc_addr(0, n16) : lds_dummy + n16;
@@ -610,12 +630,12 @@ decode_mfma_kernel(DecodeArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
     rescale(n);
-    const uint4 vv[4] = {rv0, rv1, rv2, rv3};
+    const u32x4 vv[4] = {rv0, rv1, rv2, rv3};
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const int ti = tg + 4 * i;
       const bool ok = ti < n;
-      const uint32_t w4[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+      const uint32_t w4[4] = {vv[i][0], vv[i][1], vv[i][2], vv[i][3]};
       float v[8];
 #pragma unroll
       for (int e = 0; e < 4; e++) {
@@ -655,11 +675,38 @@ decode_mfma_kernel(DecodeArgs a) {
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int i = 0; i < 4; i++) ar[i] = *reinterpret_cast<const half8*>(res_rd + i * ROWS * 64);
+  // fused append: the lanes holding the new token store it into its residual
+  // slot (one wave of one split per plane; no load in this launch reads the
+  // slot, the token itself came from its input row)
+  auto write_new = [&](int t16) __attribute__((always_inline)) {
+    const int dn = t_new - t16;
+    if (dn < 0 || dn >= 16) return;           // uniform: this batch lacks it
+    const uint32_t row = (uint32_t)t_new * kD * 2;
+    if (n16 == dn) {
+      const uint32_t o = row + kg * 16;
+      st16(r_kr, o, rk0);
+      st16(r_kr, o + 64, rk1);
+      st16(r_kr, o + 128, rk2);
+      st16(r_kr, o + 192, rk3);
+    }
+    if (tg == (dn & 3)) {
+      // i = dn / 4 is uniform: plain branches (a value select here would
+      // become a pointer select over the captured registers)
+      const uint32_t o = row + c8 * 16;
+      const int i = dn >> 2;
+      if (i == 0) st16(r_vr, o, rv0);
+      else if (i == 1) st16(r_vr, o, rv1);
+      else if (i == 2) st16(r_vr, o, rv2);
+      else st16(r_vr, o, rv3);
+    }
+  };
   res_batch(r_begin);
+  if (fused) write_new(r_begin);
   // slices longer than one batch (short contexts, few splits) load the rest here
   for (int t16 = r_begin + 16; t16 < r_end; t16 += 16) {
     load_res(t16);
     res_batch(t16);
+    if (fused) write_new(t16);
   }
 
   // ---------------- quantized tiles, DEPTH tiles of loads in flight

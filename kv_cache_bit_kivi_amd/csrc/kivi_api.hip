@@ -256,66 +256,124 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* s, int32_t num_splits) {
   return ws_bytes(*s, num_splits == 0 ? max_auto_splits(*s) : num_splits);
 }
 
+// Checks a decode at lengths (tq, tr) and fills the launch arguments; no HIP
+// call except the (cached) compute-unit count.
+static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q,
+                          float softmax_scale, uint16_t* out, void* workspace,
+                          size_t workspace_bytes, int32_t num_splits, DecodeArgs* a) {
+  if (!q || !out) return KIVI_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
+  if (num_splits < 0) return KIVI_EINVAL;
+  const kivi_shape& s = c->shape;
+  const int L = tq + tr;
+  if (L < 1) return KIVI_ESHAPE;
+  if (num_splits > 0 && num_splits > L) return KIVI_ESHAPE;
+  int S = num_splits;
+  if (S == 0) {
+    const int cus = device_cu_count();
+    if (cus < 0) return KIVI_EHIP;
+    S = auto_splits(s, tq, tr, cus);
+  }
+  if (S > 1) {
+    if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
+    if (!workspace) return KIVI_EINVAL;
+    if (!aligned16(workspace)) return KIVI_EALIGN;
+  }
+  a->k_codes = c->k_codes;
+  a->k_scale = c->k_scale;
+  a->k_zero = c->k_zero;
+  a->v_codes = c->v_codes;
+  a->v_scale = c->v_scale;
+  a->v_zero = c->v_zero;
+  a->k_res = c->k_res;
+  a->v_res = c->v_res;
+  a->k_new = nullptr;
+  a->v_new = nullptr;
+  a->q = q;
+  a->out = out;
+  a->ws = static_cast<float*>(workspace);
+  a->B = s.batch;
+  a->H = s.num_kv_heads;
+  a->r = s.gqa_ratio;
+  a->D = s.head_dim;
+  a->bits = s.bits;
+  a->G = s.group;
+  a->R = s.residual;
+  a->cap = s.capacity;
+  a->tq = tq;
+  a->tr = tr;
+  a->S = S;
+  a->scale = softmax_scale;
+  return KIVI_OK;
+}
+
+static int enqueue_decode(const kivi_shape& s, const DecodeArgs& a, hipStream_t st) {
+  hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
+                             : kivi::launch_decode_generic(a, st);
+  if (e != hipSuccess) return KIVI_EHIP;
+  if (a.S > 1) {
+    e = kivi::launch_combine(a, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+  }
+  return KIVI_OK;
+}
+
 int kivi_decode_attn(const kivi_cache* c, const uint16_t* q, float softmax_scale, uint16_t* out,
                      void* workspace, size_t workspace_bytes, int32_t num_splits,
                      void* stream) {
   int rc = check_cache(c);
   if (rc) return rc;
-  if (!q || !out) return KIVI_EINVAL;
-  if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
-  if (num_splits < 0) return KIVI_EINVAL;
-  const kivi_shape& s = c->shape;
-  const int L = c->tq + c->tr;
-  if (L < 1) return KIVI_ESHAPE;
-  if (num_splits > 0 && num_splits > L) return KIVI_ESHAPE;
-  if (num_splits > 1) {
-    if (workspace_bytes < ws_bytes(s, num_splits)) return KIVI_EWORKSPACE;
-    if (!workspace) return KIVI_EINVAL;
-    if (!aligned16(workspace)) return KIVI_EALIGN;
-  }
-  int S = num_splits;
-  if (S == 0) {
-    const int cus = device_cu_count();
-    if (cus < 0) return KIVI_EHIP;
-    S = auto_splits(s, c->tq, c->tr, cus);
-    if (S > 1) {
-      if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
-      if (!workspace) return KIVI_EINVAL;
-      if (!aligned16(workspace)) return KIVI_EALIGN;
-    }
-  }
   DecodeArgs a;
-  a.k_codes = c->k_codes;
-  a.k_scale = c->k_scale;
-  a.k_zero = c->k_zero;
-  a.v_codes = c->v_codes;
-  a.v_scale = c->v_scale;
-  a.v_zero = c->v_zero;
-  a.k_res = c->k_res;
-  a.v_res = c->v_res;
-  a.q = q;
-  a.out = out;
-  a.ws = static_cast<float*>(workspace);
-  a.B = s.batch;
-  a.H = s.num_kv_heads;
-  a.r = s.gqa_ratio;
-  a.D = s.head_dim;
-  a.bits = s.bits;
-  a.G = s.group;
-  a.R = s.residual;
-  a.cap = s.capacity;
-  a.tq = c->tq;
-  a.tr = c->tr;
-  a.S = S;
-  a.scale = softmax_scale;
+  rc = prepare_decode(c, c->tq, c->tr, q, softmax_scale, out, workspace, workspace_bytes,
+                      num_splits, &a);
+  if (rc) return rc;
+  return enqueue_decode(c->shape, a, (hipStream_t)stream);
+}
+
+int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                            const uint16_t* q, float softmax_scale, uint16_t* out,
+                            void* workspace, size_t workspace_bytes, int32_t num_splits,
+                            void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  // lengths after the append (a full residual is flushed first)
+  const bool flush = c->tr == s.residual;
+  if (flush && (int64_t)c->tq + s.residual > s.capacity) return KIVI_ECAPACITY;
+  const int tq = c->tq + (flush ? s.residual : 0);
+  const int slot = flush ? 0 : c->tr;     // residual slot of the new token
+  DecodeArgs a;
+  rc = prepare_decode(c, tq, slot + 1, q, softmax_scale, out, workspace, workspace_bytes,
+                      num_splits, &a);
+  if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
-                             : kivi::launch_decode_generic(a, st);
-  if (e != hipSuccess) return KIVI_EHIP;
-  if (S > 1) {
-    e = kivi::launch_combine(a, st);
+  if (flush) {
+    hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
+                                           s.bits, s.group, s.capacity, s.residual, s.residual,
+                                           c->tq, c->k_codes, c->k_scale, c->k_zero, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+    e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
+                                s.capacity, s.residual, s.residual, c->tq, c->v_codes,
+                                c->v_scale, c->v_zero, st);
     if (e != hipSuccess) return KIVI_EHIP;
   }
+  if (use_mfma(s)) {
+    // the decode kernel reads the new token from its input rows and writes it
+    // into the residual slot itself
+    a.k_new = k_new;
+    a.v_new = v_new;
+  } else {
+    hipError_t e = kivi::launch_copy_tokens(k_new, v_new, 1, 0, c->k_res, c->v_res,
+                                            s.residual, slot, 1, s.batch, s.num_kv_heads,
+                                            s.head_dim, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+  }
+  rc = enqueue_decode(s, a, st);
+  if (rc) return rc;
+  c->tq = tq;
+  c->tr = slot + 1;
   return KIVI_OK;
 }
 

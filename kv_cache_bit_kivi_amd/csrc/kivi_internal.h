@@ -18,6 +18,10 @@ struct DecodeArgs {
   const float* v_zero;
   const uint16_t* k_res;
   const uint16_t* v_res;
+  // fused append: the token in residual slot tr - 1 is read from these rows
+  // ([B][Hkv][D]) and written into the residual by the kernel; null otherwise
+  const uint16_t* k_new;
+  const uint16_t* v_new;
   const uint16_t* q;
   uint16_t* out;
   float* ws;          // split partials: m, l [rows][S], o [rows][S][D]

@@ -160,3 +160,26 @@ def test_workspace_bytes():
     assert ws(ctypes.byref(s), 4) == rows * 4 * (128 + 2) * 4
     assert ws(ctypes.byref(s), 0) >= ws(ctypes.byref(s), 4)
     assert ws(ctypes.byref(shape(bits=5)), 4) == 0
+
+
+def test_append_decode_errors_leave_state():
+    """The fused step checks the append's and the (post-append) decode's
+    conditions before enqueueing anything."""
+    ad = _lib.kivi_append_decode_attn
+    c = cache(tq=416, tr=128)          # the flush would end at 544 > capacity 512
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_ECAPACITY
+    assert (c.tq, c.tr) == (416, 128)
+    c = cache(tq=64, tr=3)
+    assert ad(ctypes.byref(c), None, P, P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert ad(ctypes.byref(c), P, P + 4, P, 0.1, P, None, 0, 1, None) == KIVI_EALIGN
+    assert ad(ctypes.byref(c), P, P, None, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P + 2, None, 0, 1, None) == KIVI_EALIGN
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, -1, None) == KIVI_EINVAL
+    # 64 + 4 tokens after the append: 68 splits are allowed, 69 are not
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 69, None) == KIVI_ESHAPE
+    need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4)
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, need, 4, None) == KIVI_EINVAL
+    assert (c.tq, c.tr) == (64, 3)
+    c = cache(ptrs=[P] * 7 + [0])
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL

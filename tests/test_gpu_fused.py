@@ -1,0 +1,101 @@
+"""The fused step kivi_append_decode_attn against the two separate calls
+kivi_append + kivi_decode_attn: identical fp16 output and identical cache
+buffers, bit for bit, at every step (through flushes, for several split
+counts, both bit widths, GQA ratios 1/2/4/8 and a shape outside the
+matrix-core kernel), and the oracle's attention within the usual bar."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import synth
+from kv_cache_bit_kivi_amd.cache import KiviCache
+from tests.gpu_util import ATTN_TOL, announce, dev, host, require_gpu, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 0.0883883461356163
+
+CASES = [
+    # B, H, r, D, bits, G, R, tq0, tr0, steps, splits
+    (2, 3, 1, 128, 2, 32, 128, 256, 120, 12, 0),    # flush after 8 steps
+    (2, 2, 1, 128, 4, 32, 128, 192, 128, 3, 0),     # flush at the first step
+    (1, 2, 4, 128, 2, 32, 128, 512, 64, 4, 3),      # GQA, split-K
+    (1, 2, 2, 128, 2, 32, 32, 64, 30, 5, 2),        # short residual, flush at step 3
+    (1, 1, 8, 128, 4, 32, 128, 320, 0, 3, 1),       # empty residual before the first step
+    (2, 2, 1, 128, 2, 32, 128, 1024, 17, 3, 7),     # many splits, ragged residual
+    (1, 2, 2, 64, 2, 32, 64, 128, 63, 3, 0),        # head_dim 64: generic kernel path
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dr%dD%db%dG%dR%d_tq%d_tr%d_n%d_S%d" % c)
+def test_fused_equals_separate(case):
+    require_gpu()
+    B, H, r, D, bits, G, R, tq0, tr0, steps, S = case
+    announce(f"fused append+decode {case}")
+    seed = sum(case)
+    T = tq0 + tr0 + steps
+    k = synth.random_fp16(seed, (B, H, T, D), scale=2.0)
+    k[..., 3] *= np.float16(10)
+    v = synth.random_fp16(seed + 1, (B, H, T, D))
+    qs = synth.random_fp16(seed + 2, (steps, B, H * r, D))
+    cap = (T + R + 63) // 64 * 64
+    cap = (cap + G - 1) // G * G
+    sep = KiviCache(B, H, r, D, bits, G, R, cap)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap)
+    kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
+    sep.prefill(kd, vd, tq0)
+    fus.prefill(kd, vd, tq0)
+    oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap)
+    oc.prefill(k[:, :, : tq0 + tr0], v[:, :, : tq0 + tr0], tq0)
+    for i in range(steps):
+        t = tq0 + tr0 + i
+        kn, vn = np.ascontiguousarray(k[:, :, t]), np.ascontiguousarray(v[:, :, t])
+        q = dev(qs[i])
+        sep.append(dev(kn), dev(vn))
+        o_sep = host(sep.decode(q, SCALE, num_splits=S))
+        o_fus = host(fus.append_decode(dev(kn), dev(vn), q, SCALE, num_splits=S))
+        assert (fus.tq, fus.tr) == (sep.tq, sep.tr), i
+        assert np.array_equal(o_fus.view(np.uint16), o_sep.view(np.uint16)), f"step {i} output"
+        for name in ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero"):
+            a, b = host(getattr(fus, name)), host(getattr(sep, name))
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"step {i} {name}"
+        for name in ("k_res", "v_res"):
+            a = host(getattr(fus, name)).view(np.uint16)[:, :, : fus.tr]
+            b = host(getattr(sep, name)).view(np.uint16)[:, :, : sep.tr]
+            assert np.array_equal(a, b), f"step {i} {name}"
+        oc.append(kn, vn)
+        ref = oc.decode(np.ascontiguousarray(qs[i]), SCALE)
+        err = row_rel_err(o_fus.astype(np.float64), ref)
+        assert err <= ATTN_TOL, (i, err)
+
+
+def test_fused_bench_workload_steps():
+    """The batch-8 Llama-2-7B-shaped layer: one fused step from a full
+    residual (flush) and one plain step, against the separate calls."""
+    require_gpu()
+    w = synth.WORKLOADS["llama2_7b_b8_ctx4096"]
+    announce("fused append+decode llama2_7b_b8_ctx4096")
+    k, v = synth.kv(w)
+    cap = w.capacity(64)
+    sep = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap)
+    fus = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap)
+    kd, vd = dev(k), dev(v)
+    sep.prefill(kd, vd, w.tq)
+    fus.prefill(kd, vd, w.tq)
+    del kd, vd
+    for s in (1, 2):
+        kn, vn = synth.new_token(w, s)
+        q = dev(synth.query(w, s))
+        sep.append(dev(kn), dev(vn))
+        o_sep = host(sep.decode(q, w.softmax_scale))
+        o_fus = host(fus.append_decode(dev(kn), dev(vn), q, w.softmax_scale))
+        assert np.array_equal(o_fus.view(np.uint16), o_sep.view(np.uint16)), s
+        assert (fus.tq, fus.tr) == (sep.tq, sep.tr)
+        a = host(fus.k_res).view(np.uint16)[:, :, : fus.tr]
+        b = host(sep.k_res).view(np.uint16)[:, :, : sep.tr]
+        assert np.array_equal(a, b)
+        a = host(fus.v_res).view(np.uint16)[:, :, : fus.tr]
+        b = host(sep.v_res).view(np.uint16)[:, :, : sep.tr]
+        assert np.array_equal(a, b)
+    torch.cuda.synchronize()
