@@ -12,17 +12,22 @@
 //                                       Gamma = sum_t p_t * z_t
 // (sc = softmax scale * log2(e): scores live in the log2 domain, p = 2^(s-m)).
 //
-// Both contractions run on v_mfma_f32_16x16x32_f16.  Operand B is the codes,
-// converted exactly to fp16 (2-bit codes via the e2m1 convert with scale 2,
-// 4-bit codes via the e4m3 convert with scale 2^9).  Operand A is the factor
-// q' (or p'), split into fp16 hi + lo rows (round toward zero, then the
-// remainder) so the products keep about 20 significant bits:
-//   keys:   A = rows (head, hi|lo) x 32 channels, B = 32 channels x 16 tokens
-//   values: A = rows (head, hi|lo) x 32 tokens,   B = 32 tokens x 16 channels
+// Both contractions run on 16x16x32 MFMAs.  Operand B is the codes, converted
+// exactly (2-bit codes via the e2m1 convert with scale 2, 4-bit codes via the
+// e4m3 convert with scale 2^9).  Operand A is the factor q' (or p'), split
+// into hi + lo rows so the products keep at least 16 significant bits:
+//   keys (fp16):   A = rows (head, hi|lo) x 32 channels, B = 32 channels x 16
+//                  tokens; hi = q' rounded toward zero, lo = the remainder.
+//                  The query is normalised per wave by a power of two so that
+//                  |q'| < 2^16 and the fp16 hi part never overflows.
+//   values (bf16): A = rows (head, hi|lo) x 32 tokens, B = 32 tokens x 16
+//                  channels; hi = p' truncated to bf16, lo = the remainder.
+//                  bf16 keeps binary32's exponent range, so p' needs no
+//                  normalisation however small or large the value scales are.
 // The 8 K-slots a lane supplies map to code positions in the order the
 // converts produce them (k_pos / v_pos); A is written to LDS in that order.
-// The query is normalised per wave by a power of two so that |q'| < 2^16 and
-// the fp16 hi part never overflows; scores are scaled back after the MFMA.
+// The online-softmax reference moves only when a score exceeds it by more
+// than 2^8 (p <= 256), so the accumulators are rarely rescaled.
 // Residual keys (fp16) feed the MFMA directly; residual values use the VALU.
 //
 // Work: one block of NW waves per (b*Hkv + h, split).  Each wave owns a
@@ -47,6 +52,8 @@ namespace kivi {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __fp16 hrtz2 __attribute__((ext_vector_type(2)));
 typedef float float4v __attribute__((ext_vector_type(4)));
@@ -56,6 +63,7 @@ constexpr int kG = 32;
 constexpr int kNG = kD / kG;   // value groups per token
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;   // log2 slack of the online-softmax reference
 
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
@@ -109,8 +117,38 @@ __device__ __forceinline__ half8 cvt_word4(uint32_t w) {
   half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
   return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
+// the same two code converts to bf16 (value side)
+__device__ __forceinline__ bf16x8 cvt_nib2_bf(uint32_t x) {
+  bf16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 0);
+  bf16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 1);
+  bf16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 2);
+  bf16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 3);
+  return bf16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+__device__ __forceinline__ bf16x8 cvt_word4_bf(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
+  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
+}
 __device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ float4v mfma_bf(bf16x8 a, bf16x8 b, float4v c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// (hi, lo) bf16 pairs of two binary32 values: hi = x truncated to bf16, lo =
+// the remainder truncated; hi + lo = x within 2^-16 |x|, over the full
+// binary32 exponent range.  Lane 0 of each pair holds x0, lane 1 x1.
+__device__ __forceinline__ void split2_bf(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  const uint32_t u0 = __builtin_bit_cast(uint32_t, x0), u1 = __builtin_bit_cast(uint32_t, x1);
+  const float r0 = x0 - __builtin_bit_cast(float, u0 & 0xFFFF0000u);
+  const float r1 = x1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // upper halves of u0, u1
+  lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0),
+                             0x07060302u);
 }
 // (hi, lo) fp16 pairs of two binary32 values: hi = x rounded toward zero,
 // lo = the remainder rounded toward zero; hi + lo = x within 2^-20 |x|
@@ -470,16 +508,19 @@ decode_mfma_kernel(DecodeArgs a) {
   };
 
   // new maximum over the ntok scores in LDS -> rescale every running quantity
-  auto rescale = [&](int ntok) __attribute__((always_inline)) {
+  // new running maximum of each head -> rescale every running quantity
+  auto apply_max = [&](const float (&mxs)[R]) __attribute__((always_inline)) {
     float alpha[R];
     bool any = false;
 #pragma unroll
     for (int h = 0; h < R; h++) {
-      const float mx = wave_max(lane < ntok ? lds_sc[h * CH + lane] : -INFINITY);
-      const float m_new = fmaxf(m_run[h], mx);
-      // a head still without any finite score keeps factor 1 (-inf - -inf)
-      alpha[h] = m_new == -INFINITY ? 1.f : fast_exp2(m_run[h] - m_new);
-      any |= m_new != m_run[h];
+      // lazy reference: move it only when a score exceeds it by more than
+      // 2^kLazy (p stays <= 2^kLazy; fine for the fp32 sums and the bf16 P.V
+      // operand); a head without any finite score keeps -inf
+      const bool grow = mxs[h] > m_run[h] + kLazy;
+      const float m_new = grow ? mxs[h] : m_run[h];
+      alpha[h] = grow ? fast_exp2(m_run[h] - m_new) : 1.f;
+      any |= grow;
       m_run[h] = m_new;
     }
     if (any) {
@@ -501,6 +542,13 @@ decode_mfma_kernel(DecodeArgs a) {
         cv[nb][3] *= a1;
       }
     }
+  };
+  // maximum over the ntok scores in LDS (residual batches)
+  auto rescale = [&](int ntok) __attribute__((always_inline)) {
+    float mxs[R];
+#pragma unroll
+    for (int h = 0; h < R; h++) mxs[h] = wave_max(lane < ntok ? lds_sc[h * CH + lane] : -INFINITY);
+    apply_max(mxs);
   };
 
   // ---------------- tile loads: NLD code loads + 4 metadata loads, 16 B each
@@ -535,6 +583,8 @@ decode_mfma_kernel(DecodeArgs a) {
     }
     __builtin_amdgcn_wave_barrier();
     const int ngr = half_tile ? 1 : 2;
+    // per-lane maxima of the scores this lane produces (heads 2kg, 2kg+1)
+    float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
     for (int g = 0; g < 2; g++) {
       if (g < ngr) {
@@ -561,13 +611,34 @@ decode_mfma_kernel(DecodeArgs a) {
             acc = mfma(af[3], cvt_word4(x.w), acc);
           }
           const int k = 16 * mb + n16;
-          *sc_addr(0, k) = (acc[0] + acc[1]) * qup + b0;
-          *sc_addr(1, k) = (acc[2] + acc[3]) * qup + b1;
+          const float s0 = (acc[0] + acc[1]) * qup + b0;
+          const float s1 = (acc[2] + acc[3]) * qup + b1;
+          *sc_addr(0, k) = s0;
+          *sc_addr(1, k) = s1;
+          mx0 = fmaxf(mx0, s0);
+          mx1 = fmaxf(mx1, s1);
         }
       }
     }
     __builtin_amdgcn_wave_barrier();
-    rescale(64);
+    // tile maximum per head straight from the MFMA output: reduce over the 16
+    // token lanes of each row (heads 2kg, 2kg+1 live in lane row kg)
+    {
+      mx0 = fmaxf(mx0, dpp<0x128>(mx0));
+      mx0 = fmaxf(mx0, dpp<0x124>(mx0));
+      mx0 = fmaxf(mx0, dpp<0x122>(mx0));
+      mx0 = fmaxf(mx0, dpp<0x121>(mx0));
+      if constexpr (R >= 2) {
+        mx1 = fmaxf(mx1, dpp<0x128>(mx1));
+        mx1 = fmaxf(mx1, dpp<0x124>(mx1));
+        mx1 = fmaxf(mx1, dpp<0x122>(mx1));
+        mx1 = fmaxf(mx1, dpp<0x121>(mx1));
+      }
+      float mxs[R];
+#pragma unroll
+      for (int h = 0; h < R; h++) mxs[h] = lane_read((h & 1) ? mx1 : mx0, 16 * (h >> 1));
+      apply_max(mxs);
+    }
     // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
     const bool valid = tile * 64 + lane < tq;
     const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
@@ -578,33 +649,37 @@ decode_mfma_kernel(DecodeArgs a) {
       const float p = valid ? fast_exp2(lds_sc[h * CH + lane] - m_run[h]) : 0.f;
       l_acc[h] += p;
 #pragma unroll
-      for (int j = 0; j < kNG; j++) {
-        gam[h][j] += p * vzv[j];
-        const float x = valid ? p * vsv[j] : 0.f;
-        const _Float16 hi = (_Float16)x;
-        const _Float16 lo = (_Float16)(x - (float)hi);
-        char* dst = lds_a + vwr + (uint32_t)(j * 2 * ROWS * 64);
-        *reinterpret_cast<_Float16*>(dst + (2 * h) * 64) = hi;
-        *reinterpret_cast<_Float16*>(dst + (2 * h + 1) * 64) = lo;
+      for (int j = 0; j < kNG; j++) gam[h][j] += p * vzv[j];
+      // hi/lo halves of p * s for the group pairs (0,1), (2,3), two at a time
+#pragma unroll
+      for (int jj = 0; jj < kNG; jj += 2) {
+        uint32_t hi, lo;
+        split2_bf(valid ? p * vsv[jj] : 0.f, valid ? p * vsv[jj + 1] : 0.f, hi, lo);
+        char* d0 = lds_a + vwr + (uint32_t)(jj * 2 * ROWS * 64);
+        char* d1 = d0 + 2 * ROWS * 64;
+        *reinterpret_cast<uint16_t*>(d0 + (2 * h) * 64) = (uint16_t)hi;
+        *reinterpret_cast<uint16_t*>(d1 + (2 * h) * 64) = (uint16_t)(hi >> 16);
+        *reinterpret_cast<uint16_t*>(d0 + (2 * h + 1) * 64) = (uint16_t)lo;
+        *reinterpret_cast<uint16_t*>(d1 + (2 * h + 1) * 64) = (uint16_t)(lo >> 16);
       }
     }
     __builtin_amdgcn_wave_barrier();
     const char* vstg = stg + C::KC_BYTES;
 #pragma unroll
     for (int j = 0; j < kNG; j++) {
-      const half8 av0 = *reinterpret_cast<const half8*>(a_rd + (j * 2 + 0) * ROWS * 64);
-      const half8 av1 = *reinterpret_cast<const half8*>(a_rd + (j * 2 + 1) * ROWS * 64);
+      const bf16x8 av0 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 0) * ROWS * 64);
+      const bf16x8 av1 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 1) * ROWS * 64);
 #pragma unroll
       for (int nbj = 0; nbj < 2; nbj++) {
         const int nb = 2 * j + nbj;
         if constexpr (BITS == 2) {
           const uint32_t x = *reinterpret_cast<const uint32_t*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 4);
-          cv[nb] = mfma(av0, cvt_nib2(x & 0x33333333u), cv[nb]);
-          cv[nb] = mfma(av1, cvt_nib2((x >> 2) & 0x33333333u), cv[nb]);
+          cv[nb] = mfma_bf(av0, cvt_nib2_bf(x & 0x33333333u), cv[nb]);
+          cv[nb] = mfma_bf(av1, cvt_nib2_bf((x >> 2) & 0x33333333u), cv[nb]);
         } else {
           const uint2 x = *reinterpret_cast<const uint2*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 8);
-          cv[nb] = mfma(av0, cvt_word4(x.x), cv[nb]);
-          cv[nb] = mfma(av1, cvt_word4(x.y), cv[nb]);
+          cv[nb] = mfma_bf(av0, cvt_word4_bf(x.x), cv[nb]);
+          cv[nb] = mfma_bf(av1, cvt_word4_bf(x.y), cv[nb]);
         }
       }
     }

@@ -17,14 +17,15 @@ from tests.gpu_util import ATTN_TOL, announce, dev, host, require_gpu, row_rel_e
 pytestmark = pytest.mark.gpu
 
 
-def build_pair(B, H, r, D, bits, G, R, tq, tr, seed, cap=None, k_scale=2.0):
+def build_pair(B, H, r, D, bits, G, R, tq, tr, seed, cap=None, k_scale=2.0, v_scale=1.0,
+               q_scale=1.0):
     L = tq + tr
     cap = cap or max(64, (tq + R + 63) // 64 * 64)
     cap = (cap + G - 1) // G * G
     k = synth.random_fp16(seed, (B, H, L, D), scale=k_scale)
     k[..., 5] *= np.float16(10)
-    v = synth.random_fp16(seed + 1, (B, H, L, D))
-    q = synth.random_fp16(seed + 2, (B, H * r, D))
+    v = synth.random_fp16(seed + 1, (B, H, L, D), scale=v_scale)
+    q = synth.random_fp16(seed + 2, (B, H * r, D), scale=q_scale)
     gc = KiviCache(B, H, r, D, bits, G, R, cap)
     gc.prefill(dev(k), dev(v), tq)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap)
@@ -151,3 +152,21 @@ def test_decode_long_context():
         ref = oc.decode(np.ascontiguousarray(q[:, h:h + 1]), w.softmax_scale)
         err = row_rel_err(out[:, h:h + 1], ref)
         assert err <= ATTN_TOL, (h, err)
+
+
+@pytest.mark.parametrize("v_scale", [1e-2, 1e-3, 1e3])
+@pytest.mark.parametrize("q_scale", [0.25, 3.0])
+@pytest.mark.parametrize("bits,r", [(2, 1), (4, 1), (2, 4)])
+def test_small_value_scales(v_scale, q_scale, bits, r):
+    """Value scales far from 1 (1e-2, 1e-3 and 1e3 times the keys' spread),
+    with flat (small q) and sharp (large q) attention: the P.V factor p * s
+    spans many binades, and with the lazy softmax reference p reaches 2^8, so
+    the factor must keep its relative precision without an fp16 range limit."""
+    require_gpu()
+    announce(f"decode small values v_scale={v_scale} q_scale={q_scale} bits={bits} r={r}")
+    gc, oc, q = build_pair(1, 2, r, 128, bits, 32, 128, 4032, 64, seed=77 + bits + r,
+                           v_scale=v_scale, q_scale=q_scale)
+    ref = oc.decode(q, 0.0883883461356163)
+    out = host(gc.decode(dev(q), 0.0883883461356163)).astype(np.float64)
+    err = row_rel_err(out, ref)
+    assert err <= ATTN_TOL, err
