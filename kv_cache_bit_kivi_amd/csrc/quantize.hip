@@ -45,6 +45,13 @@ __device__ __forceinline__ uint32_t encode(float x, float s, float z) {
   return (uint32_t)c;
 }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte copy with a non-temporal (read-once) source load
+__device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
+  *reinterpret_cast<u32x4_t*>(dst) =
+      __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
+}
+
 // One block per (group of G source tokens, b*H + h).
 template <int BITS>
 __global__ void __launch_bounds__(256)
@@ -59,7 +66,7 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
   const size_t bh = blockIdx.y;
   const uint4* src = reinterpret_cast<const uint4*>(k + (bh * in_stride + (size_t)g * G) * D);
   for (int i = threadIdx.x; i < G * D / 8; i += blockDim.x)
-    reinterpret_cast<uint4*>(tile)[i] = src[i];
+    copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
   __syncthreads();
 
   const size_t gg = (size_t)(dst_off / G + g);
@@ -111,7 +118,7 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
   const size_t bh = blockIdx.y;
   const uint4* src = reinterpret_cast<const uint4*>(v + (bh * in_stride + (size_t)blk * 32) * D);
   for (int i = threadIdx.x; i < 32 * D / 8; i += blockDim.x)
-    reinterpret_cast<uint4*>(tile)[i] = src[i];
+    copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
   __syncthreads();
 
   const int t_base = dst_off + blk * 32;  // cache token of local token 0
@@ -165,8 +172,8 @@ copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restric
     const int t = i / per_tok, c = i % per_tok;
     const size_t so = ((bh * src_stride + t0 + t) * D) / 8 + c;
     const size_t dd = ((bh * dst_stride + slot0 + t) * D) / 8 + c;
-    reinterpret_cast<uint4*>(k_dst)[dd] = reinterpret_cast<const uint4*>(k_src)[so];
-    reinterpret_cast<uint4*>(v_dst)[dd] = reinterpret_cast<const uint4*>(v_src)[so];
+    copy16_nt(reinterpret_cast<uint4*>(k_dst) + dd, reinterpret_cast<const uint4*>(k_src) + so);
+    copy16_nt(reinterpret_cast<uint4*>(v_dst) + dd, reinterpret_cast<const uint4*>(v_src) + so);
   }
 }
 
