@@ -9,8 +9,10 @@ from .oracle import (  # noqa: F401
     OracleCache,
     build,
     decode_attn,
+    float_to_half,
     half_to_float,
     load,
+    meta_dtype,
     quantize_k,
     quantize_v,
 )

@@ -96,7 +96,54 @@ float kivio_half_to_float(uint16_t h) {
   return f;
 }
 
+/* ---- binary32 -> binary16, round to nearest even (IEEE 754) -------------- */
+uint16_t kivio_float_to_half(float f) {
+  uint32_t x;
+  memcpy(&x, &f, sizeof x);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t exp = (x >> 23) & 0xffu;
+  uint32_t man = x & 0x7fffffu;
+  if (exp == 0xffu) /* inf / nan (nan keeps a payload bit) */
+    return (uint16_t)(sign | 0x7c00u | (man ? 0x200u | (man >> 13) : 0u));
+  const int e = (int)exp - 127; /* unbiased exponent of a normal float */
+  if (exp == 0 || e < -25)      /* zero, float subnormal, or below half the
+                                   smallest half subnormal: rounds to 0 */
+    return (uint16_t)sign;
+  man |= 0x800000u; /* 24-bit significand */
+  if (e > 15) return (uint16_t)(sign | 0x7c00u); /* overflow -> inf */
+  /* keep 11 significant bits for a normal half (e >= -14), fewer for a
+     subnormal half; drop `shift` bits with round-half-even */
+  const int shift = e >= -14 ? 13 : 13 + (-14 - e);
+  uint32_t q = man >> shift;
+  const uint32_t rem = man & ((1u << shift) - 1);
+  const uint32_t half = 1u << (shift - 1);
+  if (rem > half || (rem == half && (q & 1u))) q++;
+  /* q is the significand in half units: normal halves carry the implicit bit
+     (value 0x400..0x800), subnormals do not; a carry into 0x800 bumps the
+     exponent, which the addition below does by itself */
+  uint32_t h;
+  if (e >= -14)
+    h = ((uint32_t)(e + 15) << 10) + (q - 0x400u);
+  else
+    h = q; /* subnormal (q may reach 0x400: the smallest normal) */
+  if (h >= 0x7c00u) return (uint16_t)(sign | 0x7c00u);
+  return (uint16_t)(sign | h);
+}
+
 static int words_per_row(int D, int bits) { return D * bits / 32; }
+
+/* metadata element m of a scale / zero array: binary32, or binary16 when
+ * meta_half (the variant with half-width scale and zero) */
+static double meta_get(const void* a, size_t m, int meta_half) {
+  if (meta_half) return (double)kivio_half_to_float(((const uint16_t*)a)[m]);
+  return (double)((const float*)a)[m];
+}
+static void meta_put(void* a, size_t m, float v, int meta_half) {
+  if (meta_half)
+    ((uint16_t*)a)[m] = kivio_float_to_half(v);
+  else
+    ((float*)a)[m] = v;
+}
 
 /* Quantize one group of n binary32 values (already widened from binary16).
  * Writes n codes and the group's scale and zero.  The order of operations is
@@ -141,9 +188,9 @@ static int check_common(int B, int H, int D, int bits, int G, int cap) {
 /* Key quantization, per channel over groups of G consecutive tokens
  * [KIVI-abs, KIVI-sum].  Source tokens [0, ntok) of k ([B][H][in_stride][D]
  * binary16) go to cache tokens [dst_off, dst_off + ntok). */
-int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap,
+int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap, int meta_half,
                      const uint16_t* k, int in_stride, int ntok, int dst_off,
-                     uint32_t* codes, float* scale, float* zero) {
+                     uint32_t* codes, void* scale, void* zero) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
@@ -157,8 +204,7 @@ int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap,
     for (int h = 0; h < H; h++) {
       const uint16_t* src = k + ((size_t)b * H + h) * (size_t)in_stride * D;
       uint32_t* cw = codes + ((size_t)b * H + h) * (size_t)cap * W;
-      float* sc = scale + ((size_t)b * H + h) * (size_t)(cap / G) * D;
-      float* zr = zero + ((size_t)b * H + h) * (size_t)(cap / G) * D;
+      const size_t mbase = ((size_t)b * H + h) * (size_t)(cap / G) * D;
       /* clear the destination rows, then OR codes in */
       for (int t = 0; t < ntok; t++)
         for (int w = 0; w < W; w++) cw[(size_t)(dst_off + t) * W + w] = 0;
@@ -169,8 +215,8 @@ int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap,
           float s, z;
           quantize_group(xs, G, bits, cs, &s, &z);
           int gg = (dst_off / G) + g;
-          sc[(size_t)gg * D + d] = s;
-          zr[(size_t)gg * D + d] = z;
+          meta_put(scale, mbase + (size_t)gg * D + d, s, meta_half);
+          meta_put(zero, mbase + (size_t)gg * D + d, z, meta_half);
           for (int i = 0; i < G; i++) {
             int t = dst_off + g * G + i;
             cw[(size_t)t * W + d / E] |= (uint32_t)cs[i] << (bits * (d % E));
@@ -189,9 +235,9 @@ static size_t v_word_index(int D, int bits, int t, int d) {
 /* Value quantization, per token over groups of G consecutive channels
  * [KIVI-abs]; quantized tokens are appended along the token axis
  * [KIVI-sum]. */
-int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap,
+int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_half,
                      const uint16_t* v, int in_stride, int ntok, int dst_off,
-                     uint32_t* codes, float* scale, float* zero) {
+                     uint32_t* codes, void* scale, void* zero) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
@@ -206,8 +252,7 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap,
     for (int h = 0; h < H; h++) {
       const uint16_t* src = v + ((size_t)b * H + h) * (size_t)in_stride * D;
       uint32_t* cw = codes + ((size_t)b * H + h) * plane_words;
-      float* sc = scale + ((size_t)b * H + h) * (size_t)cap * NG;
-      float* zr = zero + ((size_t)b * H + h) * (size_t)cap * NG;
+      const size_t mbase = ((size_t)b * H + h) * (size_t)cap * NG;
       for (int t = 0; t < ntok; t++)
         for (int d = 0; d < D; d++) cw[v_word_index(D, bits, dst_off + t, d)] = 0;
       for (int t = 0; t < ntok; t++)
@@ -217,8 +262,8 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap,
           float s, z;
           quantize_group(xs, G, bits, cs, &s, &z);
           int tt = dst_off + t;
-          sc[(size_t)tt * NG + j] = s;
-          zr[(size_t)tt * NG + j] = z;
+          meta_put(scale, mbase + (size_t)tt * NG + j, s, meta_half);
+          meta_put(zero, mbase + (size_t)tt * NG + j, z, meta_half);
           for (int i = 0; i < G; i++) {
             int d = j * G + i;
             cw[v_word_index(D, bits, tt, d)] |= (uint32_t)cs[i]
@@ -235,9 +280,9 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap,
  * and the residual already holds R tokens, all R are quantized into the
  * grouped part first (keys and values alike), then the new token is stored
  * in the residual.  *tq, *tr are updated only on success. */
-int kivio_append(int B, int H, int D, int bits, int G, int R, int cap,
-                 uint32_t* k_codes, float* ks, float* kz, uint32_t* v_codes,
-                 float* vs, float* vz, uint16_t* k_res, uint16_t* v_res,
+int kivio_append(int B, int H, int D, int bits, int G, int R, int cap, int meta_half,
+                 uint32_t* k_codes, void* ks, void* kz, uint32_t* v_codes,
+                 void* vs, void* vz, uint16_t* k_res, uint16_t* v_res,
                  const uint16_t* k_new, const uint16_t* v_new, int* tq,
                  int* tr) {
   int rc = check_common(B, H, D, bits, G, cap);
@@ -247,9 +292,9 @@ int kivio_append(int B, int H, int D, int bits, int G, int R, int cap,
   if (q < 0 || q % G || r < 0 || r > R) return KIVIO_ESHAPE;
   if (r == R) {
     if (q + R > cap) return KIVIO_ECAPACITY;
-    rc = kivio_quantize_k(B, H, D, bits, G, cap, k_res, R, R, q, k_codes, ks, kz);
+    rc = kivio_quantize_k(B, H, D, bits, G, cap, meta_half, k_res, R, R, q, k_codes, ks, kz);
     if (rc) return rc;
-    rc = kivio_quantize_v(B, H, D, bits, G, cap, v_res, R, R, q, v_codes, vs, vz);
+    rc = kivio_quantize_v(B, H, D, bits, G, cap, meta_half, v_res, R, R, q, v_codes, vs, vz);
     if (rc) return rc;
     q += R;
     r = 0;
@@ -268,30 +313,31 @@ int kivio_append(int B, int H, int D, int bits, int G, int R, int cap,
 }
 
 /* dequantized key / value of cache token t (< tq), channel d, in binary64 */
-static double dequant_k(const uint32_t* cw, const float* sc, const float* zr,
-                        int D, int bits, int G, int t, int d) {
+/* (sc, zr point at the plane's metadata; mb is the plane's element offset) */
+static double dequant_k(const uint32_t* cw, const void* sc, const void* zr, size_t mb,
+                        int meta_half, int D, int bits, int G, int t, int d) {
   const int E = 32 / bits, W = words_per_row(D, bits);
   uint32_t c = (cw[(size_t)t * W + d / E] >> (bits * (d % E))) & ((1u << bits) - 1);
-  size_t m = (size_t)(t / G) * D + d;
-  return (double)c * (double)sc[m] + (double)zr[m];
+  size_t m = mb + (size_t)(t / G) * D + d;
+  return (double)c * meta_get(sc, m, meta_half) + meta_get(zr, m, meta_half);
 }
 
-static double dequant_v(const uint32_t* cw, const float* sc, const float* zr,
-                        int D, int bits, int G, int t, int d) {
+static double dequant_v(const uint32_t* cw, const void* sc, const void* zr, size_t mb,
+                        int meta_half, int D, int bits, int G, int t, int d) {
   const int E = 32 / bits;
   uint32_t c = (cw[v_word_index(D, bits, t, d)] >> (bits * ((t % 64) % E))) &
                ((1u << bits) - 1);
-  size_t m = (size_t)t * (D / G) + d / G;
-  return (double)c * (double)sc[m] + (double)zr[m];
+  size_t m = mb + (size_t)t * (D / G) + d / G;
+  return (double)c * meta_get(sc, m, meta_half) + meta_get(zr, m, meta_half);
 }
 
 /* Decode attention over the mixed cache [KIVI-sum: scores on the grouped
  * part, then the residual part is combined with it], binary64 throughout.
  * q, out: [B][H*r][D].  Work space: 2*(tq+tr) doubles in `scratch`. */
 int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
-                      int cap, const uint32_t* k_codes, const float* ks,
-                      const float* kz, const uint32_t* v_codes,
-                      const float* vs, const float* vz, const uint16_t* k_res,
+                      int cap, int meta_half, const uint32_t* k_codes, const void* ks,
+                      const void* kz, const uint32_t* v_codes,
+                      const void* vs, const void* vz, const uint16_t* k_res,
                       const uint16_t* v_res, int tq, int tr, const uint16_t* q,
                       float softmax_scale, double* out, double* scratch) {
   int rc = check_common(B, H, D, bits, G, cap);
@@ -308,18 +354,16 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       const int h = hq / r;
       const size_t bh = (size_t)b * H + h;
       const uint32_t* kc = k_codes + bh * (size_t)cap * W;
-      const float* ksp = ks + bh * (size_t)(cap / G) * D;
-      const float* kzp = kz + bh * (size_t)(cap / G) * D;
+      const size_t kmb = bh * (size_t)(cap / G) * D;
       const uint32_t* vc = v_codes + bh * (size_t)cap * D / E;
-      const float* vsp = vs + bh * (size_t)cap * (D / G);
-      const float* vzp = vz + bh * (size_t)cap * (D / G);
+      const size_t vmb = bh * (size_t)cap * (D / G);
       const uint16_t* kr = k_res + bh * (size_t)R * D;
       const uint16_t* vr = v_res + bh * (size_t)R * D;
       const uint16_t* qv = q + ((size_t)b * Hq + hq) * D;
       for (int t = 0; t < L; t++) {
         double dot = 0.0;
         for (int d = 0; d < D; d++) {
-          double kv = (t < tq) ? dequant_k(kc, ksp, kzp, D, bits, G, t, d)
+          double kv = (t < tq) ? dequant_k(kc, ks, kz, kmb, meta_half, D, bits, G, t, d)
                                : (double)kivio_half_to_float(kr[(size_t)(t - tq) * D + d]);
           dot += (double)kivio_half_to_float(qv[d]) * kv;
         }
@@ -337,7 +381,7 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       for (int d = 0; d < D; d++) {
         double acc = 0.0;
         for (int t = 0; t < L; t++) {
-          double vv = (t < tq) ? dequant_v(vc, vsp, vzp, D, bits, G, t, d)
+          double vv = (t < tq) ? dequant_v(vc, vs, vz, vmb, meta_half, D, bits, G, t, d)
                                : (double)kivio_half_to_float(vr[(size_t)(t - tq) * D + d]);
           acc += p[t] * vv;
         }

@@ -26,6 +26,7 @@ _u32p = ctypes.POINTER(ctypes.c_uint32)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i32p = ctypes.POINTER(ctypes.c_int)
+_vp = ctypes.c_void_p
 _int = ctypes.c_int
 
 ERRORS = {0: "ok", 1: "EINVAL", 2: "ESHAPE", 3: "ECAPACITY"}
@@ -53,16 +54,18 @@ def load():
     lib = ctypes.CDLL(_LIB)
     lib.kivio_half_to_float.argtypes = [ctypes.c_uint16]
     lib.kivio_half_to_float.restype = ctypes.c_float
-    q_args = [_int] * 6 + [_u16p, _int, _int, _int, _u32p, _f32p, _f32p]
+    lib.kivio_float_to_half.argtypes = [ctypes.c_float]
+    lib.kivio_float_to_half.restype = ctypes.c_uint16
+    q_args = [_int] * 7 + [_u16p, _int, _int, _int, _u32p, _vp, _vp]
     lib.kivio_quantize_k.argtypes = q_args
     lib.kivio_quantize_v.argtypes = q_args
     lib.kivio_quantize_k.restype = _int
     lib.kivio_quantize_v.restype = _int
-    lib.kivio_append.argtypes = [_int] * 7 + [_u32p, _f32p, _f32p, _u32p, _f32p, _f32p,
+    lib.kivio_append.argtypes = [_int] * 8 + [_u32p, _vp, _vp, _u32p, _vp, _vp,
                                              _u16p, _u16p, _u16p, _u16p, _i32p, _i32p]
     lib.kivio_append.restype = _int
-    lib.kivio_decode_attn.argtypes = [_int] * 8 + [_u32p, _f32p, _f32p, _u32p, _f32p,
-                                                   _f32p, _u16p, _u16p, _int, _int, _u16p,
+    lib.kivio_decode_attn.argtypes = [_int] * 9 + [_u32p, _vp, _vp, _u32p, _vp,
+                                                   _vp, _u16p, _u16p, _int, _int, _u16p,
                                                    ctypes.c_float, _f64p, _f64p]
     lib.kivio_decode_attn.restype = _int
     _lib = lib
@@ -73,6 +76,17 @@ def _p(a: np.ndarray, ctype, dtype):
     assert a.dtype == dtype, (a.dtype, dtype)
     assert a.flags["C_CONTIGUOUS"]
     return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def _m(a: np.ndarray, meta_half: bool):
+    """Metadata array pointer: binary32, or binary16 bits (uint16) when meta_half."""
+    assert a.dtype == (np.uint16 if meta_half else np.float32), a.dtype
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_vp)
+
+
+def meta_dtype(meta_half: bool):
+    return np.uint16 if meta_half else np.float32
 
 
 def _h(a):  # binary16 bits, as uint16 (accepts float16 arrays too)
@@ -91,33 +105,42 @@ def half_to_float(bits: int) -> float:
     return float(load().kivio_half_to_float(int(bits)))
 
 
+def float_to_half(x: float) -> int:
+    """binary32 -> binary16 bits, round to nearest even (the oracle's own)."""
+    return int(load().kivio_float_to_half(float(x)))
+
+
 def code_words_k(cap: int, D: int, bits: int) -> int:
     return cap * D * bits // 32
 
 
-def _quantize(fn, x, bits, G, cap, ntok, dst_off, codes, scale, zero):
+def _quantize(fn, x, bits, G, cap, ntok, dst_off, codes, scale, zero, meta_half):
     x = _h(x)
     B, H, in_stride, D = x.shape
-    _check(fn(B, H, D, bits, G, cap, _p(x, ctypes.c_uint16, np.uint16), in_stride, ntok,
-              dst_off, _p(codes, ctypes.c_uint32, np.uint32),
-              _p(scale, ctypes.c_float, np.float32), _p(zero, ctypes.c_float, np.float32)))
+    _check(fn(B, H, D, bits, G, cap, int(meta_half), _p(x, ctypes.c_uint16, np.uint16),
+              in_stride, ntok, dst_off, _p(codes, ctypes.c_uint32, np.uint32),
+              _m(scale, meta_half), _m(zero, meta_half)))
 
 
-def quantize_k(k, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, zero=None):
+def quantize_k(k, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, zero=None,
+               meta_half=False):
     """Quantize keys k[B][H][T][D] (binary16) tokens [0, ntok) into a store of
-    capacity cap at token offset dst_off.  Returns (codes, scale, zero)."""
+    capacity cap at token offset dst_off.  Returns (codes, scale, zero); scale
+    and zero are binary32, or binary16 bits (uint16) when meta_half."""
     k = _h(k)
     B, H, T, D = k.shape
     ntok = T if ntok is None else ntok
     if codes is None:
         codes = np.zeros((B, H, cap, D * bits // 32), np.uint32)
-        scale = np.zeros((B, H, cap // G, D), np.float32)
-        zero = np.zeros((B, H, cap // G, D), np.float32)
-    _quantize(load().kivio_quantize_k, k, bits, G, cap, ntok, dst_off, codes, scale, zero)
+        scale = np.zeros((B, H, cap // G, D), meta_dtype(meta_half))
+        zero = np.zeros((B, H, cap // G, D), meta_dtype(meta_half))
+    _quantize(load().kivio_quantize_k, k, bits, G, cap, ntok, dst_off, codes, scale, zero,
+              meta_half)
     return codes, scale, zero
 
 
-def quantize_v(v, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, zero=None):
+def quantize_v(v, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, zero=None,
+               meta_half=False):
     """Quantize values v[B][H][T][D] (binary16).  Returns (codes, scale, zero)
     with codes in the 64-token channel-major tile layout."""
     v = _h(v)
@@ -125,9 +148,10 @@ def quantize_v(v, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, ze
     ntok = T if ntok is None else ntok
     if codes is None:
         codes = np.zeros((B, H, cap // 64, D, 64 * bits // 32), np.uint32)
-        scale = np.zeros((B, H, cap, D // G), np.float32)
-        zero = np.zeros((B, H, cap, D // G), np.float32)
-    _quantize(load().kivio_quantize_v, v, bits, G, cap, ntok, dst_off, codes, scale, zero)
+        scale = np.zeros((B, H, cap, D // G), meta_dtype(meta_half))
+        zero = np.zeros((B, H, cap, D // G), meta_dtype(meta_half))
+    _quantize(load().kivio_quantize_v, v, bits, G, cap, ntok, dst_off, codes, scale, zero,
+              meta_half)
     return codes, scale, zero
 
 
@@ -142,6 +166,7 @@ class OracleCache:
     G: int
     R: int
     cap: int
+    meta_half: bool = False
     tq: int = 0
     tr: int = 0
     k_codes: np.ndarray = field(default=None, repr=False)
@@ -156,12 +181,13 @@ class OracleCache:
 
     def __post_init__(self):
         B, H, D, bits, G, R, cap = self.B, self.H, self.D, self.bits, self.G, self.R, self.cap
+        md = meta_dtype(self.meta_half)
         self.k_codes = np.zeros((B, H, cap, D * bits // 32), np.uint32)
-        self.ks = np.zeros((B, H, cap // G, D), np.float32)
-        self.kz = np.zeros((B, H, cap // G, D), np.float32)
+        self.ks = np.zeros((B, H, cap // G, D), md)
+        self.kz = np.zeros((B, H, cap // G, D), md)
         self.v_codes = np.zeros((B, H, cap // 64, D, 64 * bits // 32), np.uint32)
-        self.vs = np.zeros((B, H, cap, D // G), np.float32)
-        self.vz = np.zeros((B, H, cap, D // G), np.float32)
+        self.vs = np.zeros((B, H, cap, D // G), md)
+        self.vz = np.zeros((B, H, cap, D // G), md)
         self.k_res = np.zeros((B, H, R, D), np.uint16)
         self.v_res = np.zeros((B, H, R, D), np.uint16)
 
@@ -172,8 +198,10 @@ class OracleCache:
         if not (0 <= T - tq <= self.R):
             raise OracleError("ESHAPE")
         if tq:
-            quantize_k(k, self.bits, self.G, self.cap, tq, 0, self.k_codes, self.ks, self.kz)
-            quantize_v(v, self.bits, self.G, self.cap, tq, 0, self.v_codes, self.vs, self.vz)
+            quantize_k(k, self.bits, self.G, self.cap, tq, 0, self.k_codes, self.ks, self.kz,
+                       self.meta_half)
+            quantize_v(v, self.bits, self.G, self.cap, tq, 0, self.v_codes, self.vs, self.vz,
+                       self.meta_half)
         self.k_res[:, :, : T - tq] = k[:, :, tq:]
         self.v_res[:, :, : T - tq] = v[:, :, tq:]
         self.tq, self.tr = tq, T - tq
@@ -183,11 +211,11 @@ class OracleCache:
         tq = ctypes.c_int(self.tq)
         tr = ctypes.c_int(self.tr)
         before = self.tq
+        mh = self.meta_half
         _check(load().kivio_append(
-            self.B, self.H, self.D, self.bits, self.G, self.R, self.cap,
-            _p(self.k_codes, ctypes.c_uint32, np.uint32), _p(self.ks, ctypes.c_float, np.float32),
-            _p(self.kz, ctypes.c_float, np.float32), _p(self.v_codes, ctypes.c_uint32, np.uint32),
-            _p(self.vs, ctypes.c_float, np.float32), _p(self.vz, ctypes.c_float, np.float32),
+            self.B, self.H, self.D, self.bits, self.G, self.R, self.cap, int(mh),
+            _p(self.k_codes, ctypes.c_uint32, np.uint32), _m(self.ks, mh), _m(self.kz, mh),
+            _p(self.v_codes, ctypes.c_uint32, np.uint32), _m(self.vs, mh), _m(self.vz, mh),
             _p(self.k_res, ctypes.c_uint16, np.uint16), _p(self.v_res, ctypes.c_uint16, np.uint16),
             _p(k_new, ctypes.c_uint16, np.uint16), _p(v_new, ctypes.c_uint16, np.uint16),
             ctypes.byref(tq), ctypes.byref(tr)))
@@ -205,11 +233,11 @@ def decode_attn(c: OracleCache, q, softmax_scale):
     assert q.shape == (c.B, c.H * c.r, c.D), q.shape
     out = np.zeros((c.B, c.H * c.r, c.D), np.float64)
     scratch = np.zeros(2 * max(1, c.tq + c.tr), np.float64)
+    mh = c.meta_half
     _check(load().kivio_decode_attn(
-        c.B, c.H, c.r, c.D, c.bits, c.G, c.R, c.cap,
-        _p(c.k_codes, ctypes.c_uint32, np.uint32), _p(c.ks, ctypes.c_float, np.float32),
-        _p(c.kz, ctypes.c_float, np.float32), _p(c.v_codes, ctypes.c_uint32, np.uint32),
-        _p(c.vs, ctypes.c_float, np.float32), _p(c.vz, ctypes.c_float, np.float32),
+        c.B, c.H, c.r, c.D, c.bits, c.G, c.R, c.cap, int(mh),
+        _p(c.k_codes, ctypes.c_uint32, np.uint32), _m(c.ks, mh), _m(c.kz, mh),
+        _p(c.v_codes, ctypes.c_uint32, np.uint32), _m(c.vs, mh), _m(c.vz, mh),
         _p(c.k_res, ctypes.c_uint16, np.uint16), _p(c.v_res, ctypes.c_uint16, np.uint16),
         c.tq, c.tr, _p(q, ctypes.c_uint16, np.uint16), float(softmax_scale),
         _p(out, ctypes.c_double, np.float64), _p(scratch, ctypes.c_double, np.float64)))

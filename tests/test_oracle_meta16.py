@@ -1,0 +1,138 @@
+"""Pins of the oracle's half-width metadata variant (binary16 scale and zero).
+
+Reading: the codec computes s and z in binary32 exactly as the full-width
+variant does, then stores them rounded to binary16 (round to nearest even);
+the codes are those of the binary32 computation and dequantization uses the
+stored halves.  The zero (a group minimum of binary16 inputs) is always
+representable, so only the scale rounds.  The oracle's float -> half rounding
+is pinned against NumPy's own conversion, an independent implementation of
+the same IEEE operation."""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_bit_kivi_amd import synth
+from tests.helpers import attention_f64, dequant_k, dequant_v, unpack_k, unpack_v
+
+
+@pytest.fixture(scope="module")
+def oracle_lib():
+    oracle.build(force=False)
+    return oracle.load()
+
+
+def h2d(a):
+    """binary16 bits (uint16) -> float64"""
+    return np.ascontiguousarray(a).view(np.float16).astype(np.float64)
+
+
+def test_half_roundtrip_exhaustive(oracle_lib):
+    """Every finite binary16 value (both zeros, subnormals, max) survives
+    half -> float -> half."""
+    for h in range(65536):
+        if (h >> 10) & 0x1F == 0x1F:
+            continue
+        assert oracle.float_to_half(oracle.half_to_float(h)) == h, hex(h)
+
+
+def test_float_to_half_matches_numpy(oracle_lib):
+    rng = np.random.default_rng(11)
+    n = 60000
+    x = (rng.standard_normal(n) * np.exp2(rng.integers(-30, 18, n).astype(np.float64)))
+    x = x.astype(np.float32)
+    # exact midpoints between consecutive halves (ties go to the even half)
+    hs = rng.integers(0, 0x7BFF, 4000).astype(np.uint16)
+    lo = hs.view(np.float16).astype(np.float32)
+    hi = (hs + 1).view(np.float16).astype(np.float32)
+    mids = ((lo.astype(np.float64) + hi.astype(np.float64)) / 2).astype(np.float32)
+    special = np.array([0.0, -0.0, 65504.0, 65519.99, 65520.0, 65536.0, 1e9, -1e9,
+                        2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26, 2.0 ** -14,
+                        2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 1e-40,
+                        -1e-40, np.inf, -np.inf, 43669.33], np.float32)
+    allx = np.concatenate([x, mids, -mids, special])
+    with np.errstate(over="ignore"):
+        want = allx.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.float_to_half(float(v)) for v in allx], np.uint16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, [(float(allx[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("G", [32, 64])
+def test_meta16_is_rounded_meta32(oracle_lib, bits, G):
+    """Same codes; scale = binary16(binary32 scale); zero equal and exact."""
+    B, H, T, D = 2, 3, 128, 128
+    x = synth.random_fp16(300 + bits + G, (B, H, T, D), scale=3.0)
+    x[..., 7] *= np.float16(10)
+    for fn in (oracle.quantize_k, oracle.quantize_v):
+        c32, s32, z32 = fn(x, bits, G, T)
+        c16, s16, z16 = fn(x, bits, G, T, meta_half=True)
+        assert np.array_equal(c16, c32)
+        assert np.array_equal(s16, s32.astype(np.float16).view(np.uint16))
+        assert np.array_equal(z16, z32.astype(np.float16).view(np.uint16))
+        assert np.array_equal(z32.astype(np.float16).astype(np.float32), z32)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_meta16_error_bound(oracle_lib, bits):
+    """|x - (c s16 + z16)| <= s (1/2 + 2^-18) + c |s - s16|: the binary32
+    bound plus what rounding the scale can add, per element."""
+    B, H, T, D, G = 1, 2, 128, 64, 32
+    k = synth.random_fp16(400 + bits, (B, H, T, D), scale=5.0)
+    c32, s32, z32 = oracle.quantize_k(k, bits, G, T)
+    c16, s16, z16 = oracle.quantize_k(k, bits, G, T, meta_half=True)
+    codes = unpack_k(c16, bits, T, D).astype(np.float64)
+    s = np.repeat(s32.astype(np.float64), G, axis=2)
+    sh = np.repeat(h2d(s16), G, axis=2)
+    zh = np.repeat(h2d(z16), G, axis=2)
+    xh = codes * sh + zh
+    err = np.abs(k.astype(np.float64) - xh)
+    bound = s * (0.5 + 2.0 ** -18) + codes * np.abs(s - sh) + 1e-300
+    assert np.all(err <= bound)
+    # and the scale rounding is at most half a binary16 ulp of the scale
+    assert np.all(np.abs(s - sh) <= np.abs(s) * 2.0 ** -11 + 2.0 ** -25)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("r", [1, 4])
+@pytest.mark.parametrize("tq,tr", [(64, 0), (96, 31)])
+def test_meta16_decode_brute_force(oracle_lib, bits, r, tq, tr):
+    """Decode over a half-metadata cache equals NumPy binary64 attention on
+    the arrays dequantized with the stored halves."""
+    B, H, D, G, R = 2, 2, 32, 32, 32
+    L = tq + tr
+    k = synth.random_fp16(500 + bits, (B, H, L, D), scale=2.0)
+    k[..., 3] *= np.float16(10)
+    v = synth.random_fp16(510 + bits, (B, H, L, D))
+    q = synth.random_fp16(520 + r, (B, H * r, D))
+    c = oracle.OracleCache(B, H, r, D, bits, G, R, 128, meta_half=True)
+    c.prefill(k, v, tq)
+    got = c.decode(q, 0.2)
+    kh = np.concatenate([dequant_k(c.k_codes, h2d(c.ks), h2d(c.kz), bits, G, tq, D),
+                         k[:, :, tq:].astype(np.float64)], axis=2)
+    vh = np.concatenate([dequant_v(c.v_codes, h2d(c.vs), h2d(c.vz), bits, G, tq, D),
+                         v[:, :, tq:].astype(np.float64)], axis=2)
+    ref = attention_f64(q, kh, vh, np.float32(0.2))
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_meta16_stream_equals_one_shot(oracle_lib, bits):
+    """Prefill + appends (with flushes) == one-shot quantization, bit for bit."""
+    B, H, D, G, R = 1, 2, 64, 32, 32
+    tq0, n = 64, 3 * R + 5
+    T = tq0 + R + n
+    k = synth.random_fp16(600 + bits, (B, H, T, D), scale=1.5)
+    v = synth.random_fp16(610 + bits, (B, H, T, D))
+    c = oracle.OracleCache(B, H, 1, D, bits, G, R, 256, meta_half=True)
+    c.prefill(k[:, :, : tq0 + R], v[:, :, : tq0 + R], tq0)
+    for i in range(n):
+        t = tq0 + R + i
+        c.append(np.ascontiguousarray(k[:, :, t]), np.ascontiguousarray(v[:, :, t]))
+    assert c.flushes == 4  # the residual starts full: the first append flushes
+    kc, ks, kz = oracle.quantize_k(k, bits, G, 256, c.tq, meta_half=True)
+    vc, vs, vz = oracle.quantize_v(v, bits, G, 256, c.tq, meta_half=True)
+    for got, want in ((c.k_codes, kc), (c.ks, ks), (c.kz, kz), (c.v_codes, vc), (c.vs, vs),
+                      (c.vz, vz)):
+        assert np.array_equal(got, want)
+    assert np.array_equal(unpack_v(c.v_codes, bits, c.tq, D), unpack_v(vc, bits, c.tq, D))
