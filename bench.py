@@ -35,21 +35,23 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
 
 
-def decode_bytes(B, H, r, D, bits, G, tq, tr):
-    """Algorithmic bytes of one decode call: packed K/V codes, fp32 scale and
-    zero of both, fp16 residual K/V, fp16 q and out."""
-    per = (2 * tq * D * bits // 8 + (tq // G) * D * 8 + tq * (D // G) * 8 + 4 * tr * D
-           + 4 * r * D)
+def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4):
+    """Algorithmic bytes of one decode call: packed K/V codes, scale and zero
+    of both (mb bytes each: 4 for binary32, 2 for binary16), fp16 residual
+    K/V, fp16 q and out."""
+    per = (2 * tq * D * bits // 8 + (tq // G) * D * 2 * mb + tq * (D // G) * 2 * mb
+           + 4 * tr * D + 4 * r * D)
     return B * H * per
 
 
-def append_bytes(B, H, D, bits, G, R, flush):
+def append_bytes(B, H, D, bits, G, R, flush, mb=4):
     """Algorithmic bytes of one append: read the new K/V token, write it to
     the residual; a flush reads R residual tokens of K and V and writes their
     codes, scales and zeros."""
     b = B * H * D * 2 * 2 * 2
     if flush:
-        b += B * H * (2 * R * D * 2 + 2 * R * D * bits // 8 + (R // G) * D * 8 + R * (D // G) * 8)
+        b += B * H * (2 * R * D * 2 + 2 * R * D * bits // 8 + (R // G) * D * 2 * mb
+                      + R * (D // G) * 2 * mb)
     return b
 
 
@@ -133,7 +135,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, 
     print(json.dumps(out))
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False):
     """The C oracle (single thread) on a bounded sample of the same workload:
     whole decode steps (append with its flush, then attention for all 256
     query heads) repeated until about `min_seconds` of CPU work."""
@@ -145,9 +147,10 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
     k, v = synth.kv(w)
     cap = w.capacity(64)
     oc = oracle.OracleCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                            w.residual, cap)
+                            w.residual, cap, meta_half=meta_half)
     oc.prefill(k, v, w.tq)
     del k, v
+    mb = 2 if meta_half else 4
     nbytes, steps, t_total = 0, 0, 0.0
     while t_total < min_seconds and steps < 64:
         kn, vn = synth.new_token(w, steps + 1)
@@ -159,9 +162,9 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0):
         dt = time.perf_counter() - t0
         t_total += dt
         nbytes += append_bytes(w.batch, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
-                               flush)
+                               flush, mb)
         nbytes += decode_bytes(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
-                               oc.tr)
+                               oc.tr, mb)
         steps += 1
         if t_total > max_seconds:
             break
@@ -186,6 +189,8 @@ def main():
     ap.add_argument("--workload", default="llama2_7b_b8_ctx4096")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
+    ap.add_argument("--meta", choices=["fp32", "fp16"], default="fp32",
+                    help="storage of the quantization scales and zeros")
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -196,9 +201,13 @@ def main():
                     help="write the calibrated traffic summary from two PMC runs and exit")
     args = ap.parse_args()
 
+    meta_half = args.meta == "fp16"
+    mb = 2 if meta_half else 4
+    # profiles are keyed by workload and metadata width
+    tag = args.workload + ("_meta16" if meta_half else "")
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
-        pmc_summary(fcsv, wcsv, int(mib) << 20, args.workload, cmd)
+        pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
         return
 
     if args.gpus != 1:
@@ -232,7 +241,7 @@ def main():
     del k, v
     caches = []
     for _ in range(NL):
-        c = KiviCache(B, H, r, D, bits, G, R, cap)
+        c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
         c.prefill(kd, vd, w.tq)
         caches.append(c)
     del kd, vd
@@ -316,15 +325,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    dec_bytes = [decode_bytes(B, H, r, D, bits, G, tq, tr) for _, tq, tr in meta]
-    app_bytes = [append_bytes(B, H, D, bits, G, R, f) for f, _, _ in meta]
+    dec_bytes = [decode_bytes(B, H, r, D, bits, G, tq, tr, mb) for _, tq, tr in meta]
+    app_bytes = [append_bytes(B, H, D, bits, G, R, f, mb) for f, _, _ in meta]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
     # The timed call is the decode launch, carrying the new token's append when
     # fused.  Flush steps (a full residual quantized first: 1 in R steps per
     # layer) also run the quantize launches inside the timed interval, so the
     # roofline of the decode kernel averages the other steps only.
     plain = [not f for f, _, _ in meta]
-    new_tok = append_bytes(B, H, D, bits, G, R, False)
+    new_tok = append_bytes(B, H, D, bits, G, R, False, mb)
     call_bytes = np.array([d + (0 if args.separate else new_tok) for d in dec_bytes])[plain]
     dec_ms = np.array([a.elapsed_time(b) for a, b in events])[plain]
     value = total_bytes / elapsed / 1e9
@@ -347,6 +356,7 @@ def main():
         "config": {
             "workload": w.name, "batch": B, "q_heads": H * r, "kv_heads": H, "head_dim": D,
             "context_at_start": w.context, "bits": bits, "group": G, "residual": R,
+            "scale_zero": "fp16" if meta_half else "fp32",
             "layers_rotated": NL, "decode_splits": splits_used,
             "step_call": "kivi_append + kivi_decode_attn" if args.separate else
                          "kivi_append_decode_attn",
@@ -363,7 +373,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(tag),
             "bytes_per_launch": int(call_bytes.mean()),
             "launches_averaged": int(len(call_bytes)),
             "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 3),
@@ -373,7 +383,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half)
     print(json.dumps(result), flush=True)
 
 

@@ -16,6 +16,11 @@
  * code = round-half-even((x - z) / s) clamped to 2^b - 1, each step one IEEE
  * binary32 operation in that order (true division, no fused multiply-add);
  * a group with max == min stores s = 0, z = that value and zero codes.
+ * Metadata width (kivi_shape.meta_half): s and z are stored as binary32, or,
+ * with meta_half = 1, as binary16 rounded to nearest even from those binary32
+ * values (the codes stay those of the binary32 computation; z, a binary16
+ * input, is exact; s never overflows since it is at most 131008/3).
+ * Dequantization always uses the stored values.
  *
  * Conventions for every function below:
  *   - All buffer pointers are DEVICE pointers (hipMalloc'd or torch CUDA
@@ -34,12 +39,13 @@
  * Storage layout (E = 32 / bits codes per 32-bit word, little-endian bits):
  *   k_codes : uint32 [B][Hkv][cap][D/E]; channel d of token t is in word d/E
  *             at bits [bits*(d%E), +bits).
- *   k_scale, k_zero : float [B][Hkv][cap/G][D]   (one pair per channel per
- *             group of G tokens).
+ *   k_scale, k_zero : meta [B][Hkv][cap/G][D]    (one pair per channel per
+ *             group of G tokens); meta = float, or binary16 bits (uint16)
+ *             when meta_half.
  *   v_codes : uint32 [B][Hkv][cap/64][D][64/E]; 64-token tiles, channel-major
  *             inside a tile: token t, channel d is in tile t/64, word
  *             (t%64)/E of channel d, bits [bits*((t%64)%E), +bits).
- *   v_scale, v_zero : float [B][Hkv][cap][D/G]   (one pair per token per
+ *   v_scale, v_zero : meta [B][Hkv][cap][D/G]    (one pair per token per
  *             group of G channels).
  *   k_res, v_res : fp16 [B][Hkv][R][D]; residual slot i holds cache token
  *             tq + i.
@@ -74,7 +80,10 @@ enum kivi_status {
  *     head_dim (KIVI_EUNSUPPORTED for other head_dim/group values);
  *   residual >= group and a multiple of group;
  *   capacity >= 0, a multiple of 64 and of group;
- *   gqa_ratio <= 16. */
+ *   gqa_ratio <= 16;
+ *   meta_half in {0, 1} (KIVI_EINVAL): 0 = binary32 scale / zero, 1 =
+ *     binary16 (half the metadata bytes; a zero-initialised shape keeps
+ *     binary32). */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -84,6 +93,7 @@ typedef struct {
   int32_t group;
   int32_t residual;
   int32_t capacity;
+  int32_t meta_half;
 } kivi_shape;
 
 /* One mixed-precision cache: device buffers (layouts above) plus the host-side
@@ -92,11 +102,11 @@ typedef struct {
 typedef struct {
   kivi_shape shape;
   uint32_t* k_codes;
-  float* k_scale;
-  float* k_zero;
+  void* k_scale;     /* float, or uint16 binary16 bits when shape.meta_half */
+  void* k_zero;
   uint32_t* v_codes;
-  float* v_scale;
-  float* v_zero;
+  void* v_scale;
+  void* v_zero;
   uint16_t* k_res;
   uint16_t* v_res;
   int32_t tq;
@@ -113,22 +123,23 @@ int kivi_cache_bytes(const kivi_shape* shape, size_t* k_codes, size_t* k_meta,
  * the channel dimension; study.space summary: the key groups span tokens).
  * Quantizes source tokens [0, ntok) of `k` (fp16 [B][Hkv][in_tok_stride][D])
  * into cache tokens [dst_tok_offset, dst_tok_offset + ntok) of `codes`,
- * `scale`, `zero` (layouts above).  Each (channel, group of G tokens) gets
- * its own scale and zero; results are bit-exact to the formula above.
+ * `scale`, `zero` (layouts above; element type set by shape->meta_half).
+ * Each (channel, group of G tokens) gets its own scale and zero; results are
+ * bit-exact to the formula above.
  * ntok >= 1, ntok and dst_tok_offset multiples of group, in_tok_stride >=
  * ntok; dst_tok_offset + ntok > capacity gives KIVI_ECAPACITY. */
 int kivi_quantize_k(const kivi_shape* shape, const uint16_t* k,
                     int32_t in_tok_stride, int32_t ntok,
-                    int32_t dst_tok_offset, uint32_t* codes, float* scale,
-                    float* zero, void* stream);
+                    int32_t dst_tok_offset, uint32_t* codes, void* scale,
+                    void* zero, void* stream);
 
 /* Per-token value quantization ("KIVI...", Abstract: values are quantized
  * per token).  Same arguments and rules as kivi_quantize_k; each (token,
  * group of G channels) gets its own scale and zero. */
 int kivi_quantize_v(const kivi_shape* shape, const uint16_t* v,
                     int32_t in_tok_stride, int32_t ntok,
-                    int32_t dst_tok_offset, uint32_t* codes, float* scale,
-                    float* zero, void* stream);
+                    int32_t dst_tok_offset, uint32_t* codes, void* scale,
+                    void* zero, void* stream);
 
 /* Fill an empty cache from a prompt (study.space summary: the cache is split
  * into grouped and residual parts).  k, v: fp16 [B][Hkv][ntok][D].  Tokens

@@ -21,18 +21,24 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity) -> kivi_shape:
-    return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity)
+def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+               meta_half=False) -> kivi_shape:
+    return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                      int(bool(meta_half)))
 
 
 class KiviCache:
-    """One layer's cache: packed K/V codes, fp32 scale/zero, fp16 residual.
+    """One layer's cache: packed K/V codes, scale/zero (fp32, or fp16 when
+    meta_half), fp16 residual.
 
     Layouts are those of include/kivi.h; the host keeps (tq, tr)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 device="cuda"):
-        self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity)
+                 device="cuda", meta_half=False):
+        self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                                meta_half)
+        self.meta_half = bool(meta_half)
+        mdt = torch.float16 if meta_half else torch.float32
         sizes = [ctypes.c_size_t() for _ in range(6)]
         check(_lib.kivi_cache_bytes(ctypes.byref(self.shape), *[ctypes.byref(s) for s in sizes]),
               "kivi_cache_bytes")
@@ -40,17 +46,17 @@ class KiviCache:
         E = 32 // bits
         dev = torch.device(device)
         self.k_codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device=dev)
-        self.k_scale = torch.zeros((B, H, cap // G, D), dtype=torch.float32, device=dev)
-        self.k_zero = torch.zeros((B, H, cap // G, D), dtype=torch.float32, device=dev)
+        self.k_scale = torch.zeros((B, H, cap // G, D), dtype=mdt, device=dev)
+        self.k_zero = torch.zeros((B, H, cap // G, D), dtype=mdt, device=dev)
         self.v_codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device=dev)
-        self.v_scale = torch.zeros((B, H, cap, D // G), dtype=torch.float32, device=dev)
-        self.v_zero = torch.zeros((B, H, cap, D // G), dtype=torch.float32, device=dev)
+        self.v_scale = torch.zeros((B, H, cap, D // G), dtype=mdt, device=dev)
+        self.v_zero = torch.zeros((B, H, cap, D // G), dtype=mdt, device=dev)
         self.k_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
         self.v_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
         assert self.k_codes.numel() * 4 == sizes[0].value
-        assert self.k_scale.numel() * 4 == sizes[1].value
+        assert self.k_scale.nbytes == sizes[1].value
         assert self.v_codes.numel() * 4 == sizes[2].value
-        assert self.v_scale.numel() * 4 == sizes[3].value
+        assert self.v_scale.nbytes == sizes[3].value
         assert self.k_res.numel() * 2 == sizes[4].value
         self.c = kivi_cache(self.shape, *[t.data_ptr() for t in (
             self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,

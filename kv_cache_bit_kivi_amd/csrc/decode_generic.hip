@@ -31,6 +31,11 @@ __device__ __forceinline__ uint16_t f2h(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// scale / zero element i of a metadata plane (binary32, or binary16 when mh)
+__device__ __forceinline__ float meta_at(const void* p, size_t i, int mh) {
+  return mh ? h2f(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+}
+
 __device__ float block_reduce(float v, bool is_max, float* scratch) {
   for (int off = 32; off > 0; off >>= 1) {
     float o = __shfl_xor(v, off, 64);
@@ -71,11 +76,13 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
 
   const size_t kvp = (size_t)u;                   // plane index
   const uint32_t* kc = a.k_codes + kvp * (size_t)a.cap * W;
-  const float* ks = a.k_scale + kvp * (size_t)(a.cap / G) * D;
-  const float* kz = a.k_zero + kvp * (size_t)(a.cap / G) * D;
+  const int mh = a.mh;
+  const size_t mb = mh ? 2 : 4;   // metadata element bytes
+  const char* ks = static_cast<const char*>(a.k_scale) + kvp * (size_t)(a.cap / G) * D * mb;
+  const char* kz = static_cast<const char*>(a.k_zero) + kvp * (size_t)(a.cap / G) * D * mb;
   const uint32_t* vc = a.v_codes + kvp * (size_t)a.cap * D / E;
-  const float* vs = a.v_scale + kvp * (size_t)a.cap * NG;
-  const float* vz = a.v_zero + kvp * (size_t)a.cap * NG;
+  const char* vs = static_cast<const char*>(a.v_scale) + kvp * (size_t)a.cap * NG * mb;
+  const char* vz = static_cast<const char*>(a.v_zero) + kvp * (size_t)a.cap * NG * mb;
   const uint16_t* kr = a.k_res + kvp * (size_t)a.R * D;
   const uint16_t* vr = a.v_res + kvp * (size_t)a.R * D;
   const size_t qrow0 = (size_t)b * a.H * r + (size_t)h * r;   // first query row
@@ -103,13 +110,13 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
       for (int i = 0; i < RR; i++) acc[i] = 0.f;
       if (t < a.tq) {
         const uint32_t* row = kc + (size_t)t * W;
-        const float* s_row = ks + (size_t)(t / G) * D;
-        const float* z_row = kz + (size_t)(t / G) * D;
+        const size_t m0 = (size_t)(t / G) * D;
         for (int w = 0; w < W; w++) {
           const uint32_t word = row[w];
           for (int e = 0; e < E; e++) {
             const int dd = w * E + e;
-            const float kh = (float)((word >> (bits * e)) & mask) * s_row[dd] + z_row[dd];
+            const float kh = (float)((word >> (bits * e)) & mask) * meta_at(ks, m0 + dd, mh) +
+                             meta_at(kz, m0 + dd, mh);
 #pragma unroll
             for (int i = 0; i < RR; i++)
               if (i < r) acc[i] += sq[i * D + dd] * kh;
@@ -163,8 +170,8 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
         if (t < a.tq) {
           const uint32_t word = vc[((size_t)(t / 64) * D + d) * WPC + (t % 64) / E];
           const int j = d / G;
-          vh = (float)((word >> (bits * ((t % 64) % E))) & mask) * vs[(size_t)t * NG + j] +
-               vz[(size_t)t * NG + j];
+          vh = (float)((word >> (bits * ((t % 64) % E))) & mask) *
+                   meta_at(vs, (size_t)t * NG + j, mh) + meta_at(vz, (size_t)t * NG + j, mh);
         } else {
           vh = h2f(vr[(size_t)(t - a.tq) * D + d]);
         }

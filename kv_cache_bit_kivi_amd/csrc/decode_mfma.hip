@@ -35,7 +35,8 @@
 // tile it computes the key scores into LDS, updates the running maximum
 // (online softmax; accumulators are rescaled only when the maximum grows) and
 // accumulates P.V.  Codes and metadata arrive through raw buffer loads, 16
-// bytes per lane, one or two tiles ahead of the compute; absent tiles and
+// bytes per lane (8 for binary16 metadata, widened to binary32 when the tile
+// is computed), one or two tiles ahead of the compute; absent tiles and
 // tokens are loaded out of range (zeros, no memory access) instead of being
 // branched around, so the completion counter never forces a full drain.
 // Codes are staged through LDS and re-read in the MFMA operand layout.  The
@@ -209,6 +210,16 @@ __device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t off) {
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
   return uint2{v.x, v.y};
 }
+__device__ __forceinline__ uint2 ld8s(rsrc_t r, uint32_t off) {
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kStream);
+  return uint2{v.x, v.y};
+}
+// four metadata values of a lane: binary32 as loaded, or four binary16 widened
+__device__ __forceinline__ float4 meta4(float4 v) { return v; }
+__device__ __forceinline__ float4 meta4(uint2 v) {
+  return float4{h2f((uint16_t)(v.x & 0xFFFFu)), h2f((uint16_t)(v.x >> 16)),
+                h2f((uint16_t)(v.y & 0xFFFFu)), h2f((uint16_t)(v.y >> 16))};
+}
 
 // slot of position q (0..7) inside a 4-bit word's half8
 __device__ __forceinline__ int slot4(int q) { return (q & 1) ? 4 + (q >> 1) : (q >> 1); }
@@ -265,9 +276,11 @@ struct Cfg {
 };
 
 // register budget of the occupancy target: one wave per SIMD for 8 heads, the
-// three-wave budget for one head at 2 bits (it fits without spilling and
-// measured fastest), two waves otherwise.  Blocks of 8 waves still place two
-// per SIMD.
+// three-wave budget for one head at 2 bits (measured fastest), two waves
+// otherwise.  Blocks of 8 waves still place two per SIMD.  At these budgets
+// the tile loop holds no spill; the one-head 2-bit and four-head 4-bit
+// variants spill a few registers around the loop over residual slices longer
+// than one batch, which runs only for short contexts with few splits.
 template <int BITS, int R>
 constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS == 2 && R == 1) ? 3 : 2); }
 
@@ -278,7 +291,7 @@ constexpr int prefetch_depth() {
   return R >= 8 ? 2 : 1;
 }
 
-template <int BITS, int R, int NW>
+template <int BITS, int R, int NW, bool MH>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
 decode_mfma_kernel(DecodeArgs a) {
@@ -311,11 +324,15 @@ decode_mfma_kernel(DecodeArgs a) {
   // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
   const size_t plane = (size_t)u, cap = (size_t)a.cap;
   const rsrc_t r_kc = make_rsrc(a.k_codes + plane * cap * W, (uint32_t)(cap * W * 4));
-  const rsrc_t r_ks = make_rsrc(a.k_scale + plane * (cap / kG) * kD, (uint32_t)(cap / kG * kD * 4));
-  const rsrc_t r_kz = make_rsrc(a.k_zero + plane * (cap / kG) * kD, (uint32_t)(cap / kG * kD * 4));
+  // metadata: MB bytes per value (binary16 or binary32)
+  constexpr uint32_t MB = MH ? 2 : 4;
+  using MetaT = std::conditional_t<MH, uint2, float4>;
+  const size_t kmp = (cap / kG) * kD * MB, vmp = cap * kNG * MB;   // plane bytes
+  const rsrc_t r_ks = make_rsrc(static_cast<const char*>(a.k_scale) + plane * kmp, (uint32_t)kmp);
+  const rsrc_t r_kz = make_rsrc(static_cast<const char*>(a.k_zero) + plane * kmp, (uint32_t)kmp);
   const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD / E), (uint32_t)(cap * (kD / E) * 4));
-  const rsrc_t r_vs = make_rsrc(a.v_scale + plane * cap * kNG, (uint32_t)(cap * kNG * 4));
-  const rsrc_t r_vz = make_rsrc(a.v_zero + plane * cap * kNG, (uint32_t)(cap * kNG * 4));
+  const rsrc_t r_vs = make_rsrc(static_cast<const char*>(a.v_scale) + plane * vmp, (uint32_t)vmp);
+  const rsrc_t r_vz = make_rsrc(static_cast<const char*>(a.v_zero) + plane * vmp, (uint32_t)vmp);
   const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
   const rsrc_t r_vr = make_rsrc(a.v_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
   // fused append: the new token (residual slot t_new) comes from its input row
@@ -393,14 +410,22 @@ decode_mfma_kernel(DecodeArgs a) {
       x7 = ld16(r_vc, co + 3072);
     }
   };
-  auto load_meta = [&](int tile, float4& ks, float4& kz, float4& vs, float4& vz)
+  auto load_meta = [&](int tile, MetaT& ks, MetaT& kz, MetaT& vs, MetaT& vz)
       __attribute__((always_inline)) {
-    // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 1 KB each
-    const uint32_t mo = tile < t_end ? (uint32_t)tile * 1024 + l16 : kOut;
-    ks = ld16f(r_ks, mo);
-    kz = ld16f(r_kz, mo);
-    vs = ld16f(r_vs, mo);
-    vz = ld16f(r_vz, mo);
+    // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 256 values
+    // each, 4 per lane (converted to binary32 when the tile is computed)
+    const uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
+    if constexpr (MH) {
+      ks = ld8s(r_ks, mo);
+      kz = ld8s(r_kz, mo);
+      vs = ld8s(r_vs, mo);
+      vz = ld8s(r_vz, mo);
+    } else {
+      ks = ld16f(r_ks, mo);
+      kz = ld16f(r_kz, mo);
+      vs = ld16f(r_vs, mo);
+      vz = ld16f(r_vz, mo);
+    }
   };
   auto stage = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
                    const uint4& x4, const uint4& x5, const uint4& x6, const uint4& x7)
@@ -446,7 +471,7 @@ decode_mfma_kernel(DecodeArgs a) {
   // overlaps them.
   constexpr int DEPTH = prefetch_depth<BITS, R>();
   uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
-  float4 a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
+  MetaT a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
   // (the same issue order as the loop: codes A, meta A, codes B, meta B)
   load_codes(t_begin, a0, a1, a2, a3, a4, a5, a6, a7);
   __builtin_amdgcn_sched_barrier(0);
@@ -551,10 +576,11 @@ decode_mfma_kernel(DecodeArgs a) {
     apply_max(mxs);
   };
 
-  // ---------------- tile loads: NLD code loads + 4 metadata loads, 16 B each
   // one tile (codes already staged in LDS): key scores -> LDS, online-softmax
   // rescale, P.V
-  auto do_tile = [&](int tile, float4 ks4, float4 kz4, float4 vs4, float4 vz4) __attribute__((always_inline)) {
+  auto do_tile = [&](int tile, MetaT ksm, MetaT kzm, MetaT vsm, MetaT vzm)
+      __attribute__((always_inline)) {
+    const float4 ks4 = meta4(ksm), kz4 = meta4(kzm), vs4 = meta4(vsm), vz4 = meta4(vzm);
     const bool half_tile = tile * 64 + 64 > tq;   // only the first 32 tokens exist
     // key factors (both groups at once: lanes 0-31 group 0, 32-63 group 1)
     const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
@@ -908,14 +934,18 @@ constexpr int block_waves(int nw) {
   return (R >= 8 || nw < 8) ? 4 : 8;
 }
 
-template <int BITS, int R>
-hipError_t launch_r(const DecodeArgs& a, int nw, hipStream_t st) {
+template <int BITS, int R, bool MH>
+hipError_t launch_m(const DecodeArgs& a, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
   if (block_waves<R>(nw) == 8)
-    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4)><<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a);
+    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH><<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a);
   else
-    decode_mfma_kernel<BITS, R, 4><<<grid, 4 * 64, 0, st>>>(a);
+    decode_mfma_kernel<BITS, R, 4, MH><<<grid, 4 * 64, 0, st>>>(a);
   return hipGetLastError();
+}
+template <int BITS, int R>
+hipError_t launch_r(const DecodeArgs& a, int nw, hipStream_t st) {
+  return a.mh ? launch_m<BITS, R, true>(a, nw, st) : launch_m<BITS, R, false>(a, nw, st);
 }
 
 template <int BITS>
@@ -935,11 +965,12 @@ bool decode_mfma_supported(int D, int G, int r) {
 }
 
 namespace {
+// (the binary32-metadata variant: it holds the most registers of the two)
 template <int BITS, int R, int NW>
 int occupancy_of() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW>), NW * 64, 0) !=
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false>), NW * 64, 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;

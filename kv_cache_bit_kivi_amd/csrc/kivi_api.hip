@@ -19,6 +19,7 @@ int check_shape(const kivi_shape* s) {
   if (!s) return KIVI_EINVAL;
   if (s->batch < 1 || s->num_kv_heads < 1 || s->gqa_ratio < 1) return KIVI_EINVAL;
   if (s->bits != 2 && s->bits != 4) return KIVI_EINVAL;
+  if (s->meta_half != 0 && s->meta_half != 1) return KIVI_EINVAL;
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
   if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
@@ -49,7 +50,7 @@ int check_cache(const kivi_cache* c) {
 }
 
 int check_quantize(const kivi_shape* s, const uint16_t* x, int32_t in_stride, int32_t ntok,
-                   int32_t dst, const uint32_t* codes, const float* scale, const float* zero) {
+                   int32_t dst, const uint32_t* codes, const void* scale, const void* zero) {
   int rc = check_shape(s);
   if (rc) return rc;
   if (!x || !codes || !scale || !zero) return KIVI_EINVAL;
@@ -155,30 +156,31 @@ int kivi_cache_bytes(const kivi_shape* s, size_t* k_codes, size_t* k_meta, size_
   const size_t codes = planes * cap * D * s->bits / 8;
   if (k_codes) *k_codes = codes;
   if (v_codes) *v_codes = codes;
-  if (k_meta) *k_meta = planes * (cap / G) * D * sizeof(float);
-  if (v_meta) *v_meta = planes * cap * (D / G) * sizeof(float);
+  const size_t mb = s->meta_half ? 2 : sizeof(float);
+  if (k_meta) *k_meta = planes * (cap / G) * D * mb;
+  if (v_meta) *v_meta = planes * cap * (D / G) * mb;
   if (residual) *residual = planes * (size_t)s->residual * D * 2;
   if (query) *query = planes * (size_t)s->gqa_ratio * D * 2;
   return KIVI_OK;
 }
 
 int kivi_quantize_k(const kivi_shape* s, const uint16_t* k, int32_t in_tok_stride, int32_t ntok,
-                    int32_t dst, uint32_t* codes, float* scale, float* zero, void* stream) {
+                    int32_t dst, uint32_t* codes, void* scale, void* zero, void* stream) {
   int rc = check_quantize(s, k, in_tok_stride, ntok, dst, codes, scale, zero);
   if (rc) return rc;
   hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, (hipStream_t)stream);
+                                         scale, zero, s->meta_half, (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
 }
 
 int kivi_quantize_v(const kivi_shape* s, const uint16_t* v, int32_t in_tok_stride, int32_t ntok,
-                    int32_t dst, uint32_t* codes, float* scale, float* zero, void* stream) {
+                    int32_t dst, uint32_t* codes, void* scale, void* zero, void* stream) {
   int rc = check_quantize(s, v, in_tok_stride, ntok, dst, codes, scale, zero);
   if (rc) return rc;
   hipError_t e = kivi::launch_quantize_v(v, s->batch, s->num_kv_heads, s->head_dim, s->bits,
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, (hipStream_t)stream);
+                                         scale, zero, s->meta_half, (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
 }
 
@@ -196,10 +198,11 @@ int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t nt
   if (tq > 0) {
     hipError_t e = kivi::launch_quantize_k(k, s.batch, s.num_kv_heads, s.head_dim, s.bits,
                                            s.group, s.capacity, ntok, tq, 0, c->k_codes,
-                                           c->k_scale, c->k_zero, st);
+                                           c->k_scale, c->k_zero, s.meta_half, st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(v, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
-                                s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero, st);
+                                s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero,
+                                s.meta_half, st);
     if (e != hipSuccess) return KIVI_EHIP;
   }
   if (ntok > tq) {
@@ -226,11 +229,12 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
     // below is enqueued after, so slot 0 is read before it is overwritten
     hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
-                                           tq, c->k_codes, c->k_scale, c->k_zero, st);
+                                           tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
+                                           st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, tq, c->v_codes, c->v_scale,
-                                c->v_zero, st);
+                                c->v_zero, s.meta_half, st);
     if (e != hipSuccess) return KIVI_EHIP;
     tq += s.residual;
     tr = 0;
@@ -303,6 +307,7 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->tq = tq;
   a->tr = tr;
   a->S = S;
+  a->mh = s.meta_half;
   a->scale = softmax_scale;
   return KIVI_OK;
 }
@@ -352,11 +357,12 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
   if (flush) {
     hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
-                                           c->tq, c->k_codes, c->k_scale, c->k_zero, st);
+                                           c->tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
+                                           st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, c->tq, c->v_codes,
-                                c->v_scale, c->v_zero, st);
+                                c->v_scale, c->v_zero, s.meta_half, st);
     if (e != hipSuccess) return KIVI_EHIP;
   }
   if (use_mfma(s)) {

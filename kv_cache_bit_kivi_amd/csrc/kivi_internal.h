@@ -11,11 +11,11 @@ namespace kivi {
 // Device pointers and lengths of one decode call.
 struct DecodeArgs {
   const uint32_t* k_codes;
-  const float* k_scale;
-  const float* k_zero;
+  const void* k_scale;   // float, or binary16 bits when mh
+  const void* k_zero;
   const uint32_t* v_codes;
-  const float* v_scale;
-  const float* v_zero;
+  const void* v_scale;
+  const void* v_zero;
   const uint16_t* k_res;
   const uint16_t* v_res;
   // fused append: the token in residual slot tr - 1 is read from these rows
@@ -26,6 +26,7 @@ struct DecodeArgs {
   uint16_t* out;
   float* ws;          // split partials: m, l [rows][S], o [rows][S][D]
   int B, H, r, D, bits, G, R, cap, tq, tr, S;
+  int mh;             // metadata stored as binary16 (1) or binary32 (0)
   float scale;
 };
 
@@ -33,10 +34,10 @@ struct DecodeArgs {
 // launch.
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G,
                              int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             float* scale, float* zero, hipStream_t st);
+                             void* scale, void* zero, int mh, hipStream_t st);
 hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G,
                              int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             float* scale, float* zero, hipStream_t st);
+                             void* scale, void* zero, int mh, hipStream_t st);
 // Copies tokens [t0, t0 + n) of src ([B][H][src_stride][D]) into slots
 // [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once.
 hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,

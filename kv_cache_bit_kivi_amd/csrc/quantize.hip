@@ -11,6 +11,8 @@
 //   mx == mn : scale 0, zero mn, codes 0 (the group dequantizes exactly);
 //   else     : range = mx - mn; s = range / (2^b - 1); z = mn;
 //              code = min(rint((x - z) / s), 2^b - 1), rint = half-to-even.
+// Half-width metadata stores s and z rounded to binary16 (nearest even) after
+// the codes have been computed from the binary32 values.
 // Each block stages its fp16 tile in LDS with 16-byte loads, computes the
 // group statistics from LDS, then writes whole 32-bit code words, so any
 // number of blocks can run concurrently without read-modify-write.
@@ -45,6 +47,15 @@ __device__ __forceinline__ uint32_t encode(float x, float s, float z) {
   return (uint32_t)c;
 }
 
+// metadata store: binary32, or binary16 rounded to nearest even
+template <bool MH>
+__device__ __forceinline__ void put_meta(void* p, size_t i, float x) {
+  if constexpr (MH)
+    static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  else
+    static_cast<float*>(p)[i] = x;
+}
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // 16-byte copy with a non-temporal (read-once) source load
 __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
@@ -53,11 +64,11 @@ __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
 }
 
 // One block per (group of G source tokens, b*H + h).
-template <int BITS>
+template <int BITS, bool MH>
 __global__ void __launch_bounds__(256)
 quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
-                  int dst_off, uint32_t* __restrict__ codes, float* __restrict__ scale,
-                  float* __restrict__ zero) {
+                  int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
+                  void* __restrict__ zero) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
   float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
@@ -82,8 +93,8 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
     s_sc[d] = s;
     s_zr[d] = mn;
     size_t m = (bh * (cap / G) + gg) * D + d;
-    scale[m] = s;
-    zero[m] = mn;
+    put_meta<MH>(scale, m, s);
+    put_meta<MH>(zero, m, mn);
   }
   __syncthreads();
 
@@ -104,11 +115,11 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
 
 // One block per (32 source tokens, b*H + h).  Value codes are stored in
 // 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E) + (t%64)/E.
-template <int BITS>
+template <int BITS, bool MH>
 __global__ void __launch_bounds__(256)
 quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_stride,
-                  int dst_off, uint32_t* __restrict__ codes, float* __restrict__ scale,
-                  float* __restrict__ zero) {
+                  int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
+                  void* __restrict__ zero) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [32][D]
   const int NG = D / G;
@@ -136,8 +147,8 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
     s_sc[it] = s;
     s_zr[it] = mn;
     size_t m = (bh * cap + t_base + t) * NG + j;
-    scale[m] = s;
-    zero[m] = mn;
+    put_meta<MH>(scale, m, s);
+    put_meta<MH>(zero, m, mn);
   }
   __syncthreads();
 
@@ -181,29 +192,31 @@ copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restric
 
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G, int cap,
                              int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             float* scale, float* zero, hipStream_t st) {
+                             void* scale, void* zero, int mh, hipStream_t st) {
   dim3 grid(ntok / G, B * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero);
+  };
   if (bits == 2)
-    quantize_k_kernel<2><<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes,
-                                                 scale, zero);
+    mh ? go(quantize_k_kernel<2, true>) : go(quantize_k_kernel<2, false>);
   else
-    quantize_k_kernel<4><<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes,
-                                                 scale, zero);
+    mh ? go(quantize_k_kernel<4, true>) : go(quantize_k_kernel<4, false>);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G, int cap,
                              int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             float* scale, float* zero, hipStream_t st) {
+                             void* scale, void* zero, int mh, hipStream_t st) {
   dim3 grid(ntok / 32, B * H);
   size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero);
+  };
   if (bits == 2)
-    quantize_v_kernel<2><<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes,
-                                                 scale, zero);
+    mh ? go(quantize_v_kernel<2, true>) : go(quantize_v_kernel<2, false>);
   else
-    quantize_v_kernel<4><<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes,
-                                                 scale, zero);
+    mh ? go(quantize_v_kernel<4, true>) : go(quantize_v_kernel<4, false>);
   return hipGetLastError();
 }
 

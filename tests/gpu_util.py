@@ -41,7 +41,8 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 def gpu_cache_from_oracle_shape(oc, device="cuda"):
     from kv_cache_bit_kivi_amd.cache import KiviCache
-    return KiviCache(oc.B, oc.H, oc.r, oc.D, oc.bits, oc.G, oc.R, oc.cap, device=device)
+    return KiviCache(oc.B, oc.H, oc.r, oc.D, oc.bits, oc.G, oc.R, oc.cap, device=device,
+                     meta_half=oc.meta_half)
 
 
 def assert_cache_equal(gc, oc, planes=None, what=""):
@@ -59,6 +60,9 @@ def assert_cache_equal(gc, oc, planes=None, what=""):
         o = getattr(oc, oname)
         if g.dtype == np.float32:
             g, o = g.view(np.uint32), o.view(np.uint32)
+        elif g.dtype == np.float16:           # binary16 metadata: compare the bits
+            g = g.view(np.uint16)
+            assert o.dtype == np.uint16, (gname, o.dtype)
         if not np.array_equal(g, o):
             bad = np.argwhere(g != o)
             raise AssertionError(f"{what} {gname}: {len(bad)} mismatches, first at "

@@ -39,7 +39,7 @@ def test_strerror():
 
 def shape(**kw):
     d = dict(batch=2, num_kv_heads=4, gqa_ratio=2, head_dim=128, bits=2, group=32,
-             residual=128, capacity=512)
+             residual=128, capacity=512, meta_half=0)
     d.update(kw)
     return kivi_shape(*[d[n] for n, _ in kivi_shape._fields_])
 
@@ -58,6 +58,12 @@ def test_cache_bytes():
                   planes * cap * 4 * 4, planes * 128 * D * 2, planes * 2 * D * 2]
     rc, sz = sizes(shape(bits=4))
     assert sz[0] == planes * cap * D // 2
+    # binary16 metadata: half the scale / zero bytes, nothing else changes
+    rc, sz16 = sizes(shape(meta_half=1))
+    assert rc == KIVI_OK
+    _, sz32 = sizes(shape())
+    assert sz16[1] * 2 == sz32[1] and sz16[3] * 2 == sz32[3]
+    assert [sz16[i] for i in (0, 2, 4, 5)] == [sz32[i] for i in (0, 2, 4, 5)]
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -68,6 +74,7 @@ def test_cache_bytes():
     (dict(residual=48), KIVI_ESHAPE), (dict(residual=16, group=32), KIVI_ESHAPE),
     (dict(capacity=96), KIVI_ESHAPE), (dict(capacity=-64), KIVI_ESHAPE),
     (dict(group=128, capacity=192), KIVI_ESHAPE),
+    (dict(meta_half=2), KIVI_EINVAL), (dict(meta_half=-1), KIVI_EINVAL),
 ])
 def test_shape_errors(kw, code):
     assert sizes(shape(**kw))[0] == code

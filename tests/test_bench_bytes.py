@@ -1,0 +1,36 @@
+"""The benchmark's algorithmic byte counts agree with the library's own
+buffer sizes (kivi_cache_bytes) for a cache filled to capacity, for both
+metadata widths, so the roofline's bytes per launch are the cache's bytes."""
+import ctypes
+
+import pytest
+
+import bench
+from kv_cache_bit_kivi_amd import _lib
+from kv_cache_bit_kivi_amd.cache import make_shape
+
+
+@pytest.mark.parametrize("meta_half", [False, True])
+@pytest.mark.parametrize("B,H,r,D,bits,G,R,cap", [
+    (8, 32, 1, 128, 2, 32, 128, 4096),
+    (2, 8, 4, 128, 4, 32, 128, 1024),
+    (1, 2, 2, 64, 2, 64, 64, 512),
+])
+def test_decode_bytes_match_cache_sizes(meta_half, B, H, r, D, bits, G, R, cap):
+    s = make_shape(B, H, r, D, bits, G, R, cap, meta_half)
+    sz = [ctypes.c_size_t() for _ in range(6)]
+    assert _lib.kivi_cache_bytes(ctypes.byref(s), *[ctypes.byref(x) for x in sz]) == 0
+    kc, km, vc, vm, res, q = [x.value for x in sz]
+    mb = 2 if meta_half else 4
+    # decode at tq = cap, tr = R: every code, 2 metadata arrays each side,
+    # both residual planes, the query and the output
+    want = kc + vc + 2 * km + 2 * vm + 2 * res + 2 * q
+    assert bench.decode_bytes(B, H, r, D, bits, G, cap, R, mb) == want
+    # a flush reads R tokens of K and V and writes their codes and metadata;
+    # plus the new token read and written
+    per_tok_codes = kc // cap
+    flush = (2 * res + 2 * per_tok_codes * R + 2 * (km // (cap // G)) * (R // G)
+             + 2 * (vm // cap) * R)
+    tok = 2 * B * H * D * 2 * 2
+    assert bench.append_bytes(B, H, D, bits, G, R, True, mb) == tok + flush
+    assert bench.append_bytes(B, H, D, bits, G, R, False, mb) == tok

@@ -1,0 +1,190 @@
+"""Binary16 scale / zero (meta_half) on the GPU against the oracle's
+meta_half variant: codes, scales and zeros bit-exact (quantize, prefill,
+append through flushes), decode attention within the usual row bar on both
+kernel paths, the fused step equal to the separate calls, and the full-size
+Llama-2-7B-shaped batch-8 layer."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import synth
+from kv_cache_bit_kivi_amd.cache import KiviCache, make_shape, quantize_k, quantize_v
+from tests.gpu_util import (ATTN_TOL, announce, assert_cache_equal, dev, host, require_gpu,
+                            row_rel_err)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 0.0883883461356163
+
+
+def gpu_quant16(fn, x, bits, G, cap, ntok, dst):
+    B, H, T, D = x.shape
+    E = 32 // bits
+    shape = make_shape(B, H, 1, D, bits, G, max(G, 32), cap, meta_half=True)
+    if fn is quantize_k:
+        codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device="cuda")
+        sc = torch.zeros((B, H, cap // G, D), dtype=torch.float16, device="cuda")
+    else:
+        codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device="cuda")
+        sc = torch.zeros((B, H, cap, D // G), dtype=torch.float16, device="cuda")
+    zr = torch.zeros_like(sc)
+    fn(shape, dev(x), ntok, dst, codes, sc, zr)
+    return host(codes), host(sc).view(np.uint16), host(zr).view(np.uint16)
+
+
+def compare16(x, bits, G, cap, ntok, dst, what):
+    for gfn, ofn in ((quantize_k, oracle.quantize_k), (quantize_v, oracle.quantize_v)):
+        gc, gs, gz = gpu_quant16(gfn, x, bits, G, cap, ntok, dst)
+        oc, os_, oz = ofn(x, bits, G, cap, ntok, dst, meta_half=True)
+        name = f"{what} {gfn.__name__}"
+        assert np.array_equal(gc, oc), name + " codes"
+        bad = np.argwhere(gs != os_)
+        assert bad.size == 0, (name + " scale", bad[:3].tolist(),
+                               gs[tuple(bad[0])] if bad.size else None,
+                               os_[tuple(bad[0])] if bad.size else None)
+        assert np.array_equal(gz, oz), name + " zero"
+
+
+CODEC_CASES = [
+    # bits, B, H, D, G, T_in, ntok, dst, cap
+    (2, 1, 2, 128, 32, 512, 512, 0, 512),
+    (4, 1, 2, 128, 32, 512, 512, 0, 512),
+    (2, 2, 3, 64, 32, 96, 96, 32, 192),
+    (4, 2, 3, 64, 64, 200, 128, 64, 256),
+    (4, 1, 2, 256, 128, 256, 256, 128, 384),
+]
+
+
+@pytest.mark.parametrize("case", CODEC_CASES, ids=lambda c: "b%d_B%dH%dD%dG%d_n%d_o%d" % (
+    c[0], c[1], c[2], c[3], c[4], c[6], c[7]))
+def test_quantize16_shapes(case):
+    require_gpu()
+    bits, B, H, D, G, T, ntok, dst, cap = case
+    announce(f"quantize meta16 {case}")
+    x = synth.random_fp16(sum(case), (B, H, T, D), scale=2.0)
+    x[..., 1] *= np.float16(10)
+    compare16(x, bits, G, cap, ntok, dst, str(case))
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_quantize16_scale_rounding(bits):
+    """Scales across the whole binary16 range: subnormal results (ranges of a
+    few 2^-24 ulps, where the scale rounds to a multiple of 2^-24 or to
+    zero), every binade in between, and the largest ranges (+-65504)."""
+    require_gpu()
+    announce(f"quantize meta16 scale rounding bits={bits}")
+    G, D, T = 32, 128, 256
+    rng = np.random.default_rng(77 + bits)
+    # per (token group, channel) spread: integer multiples of 2^-24 up to m,
+    # then binades 2^e for e in [-24, 15]
+    x = np.zeros((1, 4, T, D), np.float32)
+    m = rng.integers(1, 48, (T // G, D))
+    ints = rng.integers(0, 48, (T, D))
+    x[0, 0] = np.minimum(ints, np.repeat(m, G, axis=0)) * 2.0 ** -24
+    e = rng.integers(-24, 16, (T // G, D)).astype(np.float64)
+    x[0, 1] = rng.uniform(-1, 1, (T, D)) * np.repeat(2.0 ** e, G, axis=0)
+    x[0, 2] = rng.choice([-65504.0, 65504.0, -1.0, 0.5], (T, D))
+    x[0, 3] = rng.integers(-3, 4, (T, D)) * 2.0 ** -14 + 1000.0
+    x = np.clip(x, -65504, 65504).astype(np.float16)
+    compare16(x, bits, G, T, T, 0, "scale rounding")
+
+
+@pytest.mark.parametrize("shp", [
+    # B, H, r, D, bits, G, R, tq, tr
+    (2, 2, 1, 128, 2, 32, 128, 992, 128),     # half-filled last value tile
+    (2, 2, 1, 128, 4, 32, 128, 1024, 77),
+    (1, 3, 4, 128, 2, 32, 128, 2016, 100),
+    (1, 2, 8, 128, 2, 32, 128, 512, 40),
+    (2, 1, 2, 128, 4, 32, 32, 640, 32),
+    (2, 2, 2, 64, 4, 64, 128, 448, 1),        # generic kernel
+    (3, 1, 1, 32, 2, 32, 32, 96, 31),         # generic kernel
+    (1, 2, 1, 128, 2, 32, 128, 0, 97),        # residual only
+], ids=lambda s: "B%dH%dr%dD%db%dG%dR%d_tq%d_tr%d" % s)
+@pytest.mark.parametrize("splits", [0, 1, 5])
+def test_decode16_shapes(shp, splits):
+    require_gpu()
+    B, H, r, D, bits, G, R, tq, tr = shp
+    announce(f"decode meta16 {shp} splits={splits}")
+    if splits > tq + tr:
+        pytest.skip("more splits than tokens")
+    seed = sum(shp)
+    L = tq + tr
+    cap = max(64, (tq + R + 63) // 64 * 64)
+    cap = (cap + G - 1) // G * G
+    k = synth.random_fp16(seed, (B, H, L, D), scale=2.0)
+    k[..., 5] *= np.float16(10)
+    v = synth.random_fp16(seed + 1, (B, H, L, D))
+    q = synth.random_fp16(seed + 2, (B, H * r, D))
+    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    gc.prefill(dev(k), dev(v), tq)
+    oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    oc.prefill(k, v, tq)
+    assert_cache_equal(gc, oc, what="prefill")
+    ref = oc.decode(q, SCALE)
+    out = host(gc.decode(dev(q), SCALE, num_splits=splits)).astype(np.float64)
+    err = row_rel_err(out, ref)
+    assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("r", [1, 4])
+def test_stream16_fused(bits, r):
+    """Appends through two flushes: the fused step equals append + decode bit
+    for bit, every cache buffer equals the oracle's, attention within the bar."""
+    require_gpu()
+    announce(f"stream meta16 bits={bits} r={r}")
+    B, H, D, G, R = 2, 2, 128, 32, 32
+    tq0, tr0, n = 128, 30, 2 * R + 5
+    T = tq0 + tr0 + n
+    k = synth.random_fp16(900 + bits + r, (B, H, T, D), scale=1.5)
+    k[..., 2] *= np.float16(10)
+    v = synth.random_fp16(910 + bits + r, (B, H, T, D))
+    qs = synth.random_fp16(920 + bits + r, (n, B, H * r, D))
+    cap = (T + R + 63) // 64 * 64
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
+    sep.prefill(kd, vd, tq0)
+    fus.prefill(kd, vd, tq0)
+    oc.prefill(k[:, :, : tq0 + tr0], v[:, :, : tq0 + tr0], tq0)
+    for i in range(n):
+        t = tq0 + tr0 + i
+        kn, vn = np.ascontiguousarray(k[:, :, t]), np.ascontiguousarray(v[:, :, t])
+        q = dev(qs[i])
+        sep.append(dev(kn), dev(vn))
+        o_sep = host(sep.decode(q, SCALE))
+        o_fus = host(fus.append_decode(dev(kn), dev(vn), q, SCALE))
+        assert np.array_equal(o_fus.view(np.uint16), o_sep.view(np.uint16)), f"step {i}"
+        oc.append(kn, vn)
+        if i in (0, 1, 2, R + 2, n - 1):
+            assert_cache_equal(fus, oc, what=f"fused step {i}")
+            assert_cache_equal(sep, oc, what=f"separate step {i}")
+        ref = oc.decode(np.ascontiguousarray(qs[i]), SCALE)
+        err = row_rel_err(o_fus.astype(np.float64), ref)
+        assert err <= ATTN_TOL, (i, err)
+    assert oc.flushes == 3   # at appends 3, 35 and 67
+
+
+def test_decode16_workload():
+    """The batch-8 Llama-2-7B-shaped layer (32 heads, head_dim 128, 4096
+    quantized + 128 residual tokens, 2-bit, G = 32) with binary16 metadata:
+    prefill bit-exact, decode of every row within the bar."""
+    require_gpu()
+    w = synth.WORKLOADS["llama2_7b_b8_ctx4096"]
+    announce("decode meta16 llama2_7b_b8_ctx4096")
+    k, v = synth.kv(w)
+    q = synth.query(w)
+    gc = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual,
+                   w.capacity(), meta_half=True)
+    gc.prefill(dev(k), dev(v), w.tq)
+    out = host(gc.decode(dev(q), w.softmax_scale)).astype(np.float64)
+    oc = oracle.OracleCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
+                            w.residual, w.capacity(), meta_half=True)
+    oc.prefill(k, v, w.tq)
+    assert_cache_equal(gc, oc, what="prefill")
+    ref = oc.decode(q, w.softmax_scale)
+    err = row_rel_err(out, ref)
+    assert err <= ATTN_TOL, err
+    torch.cuda.synchronize()
