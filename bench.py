@@ -15,8 +15,9 @@ once per 128 appends, the method's own rate.
 
 Prints one JSON line: whole-step algorithmic HBM GB/s (value), query-heads/s,
 the roofline of the dominant kernel (decode attention with the folded append,
-timed with HIP events on the launch stream around each call) and the CPU
-oracle timed on a bounded sample.
+timed with HIP events on the launch stream around windows of `--window`
+consecutive calls inside the timed region, windows holding a flush left out)
+and the CPU oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -193,6 +194,8 @@ def main():
                     help="storage of the quantization scales and zeros")
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
+    ap.add_argument("--window", type=int, default=16, metavar="W",
+                    help="HIP events bracket windows of W consecutive timed steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -272,7 +275,8 @@ def main():
     import ctypes
 
     L = lib()
-    stream = torch.cuda.current_stream().cuda_stream
+    cur = torch.cuda.current_stream()
+    stream = cur.cuda_stream
     crefs = [ctypes.byref(c.c) for c in caches]
     kptr = [t.data_ptr() for t in knew]
     vptr = [t.data_ptr() for t in vnew]
@@ -284,7 +288,7 @@ def main():
     append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
     fused_fn = L.kivi_append_decode_attn
 
-    def step(i, ev=None):
+    def step(i, ev0=None, ev1=None):
         li = i % NL
         c = caches[li].c
         j = i % n_tok
@@ -293,17 +297,17 @@ def main():
             rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
             if rc:
                 raise RuntimeError(f"kivi_append failed: {rc}")
-            if ev is not None:
-                ev[0].record()
+            if ev0 is not None:
+                ev0.record(cur)
             rc = decode_fn(crefs[li], qptr[j], scale, optr[li], wsp[li][0], wsp[li][1],
                            args.splits, stream)
         else:
-            if ev is not None:
-                ev[0].record()
+            if ev0 is not None:
+                ev0.record(cur)
             rc = fused_fn(crefs[li], kptr[j], vptr[j], qptr[j], scale, optr[li], wsp[li][0],
                           wsp[li][1], args.splits, stream)
-        if ev is not None:
-            ev[1].record()
+        if ev1 is not None:
+            ev1.record(cur)
         if rc:
             raise RuntimeError(f"decode step failed: {rc}")
         return flush, c.tq, c.tr
@@ -315,13 +319,21 @@ def main():
         c.set_lengths(w.tq, w.tr)
     splits_used = caches[0].auto_splits() if args.splits == 0 else args.splits
 
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
+    # HIP events on the launch stream bracket windows of W consecutive steps
+    # (an event is a packet on that stream: bracketing every launch would add
+    # its own dispatch latency to each measured launch and slow the loop).
+    W = max(1, min(args.window, args.steps))
+    nwin = args.steps // W
+    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(nwin)]
     meta = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        meta.append(step(i, events[i]))
+        wi, j = divmod(i, W)
+        e0 = wev[wi][0] if wi < nwin and j == 0 else None
+        e1 = wev[wi][1] if wi < nwin and j == W - 1 else None
+        meta.append(step(i, e0, e1))
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
@@ -332,10 +344,21 @@ def main():
     # fused.  Flush steps (a full residual quantized first: 1 in R steps per
     # layer) also run the quantize launches inside the timed interval, so the
     # roofline of the decode kernel averages the other steps only.
-    plain = [not f for f, _, _ in meta]
+    # windows holding a flush step (a full residual quantized first) are left
+    # out: the roofline is that of the decode launch alone
     new_tok = append_bytes(B, H, D, bits, G, R, False, mb)
-    call_bytes = np.array([d + (0 if args.separate else new_tok) for d in dec_bytes])[plain]
-    dec_ms = np.array([a.elapsed_time(b) for a, b in events])[plain]
+    per_call = [d + new_tok for d in dec_bytes]   # (separate mode: the append launch too)
+    win_ms, win_bytes = [], []
+    for wi in range(nwin):
+        steps_w = range(wi * W, (wi + 1) * W)
+        if any(meta[i][0] for i in steps_w):
+            continue
+        win_ms.append(wev[wi][0].elapsed_time(wev[wi][1]) / W)
+        win_bytes.append(sum(per_call[i] for i in steps_w) / W)
+    if not win_ms:
+        raise SystemExit("no window of the timed region is free of flush steps: raise --steps")
+    call_bytes = np.array(win_bytes)
+    dec_ms = np.array(win_ms)
     value = total_bytes / elapsed / 1e9
     achieved = call_bytes.mean() / (dec_ms.mean() * 1e-3) / 1e9
     n_flush = sum(1 for f, _, _ in meta if f)
@@ -366,19 +389,21 @@ def main():
         "query_heads_per_s": round(args.steps * B * H * r / elapsed, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("kivi decode attention (one kivi_decode_attn call)" if args.separate else
-                       "kivi decode attention with the append folded in (one "
-                       "kivi_append_decode_attn call); flush steps excluded"),
+            "kernel": ("kivi_append + kivi_decode_attn (two launches per step)" if args.separate
+                       else "kivi decode attention with the append folded in (one "
+                       "kivi_append_decode_attn launch per step)") +
+                      f"; HIP events around windows of {W} steps, windows with a flush excluded",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(tag),
             "bytes_per_launch": int(call_bytes.mean()),
-            "launches_averaged": int(len(call_bytes)),
+            "launches_averaged": int(len(call_bytes)) * W,
+            "window_launches": W,
             "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 3),
-            "p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-            "p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
+            "window_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
+            "window_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
         },
         "kernel_source_hash": kernel_source_hash(),
     }
