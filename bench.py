@@ -408,7 +408,7 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half)
     print(json.dumps(result), flush=True)
 
 

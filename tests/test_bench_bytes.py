@@ -34,3 +34,15 @@ def test_decode_bytes_match_cache_sizes(meta_half, B, H, r, D, bits, G, R, cap):
     tok = 2 * B * H * D * 2 * 2
     assert bench.append_bytes(B, H, D, bits, G, R, True, mb) == tok + flush
     assert bench.append_bytes(B, H, D, bits, G, R, False, mb) == tok
+
+
+@pytest.mark.parametrize("meta_half", [False, True])
+def test_cpu_baseline_runs_its_sample(meta_half):
+    """The CPU leg keeps stepping until its time budget (or step cap) is
+    reached, for both metadata widths."""
+    from kv_cache_bit_kivi_amd import synth
+    w = synth.WORKLOADS["single_head_512"]
+    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, meta_half=meta_half)
+    steps = int(r["sample"].split()[0])
+    assert steps > 1
+    assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
