@@ -204,6 +204,76 @@ int kivi_append_decode_attn(kivi_cache* cache, const uint16_t* k_new,
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
 
+/* ---- Ragged batches: a different length for every sequence ------------
+ * In a serving batch every sequence has its own context length, so the
+ * quantized and residual token counts differ per sequence (study.space
+ * summary: tokens are appended along the token axis of each sequence's
+ * grouped + residual cache; scholarfeed "KIVI" quote page: the residual is a
+ * fixed-length buffer per sequence).  A kivi_ragged_cache has the same device
+ * buffers and layouts as kivi_cache (every sequence owns `capacity` token
+ * slots); its lengths are HOST arrays owned by the caller, tq[b] and tr[b]
+ * for b < shape.batch, each obeying the kivi_cache rules (tq[b] a multiple of
+ * group and <= capacity, 0 <= tr[b] <= residual).  Calls read them and, on
+ * success, update them in place; on error nothing is enqueued and they are
+ * unchanged.  Results for each sequence are bit-identical (codes, scales,
+ * zeros, residual) to a one-sequence kivi_cache holding that sequence alone;
+ * attention meets the same tolerance.  Per-sequence lengths travel with each
+ * launch (batches above 128 sequences take several launches). */
+typedef struct {
+  kivi_shape shape;
+  uint32_t* k_codes;
+  void* k_scale;
+  void* k_zero;
+  uint32_t* v_codes;
+  void* v_scale;
+  void* v_zero;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  int32_t* tq;       /* host [batch] */
+  int32_t* tr;       /* host [batch] */
+} kivi_ragged_cache;
+
+/* Fill an empty ragged cache from padded prompts.  k, v: fp16
+ * [B][Hkv][in_tok_stride][D]; sequence b has ntok[b] tokens (0 <= ntok[b] <=
+ * in_tok_stride, host array); tokens [0, tq[b]) are quantized (tq[b] a
+ * multiple of group, <= capacity: KIVI_ECAPACITY otherwise) and tokens
+ * [tq[b], ntok[b]) copied into the residual (ntok[b] - tq[b] <= residual).
+ * A sequence may be empty (ntok[b] = 0).  Sets cache->tq, cache->tr. */
+int kivi_ragged_prefill(kivi_ragged_cache* cache, const uint16_t* k,
+                        const uint16_t* v, int32_t in_tok_stride,
+                        const int32_t* ntok, const int32_t* tq, void* stream);
+
+/* Append one token to every sequence (k_new, v_new: fp16 [B][Hkv][D]).  Each
+ * sequence whose residual is full is flushed first, as in kivi_append
+ * (KIVI_ECAPACITY if any of them would overflow capacity). */
+int kivi_ragged_append(kivi_ragged_cache* cache, const uint16_t* k_new,
+                       const uint16_t* v_new, void* stream);
+
+/* Split count kivi_ragged_decode_attn uses when num_splits == 0 (chosen for
+ * the longest sequence).  Returns >= 1, or a negative error code. */
+int kivi_ragged_decode_auto_splits(const kivi_ragged_cache* cache);
+
+/* Decode attention for every sequence at its own lengths (the operation of
+ * kivi_decode_attn).  Every sequence must hold at least one token
+ * (KIVI_ESHAPE).  num_splits (0 = automatic) applies to every sequence; a
+ * split past a short sequence's end contributes nothing.  The workspace is
+ * sized by kivi_decode_workspace_bytes(&cache->shape, num_splits). */
+int kivi_ragged_decode_attn(const kivi_ragged_cache* cache, const uint16_t* q,
+                            float softmax_scale, uint16_t* out,
+                            void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream);
+
+/* One decode step of a ragged batch: exactly kivi_ragged_append followed by
+ * kivi_ragged_decode_attn (same validation, bit-identical results), with the
+ * append folded into the decode launch where the matrix-core kernel
+ * applies. */
+int kivi_ragged_append_decode_attn(kivi_ragged_cache* cache,
+                                   const uint16_t* k_new,
+                                   const uint16_t* v_new, const uint16_t* q,
+                                   float softmax_scale, uint16_t* out,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t num_splits, void* stream);
+
 /* Short static description of a status code. */
 const char* kivi_strerror(int status);
 

@@ -43,11 +43,23 @@ class kivi_cache(ctypes.Structure):
     ]
 
 
+class kivi_ragged_cache(ctypes.Structure):
+    _fields_ = [
+        ("shape", kivi_shape),
+        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("tq", ctypes.POINTER(ctypes.c_int32)), ("tr", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
 # name -> (restype, argtypes), mirroring include/kivi.h
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SZP = ctypes.POINTER(ctypes.c_size_t)
 _SHP = ctypes.POINTER(kivi_shape)
 _CP = ctypes.POINTER(kivi_cache)
+_RP = ctypes.POINTER(kivi_ragged_cache)
+_I32P = ctypes.POINTER(ctypes.c_int32)
 PROTOTYPES = {
     "kivi_cache_bytes": (ctypes.c_int, [_SHP, _SZP, _SZP, _SZP, _SZP, _SZP, _SZP]),
     "kivi_quantize_k": (ctypes.c_int, [_SHP, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -59,6 +71,12 @@ PROTOTYPES = {
     "kivi_decode_attn": (ctypes.c_int, [_CP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
     "kivi_append_decode_attn": (ctypes.c_int, [_CP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz,
                                                _i32, _vp]),
+    "kivi_ragged_prefill": (ctypes.c_int, [_RP, _vp, _vp, _i32, _I32P, _I32P, _vp]),
+    "kivi_ragged_append": (ctypes.c_int, [_RP, _vp, _vp, _vp]),
+    "kivi_ragged_decode_auto_splits": (ctypes.c_int, [_RP]),
+    "kivi_ragged_decode_attn": (ctypes.c_int, [_RP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
+    "kivi_ragged_append_decode_attn": (ctypes.c_int, [_RP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                                      _sz, _i32, _vp]),
     "kivi_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -111,4 +129,9 @@ kivi_decode_auto_splits = _fn("kivi_decode_auto_splits")
 kivi_decode_workspace_bytes = _fn("kivi_decode_workspace_bytes")
 kivi_decode_attn = _fn("kivi_decode_attn")
 kivi_append_decode_attn = _fn("kivi_append_decode_attn")
+kivi_ragged_prefill = _fn("kivi_ragged_prefill")
+kivi_ragged_append = _fn("kivi_ragged_append")
+kivi_ragged_decode_auto_splits = _fn("kivi_ragged_decode_auto_splits")
+kivi_ragged_decode_attn = _fn("kivi_ragged_decode_attn")
+kivi_ragged_append_decode_attn = _fn("kivi_ragged_append_decode_attn")
 kivi_strerror = _fn("kivi_strerror")

@@ -9,8 +9,10 @@ import ctypes
 
 import torch
 
+import numpy as np
+
 from . import _lib
-from ._lib import check, kivi_cache, kivi_shape
+from ._lib import check, kivi_cache, kivi_ragged_cache, kivi_shape
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -142,3 +144,83 @@ def quantize_v(shape: kivi_shape, v: torch.Tensor, ntok: int, dst_off: int, code
     check(_lib.kivi_quantize_v(ctypes.byref(shape), v.data_ptr(), v.shape[2], ntok, dst_off,
                                codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()),
           "kivi_quantize_v")
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class RaggedKiviCache(KiviCache):
+    """A batch whose sequences have their own lengths: the same device
+    buffers as KiviCache, per-sequence host length arrays ``tq``, ``tr``
+    (int32 NumPy arrays the C struct points at; the library updates them)."""
+
+    def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                 device="cuda", meta_half=False):
+        super().__init__(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                         device=device, meta_half=meta_half)
+        self.tq_arr = np.zeros(batch, np.int32)
+        self.tr_arr = np.zeros(batch, np.int32)
+        self.rc = kivi_ragged_cache(self.shape, *[t.data_ptr() for t in (
+            self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
+            self.k_res, self.v_res)], _i32p(self.tq_arr), _i32p(self.tr_arr))
+
+    @property
+    def tq(self) -> np.ndarray:
+        return self.tq_arr.copy()
+
+    @property
+    def tr(self) -> np.ndarray:
+        return self.tr_arr.copy()
+
+    def set_lengths(self, tq, tr) -> None:
+        self.tq_arr[:] = tq
+        self.tr_arr[:] = tr
+
+    def prefill(self, k: torch.Tensor, v: torch.Tensor, ntok, tq) -> None:
+        """k, v: fp16 [B][Hkv][T][D]; sequence b uses its first ntok[b] tokens,
+        the first tq[b] of them quantized."""
+        assert k.dtype == torch.float16 and k.is_contiguous() and v.is_contiguous()
+        n = np.ascontiguousarray(ntok, np.int32)
+        t = np.ascontiguousarray(tq, np.int32)
+        check(_lib.kivi_ragged_prefill(ctypes.byref(self.rc), k.data_ptr(), v.data_ptr(),
+                                       k.shape[2], _i32p(n), _i32p(t), _stream()),
+              "kivi_ragged_prefill")
+
+    def append(self, k_new: torch.Tensor, v_new: torch.Tensor) -> None:
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        check(_lib.kivi_ragged_append(ctypes.byref(self.rc), k_new.data_ptr(), v_new.data_ptr(),
+                                      _stream()), "kivi_ragged_append")
+
+    def decode(self, q: torch.Tensor, softmax_scale: float, out: torch.Tensor | None = None,
+               num_splits: int = 0) -> torch.Tensor:
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_ragged_decode_attn(ctypes.byref(self.rc), q.data_ptr(),
+                                           float(softmax_scale), out.data_ptr(), _ptr(ws), nb,
+                                           num_splits, _stream()), "kivi_ragged_decode_attn")
+        return out
+
+    def append_decode(self, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                      softmax_scale: float, out: torch.Tensor | None = None,
+                      num_splits: int = 0) -> torch.Tensor:
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_ragged_append_decode_attn(
+            ctypes.byref(self.rc), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(),
+            float(softmax_scale), out.data_ptr(), _ptr(ws), nb, num_splits, _stream()),
+            "kivi_ragged_append_decode_attn")
+        return out
+
+    def auto_splits(self) -> int:
+        s = _lib.kivi_ragged_decode_auto_splits(ctypes.byref(self.rc))
+        if s < 0:
+            check(-s, "kivi_ragged_decode_auto_splits")
+        return s

@@ -54,8 +54,9 @@ __device__ float block_reduce(float v, bool is_max, float* scratch) {
 template <int RR>
 constexpr int sub_tokens() { return RR <= 2 ? 1024 : 2048 / RR; }
 
-template <int RR>
-__global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, int chunk) {
+template <int RR, bool RAG>
+__global__ void __launch_bounds__(kThreads)
+decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   constexpr int kSub = sub_tokens<RR>();
   extern __shared__ __align__(16) float sm[];
   const int r = a.r, D = a.D, G = a.G, bits = a.bits;
@@ -68,7 +69,9 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
   const int split = blockIdx.x;
   const int u = blockIdx.y;          // b * H + h
   const int b = u / a.H, h = u % a.H;
-  const int L = a.tq + a.tr;
+  const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
+  const int L = tq + tr;
+  if constexpr (RAG) chunk = (L + a.S - 1) / a.S;   // per sequence
   const int t0 = split * chunk;
   const int t1 = min(L, t0 + chunk);
   const int E = 32 / bits, W = D / E, WPC = 64 / E, NG = D / G;
@@ -108,7 +111,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
       float acc[RR];
 #pragma unroll
       for (int i = 0; i < RR; i++) acc[i] = 0.f;
-      if (t < a.tq) {
+      if (t < tq) {
         const uint32_t* row = kc + (size_t)t * W;
         const size_t m0 = (size_t)(t / G) * D;
         for (int w = 0; w < W; w++) {
@@ -123,7 +126,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
           }
         }
       } else {
-        const uint16_t* row = kr + (size_t)(t - a.tq) * D;
+        const uint16_t* row = kr + (size_t)(t - tq) * D;
         for (int dd = 0; dd < D; dd++) {
           const float kh = h2f(row[dd]);
 #pragma unroll
@@ -167,13 +170,13 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a, 
         if (i < r) o[i] *= stat[2 * RR + i];
       for (int t = c0 + sub; t < c1; t += nsub) {
         float vh;
-        if (t < a.tq) {
+        if (t < tq) {
           const uint32_t word = vc[((size_t)(t / 64) * D + d) * WPC + (t % 64) / E];
           const int j = d / G;
           vh = (float)((word >> (bits * ((t % 64) % E))) & mask) *
                    meta_at(vs, (size_t)t * NG + j, mh) + meta_at(vz, (size_t)t * NG + j, mh);
         } else {
-          vh = h2f(vr[(size_t)(t - a.tq) * D + d]);
+          vh = h2f(vr[(size_t)(t - tq) * D + d]);
         }
 #pragma unroll
         for (int i = 0; i < RR; i++)
@@ -233,22 +236,31 @@ size_t decode_generic_lds_bytes(int r, int D) {
   return sizeof(float) * ((size_t)r * D + (size_t)r * sub + (size_t)rr * kThreads + 8 + 3 * rr);
 }
 
-hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+template <bool RAG>
+static hipError_t launch_generic(const DecodeArgs& a, const LensT<RAG>& lens, hipStream_t st) {
   const int L = a.tq + a.tr;
-  const int chunk = (L + a.S - 1) / a.S;
+  const int chunk = (L + a.S - 1) / a.S;   // (per sequence in the kernel when ragged)
   dim3 grid(a.S, a.B * a.H);
   const size_t lds = decode_generic_lds_bytes(a.r, a.D);
   if (a.r == 1)
-    decode_generic_kernel<1><<<grid, kThreads, lds, st>>>(a, chunk);
+    decode_generic_kernel<1, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r == 2)
-    decode_generic_kernel<2><<<grid, kThreads, lds, st>>>(a, chunk);
+    decode_generic_kernel<2, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r <= 4)
-    decode_generic_kernel<4><<<grid, kThreads, lds, st>>>(a, chunk);
+    decode_generic_kernel<4, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r <= 8)
-    decode_generic_kernel<8><<<grid, kThreads, lds, st>>>(a, chunk);
+    decode_generic_kernel<8, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else
-    decode_generic_kernel<16><<<grid, kThreads, lds, st>>>(a, chunk);
+    decode_generic_kernel<16, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
+  return launch_generic<false>(a, NoLens{}, st);
+}
+
+hipError_t launch_decode_generic_ragged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st) {
+  return launch_generic<true>(a, lens, st);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {

@@ -42,923 +42,9 @@
 // Codes are staged through LDS and re-read in the MFMA operand layout.  The
 // block merges its waves in LDS; one split writes fp16 output, more splits
 // write (max, sum, o) partials for the combine kernel.
-#include <math.h>
-
-#include <atomic>
-#include <type_traits>
-
-#include "kivi_internal.h"
+#include "decode_mfma_impl.h"
 
 namespace kivi {
-namespace {
-
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef __fp16 hrtz2 __attribute__((ext_vector_type(2)));
-typedef float float4v __attribute__((ext_vector_type(4)));
-
-constexpr int kD = 128;
-constexpr int kG = 32;
-constexpr int kNG = kD / kG;   // value groups per token
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-constexpr float kLazy = 8.f;   // log2 slack of the online-softmax reference
-
-__device__ __forceinline__ float h2f(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-__device__ __forceinline__ uint16_t f2h(float x) {
-  return __builtin_bit_cast(uint16_t, (_Float16)x);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_read(float v, int l) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-// all-lane reductions over the 64-lane wave (result uniform)
-__device__ __forceinline__ float wave_sum(float v) {
-  v += dpp<0x128>(v);  // row_ror:8
-  v += dpp<0x124>(v);  // row_ror:4
-  v += dpp<0x122>(v);  // row_ror:2
-  v += dpp<0x121>(v);  // row_ror:1
-  return (lane_read(v, 0) + lane_read(v, 16)) + (lane_read(v, 32) + lane_read(v, 48));
-}
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp<0x128>(v));
-  v = fmaxf(v, dpp<0x124>(v));
-  v = fmaxf(v, dpp<0x122>(v));
-  v = fmaxf(v, dpp<0x121>(v));
-  return fmaxf(fmaxf(lane_read(v, 0), lane_read(v, 16)), fmaxf(lane_read(v, 32), lane_read(v, 48)));
-}
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// 8 two-bit codes held one per nibble (upper two bits zero) -> 8 exact halves,
-// slot s = nibble s
-__device__ __forceinline__ half8 cvt_nib2(uint32_t x) {
-  half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0);
-  half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1);
-  half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2);
-  half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3);
-  return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-// one word of 8 four-bit codes -> 8 exact halves; slots 0..3 = even
-// positions 0,2,4,6, slots 4..7 = odd positions 1,3,5,7
-__device__ __forceinline__ half8 cvt_word4(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  half2v a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);
-  half2v b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);
-  half2v c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);
-  half2v d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);
-  return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-// the same two code converts to bf16 (value side)
-__device__ __forceinline__ bf16x8 cvt_nib2_bf(uint32_t x) {
-  bf16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 0);
-  bf16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 1);
-  bf16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 2);
-  bf16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 3);
-  return bf16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
-}
-__device__ __forceinline__ bf16x8 cvt_word4_bf(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
-  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, false);
-  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 512.0f, true);
-  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, false);
-  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 512.0f, true);
-  return bf16x8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
-}
-__device__ __forceinline__ float4v mfma(half8 a, half8 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ float4v mfma_bf(bf16x8 a, bf16x8 b, float4v c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-// (hi, lo) bf16 pairs of two binary32 values: hi = x truncated to bf16, lo =
-// the remainder truncated; hi + lo = x within 2^-16 |x|, over the full
-// binary32 exponent range.  Lane 0 of each pair holds x0, lane 1 x1.
-__device__ __forceinline__ void split2_bf(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t u0 = __builtin_bit_cast(uint32_t, x0), u1 = __builtin_bit_cast(uint32_t, x1);
-  const float r0 = x0 - __builtin_bit_cast(float, u0 & 0xFFFF0000u);
-  const float r1 = x1 - __builtin_bit_cast(float, u1 & 0xFFFF0000u);
-  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);   // upper halves of u0, u1
-  lo = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, r1), __builtin_bit_cast(uint32_t, r0),
-                             0x07060302u);
-}
-// (hi, lo) fp16 pairs of two binary32 values: hi = x rounded toward zero,
-// lo = the remainder rounded toward zero; hi + lo = x within 2^-20 |x|
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const hrtz2 h = __builtin_amdgcn_cvt_pkrtz(x0, x1);
-  const hrtz2 l = __builtin_amdgcn_cvt_pkrtz(x0 - (float)h.x, x1 - (float)h.y);
-  hi = __builtin_bit_cast(uint32_t, h);
-  lo = __builtin_bit_cast(uint32_t, l);
-}
-
-// Raw buffer loads: a resource covers one plane; an offset at or past its end
-// returns zeros and touches no memory.  Absent tiles and tokens are loaded at
-// kOut instead of being branched around, so every wave issues one fixed load
-// sequence and the in-order completion counter stays exact.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOut = 0x80000000u;   // past every plane (planes stay < 2^31 bytes)
-// Cache policy of the streamed cache reads: non-temporal.  Every cache byte is
-// read once per call, so keeping it out of the normal cache-allocation path
-// costs nothing and measurably raises the achieved read bandwidth.
-constexpr int kStream = 2;
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-__device__ __forceinline__ uint4 ld16(rsrc_t r, uint32_t off) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream);
-  return uint4{v.x, v.y, v.z, v.w};
-}
-// (bit-cast the whole vector: clang bit-casts an ext-vector element access
-// from the vector's first element)
-__device__ __forceinline__ float4 ld16f(rsrc_t r, uint32_t off) {
-  const f32x4 v =
-      __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream));
-  return float4{v[0], v[1], v[2], v[3]};
-}
-__device__ __forceinline__ u32x4 ld16v(rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kStream);
-}
-// one 16-byte slice of residual token t: from the residual plane (zeros past
-// the slice), or from the new-token row when t is the freshly appended token.
-// The two arms are exec-masked loads into one register: one load per lane.
-__device__ __forceinline__ u32x4 ld_res(rsrc_t res, rsrc_t nw, int t, int t_end, int t_new,
-                                        uint32_t row_bytes, uint32_t col) {
-  u32x4 v;
-  if (t != t_new)
-    v = ld16v(res, t < t_end ? (uint32_t)t * row_bytes + col : kOut);
-  else
-    v = ld16v(nw, col);
-  return v;
-}
-__device__ __forceinline__ void st16(rsrc_t r, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
-}
-__device__ __forceinline__ uint2 ld8(rsrc_t r, uint32_t off) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-  return uint2{v.x, v.y};
-}
-__device__ __forceinline__ uint2 ld8s(rsrc_t r, uint32_t off) {
-  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kStream);
-  return uint2{v.x, v.y};
-}
-// four metadata values of a lane: binary32 as loaded, or four binary16 widened
-__device__ __forceinline__ float4 meta4(float4 v) { return v; }
-__device__ __forceinline__ float4 meta4(uint2 v) {
-  return float4{h2f((uint16_t)(v.x & 0xFFFFu)), h2f((uint16_t)(v.x >> 16)),
-                h2f((uint16_t)(v.y & 0xFFFFu)), h2f((uint16_t)(v.y >> 16))};
-}
-
-// slot of position q (0..7) inside a 4-bit word's half8
-__device__ __forceinline__ int slot4(int q) { return (q & 1) ? 4 + (q >> 1) : (q >> 1); }
-
-// Key side: channel c' (0..31 inside a lane group's 32 channels) -> (mfma m, slot s)
-template <int BITS>
-__device__ __forceinline__ void k_pos(int cp, int& m, int& s) {
-  if (BITS == 2) {  // word cp/16, even/odd nibble plane, nibble index
-    m = 2 * (cp >> 4) + (cp & 1);
-    s = (cp & 15) >> 1;
-  } else {          // word cp/8
-    m = cp >> 3;
-    s = slot4(cp & 7);
-  }
-}
-// Value side: token position p (0..15 inside a lane group's 16 tokens)
-template <int BITS>
-__device__ __forceinline__ void v_pos(int p, int& m, int& s) {
-  if (BITS == 2) {
-    m = p & 1;
-    s = p >> 1;
-  } else {
-    m = p >> 3;
-    s = slot4(p & 7);
-  }
-}
-
-// value arr[2*g + hh] for lane group g without dynamic register indexing
-template <int R>
-__device__ __forceinline__ float pick(const float (&arr)[R], int g, int hh) {
-  float v = arr[hh < R ? hh : 0];
-#pragma unroll
-  for (int i = 1; i < (R + 1) / 2; i++)
-    if (g == i && 2 * i + hh < R) v = arr[2 * i + hh];
-  return v;
-}
-
-template <int BITS, int R>
-struct Cfg {
-  static constexpr int ROWS = 2 * R;                    // A rows: (head, hi|lo)
-  static constexpr int CH = 64;                         // score slots: one tile
-  static constexpr int KC_BYTES = 64 * kD * BITS / 8;   // key codes of one tile
-  static constexpr int VC_BYTES = 64 * kD * BITS / 8;   // value codes of one tile
-  static constexpr int A_BYTES = kNG * 2 * ROWS * 64;   // value A (two key groups: same)
-  static constexpr int RES_BYTES = 4 * ROWS * 64;       // residual key A
-  static constexpr int SC_BYTES = R * CH * 4;
-  static constexpr int O_BYTES = ((R * kD + 2 * R) * 4 + 15) / 16 * 16;  // keeps stg 16-aligned
-  static constexpr int DUMMY_BYTES = 64;                // sink for writes of absent heads
-  static constexpr int STG_BYTES = KC_BYTES + VC_BYTES; // staged codes of one tile
-  static constexpr int WAVE_BYTES =
-      A_BYTES + RES_BYTES + SC_BYTES + O_BYTES + DUMMY_BYTES + STG_BYTES;
-  static constexpr int ZERO_BYTES = ROWS < 16 ? A_BYTES : 0;  // all-zero rows, per block
-  static_assert(WAVE_BYTES % 16 == 0 && A_BYTES % 16 == 0, "b128 LDS accesses need 16-byte alignment");
-};
-
-// register budget of the occupancy target: one wave per SIMD for 8 heads, the
-// three-wave budget for one head at 2 bits (measured fastest), two waves
-// otherwise.  Blocks of 8 waves still place two per SIMD.  At these budgets
-// the tile loop holds no spill; the one-head 2-bit and four-head 4-bit
-// variants spill a few registers around the loop over residual slices longer
-// than one batch, which runs only for short contexts with few splits.
-template <int BITS, int R>
-constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS == 2 && R == 1) ? 3 : 2); }
-
-// tiles of loads in flight per wave: one (a second register set measured no
-// faster at two waves per SIMD), two for 8 heads at one wave per SIMD
-template <int BITS, int R>
-constexpr int prefetch_depth() {
-  return R >= 8 ? 2 : 1;
-}
-
-template <int BITS, int R, int NW, bool MH>
-__global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
-decode_mfma_kernel(DecodeArgs a) {
-  using C = Cfg<BITS, R>;
-  constexpr int ROWS = C::ROWS, CH = C::CH;
-  constexpr int E = 32 / BITS;
-  constexpr int W = kD / E;        // words per key row
-  constexpr int WPC = 64 / E;      // words per channel per value tile
-  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES];
-
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int n16 = lane & 15, kg = lane >> 4;
-  const int S = a.S, H = a.H;
-  const int u = blockIdx.x / S, split = blockIdx.x % S;
-  const int b = u / H;
-  const int tq = a.tq, tr = a.tr;
-
-  char* zero = smem;
-  char* my = smem + C::ZERO_BYTES + wv * C::WAVE_BYTES;
-  char* lds_a = my;                                     // key / value A tiles
-  char* lds_res = my + C::A_BYTES;                      // residual key A tile
-  float* lds_sc = reinterpret_cast<float*>(lds_res + C::RES_BYTES);   // [R][CH]
-  float* lds_o = reinterpret_cast<float*>(lds_res + C::RES_BYTES + C::SC_BYTES);
-  float* lds_dummy = reinterpret_cast<float*>(reinterpret_cast<char*>(lds_o) + C::O_BYTES);
-  char* stg = reinterpret_cast<char*>(lds_dummy) + C::DUMMY_BYTES;   // staged tile codes
-  for (int i = threadIdx.x; i < C::ZERO_BYTES / 16; i += NW * 64)
-    reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
-  __syncthreads();
-
-  // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
-  const size_t plane = (size_t)u, cap = (size_t)a.cap;
-  const rsrc_t r_kc = make_rsrc(a.k_codes + plane * cap * W, (uint32_t)(cap * W * 4));
-  // metadata: MB bytes per value (binary16 or binary32)
-  constexpr uint32_t MB = MH ? 2 : 4;
-  using MetaT = std::conditional_t<MH, uint2, float4>;
-  const size_t kmp = (cap / kG) * kD * MB, vmp = cap * kNG * MB;   // plane bytes
-  const rsrc_t r_ks = make_rsrc(static_cast<const char*>(a.k_scale) + plane * kmp, (uint32_t)kmp);
-  const rsrc_t r_kz = make_rsrc(static_cast<const char*>(a.k_zero) + plane * kmp, (uint32_t)kmp);
-  const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD / E), (uint32_t)(cap * (kD / E) * 4));
-  const rsrc_t r_vs = make_rsrc(static_cast<const char*>(a.v_scale) + plane * vmp, (uint32_t)vmp);
-  const rsrc_t r_vz = make_rsrc(static_cast<const char*>(a.v_zero) + plane * vmp, (uint32_t)vmp);
-  const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
-  const rsrc_t r_vr = make_rsrc(a.v_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
-  // fused append: the new token (residual slot t_new) comes from its input row
-  const bool fused = a.k_new != nullptr;
-  const int t_new = fused ? tr - 1 : -1;
-  const rsrc_t r_kn = make_rsrc(fused ? a.k_new + plane * kD : a.k_res, fused ? kD * 2 : 0);
-  const rsrc_t r_vn = make_rsrc(fused ? a.v_new + plane * kD : a.v_res, fused ? kD * 2 : 0);
-  const size_t qrow0 = (size_t)b * H * R + (size_t)(u % H) * R;
-  const rsrc_t r_q = make_rsrc(a.q + qrow0 * kD, (uint32_t)(R * kD * 2));
-
-  // this wave's share: value tiles [t_begin, t_end) and residual [r_begin, r_end)
-  const int NWT = S * NW, gw = split * NW + wv;
-  const int nT = (tq + 63) / 64;
-  const int t_begin = (int)((int64_t)gw * nT / NWT), t_end = (int)((int64_t)(gw + 1) * nT / NWT);
-  const int r_begin = (int)((int64_t)gw * tr / NWT), r_end = (int)((int64_t)(gw + 1) * tr / NWT);
-
-  // Lane roles.  Every global load is 16 bytes per lane over 1 KB contiguous.
-  //  key factors: lane -> key group kgrp = lane/32 of the tile and channels
-  //    cq..cq+3 (cq = 4*(lane%32)), i.e. exactly its own 16-byte scale / zero
-  //    load; channels cq, cq+2 (and cq+1, cq+3) sit in adjacent A slots, so
-  //    hi/lo pairs are written as 32-bit words;
-  //  value factors: lane -> token lane of the tile, its own 16-byte scale /
-  //    zero load (4 value groups);
-  //  codes: staged through LDS and re-read in the MFMA operand layout.
-  const int kgrp = lane >> 5, cq = 4 * (lane & 31);
-  uint32_t kwr[2];      // A offsets of channel pairs (cq, cq+2), (cq+1, cq+3)
-#pragma unroll
-  for (int e = 0; e < 2; e++) {
-    const int c = cq + e;
-    int m, s;
-    k_pos<BITS>(c & 31, m, s);
-    kwr[e] = (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
-  }
-  int vm, vs0;
-  v_pos<BITS>(lane & 15, vm, vs0);
-  const uint32_t vwr = (uint32_t)(((vm * ROWS) * 4 + kg) * 16 + 2 * vs0);
-  // A read base: lanes of absent rows read the all-zero region instead
-  const bool row_ok = n16 < ROWS;
-  const char* a_rd = row_ok ? lds_a + (n16 * 4 + kg) * 16 : zero + kg * 16;
-  const char* res_rd = row_ok ? lds_res + (n16 * 4 + kg) * 16 : zero + kg * 16;
-
-  // Issue order matters: vector-memory loads complete in order, so the query
-  // goes first, then the first residual batch, then the tile prefetch; waiting
-  // for an earlier group never waits for a later one.
-  uint2 q4r[R];
-#pragma unroll
-  for (int h = 0; h < R; h++) q4r[h] = ld8(r_q, (uint32_t)((h * kD + cq) * 2));
-  __builtin_amdgcn_sched_barrier(0);
-
-  // registers of a tile in flight: codes (2-bit uses x0..x3: key codes, then
-  // value codes; 4-bit x0..x7), key scale / zero of key group kgrp, channels
-  // cq..cq+3, value scale / zero of the token lane
-  const uint32_t l16 = (uint32_t)lane * 16;
-  // codes / metadata of tile `tile` of this wave, or zeros (no memory access)
-  // when it is past the wave's last tile.  Codes are reloaded as soon as they
-  // are staged, metadata once the tile's compute has consumed them, so that
-  // no register holds two generations at once (that would need copies, and a
-  // copy waits for its load).
-  auto load_codes = [&](int tile, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& x4,
-                        uint4& x5, uint4& x6, uint4& x7) __attribute__((always_inline)) {
-    const uint32_t co = tile < t_end ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
-    if constexpr (BITS == 2) {
-      x0 = ld16(r_kc, co);
-      x1 = ld16(r_kc, co + 1024);
-      x2 = ld16(r_vc, co);
-      x3 = ld16(r_vc, co + 1024);
-    } else {
-      x0 = ld16(r_kc, co);
-      x1 = ld16(r_kc, co + 1024);
-      x2 = ld16(r_kc, co + 2048);
-      x3 = ld16(r_kc, co + 3072);
-      x4 = ld16(r_vc, co);
-      x5 = ld16(r_vc, co + 1024);
-      x6 = ld16(r_vc, co + 2048);
-      x7 = ld16(r_vc, co + 3072);
-    }
-  };
-  auto load_meta = [&](int tile, MetaT& ks, MetaT& kz, MetaT& vs, MetaT& vz)
-      __attribute__((always_inline)) {
-    // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 256 values
-    // each, 4 per lane (converted to binary32 when the tile is computed)
-    const uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
-    if constexpr (MH) {
-      ks = ld8s(r_ks, mo);
-      kz = ld8s(r_kz, mo);
-      vs = ld8s(r_vs, mo);
-      vz = ld8s(r_vz, mo);
-    } else {
-      ks = ld16f(r_ks, mo);
-      kz = ld16f(r_kz, mo);
-      vs = ld16f(r_vs, mo);
-      vz = ld16f(r_vz, mo);
-    }
-  };
-  auto stage = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
-                   const uint4& x4, const uint4& x5, const uint4& x6, const uint4& x7)
-      __attribute__((always_inline)) {
-    uint4* d = reinterpret_cast<uint4*>(stg + l16);
-    d[0] = x0;
-    d[64] = x1;
-    d[128] = x2;
-    d[192] = x3;
-    if constexpr (BITS == 4) {
-      d[256] = x4;
-      d[320] = x5;
-      d[384] = x6;
-      d[448] = x7;
-    }
-  };
-
-  // residual slice, 16 tokens per batch.  Key lanes: token n16 of the batch,
-  // channels 8*kg + 32*i .. +7 (MFMA B operand); value lanes: token group
-  // tg = lane/16 (tokens tg, tg+4, tg+8, tg+12), channels 8*c8 .. 8*c8+7.
-  // Tokens past the slice read zeros and weigh zero.  Under a fused append
-  // every lane loads from both the residual and the new-token row, one of the
-  // two offsets out of range, and ORs the results (no per-lane branch).
-  const int tg = lane >> 4, c8 = lane & 15;
-  u32x4 rk0, rk1, rk2, rk3;   // key rows (8 fp16 each, MFMA B operand)
-  u32x4 rv0, rv1, rv2, rv3;   // value rows (8 fp16 each)
-  auto load_res = [&](int t16) __attribute__((always_inline)) {
-    const uint32_t rb = kD * 2;
-    rk0 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16);
-    rk1 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 64);
-    rk2 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 128);
-    rk3 = ld_res(r_kr, r_kn, t16 + n16, r_end, t_new, rb, kg * 16 + 192);
-    rv0 = ld_res(r_vr, r_vn, t16 + tg, r_end, t_new, rb, c8 * 16);
-    rv1 = ld_res(r_vr, r_vn, t16 + tg + 4, r_end, t_new, rb, c8 * 16);
-    rv2 = ld_res(r_vr, r_vn, t16 + tg + 8, r_end, t_new, rb, c8 * 16);
-    rv3 = ld_res(r_vr, r_vn, t16 + tg + 12, r_end, t_new, rb, c8 * 16);
-  };
-  load_res(r_begin);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Loads run DEPTH tiles ahead of the compute, in DEPTH register sets used
-  // round robin.  They are issued before the residual slice so that it
-  // overlaps them.
-  constexpr int DEPTH = prefetch_depth<BITS, R>();
-  uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
-  MetaT a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
-  // (the same issue order as the loop: codes A, meta A, codes B, meta B)
-  load_codes(t_begin, a0, a1, a2, a3, a4, a5, a6, a7);
-  __builtin_amdgcn_sched_barrier(0);
-  load_meta(t_begin, a_ks, a_kz, a_vs, a_vz);
-  if constexpr (DEPTH == 2) {
-    __builtin_amdgcn_sched_barrier(0);
-    load_codes(t_begin + 1, b0, b1, b2, b3, b4, b5, b6, b7);
-    __builtin_amdgcn_sched_barrier(0);
-    load_meta(t_begin + 1, b_ks, b_kz, b_vs, b_vz);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // scaled query (log2 domain) of channels cq..cq+3, and its power-of-two
-  // normalisation qn so that |q * qn| < 1 (then |q' * qn| < 65536 / 1.5)
-  const float qs = a.scale * kLog2e;
-  float sq[R][4];
-  float qabs = 0.f;
-#pragma unroll
-  for (int h = 0; h < R; h++) {
-    const uint2 q4 = q4r[h];
-    sq[h][0] = qs * h2f((uint16_t)(q4.x & 0xFFFFu));
-    sq[h][1] = qs * h2f((uint16_t)(q4.x >> 16));
-    sq[h][2] = qs * h2f((uint16_t)(q4.y & 0xFFFFu));
-    sq[h][3] = qs * h2f((uint16_t)(q4.y >> 16));
-#pragma unroll
-    for (int e = 0; e < 4; e++) qabs = fmaxf(qabs, fabsf(sq[h][e]));
-  }
-  qabs = wave_max(qabs);
-  int qe = (int)((__builtin_bit_cast(uint32_t, qabs) >> 23) & 0xFF) - 126;  // qabs < 2^qe
-  qe = qe < -100 ? -100 : (qe > 100 ? 100 : qe);
-  const float qn = __builtin_bit_cast(float, (uint32_t)(127 - qe) << 23);
-  const float qup = __builtin_bit_cast(float, (uint32_t)(127 + qe) << 23);
-  float sqn[R][4];
-#pragma unroll
-  for (int h = 0; h < R; h++)
-#pragma unroll
-    for (int e = 0; e < 4; e++) sqn[h][e] = sq[h][e] * qn;
-
-  float m_run[R], l_acc[R], l_res[R];
-  float gam[R][kNG];
-  float ores[R][8];
-#pragma unroll
-  for (int h = 0; h < R; h++) {
-    m_run[h] = -INFINITY;
-    l_acc[h] = l_res[h] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kNG; j++) gam[h][j] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; e++) ores[h][e] = 0.f;
-  }
-  float4v cv[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; nb++) cv[nb] = float4v{0.f, 0.f, 0.f, 0.f};
-
-  // score slot of head 2*kg + hh for token index k (absent heads go to a sink)
-  auto sc_addr = [&](int hh, int k) __attribute__((always_inline)) -> float* {
-    const int h = 2 * kg + hh;
-    return h < R ? lds_sc + h * CH + k : lds_dummy + n16;
-  };
-
-  // new maximum over the ntok scores in LDS -> rescale every running quantity
-  // new running maximum of each head -> rescale every running quantity
-  auto apply_max = [&](const float (&mxs)[R]) __attribute__((always_inline)) {
-    float alpha[R];
-    bool any = false;
-#pragma unroll
-    for (int h = 0; h < R; h++) {
-      // lazy reference: move it only when a score exceeds it by more than
-      // 2^kLazy (p stays <= 2^kLazy; fine for the fp32 sums and the bf16 P.V
-      // operand); a head without any finite score keeps -inf
-      const bool grow = mxs[h] > m_run[h] + kLazy;
-      const float m_new = grow ? mxs[h] : m_run[h];
-      alpha[h] = grow ? fast_exp2(m_run[h] - m_new) : 1.f;
-      any |= grow;
-      m_run[h] = m_new;
-    }
-    if (any) {
-#pragma unroll
-      for (int h = 0; h < R; h++) {
-        l_acc[h] *= alpha[h];
-        l_res[h] *= alpha[h];
-#pragma unroll
-        for (int j = 0; j < kNG; j++) gam[h][j] *= alpha[h];
-#pragma unroll
-        for (int e = 0; e < 8; e++) ores[h][e] *= alpha[h];
-      }
-      const float a0 = pick<R>(alpha, kg, 0), a1 = pick<R>(alpha, kg, 1);
-#pragma unroll
-      for (int nb = 0; nb < 8; nb++) {
-        cv[nb][0] *= a0;
-        cv[nb][1] *= a0;
-        cv[nb][2] *= a1;
-        cv[nb][3] *= a1;
-      }
-    }
-  };
-  // maximum over the ntok scores in LDS (residual batches)
-  auto rescale = [&](int ntok) __attribute__((always_inline)) {
-    float mxs[R];
-#pragma unroll
-    for (int h = 0; h < R; h++) mxs[h] = wave_max(lane < ntok ? lds_sc[h * CH + lane] : -INFINITY);
-    apply_max(mxs);
-  };
-
-  // one tile (codes already staged in LDS): key scores -> LDS, online-softmax
-  // rescale, P.V
-  auto do_tile = [&](int tile, MetaT ksm, MetaT kzm, MetaT vsm, MetaT vzm)
-      __attribute__((always_inline)) {
-    const float4 ks4 = meta4(ksm), kz4 = meta4(kzm), vs4 = meta4(vsm), vz4 = meta4(vzm);
-    const bool half_tile = tile * 64 + 64 > tq;   // only the first 32 tokens exist
-    // key factors (both groups at once: lanes 0-31 group 0, 32-63 group 1)
-    const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
-    const float kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
-    float beta0[R], beta1[R];
-#pragma unroll
-    for (int h = 0; h < R; h++) {
-#pragma unroll
-      for (int e = 0; e < 2; e++) {
-        uint32_t hi, lo;
-        split2(sqn[h][e] * ksv[e], sqn[h][e + 2] * ksv[e + 2], hi, lo);
-        *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h) * 64) = hi;
-        *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h + 1) * 64) = lo;
-      }
-      float bp = sq[h][0] * kzv[0] + sq[h][1] * kzv[1] + sq[h][2] * kzv[2] + sq[h][3] * kzv[3];
-      bp += dpp<0x128>(bp);
-      bp += dpp<0x124>(bp);
-      bp += dpp<0x122>(bp);
-      bp += dpp<0x121>(bp);
-      beta0[h] = lane_read(bp, 0) + lane_read(bp, 16);
-      beta1[h] = lane_read(bp, 32) + lane_read(bp, 48);
-    }
-    if (half_tile && lane < 32) {
-#pragma unroll
-      for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int ngr = half_tile ? 1 : 2;
-    // per-lane maxima of the scores this lane produces (heads 2kg, 2kg+1)
-    float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 2; g++) {
-      if (g < ngr) {
-        half8 af[4];
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-          af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
-        const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
-#pragma unroll
-        for (int mb2 = 0; mb2 < 2; mb2++) {
-          const int mb = 2 * g + mb2;
-          float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-          if constexpr (BITS == 2) {
-            const uint2 x = *reinterpret_cast<const uint2*>(stg + (16 * mb + n16) * W * 4 + kg * 8);
-            acc = mfma(af[0], cvt_nib2(x.x & 0x33333333u), acc);
-            acc = mfma(af[1], cvt_nib2((x.x >> 2) & 0x33333333u), acc);
-            acc = mfma(af[2], cvt_nib2(x.y & 0x33333333u), acc);
-            acc = mfma(af[3], cvt_nib2((x.y >> 2) & 0x33333333u), acc);
-          } else {
-            const uint4 x = *reinterpret_cast<const uint4*>(stg + (16 * mb + n16) * W * 4 + kg * 16);
-            acc = mfma(af[0], cvt_word4(x.x), acc);
-            acc = mfma(af[1], cvt_word4(x.y), acc);
-            acc = mfma(af[2], cvt_word4(x.z), acc);
-            acc = mfma(af[3], cvt_word4(x.w), acc);
-          }
-          const int k = 16 * mb + n16;
-          const float s0 = (acc[0] + acc[1]) * qup + b0;
-          const float s1 = (acc[2] + acc[3]) * qup + b1;
-          *sc_addr(0, k) = s0;
-          *sc_addr(1, k) = s1;
-          mx0 = fmaxf(mx0, s0);
-          mx1 = fmaxf(mx1, s1);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    // tile maximum per head straight from the MFMA output: reduce over the 16
-    // token lanes of each row (heads 2kg, 2kg+1 live in lane row kg)
-    {
-      mx0 = fmaxf(mx0, dpp<0x128>(mx0));
-      mx0 = fmaxf(mx0, dpp<0x124>(mx0));
-      mx0 = fmaxf(mx0, dpp<0x122>(mx0));
-      mx0 = fmaxf(mx0, dpp<0x121>(mx0));
-      if constexpr (R >= 2) {
-        mx1 = fmaxf(mx1, dpp<0x128>(mx1));
-        mx1 = fmaxf(mx1, dpp<0x124>(mx1));
-        mx1 = fmaxf(mx1, dpp<0x122>(mx1));
-        mx1 = fmaxf(mx1, dpp<0x121>(mx1));
-      }
-      float mxs[R];
-#pragma unroll
-      for (int h = 0; h < R; h++) mxs[h] = lane_read((h & 1) ? mx1 : mx0, 16 * (h >> 1));
-      apply_max(mxs);
-    }
-    // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
-    const bool valid = tile * 64 + lane < tq;
-    const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
-    const float vzv[4] = {valid ? vz4.x : 0.f, valid ? vz4.y : 0.f, valid ? vz4.z : 0.f,
-                          valid ? vz4.w : 0.f};
-#pragma unroll
-    for (int h = 0; h < R; h++) {
-      const float p = valid ? fast_exp2(lds_sc[h * CH + lane] - m_run[h]) : 0.f;
-      l_acc[h] += p;
-#pragma unroll
-      for (int j = 0; j < kNG; j++) gam[h][j] += p * vzv[j];
-      // hi/lo halves of p * s for the group pairs (0,1), (2,3), two at a time
-#pragma unroll
-      for (int jj = 0; jj < kNG; jj += 2) {
-        uint32_t hi, lo;
-        split2_bf(valid ? p * vsv[jj] : 0.f, valid ? p * vsv[jj + 1] : 0.f, hi, lo);
-        char* d0 = lds_a + vwr + (uint32_t)(jj * 2 * ROWS * 64);
-        char* d1 = d0 + 2 * ROWS * 64;
-        *reinterpret_cast<uint16_t*>(d0 + (2 * h) * 64) = (uint16_t)hi;
-        *reinterpret_cast<uint16_t*>(d1 + (2 * h) * 64) = (uint16_t)(hi >> 16);
-        *reinterpret_cast<uint16_t*>(d0 + (2 * h + 1) * 64) = (uint16_t)lo;
-        *reinterpret_cast<uint16_t*>(d1 + (2 * h + 1) * 64) = (uint16_t)(lo >> 16);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const char* vstg = stg + C::KC_BYTES;
-#pragma unroll
-    for (int j = 0; j < kNG; j++) {
-      const bf16x8 av0 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 0) * ROWS * 64);
-      const bf16x8 av1 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 1) * ROWS * 64);
-#pragma unroll
-      for (int nbj = 0; nbj < 2; nbj++) {
-        const int nb = 2 * j + nbj;
-        if constexpr (BITS == 2) {
-          const uint32_t x = *reinterpret_cast<const uint32_t*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 4);
-          cv[nb] = mfma_bf(av0, cvt_nib2_bf(x & 0x33333333u), cv[nb]);
-          cv[nb] = mfma_bf(av1, cvt_nib2_bf((x >> 2) & 0x33333333u), cv[nb]);
-        } else {
-          const uint2 x = *reinterpret_cast<const uint2*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 8);
-          cv[nb] = mfma_bf(av0, cvt_word4_bf(x.x), cv[nb]);
-          cv[nb] = mfma_bf(av1, cvt_word4_bf(x.y), cv[nb]);
-        }
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
-
-  // ---------------- residual slice (full precision), overlapping the tile loads
-  // one batch of 16 tokens from rk*/rv*: scores by MFMA, values on the VALU
-  half8 ar[4];
-  auto res_batch = [&](int t16) __attribute__((always_inline)) {
-    const int n = min(16, r_end - t16);
-    float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-    acc = mfma(ar[0], __builtin_bit_cast(half8, rk0), acc);
-    acc = mfma(ar[1], __builtin_bit_cast(half8, rk1), acc);
-    acc = mfma(ar[2], __builtin_bit_cast(half8, rk2), acc);
-    acc = mfma(ar[3], __builtin_bit_cast(half8, rk3), acc);
-    {
-      const bool ok = n16 < n;
-      float* p0 = ok ? sc_addr(0, n16) : lds_dummy + n16;
-      float* p1 = ok ? sc_addr(1, n16) : lds_dummy + n16;
-      *p0 = (acc[0] + acc[1]) * qup;
-      *p1 = (acc[2] + acc[3]) * qup;
-    }
-    __builtin_amdgcn_wave_barrier();
-    rescale(n);
-    const u32x4 vv[4] = {rv0, rv1, rv2, rv3};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      const int ti = tg + 4 * i;
-      const bool ok = ti < n;
-      const uint32_t w4[4] = {vv[i][0], vv[i][1], vv[i][2], vv[i][3]};
-      float v[8];
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        v[2 * e] = h2f((uint16_t)(w4[e] & 0xFFFFu));
-        v[2 * e + 1] = h2f((uint16_t)(w4[e] >> 16));
-      }
-#pragma unroll
-      for (int h = 0; h < R; h++) {
-        const float p = ok ? fast_exp2(lds_sc[h * CH + (ok ? ti : 0)] - m_run[h]) : 0.f;
-        if (c8 == 0) l_res[h] += p;     // each token counted once
-#pragma unroll
-        for (int e = 0; e < 8; e++) ores[h][e] += p * v[e];
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-  };
-  // The first batch runs in every wave (an empty slice weighs zero), so that
-  // its loads stay ahead of the tile loads instead of sinking into a branch.
-  // Residual key A: row (h, hi|lo), MFMA i, lane group kgr, slot s <->
-  // channel 32 i + 8 kgr + s.  Lanes 0-31 write channel pairs (cq, cq+1),
-  // (cq+2, cq+3) from the scaled query already in registers.
-  if (lane < 32) {
-#pragma unroll
-    for (int e = 0; e < 2; e++) {
-      const int ch = cq + 2 * e;
-      const uint32_t off =
-          (uint32_t)((((ch >> 5) * ROWS) * 4 + ((ch & 31) >> 3)) * 16 + 2 * (ch & 7));
-#pragma unroll
-      for (int h = 0; h < R; h++) {
-        uint32_t hi, lo;
-        split2(sqn[h][2 * e], sqn[h][2 * e + 1], hi, lo);
-        *reinterpret_cast<uint32_t*>(lds_res + off + (2 * h) * 64) = hi;
-        *reinterpret_cast<uint32_t*>(lds_res + off + (2 * h + 1) * 64) = lo;
-      }
-    }
-  }
-  __builtin_amdgcn_wave_barrier();
-#pragma unroll
-  for (int i = 0; i < 4; i++) ar[i] = *reinterpret_cast<const half8*>(res_rd + i * ROWS * 64);
-  // fused append: the lanes holding the new token store it into its residual
-  // slot (one wave of one split per plane; no load in this launch reads the
-  // slot, the token itself came from its input row)
-  auto write_new = [&](int t16) __attribute__((always_inline)) {
-    const int dn = t_new - t16;
-    if (dn < 0 || dn >= 16) return;           // uniform: this batch lacks it
-    const uint32_t row = (uint32_t)t_new * kD * 2;
-    if (n16 == dn) {
-      const uint32_t o = row + kg * 16;
-      st16(r_kr, o, rk0);
-      st16(r_kr, o + 64, rk1);
-      st16(r_kr, o + 128, rk2);
-      st16(r_kr, o + 192, rk3);
-    }
-    if (tg == (dn & 3)) {
-      // i = dn / 4 is uniform: plain branches (a value select here would
-      // become a pointer select over the captured registers)
-      const uint32_t o = row + c8 * 16;
-      const int i = dn >> 2;
-      if (i == 0) st16(r_vr, o, rv0);
-      else if (i == 1) st16(r_vr, o, rv1);
-      else if (i == 2) st16(r_vr, o, rv2);
-      else st16(r_vr, o, rv3);
-    }
-  };
-  res_batch(r_begin);
-  if (fused) write_new(r_begin);
-  // slices longer than one batch (short contexts, few splits) load the rest here
-  for (int t16 = r_begin + 16; t16 < r_end; t16 += 16) {
-    load_res(t16);
-    res_batch(t16);
-    if (fused) write_new(t16);
-  }
-
-  // ---------------- quantized tiles, DEPTH tiles of loads in flight
-  // the scheduling barriers keep "stage tile t, issue loads of t+DEPTH,
-  // compute t" in that order, so no wait for a later tile lands before the
-  // compute of tile t.  Loads past the wave's last tile read zeros; the only
-  // branch in the loop (an odd tile count under DEPTH 2) holds no load.
-  if constexpr (DEPTH == 2) {
-    for (int t = t_begin; t < t_end; t += 2) {
-      __builtin_amdgcn_sched_barrier(0);
-      stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 2, a0, a1, a2, a3, a4, a5, a6, a7);
-      __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz);
-      __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz);
-      __builtin_amdgcn_sched_barrier(0);
-      stage(b0, b1, b2, b3, b4, b5, b6, b7);
-      load_codes(t + 3, b0, b1, b2, b3, b4, b5, b6, b7);
-      __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz);
-      __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 3, b_ks, b_kz, b_vs, b_vz);
-    }
-  } else {
-    for (int t = t_begin; t < t_end; t++) {
-      __builtin_amdgcn_sched_barrier(0);
-      stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 1, a0, a1, a2, a3, a4, a5, a6, a7);
-      __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz);
-      __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 1, a_ks, a_kz, a_vs, a_vz);
-    }
-  }
-
-  // ---------------- wave result -> LDS: o[h][d], m[h], l[h]
-  {
-    const int h0 = 2 * kg, h1 = 2 * kg + 1;
-#pragma unroll
-    for (int nb = 0; nb < 8; nb++) {
-      float* o0 = h0 < R ? lds_o + h0 * kD + 16 * nb + n16 : lds_dummy + n16;
-      float* o1 = h1 < R ? lds_o + h1 * kD + 16 * nb + n16 : lds_dummy + n16;
-      *o0 = cv[nb][0] + cv[nb][1];
-      *o1 = cv[nb][2] + cv[nb][3];
-    }
-  }
-  // residual P.V partials: lanes c8, c8+16, c8+32, c8+48 (the 4 token groups)
-  // hold channels 8*c8..8*c8+7; sum them across lanes, then lane (tg, c8) adds
-  // channels 8*c8+2*tg, 8*c8+2*tg+1 (value group c8/4) together with the Gamma
-  // term of that group
-  __builtin_amdgcn_wave_barrier();
-  {
-    const int tg = lane >> 4, c8 = lane & 15, grp = c8 >> 2;
-#pragma unroll
-    for (int h = 0; h < R; h++) {
-      float g[kNG];
-#pragma unroll
-      for (int j = 0; j < kNG; j++) g[j] = wave_sum(gam[h][j]);
-      const float lsum = wave_sum(l_acc[h]) + wave_sum(l_res[h]);
-      float gj = g[0];
-#pragma unroll
-      for (int j = 1; j < kNG; j++)
-        if (grp == j) gj = g[j];
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        float x = ores[h][e];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (e == 2 * tg) rs0 = x;
-        if (e == 2 * tg + 1) rs1 = x;
-      }
-      float2* op = reinterpret_cast<float2*>(lds_o + h * kD + 8 * c8 + 2 * tg);
-      float2 o2 = *op;
-      o2.x += gj + rs0;
-      o2.y += gj + rs1;
-      *op = o2;
-      if (lane == 0) {
-        lds_o[R * kD + h] = m_run[h];
-        lds_o[R * kD + R + h] = lsum;
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---------------- merge the block's waves
-  for (int idx = threadIdx.x; idx < R * kD; idx += NW * 64) {
-    const int h = idx / kD, d = idx % kD;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; w++) {
-      const float* ow = reinterpret_cast<const float*>(smem + C::ZERO_BYTES + w * C::WAVE_BYTES +
-                                                       C::A_BYTES + C::RES_BYTES + C::SC_BYTES);
-      M = fmaxf(M, ow[R * kD + h]);
-    }
-    float O = 0.f, L = 0.f;
-    if (M != -INFINITY) {
-#pragma unroll
-      for (int w = 0; w < NW; w++) {
-        const float* ow = reinterpret_cast<const float*>(
-            smem + C::ZERO_BYTES + w * C::WAVE_BYTES + C::A_BYTES + C::RES_BYTES + C::SC_BYTES);
-        const float f = fast_exp2(ow[R * kD + h] - M);
-        O += ow[h * kD + d] * f;
-        L += ow[R * kD + R + h] * f;
-      }
-    }
-    const size_t row = qrow0 + h;
-    if (S == 1) {
-      a.out[row * kD + d] = f2h(O / L);
-    } else {
-      const size_t rows = (size_t)a.B * H * R;
-      if (d == 0) {
-        a.ws[row * S + split] = M * kLn2;          // natural-log units for the combine
-        a.ws[rows * S + row * S + split] = L;
-      }
-      a.ws[2 * rows * S + (row * S + split) * kD + d] = O;
-    }
-  }
-}
-
-template <int R>
-constexpr int block_waves(int nw) {
-  return (R >= 8 || nw < 8) ? 4 : 8;
-}
-
-template <int BITS, int R, bool MH>
-hipError_t launch_m(const DecodeArgs& a, int nw, hipStream_t st) {
-  const dim3 grid(a.B * a.H * a.S);
-  if (block_waves<R>(nw) == 8)
-    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH><<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a);
-  else
-    decode_mfma_kernel<BITS, R, 4, MH><<<grid, 4 * 64, 0, st>>>(a);
-  return hipGetLastError();
-}
-template <int BITS, int R>
-hipError_t launch_r(const DecodeArgs& a, int nw, hipStream_t st) {
-  return a.mh ? launch_m<BITS, R, true>(a, nw, st) : launch_m<BITS, R, false>(a, nw, st);
-}
-
-template <int BITS>
-hipError_t launch_bits(const DecodeArgs& a, int nw, hipStream_t st) {
-  switch (a.r) {
-    case 1: return launch_r<BITS, 1>(a, nw, st);
-    case 2: return launch_r<BITS, 2>(a, nw, st);
-    case 4: return launch_r<BITS, 4>(a, nw, st);
-    default: return launch_r<BITS, 8>(a, nw, st);
-  }
-}
-
-}  // namespace
 
 bool decode_mfma_supported(int D, int G, int r) {
   return D == kD && G == kG && (r == 1 || r == 2 || r == 4 || r == 8);
@@ -970,7 +56,8 @@ template <int BITS, int R, int NW>
 int occupancy_of() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false>), NW * 64, 0) !=
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false>),
+          NW * 64, 0) !=
       hipSuccess)
     return 1;
   return n > 0 ? n : 1;
@@ -1015,7 +102,8 @@ int decode_mfma_block_waves(int r, int nw) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
-  return a.bits == 2 ? launch_bits<2>(a, nw, st) : launch_bits<4>(a, nw, st);
+  const NoLens none;
+  return a.bits == 2 ? launch_bits<2, false>(a, none, nw, st) : launch_bits<4, false>(a, none, nw, st);
 }
 
 }  // namespace kivi

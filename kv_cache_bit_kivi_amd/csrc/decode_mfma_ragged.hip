@@ -1,0 +1,13 @@
+// Matrix-core decode over per-sequence lengths (ragged batches): the kernel
+// of decode_mfma.hip with each block reading its sequence's quantized and
+// residual token counts from the launch's length arrays.
+#include "decode_mfma_impl.h"
+
+namespace kivi {
+
+hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                     hipStream_t st) {
+  return a.bits == 2 ? launch_bits<2, true>(a, lens, nw, st) : launch_bits<4, true>(a, lens, nw, st);
+}
+
+}  // namespace kivi

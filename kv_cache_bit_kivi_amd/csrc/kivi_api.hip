@@ -4,8 +4,10 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdlib>
+#include <vector>
 
 #include "kivi_internal.h"
 
@@ -127,6 +129,185 @@ size_t ws_bytes(const kivi_shape& s, int S) {
   if (S <= 1) return 0;
   const size_t rows = (size_t)s.batch * s.num_kv_heads * s.gqa_ratio;
   return rows * (size_t)S * (size_t)(s.head_dim + 2) * sizeof(float);
+}
+
+// ---- ragged batches -------------------------------------------------------
+
+int check_ragged(const kivi_ragged_cache* c) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  const void* ptrs[] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
+                        c->v_scale, c->v_zero,  c->k_res,  c->v_res};
+  for (const void* p : ptrs)
+    if (!p) return KIVI_EINVAL;
+  if (!c->tq || !c->tr) return KIVI_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  for (int b = 0; b < s.batch; b++) {
+    const int tq = c->tq[b], tr = c->tr[b];
+    if (tq < 0 || tq % s.group != 0 || tr < 0 || tr > s.residual) return KIVI_ESHAPE;
+    if (tq > s.capacity) return KIVI_ECAPACITY;
+  }
+  return KIVI_OK;
+}
+
+// per-(b, h) plane extents of the cache buffers
+struct PlaneSizes {
+  size_t code_words, kmeta_bytes, vmeta_bytes, res_elems;
+};
+PlaneSizes plane_sizes(const kivi_shape& s) {
+  const size_t cap = s.capacity, D = s.head_dim, G = s.group, mb = s.meta_half ? 2 : 4;
+  return {cap * D * s.bits / 32, (cap / G) * D * mb, cap * (D / G) * mb, (size_t)s.residual * D};
+}
+
+// Runs `launch(list)` over the items added with `add`, kMaxSeq at a time.
+template <class F>
+struct ListBatcher {
+  kivi::SeqList list;
+  F launch;
+  int rc = KIVI_OK;
+  explicit ListBatcher(F f) : launch(f) { list.n = 0; }
+  void add(int seq, int a, int b, int c) {
+    if (rc) return;
+    list.seq[list.n] = seq;
+    list.a[list.n] = a;
+    list.b[list.n] = b;
+    list.c[list.n] = c;
+    if (++list.n == kivi::kMaxSeq) flush();
+  }
+  int flush() {
+    if (!rc && list.n) rc = launch(list);
+    list.n = 0;
+    return rc;
+  }
+};
+template <class F>
+ListBatcher<F> batcher(F f) { return ListBatcher<F>(f); }
+
+// Quantizes the full residual of every sequence whose residual holds R tokens
+// into its grouped store at tq[b] (the lazy flush), K then V per launch.
+int enqueue_ragged_flush(const kivi_ragged_cache* c, hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  const int R = s.residual;
+  auto fl = batcher([&](const kivi::SeqList& L) {
+    hipError_t e = kivi::launch_quantize_k_list(c->k_res, L, s.num_kv_heads, s.head_dim, s.bits,
+                                                s.group, s.capacity, R, R, c->k_codes, c->k_scale,
+                                                c->k_zero, s.meta_half, st);
+    if (e == hipSuccess)
+      e = kivi::launch_quantize_v_list(c->v_res, L, s.num_kv_heads, s.head_dim, s.bits, s.group,
+                                       s.capacity, R, R, c->v_codes, c->v_scale, c->v_zero,
+                                       s.meta_half, st);
+    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  });
+  for (int b = 0; b < s.batch; b++)
+    if (c->tr[b] == R) fl.add(b, R, c->tq[b], 0);
+  return fl.flush();
+}
+
+// Writes token row b of k_new / v_new into residual slot slot[b].
+int enqueue_ragged_token_copy(const kivi_ragged_cache* c, const uint16_t* k_new,
+                              const uint16_t* v_new, const std::vector<int>& slot,
+                              hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  auto cp = batcher([&](const kivi::SeqList& L) {
+    hipError_t e = kivi::launch_copy_tokens_list(k_new, v_new, 1, c->k_res, c->v_res, s.residual,
+                                                 L, 1, s.num_kv_heads, s.head_dim, st);
+    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  });
+  for (int b = 0; b < s.batch; b++) cp.add(b, 0, slot[b], 1);
+  return cp.flush();
+}
+
+// A validated ragged decode: split count and the lengths to decode at.
+struct RaggedPlan {
+  int S;
+  std::vector<int> tq, tr;
+};
+
+int plan_ragged_decode(const kivi_ragged_cache* c, std::vector<int> tq, std::vector<int> tr,
+                       const uint16_t* q, uint16_t* out, void* workspace,
+                       size_t workspace_bytes, int32_t num_splits, RaggedPlan* plan) {
+  if (!q || !out) return KIVI_EINVAL;
+  if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
+  if (num_splits < 0) return KIVI_EINVAL;
+  const kivi_shape& s = c->shape;
+  int max_tq = 0, max_tr = 0;
+  for (int b = 0; b < s.batch; b++) {
+    if (tq[b] + tr[b] < 1) return KIVI_ESHAPE;
+    max_tq = std::max(max_tq, tq[b]);
+    max_tr = std::max(max_tr, tr[b]);
+  }
+  int S = num_splits;
+  if (S == 0) {
+    const int cus = device_cu_count();
+    if (cus < 0) return KIVI_EHIP;
+    S = auto_splits(s, max_tq, max_tr, cus);
+  }
+  if (S > 1) {
+    if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
+    if (!workspace) return KIVI_EINVAL;
+    if (!aligned16(workspace)) return KIVI_EALIGN;
+  }
+  plan->S = S;
+  plan->tq = std::move(tq);
+  plan->tr = std::move(tr);
+  return KIVI_OK;
+}
+
+// Decode launches over chunks of at most kMaxSeq sequences: pointers offset to
+// the chunk's planes, rows and workspace, lengths passed by value.
+int enqueue_ragged_decode(const kivi_ragged_cache* c, const RaggedPlan& p, const uint16_t* q,
+                          float softmax_scale, uint16_t* out, void* workspace,
+                          const uint16_t* k_new, const uint16_t* v_new, hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  const PlaneSizes ps = plane_sizes(s);
+  const int H = s.num_kv_heads, r = s.gqa_ratio, D = s.head_dim, S = p.S;
+  for (int c0 = 0; c0 < s.batch; c0 += kivi::kMaxSeq) {
+    const int n = std::min(kivi::kMaxSeq, s.batch - c0);
+    const size_t pl = (size_t)c0 * H;   // first plane of the chunk
+    DecodeArgs a;
+    a.k_codes = c->k_codes + pl * ps.code_words;
+    a.k_scale = static_cast<const char*>(c->k_scale) + pl * ps.kmeta_bytes;
+    a.k_zero = static_cast<const char*>(c->k_zero) + pl * ps.kmeta_bytes;
+    a.v_codes = c->v_codes + pl * ps.code_words;
+    a.v_scale = static_cast<const char*>(c->v_scale) + pl * ps.vmeta_bytes;
+    a.v_zero = static_cast<const char*>(c->v_zero) + pl * ps.vmeta_bytes;
+    a.k_res = c->k_res + pl * ps.res_elems;
+    a.v_res = c->v_res + pl * ps.res_elems;
+    a.k_new = k_new ? k_new + pl * D : nullptr;
+    a.v_new = v_new ? v_new + pl * D : nullptr;
+    a.q = q + pl * r * D;
+    a.out = out + pl * r * D;
+    a.ws = S > 1 ? static_cast<float*>(workspace) + pl * r * (size_t)S * (D + 2) : nullptr;
+    a.B = n;
+    a.H = H;
+    a.r = r;
+    a.D = D;
+    a.bits = s.bits;
+    a.G = s.group;
+    a.R = s.residual;
+    a.cap = s.capacity;
+    kivi::SeqLens lens;
+    int mq = 0, mr = 0;
+    for (int i = 0; i < n; i++) {
+      lens.tq[i] = p.tq[c0 + i];
+      lens.tr[i] = p.tr[c0 + i];
+      mq = std::max(mq, lens.tq[i]);
+      mr = std::max(mr, lens.tr[i]);
+    }
+    a.tq = mq;   // (unused by the per-sequence kernels)
+    a.tr = mr;
+    a.S = S;
+    a.mh = s.meta_half;
+    a.scale = softmax_scale;
+    hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma_ragged(a, lens, mfma_waves(), st)
+                               : kivi::launch_decode_generic_ragged(a, lens, st);
+    if (e != hipSuccess) return KIVI_EHIP;
+    if (S > 1 && kivi::launch_combine(a, st) != hipSuccess) return KIVI_EHIP;
+  }
+  return KIVI_OK;
 }
 
 }  // namespace
@@ -380,6 +561,153 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
   if (rc) return rc;
   c->tq = tq;
   c->tr = slot + 1;
+  return KIVI_OK;
+}
+
+// ---- ragged batches ---------------------------------------------------------
+
+int kivi_ragged_prefill(kivi_ragged_cache* c, const uint16_t* k, const uint16_t* v,
+                        int32_t in_tok_stride, const int32_t* ntok, const int32_t* tq,
+                        void* stream) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  const void* ptrs[] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
+                        c->v_scale, c->v_zero,  c->k_res,  c->v_res};
+  for (const void* p : ptrs)
+    if (!p) return KIVI_EINVAL;
+  if (!c->tq || !c->tr || !k || !v || !ntok || !tq) return KIVI_EINVAL;
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return KIVI_EALIGN;
+  if (!aligned16(k) || !aligned16(v)) return KIVI_EALIGN;
+  const kivi_shape& s = c->shape;
+  if (in_tok_stride < 1) return KIVI_ESHAPE;
+  for (int b = 0; b < s.batch; b++) {
+    if (ntok[b] < 0 || ntok[b] > in_tok_stride || tq[b] < 0 || tq[b] % s.group != 0 ||
+        ntok[b] < tq[b] || ntok[b] - tq[b] > s.residual)
+      return KIVI_ESHAPE;
+    if (tq[b] > s.capacity) return KIVI_ECAPACITY;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  const int H = s.num_kv_heads, D = s.head_dim;
+  int max_tq = 0, max_n = 0;
+  for (int b = 0; b < s.batch; b++) {
+    max_tq = std::max(max_tq, (int)tq[b]);
+    max_n = std::max(max_n, (int)(ntok[b] - tq[b]));
+  }
+  auto qz = batcher([&](const kivi::SeqList& L) {
+    hipError_t e = kivi::launch_quantize_k_list(k, L, H, D, s.bits, s.group, s.capacity,
+                                                in_tok_stride, max_tq, c->k_codes, c->k_scale,
+                                                c->k_zero, s.meta_half, st);
+    if (e == hipSuccess)
+      e = kivi::launch_quantize_v_list(v, L, H, D, s.bits, s.group, s.capacity, in_tok_stride,
+                                       max_tq, c->v_codes, c->v_scale, c->v_zero, s.meta_half, st);
+    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  });
+  for (int b = 0; b < s.batch; b++)
+    if (tq[b] > 0) qz.add(b, tq[b], 0, 0);
+  if ((rc = qz.flush())) return rc;
+  auto cp = batcher([&](const kivi::SeqList& L) {
+    hipError_t e = kivi::launch_copy_tokens_list(k, v, in_tok_stride, c->k_res, c->v_res,
+                                                 s.residual, L, max_n, H, D, st);
+    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  });
+  for (int b = 0; b < s.batch; b++)
+    if (ntok[b] > tq[b]) cp.add(b, tq[b], 0, ntok[b] - tq[b]);
+  if ((rc = cp.flush())) return rc;
+  for (int b = 0; b < s.batch; b++) {
+    c->tq[b] = tq[b];
+    c->tr[b] = ntok[b] - tq[b];
+  }
+  return KIVI_OK;
+}
+
+// lengths after appending one token to every sequence; false on overflow
+static bool ragged_after_append(const kivi_ragged_cache* c, std::vector<int>& tq,
+                                std::vector<int>& tr, std::vector<int>& slot) {
+  const kivi_shape& s = c->shape;
+  tq.resize(s.batch);
+  tr.resize(s.batch);
+  slot.resize(s.batch);
+  for (int b = 0; b < s.batch; b++) {
+    const bool flush = c->tr[b] == s.residual;
+    if (flush && (int64_t)c->tq[b] + s.residual > s.capacity) return false;
+    tq[b] = c->tq[b] + (flush ? s.residual : 0);
+    slot[b] = flush ? 0 : c->tr[b];
+    tr[b] = slot[b] + 1;
+  }
+  return true;
+}
+
+int kivi_ragged_append(kivi_ragged_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                       void* stream) {
+  int rc = check_ragged(c);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  std::vector<int> tq, tr, slot;
+  if (!ragged_after_append(c, tq, tr, slot)) return KIVI_ECAPACITY;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = enqueue_ragged_flush(c, st))) return rc;
+  if ((rc = enqueue_ragged_token_copy(c, k_new, v_new, slot, st))) return rc;
+  for (int b = 0; b < c->shape.batch; b++) {
+    c->tq[b] = tq[b];
+    c->tr[b] = tr[b];
+  }
+  return KIVI_OK;
+}
+
+int kivi_ragged_decode_auto_splits(const kivi_ragged_cache* c) {
+  int rc = check_ragged(c);
+  if (rc) return -rc;
+  const int cus = device_cu_count();
+  if (cus < 0) return cus;
+  int max_tq = 0, max_tr = 0;
+  for (int b = 0; b < c->shape.batch; b++) {
+    max_tq = std::max(max_tq, (int)c->tq[b]);
+    max_tr = std::max(max_tr, (int)c->tr[b]);
+  }
+  return auto_splits(c->shape, max_tq, max_tr, cus);
+}
+
+int kivi_ragged_decode_attn(const kivi_ragged_cache* c, const uint16_t* q, float softmax_scale,
+                            uint16_t* out, void* workspace, size_t workspace_bytes,
+                            int32_t num_splits, void* stream) {
+  int rc = check_ragged(c);
+  if (rc) return rc;
+  RaggedPlan p;
+  rc = plan_ragged_decode(c, std::vector<int>(c->tq, c->tq + c->shape.batch),
+                          std::vector<int>(c->tr, c->tr + c->shape.batch), q, out, workspace,
+                          workspace_bytes, num_splits, &p);
+  if (rc) return rc;
+  return enqueue_ragged_decode(c, p, q, softmax_scale, out, workspace, nullptr, nullptr,
+                               (hipStream_t)stream);
+}
+
+int kivi_ragged_append_decode_attn(kivi_ragged_cache* c, const uint16_t* k_new,
+                                   const uint16_t* v_new, const uint16_t* q, float softmax_scale,
+                                   uint16_t* out, void* workspace, size_t workspace_bytes,
+                                   int32_t num_splits, void* stream) {
+  int rc = check_ragged(c);
+  if (rc) return rc;
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  std::vector<int> tq, tr, slot;
+  if (!ragged_after_append(c, tq, tr, slot)) return KIVI_ECAPACITY;
+  RaggedPlan p;
+  rc = plan_ragged_decode(c, tq, tr, q, out, workspace, workspace_bytes, num_splits, &p);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  if ((rc = enqueue_ragged_flush(c, st))) return rc;
+  const bool fused = use_mfma(c->shape);
+  if (!fused && (rc = enqueue_ragged_token_copy(c, k_new, v_new, slot, st))) return rc;
+  rc = enqueue_ragged_decode(c, p, q, softmax_scale, out, workspace, fused ? k_new : nullptr,
+                             fused ? v_new : nullptr, st);
+  if (rc) return rc;
+  for (int b = 0; b < c->shape.batch; b++) {
+    c->tq[b] = tq[b];
+    c->tr[b] = tr[b];
+  }
   return KIVI_OK;
 }
 

@@ -6,7 +6,31 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kivi {
+
+// Sequences handled by one launch over per-sequence lengths (larger batches
+// are split into launches of at most this many sequences).
+constexpr int kMaxSeq = 128;
+
+// Per-sequence lengths of one ragged decode launch, passed by value: the
+// sequences b = 0 .. B-1 of the launch (pointers already offset to them).
+struct SeqLens {
+  int tq[kMaxSeq];
+  int tr[kMaxSeq];
+};
+
+// A list of per-sequence work items, passed by value: item i works on
+// sequence seq[i] of the launch's batch with three integer parameters whose
+// meaning is the launcher's (documented there).
+struct SeqList {
+  int n;
+  int seq[kMaxSeq];
+  int a[kMaxSeq];
+  int b[kMaxSeq];
+  int c[kMaxSeq];
+};
 
 // Device pointers and lengths of one decode call.
 struct DecodeArgs {
@@ -30,6 +54,21 @@ struct DecodeArgs {
   float scale;
 };
 
+// Kernel parameter of the decode kernels: nothing (uniform lengths, taken
+// from DecodeArgs) or the launch's per-sequence lengths.
+struct NoLens {};
+template <bool RAG>
+using LensT = std::conditional_t<RAG, SeqLens, NoLens>;
+// lengths of sequence b of the launch
+template <bool RAG>
+__device__ __forceinline__ int seq_tq(const DecodeArgs& a, const LensT<RAG>& l, int b) {
+  if constexpr (RAG) return l.tq[b]; else return a.tq;
+}
+template <bool RAG>
+__device__ __forceinline__ int seq_tr(const DecodeArgs& a, const LensT<RAG>& l, int b) {
+  if constexpr (RAG) return l.tr[b]; else return a.tr;
+}
+
 // Launchers: validate nothing (the C ABI layer did), return hipError_t of the
 // launch.
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G,
@@ -44,8 +83,26 @@ hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int 
                               int t0, uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
                               int slot0, int n, int B, int H, int D, hipStream_t st);
 
-// Generic decode kernel (any supported shape) + split combine.
+// Per-sequence variants.  Quantize: item i quantizes tokens [0, a[i]) of
+// sequence seq[i] of src ([*][H][in_stride][D]) into cache tokens
+// [b[i], b[i] + a[i]) of that sequence (a[i], b[i] multiples of G, a[i] <=
+// ntok_max).  Copy: item i copies tokens [a[i], a[i] + c[i]) of sequence
+// seq[i] of src into residual slots [b[i], b[i] + c[i]) (c[i] <= n_max).
+hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
+                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
+                                  void* scale, void* zero, int mh, hipStream_t st);
+hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H, int D, int bits,
+                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
+                                  void* scale, void* zero, int mh, hipStream_t st);
+hipError_t launch_copy_tokens_list(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
+                                   uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
+                                   const SeqList& list, int n_max, int H, int D, hipStream_t st);
+
+// Generic decode kernel (any supported shape) + split combine.  The ragged
+// variants take the launch's per-sequence lengths (a.tq / a.tr unused) and
+// need every sequence to hold at least one token.
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
+hipError_t launch_decode_generic_ragged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st);
 size_t decode_generic_lds_bytes(int r, int D);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
 
@@ -54,6 +111,8 @@ bool decode_mfma_supported(int D, int G, int r);
 // nw: requested waves per block (4 or 8); the block size actually used
 // for a gqa ratio r is decode_mfma_block_waves(r, nw)
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st);
+hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                     hipStream_t st);
 int decode_mfma_block_waves(int r, int nw);
 // resident blocks per compute unit of that kernel variant (occupancy query)
 int decode_mfma_blocks_per_cu(int bits, int r, int nw);

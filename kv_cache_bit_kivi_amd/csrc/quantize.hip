@@ -16,6 +16,10 @@
 // Each block stages its fp16 tile in LDS with 16-byte loads, computes the
 // group statistics from LDS, then writes whole 32-bit code words, so any
 // number of blocks can run concurrently without read-modify-write.
+// The LIST variants work on a list of sequences with per-sequence token
+// counts and offsets (ragged batches: prefill and per-sequence flushes).
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -56,6 +60,10 @@ __device__ __forceinline__ void put_meta(void* p, size_t i, float x) {
     static_cast<float*>(p)[i] = x;
 }
 
+struct NoList {};
+template <bool LIST>
+using ListT = std::conditional_t<LIST, SeqList, NoList>;
+
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // 16-byte copy with a non-temporal (read-once) source load
 __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
@@ -63,18 +71,25 @@ __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
       __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
 }
 
-// One block per (group of G source tokens, b*H + h).
-template <int BITS, bool MH>
+// One block per (group of G source tokens, b*H + h), or per (group, item*H +
+// h) over a sequence list (blocks past the item's token count exit).
+template <int BITS, bool MH, bool LIST>
 __global__ void __launch_bounds__(256)
 quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
                   int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero) {
+                  void* __restrict__ zero, int H, ListT<LIST> list) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
   float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
   float* s_zr = s_sc + D;                                    // [D]
   const int g = blockIdx.x;
-  const size_t bh = blockIdx.y;
+  size_t bh = blockIdx.y;
+  if constexpr (LIST) {
+    const int item = blockIdx.y / H;
+    if (g * G >= list.a[item]) return;   // the whole block: uniform
+    bh = (size_t)list.seq[item] * H + blockIdx.y % H;
+    dst_off = list.b[item];
+  }
   const uint4* src = reinterpret_cast<const uint4*>(k + (bh * in_stride + (size_t)g * G) * D);
   for (int i = threadIdx.x; i < G * D / 8; i += blockDim.x)
     copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
@@ -113,20 +128,27 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
   }
 }
 
-// One block per (32 source tokens, b*H + h).  Value codes are stored in
-// 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E) + (t%64)/E.
-template <int BITS, bool MH>
+// One block per (32 source tokens, b*H + h) (or per item, as above).  Value
+// codes are stored in 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E)
+// + (t%64)/E.
+template <int BITS, bool MH, bool LIST>
 __global__ void __launch_bounds__(256)
 quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_stride,
                   int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero) {
+                  void* __restrict__ zero, int H, ListT<LIST> list) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [32][D]
   const int NG = D / G;
   float* s_sc = reinterpret_cast<float*>(tile + 32 * D);     // [32][NG]
   float* s_zr = s_sc + 32 * NG;
   const int blk = blockIdx.x;
-  const size_t bh = blockIdx.y;
+  size_t bh = blockIdx.y;
+  if constexpr (LIST) {
+    const int item = blockIdx.y / H;
+    if (blk * 32 >= list.a[item]) return;   // the whole block: uniform
+    bh = (size_t)list.seq[item] * H + blockIdx.y % H;
+    dst_off = list.b[item];
+  }
   const uint4* src = reinterpret_cast<const uint4*>(v + (bh * in_stride + (size_t)blk * 32) * D);
   for (int i = threadIdx.x; i < 32 * D / 8; i += blockDim.x)
     copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
@@ -172,11 +194,20 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
   }
 }
 
+template <bool LIST>
 __global__ void __launch_bounds__(256)
 copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restrict__ v_src,
                    int src_stride, int t0, uint16_t* __restrict__ k_dst,
-                   uint16_t* __restrict__ v_dst, int dst_stride, int slot0, int n, int D) {
-  const size_t bh = blockIdx.y;
+                   uint16_t* __restrict__ v_dst, int dst_stride, int slot0, int n, int D, int H,
+                   ListT<LIST> list) {
+  size_t bh = blockIdx.y;
+  if constexpr (LIST) {
+    const int item = blockIdx.y / H;
+    bh = (size_t)list.seq[item] * H + blockIdx.y % H;
+    t0 = list.a[item];
+    slot0 = list.b[item];
+    n = list.c[item];
+  }
   const int per_tok = D / 8;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n * per_tok;
        i += gridDim.x * blockDim.x) {
@@ -196,12 +227,13 @@ hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, i
   dim3 grid(ntok / G, B * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero);
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
+                                   NoList{});
   };
   if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true>) : go(quantize_k_kernel<2, false>);
+    mh ? go(quantize_k_kernel<2, true, false>) : go(quantize_k_kernel<2, false, false>);
   else
-    mh ? go(quantize_k_kernel<4, true>) : go(quantize_k_kernel<4, false>);
+    mh ? go(quantize_k_kernel<4, true, false>) : go(quantize_k_kernel<4, false, false>);
   return hipGetLastError();
 }
 
@@ -211,12 +243,45 @@ hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, i
   dim3 grid(ntok / 32, B * H);
   size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero);
+    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
+                                   NoList{});
   };
   if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true>) : go(quantize_v_kernel<2, false>);
+    mh ? go(quantize_v_kernel<2, true, false>) : go(quantize_v_kernel<2, false, false>);
   else
-    mh ? go(quantize_v_kernel<4, true>) : go(quantize_v_kernel<4, false>);
+    mh ? go(quantize_v_kernel<4, true, false>) : go(quantize_v_kernel<4, false, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
+                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
+                                  void* scale, void* zero, int mh, hipStream_t st) {
+  if (list.n == 0 || ntok_max == 0) return hipSuccess;
+  dim3 grid(ntok_max / G, list.n * H);
+  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, H, list);
+  };
+  if (bits == 2)
+    mh ? go(quantize_k_kernel<2, true, true>) : go(quantize_k_kernel<2, false, true>);
+  else
+    mh ? go(quantize_k_kernel<4, true, true>) : go(quantize_k_kernel<4, false, true>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H, int D, int bits,
+                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
+                                  void* scale, void* zero, int mh, hipStream_t st) {
+  if (list.n == 0 || ntok_max == 0) return hipSuccess;
+  dim3 grid(ntok_max / 32, list.n * H);
+  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, 0, codes, scale, zero, H, list);
+  };
+  if (bits == 2)
+    mh ? go(quantize_v_kernel<2, true, true>) : go(quantize_v_kernel<2, false, true>);
+  else
+    mh ? go(quantize_v_kernel<4, true, true>) : go(quantize_v_kernel<4, false, true>);
   return hipGetLastError();
 }
 
@@ -225,8 +290,19 @@ hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int 
                               int slot0, int n, int B, int H, int D, hipStream_t st) {
   const int items = n * D / 8;
   dim3 grid((items + 255) / 256, B * H);
-  copy_tokens_kernel<<<grid, 256, 0, st>>>(k_src, v_src, src_stride, t0, k_dst, v_dst,
-                                           dst_stride, slot0, n, D);
+  copy_tokens_kernel<false><<<grid, 256, 0, st>>>(k_src, v_src, src_stride, t0, k_dst, v_dst,
+                                                  dst_stride, slot0, n, D, H, NoList{});
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_tokens_list(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
+                                   uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
+                                   const SeqList& list, int n_max, int H, int D, hipStream_t st) {
+  if (list.n == 0 || n_max == 0) return hipSuccess;
+  const int items = n_max * D / 8;
+  dim3 grid((items + 255) / 256, list.n * H);
+  copy_tokens_kernel<true><<<grid, 256, 0, st>>>(k_src, v_src, src_stride, 0, k_dst, v_dst,
+                                                 dst_stride, 0, 0, D, H, list);
   return hipGetLastError();
 }
 

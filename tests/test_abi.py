@@ -190,3 +190,99 @@ def test_append_decode_errors_leave_state():
     assert (c.tq, c.tr) == (64, 3)
     c = cache(ptrs=[P] * 7 + [0])
     assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+
+
+# ---- ragged batches: validation before any HIP call, lengths untouched ----
+
+def ragged(tq, tr, ptrs=None, **kw):
+    """A ragged cache over fake device pointers; tq / tr are kept alive on the
+    returned struct (the C side reads and writes them in place)."""
+    import numpy as np
+    from kv_cache_bit_kivi_amd._lib import kivi_ragged_cache
+    s = shape(**kw)
+    tqa = np.ascontiguousarray(tq, np.int32)
+    tra = np.ascontiguousarray(tr, np.int32)
+    assert len(tqa) == s.batch and len(tra) == s.batch
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    c = kivi_ragged_cache(s, *(ptrs or [P] * 8), tqa.ctypes.data_as(p32),
+                          tra.ctypes.data_as(p32))
+    c._keep = (tqa, tra)
+    return c
+
+
+def lens(c):
+    return c._keep[0].tolist(), c._keep[1].tolist()
+
+
+def test_ragged_append_errors_leave_state():
+    ap = _lib.kivi_ragged_append
+    c = ragged([416, 0], [128, 5])       # sequence 0 would flush past capacity 512
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    assert lens(c) == ([416, 0], [128, 5])
+    c = ragged([64, 33], [1, 1])         # tq not a multiple of the group
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_ESHAPE
+    c = ragged([64, 32], [1, 129])       # residual longer than R
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_ESHAPE
+    assert lens(c) == ([64, 32], [1, 129])
+    c = ragged([64, 1024], [1, 0])       # past capacity
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    c = ragged([0, 0], [0, 0])
+    assert ap(ctypes.byref(c), None, P, None) == KIVI_EINVAL
+    assert ap(ctypes.byref(c), P, P + 4, None) == KIVI_EALIGN
+    c = ragged([0, 0], [0, 0], ptrs=[P] * 7 + [0])
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_EINVAL
+    c = ragged([0, 0], [0, 0])
+    c.tq = None
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_EINVAL
+
+
+def test_ragged_prefill_errors():
+    import numpy as np
+    pf = _lib.kivi_ragged_prefill
+    p32 = ctypes.POINTER(ctypes.c_int32)
+
+    def call(c, stride, ntok, tq, k=P):
+        n = np.asarray(ntok, np.int32)
+        t = np.asarray(tq, np.int32)
+        return pf(ctypes.byref(c), k, P, stride, n.ctypes.data_as(p32), t.ctypes.data_as(p32),
+                  None)
+
+    c = ragged([0, 0], [0, 0])
+    assert call(c, 256, [300, 64], [256, 64]) == KIVI_ESHAPE    # ntok > stride
+    assert call(c, 512, [300, 64], [128, 64]) == KIVI_ESHAPE    # residual part > R
+    assert call(c, 256, [100, 64], [48, 64]) == KIVI_ESHAPE     # tq % G
+    assert call(c, 256, [10, 64], [32, 64]) == KIVI_ESHAPE      # tq > ntok
+    assert call(c, 640, [600, 64], [544, 64]) == KIVI_ECAPACITY
+    assert call(c, 0, [0, 0], [0, 0]) == KIVI_ESHAPE            # stride < 1
+    assert call(c, 64, [64, 64], [64, 64], k=None) == KIVI_EINVAL
+    assert call(c, 64, [64, 64], [64, 64], k=P + 2) == KIVI_EALIGN
+    assert lens(c) == ([0, 0], [0, 0])
+
+
+def test_ragged_decode_errors():
+    dec = _lib.kivi_ragged_decode_attn
+    c = ragged([64, 0], [3, 0])          # sequence 1 is empty
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    c = ragged([64, 32], [3, 1])
+    assert dec(ctypes.byref(c), None, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert dec(ctypes.byref(c), P, 0.1, P + 2, None, 0, 1, None) == KIVI_EALIGN
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, -1, None) == KIVI_EINVAL
+    need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4)
+    assert dec(ctypes.byref(c), P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
+    assert dec(ctypes.byref(c), P, 0.1, P, None, need, 4, None) == KIVI_EINVAL
+    assert dec(ctypes.byref(c), P, 0.1, P, P + 4, need, 4, None) == KIVI_EALIGN
+    c = ragged([64, 32], [3, 200])
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+
+
+def test_ragged_append_decode_errors_leave_state():
+    ad = _lib.kivi_ragged_append_decode_attn
+    c = ragged([416, 64], [128, 7])      # sequence 0's flush would pass capacity
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_ECAPACITY
+    assert lens(c) == ([416, 64], [128, 7])
+    c = ragged([0, 0], [0, 0])           # empty before, one token each after: valid sizes
+    assert ad(ctypes.byref(c), P, P, None, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, -1, None) == KIVI_EINVAL
+    need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4)
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
+    assert lens(c) == ([0, 0], [0, 0])
