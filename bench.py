@@ -147,25 +147,32 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False):
 
     k, v = synth.kv(w)
     cap = w.capacity(64)
-    oc = oracle.OracleCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                            w.residual, cap, meta_half=meta_half)
-    oc.prefill(k, v, w.tq)
+    # one oracle cache per sequence for a ragged batch, one for the whole batch otherwise
+    groups = ([(b, b + 1) for b in range(w.batch)] if w.ragged else [(0, w.batch)])
+    ctx, tqs = w.contexts(), w.tqs()
+    ocs = []
+    for b0, b1 in groups:
+        oc = oracle.OracleCache(b1 - b0, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
+                                w.residual, cap, meta_half=meta_half)
+        oc.prefill(k[b0:b1, :, : int(ctx[b0])], v[b0:b1, :, : int(ctx[b0])], int(tqs[b0]))
+        ocs.append(oc)
     del k, v
     mb = 2 if meta_half else 4
     nbytes, steps, t_total = 0, 0, 0.0
     while t_total < min_seconds and steps < 64:
         kn, vn = synth.new_token(w, steps + 1)
         q = synth.query(w, steps + 1)
-        flush = oc.tr == w.residual
-        t0 = time.perf_counter()
-        oc.append(kn, vn)
-        oc.decode(q, w.softmax_scale)
-        dt = time.perf_counter() - t0
-        t_total += dt
-        nbytes += append_bytes(w.batch, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
-                               flush, mb)
-        nbytes += decode_bytes(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
-                               oc.tr, mb)
+        for (b0, b1), oc in zip(groups, ocs):
+            flush = oc.tr == w.residual
+            t0 = time.perf_counter()
+            oc.append(np.ascontiguousarray(kn[b0:b1]), np.ascontiguousarray(vn[b0:b1]))
+            oc.decode(np.ascontiguousarray(q[b0:b1]), w.softmax_scale)
+            t_total += time.perf_counter() - t0
+            n = b1 - b0
+            nbytes += append_bytes(n, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
+                                   flush, mb)
+            nbytes += decode_bytes(n, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
+                                   oc.tr, mb)
         steps += 1
         if t_total > max_seconds:
             break
@@ -224,7 +231,7 @@ def main():
 
     from kv_cache_bit_kivi_amd import synth
     from kv_cache_bit_kivi_amd._lib import lib
-    from kv_cache_bit_kivi_amd.cache import KiviCache
+    from kv_cache_bit_kivi_amd.cache import KiviCache, RaggedKiviCache
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -239,13 +246,21 @@ def main():
     per_layer_appends = (total_steps + NL - 1) // NL
     cap = w.capacity(per_layer_appends + R)
 
+    ragged = w.ragged
+    ctx0 = w.contexts().astype(np.int32)          # per-sequence lengths at the start
+    tq0 = w.tqs().astype(np.int32)
+    tr0 = ctx0 - tq0
     k, v = synth.kv(w)
     kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     del k, v
     caches = []
     for _ in range(NL):
-        c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
-        c.prefill(kd, vd, w.tq)
+        if ragged:
+            c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+            c.prefill(kd, vd, ctx0, tq0)
+        else:
+            c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+            c.prefill(kd, vd, w.tq)
         caches.append(c)
     del kd, vd
     # distinct synthetic tokens / queries for every step, resident on the GPU
@@ -270,14 +285,13 @@ def main():
     torch.cuda.synchronize()
 
     # The step loop calls the C ABI directly with pointers bound once, so the
-    # host enqueues faster than the GPU drains and the events around each
-    # decode bracket queued work, not host-side gaps.
+    # host enqueues faster than the GPU drains and the events bracket queued
+    # work, not host-side gaps.
     import ctypes
 
     L = lib()
     cur = torch.cuda.current_stream()
     stream = cur.cuda_stream
-    crefs = [ctypes.byref(c.c) for c in caches]
     kptr = [t.data_ptr() for t in knew]
     vptr = [t.data_ptr() for t in vnew]
     qptr = [t.data_ptr() for t in qs]
@@ -285,83 +299,114 @@ def main():
     wsp = [(c.workspace.data_ptr(), c.workspace.numel()) if c.workspace is not None else (None, 0)
            for c in caches]
     scale = float(w.softmax_scale)
-    append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
-    fused_fn = L.kivi_append_decode_attn
+    if ragged:
+        crefs = [ctypes.byref(c.rc) for c in caches]
+        append_fn, decode_fn = L.kivi_ragged_append, L.kivi_ragged_decode_attn
+        fused_fn = L.kivi_ragged_append_decode_attn
 
-    def step(i, ev0=None, ev1=None):
+        def flushes(li):          # sequences whose residual is full (flush on this append)
+            return caches[li].tr_arr == R
+
+        def lengths(li):
+            return caches[li].tq_arr.copy(), caches[li].tr_arr.copy()
+    else:
+        crefs = [ctypes.byref(c.c) for c in caches]
+        append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
+        fused_fn = L.kivi_append_decode_attn
+
+        def flushes(li):
+            return caches[li].c.tr == R
+
+        def lengths(li):
+            return caches[li].c.tq, caches[li].c.tr
+
+    def step(i):
         li = i % NL
-        c = caches[li].c
         j = i % n_tok
-        flush = c.tr == R
+        fl = flushes(li)
         if args.separate:
             rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
             if rc:
-                raise RuntimeError(f"kivi_append failed: {rc}")
-            if ev0 is not None:
-                ev0.record(cur)
+                raise RuntimeError(f"append failed: {rc}")
             rc = decode_fn(crefs[li], qptr[j], scale, optr[li], wsp[li][0], wsp[li][1],
                            args.splits, stream)
         else:
-            if ev0 is not None:
-                ev0.record(cur)
             rc = fused_fn(crefs[li], kptr[j], vptr[j], qptr[j], scale, optr[li], wsp[li][0],
                           wsp[li][1], args.splits, stream)
-        if ev1 is not None:
-            ev1.record(cur)
         if rc:
             raise RuntimeError(f"decode step failed: {rc}")
-        return flush, c.tq, c.tr
+        return (fl, *lengths(li))
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    for c in caches:       # back to the workload's starting lengths (full residual)
-        c.set_lengths(w.tq, w.tr)
+    for c in caches:       # back to the workload's starting lengths
+        if ragged:
+            c.set_lengths(tq0, tr0)
+        else:
+            c.set_lengths(w.tq, w.tr)
     splits_used = caches[0].auto_splits() if args.splits == 0 else args.splits
 
-    # HIP events on the launch stream bracket windows of W consecutive steps
-    # (an event is a packet on that stream: bracketing every launch would add
-    # its own dispatch latency to each measured launch and slow the loop).
-    W = max(1, min(args.window, args.steps))
-    nwin = args.steps // W
-    wev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(nwin)]
+    # HIP events on the launch stream bracket windows of up to W consecutive
+    # steps that flush nothing (an event is a packet on that stream:
+    # bracketing every launch would add its own dispatch latency to each
+    # measured launch and slow the loop).  Whether a step flushes is known on
+    # the host before its call, so a window closes before any flush step.
+    W = max(1, args.window)
+    pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 2)]
+    windows, open_w, pi = [], None, 0
     meta = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        wi, j = divmod(i, W)
-        e0 = wev[wi][0] if wi < nwin and j == 0 else None
-        e1 = wev[wi][1] if wi < nwin and j == W - 1 else None
-        meta.append(step(i, e0, e1))
+        fl = bool(np.any(flushes(i % NL)))
+        if open_w is not None and (fl or len(open_w[2]) == W):
+            open_w[1].record(cur)
+            windows.append(open_w)
+            open_w = None
+        if not fl and open_w is None:
+            open_w = (pool[pi], pool[pi + 1], [])
+            pi += 2
+            open_w[0].record(cur)
+        meta.append(step(i))
+        if open_w is not None:
+            open_w[2].append(i)
+    if open_w is not None:
+        open_w[1].record(cur)
+        windows.append(open_w)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    dec_bytes = [decode_bytes(B, H, r, D, bits, G, tq, tr, mb) for _, tq, tr in meta]
-    app_bytes = [append_bytes(B, H, D, bits, G, R, f, mb) for f, _, _ in meta]
+    # algorithmic bytes of every step, at the lengths the decode reads (after
+    # the step's append); ragged: summed over the sequences
+    per_seq = 1 if ragged else B
+    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, np.asarray(tq, np.int64),
+                                         np.asarray(tr, np.int64), mb)))
+                 for _, tq, tr in meta]
+    app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb)
+                             for f in np.atleast_1d(fl)]))
+                 for fl, _, _ in meta]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
     # The timed call is the decode launch, carrying the new token's append when
-    # fused.  Flush steps (a full residual quantized first: 1 in R steps per
-    # layer) also run the quantize launches inside the timed interval, so the
-    # roofline of the decode kernel averages the other steps only.
-    # windows holding a flush step (a full residual quantized first) are left
-    # out: the roofline is that of the decode launch alone
+    # fused (separate mode: the append launch too); windows hold no flush.
     new_tok = append_bytes(B, H, D, bits, G, R, False, mb)
-    per_call = [d + new_tok for d in dec_bytes]   # (separate mode: the append launch too)
-    win_ms, win_bytes = [], []
-    for wi in range(nwin):
-        steps_w = range(wi * W, (wi + 1) * W)
-        if any(meta[i][0] for i in steps_w):
-            continue
-        win_ms.append(wev[wi][0].elapsed_time(wev[wi][1]) / W)
-        win_bytes.append(sum(per_call[i] for i in steps_w) / W)
-    if not win_ms:
-        raise SystemExit("no window of the timed region is free of flush steps: raise --steps")
-    call_bytes = np.array(win_bytes)
-    dec_ms = np.array(win_ms)
+    per_call = [d + new_tok for d in dec_bytes]
+    win_ms = np.array([e0.elapsed_time(e1) / len(ix) for e0, e1, ix in windows])
+    win_bytes = np.array([sum(per_call[i] for i in ix) / len(ix) for _, _, ix in windows])
+    if not len(win_ms):
+        raise SystemExit("every timed step flushes: raise --steps")
+    n_launch = sum(len(ix) for _, _, ix in windows)
+    w_time = float(sum(t * len(ix) for t, (_, _, ix) in zip(win_ms, windows)))   # ms
+    w_bytes = float(sum(b * len(ix) for b, (_, _, ix) in zip(win_bytes, windows)))
+    n_flush = sum(int(np.sum(fl)) for fl, _, _ in meta)
+
     value = total_bytes / elapsed / 1e9
-    achieved = call_bytes.mean() / (dec_ms.mean() * 1e-3) / 1e9
-    n_flush = sum(1 for f, _, _ in meta if f)
+    achieved = w_bytes / (w_time * 1e-3) / 1e9
+    if ragged:
+        calls = ("kivi_ragged_append + kivi_ragged_decode_attn" if args.separate
+                 else "kivi_ragged_append_decode_attn")
+    else:
+        calls = "kivi_append + kivi_decode_attn" if args.separate else "kivi_append_decode_attn"
 
     result = {
         "metric": METRIC,
@@ -378,32 +423,35 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "q_heads": H * r, "kv_heads": H, "head_dim": D,
-            "context_at_start": w.context, "bits": bits, "group": G, "residual": R,
+            "context_at_start": (w.context if not ragged else
+                                 {"min": int(ctx0.min()), "mean": round(float(ctx0.mean()), 1),
+                                  "max": int(ctx0.max()), "per_sequence": ctx0.tolist()}),
+            "bits": bits, "group": G, "residual": R,
             "scale_zero": "fp16" if meta_half else "fp32",
             "layers_rotated": NL, "decode_splits": splits_used,
-            "step_call": "kivi_append + kivi_decode_attn" if args.separate else
-                         "kivi_append_decode_attn",
-            "flushes_in_timed_region": n_flush,
+            "step_call": calls,
+            "sequence_flushes_in_timed_region": n_flush,
         },
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "query_heads_per_s": round(args.steps * B * H * r / elapsed, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("kivi_append + kivi_decode_attn (two launches per step)" if args.separate
-                       else "kivi decode attention with the append folded in (one "
-                       "kivi_append_decode_attn launch per step)") +
-                      f"; HIP events around windows of {W} steps, windows with a flush excluded",
+            "kernel": (f"{calls} (append and decode launches)" if args.separate
+                       else f"kivi decode attention with the append folded in ({calls}: one "
+                       "decode launch per step)") +
+                      f"; HIP events around runs of up to {W} consecutive steps without a flush",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": measured_traffic(tag),
-            "bytes_per_launch": int(call_bytes.mean()),
-            "launches_averaged": int(len(call_bytes)) * W,
+            "bytes_per_launch": int(w_bytes / n_launch),
+            "launches_averaged": int(n_launch),
             "window_launches": W,
-            "avg_launch_us": round(float(dec_ms.mean()) * 1e3, 3),
-            "window_p10_us": round(float(np.percentile(dec_ms, 10)) * 1e3, 3),
-            "window_p90_us": round(float(np.percentile(dec_ms, 90)) * 1e3, 3),
+            "windows": len(windows),
+            "avg_launch_us": round(w_time / n_launch * 1e3, 3),
+            "window_p10_us": round(float(np.percentile(win_ms, 10)) * 1e3, 3),
+            "window_p90_us": round(float(np.percentile(win_ms, 90)) * 1e3, 3),
         },
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -67,7 +67,7 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   float* stat = red + 8;             // [RR] running max, [RR] running sum, [RR] rescale
 
   const int split = blockIdx.x;
-  const int u = blockIdx.y;          // b * H + h
+  const int u = seq_plane<RAG>(lens, blockIdx.y, a.H);   // b * H + h
   const int b = u / a.H, h = u % a.H;
   const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
   const int L = tq + tr;

@@ -268,7 +268,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
   const int S = a.S, H = a.H;
-  const int u = blockIdx.x / S, split = blockIdx.x % S;
+  const int u = seq_plane<RAG>(lens, blockIdx.x / S, H), split = blockIdx.x % S;
   const int b = u / H;
   const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
 

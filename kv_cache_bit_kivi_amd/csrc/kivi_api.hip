@@ -297,6 +297,11 @@ int enqueue_ragged_decode(const kivi_ragged_cache* c, const RaggedPlan& p, const
       mq = std::max(mq, lens.tq[i]);
       mr = std::max(mr, lens.tr[i]);
     }
+    // longest sequences first (dispatch order; ties keep the batch order)
+    for (int i = 0; i < n; i++) lens.order[i] = i;
+    std::stable_sort(lens.order, lens.order + n, [&](int x, int y) {
+      return lens.tq[x] + lens.tr[x] > lens.tq[y] + lens.tr[y];
+    });
     a.tq = mq;   // (unused by the per-sequence kernels)
     a.tr = mr;
     a.S = S;

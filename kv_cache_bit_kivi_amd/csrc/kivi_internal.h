@@ -16,9 +16,13 @@ constexpr int kMaxSeq = 128;
 
 // Per-sequence lengths of one ragged decode launch, passed by value: the
 // sequences b = 0 .. B-1 of the launch (pointers already offset to them).
+// order[] lists the sequences longest first: the blocks are dispatched in
+// index order, so taking sequence order[i] for the i-th group of blocks
+// starts the longest work first and lets the short work fill in behind it.
 struct SeqLens {
   int tq[kMaxSeq];
   int tr[kMaxSeq];
+  int order[kMaxSeq];
 };
 
 // A list of per-sequence work items, passed by value: item i works on
@@ -67,6 +71,11 @@ __device__ __forceinline__ int seq_tq(const DecodeArgs& a, const LensT<RAG>& l, 
 template <bool RAG>
 __device__ __forceinline__ int seq_tr(const DecodeArgs& a, const LensT<RAG>& l, int b) {
   if constexpr (RAG) return l.tr[b]; else return a.tr;
+}
+// (b, h) plane of the i-th group of blocks (i = sequence-major plane index)
+template <bool RAG>
+__device__ __forceinline__ int seq_plane(const LensT<RAG>& l, int i, int H) {
+  if constexpr (RAG) return l.order[i / H] * H + i % H; else return i;
 }
 
 // Launchers: validate nothing (the C ABI layer did), return hipError_t of the

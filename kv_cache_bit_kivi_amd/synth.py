@@ -22,7 +22,7 @@ from dataclasses import dataclass
 import numpy as np
 
 # stream ids of SeedSequence([seed, stream, ...])
-S_OUTLIER, S_K, S_V, S_Q, S_KNEW, S_VNEW, S_QNEW = range(7)
+S_OUTLIER, S_K, S_V, S_Q, S_KNEW, S_VNEW, S_QNEW, S_LEN = range(8)
 
 
 @dataclass(frozen=True)
@@ -41,6 +41,7 @@ class Workload:
     n_outliers: int
     seed: int
     steps: int = 0      # streaming decode steps after the prefill
+    min_context: int = 0   # > 0: ragged batch, contexts drawn in [min_context, context]
 
     @property
     def gqa(self) -> int:
@@ -49,6 +50,24 @@ class Workload:
     @property
     def tr(self) -> int:
         return self.context - self.tq
+
+    @property
+    def ragged(self) -> bool:
+        return self.min_context > 0
+
+    def contexts(self) -> np.ndarray:
+        """Per-sequence context lengths: all ``context``, or (ragged) drawn
+        uniformly from [min_context, context] by a seeded stream."""
+        if not self.ragged:
+            return np.full(self.batch, self.context, np.int64)
+        g = _rng(self.seed, S_LEN)
+        return g.integers(self.min_context, self.context + 1, self.batch)
+
+    def tqs(self) -> np.ndarray:
+        """Per-sequence quantized lengths (the residual holds the rest)."""
+        if not self.ragged:
+            return np.full(self.batch, self.tq, np.int64)
+        return np.array([_resid_split(int(L), self.residual) for L in self.contexts()])
 
     @property
     def softmax_scale(self) -> float:
@@ -89,6 +108,10 @@ WORKLOADS = {
     # long context: batch 1, 32 heads, 262144 tokens
     "long_ctx_262144": Workload("long_ctx_262144", 1, 32, 32, 128, 262144, 2, 32, 128,
                                 _resid_split(262144, 128), 8, 1005),
+    # ragged serving batch: 16 Llama-2-7B-shaped sequences, contexts uniform in
+    # [512, 8192] (each residual at its own fill level)
+    "ragged_b16_ctx512_8192": Workload("ragged_b16_ctx512_8192", 16, 32, 32, 128, 8192, 2, 32,
+                                       128, _resid_split(8192, 128), 8, 1006, min_context=512),
 }
 
 

@@ -3,6 +3,8 @@ buffer sizes (kivi_cache_bytes) for a cache filled to capacity, for both
 metadata widths, so the roofline's bytes per launch are the cache's bytes."""
 import ctypes
 
+import numpy as np
+
 import pytest
 
 import bench
@@ -46,3 +48,27 @@ def test_cpu_baseline_runs_its_sample(meta_half):
     steps = int(r["sample"].split()[0])
     assert steps > 1
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+
+
+def test_ragged_workload_lengths():
+    """The ragged workload's per-sequence lengths: inside [min_context,
+    context], seeded (stable), tq a multiple of the group, 1..R residual."""
+    from kv_cache_bit_kivi_amd import synth
+    w = synth.WORKLOADS["ragged_b16_ctx512_8192"]
+    ctx, tq = w.contexts(), w.tqs()
+    assert len(ctx) == w.batch and w.ragged
+    assert ctx.min() >= w.min_context and ctx.max() <= w.context
+    assert len(set(ctx.tolist())) > w.batch // 2          # genuinely ragged
+    assert np.all(tq % w.group == 0)
+    assert np.all((ctx - tq >= 1) & (ctx - tq <= w.residual))
+    assert np.array_equal(ctx, w.contexts())
+    u = synth.WORKLOADS["llama2_7b_b8_ctx4096"]
+    assert not u.ragged and np.all(u.contexts() == u.context) and np.all(u.tqs() == u.tq)
+
+
+def test_cpu_baseline_ragged_sample():
+    from kv_cache_bit_kivi_amd import synth
+    w = synth.WORKLOADS["ragged_b16_ctx512_8192"].with_(batch=3, q_heads=2, kv_heads=2,
+                                                        context=384, min_context=40)
+    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0)
+    assert int(r["sample"].split()[0]) > 1 and r["value"] > 0
