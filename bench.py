@@ -22,7 +22,6 @@ and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import os
@@ -56,10 +55,16 @@ def append_bytes(B, H, D, bits, G, R, flush, mb=4):
     return b
 
 
+# the sources that define the decode kernel and its launch configuration
+DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.hip",
+                  "kivi_internal.h", "kivi_api.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
