@@ -57,7 +57,7 @@ def append_bytes(B, H, D, bits, G, R, flush, mb=4):
 
 # the sources that define the decode kernel and its launch configuration
 DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.hip",
-                  "kivi_internal.h", "kivi_api.hip")
+                  "decode_mfma_paged.hip", "kivi_internal.h", "kivi_api.hip")
 
 
 def kernel_source_hash() -> str:

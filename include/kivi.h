@@ -274,6 +274,74 @@ int kivi_ragged_append_decode_attn(kivi_ragged_cache* cache,
                                    void* workspace, size_t workspace_bytes,
                                    int32_t num_splits, void* stream);
 
+/* ---- Paged quantized store --------------------------------------------
+ * A server keeps many sequences of unpredictable length, so the quantized
+ * part of each sequence lives in fixed-size pages drawn from shared pools, as
+ * in paged attention (mlsanity KIVI page, Key facts and Abstract: KIVI plugs
+ * into a serving stack; scholarfeed "KIVI" quote page: the quantized tokens
+ * and the fixed-length full-precision residual are kept apart, so they are
+ * managed apart here too).  A page holds P = page_tokens consecutive tokens of
+ * one sequence for every KV head; page p, head h is a "slice" with exactly the
+ * layout of a kivi_cache plane of capacity P:
+ *   k_codes : uint32 [num_pages][Hkv][P][D/E]
+ *   k_scale, k_zero : meta [num_pages][Hkv][P/G][D]
+ *   v_codes : uint32 [num_pages][Hkv][P/64][D][64/E]
+ *   v_scale, v_zero : meta [num_pages][Hkv][P][D/G]
+ * Logical token t of sequence b is token t mod P of page
+ * block_table[b * (capacity / P) + t / P].  The residual stays one
+ * fixed-length pool per sequence: k_res, v_res fp16 [B][Hkv][R][D].
+ * shape.capacity is the most tokens one sequence may quantize (a multiple of
+ * P); P is a power of two, at least 64 and at least group (KIVI_ESHAPE
+ * otherwise).  The block
+ * table is a DEVICE int32 array [batch][capacity / P] (4-byte aligned) owned
+ * and filled by the caller: every entry a call may touch must name a page
+ * (the pages of tokens [0, tq[b]) for a decode, plus those of [tq[b],
+ * tq[b] + residual) for a call that may flush, i.e. prefill and append), and
+ * pages written by different sequences must be distinct.  Entries outside
+ * [0, num_pages) are never written and read as zeros.  Lengths, validation,
+ * updates and results are those of kivi_ragged_cache: each sequence is
+ * bit-identical to the same sequence in a ragged (contiguous) cache. */
+typedef struct {
+  kivi_shape shape;
+  int32_t page_tokens;
+  int32_t num_pages;
+  uint32_t* k_codes;
+  void* k_scale;
+  void* k_zero;
+  uint32_t* v_codes;
+  void* v_scale;
+  void* v_zero;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  const int32_t* block_table;   /* device [batch][capacity / page_tokens] */
+  int32_t* tq;                  /* host [batch] */
+  int32_t* tr;                  /* host [batch] */
+} kivi_paged_cache;
+
+/* Bytes of each page pool for a shape, page size and page count (host
+ * arithmetic only).  KIVI_OK, or a shape error. */
+int kivi_paged_pool_bytes(const kivi_shape* shape, int32_t page_tokens,
+                          int32_t num_pages, size_t* k_codes, size_t* k_meta,
+                          size_t* v_codes, size_t* v_meta);
+
+/* The kivi_ragged_* calls on a paged store (same arguments and rules). */
+int kivi_paged_prefill(kivi_paged_cache* cache, const uint16_t* k,
+                       const uint16_t* v, int32_t in_tok_stride,
+                       const int32_t* ntok, const int32_t* tq, void* stream);
+int kivi_paged_append(kivi_paged_cache* cache, const uint16_t* k_new,
+                      const uint16_t* v_new, void* stream);
+int kivi_paged_decode_auto_splits(const kivi_paged_cache* cache);
+int kivi_paged_decode_attn(const kivi_paged_cache* cache, const uint16_t* q,
+                           float softmax_scale, uint16_t* out, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits,
+                           void* stream);
+int kivi_paged_append_decode_attn(kivi_paged_cache* cache,
+                                  const uint16_t* k_new, const uint16_t* v_new,
+                                  const uint16_t* q, float softmax_scale,
+                                  uint16_t* out, void* workspace,
+                                  size_t workspace_bytes, int32_t num_splits,
+                                  void* stream);
+
 /* Short static description of a status code. */
 const char* kivi_strerror(int status);
 

@@ -53,6 +53,18 @@ class kivi_ragged_cache(ctypes.Structure):
     ]
 
 
+class kivi_paged_cache(ctypes.Structure):
+    _fields_ = [
+        ("shape", kivi_shape),
+        ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("tq", ctypes.POINTER(ctypes.c_int32)), ("tr", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
 # name -> (restype, argtypes), mirroring include/kivi.h
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
 _SZP = ctypes.POINTER(ctypes.c_size_t)
@@ -60,6 +72,7 @@ _SHP = ctypes.POINTER(kivi_shape)
 _CP = ctypes.POINTER(kivi_cache)
 _RP = ctypes.POINTER(kivi_ragged_cache)
 _I32P = ctypes.POINTER(ctypes.c_int32)
+_PP = ctypes.POINTER(kivi_paged_cache)
 PROTOTYPES = {
     "kivi_cache_bytes": (ctypes.c_int, [_SHP, _SZP, _SZP, _SZP, _SZP, _SZP, _SZP]),
     "kivi_quantize_k": (ctypes.c_int, [_SHP, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
@@ -77,6 +90,13 @@ PROTOTYPES = {
     "kivi_ragged_decode_attn": (ctypes.c_int, [_RP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
     "kivi_ragged_append_decode_attn": (ctypes.c_int, [_RP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
                                                       _sz, _i32, _vp]),
+    "kivi_paged_pool_bytes": (ctypes.c_int, [_SHP, _i32, _i32, _SZP, _SZP, _SZP, _SZP]),
+    "kivi_paged_prefill": (ctypes.c_int, [_PP, _vp, _vp, _i32, _I32P, _I32P, _vp]),
+    "kivi_paged_append": (ctypes.c_int, [_PP, _vp, _vp, _vp]),
+    "kivi_paged_decode_auto_splits": (ctypes.c_int, [_PP]),
+    "kivi_paged_decode_attn": (ctypes.c_int, [_PP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
+    "kivi_paged_append_decode_attn": (ctypes.c_int, [_PP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp,
+                                                     _sz, _i32, _vp]),
     "kivi_strerror": (ctypes.c_char_p, [ctypes.c_int]),
 }
 
@@ -134,4 +154,10 @@ kivi_ragged_append = _fn("kivi_ragged_append")
 kivi_ragged_decode_auto_splits = _fn("kivi_ragged_decode_auto_splits")
 kivi_ragged_decode_attn = _fn("kivi_ragged_decode_attn")
 kivi_ragged_append_decode_attn = _fn("kivi_ragged_append_decode_attn")
+kivi_paged_pool_bytes = _fn("kivi_paged_pool_bytes")
+kivi_paged_prefill = _fn("kivi_paged_prefill")
+kivi_paged_append = _fn("kivi_paged_append")
+kivi_paged_decode_auto_splits = _fn("kivi_paged_decode_auto_splits")
+kivi_paged_decode_attn = _fn("kivi_paged_decode_attn")
+kivi_paged_append_decode_attn = _fn("kivi_paged_append_decode_attn")
 kivi_strerror = _fn("kivi_strerror")

@@ -30,8 +30,8 @@ COMMON = [
 EXTRA = {
     "quantize.hip": ["-ffp-contract=off"],
 }
-SOURCES = ["decode_mfma.hip", "decode_mfma_ragged.hip", "kivi_api.hip", "quantize.hip",
-           "decode_generic.hip"]
+SOURCES = ["decode_mfma.hip", "decode_mfma_ragged.hip", "decode_mfma_paged.hip", "kivi_api.hip",
+           "quantize.hip", "decode_generic.hip"]
 
 
 def _compile(src: str) -> str:

@@ -12,7 +12,7 @@ import torch
 import numpy as np
 
 from . import _lib
-from ._lib import check, kivi_cache, kivi_ragged_cache, kivi_shape
+from ._lib import check, kivi_cache, kivi_paged_cache, kivi_ragged_cache, kivi_shape
 
 
 def _ptr(t: torch.Tensor | None) -> int | None:
@@ -224,3 +224,111 @@ class RaggedKiviCache(KiviCache):
         if s < 0:
             check(-s, "kivi_ragged_decode_auto_splits")
         return s
+
+
+class PagedKiviCache(RaggedKiviCache):
+    """A ragged batch whose quantized tokens live in page pools.
+
+    ``table`` (int32 [batch][capacity // page_tokens], host array) names the
+    page of every logical page of every sequence; it is copied to a device
+    tensor (``self.table``).  By default sequence b's j-th page is page
+    b * (capacity // page_tokens) + j.  Pools have the layouts of
+    include/kivi.h; the residual stays per sequence."""
+
+    def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                 page_tokens, num_pages=None, table=None, device="cuda", meta_half=False):
+        self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
+                                meta_half)
+        self.meta_half = bool(meta_half)
+        P = page_tokens
+        max_pages = capacity // P
+        if num_pages is None:
+            num_pages = batch * max_pages
+        sizes = [ctypes.c_size_t() for _ in range(4)]
+        check(_lib.kivi_paged_pool_bytes(ctypes.byref(self.shape), P, num_pages,
+                                         *[ctypes.byref(x) for x in sizes]),
+              "kivi_paged_pool_bytes")
+        B, H, D, G, R = batch, kv_heads, head_dim, group, residual
+        E = 32 // bits
+        dev = torch.device(device)
+        mdt = torch.float16 if meta_half else torch.float32
+        self.page_tokens, self.num_pages, self.max_pages = P, num_pages, max_pages
+        self.k_codes = torch.zeros((num_pages, H, P, D // E), dtype=torch.int32, device=dev)
+        self.k_scale = torch.zeros((num_pages, H, P // G, D), dtype=mdt, device=dev)
+        self.k_zero = torch.zeros((num_pages, H, P // G, D), dtype=mdt, device=dev)
+        self.v_codes = torch.zeros((num_pages, H, P // 64, D, 64 // E), dtype=torch.int32,
+                                   device=dev)
+        self.v_scale = torch.zeros((num_pages, H, P, D // G), dtype=mdt, device=dev)
+        self.v_zero = torch.zeros((num_pages, H, P, D // G), dtype=mdt, device=dev)
+        self.k_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
+        self.v_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
+        assert self.k_codes.nbytes == sizes[0].value and self.k_scale.nbytes == sizes[1].value
+        assert self.v_codes.nbytes == sizes[2].value and self.v_scale.nbytes == sizes[3].value
+        if table is None:
+            table = np.arange(B * max_pages, dtype=np.int32).reshape(B, max_pages)
+        self.table_host = np.ascontiguousarray(table, np.int32).reshape(B, max_pages)
+        self.table = torch.from_numpy(self.table_host.copy()).to(dev)
+        self.tq_arr = np.zeros(batch, np.int32)
+        self.tr_arr = np.zeros(batch, np.int32)
+        self.pc = kivi_paged_cache(self.shape, P, num_pages, *[t.data_ptr() for t in (
+            self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
+            self.k_res, self.v_res, self.table)], _i32p(self.tq_arr), _i32p(self.tr_arr))
+        self.workspace = None
+
+    def prefill(self, k, v, ntok, tq) -> None:
+        assert k.dtype == torch.float16 and k.is_contiguous() and v.is_contiguous()
+        n = np.ascontiguousarray(ntok, np.int32)
+        t = np.ascontiguousarray(tq, np.int32)
+        check(_lib.kivi_paged_prefill(ctypes.byref(self.pc), k.data_ptr(), v.data_ptr(),
+                                      k.shape[2], _i32p(n), _i32p(t), _stream()),
+              "kivi_paged_prefill")
+
+    def append(self, k_new, v_new) -> None:
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        check(_lib.kivi_paged_append(ctypes.byref(self.pc), k_new.data_ptr(), v_new.data_ptr(),
+                                     _stream()), "kivi_paged_append")
+
+    def decode(self, q, softmax_scale, out=None, num_splits=0):
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_paged_decode_attn(ctypes.byref(self.pc), q.data_ptr(),
+                                          float(softmax_scale), out.data_ptr(), _ptr(ws), nb,
+                                          num_splits, _stream()), "kivi_paged_decode_attn")
+        return out
+
+    def append_decode(self, k_new, v_new, q, softmax_scale, out=None, num_splits=0):
+        assert k_new.is_contiguous() and v_new.is_contiguous()
+        assert q.dtype == torch.float16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty_like(q)
+        ws = self.workspace_for(num_splits)
+        nb = 0 if ws is None else ws.numel()
+        check(_lib.kivi_paged_append_decode_attn(
+            ctypes.byref(self.pc), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(),
+            float(softmax_scale), out.data_ptr(), _ptr(ws), nb, num_splits, _stream()),
+            "kivi_paged_append_decode_attn")
+        return out
+
+    def auto_splits(self) -> int:
+        s = _lib.kivi_paged_decode_auto_splits(ctypes.byref(self.pc))
+        if s < 0:
+            check(-s, "kivi_paged_decode_auto_splits")
+        return s
+
+    def gather(self, name: str) -> np.ndarray:
+        """Host copy of a quantized-store buffer in the contiguous layout
+        ([batch][H][capacity-derived axis]...), assembled from the pages named
+        by the table (logical pages with an entry outside the pool are zero)."""
+        pool = getattr(self, name).cpu().numpy()
+        B, mp = self.table_host.shape
+        parts = []
+        for b in range(B):
+            row = []
+            for j in range(mp):
+                pg = int(self.table_host[b, j])
+                row.append(pool[pg] if 0 <= pg < self.num_pages else np.zeros_like(pool[0]))
+            parts.append(np.concatenate(row, axis=1))
+        return np.stack(parts)

@@ -54,7 +54,7 @@ __device__ float block_reduce(float v, bool is_max, float* scratch) {
 template <int RR>
 constexpr int sub_tokens() { return RR <= 2 ? 1024 : 2048 / RR; }
 
-template <int RR, bool RAG>
+template <int RR, bool RAG, bool PG>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   constexpr int kSub = sub_tokens<RR>();
@@ -78,14 +78,20 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   const uint32_t mask = (1u << bits) - 1u;
 
   const size_t kvp = (size_t)u;                   // plane index
-  const uint32_t* kc = a.k_codes + kvp * (size_t)a.cap * W;
   const int mh = a.mh;
   const size_t mb = mh ? 2 : 4;   // metadata element bytes
-  const char* ks = static_cast<const char*>(a.k_scale) + kvp * (size_t)(a.cap / G) * D * mb;
-  const char* kz = static_cast<const char*>(a.k_zero) + kvp * (size_t)(a.cap / G) * D * mb;
-  const uint32_t* vc = a.v_codes + kvp * (size_t)a.cap * D / E;
-  const char* vs = static_cast<const char*>(a.v_scale) + kvp * (size_t)a.cap * NG * mb;
-  const char* vz = static_cast<const char*>(a.v_zero) + kvp * (size_t)a.cap * NG * mb;
+  // quantized token t: its slice plane (the contiguous plane, or the page
+  // slice named by the block table) and its token inside that slice
+  const size_t scap = PG ? (size_t)a.pages.page_tokens : (size_t)a.cap;
+  auto slot = [&](int t, size_t& pl, int& lt) -> bool {
+    if constexpr (PG) {
+      return page_slot(a.pages, b, h, a.H, t, pl, lt);
+    } else {
+      pl = kvp;
+      lt = t;
+      return true;
+    }
+  };
   const uint16_t* kr = a.k_res + kvp * (size_t)a.R * D;
   const uint16_t* vr = a.v_res + kvp * (size_t)a.R * D;
   const size_t qrow0 = (size_t)b * a.H * r + (size_t)h * r;   // first query row
@@ -111,21 +117,24 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
       float acc[RR];
 #pragma unroll
       for (int i = 0; i < RR; i++) acc[i] = 0.f;
-      if (t < tq) {
-        const uint32_t* row = kc + (size_t)t * W;
-        const size_t m0 = (size_t)(t / G) * D;
+      size_t pl;
+      int lt;
+      if (t < tq && slot(t, pl, lt)) {
+        const uint32_t* row = a.k_codes + (pl * scap + lt) * W;
+        const size_t m0 = (pl * (scap / G) + lt / G) * D;
         for (int w = 0; w < W; w++) {
           const uint32_t word = row[w];
           for (int e = 0; e < E; e++) {
             const int dd = w * E + e;
-            const float kh = (float)((word >> (bits * e)) & mask) * meta_at(ks, m0 + dd, mh) +
-                             meta_at(kz, m0 + dd, mh);
+            const float kh = (float)((word >> (bits * e)) & mask) *
+                                 meta_at(a.k_scale, m0 + dd, mh) +
+                             meta_at(a.k_zero, m0 + dd, mh);
 #pragma unroll
             for (int i = 0; i < RR; i++)
               if (i < r) acc[i] += sq[i * D + dd] * kh;
           }
         }
-      } else {
+      } else if (t >= tq) {
         const uint16_t* row = kr + (size_t)(t - tq) * D;
         for (int dd = 0; dd < D; dd++) {
           const float kh = h2f(row[dd]);
@@ -169,12 +178,17 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
       for (int i = 0; i < RR; i++)
         if (i < r) o[i] *= stat[2 * RR + i];
       for (int t = c0 + sub; t < c1; t += nsub) {
-        float vh;
+        float vh = 0.f;
+        size_t pl;
+        int lt;
         if (t < tq) {
-          const uint32_t word = vc[((size_t)(t / 64) * D + d) * WPC + (t % 64) / E];
-          const int j = d / G;
-          vh = (float)((word >> (bits * ((t % 64) % E))) & mask) *
-                   meta_at(vs, (size_t)t * NG + j, mh) + meta_at(vz, (size_t)t * NG + j, mh);
+          if (slot(t, pl, lt)) {
+            const uint32_t word =
+                a.v_codes[pl * scap * D / E + ((size_t)(lt / 64) * D + d) * WPC + (lt % 64) / E];
+            const size_t mi = (pl * scap + lt) * NG + d / G;
+            vh = (float)((word >> (bits * ((lt % 64) % E))) & mask) * meta_at(a.v_scale, mi, mh) +
+                 meta_at(a.v_zero, mi, mh);
+          }
         } else {
           vh = h2f(vr[(size_t)(t - tq) * D + d]);
         }
@@ -236,31 +250,35 @@ size_t decode_generic_lds_bytes(int r, int D) {
   return sizeof(float) * ((size_t)r * D + (size_t)r * sub + (size_t)rr * kThreads + 8 + 3 * rr);
 }
 
-template <bool RAG>
+template <bool RAG, bool PG>
 static hipError_t launch_generic(const DecodeArgs& a, const LensT<RAG>& lens, hipStream_t st) {
   const int L = a.tq + a.tr;
   const int chunk = (L + a.S - 1) / a.S;   // (per sequence in the kernel when ragged)
   dim3 grid(a.S, a.B * a.H);
   const size_t lds = decode_generic_lds_bytes(a.r, a.D);
   if (a.r == 1)
-    decode_generic_kernel<1, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
+    decode_generic_kernel<1, RAG, PG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r == 2)
-    decode_generic_kernel<2, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
+    decode_generic_kernel<2, RAG, PG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r <= 4)
-    decode_generic_kernel<4, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
+    decode_generic_kernel<4, RAG, PG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else if (a.r <= 8)
-    decode_generic_kernel<8, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
+    decode_generic_kernel<8, RAG, PG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   else
-    decode_generic_kernel<16, RAG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
+    decode_generic_kernel<16, RAG, PG><<<grid, kThreads, lds, st>>>(a, chunk, lens);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st) {
-  return launch_generic<false>(a, NoLens{}, st);
+  return launch_generic<false, false>(a, NoLens{}, st);
 }
 
 hipError_t launch_decode_generic_ragged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st) {
-  return launch_generic<true>(a, lens, st);
+  return launch_generic<true, false>(a, lens, st);
+}
+
+hipError_t launch_decode_generic_paged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st) {
+  return launch_generic<true, true>(a, lens, st);
 }
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {

@@ -56,7 +56,7 @@ template <int BITS, int R, int NW>
 int occupancy_of() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false>),
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false, false>),
           NW * 64, 0) !=
       hipSuccess)
     return 1;
@@ -103,7 +103,8 @@ int decode_mfma_block_waves(int r, int nw) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
   const NoLens none;
-  return a.bits == 2 ? launch_bits<2, false>(a, none, nw, st) : launch_bits<4, false>(a, none, nw, st);
+  return a.bits == 2 ? launch_bits<2, false, false>(a, none, nw, st)
+                     : launch_bits<4, false, false>(a, none, nw, st);
 }
 
 }  // namespace kivi

@@ -254,10 +254,11 @@ constexpr int prefetch_depth() {
   return R >= 8 ? 2 : 1;
 }
 
-template <int BITS, int R, int NW, bool MH, bool RAG>
+template <int BITS, int R, int NW, bool MH, bool RAG, bool PG>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
 decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
+  static_assert(!PG || RAG, "paged launches carry per-sequence lengths");
   using C = Cfg<BITS, R>;
   constexpr int ROWS = C::ROWS, CH = C::CH;
   constexpr int E = 32 / BITS;
@@ -269,7 +270,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const int n16 = lane & 15, kg = lane >> 4;
   const int S = a.S, H = a.H;
   const int u = seq_plane<RAG>(lens, blockIdx.x / S, H), split = blockIdx.x % S;
-  const int b = u / H;
+  const int b = u / H, hh = u % H;
   const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
 
   char* zero = smem;
@@ -349,6 +350,21 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // value codes; 4-bit x0..x7), key scale / zero of key group kgrp, channels
   // cq..cq+3, value scale / zero of the token lane
   const uint32_t l16 = (uint32_t)lane * 16;
+  // Paged store: the page slice of a tile (a scalar table lookup at a
+  // wave-uniform index) and the tile's offset inside the slice.  Absent tiles
+  // look up an entry that exists in the sequence's table row (tile t_begin,
+  // clamped to the sequence's last tile, or tile 0 when it has none) and
+  // load nothing.
+  const int P = a.pages.page_tokens;
+  const int t_last = nT > 0 ? nT - 1 : 0;
+  auto page_tile = [&](int tile, size_t& sp, uint32_t& lt64) __attribute__((always_inline)) {
+    const int tu =
+        __builtin_amdgcn_readfirstlane(tile < t_end ? tile : (t_begin < t_last ? t_begin : t_last));
+    int tok;
+    const bool ok = page_slot(a.pages, b, hh, H, tu * 64, sp, tok);
+    lt64 = (uint32_t)(tok / 64);
+    return ok && tile < t_end;
+  };
   // codes / metadata of tile `tile` of this wave, or zeros (no memory access)
   // when it is past the wave's last tile.  Codes are reloaded as soon as they
   // are staged, metadata once the tile's compute has consumed them, so that
@@ -356,38 +372,59 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // copy waits for its load).
   auto load_codes = [&](int tile, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& x4,
                         uint4& x5, uint4& x6, uint4& x7) __attribute__((always_inline)) {
-    const uint32_t co = tile < t_end ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
+    uint32_t co = tile < t_end ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
+    rsrc_t rkc = r_kc, rvc = r_vc;
+    if constexpr (PG) {
+      size_t sp;
+      uint32_t lt;
+      const bool ok = page_tile(tile, sp, lt);
+      rkc = make_rsrc(a.k_codes + sp * P * W, (uint32_t)(P * W * 4));
+      rvc = make_rsrc(a.v_codes + sp * P * (kD / E), (uint32_t)(P * (kD / E) * 4));
+      co = ok ? lt * C::KC_BYTES + l16 : kOut;
+    }
     if constexpr (BITS == 2) {
-      x0 = ld16(r_kc, co);
-      x1 = ld16(r_kc, co + 1024);
-      x2 = ld16(r_vc, co);
-      x3 = ld16(r_vc, co + 1024);
+      x0 = ld16(rkc, co);
+      x1 = ld16(rkc, co + 1024);
+      x2 = ld16(rvc, co);
+      x3 = ld16(rvc, co + 1024);
     } else {
-      x0 = ld16(r_kc, co);
-      x1 = ld16(r_kc, co + 1024);
-      x2 = ld16(r_kc, co + 2048);
-      x3 = ld16(r_kc, co + 3072);
-      x4 = ld16(r_vc, co);
-      x5 = ld16(r_vc, co + 1024);
-      x6 = ld16(r_vc, co + 2048);
-      x7 = ld16(r_vc, co + 3072);
+      x0 = ld16(rkc, co);
+      x1 = ld16(rkc, co + 1024);
+      x2 = ld16(rkc, co + 2048);
+      x3 = ld16(rkc, co + 3072);
+      x4 = ld16(rvc, co);
+      x5 = ld16(rvc, co + 1024);
+      x6 = ld16(rvc, co + 2048);
+      x7 = ld16(rvc, co + 3072);
     }
   };
   auto load_meta = [&](int tile, MetaT& ks, MetaT& kz, MetaT& vs, MetaT& vz)
       __attribute__((always_inline)) {
     // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 256 values
     // each, 4 per lane (converted to binary32 when the tile is computed)
-    const uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
+    uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
+    rsrc_t rks = r_ks, rkz = r_kz, rvs = r_vs, rvz = r_vz;
+    if constexpr (PG) {
+      size_t sp;
+      uint32_t lt;
+      const bool ok = page_tile(tile, sp, lt);
+      const size_t kb = (size_t)(P / kG) * kD * MB, vb = (size_t)P * kNG * MB;  // slice bytes
+      rks = make_rsrc(static_cast<const char*>(a.k_scale) + sp * kb, (uint32_t)kb);
+      rkz = make_rsrc(static_cast<const char*>(a.k_zero) + sp * kb, (uint32_t)kb);
+      rvs = make_rsrc(static_cast<const char*>(a.v_scale) + sp * vb, (uint32_t)vb);
+      rvz = make_rsrc(static_cast<const char*>(a.v_zero) + sp * vb, (uint32_t)vb);
+      mo = ok ? lt * (256 * MB) + lane * (4 * MB) : kOut;
+    }
     if constexpr (MH) {
-      ks = ld8s(r_ks, mo);
-      kz = ld8s(r_kz, mo);
-      vs = ld8s(r_vs, mo);
-      vz = ld8s(r_vz, mo);
+      ks = ld8s(rks, mo);
+      kz = ld8s(rkz, mo);
+      vs = ld8s(rvs, mo);
+      vz = ld8s(rvz, mo);
     } else {
-      ks = ld16f(r_ks, mo);
-      kz = ld16f(r_kz, mo);
-      vs = ld16f(r_vs, mo);
-      vz = ld16f(r_vz, mo);
+      ks = ld16f(rks, mo);
+      kz = ld16f(rkz, mo);
+      vs = ld16f(rvs, mo);
+      vz = ld16f(rvz, mo);
     }
   };
   auto stage = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
@@ -897,29 +934,29 @@ constexpr int block_waves(int nw) {
   return (R >= 8 || nw < 8) ? 4 : 8;
 }
 
-template <int BITS, int R, bool MH, bool RAG>
+template <int BITS, int R, bool MH, bool RAG, bool PG>
 hipError_t launch_m(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
   if (block_waves<R>(nw) == 8)
-    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG>
+    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG, PG>
         <<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a, lens);
   else
-    decode_mfma_kernel<BITS, R, 4, MH, RAG><<<grid, 4 * 64, 0, st>>>(a, lens);
+    decode_mfma_kernel<BITS, R, 4, MH, RAG, PG><<<grid, 4 * 64, 0, st>>>(a, lens);
   return hipGetLastError();
 }
-template <int BITS, int R, bool RAG>
+template <int BITS, int R, bool RAG, bool PG>
 hipError_t launch_r(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
-  return a.mh ? launch_m<BITS, R, true, RAG>(a, lens, nw, st)
-              : launch_m<BITS, R, false, RAG>(a, lens, nw, st);
+  return a.mh ? launch_m<BITS, R, true, RAG, PG>(a, lens, nw, st)
+              : launch_m<BITS, R, false, RAG, PG>(a, lens, nw, st);
 }
 
-template <int BITS, bool RAG>
+template <int BITS, bool RAG, bool PG>
 hipError_t launch_bits(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   switch (a.r) {
-    case 1: return launch_r<BITS, 1, RAG>(a, lens, nw, st);
-    case 2: return launch_r<BITS, 2, RAG>(a, lens, nw, st);
-    case 4: return launch_r<BITS, 4, RAG>(a, lens, nw, st);
-    default: return launch_r<BITS, 8, RAG>(a, lens, nw, st);
+    case 1: return launch_r<BITS, 1, RAG, PG>(a, lens, nw, st);
+    case 2: return launch_r<BITS, 2, RAG, PG>(a, lens, nw, st);
+    case 4: return launch_r<BITS, 4, RAG, PG>(a, lens, nw, st);
+    default: return launch_r<BITS, 8, RAG, PG>(a, lens, nw, st);
   }
 }
 

@@ -7,7 +7,8 @@ namespace kivi {
 
 hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, int nw,
                                      hipStream_t st) {
-  return a.bits == 2 ? launch_bits<2, true>(a, lens, nw, st) : launch_bits<4, true>(a, lens, nw, st);
+  return a.bits == 2 ? launch_bits<2, true, false>(a, lens, nw, st)
+                     : launch_bits<4, true, false>(a, lens, nw, st);
 }
 
 }  // namespace kivi

@@ -131,29 +131,96 @@ size_t ws_bytes(const kivi_shape& s, int S) {
   return rows * (size_t)S * (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
-// ---- ragged batches -------------------------------------------------------
+// ---- ragged batches and the paged store -------------------------------------
+// Both carry per-sequence host lengths; the paged store also a page map.  The
+// calls below work on this common view.
 
-int check_ragged(const kivi_ragged_cache* c) {
-  if (!c) return KIVI_EINVAL;
-  int rc = check_shape(&c->shape);
-  if (rc) return rc;
-  const void* ptrs[] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
-                        c->v_scale, c->v_zero,  c->k_res,  c->v_res};
+struct Rg {
+  const kivi_shape* s;
+  uint32_t* k_codes;
+  void* k_scale;
+  void* k_zero;
+  uint32_t* v_codes;
+  void* v_scale;
+  void* v_zero;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  int32_t* tq;
+  int32_t* tr;
+  bool paged;
+  kivi::PageMap pm;   // paged: pools of pm.num_pages pages, device table [batch][max_pages]
+};
+
+Rg view(const kivi_ragged_cache* c) {
+  return Rg{&c->shape, c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
+            c->k_res,  c->v_res,   c->tq,      c->tr,      false,      kivi::PageMap{nullptr, 0, 0, 0, 0}};
+}
+Rg view(const kivi_paged_cache* c) {
+  const int P = c->page_tokens > 0 ? c->page_tokens : 1;
+  int shift = 0;
+  while ((1 << shift) < P) shift++;
+  return Rg{&c->shape, c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
+            c->k_res,  c->v_res,   c->tq,      c->tr,      true,
+            kivi::PageMap{c->block_table, c->page_tokens, c->shape.capacity / P, c->num_pages,
+                          shift}};
+}
+
+// buffers present and aligned, length arrays present (shape already checked)
+int check_buffers(const Rg& g) {
+  const void* ptrs[] = {g.k_codes, g.k_scale, g.k_zero, g.v_codes,
+                        g.v_scale, g.v_zero,  g.k_res,  g.v_res};
   for (const void* p : ptrs)
     if (!p) return KIVI_EINVAL;
-  if (!c->tq || !c->tr) return KIVI_EINVAL;
+  if (!g.tq || !g.tr) return KIVI_EINVAL;
+  if (g.paged && !g.pm.table) return KIVI_EINVAL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return KIVI_EALIGN;
-  const kivi_shape& s = c->shape;
+  if (g.paged && (reinterpret_cast<uintptr_t>(g.pm.table) & 3u)) return KIVI_EALIGN;
+  return KIVI_OK;
+}
+
+int check_lengths(const Rg& g) {
+  const kivi_shape& s = *g.s;
   for (int b = 0; b < s.batch; b++) {
-    const int tq = c->tq[b], tr = c->tr[b];
+    const int tq = g.tq[b], tr = g.tr[b];
     if (tq < 0 || tq % s.group != 0 || tr < 0 || tr > s.residual) return KIVI_ESHAPE;
     if (tq > s.capacity) return KIVI_ECAPACITY;
   }
   return KIVI_OK;
 }
 
-// per-(b, h) plane extents of the cache buffers
+// page size and pool: P a power of two, at least 64 and the group, capacity
+// a multiple of P, at least one page, page slices addressable with 32 bits
+int check_pages(const kivi_paged_cache* c) {
+  const kivi_shape& s = c->shape;
+  const int P = c->page_tokens;
+  if (P < 64 || (P & (P - 1)) != 0 || P % s.group != 0) return KIVI_ESHAPE;
+  if (s.capacity % P != 0) return KIVI_ESHAPE;
+  if (c->num_pages < 1) return KIVI_ESHAPE;
+  if ((int64_t)P * s.head_dim > (int64_t)1 << 31) return KIVI_ESHAPE;
+  return KIVI_OK;
+}
+
+int check_ragged(const kivi_ragged_cache* c) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  const Rg g = view(c);
+  if ((rc = check_buffers(g))) return rc;
+  return check_lengths(g);
+}
+
+int check_paged(const kivi_paged_cache* c) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  if ((rc = check_pages(c))) return rc;
+  const Rg g = view(c);
+  if ((rc = check_buffers(g))) return rc;
+  return check_lengths(g);
+}
+
+// per-(b, h) plane extents of the contiguous cache buffers
 struct PlaneSizes {
   size_t code_words, kmeta_bytes, vmeta_bytes, res_elems;
 };
@@ -186,34 +253,49 @@ struct ListBatcher {
 template <class F>
 ListBatcher<F> batcher(F f) { return ListBatcher<F>(f); }
 
+// Quantize list items of src ([batch][H][in_stride][D]) into the grouped store
+// (contiguous planes, or the pages of the table), K from k_src, V from v_src.
+int enqueue_quantize_list(const Rg& g, const uint16_t* k_src, const uint16_t* v_src,
+                          int in_stride, int ntok_max, const kivi::SeqList& L, hipStream_t st) {
+  const kivi_shape& s = *g.s;
+  const int H = s.num_kv_heads, D = s.head_dim;
+  hipError_t e;
+  if (g.paged) {
+    e = kivi::launch_quantize_k_paged(k_src, L, g.pm, H, D, s.bits, s.group, in_stride, ntok_max,
+                                      g.k_codes, g.k_scale, g.k_zero, s.meta_half, st);
+    if (e == hipSuccess)
+      e = kivi::launch_quantize_v_paged(v_src, L, g.pm, H, D, s.bits, s.group, in_stride,
+                                        ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
+  } else {
+    e = kivi::launch_quantize_k_list(k_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
+                                     ntok_max, g.k_codes, g.k_scale, g.k_zero, s.meta_half, st);
+    if (e == hipSuccess)
+      e = kivi::launch_quantize_v_list(v_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
+                                       ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
+  }
+  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+}
+
 // Quantizes the full residual of every sequence whose residual holds R tokens
-// into its grouped store at tq[b] (the lazy flush), K then V per launch.
-int enqueue_ragged_flush(const kivi_ragged_cache* c, hipStream_t st) {
-  const kivi_shape& s = c->shape;
+// into its grouped store at tq[b] (the lazy flush).
+int enqueue_ragged_flush(const Rg& g, hipStream_t st) {
+  const kivi_shape& s = *g.s;
   const int R = s.residual;
   auto fl = batcher([&](const kivi::SeqList& L) {
-    hipError_t e = kivi::launch_quantize_k_list(c->k_res, L, s.num_kv_heads, s.head_dim, s.bits,
-                                                s.group, s.capacity, R, R, c->k_codes, c->k_scale,
-                                                c->k_zero, s.meta_half, st);
-    if (e == hipSuccess)
-      e = kivi::launch_quantize_v_list(c->v_res, L, s.num_kv_heads, s.head_dim, s.bits, s.group,
-                                       s.capacity, R, R, c->v_codes, c->v_scale, c->v_zero,
-                                       s.meta_half, st);
-    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+    return enqueue_quantize_list(g, g.k_res, g.v_res, R, R, L, st);
   });
   for (int b = 0; b < s.batch; b++)
-    if (c->tr[b] == R) fl.add(b, R, c->tq[b], 0);
+    if (g.tr[b] == R) fl.add(b, R, g.tq[b], 0);
   return fl.flush();
 }
 
 // Writes token row b of k_new / v_new into residual slot slot[b].
-int enqueue_ragged_token_copy(const kivi_ragged_cache* c, const uint16_t* k_new,
-                              const uint16_t* v_new, const std::vector<int>& slot,
-                              hipStream_t st) {
-  const kivi_shape& s = c->shape;
+int enqueue_ragged_token_copy(const Rg& g, const uint16_t* k_new, const uint16_t* v_new,
+                              const std::vector<int>& slot, hipStream_t st) {
+  const kivi_shape& s = *g.s;
   auto cp = batcher([&](const kivi::SeqList& L) {
-    hipError_t e = kivi::launch_copy_tokens_list(k_new, v_new, 1, c->k_res, c->v_res, s.residual,
-                                                 L, 1, s.num_kv_heads, s.head_dim, st);
+    hipError_t e = kivi::launch_copy_tokens_list(k_new, v_new, 1, g.k_res, g.v_res, s.residual, L,
+                                                 1, s.num_kv_heads, s.head_dim, st);
     return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
   });
   for (int b = 0; b < s.batch; b++) cp.add(b, 0, slot[b], 1);
@@ -226,13 +308,13 @@ struct RaggedPlan {
   std::vector<int> tq, tr;
 };
 
-int plan_ragged_decode(const kivi_ragged_cache* c, std::vector<int> tq, std::vector<int> tr,
-                       const uint16_t* q, uint16_t* out, void* workspace,
-                       size_t workspace_bytes, int32_t num_splits, RaggedPlan* plan) {
+int plan_ragged_decode(const Rg& g, std::vector<int> tq, std::vector<int> tr, const uint16_t* q,
+                       uint16_t* out, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                       RaggedPlan* plan) {
   if (!q || !out) return KIVI_EINVAL;
   if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
   if (num_splits < 0) return KIVI_EINVAL;
-  const kivi_shape& s = c->shape;
+  const kivi_shape& s = *g.s;
   int max_tq = 0, max_tr = 0;
   for (int b = 0; b < s.batch; b++) {
     if (tq[b] + tr[b] < 1) return KIVI_ESHAPE;
@@ -256,26 +338,28 @@ int plan_ragged_decode(const kivi_ragged_cache* c, std::vector<int> tq, std::vec
   return KIVI_OK;
 }
 
-// Decode launches over chunks of at most kMaxSeq sequences: pointers offset to
-// the chunk's planes, rows and workspace, lengths passed by value.
-int enqueue_ragged_decode(const kivi_ragged_cache* c, const RaggedPlan& p, const uint16_t* q,
+// Decode launches over chunks of at most kMaxSeq sequences: query, output,
+// residual and workspace pointers offset to the chunk, and either the
+// contiguous cache planes or the block-table rows too; lengths by value.
+int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
                           float softmax_scale, uint16_t* out, void* workspace,
                           const uint16_t* k_new, const uint16_t* v_new, hipStream_t st) {
-  const kivi_shape& s = c->shape;
+  const kivi_shape& s = *g.s;
   const PlaneSizes ps = plane_sizes(s);
   const int H = s.num_kv_heads, r = s.gqa_ratio, D = s.head_dim, S = p.S;
   for (int c0 = 0; c0 < s.batch; c0 += kivi::kMaxSeq) {
     const int n = std::min(kivi::kMaxSeq, s.batch - c0);
     const size_t pl = (size_t)c0 * H;   // first plane of the chunk
+    const size_t cp = g.paged ? 0 : pl; // first cache plane (pools are shared)
     DecodeArgs a;
-    a.k_codes = c->k_codes + pl * ps.code_words;
-    a.k_scale = static_cast<const char*>(c->k_scale) + pl * ps.kmeta_bytes;
-    a.k_zero = static_cast<const char*>(c->k_zero) + pl * ps.kmeta_bytes;
-    a.v_codes = c->v_codes + pl * ps.code_words;
-    a.v_scale = static_cast<const char*>(c->v_scale) + pl * ps.vmeta_bytes;
-    a.v_zero = static_cast<const char*>(c->v_zero) + pl * ps.vmeta_bytes;
-    a.k_res = c->k_res + pl * ps.res_elems;
-    a.v_res = c->v_res + pl * ps.res_elems;
+    a.k_codes = g.k_codes + cp * ps.code_words;
+    a.k_scale = static_cast<const char*>(g.k_scale) + cp * ps.kmeta_bytes;
+    a.k_zero = static_cast<const char*>(g.k_zero) + cp * ps.kmeta_bytes;
+    a.v_codes = g.v_codes + cp * ps.code_words;
+    a.v_scale = static_cast<const char*>(g.v_scale) + cp * ps.vmeta_bytes;
+    a.v_zero = static_cast<const char*>(g.v_zero) + cp * ps.vmeta_bytes;
+    a.k_res = g.k_res + pl * ps.res_elems;
+    a.v_res = g.v_res + pl * ps.res_elems;
     a.k_new = k_new ? k_new + pl * D : nullptr;
     a.v_new = v_new ? v_new + pl * D : nullptr;
     a.q = q + pl * r * D;
@@ -289,6 +373,8 @@ int enqueue_ragged_decode(const kivi_ragged_cache* c, const RaggedPlan& p, const
     a.G = s.group;
     a.R = s.residual;
     a.cap = s.capacity;
+    a.pages = g.pm;
+    if (g.paged) a.pages.table = g.pm.table + (size_t)c0 * g.pm.max_pages;
     kivi::SeqLens lens;
     int mq = 0, mr = 0;
     for (int i = 0; i < n; i++) {
@@ -307,10 +393,133 @@ int enqueue_ragged_decode(const kivi_ragged_cache* c, const RaggedPlan& p, const
     a.S = S;
     a.mh = s.meta_half;
     a.scale = softmax_scale;
-    hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma_ragged(a, lens, mfma_waves(), st)
-                               : kivi::launch_decode_generic_ragged(a, lens, st);
+    hipError_t e;
+    if (use_mfma(s))
+      e = g.paged ? kivi::launch_decode_mfma_paged(a, lens, mfma_waves(), st)
+                  : kivi::launch_decode_mfma_ragged(a, lens, mfma_waves(), st);
+    else
+      e = g.paged ? kivi::launch_decode_generic_paged(a, lens, st)
+                  : kivi::launch_decode_generic_ragged(a, lens, st);
     if (e != hipSuccess) return KIVI_EHIP;
     if (S > 1 && kivi::launch_combine(a, st) != hipSuccess) return KIVI_EHIP;
+  }
+  return KIVI_OK;
+}
+
+// lengths after appending one token to every sequence; false on overflow
+bool ragged_after_append(const Rg& g, std::vector<int>& tq, std::vector<int>& tr,
+                         std::vector<int>& slot) {
+  const kivi_shape& s = *g.s;
+  tq.resize(s.batch);
+  tr.resize(s.batch);
+  slot.resize(s.batch);
+  for (int b = 0; b < s.batch; b++) {
+    const bool flush = g.tr[b] == s.residual;
+    if (flush && (int64_t)g.tq[b] + s.residual > s.capacity) return false;
+    tq[b] = g.tq[b] + (flush ? s.residual : 0);
+    slot[b] = flush ? 0 : g.tr[b];
+    tr[b] = slot[b] + 1;
+  }
+  return true;
+}
+
+// The call bodies shared by the ragged and the paged entry points (arguments
+// of the cache already validated).
+int do_prefill(const Rg& g, const uint16_t* k, const uint16_t* v, int32_t in_tok_stride,
+               const int32_t* ntok, const int32_t* tq, hipStream_t st) {
+  if (!k || !v || !ntok || !tq) return KIVI_EINVAL;
+  if (!aligned16(k) || !aligned16(v)) return KIVI_EALIGN;
+  const kivi_shape& s = *g.s;
+  if (in_tok_stride < 1) return KIVI_ESHAPE;
+  for (int b = 0; b < s.batch; b++) {
+    if (ntok[b] < 0 || ntok[b] > in_tok_stride || tq[b] < 0 || tq[b] % s.group != 0 ||
+        ntok[b] < tq[b] || ntok[b] - tq[b] > s.residual)
+      return KIVI_ESHAPE;
+    if (tq[b] > s.capacity) return KIVI_ECAPACITY;
+  }
+  int max_tq = 0, max_n = 0;
+  for (int b = 0; b < s.batch; b++) {
+    max_tq = std::max(max_tq, (int)tq[b]);
+    max_n = std::max(max_n, (int)(ntok[b] - tq[b]));
+  }
+  auto qz = batcher([&](const kivi::SeqList& L) {
+    return enqueue_quantize_list(g, k, v, in_tok_stride, max_tq, L, st);
+  });
+  for (int b = 0; b < s.batch; b++)
+    if (tq[b] > 0) qz.add(b, tq[b], 0, 0);
+  int rc = qz.flush();
+  if (rc) return rc;
+  auto cp = batcher([&](const kivi::SeqList& L) {
+    hipError_t e = kivi::launch_copy_tokens_list(k, v, in_tok_stride, g.k_res, g.v_res,
+                                                 s.residual, L, max_n, s.num_kv_heads,
+                                                 s.head_dim, st);
+    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  });
+  for (int b = 0; b < s.batch; b++)
+    if (ntok[b] > tq[b]) cp.add(b, tq[b], 0, ntok[b] - tq[b]);
+  if ((rc = cp.flush())) return rc;
+  for (int b = 0; b < s.batch; b++) {
+    g.tq[b] = tq[b];
+    g.tr[b] = ntok[b] - tq[b];
+  }
+  return KIVI_OK;
+}
+
+int do_append(const Rg& g, const uint16_t* k_new, const uint16_t* v_new, hipStream_t st) {
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  std::vector<int> tq, tr, slot;
+  if (!ragged_after_append(g, tq, tr, slot)) return KIVI_ECAPACITY;
+  int rc = enqueue_ragged_flush(g, st);
+  if (rc) return rc;
+  if ((rc = enqueue_ragged_token_copy(g, k_new, v_new, slot, st))) return rc;
+  for (int b = 0; b < g.s->batch; b++) {
+    g.tq[b] = tq[b];
+    g.tr[b] = tr[b];
+  }
+  return KIVI_OK;
+}
+
+int do_auto_splits(const Rg& g) {
+  const int cus = device_cu_count();
+  if (cus < 0) return cus;
+  int max_tq = 0, max_tr = 0;
+  for (int b = 0; b < g.s->batch; b++) {
+    max_tq = std::max(max_tq, (int)g.tq[b]);
+    max_tr = std::max(max_tr, (int)g.tr[b]);
+  }
+  return auto_splits(*g.s, max_tq, max_tr, cus);
+}
+
+int do_decode(const Rg& g, const uint16_t* q, float softmax_scale, uint16_t* out,
+              void* workspace, size_t workspace_bytes, int32_t num_splits, hipStream_t st) {
+  RaggedPlan p;
+  const int B = g.s->batch;
+  int rc = plan_ragged_decode(g, std::vector<int>(g.tq, g.tq + B), std::vector<int>(g.tr, g.tr + B),
+                              q, out, workspace, workspace_bytes, num_splits, &p);
+  if (rc) return rc;
+  return enqueue_ragged_decode(g, p, q, softmax_scale, out, workspace, nullptr, nullptr, st);
+}
+
+int do_append_decode(const Rg& g, const uint16_t* k_new, const uint16_t* v_new,
+                     const uint16_t* q, float softmax_scale, uint16_t* out, void* workspace,
+                     size_t workspace_bytes, int32_t num_splits, hipStream_t st) {
+  if (!k_new || !v_new) return KIVI_EINVAL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
+  std::vector<int> tq, tr, slot;
+  if (!ragged_after_append(g, tq, tr, slot)) return KIVI_ECAPACITY;
+  RaggedPlan p;
+  int rc = plan_ragged_decode(g, tq, tr, q, out, workspace, workspace_bytes, num_splits, &p);
+  if (rc) return rc;
+  if ((rc = enqueue_ragged_flush(g, st))) return rc;
+  const bool fused = use_mfma(*g.s);
+  if (!fused && (rc = enqueue_ragged_token_copy(g, k_new, v_new, slot, st))) return rc;
+  rc = enqueue_ragged_decode(g, p, q, softmax_scale, out, workspace, fused ? k_new : nullptr,
+                             fused ? v_new : nullptr, st);
+  if (rc) return rc;
+  for (int b = 0; b < g.s->batch; b++) {
+    g.tq[b] = tq[b];
+    g.tr[b] = tr[b];
   }
   return KIVI_OK;
 }
@@ -495,6 +704,7 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->S = S;
   a->mh = s.meta_half;
   a->scale = softmax_scale;
+  a->pages = kivi::PageMap{nullptr, 0, 0, 0, 0};
   return KIVI_OK;
 }
 
@@ -577,102 +787,22 @@ int kivi_ragged_prefill(kivi_ragged_cache* c, const uint16_t* k, const uint16_t*
   if (!c) return KIVI_EINVAL;
   int rc = check_shape(&c->shape);
   if (rc) return rc;
-  const void* ptrs[] = {c->k_codes, c->k_scale, c->k_zero, c->v_codes,
-                        c->v_scale, c->v_zero,  c->k_res,  c->v_res};
-  for (const void* p : ptrs)
-    if (!p) return KIVI_EINVAL;
-  if (!c->tq || !c->tr || !k || !v || !ntok || !tq) return KIVI_EINVAL;
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return KIVI_EALIGN;
-  if (!aligned16(k) || !aligned16(v)) return KIVI_EALIGN;
-  const kivi_shape& s = c->shape;
-  if (in_tok_stride < 1) return KIVI_ESHAPE;
-  for (int b = 0; b < s.batch; b++) {
-    if (ntok[b] < 0 || ntok[b] > in_tok_stride || tq[b] < 0 || tq[b] % s.group != 0 ||
-        ntok[b] < tq[b] || ntok[b] - tq[b] > s.residual)
-      return KIVI_ESHAPE;
-    if (tq[b] > s.capacity) return KIVI_ECAPACITY;
-  }
-  hipStream_t st = (hipStream_t)stream;
-  const int H = s.num_kv_heads, D = s.head_dim;
-  int max_tq = 0, max_n = 0;
-  for (int b = 0; b < s.batch; b++) {
-    max_tq = std::max(max_tq, (int)tq[b]);
-    max_n = std::max(max_n, (int)(ntok[b] - tq[b]));
-  }
-  auto qz = batcher([&](const kivi::SeqList& L) {
-    hipError_t e = kivi::launch_quantize_k_list(k, L, H, D, s.bits, s.group, s.capacity,
-                                                in_tok_stride, max_tq, c->k_codes, c->k_scale,
-                                                c->k_zero, s.meta_half, st);
-    if (e == hipSuccess)
-      e = kivi::launch_quantize_v_list(v, L, H, D, s.bits, s.group, s.capacity, in_tok_stride,
-                                       max_tq, c->v_codes, c->v_scale, c->v_zero, s.meta_half, st);
-    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
-  });
-  for (int b = 0; b < s.batch; b++)
-    if (tq[b] > 0) qz.add(b, tq[b], 0, 0);
-  if ((rc = qz.flush())) return rc;
-  auto cp = batcher([&](const kivi::SeqList& L) {
-    hipError_t e = kivi::launch_copy_tokens_list(k, v, in_tok_stride, c->k_res, c->v_res,
-                                                 s.residual, L, max_n, H, D, st);
-    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
-  });
-  for (int b = 0; b < s.batch; b++)
-    if (ntok[b] > tq[b]) cp.add(b, tq[b], 0, ntok[b] - tq[b]);
-  if ((rc = cp.flush())) return rc;
-  for (int b = 0; b < s.batch; b++) {
-    c->tq[b] = tq[b];
-    c->tr[b] = ntok[b] - tq[b];
-  }
-  return KIVI_OK;
-}
-
-// lengths after appending one token to every sequence; false on overflow
-static bool ragged_after_append(const kivi_ragged_cache* c, std::vector<int>& tq,
-                                std::vector<int>& tr, std::vector<int>& slot) {
-  const kivi_shape& s = c->shape;
-  tq.resize(s.batch);
-  tr.resize(s.batch);
-  slot.resize(s.batch);
-  for (int b = 0; b < s.batch; b++) {
-    const bool flush = c->tr[b] == s.residual;
-    if (flush && (int64_t)c->tq[b] + s.residual > s.capacity) return false;
-    tq[b] = c->tq[b] + (flush ? s.residual : 0);
-    slot[b] = flush ? 0 : c->tr[b];
-    tr[b] = slot[b] + 1;
-  }
-  return true;
+  const Rg g = view(c);
+  if ((rc = check_buffers(g))) return rc;
+  return do_prefill(g, k, v, in_tok_stride, ntok, tq, (hipStream_t)stream);
 }
 
 int kivi_ragged_append(kivi_ragged_cache* c, const uint16_t* k_new, const uint16_t* v_new,
                        void* stream) {
   int rc = check_ragged(c);
   if (rc) return rc;
-  if (!k_new || !v_new) return KIVI_EINVAL;
-  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
-  std::vector<int> tq, tr, slot;
-  if (!ragged_after_append(c, tq, tr, slot)) return KIVI_ECAPACITY;
-  hipStream_t st = (hipStream_t)stream;
-  if ((rc = enqueue_ragged_flush(c, st))) return rc;
-  if ((rc = enqueue_ragged_token_copy(c, k_new, v_new, slot, st))) return rc;
-  for (int b = 0; b < c->shape.batch; b++) {
-    c->tq[b] = tq[b];
-    c->tr[b] = tr[b];
-  }
-  return KIVI_OK;
+  return do_append(view(c), k_new, v_new, (hipStream_t)stream);
 }
 
 int kivi_ragged_decode_auto_splits(const kivi_ragged_cache* c) {
   int rc = check_ragged(c);
   if (rc) return -rc;
-  const int cus = device_cu_count();
-  if (cus < 0) return cus;
-  int max_tq = 0, max_tr = 0;
-  for (int b = 0; b < c->shape.batch; b++) {
-    max_tq = std::max(max_tq, (int)c->tq[b]);
-    max_tr = std::max(max_tr, (int)c->tr[b]);
-  }
-  return auto_splits(c->shape, max_tq, max_tr, cus);
+  return do_auto_splits(view(c));
 }
 
 int kivi_ragged_decode_attn(const kivi_ragged_cache* c, const uint16_t* q, float softmax_scale,
@@ -680,13 +810,8 @@ int kivi_ragged_decode_attn(const kivi_ragged_cache* c, const uint16_t* q, float
                             int32_t num_splits, void* stream) {
   int rc = check_ragged(c);
   if (rc) return rc;
-  RaggedPlan p;
-  rc = plan_ragged_decode(c, std::vector<int>(c->tq, c->tq + c->shape.batch),
-                          std::vector<int>(c->tr, c->tr + c->shape.batch), q, out, workspace,
-                          workspace_bytes, num_splits, &p);
-  if (rc) return rc;
-  return enqueue_ragged_decode(c, p, q, softmax_scale, out, workspace, nullptr, nullptr,
-                               (hipStream_t)stream);
+  return do_decode(view(c), q, softmax_scale, out, workspace, workspace_bytes, num_splits,
+                   (hipStream_t)stream);
 }
 
 int kivi_ragged_append_decode_attn(kivi_ragged_cache* c, const uint16_t* k_new,
@@ -695,25 +820,72 @@ int kivi_ragged_append_decode_attn(kivi_ragged_cache* c, const uint16_t* k_new,
                                    int32_t num_splits, void* stream) {
   int rc = check_ragged(c);
   if (rc) return rc;
-  if (!k_new || !v_new) return KIVI_EINVAL;
-  if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
-  std::vector<int> tq, tr, slot;
-  if (!ragged_after_append(c, tq, tr, slot)) return KIVI_ECAPACITY;
-  RaggedPlan p;
-  rc = plan_ragged_decode(c, tq, tr, q, out, workspace, workspace_bytes, num_splits, &p);
+  return do_append_decode(view(c), k_new, v_new, q, softmax_scale, out, workspace,
+                          workspace_bytes, num_splits, (hipStream_t)stream);
+}
+
+// ---- paged store -------------------------------------------------------------
+
+int kivi_paged_pool_bytes(const kivi_shape* s, int32_t page_tokens, int32_t num_pages,
+                          size_t* k_codes, size_t* k_meta, size_t* v_codes, size_t* v_meta) {
+  int rc = check_shape(s);
   if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  if ((rc = enqueue_ragged_flush(c, st))) return rc;
-  const bool fused = use_mfma(c->shape);
-  if (!fused && (rc = enqueue_ragged_token_copy(c, k_new, v_new, slot, st))) return rc;
-  rc = enqueue_ragged_decode(c, p, q, softmax_scale, out, workspace, fused ? k_new : nullptr,
-                             fused ? v_new : nullptr, st);
-  if (rc) return rc;
-  for (int b = 0; b < c->shape.batch; b++) {
-    c->tq[b] = tq[b];
-    c->tr[b] = tr[b];
-  }
+  kivi_paged_cache c{};
+  c.shape = *s;
+  c.page_tokens = page_tokens;
+  c.num_pages = num_pages;
+  if ((rc = check_pages(&c))) return rc;
+  const size_t slices = (size_t)num_pages * s->num_kv_heads;
+  const size_t P = page_tokens, D = s->head_dim, G = s->group, mb = s->meta_half ? 2 : 4;
+  if (k_codes) *k_codes = slices * P * D * s->bits / 8;
+  if (v_codes) *v_codes = slices * P * D * s->bits / 8;
+  if (k_meta) *k_meta = slices * (P / G) * D * mb;
+  if (v_meta) *v_meta = slices * P * (D / G) * mb;
   return KIVI_OK;
+}
+
+int kivi_paged_prefill(kivi_paged_cache* c, const uint16_t* k, const uint16_t* v,
+                       int32_t in_tok_stride, const int32_t* ntok, const int32_t* tq,
+                       void* stream) {
+  if (!c) return KIVI_EINVAL;
+  int rc = check_shape(&c->shape);
+  if (rc) return rc;
+  if ((rc = check_pages(c))) return rc;
+  const Rg g = view(c);
+  if ((rc = check_buffers(g))) return rc;
+  return do_prefill(g, k, v, in_tok_stride, ntok, tq, (hipStream_t)stream);
+}
+
+int kivi_paged_append(kivi_paged_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                      void* stream) {
+  int rc = check_paged(c);
+  if (rc) return rc;
+  return do_append(view(c), k_new, v_new, (hipStream_t)stream);
+}
+
+int kivi_paged_decode_auto_splits(const kivi_paged_cache* c) {
+  int rc = check_paged(c);
+  if (rc) return -rc;
+  return do_auto_splits(view(c));
+}
+
+int kivi_paged_decode_attn(const kivi_paged_cache* c, const uint16_t* q, float softmax_scale,
+                           uint16_t* out, void* workspace, size_t workspace_bytes,
+                           int32_t num_splits, void* stream) {
+  int rc = check_paged(c);
+  if (rc) return rc;
+  return do_decode(view(c), q, softmax_scale, out, workspace, workspace_bytes, num_splits,
+                   (hipStream_t)stream);
+}
+
+int kivi_paged_append_decode_attn(kivi_paged_cache* c, const uint16_t* k_new,
+                                  const uint16_t* v_new, const uint16_t* q, float softmax_scale,
+                                  uint16_t* out, void* workspace, size_t workspace_bytes,
+                                  int32_t num_splits, void* stream) {
+  int rc = check_paged(c);
+  if (rc) return rc;
+  return do_append_decode(view(c), k_new, v_new, q, softmax_scale, out, workspace,
+                          workspace_bytes, num_splits, (hipStream_t)stream);
 }
 
 }  // extern "C"

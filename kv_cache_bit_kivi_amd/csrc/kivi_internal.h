@@ -36,6 +36,32 @@ struct SeqList {
   int c[kMaxSeq];
 };
 
+// Paged quantized store: the quantized tokens of sequence b, head h live in
+// pages of `page_tokens` tokens drawn from a pool of `num_pages` pages; page
+// p holds every head, and its (p, h) slice has the layout of a contiguous
+// plane of capacity page_tokens.  Logical token t of sequence b is token
+// t % page_tokens of page table[b * max_pages + t / page_tokens].  Entries
+// outside [0, num_pages) read as zeros and are never written.
+struct PageMap {
+  const int* table;   // device [batch][max_pages]
+  int page_tokens, max_pages, num_pages;
+  int page_shift;     // log2(page_tokens): page sizes are powers of two
+};
+
+// (slice plane, token inside it) of logical token t of (sequence b, head h):
+// the contiguous plane b*H + h itself, or the page slice holding t.  Returns
+// false for a page outside the pool.  The table is read through the constant
+// address space so that a wave-uniform lookup is a scalar load.
+__device__ __forceinline__ bool page_slot(const PageMap& pm, int b, int h, int H, int t,
+                                          size_t& plane, int& tok) {
+  const __attribute__((address_space(4))) int* tbl =
+      (const __attribute__((address_space(4))) int*)pm.table;
+  const int pg = tbl[(size_t)b * pm.max_pages + (t >> pm.page_shift)];
+  plane = (size_t)pg * H + h;
+  tok = t & (pm.page_tokens - 1);
+  return pg >= 0 && pg < pm.num_pages;
+}
+
 // Device pointers and lengths of one decode call.
 struct DecodeArgs {
   const uint32_t* k_codes;
@@ -56,6 +82,7 @@ struct DecodeArgs {
   int B, H, r, D, bits, G, R, cap, tq, tr, S;
   int mh;             // metadata stored as binary16 (1) or binary32 (0)
   float scale;
+  PageMap pages;      // paged launches only (table null otherwise)
 };
 
 // Kernel parameter of the decode kernels: nothing (uniform lengths, taken
@@ -106,12 +133,27 @@ hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H,
 hipError_t launch_copy_tokens_list(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
                                    uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
                                    const SeqList& list, int n_max, int H, int D, hipStream_t st);
+// The same quantize lists writing into a paged store: destination token
+// b[i] + j of sequence seq[i] goes to its page slice (pm.page_tokens is the
+// slice capacity, `cap` unused).
+hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
+                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
+                                   uint32_t* codes, void* scale, void* zero, int mh,
+                                   hipStream_t st);
+hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const PageMap& pm,
+                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
+                                   uint32_t* codes, void* scale, void* zero, int mh,
+                                   hipStream_t st);
 
 // Generic decode kernel (any supported shape) + split combine.  The ragged
 // variants take the launch's per-sequence lengths (a.tq / a.tr unused) and
 // need every sequence to hold at least one token.
 hipError_t launch_decode_generic(const DecodeArgs& a, hipStream_t st);
 hipError_t launch_decode_generic_ragged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st);
+// paged store (a.pages; per-sequence lengths as in the ragged launch; the
+// cache pointers are the pools, the sequence index b is the launch's
+// sequence b0 + b with b0 = a.pages' row offset already applied to table)
+hipError_t launch_decode_generic_paged(const DecodeArgs& a, const SeqLens& lens, hipStream_t st);
 size_t decode_generic_lds_bytes(int r, int D);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
 
@@ -122,6 +164,8 @@ bool decode_mfma_supported(int D, int G, int r);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st);
 hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, int nw,
                                      hipStream_t st);
+hipError_t launch_decode_mfma_paged(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                    hipStream_t st);
 int decode_mfma_block_waves(int r, int nw);
 // resident blocks per compute unit of that kernel variant (occupancy query)
 int decode_mfma_blocks_per_cu(int bits, int r, int nw);

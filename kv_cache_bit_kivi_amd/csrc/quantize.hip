@@ -72,30 +72,41 @@ __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
 }
 
 // One block per (group of G source tokens, b*H + h), or per (group, item*H +
-// h) over a sequence list (blocks past the item's token count exit).
-template <int BITS, bool MH, bool LIST>
+// h) over a sequence list (blocks past the item's token count exit).  PG: the
+// destination is the page slice the block table names for the group's
+// tokens (a group never straddles a page; a page outside the pool is skipped).
+template <int BITS, bool MH, bool LIST, bool PG>
 __global__ void __launch_bounds__(256)
 quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
                   int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero, int H, ListT<LIST> list) {
+                  void* __restrict__ zero, int H, ListT<LIST> list, PageMap pm) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
   float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
   float* s_zr = s_sc + D;                                    // [D]
   const int g = blockIdx.x;
   size_t bh = blockIdx.y;
+  int seq = 0;
   if constexpr (LIST) {
     const int item = blockIdx.y / H;
     if (g * G >= list.a[item]) return;   // the whole block: uniform
-    bh = (size_t)list.seq[item] * H + blockIdx.y % H;
+    seq = list.seq[item];
+    bh = (size_t)seq * H + blockIdx.y % H;
     dst_off = list.b[item];
+  }
+  // destination: tokens [otok, otok + G) of plane ob, a plane of ocap tokens
+  size_t ob = bh;
+  int otok = dst_off + g * G, ocap = cap;
+  if constexpr (PG) {
+    if (!page_slot(pm, seq, (int)(bh % H), H, otok, ob, otok)) return;   // uniform
+    ocap = pm.page_tokens;
   }
   const uint4* src = reinterpret_cast<const uint4*>(k + (bh * in_stride + (size_t)g * G) * D);
   for (int i = threadIdx.x; i < G * D / 8; i += blockDim.x)
     copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
   __syncthreads();
 
-  const size_t gg = (size_t)(dst_off / G + g);
+  const size_t gg = (size_t)(otok / G);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
     float mn = h2f(tile[d]), mx = mn;
     for (int i = 1; i < G; i++) {
@@ -107,7 +118,7 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
     group_stats<BITS>(mn, mx, &s);
     s_sc[d] = s;
     s_zr[d] = mn;
-    size_t m = (bh * (cap / G) + gg) * D + d;
+    size_t m = (ob * (ocap / G) + gg) * D + d;
     put_meta<MH>(scale, m, s);
     put_meta<MH>(zero, m, mn);
   }
@@ -115,7 +126,7 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
 
   constexpr int E = 32 / BITS;
   const int W = D / E;
-  uint32_t* dst = codes + (bh * cap + dst_off + (size_t)g * G) * W;
+  uint32_t* dst = codes + (ob * ocap + otok) * W;
   for (int it = threadIdx.x; it < G * W; it += blockDim.x) {
     const int i = it / W, w = it % W;
     uint32_t word = 0;
@@ -131,11 +142,11 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
 // One block per (32 source tokens, b*H + h) (or per item, as above).  Value
 // codes are stored in 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E)
 // + (t%64)/E.
-template <int BITS, bool MH, bool LIST>
+template <int BITS, bool MH, bool LIST, bool PG>
 __global__ void __launch_bounds__(256)
 quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_stride,
                   int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero, int H, ListT<LIST> list) {
+                  void* __restrict__ zero, int H, ListT<LIST> list, PageMap pm) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [32][D]
   const int NG = D / G;
@@ -143,18 +154,26 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
   float* s_zr = s_sc + 32 * NG;
   const int blk = blockIdx.x;
   size_t bh = blockIdx.y;
+  int seq = 0;
   if constexpr (LIST) {
     const int item = blockIdx.y / H;
     if (blk * 32 >= list.a[item]) return;   // the whole block: uniform
-    bh = (size_t)list.seq[item] * H + blockIdx.y % H;
+    seq = list.seq[item];
+    bh = (size_t)seq * H + blockIdx.y % H;
     dst_off = list.b[item];
+  }
+  // destination: tokens [t_base, t_base + 32) of plane ob (ocap tokens)
+  size_t ob = bh;
+  int t_base = dst_off + blk * 32, ocap = cap;
+  if constexpr (PG) {
+    if (!page_slot(pm, seq, (int)(bh % H), H, t_base, ob, t_base)) return;   // uniform
+    ocap = pm.page_tokens;
   }
   const uint4* src = reinterpret_cast<const uint4*>(v + (bh * in_stride + (size_t)blk * 32) * D);
   for (int i = threadIdx.x; i < 32 * D / 8; i += blockDim.x)
     copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
   __syncthreads();
 
-  const int t_base = dst_off + blk * 32;  // cache token of local token 0
   for (int it = threadIdx.x; it < 32 * NG; it += blockDim.x) {
     const int t = it / NG, j = it % NG;
     const uint16_t* row = tile + t * D + j * G;
@@ -168,7 +187,7 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
     group_stats<BITS>(mn, mx, &s);
     s_sc[it] = s;
     s_zr[it] = mn;
-    size_t m = (bh * cap + t_base + t) * NG + j;
+    size_t m = (ob * ocap + t_base + t) * NG + j;
     put_meta<MH>(scale, m, s);
     put_meta<MH>(zero, m, mn);
   }
@@ -177,7 +196,7 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
   constexpr int E = 32 / BITS;
   constexpr int WPB = 32 / E;   // words per channel in this 32-token block
   constexpr int WPC = 64 / E;   // words per channel per 64-token tile
-  uint32_t* plane = codes + bh * ((size_t)cap * D / E);
+  uint32_t* plane = codes + ob * ((size_t)ocap * D / E);
   const size_t tile_idx = (size_t)(t_base / 64);
   const int word0 = (t_base % 64) / E;
   for (int it = threadIdx.x; it < D * WPB; it += blockDim.x) {
@@ -228,12 +247,12 @@ hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, i
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
     kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
-                                   NoList{});
+                                   NoList{}, PageMap{});
   };
   if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true, false>) : go(quantize_k_kernel<2, false, false>);
+    mh ? go(quantize_k_kernel<2, true, false, false>) : go(quantize_k_kernel<2, false, false, false>);
   else
-    mh ? go(quantize_k_kernel<4, true, false>) : go(quantize_k_kernel<4, false, false>);
+    mh ? go(quantize_k_kernel<4, true, false, false>) : go(quantize_k_kernel<4, false, false, false>);
   return hipGetLastError();
 }
 
@@ -244,12 +263,12 @@ hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, i
   size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
   auto go = [&](auto kernel) {
     kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
-                                   NoList{});
+                                   NoList{}, PageMap{});
   };
   if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true, false>) : go(quantize_v_kernel<2, false, false>);
+    mh ? go(quantize_v_kernel<2, true, false, false>) : go(quantize_v_kernel<2, false, false, false>);
   else
-    mh ? go(quantize_v_kernel<4, true, false>) : go(quantize_v_kernel<4, false, false>);
+    mh ? go(quantize_v_kernel<4, true, false, false>) : go(quantize_v_kernel<4, false, false, false>);
   return hipGetLastError();
 }
 
@@ -260,12 +279,13 @@ hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H,
   dim3 grid(ntok_max / G, list.n * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, H, list);
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
+                                   PageMap{});
   };
   if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true, true>) : go(quantize_k_kernel<2, false, true>);
+    mh ? go(quantize_k_kernel<2, true, true, false>) : go(quantize_k_kernel<2, false, true, false>);
   else
-    mh ? go(quantize_k_kernel<4, true, true>) : go(quantize_k_kernel<4, false, true>);
+    mh ? go(quantize_k_kernel<4, true, true, false>) : go(quantize_k_kernel<4, false, true, false>);
   return hipGetLastError();
 }
 
@@ -276,12 +296,47 @@ hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H,
   dim3 grid(ntok_max / 32, list.n * H);
   size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, 0, codes, scale, zero, H, list);
+    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
+                                   PageMap{});
   };
   if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true, true>) : go(quantize_v_kernel<2, false, true>);
+    mh ? go(quantize_v_kernel<2, true, true, false>) : go(quantize_v_kernel<2, false, true, false>);
   else
-    mh ? go(quantize_v_kernel<4, true, true>) : go(quantize_v_kernel<4, false, true>);
+    mh ? go(quantize_v_kernel<4, true, true, false>) : go(quantize_v_kernel<4, false, true, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
+                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
+                                   uint32_t* codes, void* scale, void* zero, int mh,
+                                   hipStream_t st) {
+  if (list.n == 0 || ntok_max == 0) return hipSuccess;
+  dim3 grid(ntok_max / G, list.n * H);
+  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(k, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
+  };
+  if (bits == 2)
+    mh ? go(quantize_k_kernel<2, true, true, true>) : go(quantize_k_kernel<2, false, true, true>);
+  else
+    mh ? go(quantize_k_kernel<4, true, true, true>) : go(quantize_k_kernel<4, false, true, true>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const PageMap& pm,
+                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
+                                   uint32_t* codes, void* scale, void* zero, int mh,
+                                   hipStream_t st) {
+  if (list.n == 0 || ntok_max == 0) return hipSuccess;
+  dim3 grid(ntok_max / 32, list.n * H);
+  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
+  auto go = [&](auto kernel) {
+    kernel<<<grid, 256, lds, st>>>(v, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
+  };
+  if (bits == 2)
+    mh ? go(quantize_v_kernel<2, true, true, true>) : go(quantize_v_kernel<2, false, true, true>);
+  else
+    mh ? go(quantize_v_kernel<4, true, true, true>) : go(quantize_v_kernel<4, false, true, true>);
   return hipGetLastError();
 }
 

@@ -286,3 +286,58 @@ def test_ragged_append_decode_errors_leave_state():
     need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4)
     assert ad(ctypes.byref(c), P, P, P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
     assert lens(c) == ([0, 0], [0, 0])
+
+
+# ---- paged store: page-size / pool validation, then the ragged rules ----
+
+def paged(tq, tr, page_tokens=128, num_pages=16, table=P, ptrs=None, **kw):
+    import numpy as np
+    from kv_cache_bit_kivi_amd._lib import kivi_paged_cache
+    s = shape(**kw)
+    tqa = np.ascontiguousarray(tq, np.int32)
+    tra = np.ascontiguousarray(tr, np.int32)
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    c = kivi_paged_cache(s, page_tokens, num_pages, *(ptrs or [P] * 8), table,
+                         tqa.ctypes.data_as(p32), tra.ctypes.data_as(p32))
+    c._keep = (tqa, tra)
+    return c
+
+
+def test_paged_pool_bytes():
+    out = [ctypes.c_size_t() for _ in range(4)]
+    s = shape(meta_half=1)
+    assert _lib.kivi_paged_pool_bytes(ctypes.byref(s), 256, 10, *[ctypes.byref(x) for x in out]) == 0
+    slices = 10 * 4
+    assert [x.value for x in out] == [slices * 256 * 128 // 4, slices * 8 * 128 * 2,
+                                      slices * 256 * 128 // 4, slices * 256 * 4 * 2]
+    bad = [(96, 10), (32, 10), (192, 10), (128, 0)]     # not a power of two, < 64, ..., no pages
+    for pt, npg in bad:
+        assert _lib.kivi_paged_pool_bytes(ctypes.byref(s), pt, npg, None, None, None,
+                                          None) == KIVI_ESHAPE
+    s = shape(group=128)
+    assert _lib.kivi_paged_pool_bytes(ctypes.byref(s), 64, 4, None, None, None, None) == KIVI_ESHAPE
+
+
+def test_paged_errors_leave_state():
+    ad = _lib.kivi_paged_append_decode_attn
+    ap = _lib.kivi_paged_append
+    dec = _lib.kivi_paged_decode_attn
+    c = paged([416, 64], [128, 7])       # sequence 0's flush would pass capacity 512
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_ECAPACITY
+    assert lens(c) == ([416, 64], [128, 7])
+    c = paged([64, 32], [3, 1], page_tokens=96)          # page size not a power of two
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    c = paged([64, 32], [3, 1], page_tokens=1024)        # capacity 512 not a multiple
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    c = paged([64, 32], [3, 1], num_pages=0)
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    c = paged([64, 32], [3, 1], table=None)
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    c = paged([64, 32], [3, 1], table=P + 2)             # block table not 4-byte aligned
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_EALIGN
+    c = paged([64, 0], [3, 0])                           # sequence 1 empty
+    assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    c = paged([64, 32], [3, 1], ptrs=[P] * 7 + [0])
+    assert ap(ctypes.byref(c), P, P, None) == KIVI_EINVAL
+    assert lens(c) == ([64, 32], [3, 1])

@@ -1,0 +1,140 @@
+"""Paged quantized store on the GPU: the same calls on a paged cache and on a
+ragged (contiguous) cache give bit-identical outputs at every step, and the
+pages, gathered through the block table, equal the contiguous buffers bit for
+bit (through prefill, staggered flushes and fused steps).  The table is a
+shuffled page order with spare pages that must stay untouched and, in one
+case, -1 entries past every sequence's reach that must never be needed.  The
+ragged cache itself is checked against the oracle in test_gpu_ragged.py; one
+case here also checks the paged output against the oracle directly."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_bit_kivi_amd import synth
+from kv_cache_bit_kivi_amd.cache import PagedKiviCache, RaggedKiviCache
+from tests.gpu_util import ATTN_TOL, announce, dev, host, require_gpu, row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 0.0883883461356163
+QUANT = ("k_codes", "k_scale", "k_zero", "v_codes", "v_scale", "v_zero")
+
+
+def bits_of(a):
+    return a.view({4: np.uint32, 2: np.uint16}[a.dtype.itemsize])
+
+
+def assert_same_cache(pc, rc, what):
+    assert np.array_equal(pc.tq, rc.tq) and np.array_equal(pc.tr, rc.tr), what
+    for name in QUANT:
+        g = bits_of(pc.gather(name))
+        r = bits_of(host(getattr(rc, name)))
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError(f"{what} {name}: {len(bad)} mismatches, first at {bad[0]}")
+    for name in ("k_res", "v_res"):
+        assert np.array_equal(host(getattr(pc, name)).view(np.uint16),
+                              host(getattr(rc, name)).view(np.uint16)), (what, name)
+
+
+def run_pair(B, H, r, D, bits, G, R, P, ctx, steps, seed, meta_half=False, splits=0,
+             trim_table=False):
+    tq = [c - ((c - 1) % R + 1) if c > 0 else 0 for c in ctx]
+    T = max(ctx) + steps
+    cap = ((max(tq) + (steps // R + 2) * R + P - 1) // P) * P
+    mp = cap // P
+    spare = 5
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(B * mp + spare)[: B * mp].astype(np.int32).reshape(B, mp)
+    if trim_table:
+        # logical pages past what each sequence can reach in this run: -1
+        for b in range(B):
+            need = (tq[b] + (steps // R + 1) * R + P - 1) // P
+            table[b, need:] = -1
+    used = set(int(x) for x in table.ravel() if x >= 0)
+    spare_pages = [p for p in range(B * mp + spare) if p not in used]
+    k = synth.random_fp16(seed, (B, H, T, D), scale=2.0)
+    k[..., 3] *= np.float16(10)
+    v = synth.random_fp16(seed + 1, (B, H, T, D))
+    qs = synth.random_fp16(seed + 2, (steps + 1, B, H * r, D))
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+    pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, num_pages=B * mp + spare, table=table,
+                        meta_half=meta_half)
+    kd, vd = dev(k), dev(v)
+    rc.prefill(kd, vd, ctx, tq)
+    pc.prefill(kd, vd, ctx, tq)
+    assert_same_cache(pc, rc, "prefill")
+    q = dev(qs[0])
+    a = host(rc.decode(q, SCALE, num_splits=splits))
+    b = host(pc.decode(q, SCALE, num_splits=splits))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), "decode"
+    for i in range(steps):
+        kn = dev(np.stack([k[bb, :, ctx[bb] + i] for bb in range(B)]))
+        vn = dev(np.stack([v[bb, :, ctx[bb] + i] for bb in range(B)]))
+        q = dev(qs[i + 1])
+        a = host(rc.append_decode(kn, vn, q, SCALE, num_splits=splits))
+        b = host(pc.append_decode(kn, vn, q, SCALE, num_splits=splits))
+        assert np.array_equal(a.view(np.uint16), b.view(np.uint16)), f"step {i}"
+    assert_same_cache(pc, rc, "after steps")
+    for name in QUANT:   # spare pages never written
+        pool = host(getattr(pc, name))
+        for p in spare_pages:
+            assert not np.any(bits_of(pool[p])), (name, p)
+    return pc, rc, k, v, tq
+
+
+CASES = [
+    # B, H, r, D, bits, G, R, P, ctx, meta_half
+    (4, 2, 1, 128, 2, 32, 32, 128, [69, 400, 1, 255], False),
+    (3, 2, 4, 128, 4, 32, 64, 256, [100, 700, 64], False),
+    (2, 1, 8, 128, 2, 32, 32, 64, [300, 97], True),
+    (3, 2, 2, 64, 2, 32, 32, 64, [60, 300, 2], False),      # generic kernel
+    (2, 2, 1, 32, 4, 32, 32, 64, [31, 450], True),          # generic kernel
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B%dH%dr%dD%db%dG%dR%dP%d" % c[:8] + (
+    "_m16" if c[9] else ""))
+@pytest.mark.parametrize("splits", [0, 3])
+def test_paged_equals_ragged(case, splits):
+    require_gpu()
+    B, H, r, D, bits, G, R, P, ctx, mh = case
+    announce(f"paged == ragged {case} splits={splits}")
+    run_pair(B, H, r, D, bits, G, R, P, ctx, steps=R + 5, seed=sum(ctx) + P, meta_half=mh,
+             splits=splits)
+
+
+def test_paged_trimmed_table_and_oracle():
+    """Table entries past every sequence's reach are -1 (never looked up);
+    the paged output also meets the oracle directly."""
+    require_gpu()
+    announce("paged trimmed table + oracle")
+    B, H, r, D, bits, G, R, P = 3, 2, 2, 128, 2, 32, 32, 64
+    ctx = [200, 40, 129]
+    steps = R + 3
+    pc, rc, k, v, tq = run_pair(B, H, r, D, bits, G, R, P, ctx, steps, seed=77,
+                                trim_table=True)
+    q = synth.random_fp16(78, (B, H * r, D))
+    out = host(pc.decode(dev(q), SCALE))
+    for b in range(B):
+        L = ctx[b] + steps
+        oc = oracle.OracleCache(1, H, r, D, bits, G, R, pc.shape.capacity)
+        # the same token sequence, streamed into a one-sequence oracle cache
+        oc.prefill(k[b:b + 1, :, : ctx[b]], v[b:b + 1, :, : ctx[b]], tq[b])
+        for i in range(steps):
+            oc.append(np.ascontiguousarray(k[b:b + 1, :, ctx[b] + i]),
+                      np.ascontiguousarray(v[b:b + 1, :, ctx[b] + i]))
+        assert oc.tq + oc.tr == L
+        ref = oc.decode(np.ascontiguousarray(q[b:b + 1]), SCALE)
+        assert row_rel_err(out[b:b + 1].astype(np.float64), ref) <= ATTN_TOL, b
+
+
+def test_paged_many_sequences():
+    """130 sequences: the block-table rows are offset per launch."""
+    require_gpu()
+    announce("paged 130 sequences")
+    rng = np.random.default_rng(9)
+    ctx = rng.integers(1, 400, 130).tolist()
+    run_pair(130, 1, 1, 128, 2, 32, 32, 64, ctx, steps=3, seed=10, splits=2)
+    torch.cuda.synchronize()
