@@ -204,6 +204,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--meta", choices=["fp32", "fp16"], default="fp32",
                     help="storage of the quantization scales and zeros")
+    ap.add_argument("--paged", type=int, default=0, metavar="P",
+                    help="paged quantized store with P-token pages (0: contiguous planes); the "
+                         "block table is a seeded shuffle of the page pool")
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
     ap.add_argument("--window", type=int, default=16, metavar="W",
@@ -219,7 +222,8 @@ def main():
     meta_half = args.meta == "fp16"
     mb = 2 if meta_half else 4
     # profiles are keyed by workload and metadata width
-    tag = args.workload + ("_meta16" if meta_half else "")
+    tag = (args.workload + (f"_paged{args.paged}" if args.paged else "") +
+           ("_meta16" if meta_half else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
         pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
@@ -236,7 +240,7 @@ def main():
 
     from kv_cache_bit_kivi_amd import synth
     from kv_cache_bit_kivi_amd._lib import lib
-    from kv_cache_bit_kivi_amd.cache import KiviCache, RaggedKiviCache
+    from kv_cache_bit_kivi_amd.cache import KiviCache, PagedKiviCache, RaggedKiviCache
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -251,7 +255,8 @@ def main():
     per_layer_appends = (total_steps + NL - 1) // NL
     cap = w.capacity(per_layer_appends + R)
 
-    ragged = w.ragged
+    paged = args.paged > 0
+    ragged = w.ragged or paged      # (the paged calls carry per-sequence lengths)
     ctx0 = w.contexts().astype(np.int32)          # per-sequence lengths at the start
     tq0 = w.tqs().astype(np.int32)
     tr0 = ctx0 - tq0
@@ -259,8 +264,16 @@ def main():
     kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     del k, v
     caches = []
-    for _ in range(NL):
-        if ragged:
+    if paged:
+        cap = (cap + args.paged - 1) // args.paged * args.paged
+    for li in range(NL):
+        if paged:
+            mp = cap // args.paged
+            perm = np.random.default_rng(1000 + li).permutation(B * mp).astype(np.int32)
+            c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp,
+                               table=perm.reshape(B, mp), meta_half=meta_half)
+            c.prefill(kd, vd, ctx0, tq0)
+        elif ragged:
             c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
             c.prefill(kd, vd, ctx0, tq0)
         else:
@@ -304,10 +317,15 @@ def main():
     wsp = [(c.workspace.data_ptr(), c.workspace.numel()) if c.workspace is not None else (None, 0)
            for c in caches]
     scale = float(w.softmax_scale)
-    if ragged:
+    if paged:
+        crefs = [ctypes.byref(c.pc) for c in caches]
+        append_fn, decode_fn = L.kivi_paged_append, L.kivi_paged_decode_attn
+        fused_fn = L.kivi_paged_append_decode_attn
+    elif ragged:
         crefs = [ctypes.byref(c.rc) for c in caches]
         append_fn, decode_fn = L.kivi_ragged_append, L.kivi_ragged_decode_attn
         fused_fn = L.kivi_ragged_append_decode_attn
+    if ragged:
 
         def flushes(li):          # sequences whose residual is full (flush on this append)
             return caches[li].tr_arr == R
@@ -408,8 +426,9 @@ def main():
     value = total_bytes / elapsed / 1e9
     achieved = w_bytes / (w_time * 1e-3) / 1e9
     if ragged:
-        calls = ("kivi_ragged_append + kivi_ragged_decode_attn" if args.separate
-                 else "kivi_ragged_append_decode_attn")
+        kind = "paged" if paged else "ragged"
+        calls = (f"kivi_{kind}_append + kivi_{kind}_decode_attn" if args.separate
+                 else f"kivi_{kind}_append_decode_attn")
     else:
         calls = "kivi_append + kivi_decode_attn" if args.separate else "kivi_append_decode_attn"
 
@@ -433,6 +452,8 @@ def main():
                                   "max": int(ctx0.max()), "per_sequence": ctx0.tolist()}),
             "bits": bits, "group": G, "residual": R,
             "scale_zero": "fp16" if meta_half else "fp32",
+            "store": f"paged, {args.paged}-token pages, shuffled block table" if paged
+                     else "contiguous planes",
             "layers_rotated": NL, "decode_splits": splits_used,
             "step_call": calls,
             "sequence_flushes_in_timed_region": n_flush,
