@@ -43,13 +43,20 @@
  *     reads KV head hq / r.
  *
  * Packed layout (the library's documented storage contract, re-implemented
- * here independently from its description):
- *   E = 32 / bits codes per 32-bit word, little-endian bit order.
- *   K codes : [B][H][cap][D/E] words; channel d of token t sits in word d/E
- *             at bit offset bits*(d%E).
- *   V codes : [B][H][cap/64][D][64/E] words; token t, channel d sits in
- *             tile t/64, word (t%64)/E of channel d, bit offset
- *             bits*((t%64)%E).
+ * here independently from its description).  Codes are stored in "rows" of
+ * n positions: a key row is one token's n = D channels, a value row is one
+ * channel's n = 64 tokens of a 64-token tile.  A row of n codes of b bits
+ * takes n*b/32 words; position p of a row sits at (word, bit):
+ *   b = 2, 4 : word p/E, bit b*(p%E), E = 32/b (little-endian order);
+ *   b = 1    : word p/32, bit beta(p%32),
+ *              beta(p) = 4*((p%16)/2) + 2*(p/16) + p%2;
+ *   b = 3    : code c = lo + 4*hi; lo at word p/16, bits 2*(p%16) (the
+ *              2-bit order), hi at word n/16 + p/32, bit beta(p%32) (the
+ *              1-bit order) -- the two-bit plane first, then the one-bit
+ *              plane.
+ *   K codes : [B][H][cap][D*b/32] words, one key row per token.
+ *   V codes : [B][H][cap/64][D][2*b] words: tile t/64, channel d, position
+ *             t%64 of that value row.
  *   K scale/zero : [B][H][cap/G][D] binary32.
  *   V scale/zero : [B][H][cap][D/G] binary32.
  *   residual K/V : [B][H][R][D] binary16.
@@ -132,6 +139,42 @@ uint16_t kivio_float_to_half(float f) {
 
 static int words_per_row(int D, int bits) { return D * bits / 32; }
 
+/* bit of position p (0..31) inside a one-bit word (the layout above) */
+static int beta(int p) { return 4 * ((p % 16) / 2) + 2 * (p / 16) + p % 2; }
+
+/* OR code c into position p of a row of n codes */
+static void row_put(uint32_t* row, int n, int bits, int p, uint32_t c) {
+  if (bits == 3) {
+    row[p / 16] |= (c & 3u) << (2 * (p % 16));
+    row[n / 16 + p / 32] |= (c >> 2) << beta(p % 32);
+  } else if (bits == 1) {
+    row[p / 32] |= c << beta(p % 32);
+  } else {
+    const int E = 32 / bits;
+    row[p / E] |= c << (bits * (p % E));
+  }
+}
+
+/* code at position p of a row of n codes */
+static uint32_t row_get(const uint32_t* row, int n, int bits, int p) {
+  if (bits == 3)
+    return ((row[p / 16] >> (2 * (p % 16))) & 3u) |
+           (((row[n / 16 + p / 32] >> beta(p % 32)) & 1u) << 2);
+  if (bits == 1) return (row[p / 32] >> beta(p % 32)) & 1u;
+  const int E = 32 / bits;
+  return (row[p / E] >> (bits * (p % E))) & ((1u << bits) - 1u);
+}
+
+/* zero every word that position p of the row uses */
+static void row_clear(uint32_t* row, int n, int bits, int p) {
+  if (bits == 3) {
+    row[p / 16] = 0;
+    row[n / 16 + p / 32] = 0;
+  } else {
+    row[p / (32 / bits)] = 0;
+  }
+}
+
 /* metadata element m of a scale / zero array: binary32, or binary16 when
  * meta_half (the variant with half-width scale and zero) */
 static double meta_get(const void* a, size_t m, int meta_half) {
@@ -178,7 +221,7 @@ static void quantize_group(const float* xs, int n, int bits, uint8_t* codes,
 
 static int check_common(int B, int H, int D, int bits, int G, int cap) {
   if (B < 1 || H < 1 || D < 1 || G < 1 || cap < 0) return KIVIO_EINVAL;
-  if (bits != 2 && bits != 4) return KIVIO_EINVAL;
+  if (bits < 1 || bits > 4) return KIVIO_EINVAL;
   if (D % G != 0) return KIVIO_ESHAPE;
   if ((D * bits) % 32 != 0) return KIVIO_ESHAPE;
   if (cap % 64 != 0 || cap % G != 0) return KIVIO_ESHAPE;
@@ -196,7 +239,7 @@ int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap, int meta_hal
   if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
     return KIVIO_ESHAPE;
   if (dst_off + ntok > cap) return KIVIO_ECAPACITY;
-  const int E = 32 / bits, W = words_per_row(D, bits);
+  const int W = words_per_row(D, bits);
   float xs[1024];
   uint8_t cs[1024];
   if (G > 1024) return KIVIO_ESHAPE;
@@ -219,17 +262,17 @@ int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap, int meta_hal
           meta_put(zero, mbase + (size_t)gg * D + d, z, meta_half);
           for (int i = 0; i < G; i++) {
             int t = dst_off + g * G + i;
-            cw[(size_t)t * W + d / E] |= (uint32_t)cs[i] << (bits * (d % E));
+            row_put(cw + (size_t)t * W, D, bits, d, cs[i]);
           }
         }
     }
   return KIVIO_OK;
 }
 
-/* word index (within one (b, h) plane) of value-cache token t, channel d */
-static size_t v_word_index(int D, int bits, int t, int d) {
-  const int E = 32 / bits, WPC = 64 / E; /* words per channel per tile */
-  return ((size_t)(t / 64) * D + d) * WPC + (t % 64) / E;
+/* value row (within one (b, h) plane) holding token t of channel d */
+static size_t v_row(int D, int bits, int t, int d) {
+  const int WPC = 2 * bits; /* words per channel per 64-token tile */
+  return ((size_t)(t / 64) * D + d) * WPC;
 }
 
 /* Value quantization, per token over groups of G consecutive channels
@@ -243,8 +286,8 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
   if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
     return KIVIO_ESHAPE;
   if (dst_off + ntok > cap) return KIVIO_ECAPACITY;
-  const int E = 32 / bits, NG = D / G;
-  const size_t plane_words = (size_t)cap * D / E;
+  const int NG = D / G;
+  const size_t plane_words = (size_t)cap * D * bits / 32;
   float xs[1024];
   uint8_t cs[1024];
   if (G > 1024) return KIVIO_ESHAPE;
@@ -253,8 +296,10 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
       const uint16_t* src = v + ((size_t)b * H + h) * (size_t)in_stride * D;
       uint32_t* cw = codes + ((size_t)b * H + h) * plane_words;
       const size_t mbase = ((size_t)b * H + h) * (size_t)cap * NG;
+      /* the token range is 32-aligned, so the words it uses hold no other tokens */
       for (int t = 0; t < ntok; t++)
-        for (int d = 0; d < D; d++) cw[v_word_index(D, bits, dst_off + t, d)] = 0;
+        for (int d = 0; d < D; d++)
+          row_clear(cw + v_row(D, bits, dst_off + t, d), 64, bits, (dst_off + t) % 64);
       for (int t = 0; t < ntok; t++)
         for (int j = 0; j < NG; j++) {
           for (int i = 0; i < G; i++)
@@ -266,8 +311,7 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
           meta_put(zero, mbase + (size_t)tt * NG + j, z, meta_half);
           for (int i = 0; i < G; i++) {
             int d = j * G + i;
-            cw[v_word_index(D, bits, tt, d)] |= (uint32_t)cs[i]
-                                                << (bits * ((tt % 64) % E));
+            row_put(cw + v_row(D, bits, tt, d), 64, bits, tt % 64, cs[i]);
           }
         }
     }
@@ -316,17 +360,15 @@ int kivio_append(int B, int H, int D, int bits, int G, int R, int cap, int meta_
 /* (sc, zr point at the plane's metadata; mb is the plane's element offset) */
 static double dequant_k(const uint32_t* cw, const void* sc, const void* zr, size_t mb,
                         int meta_half, int D, int bits, int G, int t, int d) {
-  const int E = 32 / bits, W = words_per_row(D, bits);
-  uint32_t c = (cw[(size_t)t * W + d / E] >> (bits * (d % E))) & ((1u << bits) - 1);
+  const int W = words_per_row(D, bits);
+  uint32_t c = row_get(cw + (size_t)t * W, D, bits, d);
   size_t m = mb + (size_t)(t / G) * D + d;
   return (double)c * meta_get(sc, m, meta_half) + meta_get(zr, m, meta_half);
 }
 
 static double dequant_v(const uint32_t* cw, const void* sc, const void* zr, size_t mb,
                         int meta_half, int D, int bits, int G, int t, int d) {
-  const int E = 32 / bits;
-  uint32_t c = (cw[v_word_index(D, bits, t, d)] >> (bits * ((t % 64) % E))) &
-               ((1u << bits) - 1);
+  uint32_t c = row_get(cw + v_row(D, bits, t, d), 64, bits, t % 64);
   size_t m = mb + (size_t)t * (D / G) + d / G;
   return (double)c * meta_get(sc, m, meta_half) + meta_get(zr, m, meta_half);
 }
@@ -345,7 +387,7 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
   if (r < 1) return KIVIO_EINVAL;
   if (tq < 0 || tq % G || tq > cap || tr < 0 || tr > R || tq + tr < 1)
     return KIVIO_ESHAPE;
-  const int Hq = H * r, W = words_per_row(D, bits), E = 32 / bits;
+  const int Hq = H * r, W = words_per_row(D, bits);
   const int L = tq + tr;
   double* logit = scratch;
   double* p = scratch + L;
@@ -355,7 +397,7 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       const size_t bh = (size_t)b * H + h;
       const uint32_t* kc = k_codes + bh * (size_t)cap * W;
       const size_t kmb = bh * (size_t)(cap / G) * D;
-      const uint32_t* vc = v_codes + bh * (size_t)cap * D / E;
+      const uint32_t* vc = v_codes + bh * (size_t)cap * D * bits / 32;
       const size_t vmb = bh * (size_t)cap * (D / G);
       const uint16_t* kr = k_res + bh * (size_t)R * D;
       const uint16_t* vr = v_res + bh * (size_t)R * D;

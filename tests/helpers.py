@@ -1,7 +1,7 @@
 """Test-side helpers written independently of the oracle and of the library.
 
 They re-read the documented packed layout (token-major key rows; value codes
-channel-major inside 64-token tiles) with NumPy, dequantize in binary64 and
+channel-major inside 64-token tiles; the per-width bit orders) with NumPy, dequantize in binary64 and
 evaluate plain softmax attention, so oracle pins do not lean on the oracle's
 own unpacking code.
 """
@@ -10,25 +10,47 @@ from __future__ import annotations
 import numpy as np
 
 
+def beta(p):
+    """Bit of position p (0..31) inside a one-bit code word: 4*((p%16)//2) +
+    2*(p//16) + p%2 (the documented one-bit order)."""
+    p = np.asarray(p)
+    return 4 * ((p % 16) // 2) + 2 * (p // 16) + p % 2
+
+
+def row_codes(rows: np.ndarray, bits: int, n: int, pos: np.ndarray) -> np.ndarray:
+    """Codes at positions ``pos`` of rows of n codes (rows: [..., n*bits/32]
+    uint32 words; pos broadcast against the leading axes) per the documented
+    layouts: b = 2, 4 little-endian E = 32/b per word; b = 1 at bit beta(p%32)
+    of word p/32; b = 3 a two-bit plane (word p/16, bits 2*(p%16)) followed
+    by a one-bit plane of the high bit (word n/16 + p/32, bit beta(p%32))."""
+    rows = rows.astype(np.int64)
+    pos = np.asarray(pos)
+
+    def word(i):
+        return np.take_along_axis(rows, np.broadcast_to(i, rows.shape[:-1])[..., None], -1)[..., 0]
+
+    if bits == 3:
+        lo = (word(pos // 16) >> (2 * (pos % 16))) & 3
+        hi = (word(n // 16 + pos // 32) >> beta(pos % 32)) & 1
+        return lo | (hi << 2)
+    if bits == 1:
+        return (word(pos // 32) >> beta(pos % 32)) & 1
+    E = 32 // bits
+    return (word(pos // E) >> (bits * (pos % E))) & ((1 << bits) - 1)
+
+
 def unpack_k(codes: np.ndarray, bits: int, tq: int, D: int) -> np.ndarray:
     """codes [B][H][cap][D*bits/32] uint32 -> [B][H][tq][D] integer codes."""
-    E = 32 // bits
-    mask = (1 << bits) - 1
-    d = np.arange(D)
-    words = codes[:, :, :tq, d // E]                       # [B][H][tq][D]
-    return ((words >> (bits * (d % E)).astype(np.uint32)) & mask).astype(np.int64)
+    rows = codes[:, :, :tq, None, :]                      # [B][H][tq][1][W]
+    rows = np.broadcast_to(rows, rows.shape[:3] + (D, rows.shape[-1]))
+    return row_codes(rows, bits, D, np.arange(D)[None, None, None, :])
 
 
 def unpack_v(codes: np.ndarray, bits: int, tq: int, D: int) -> np.ndarray:
-    """codes [B][H][cap/64][D][64*bits/32] -> [B][H][tq][D] integer codes."""
-    E = 32 // bits
-    mask = (1 << bits) - 1
+    """codes [B][H][cap/64][D][2*bits] -> [B][H][tq][D] integer codes."""
     t = np.arange(tq)
-    tile, tau = t // 64, t % 64
-    w = codes[:, :, tile, :, :]                              # [B][H][tq][D][WPC]
-    w = np.take_along_axis(w, (tau // E)[None, None, :, None, None].repeat(D, 3), axis=4)[..., 0]
-    shift = (bits * (tau % E)).astype(np.uint32)[None, None, :, None]
-    return ((w >> shift) & mask).astype(np.int64)
+    rows = codes[:, :, t // 64, :, :]                     # [B][H][tq][D][WPC]
+    return row_codes(rows, bits, 64, (t % 64)[None, None, :, None])
 
 
 def dequant_k(codes, scale, zero, bits, G, tq, D):

@@ -41,7 +41,7 @@ def test_all_residual_equals_sdpa(oracle_lib, r, L):
     np.testing.assert_allclose(got, ref.numpy(), rtol=1e-12, atol=1e-13)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("r", [1, 2, 4])
 @pytest.mark.parametrize("tq,tr", [(64, 0), (32, 1), (64, 31), (0, 5), (96, 32)])
 def test_tiny_brute_force(oracle_lib, bits, r, tq, tr):

@@ -75,7 +75,7 @@ def test_worked_examples_values(oracle_lib, case):
 
 # ---------------------------------------------------------------------------
 # constant groups dequantize exactly
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_constant_groups_exact(oracle_lib, bits):
     G, D, T = 32, 64, 128
     rng = np.random.default_rng(7)
@@ -135,7 +135,7 @@ def _groups_keys(x16, G):
     return x16.astype(np.float64).reshape(B, H, T // G, G, D).transpose(0, 1, 2, 4, 3).reshape(-1, G)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("G", [32, 64, 128])
 def test_error_bound_and_extremes(oracle_lib, bits, G):
     """|x - (c*s + z)| <= s/2 (plus binary32 slack); the group minimum gets
@@ -159,7 +159,7 @@ def test_error_bound_and_extremes(oracle_lib, bits, G):
     assert np.array_equal(zs, xs.min(1))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_nearest_level_brute_force(oracle_lib, bits):
     """Each code is the nearest of the 2^b levels z + k*s (exact rational
     distances), except within 1e-5 of a tie where binary32 rounding of the
@@ -224,7 +224,7 @@ def _emulate_group(vals, bits):
     return float(s), float(mn), codes
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_exact_rational_emulation(oracle_lib, bits):
     """Bit-exact agreement with an exact-rational emulation of each binary32
     step (subtract, divide, round half to even)."""
@@ -247,7 +247,7 @@ def test_exact_rational_emulation(oracle_lib, bits):
         assert list(c[0, 0, t, :G]) == ec
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("k", [-3, 1, 4])
 def test_power_of_two_scaling(oracle_lib, bits, k):
     """x -> 2^k x keeps every code and scales s, z by exactly 2^k."""
@@ -264,7 +264,20 @@ def test_power_of_two_scaling(oracle_lib, bits, k):
         assert np.array_equal(z2, z1 * np.float32(2.0 ** k))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+def _bit_slots(bits, n, p):
+    """[(word, bit, value bit)] that position p of a row of n codes occupies,
+    written out from the documented layout (independent of helpers.py)."""
+    beta = 4 * ((p % 32 % 16) // 2) + 2 * ((p % 32) // 16) + p % 2
+    if bits == 1:
+        return [(p // 32, beta, 0)]
+    if bits == 3:
+        return [(p // 16, 2 * (p % 16), 0), (p // 16, 2 * (p % 16) + 1, 1),
+                (n // 16 + p // 32, beta, 2)]
+    E = 32 // bits
+    return [(p // E, bits * (p % E) + i, i) for i in range(bits)]
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_packed_bit_positions(oracle_lib, bits):
     """Codes land at the documented bit positions.  Inputs are exactly the
     integer levels (scale 1, zero 0), so the code of (t, d) is known in
@@ -274,25 +287,34 @@ def test_packed_bit_positions(oracle_lib, bits):
     t = np.arange(T)[:, None]
     d = np.arange(D)[None, :]
     base = (3 * t + 5 * d) % (qmax + 1)
-    E = 32 // bits
     lk = base.copy()
     lk[::G, :] = 0             # every key group (tokens of a channel) spans 0..qmax
     lk[1::G, :] = qmax
     ck, sk, zk = oracle.quantize_k(lk.astype(np.float16)[None, None], bits, G, cap=T)
     assert np.all(sk == 1) and np.all(zk == 0)
     for tt in (0, 5, 77, 127):
-        for dd in (0, 1, E - 1, E, D - 1):
-            word = ck[0, 0, tt, dd // E]
-            assert (int(word) >> (bits * (dd % E))) & qmax == lk[tt, dd]
+        for dd in (0, 1, 15, 16, 31, 32, D - 1):
+            got = sum(((int(ck[0, 0, tt, w]) >> bit) & 1) << vb
+                      for w, bit, vb in _bit_slots(bits, D, dd))
+            assert got == lk[tt, dd], (tt, dd)
     lv = base.copy()
     lv[:, ::G] = 0             # every value group (channels of a token) spans 0..qmax
     lv[:, 1::G] = qmax
     cv, sv, zv = oracle.quantize_v(lv.astype(np.float16)[None, None], bits, G, cap=T)
     assert np.all(sv == 1) and np.all(zv == 0)
-    for tt in (0, 5, 63, 64, 100, 127):
+    for tt in (0, 5, 15, 16, 31, 32, 63, 64, 100, 127):
         for dd in (0, 7, D - 1):
-            word = cv[0, 0, tt // 64, dd, (tt % 64) // E]
-            assert (int(word) >> (bits * ((tt % 64) % E))) & qmax == lv[tt, dd]
+            got = sum(((int(cv[0, 0, tt // 64, dd, w]) >> bit) & 1) << vb
+                      for w, bit, vb in _bit_slots(bits, 64, tt % 64))
+            assert got == lv[tt, dd], (tt, dd)
+    # every word bit is used exactly once per row (the layout is a bijection)
+    for n in (D, 64):
+        seen = set()
+        for pp in range(n):
+            for w, bit, _ in _bit_slots(bits, n, pp):
+                assert (w, bit) not in seen
+                seen.add((w, bit))
+        assert len(seen) == n * bits
 
 
 def test_offset_and_stride(oracle_lib):
@@ -314,7 +336,9 @@ def test_offset_and_stride(oracle_lib):
 def test_error_codes(oracle_lib):
     x = synth.random_fp16(1, (1, 1, 64, 64))
     with pytest.raises(oracle.oracle.OracleError, match="EINVAL"):
-        oracle.quantize_k(x, 3, 32, cap=64)
+        oracle.quantize_k(x, 5, 32, cap=64)
+    with pytest.raises(oracle.oracle.OracleError, match="EINVAL"):
+        oracle.quantize_k(x, 0, 32, cap=64)
     with pytest.raises(oracle.oracle.OracleError, match="ESHAPE"):
         oracle.quantize_k(x, 2, 32, cap=64, ntok=48)
     with pytest.raises(oracle.oracle.OracleError, match="ECAPACITY"):

@@ -57,7 +57,7 @@ def test_float_to_half_matches_numpy(oracle_lib):
     assert bad.size == 0, [(float(allx[i]), hex(got[i]), hex(want[i])) for i in bad[:5]]
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("G", [32, 64])
 def test_meta16_is_rounded_meta32(oracle_lib, bits, G):
     """Same codes; scale = binary16(binary32 scale); zero equal and exact."""
@@ -73,7 +73,7 @@ def test_meta16_is_rounded_meta32(oracle_lib, bits, G):
         assert np.array_equal(z32.astype(np.float16).astype(np.float32), z32)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_meta16_error_bound(oracle_lib, bits):
     """|x - (c s16 + z16)| <= s (1/2 + 2^-18) + c |s - s16|: the binary32
     bound plus what rounding the scale can add, per element."""
@@ -93,7 +93,7 @@ def test_meta16_error_bound(oracle_lib, bits):
     assert np.all(np.abs(s - sh) <= np.abs(s) * 2.0 ** -11 + 2.0 ** -25)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("r", [1, 4])
 @pytest.mark.parametrize("tq,tr", [(64, 0), (96, 31)])
 def test_meta16_decode_brute_force(oracle_lib, bits, r, tq, tr):
@@ -116,7 +116,7 @@ def test_meta16_decode_brute_force(oracle_lib, bits, r, tq, tr):
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_meta16_stream_equals_one_shot(oracle_lib, bits):
     """Prefill + appends (with flushes) == one-shot quantization, bit for bit."""
     B, H, D, G, R = 1, 2, 64, 32, 32

@@ -15,7 +15,7 @@ from kv_cache_bit_kivi_amd import synth
 from tests.helpers import unpack_k, unpack_v
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("G,R", [(32, 32), (32, 128), (64, 128)])
 def test_stream_equals_one_shot(oracle_lib, bits, G, R):
     """prefill + n appends leaves exactly the codes/scales/zeros that one
