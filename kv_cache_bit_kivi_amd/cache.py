@@ -45,12 +45,11 @@ class KiviCache:
         check(_lib.kivi_cache_bytes(ctypes.byref(self.shape), *[ctypes.byref(s) for s in sizes]),
               "kivi_cache_bytes")
         B, H, D, G, R, cap = batch, kv_heads, head_dim, group, residual, capacity
-        E = 32 // bits
         dev = torch.device(device)
-        self.k_codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device=dev)
+        self.k_codes = torch.zeros((B, H, cap, D * bits // 32), dtype=torch.int32, device=dev)
         self.k_scale = torch.zeros((B, H, cap // G, D), dtype=mdt, device=dev)
         self.k_zero = torch.zeros((B, H, cap // G, D), dtype=mdt, device=dev)
-        self.v_codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device=dev)
+        self.v_codes = torch.zeros((B, H, cap // 64, D, 2 * bits), dtype=torch.int32, device=dev)
         self.v_scale = torch.zeros((B, H, cap, D // G), dtype=mdt, device=dev)
         self.v_zero = torch.zeros((B, H, cap, D // G), dtype=mdt, device=dev)
         self.k_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
@@ -249,14 +248,13 @@ class PagedKiviCache(RaggedKiviCache):
                                          *[ctypes.byref(x) for x in sizes]),
               "kivi_paged_pool_bytes")
         B, H, D, G, R = batch, kv_heads, head_dim, group, residual
-        E = 32 // bits
         dev = torch.device(device)
         mdt = torch.float16 if meta_half else torch.float32
         self.page_tokens, self.num_pages, self.max_pages = P, num_pages, max_pages
-        self.k_codes = torch.zeros((num_pages, H, P, D // E), dtype=torch.int32, device=dev)
+        self.k_codes = torch.zeros((num_pages, H, P, D * bits // 32), dtype=torch.int32, device=dev)
         self.k_scale = torch.zeros((num_pages, H, P // G, D), dtype=mdt, device=dev)
         self.k_zero = torch.zeros((num_pages, H, P // G, D), dtype=mdt, device=dev)
-        self.v_codes = torch.zeros((num_pages, H, P // 64, D, 64 // E), dtype=torch.int32,
+        self.v_codes = torch.zeros((num_pages, H, P // 64, D, 2 * bits), dtype=torch.int32,
                                    device=dev)
         self.v_scale = torch.zeros((num_pages, H, P, D // G), dtype=mdt, device=dev)
         self.v_zero = torch.zeros((num_pages, H, P, D // G), dtype=mdt, device=dev)

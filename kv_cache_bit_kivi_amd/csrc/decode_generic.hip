@@ -31,6 +31,21 @@ __device__ __forceinline__ uint16_t f2h(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// Code at position p of a packed row of n codes (a key row: D channels; a
+// value row: one channel's 64 tokens of a tile) for b = 1..4 bits:
+//   2, 4 bits: word p/E, bit b*(p%E), E = 32/b;  1 bit: word p/32, bit
+//   beta(p%32);  3 bits: lo (word p/16, bits 2*(p%16)) + 4 * hi (word
+//   n/16 + p/32, bit beta(p%32)),  beta(p) = 4*((p%16)/2) + 2*(p/16) + p%2.
+__device__ __forceinline__ uint32_t code_at(const uint32_t* row, int n, int bits, int p) {
+  auto beta = [](int q) { return 4 * ((q & 15) >> 1) + 2 * (q >> 4) + (q & 1); };
+  if (bits == 3)
+    return ((row[p >> 4] >> (2 * (p & 15))) & 3u) |
+           (((row[(n >> 4) + (p >> 5)] >> beta(p & 31)) & 1u) << 2);
+  if (bits == 1) return (row[p >> 5] >> beta(p & 31)) & 1u;
+  const int E = 32 / bits;
+  return (row[p / E] >> (bits * (p % E))) & ((1u << bits) - 1u);
+}
+
 // scale / zero element i of a metadata plane (binary32, or binary16 when mh)
 __device__ __forceinline__ float meta_at(const void* p, size_t i, int mh) {
   return mh ? h2f(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
@@ -74,8 +89,7 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   if constexpr (RAG) chunk = (L + a.S - 1) / a.S;   // per sequence
   const int t0 = split * chunk;
   const int t1 = min(L, t0 + chunk);
-  const int E = 32 / bits, W = D / E, WPC = 64 / E, NG = D / G;
-  const uint32_t mask = (1u << bits) - 1u;
+  const int W = D * bits / 32, WPC = 2 * bits, NG = D / G;   // words per key / value row
 
   const size_t kvp = (size_t)u;                   // plane index
   const int mh = a.mh;
@@ -122,17 +136,12 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
       if (t < tq && slot(t, pl, lt)) {
         const uint32_t* row = a.k_codes + (pl * scap + lt) * W;
         const size_t m0 = (pl * (scap / G) + lt / G) * D;
-        for (int w = 0; w < W; w++) {
-          const uint32_t word = row[w];
-          for (int e = 0; e < E; e++) {
-            const int dd = w * E + e;
-            const float kh = (float)((word >> (bits * e)) & mask) *
-                                 meta_at(a.k_scale, m0 + dd, mh) +
-                             meta_at(a.k_zero, m0 + dd, mh);
+        for (int dd = 0; dd < D; dd++) {
+          const float kh = (float)code_at(row, D, bits, dd) * meta_at(a.k_scale, m0 + dd, mh) +
+                           meta_at(a.k_zero, m0 + dd, mh);
 #pragma unroll
-            for (int i = 0; i < RR; i++)
-              if (i < r) acc[i] += sq[i * D + dd] * kh;
-          }
+          for (int i = 0; i < RR; i++)
+            if (i < r) acc[i] += sq[i * D + dd] * kh;
         }
       } else if (t >= tq) {
         const uint16_t* row = kr + (size_t)(t - tq) * D;
@@ -183,10 +192,10 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
         int lt;
         if (t < tq) {
           if (slot(t, pl, lt)) {
-            const uint32_t word =
-                a.v_codes[pl * scap * D / E + ((size_t)(lt / 64) * D + d) * WPC + (lt % 64) / E];
+            const uint32_t* row =
+                a.v_codes + pl * scap * D * bits / 32 + ((size_t)(lt / 64) * D + d) * WPC;
             const size_t mi = (pl * scap + lt) * NG + d / G;
-            vh = (float)((word >> (bits * ((lt % 64) % E))) & mask) * meta_at(a.v_scale, mi, mh) +
+            vh = (float)code_at(row, 64, bits, lt % 64) * meta_at(a.v_scale, mi, mh) +
                  meta_at(a.v_zero, mi, mh);
           }
         } else {

@@ -1,5 +1,5 @@
 // Decode attention on the mixed cache with matrix-core (MFMA) contractions,
-// for head_dim 128, group 32, 2- or 4-bit codes and GQA ratio r in {1,2,4,8}.
+// for head_dim 128, group 32, 1- to 4-bit codes and GQA ratio r in {1,2,4,8}.
 //
 // Method (study.space summary of "KIVI: A Tuning-Free Asymmetric 2bit
 // Quantization for KV Cache"): the scores of the quantized grouped part are a
@@ -13,8 +13,11 @@
 // (sc = softmax scale * log2(e): scores live in the log2 domain, p = 2^(s-m)).
 //
 // Both contractions run on 16x16x32 MFMAs.  Operand B is the codes, converted
-// exactly (2-bit codes via the e2m1 convert with scale 2, 4-bit codes via the
-// e4m3 convert with scale 2^9).  Operand A is the factor q' (or p'), split
+// exactly (2-bit codes via the e2m1 convert with scale 2 on nibble planes,
+// 1-bit codes likewise on the nibble bit-planes of their words, 3-bit codes as
+// their 2-bit plane plus their high-bit plane converted with scale 8, i.e. four
+// times the high bit, accumulated with the same factor operand; 4-bit codes
+// via the e4m3 convert with scale 2^9).  Operand A is the factor q' (or p'), split
 // into hi + lo rows so the products keep at least 16 significant bits:
 //   keys (fp16):   A = rows (head, hi|lo) x 32 channels, B = 32 channels x 16
 //                  tokens; hi = q' rounded toward zero, lo = the remainder.
@@ -80,13 +83,18 @@ int occupancy_bits(int r, int nw) {
 
 int decode_mfma_blocks_per_cu(int bits, int r, int nw) {
   // cached per (bits, r, requested waves): queried once per process
-  static std::atomic<int> cache[2][4][3];
-  const int bi = bits == 2 ? 0 : 1;
+  static std::atomic<int> cache[4][4][3];
+  const int bi = bits - 1;
   const int ri = r == 1 ? 0 : (r == 2 ? 1 : (r == 4 ? 2 : 3));
   const int wi = nw >= 8 ? 1 : 0;
   int c = cache[bi][ri][wi].load(std::memory_order_relaxed);
   if (c == 0) {
-    c = bits == 2 ? occupancy_bits<2>(r, nw) : occupancy_bits<4>(r, nw);
+    switch (bits) {
+      case 1: c = occupancy_bits<1>(r, nw); break;
+      case 2: c = occupancy_bits<2>(r, nw); break;
+      case 3: c = occupancy_bits<3>(r, nw); break;
+      default: c = occupancy_bits<4>(r, nw); break;
+    }
     cache[bi][ri][wi].store(c, std::memory_order_relaxed);
   }
   return c;
@@ -103,8 +111,12 @@ int decode_mfma_block_waves(int r, int nw) {
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
   const NoLens none;
-  return a.bits == 2 ? launch_bits<2, false, false>(a, none, nw, st)
-                     : launch_bits<4, false, false>(a, none, nw, st);
+  switch (a.bits) {
+    case 1: return launch_bits<1, false, false>(a, none, nw, st);
+    case 2: return launch_bits<2, false, false>(a, none, nw, st);
+    case 3: return launch_bits<3, false, false>(a, none, nw, st);
+    default: return launch_bits<4, false, false>(a, none, nw, st);
+  }
 }
 
 }  // namespace kivi

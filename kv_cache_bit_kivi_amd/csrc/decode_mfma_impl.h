@@ -62,13 +62,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// 8 two-bit codes held one per nibble (upper two bits zero) -> 8 exact halves,
-// slot s = nibble s
-__device__ __forceinline__ half8 cvt_nib2(uint32_t x) {
-  half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 0);
-  half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 1);
-  half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 2);
-  half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 2.0f, 3);
+// 8 codes of at most two bits held one per nibble (upper bits zero) -> 8
+// exact halves, slot s = nibble s.  The e2m1 value of nibble c is c/2, so
+// scale 2 gives the codes and scale 8 four times them (the high plane of a
+// three-bit code).
+__device__ __forceinline__ half8 cvt_nib2(uint32_t x, float sc = 2.0f) {
+  half2v h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, sc, 0);
+  half2v h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, sc, 1);
+  half2v h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, sc, 2);
+  half2v h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, sc, 3);
   return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 // one word of 8 four-bit codes -> 8 exact halves; slots 0..3 = even
@@ -82,11 +84,11 @@ __device__ __forceinline__ half8 cvt_word4(uint32_t w) {
   return half8{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 // the same two code converts to bf16 (value side)
-__device__ __forceinline__ bf16x8 cvt_nib2_bf(uint32_t x) {
-  bf16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 0);
-  bf16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 1);
-  bf16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 2);
-  bf16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, 2.0f, 3);
+__device__ __forceinline__ bf16x8 cvt_nib2_bf(uint32_t x, float sc = 2.0f) {
+  bf16x2 h0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 0);
+  bf16x2 h1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 1);
+  bf16x2 h2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 2);
+  bf16x2 h3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, sc, 3);
   return bf16x8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 __device__ __forceinline__ bf16x8 cvt_word4_bf(uint32_t w) {
@@ -187,10 +189,12 @@ __device__ __forceinline__ float4 meta4(uint2 v) {
 // slot of position q (0..7) inside a 4-bit word's half8
 __device__ __forceinline__ int slot4(int q) { return (q & 1) ? 4 + (q >> 1) : (q >> 1); }
 
-// Key side: channel c' (0..31 inside a lane group's 32 channels) -> (mfma m, slot s)
+// Key side: channel c' (0..31 inside a lane group's 32 channels) -> (mfma m,
+// slot s).  1 and 3 bits use the 2-bit mapping: the one-bit order puts code
+// position p of a word in nibble plane m, nibble s of exactly this mapping.
 template <int BITS>
 __device__ __forceinline__ void k_pos(int cp, int& m, int& s) {
-  if (BITS == 2) {  // word cp/16, even/odd nibble plane, nibble index
+  if (BITS != 4) {  // word cp/16, even/odd nibble plane, nibble index
     m = 2 * (cp >> 4) + (cp & 1);
     s = (cp & 15) >> 1;
   } else {          // word cp/8
@@ -201,7 +205,7 @@ __device__ __forceinline__ void k_pos(int cp, int& m, int& s) {
 // Value side: token position p (0..15 inside a lane group's 16 tokens)
 template <int BITS>
 __device__ __forceinline__ void v_pos(int p, int& m, int& s) {
-  if (BITS == 2) {
+  if (BITS != 4) {
     m = p & 1;
     s = p >> 1;
   } else {
@@ -245,7 +249,7 @@ struct Cfg {
 // variants spill a few registers around the loop over residual slices longer
 // than one batch, which runs only for short contexts with few splits.
 template <int BITS, int R>
-constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS == 2 && R == 1) ? 3 : 2); }
+constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS <= 2 && R == 1) ? 3 : 2); }
 
 // tiles of loads in flight per wave: one (a second register set measured no
 // faster at two waves per SIMD), two for 8 heads at one wave per SIMD
@@ -261,9 +265,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   static_assert(!PG || RAG, "paged launches carry per-sequence lengths");
   using C = Cfg<BITS, R>;
   constexpr int ROWS = C::ROWS, CH = C::CH;
-  constexpr int E = 32 / BITS;
-  constexpr int W = kD / E;        // words per key row
-  constexpr int WPC = 64 / E;      // words per channel per value tile
+  constexpr int W = kD * BITS / 32;   // words per key row
+  constexpr int WPC = 2 * BITS;       // words per channel per value tile
   __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -294,7 +297,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const size_t kmp = (cap / kG) * kD * MB, vmp = cap * kNG * MB;   // plane bytes
   const rsrc_t r_ks = make_rsrc(static_cast<const char*>(a.k_scale) + plane * kmp, (uint32_t)kmp);
   const rsrc_t r_kz = make_rsrc(static_cast<const char*>(a.k_zero) + plane * kmp, (uint32_t)kmp);
-  const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD / E), (uint32_t)(cap * (kD / E) * 4));
+  const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD * BITS / 32), (uint32_t)(cap * (kD * BITS / 32) * 4));
   const rsrc_t r_vs = make_rsrc(static_cast<const char*>(a.v_scale) + plane * vmp, (uint32_t)vmp);
   const rsrc_t r_vz = make_rsrc(static_cast<const char*>(a.v_zero) + plane * vmp, (uint32_t)vmp);
   const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
@@ -379,14 +382,24 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       uint32_t lt;
       const bool ok = page_tile(tile, sp, lt);
       rkc = make_rsrc(a.k_codes + sp * P * W, (uint32_t)(P * W * 4));
-      rvc = make_rsrc(a.v_codes + sp * P * (kD / E), (uint32_t)(P * (kD / E) * 4));
+      rvc = make_rsrc(a.v_codes + sp * P * (kD * BITS / 32), (uint32_t)(P * (kD * BITS / 32) * 4));
       co = ok ? lt * C::KC_BYTES + l16 : kOut;
     }
-    if constexpr (BITS == 2) {
+    if constexpr (BITS == 1) {
+      x0 = ld16(rkc, co);
+      x1 = ld16(rvc, co);
+    } else if constexpr (BITS == 2) {
       x0 = ld16(rkc, co);
       x1 = ld16(rkc, co + 1024);
       x2 = ld16(rvc, co);
       x3 = ld16(rvc, co + 1024);
+    } else if constexpr (BITS == 3) {
+      x0 = ld16(rkc, co);
+      x1 = ld16(rkc, co + 1024);
+      x2 = ld16(rkc, co + 2048);
+      x3 = ld16(rvc, co);
+      x4 = ld16(rvc, co + 1024);
+      x5 = ld16(rvc, co + 2048);
     } else {
       x0 = ld16(rkc, co);
       x1 = ld16(rkc, co + 1024);
@@ -430,14 +443,19 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   auto stage = [&](const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
                    const uint4& x4, const uint4& x5, const uint4& x6, const uint4& x7)
       __attribute__((always_inline)) {
+    // 2*BITS loads of 1 KB: the tile's key codes, then its value codes
     uint4* d = reinterpret_cast<uint4*>(stg + l16);
     d[0] = x0;
     d[64] = x1;
-    d[128] = x2;
-    d[192] = x3;
-    if constexpr (BITS == 4) {
+    if constexpr (BITS >= 2) {
+      d[128] = x2;
+      d[192] = x3;
+    }
+    if constexpr (BITS >= 3) {
       d[256] = x4;
       d[320] = x5;
+    }
+    if constexpr (BITS == 4) {
       d[384] = x6;
       d[448] = x7;
     }
@@ -623,13 +641,27 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         for (int mb2 = 0; mb2 < 2; mb2++) {
           const int mb = 2 * g + mb2;
           float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
-          if constexpr (BITS == 2) {
-            const uint2 x = *reinterpret_cast<const uint2*>(stg + (16 * mb + n16) * W * 4 + kg * 8);
+          const char* krow = stg + (16 * mb + n16) * W * 4;   // token 16mb + n16
+          if constexpr (BITS == 1 || BITS == 3) {
+            // one-bit plane: word kg, nibble bit-planes m = 0..3 (scale 2 for
+            // 1-bit codes; for 3-bit codes the high bit, scale 8 = 4 * hi)
+            const uint32_t x = *reinterpret_cast<const uint32_t*>(
+                krow + (BITS == 3 ? 32 : 0) + kg * 4);
+            const float sc = BITS == 3 ? 8.0f : 2.0f;
+            acc = mfma(af[0], cvt_nib2(x & 0x11111111u, sc), acc);
+            acc = mfma(af[1], cvt_nib2((x >> 1) & 0x11111111u, sc), acc);
+            acc = mfma(af[2], cvt_nib2((x >> 2) & 0x11111111u, sc), acc);
+            acc = mfma(af[3], cvt_nib2((x >> 3) & 0x11111111u, sc), acc);
+          }
+          if constexpr (BITS == 2 || BITS == 3) {
+            // two-bit plane: words 2kg, 2kg + 1
+            const uint2 x = *reinterpret_cast<const uint2*>(krow + kg * 8);
             acc = mfma(af[0], cvt_nib2(x.x & 0x33333333u), acc);
             acc = mfma(af[1], cvt_nib2((x.x >> 2) & 0x33333333u), acc);
             acc = mfma(af[2], cvt_nib2(x.y & 0x33333333u), acc);
             acc = mfma(af[3], cvt_nib2((x.y >> 2) & 0x33333333u), acc);
-          } else {
+          }
+          if constexpr (BITS == 4) {
             const uint4 x = *reinterpret_cast<const uint4*>(stg + (16 * mb + n16) * W * 4 + kg * 16);
             acc = mfma(af[0], cvt_word4(x.x), acc);
             acc = mfma(af[1], cvt_word4(x.y), acc);
@@ -698,11 +730,24 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
       for (int nbj = 0; nbj < 2; nbj++) {
         const int nb = 2 * j + nbj;
-        if constexpr (BITS == 2) {
-          const uint32_t x = *reinterpret_cast<const uint32_t*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 4);
+        const char* vrow = vstg + (16 * nb + n16) * WPC * 4;   // channel 16nb + n16
+        if constexpr (BITS == 1 || BITS == 3) {
+          // one-bit plane: word kg/2 holds this lane group's 16 tokens in
+          // nibble bit-planes 2*(kg%2) (even tokens) and 2*(kg%2) + 1 (odd)
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(
+              vrow + (BITS == 3 ? 16 : 0) + (kg >> 1) * 4);
+          const float sc = BITS == 3 ? 8.0f : 2.0f;
+          const uint32_t xs = x >> (2 * (kg & 1));
+          cv[nb] = mfma_bf(av0, cvt_nib2_bf(xs & 0x11111111u, sc), cv[nb]);
+          cv[nb] = mfma_bf(av1, cvt_nib2_bf((xs >> 1) & 0x11111111u, sc), cv[nb]);
+        }
+        if constexpr (BITS == 2 || BITS == 3) {
+          // two-bit plane: word kg
+          const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + kg * 4);
           cv[nb] = mfma_bf(av0, cvt_nib2_bf(x & 0x33333333u), cv[nb]);
           cv[nb] = mfma_bf(av1, cvt_nib2_bf((x >> 2) & 0x33333333u), cv[nb]);
-        } else {
+        }
+        if constexpr (BITS == 4) {
           const uint2 x = *reinterpret_cast<const uint2*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 8);
           cv[nb] = mfma_bf(av0, cvt_word4_bf(x.x), cv[nb]);
           cv[nb] = mfma_bf(av1, cvt_word4_bf(x.y), cv[nb]);

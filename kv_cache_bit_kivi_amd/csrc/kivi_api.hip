@@ -20,7 +20,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(const kivi_shape* s) {
   if (!s) return KIVI_EINVAL;
   if (s->batch < 1 || s->num_kv_heads < 1 || s->gqa_ratio < 1) return KIVI_EINVAL;
-  if (s->bits != 2 && s->bits != 4) return KIVI_EINVAL;
+  if (s->bits < 1 || s->bits > 4) return KIVI_EINVAL;
   if (s->meta_half != 0 && s->meta_half != 1) return KIVI_EINVAL;
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;

@@ -5,7 +5,8 @@
 // token, with asymmetric low-bit codes; study.space summary: key groups span
 // consecutive tokens and new tokens are appended along the token axis.
 //
-// Codec, per group of G values (bit-exact contract, IEEE binary32, built with
+// Codec, per group of G values, b in {1, 2, 3, 4} bits (bit-exact contract,
+// IEEE binary32, built with
 // -ffp-contract=off and correctly rounded division):
 //   mn, mx   : strict-comparison scan in index order (first extremum wins);
 //   mx == mn : scale 0, zero mn, codes 0 (the group dequantizes exactly);
@@ -58,6 +59,41 @@ __device__ __forceinline__ void put_meta(void* p, size_t i, float x) {
     static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, (_Float16)x);
   else
     static_cast<float*>(p)[i] = x;
+}
+
+// Packed layout of a row of n codes (a key row: one token's D channels; a
+// value row: one channel's 64 tokens of a tile), n*BITS/32 words:
+//   2, 4 bits: position p at word p/E, bit BITS*(p%E), E = 32/BITS;
+//   1 bit    : word p/32, bit beta(p%32);
+//   3 bits   : code = lo + 4*hi; lo at word p/16, bits 2*(p%16), then the hi
+//              bits at word n/16 + p/32, bit beta(p%32).
+// beta keeps the nibble bit-planes of a one-bit word on the code positions
+// of a two-bit word's planes (the decode's operand conversion relies on it).
+__device__ __forceinline__ int beta(int p) { return 4 * ((p & 15) >> 1) + 2 * (p >> 4) + (p & 1); }
+
+// Word k (0 .. n*BITS/32 - 1) of a row from its codes: code(p) gives the code
+// of position p of the row.
+template <int BITS, class F>
+__device__ __forceinline__ uint32_t pack_word(int n, int k, F code) {
+  uint32_t w = 0;
+  if constexpr (BITS == 1) {
+#pragma unroll
+    for (int q = 0; q < 32; q++) w |= code(32 * k + q) << beta(q);
+  } else if constexpr (BITS == 3) {
+    if (k < n / 16) {
+#pragma unroll
+      for (int q = 0; q < 16; q++) w |= (code(16 * k + q) & 3u) << (2 * q);
+    } else {
+      const int kh = k - n / 16;
+#pragma unroll
+      for (int q = 0; q < 32; q++) w |= (code(32 * kh + q) >> 2) << beta(q);
+    }
+  } else {
+    constexpr int E = 32 / BITS;
+#pragma unroll
+    for (int e = 0; e < E; e++) w |= code(E * k + e) << (BITS * e);
+  }
+  return w;
 }
 
 struct NoList {};
@@ -124,18 +160,13 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
   }
   __syncthreads();
 
-  constexpr int E = 32 / BITS;
-  const int W = D / E;
+  const int W = D * BITS / 32;   // words per key row
   uint32_t* dst = codes + (ob * ocap + otok) * W;
   for (int it = threadIdx.x; it < G * W; it += blockDim.x) {
     const int i = it / W, w = it % W;
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-      const int d = w * E + e;
-      word |= encode<BITS>(h2f(tile[i * D + d]), s_sc[d], s_zr[d]) << (BITS * e);
-    }
-    dst[it] = word;
+    dst[it] = pack_word<BITS>(D, w, [&](int d) {
+      return encode<BITS>(h2f(tile[i * D + d]), s_sc[d], s_zr[d]);
+    });
   }
 }
 
@@ -193,23 +224,27 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
   }
   __syncthreads();
 
-  constexpr int E = 32 / BITS;
-  constexpr int WPB = 32 / E;   // words per channel in this 32-token block
-  constexpr int WPC = 64 / E;   // words per channel per 64-token tile
-  uint32_t* plane = codes + ob * ((size_t)ocap * D / E);
+  constexpr int WPC = 2 * BITS;   // words per channel per 64-token tile
+  uint32_t* plane = codes + ob * ((size_t)ocap * D * BITS / 32);
   const size_t tile_idx = (size_t)(t_base / 64);
-  const int word0 = (t_base % 64) / E;
-  for (int it = threadIdx.x; it < D * WPB; it += blockDim.x) {
-    const int d = it / WPB, qw = it % WPB;
+  const int half = (t_base % 64) / 32;   // this block's half of the tile
+  // the words of a channel's tile row that hold only this half's tokens: of
+  // the 2*BITS words, those whose positions all lie in [32*half, 32*half+32)
+  for (int it = threadIdx.x; it < D * BITS; it += blockDim.x) {
+    const int d = it / BITS, k = it % BITS;
     const int j = d / G;
-    uint32_t word = 0;
-#pragma unroll
-    for (int e = 0; e < E; e++) {
-      const int t = qw * E + e;
-      word |= encode<BITS>(h2f(tile[t * D + d]), s_sc[t * NG + j], s_zr[t * NG + j])
-              << (BITS * e);
+    int rw;   // row word index
+    if constexpr (BITS == 1) {
+      rw = half;
+    } else if constexpr (BITS == 3) {
+      rw = k < 2 ? 2 * half + k : 4 + half;
+    } else {
+      rw = half * BITS + k;
     }
-    plane[(tile_idx * D + d) * WPC + word0 + qw] = word;
+    plane[(tile_idx * D + d) * WPC + rw] = pack_word<BITS>(64, rw, [&](int p) {
+      const int t = p - 32 * half;   // token of this block
+      return encode<BITS>(h2f(tile[t * D + d]), s_sc[t * NG + j], s_zr[t * NG + j]);
+    });
   }
 }
 
@@ -238,6 +273,20 @@ copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restric
   }
 }
 
+// f(bits, metadata-half) with both as compile-time constants
+template <class F>
+void dispatch_bits(int bits, int mh, F f) {
+  auto with_mh = [&](auto B) {
+    if (mh) f(B, std::true_type{}); else f(B, std::false_type{});
+  };
+  switch (bits) {
+    case 1: with_mh(std::integral_constant<int, 1>{}); break;
+    case 2: with_mh(std::integral_constant<int, 2>{}); break;
+    case 3: with_mh(std::integral_constant<int, 3>{}); break;
+    default: with_mh(std::integral_constant<int, 4>{}); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G, int cap,
@@ -249,10 +298,7 @@ hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, i
     kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
                                    NoList{}, PageMap{});
   };
-  if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true, false, false>) : go(quantize_k_kernel<2, false, false, false>);
-  else
-    mh ? go(quantize_k_kernel<4, true, false, false>) : go(quantize_k_kernel<4, false, false, false>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, false, false>); });
   return hipGetLastError();
 }
 
@@ -265,10 +311,7 @@ hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, i
     kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
                                    NoList{}, PageMap{});
   };
-  if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true, false, false>) : go(quantize_v_kernel<2, false, false, false>);
-  else
-    mh ? go(quantize_v_kernel<4, true, false, false>) : go(quantize_v_kernel<4, false, false, false>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, false, false>); });
   return hipGetLastError();
 }
 
@@ -282,10 +325,7 @@ hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H,
     kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
                                    PageMap{});
   };
-  if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true, true, false>) : go(quantize_k_kernel<2, false, true, false>);
-  else
-    mh ? go(quantize_k_kernel<4, true, true, false>) : go(quantize_k_kernel<4, false, true, false>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, false>); });
   return hipGetLastError();
 }
 
@@ -299,10 +339,7 @@ hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H,
     kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
                                    PageMap{});
   };
-  if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true, true, false>) : go(quantize_v_kernel<2, false, true, false>);
-  else
-    mh ? go(quantize_v_kernel<4, true, true, false>) : go(quantize_v_kernel<4, false, true, false>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, true, false>); });
   return hipGetLastError();
 }
 
@@ -316,10 +353,7 @@ hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const
   auto go = [&](auto kernel) {
     kernel<<<grid, 256, lds, st>>>(k, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
   };
-  if (bits == 2)
-    mh ? go(quantize_k_kernel<2, true, true, true>) : go(quantize_k_kernel<2, false, true, true>);
-  else
-    mh ? go(quantize_k_kernel<4, true, true, true>) : go(quantize_k_kernel<4, false, true, true>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, true>); });
   return hipGetLastError();
 }
 
@@ -333,10 +367,7 @@ hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const
   auto go = [&](auto kernel) {
     kernel<<<grid, 256, lds, st>>>(v, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
   };
-  if (bits == 2)
-    mh ? go(quantize_v_kernel<2, true, true, true>) : go(quantize_v_kernel<2, false, true, true>);
-  else
-    mh ? go(quantize_v_kernel<4, true, true, true>) : go(quantize_v_kernel<4, false, true, true>);
+  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, true, true>); });
   return hipGetLastError();
 }
 

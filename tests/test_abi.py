@@ -58,6 +58,9 @@ def test_cache_bytes():
                   planes * cap * 4 * 4, planes * 128 * D * 2, planes * 2 * D * 2]
     rc, sz = sizes(shape(bits=4))
     assert sz[0] == planes * cap * D // 2
+    for b in (1, 3):      # one- and three-bit codes: D*b/32 words per key row
+        rc, sz = sizes(shape(bits=b))
+        assert rc == KIVI_OK and sz[0] == sz[2] == planes * cap * D * b // 8
     # binary16 metadata: half the scale / zero bytes, nothing else changes
     rc, sz16 = sizes(shape(meta_half=1))
     assert rc == KIVI_OK
@@ -68,7 +71,8 @@ def test_cache_bytes():
 
 @pytest.mark.parametrize("kw,code", [
     (dict(batch=0), KIVI_EINVAL), (dict(num_kv_heads=0), KIVI_EINVAL),
-    (dict(gqa_ratio=0), KIVI_EINVAL), (dict(bits=3), KIVI_EINVAL), (dict(bits=8), KIVI_EINVAL),
+    (dict(gqa_ratio=0), KIVI_EINVAL), (dict(bits=0), KIVI_EINVAL), (dict(bits=5), KIVI_EINVAL),
+    (dict(bits=8), KIVI_EINVAL),
     (dict(head_dim=48), KIVI_EUNSUPPORTED), (dict(group=16), KIVI_EUNSUPPORTED),
     (dict(gqa_ratio=17), KIVI_EUNSUPPORTED), (dict(head_dim=32, group=64), KIVI_ESHAPE),
     (dict(residual=48), KIVI_ESHAPE), (dict(residual=16, group=32), KIVI_ESHAPE),
@@ -101,7 +105,7 @@ def test_quantize_errors(fn):
     assert fn(s, dst=-32) == KIVI_ESHAPE
     assert fn(s, stride=32, ntok=64) == KIVI_ESHAPE
     assert fn(s, ntok=64, dst=480) == KIVI_ECAPACITY
-    assert fn(shape(bits=3)) == KIVI_EINVAL
+    assert fn(shape(bits=5)) == KIVI_EINVAL
 
 
 def cache(**kw):

@@ -50,6 +50,13 @@ SHAPES = [
     (1, 2, 2, 128, 2, 32, 32, 1984, 32),
     (1, 1, 1, 128, 2, 32, 128, 8192, 5),       # several chunks per wave
     (1, 1, 4, 128, 4, 32, 128, 4096, 128),
+    (2, 2, 1, 128, 1, 32, 128, 992, 128),      # 1-bit codes, half-filled last tile
+    (1, 3, 4, 128, 1, 32, 64, 2048, 33),
+    (2, 2, 1, 128, 3, 32, 128, 1024, 77),      # 3-bit codes
+    (1, 2, 8, 128, 3, 32, 128, 512, 40),
+    (1, 2, 2, 128, 3, 32, 32, 1984, 32),
+    (2, 2, 2, 64, 1, 64, 128, 448, 1),         # generic kernel, 1 bit
+    (3, 1, 1, 32, 3, 32, 32, 96, 31),          # generic kernel, 3 bits
 ]
 
 

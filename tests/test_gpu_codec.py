@@ -13,13 +13,12 @@ pytestmark = pytest.mark.gpu
 
 def gpu_quant(fn, x, bits, G, cap, ntok, dst, prev=None):
     B, H, T, D = x.shape
-    E = 32 // bits
     shape = make_shape(B, H, 1, D, bits, G, max(G, 32), cap)
     if fn is quantize_k:
-        codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device="cuda")
+        codes = torch.zeros((B, H, cap, D * bits // 32), dtype=torch.int32, device="cuda")
         sc = torch.zeros((B, H, cap // G, D), dtype=torch.float32, device="cuda")
     else:
-        codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device="cuda")
+        codes = torch.zeros((B, H, cap // 64, D, 2 * bits), dtype=torch.int32, device="cuda")
         sc = torch.zeros((B, H, cap, D // G), dtype=torch.float32, device="cuda")
     zr = torch.zeros_like(sc)
     fn(shape, dev(x), ntok, dst, codes, sc, zr)
@@ -46,6 +45,12 @@ CASES = [
     (4, 1, 2, 256, 128, 256, 256, 128, 384),
     (2, 2, 2, 256, 64, 128, 64, 192, 256),
     (2, 1, 4, 128, 128, 384, 384, 0, 384),
+    (1, 1, 2, 128, 32, 512, 512, 0, 512),
+    (3, 1, 2, 128, 32, 512, 512, 0, 512),
+    (1, 2, 3, 64, 32, 96, 96, 32, 192),
+    (3, 2, 3, 64, 64, 200, 128, 64, 256),
+    (3, 3, 2, 32, 32, 64, 32, 96, 128),
+    (1, 1, 2, 256, 128, 256, 256, 128, 384),
 ]
 
 
@@ -60,7 +65,7 @@ def test_quantize_random_shapes(case):
     compare(x, bits, G, cap, ntok, dst, str(case))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("lo,hi", [(-65504.0, 65504.0), (-1.0, 1.0), (0.0, 2.0 ** -14),
                                    (-3.0, -2.0 ** -20), (1000.0, 1024.0)])
 def test_exhaustive_fp16_values(bits, lo, hi):
@@ -119,8 +124,8 @@ def test_signed_zero_and_constant_groups():
     x[0, 1, 64:96, 3] = np.float16(1.0)
     x[0, 1, 70, 3] = np.nextafter(np.float16(1.0), np.float16(2.0))
     x[0, 0, :, 1::2] = np.float16(-0.0)
-    compare(x, 2, G, T, T, 0, "zeros")
-    compare(x, 4, G, T, T, 0, "zeros")
+    for bits in (1, 2, 3, 4):
+        compare(x, bits, G, T, T, 0, "zeros")
 
 
 @pytest.mark.parametrize("name,batches", [

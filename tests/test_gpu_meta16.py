@@ -20,13 +20,12 @@ SCALE = 0.0883883461356163
 
 def gpu_quant16(fn, x, bits, G, cap, ntok, dst):
     B, H, T, D = x.shape
-    E = 32 // bits
     shape = make_shape(B, H, 1, D, bits, G, max(G, 32), cap, meta_half=True)
     if fn is quantize_k:
-        codes = torch.zeros((B, H, cap, D // E), dtype=torch.int32, device="cuda")
+        codes = torch.zeros((B, H, cap, D * bits // 32), dtype=torch.int32, device="cuda")
         sc = torch.zeros((B, H, cap // G, D), dtype=torch.float16, device="cuda")
     else:
-        codes = torch.zeros((B, H, cap // 64, D, 64 // E), dtype=torch.int32, device="cuda")
+        codes = torch.zeros((B, H, cap // 64, D, 2 * bits), dtype=torch.int32, device="cuda")
         sc = torch.zeros((B, H, cap, D // G), dtype=torch.float16, device="cuda")
     zr = torch.zeros_like(sc)
     fn(shape, dev(x), ntok, dst, codes, sc, zr)
@@ -67,7 +66,7 @@ def test_quantize16_shapes(case):
     compare16(x, bits, G, cap, ntok, dst, str(case))
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 def test_quantize16_scale_rounding(bits):
     """Scales across the whole binary16 range: subnormal results (ranges of a
     few 2^-24 ulps, where the scale rounds to a multiple of 2^-24 or to
@@ -127,7 +126,7 @@ def test_decode16_shapes(shp, splits):
     assert err <= ATTN_TOL, err
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("r", [1, 4])
 def test_stream16_fused(bits, r):
     """Appends through two flushes: the fused step equals append + decode bit

@@ -10,7 +10,7 @@ from tests.gpu_util import announce, assert_cache_equal, dev, require_gpu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
 @pytest.mark.parametrize("G,R,D", [(32, 32, 64), (32, 128, 128), (64, 128, 128), (128, 128, 256)])
 def test_append_stream_small(bits, G, R, D):
     require_gpu()
