@@ -204,6 +204,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--meta", choices=["fp32", "fp16"], default="fp32",
                     help="storage of the quantization scales and zeros")
+    ap.add_argument("--bits", type=int, default=0, choices=[0, 1, 2, 3, 4],
+                    help="code width (0: the workload's own)")
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="paged quantized store with P-token pages (0: contiguous planes); the "
                          "block table is a seeded shuffle of the page pool")
@@ -222,8 +224,8 @@ def main():
     meta_half = args.meta == "fp16"
     mb = 2 if meta_half else 4
     # profiles are keyed by workload and metadata width
-    tag = (args.workload + (f"_paged{args.paged}" if args.paged else "") +
-           ("_meta16" if meta_half else ""))
+    tag = (args.workload + (f"_b{args.bits}" if args.bits else "") +
+           (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
         pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
@@ -248,6 +250,8 @@ def main():
     lib()  # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
     w = synth.WORKLOADS[args.workload]
+    if args.bits:
+        w = w.with_(bits=args.bits)
     B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
                               w.residual)
     NL = args.layers
