@@ -13,6 +13,7 @@ from .oracle import (  # noqa: F401
     half_to_float,
     load,
     meta_dtype,
+    outlier_shape,
     quantize_k,
     quantize_v,
 )

@@ -15,6 +15,9 @@
  *               paragraph, no headings).
  *   [KIVI-quo]  scholarfeed.org "KIVI" quote page (one-line quotes from other
  *               papers about the method).
+ *   [KVQ-abs]   "KVQuant: Towards 10 Million Context Length LLM Inference with
+ *               KV Cache Quantization", codewithpapers.app paper page,
+ *               abstract (per-vector dense-and-sparse quantization).
  *
  * What the pages fix, restated:
  *   - keys are quantized per channel: one group is one channel over a run
@@ -41,6 +44,16 @@
  *   - attention: softmax(scale * q . k_t) over every cached token, no mask,
  *     in binary64 on the dequantized keys and values; a GQA query head hq
  *     reads KV head hq / r.
+ *   - key outliers (optional, n_out > 0) [KVQ-abs: outliers are isolated per
+ *     vector so that they do not stretch the quantization range]: the
+ *     "vector" is one key group (one channel over G tokens, the range that
+ *     an outlier would stretch); its n_out entries of largest magnitude
+ *     (|x| of the binary16 input; equal magnitudes: the lower position
+ *     first) form the sparse part and are kept exactly; the other G - n_out
+ *     entries form the dense part, quantized as above with min and max taken
+ *     over them alone; outlier positions get code 0 in the dense codes; a
+ *     dequantized outlier position is its kept value.  No calibration: a
+ *     fixed count per group, chosen from the group itself.
  *
  * Packed layout (the library's documented storage contract, re-implemented
  * here independently from its description).  Codes are stored in "rows" of
@@ -60,6 +73,11 @@
  *   K scale/zero : [B][H][cap/G][D] binary32.
  *   V scale/zero : [B][H][cap][D/G] binary32.
  *   residual K/V : [B][H][R][D] binary16.
+ *   K outliers : [B][H][cap/G][n_out][D] words, a compressed sparse row
+ *             store with rows of fixed length n_out (so the row offsets are
+ *             implicit): row (group g, channel d) is words [g][0..n_out)[d],
+ *             each (i << 16) | binary16 bits of the value at position i of
+ *             the group, in increasing i.
  *
  * Build: gcc -O2 -fno-fast-math -ffp-contract=off -shared -fPIC (x86-64 SSE
  * arithmetic, no excess precision).
@@ -190,11 +208,16 @@ static void meta_put(void* a, size_t m, float v, int meta_half) {
 
 /* Quantize one group of n binary32 values (already widened from binary16).
  * Writes n codes and the group's scale and zero.  The order of operations is
- * the reading stated in the file header. */
-static void quantize_group(const float* xs, int n, int bits, uint8_t* codes,
-                           float* scale_out, float* zero_out) {
-  float mn = xs[0], mx = xs[0];
-  for (int i = 1; i < n; i++) {
+ * the reading stated in the file header.  skip (NULL = none) marks the
+ * positions left out of the dense part (key outliers): min and max are taken
+ * over the other positions only, and skipped positions get code 0. */
+static void quantize_group(const float* xs, int n, int bits, const uint8_t* skip,
+                           uint8_t* codes, float* scale_out, float* zero_out) {
+  int first = 0;
+  while (skip && skip[first]) first++;
+  float mn = xs[first], mx = xs[first];
+  for (int i = first + 1; i < n; i++) {
+    if (skip && skip[i]) continue;
     if (xs[i] < mn) mn = xs[i];
     if (xs[i] > mx) mx = xs[i];
   }
@@ -209,6 +232,10 @@ static void quantize_group(const float* xs, int n, int bits, uint8_t* codes,
   float s = range / qmax;     /* one binary32 rounding */
   float z = mn;
   for (int i = 0; i < n; i++) {
+    if (skip && skip[i]) {
+      codes[i] = 0;
+      continue;
+    }
     float u = xs[i] - z;      /* one rounding, u >= 0 */
     float v = u / s;          /* one rounding */
     float c = rintf(v);       /* round half to even (default mode) */
@@ -217,6 +244,29 @@ static void quantize_group(const float* xs, int n, int bits, uint8_t* codes,
   }
   *scale_out = s;
   *zero_out = z;
+}
+
+/* The n_out positions of largest |x| in a group of n (equal magnitudes: the
+ * lower position first), marked in skip[] and listed in pos[] in increasing
+ * order [KVQ-abs; the selection rule is the reading in the file header]. */
+static void select_outliers(const float* xs, int n, int n_out, uint8_t* skip, int* pos) {
+  for (int i = 0; i < n; i++) skip[i] = 0;
+  for (int j = 0; j < n_out; j++) {
+    int best = -1;
+    float best_mag = -1.0f;
+    for (int i = 0; i < n; i++) {
+      if (skip[i]) continue;
+      float a = fabsf(xs[i]);
+      if (a > best_mag) { /* strict: the first of equal magnitudes stays */
+        best_mag = a;
+        best = i;
+      }
+    }
+    skip[best] = 1;
+  }
+  int m = 0;
+  for (int i = 0; i < n; i++)
+    if (skip[i]) pos[m++] = i;
 }
 
 static int check_common(int B, int H, int D, int bits, int G, int cap) {
@@ -230,18 +280,22 @@ static int check_common(int B, int H, int D, int bits, int G, int cap) {
 
 /* Key quantization, per channel over groups of G consecutive tokens
  * [KIVI-abs, KIVI-sum].  Source tokens [0, ntok) of k ([B][H][in_stride][D]
- * binary16) go to cache tokens [dst_off, dst_off + ntok). */
+ * binary16) go to cache tokens [dst_off, dst_off + ntok).  With n_out > 0
+ * each group also isolates its n_out outliers into `outl` (layout and rule
+ * in the file header) [KVQ-abs]. */
 int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap, int meta_half,
                      const uint16_t* k, int in_stride, int ntok, int dst_off,
-                     uint32_t* codes, void* scale, void* zero) {
+                     uint32_t* codes, void* scale, void* zero, int n_out, uint32_t* outl) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
+  if (n_out < 0 || n_out >= G || (n_out > 0 && !outl)) return KIVIO_EINVAL;
   if (ntok < 1 || ntok % G || dst_off < 0 || dst_off % G || in_stride < ntok)
     return KIVIO_ESHAPE;
   if (dst_off + ntok > cap) return KIVIO_ECAPACITY;
   const int W = words_per_row(D, bits);
   float xs[1024];
-  uint8_t cs[1024];
+  uint8_t cs[1024], skip[1024];
+  int pos[1024];
   if (G > 1024) return KIVIO_ESHAPE;
   for (int b = 0; b < B; b++)
     for (int h = 0; h < H; h++) {
@@ -255,9 +309,16 @@ int kivio_quantize_k(int B, int H, int D, int bits, int G, int cap, int meta_hal
         for (int d = 0; d < D; d++) {
           for (int i = 0; i < G; i++)
             xs[i] = kivio_half_to_float(src[(size_t)(g * G + i) * D + d]);
-          float s, z;
-          quantize_group(xs, G, bits, cs, &s, &z);
           int gg = (dst_off / G) + g;
+          if (n_out > 0) {
+            select_outliers(xs, G, n_out, skip, pos);
+            uint32_t* row = outl + (mbase + (size_t)gg * D) * n_out;  /* [gg][j][d] */
+            for (int j = 0; j < n_out; j++)
+              row[(size_t)j * D + d] =
+                  ((uint32_t)pos[j] << 16) | src[(size_t)(g * G + pos[j]) * D + d];
+          }
+          float s, z;
+          quantize_group(xs, G, bits, n_out > 0 ? skip : NULL, cs, &s, &z);
           meta_put(scale, mbase + (size_t)gg * D + d, s, meta_half);
           meta_put(zero, mbase + (size_t)gg * D + d, z, meta_half);
           for (int i = 0; i < G; i++) {
@@ -305,7 +366,7 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
           for (int i = 0; i < G; i++)
             xs[i] = kivio_half_to_float(src[(size_t)t * D + j * G + i]);
           float s, z;
-          quantize_group(xs, G, bits, cs, &s, &z);
+          quantize_group(xs, G, bits, NULL, cs, &s, &z);
           int tt = dst_off + t;
           meta_put(scale, mbase + (size_t)tt * NG + j, s, meta_half);
           meta_put(zero, mbase + (size_t)tt * NG + j, z, meta_half);
@@ -323,20 +384,23 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
  * fixed-length residual of recent tokens].  Reading: when a token arrives
  * and the residual already holds R tokens, all R are quantized into the
  * grouped part first (keys and values alike), then the new token is stored
- * in the residual.  *tq, *tr are updated only on success. */
+ * in the residual.  *tq, *tr are updated only on success.  A flush isolates
+ * key outliers as kivio_quantize_k does (n_out, k_outl). */
 int kivio_append(int B, int H, int D, int bits, int G, int R, int cap, int meta_half,
                  uint32_t* k_codes, void* ks, void* kz, uint32_t* v_codes,
                  void* vs, void* vz, uint16_t* k_res, uint16_t* v_res,
                  const uint16_t* k_new, const uint16_t* v_new, int* tq,
-                 int* tr) {
+                 int* tr, int n_out, uint32_t* k_outl) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (R < G || R % G) return KIVIO_ESHAPE;
+  if (n_out < 0 || n_out >= G || (n_out > 0 && !k_outl)) return KIVIO_EINVAL;
   int q = *tq, r = *tr;
   if (q < 0 || q % G || r < 0 || r > R) return KIVIO_ESHAPE;
   if (r == R) {
     if (q + R > cap) return KIVIO_ECAPACITY;
-    rc = kivio_quantize_k(B, H, D, bits, G, cap, meta_half, k_res, R, R, q, k_codes, ks, kz);
+    rc = kivio_quantize_k(B, H, D, bits, G, cap, meta_half, k_res, R, R, q, k_codes, ks, kz,
+                          n_out, k_outl);
     if (rc) return rc;
     rc = kivio_quantize_v(B, H, D, bits, G, cap, meta_half, v_res, R, R, q, v_codes, vs, vz);
     if (rc) return rc;
@@ -357,9 +421,15 @@ int kivio_append(int B, int H, int D, int bits, int G, int R, int cap, int meta_
 }
 
 /* dequantized key / value of cache token t (< tq), channel d, in binary64 */
-/* (sc, zr point at the plane's metadata; mb is the plane's element offset) */
+/* (sc, zr point at the plane's metadata; mb is the plane's element offset;
+ * ow, n_out: the plane's key outliers, row (t/G, d), if any) */
 static double dequant_k(const uint32_t* cw, const void* sc, const void* zr, size_t mb,
-                        int meta_half, int D, int bits, int G, int t, int d) {
+                        int meta_half, int D, int bits, int G, int t, int d,
+                        const uint32_t* ow, int n_out) {
+  for (int j = 0; j < n_out; j++) {
+    uint32_t w = ow[((size_t)(t / G) * n_out + j) * D + d];
+    if ((int)(w >> 16) == t % G) return (double)kivio_half_to_float((uint16_t)(w & 0xffffu));
+  }
   const int W = words_per_row(D, bits);
   uint32_t c = row_get(cw + (size_t)t * W, D, bits, d);
   size_t m = mb + (size_t)(t / G) * D + d;
@@ -375,16 +445,19 @@ static double dequant_v(const uint32_t* cw, const void* sc, const void* zr, size
 
 /* Decode attention over the mixed cache [KIVI-sum: scores on the grouped
  * part, then the residual part is combined with it], binary64 throughout.
- * q, out: [B][H*r][D].  Work space: 2*(tq+tr) doubles in `scratch`. */
+ * q, out: [B][H*r][D].  Work space: 2*(tq+tr) doubles in `scratch`.  Keys
+ * with isolated outliers (n_out > 0) dequantize through k_outl [KVQ-abs]. */
 int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
                       int cap, int meta_half, const uint32_t* k_codes, const void* ks,
                       const void* kz, const uint32_t* v_codes,
                       const void* vs, const void* vz, const uint16_t* k_res,
                       const uint16_t* v_res, int tq, int tr, const uint16_t* q,
-                      float softmax_scale, double* out, double* scratch) {
+                      float softmax_scale, double* out, double* scratch,
+                      int n_out, const uint32_t* k_outl) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (r < 1) return KIVIO_EINVAL;
+  if (n_out < 0 || n_out >= G || (n_out > 0 && !k_outl)) return KIVIO_EINVAL;
   if (tq < 0 || tq % G || tq > cap || tr < 0 || tr > R || tq + tr < 1)
     return KIVIO_ESHAPE;
   const int Hq = H * r, W = words_per_row(D, bits);
@@ -397,6 +470,7 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       const size_t bh = (size_t)b * H + h;
       const uint32_t* kc = k_codes + bh * (size_t)cap * W;
       const size_t kmb = bh * (size_t)(cap / G) * D;
+      const uint32_t* ko = n_out > 0 ? k_outl + kmb * n_out : NULL;
       const uint32_t* vc = v_codes + bh * (size_t)cap * D * bits / 32;
       const size_t vmb = bh * (size_t)cap * (D / G);
       const uint16_t* kr = k_res + bh * (size_t)R * D;
@@ -405,7 +479,8 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       for (int t = 0; t < L; t++) {
         double dot = 0.0;
         for (int d = 0; d < D; d++) {
-          double kv = (t < tq) ? dequant_k(kc, ks, kz, kmb, meta_half, D, bits, G, t, d)
+          double kv = (t < tq) ? dequant_k(kc, ks, kz, kmb, meta_half, D, bits, G, t, d,
+                                           ko, n_out)
                                : (double)kivio_half_to_float(kr[(size_t)(t - tq) * D + d]);
           dot += (double)kivio_half_to_float(qv[d]) * kv;
         }

@@ -57,16 +57,17 @@ def load():
     lib.kivio_float_to_half.argtypes = [ctypes.c_float]
     lib.kivio_float_to_half.restype = ctypes.c_uint16
     q_args = [_int] * 7 + [_u16p, _int, _int, _int, _u32p, _vp, _vp]
-    lib.kivio_quantize_k.argtypes = q_args
+    lib.kivio_quantize_k.argtypes = q_args + [_int, _u32p]
     lib.kivio_quantize_v.argtypes = q_args
     lib.kivio_quantize_k.restype = _int
     lib.kivio_quantize_v.restype = _int
     lib.kivio_append.argtypes = [_int] * 8 + [_u32p, _vp, _vp, _u32p, _vp, _vp,
-                                             _u16p, _u16p, _u16p, _u16p, _i32p, _i32p]
+                                             _u16p, _u16p, _u16p, _u16p, _i32p, _i32p,
+                                             _int, _u32p]
     lib.kivio_append.restype = _int
     lib.kivio_decode_attn.argtypes = [_int] * 9 + [_u32p, _vp, _vp, _u32p, _vp,
                                                    _vp, _u16p, _u16p, _int, _int, _u16p,
-                                                   ctypes.c_float, _f64p, _f64p]
+                                                   ctypes.c_float, _f64p, _f64p, _int, _u32p]
     lib.kivio_decode_attn.restype = _int
     _lib = lib
     return lib
@@ -114,19 +115,31 @@ def code_words_k(cap: int, D: int, bits: int) -> int:
     return cap * D * bits // 32
 
 
-def _quantize(fn, x, bits, G, cap, ntok, dst_off, codes, scale, zero, meta_half):
+def _quantize(fn, x, bits, G, cap, ntok, dst_off, codes, scale, zero, meta_half, *extra):
     x = _h(x)
     B, H, in_stride, D = x.shape
     _check(fn(B, H, D, bits, G, cap, int(meta_half), _p(x, ctypes.c_uint16, np.uint16),
               in_stride, ntok, dst_off, _p(codes, ctypes.c_uint32, np.uint32),
-              _m(scale, meta_half), _m(zero, meta_half)))
+              _m(scale, meta_half), _m(zero, meta_half), *extra))
+
+
+def _outl(a):
+    """Pointer to a key-outlier array, or NULL."""
+    return None if a is None else _p(a, ctypes.c_uint32, np.uint32)
+
+
+def outlier_shape(B, H, cap, G, n_out, D):
+    """Key-outlier store [B][H][cap/G][n_out][D] (uint32 words)."""
+    return (B, H, cap // G, n_out, D)
 
 
 def quantize_k(k, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, zero=None,
-               meta_half=False):
+               meta_half=False, n_out=0, outl=None):
     """Quantize keys k[B][H][T][D] (binary16) tokens [0, ntok) into a store of
     capacity cap at token offset dst_off.  Returns (codes, scale, zero); scale
-    and zero are binary32, or binary16 bits (uint16) when meta_half."""
+    and zero are binary32, or binary16 bits (uint16) when meta_half.  With
+    n_out > 0 each key group's n_out outliers go to ``outl`` (allocated when
+    None; returned as a fourth element)."""
     k = _h(k)
     B, H, T, D = k.shape
     ntok = T if ntok is None else ntok
@@ -134,8 +147,12 @@ def quantize_k(k, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, ze
         codes = np.zeros((B, H, cap, D * bits // 32), np.uint32)
         scale = np.zeros((B, H, cap // G, D), meta_dtype(meta_half))
         zero = np.zeros((B, H, cap // G, D), meta_dtype(meta_half))
+    if n_out and outl is None:
+        outl = np.zeros(outlier_shape(B, H, cap, G, n_out, D), np.uint32)
     _quantize(load().kivio_quantize_k, k, bits, G, cap, ntok, dst_off, codes, scale, zero,
-              meta_half)
+              meta_half, int(n_out), _outl(outl if n_out else None))
+    if n_out:
+        return codes, scale, zero, outl
     return codes, scale, zero
 
 
@@ -167,6 +184,7 @@ class OracleCache:
     R: int
     cap: int
     meta_half: bool = False
+    n_out: int = 0          # key outliers per key group (0: none)
     tq: int = 0
     tr: int = 0
     k_codes: np.ndarray = field(default=None, repr=False)
@@ -177,6 +195,7 @@ class OracleCache:
     vz: np.ndarray = field(default=None, repr=False)
     k_res: np.ndarray = field(default=None, repr=False)
     v_res: np.ndarray = field(default=None, repr=False)
+    k_outl: np.ndarray = field(default=None, repr=False)
     flushes: int = 0
 
     def __post_init__(self):
@@ -190,6 +209,8 @@ class OracleCache:
         self.vz = np.zeros((B, H, cap, D // G), md)
         self.k_res = np.zeros((B, H, R, D), np.uint16)
         self.v_res = np.zeros((B, H, R, D), np.uint16)
+        self.k_outl = (np.zeros(outlier_shape(B, H, cap, G, self.n_out, D), np.uint32)
+                       if self.n_out else None)
 
     def prefill(self, k, v, tq):
         """Quantize tokens [0, tq) and keep tokens [tq, T) in the residual."""
@@ -199,7 +220,7 @@ class OracleCache:
             raise OracleError("ESHAPE")
         if tq:
             quantize_k(k, self.bits, self.G, self.cap, tq, 0, self.k_codes, self.ks, self.kz,
-                       self.meta_half)
+                       self.meta_half, self.n_out, self.k_outl)
             quantize_v(v, self.bits, self.G, self.cap, tq, 0, self.v_codes, self.vs, self.vz,
                        self.meta_half)
         self.k_res[:, :, : T - tq] = k[:, :, tq:]
@@ -218,7 +239,7 @@ class OracleCache:
             _p(self.v_codes, ctypes.c_uint32, np.uint32), _m(self.vs, mh), _m(self.vz, mh),
             _p(self.k_res, ctypes.c_uint16, np.uint16), _p(self.v_res, ctypes.c_uint16, np.uint16),
             _p(k_new, ctypes.c_uint16, np.uint16), _p(v_new, ctypes.c_uint16, np.uint16),
-            ctypes.byref(tq), ctypes.byref(tr)))
+            ctypes.byref(tq), ctypes.byref(tr), int(self.n_out), _outl(self.k_outl)))
         self.tq, self.tr = tq.value, tr.value
         if self.tq != before:
             self.flushes += 1
@@ -240,5 +261,6 @@ def decode_attn(c: OracleCache, q, softmax_scale):
         _p(c.v_codes, ctypes.c_uint32, np.uint32), _m(c.vs, mh), _m(c.vz, mh),
         _p(c.k_res, ctypes.c_uint16, np.uint16), _p(c.v_res, ctypes.c_uint16, np.uint16),
         c.tq, c.tr, _p(q, ctypes.c_uint16, np.uint16), float(softmax_scale),
-        _p(out, ctypes.c_double, np.float64), _p(scratch, ctypes.c_double, np.float64)))
+        _p(out, ctypes.c_double, np.float64), _p(scratch, ctypes.c_double, np.float64),
+        int(c.n_out), _outl(c.k_outl)))
     return out

@@ -67,6 +67,32 @@ def dequant_v(codes, scale, zero, bits, G, tq, D):
     return c * s + z
 
 
+def unpack_outliers(outl: np.ndarray):
+    """Key-outlier store [B][H][cap/G][n_out][D] uint32 -> (positions, values):
+    positions inside the group (word >> 16) and binary16 values (low half),
+    both [B][H][cap/G][n_out][D] (the documented word format)."""
+    w = outl.astype(np.uint32)
+    pos = (w >> 16).astype(np.int64)
+    val = (w & 0xFFFF).astype(np.uint16).view(np.float16)
+    return pos, val
+
+
+def dequant_k_sparse(codes, scale, zero, outl, bits, G, tq, D):
+    """Dense dequantization, then every listed outlier (group g, channel d,
+    position i) replaces the value of token g*G + i, channel d."""
+    k = dequant_k(codes, scale, zero, bits, G, tq, D)
+    if outl is None:
+        return k
+    pos, val = unpack_outliers(outl)
+    B, H, NGk, n_out, _ = outl.shape
+    for g in range(tq // G):
+        for j in range(n_out):
+            t = g * G + pos[:, :, g, j, :]                       # [B][H][D]
+            bi, hi, di = np.meshgrid(np.arange(B), np.arange(H), np.arange(D), indexing="ij")
+            k[bi, hi, t, di] = val[:, :, g, j, :].astype(np.float64)
+    return k
+
+
 def attention_f64(q, k, v, scale):
     """Plain softmax attention.  q [B][Hq][D], k/v [B][Hkv][T][D] (any float
     dtype), query head h reads kv head h // (Hq/Hkv).  Returns float64."""
