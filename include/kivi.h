@@ -22,6 +22,16 @@
  * input, is exact; s never overflows since it is at most 131008/3).
  * Dequantization always uses the stored values.
  *
+ * Key outliers (kivi_shape.outliers = n > 0; "KVQuant: Towards 10 Million
+ * Context Length LLM Inference with KV Cache Quantization", codewithpapers.app
+ * paper page, abstract: outliers are isolated separately for each vector so
+ * that they do not stretch the quantization range).  Here the vector is one
+ * key group (one channel over G tokens).  Its n entries of largest magnitude
+ * (equal magnitudes: the lower token first) are kept exactly in a sparse
+ * store; the other G - n entries are quantized by the formula above with min
+ * and max taken over them alone; outlier positions carry code 0 and
+ * dequantize to their kept value.  Selection uses no calibration data.
+ *
  * Conventions for every function below:
  *   - All buffer pointers are DEVICE pointers (hipMalloc'd or torch CUDA
  *     tensors), owned by the caller; the library never allocates, frees,
@@ -50,6 +60,11 @@
  *   k_res, v_res : fp16 [B][Hkv][R][D]; residual slot i holds cache token
  *             tq + i.
  *   queries / outputs : fp16 [B][Hkv*r][D]; query head h reads KV head h/r.
+ *   k_outliers (outliers = n > 0): uint32 [B][Hkv][cap/G][n][D], a
+ *             compressed-sparse-row store with rows of fixed length n (row
+ *             offsets implicit): the row of (group g, channel d) is words
+ *             [g][0..n)[d], each (i << 16) | fp16 bits of the key at token
+ *             g*G + i, in increasing i.
  */
 #ifndef KIVI_H
 #define KIVI_H
@@ -63,7 +78,7 @@ extern "C" {
 
 enum kivi_status {
   KIVI_OK = 0,
-  KIVI_EINVAL = 1,       /* null pointer, bits not in {2,4}, a count < 1    */
+  KIVI_EINVAL = 1,       /* null pointer, bits not in 1..4, a count < 1     */
   KIVI_ESHAPE = 2,       /* sizes inconsistent (see each function)          */
   KIVI_EALIGN = 3,       /* a buffer pointer not 16-byte aligned            */
   KIVI_ECAPACITY = 4,    /* the quantized store would overflow `capacity`   */
@@ -75,7 +90,7 @@ enum kivi_status {
 /* Static configuration of one cache (one attention layer).
  * Constraints (KIVI_ESHAPE unless noted):
  *   batch, num_kv_heads, gqa_ratio >= 1 (KIVI_EINVAL);
- *   bits in {2, 4} (KIVI_EINVAL);
+ *   bits in {1, 2, 3, 4} (KIVI_EINVAL);
  *   head_dim in {32, 64, 128, 256}, group in {32, 64, 128}, group divides
  *     head_dim (KIVI_EUNSUPPORTED for other head_dim/group values);
  *   residual >= group and a multiple of group;
@@ -83,7 +98,10 @@ enum kivi_status {
  *   gqa_ratio <= 16;
  *   meta_half in {0, 1} (KIVI_EINVAL): 0 = binary32 scale / zero, 1 =
  *     binary16 (half the metadata bytes; a zero-initialised shape keeps
- *     binary32). */
+ *     binary32);
+ *   outliers in 0..8 and < group (KIVI_EINVAL): key outliers isolated per
+ *     key group (0, the zero-initialised value, = none; every cache then
+ *     needs its k_outliers buffer). */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -94,6 +112,7 @@ typedef struct {
   int32_t residual;
   int32_t capacity;
   int32_t meta_half;
+  int32_t outliers;
 } kivi_shape;
 
 /* One mixed-precision cache: device buffers (layouts above) plus the host-side
@@ -111,6 +130,7 @@ typedef struct {
   uint16_t* v_res;
   int32_t tq;
   int32_t tr;
+  uint32_t* k_outliers;   /* shape.outliers > 0 only (NULL otherwise) */
 } kivi_cache;
 
 /* Bytes of each cache buffer for a shape (host arithmetic only, no HIP call).
@@ -118,6 +138,13 @@ typedef struct {
 int kivi_cache_bytes(const kivi_shape* shape, size_t* k_codes, size_t* k_meta,
                      size_t* v_codes, size_t* v_meta, size_t* residual,
                      size_t* query);
+
+/* Bytes of the key-outlier store of a shape: the contiguous layout above
+ * when page_tokens == 0, else a page pool of num_pages pages of page_tokens
+ * tokens ([num_pages][Hkv][page_tokens/G][n][D] words).  0 bytes when
+ * shape.outliers == 0.  Host arithmetic only. */
+int kivi_outlier_bytes(const kivi_shape* shape, int32_t page_tokens,
+                       int32_t num_pages, size_t* bytes);
 
 /* Per-channel key quantization ("KIVI...", Abstract: keys are grouped along
  * the channel dimension; study.space summary: the key groups span tokens).
@@ -132,6 +159,17 @@ int kivi_quantize_k(const kivi_shape* shape, const uint16_t* k,
                     int32_t in_tok_stride, int32_t ntok,
                     int32_t dst_tok_offset, uint32_t* codes, void* scale,
                     void* zero, void* stream);
+
+/* kivi_quantize_k with key outliers isolated (KVQuant page, abstract; the
+ * rule at the top of this file): also writes the rows of the quantized
+ * groups into `outliers` (layout of k_outliers above).  Requires
+ * shape->outliers > 0 and outliers non-NULL (KIVI_EINVAL); kivi_quantize_k
+ * requires shape->outliers == 0 (KIVI_EINVAL). */
+int kivi_quantize_k_outliers(const kivi_shape* shape, const uint16_t* k,
+                             int32_t in_tok_stride, int32_t ntok,
+                             int32_t dst_tok_offset, uint32_t* codes,
+                             void* scale, void* zero, uint32_t* outliers,
+                             void* stream);
 
 /* Per-token value quantization ("KIVI...", Abstract: values are quantized
  * per token).  Same arguments and rules as kivi_quantize_k; each (token,
@@ -181,7 +219,13 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
  *   (0 = automatic); workspace: device scratch of at least
  *   kivi_decode_workspace_bytes(shape, num_splits) bytes (may be NULL when
  *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  Results are
- *   deterministic for a fixed split count (no floating-point atomics). */
+ *   deterministic for a fixed split count (no floating-point atomics in
+ *   global memory; with key outliers, each wave adds its tile's outlier score
+ *   corrections into its own LDS score buffer in a fixed instruction order).
+ * Key outliers (shape.outliers > 0): quantized keys are dequantized through
+ *   cache->k_outliers (the kept value replaces the dense one); the
+ *   matrix-core kernel handles outliers <= 2, larger counts use the generic
+ *   kernel. */
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q,
                      float softmax_scale, uint16_t* out, void* workspace,
                      size_t workspace_bytes, int32_t num_splits,
@@ -231,6 +275,7 @@ typedef struct {
   uint16_t* v_res;
   int32_t* tq;       /* host [batch] */
   int32_t* tr;       /* host [batch] */
+  uint32_t* k_outliers;   /* shape.outliers > 0 only */
 } kivi_ragged_cache;
 
 /* Fill an empty ragged cache from padded prompts.  k, v: fp16
@@ -287,6 +332,7 @@ int kivi_ragged_append_decode_attn(kivi_ragged_cache* cache,
  *   k_scale, k_zero : meta [num_pages][Hkv][P/G][D]
  *   v_codes : uint32 [num_pages][Hkv][P/64][D][64/E]
  *   v_scale, v_zero : meta [num_pages][Hkv][P][D/G]
+ *   k_outliers : uint32 [num_pages][Hkv][P/G][n][D] (outliers = n > 0)
  * Logical token t of sequence b is token t mod P of page
  * block_table[b * (capacity / P) + t / P].  The residual stays one
  * fixed-length pool per sequence: k_res, v_res fp16 [B][Hkv][R][D].
@@ -316,6 +362,7 @@ typedef struct {
   const int32_t* block_table;   /* device [batch][capacity / page_tokens] */
   int32_t* tq;                  /* host [batch] */
   int32_t* tr;                  /* host [batch] */
+  uint32_t* k_outliers;         /* pool, shape.outliers > 0 only */
 } kivi_paged_cache;
 
 /* Bytes of each page pool for a shape, page size and page count (host

@@ -30,7 +30,7 @@ STATUS_NAMES = {
 class kivi_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_kv_heads", "gqa_ratio", "head_dim", "bits", "group", "residual",
-        "capacity", "meta_half")]
+        "capacity", "meta_half", "outliers")]
 
 
 class kivi_cache(ctypes.Structure):
@@ -40,6 +40,7 @@ class kivi_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
         ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
         ("tq", ctypes.c_int32), ("tr", ctypes.c_int32),
+        ("k_outliers", ctypes.c_void_p),
     ]
 
 
@@ -50,6 +51,7 @@ class kivi_ragged_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
         ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
         ("tq", ctypes.POINTER(ctypes.c_int32)), ("tr", ctypes.POINTER(ctypes.c_int32)),
+        ("k_outliers", ctypes.c_void_p),
     ]
 
 
@@ -62,6 +64,7 @@ class kivi_paged_cache(ctypes.Structure):
         ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
         ("block_table", ctypes.c_void_p),
         ("tq", ctypes.POINTER(ctypes.c_int32)), ("tr", ctypes.POINTER(ctypes.c_int32)),
+        ("k_outliers", ctypes.c_void_p),
     ]
 
 
@@ -75,7 +78,10 @@ _I32P = ctypes.POINTER(ctypes.c_int32)
 _PP = ctypes.POINTER(kivi_paged_cache)
 PROTOTYPES = {
     "kivi_cache_bytes": (ctypes.c_int, [_SHP, _SZP, _SZP, _SZP, _SZP, _SZP, _SZP]),
+    "kivi_outlier_bytes": (ctypes.c_int, [_SHP, _i32, _i32, _SZP]),
     "kivi_quantize_k": (ctypes.c_int, [_SHP, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "kivi_quantize_k_outliers": (ctypes.c_int, [_SHP, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                                _vp]),
     "kivi_quantize_v": (ctypes.c_int, [_SHP, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kivi_prefill": (ctypes.c_int, [_CP, _vp, _vp, _i32, _i32, _vp]),
     "kivi_append": (ctypes.c_int, [_CP, _vp, _vp, _vp]),
@@ -141,7 +147,9 @@ def _fn(name):
 
 
 kivi_cache_bytes = _fn("kivi_cache_bytes")
+kivi_outlier_bytes = _fn("kivi_outlier_bytes")
 kivi_quantize_k = _fn("kivi_quantize_k")
+kivi_quantize_k_outliers = _fn("kivi_quantize_k_outliers")
 kivi_quantize_v = _fn("kivi_quantize_v")
 kivi_prefill = _fn("kivi_prefill")
 kivi_append = _fn("kivi_append")

@@ -24,22 +24,39 @@ def _stream() -> int:
 
 
 def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-               meta_half=False) -> kivi_shape:
+               meta_half=False, outliers=0) -> kivi_shape:
     return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                      int(bool(meta_half)))
+                      int(bool(meta_half)), int(outliers))
+
+
+def _outlier_store(shape: kivi_shape, lead: int, tokens: int, page_tokens: int, num_pages: int,
+                   dev) -> torch.Tensor | None:
+    """Key-outlier store [lead][H][tokens/G][n][D] (int32 words), or None."""
+    n = shape.outliers
+    if n == 0:
+        return None
+    nbytes = ctypes.c_size_t()
+    check(_lib.kivi_outlier_bytes(ctypes.byref(shape), page_tokens, num_pages,
+                                  ctypes.byref(nbytes)), "kivi_outlier_bytes")
+    t = torch.zeros((lead, shape.num_kv_heads, tokens // shape.group, n, shape.head_dim),
+                    dtype=torch.int32, device=dev)
+    assert t.nbytes == nbytes.value
+    return t
 
 
 class KiviCache:
     """One layer's cache: packed K/V codes, scale/zero (fp32, or fp16 when
-    meta_half), fp16 residual.
+    meta_half), fp16 residual, and with ``outliers`` > 0 the key-outlier
+    store (that many kept keys per key group and channel).
 
     Layouts are those of include/kivi.h; the host keeps (tq, tr)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 device="cuda", meta_half=False):
+                 device="cuda", meta_half=False, outliers=0):
         self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                                meta_half)
+                                meta_half, outliers)
         self.meta_half = bool(meta_half)
+        self.outliers = int(outliers)
         mdt = torch.float16 if meta_half else torch.float32
         sizes = [ctypes.c_size_t() for _ in range(6)]
         check(_lib.kivi_cache_bytes(ctypes.byref(self.shape), *[ctypes.byref(s) for s in sizes]),
@@ -59,9 +76,10 @@ class KiviCache:
         assert self.v_codes.numel() * 4 == sizes[2].value
         assert self.v_scale.nbytes == sizes[3].value
         assert self.k_res.numel() * 2 == sizes[4].value
+        self.k_outliers = _outlier_store(self.shape, B, cap, 0, 0, dev)
         self.c = kivi_cache(self.shape, *[t.data_ptr() for t in (
             self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
-            self.k_res, self.v_res)], 0, 0)
+            self.k_res, self.v_res)], 0, 0, _ptr(self.k_outliers))
         self.workspace = None
 
     # lengths live on the host, inside the C struct
@@ -133,7 +151,15 @@ class KiviCache:
         return s
 
 
-def quantize_k(shape: kivi_shape, k: torch.Tensor, ntok: int, dst_off: int, codes, scale, zero):
+def quantize_k(shape: kivi_shape, k: torch.Tensor, ntok: int, dst_off: int, codes, scale, zero,
+               outliers: torch.Tensor | None = None):
+    """kivi_quantize_k, or kivi_quantize_k_outliers when shape.outliers > 0."""
+    if shape.outliers > 0:
+        check(_lib.kivi_quantize_k_outliers(
+            ctypes.byref(shape), k.data_ptr(), k.shape[2], ntok, dst_off, codes.data_ptr(),
+            scale.data_ptr(), zero.data_ptr(), _ptr(outliers), _stream()),
+            "kivi_quantize_k_outliers")
+        return
     check(_lib.kivi_quantize_k(ctypes.byref(shape), k.data_ptr(), k.shape[2], ntok, dst_off,
                                codes.data_ptr(), scale.data_ptr(), zero.data_ptr(), _stream()),
           "kivi_quantize_k")
@@ -155,14 +181,15 @@ class RaggedKiviCache(KiviCache):
     (int32 NumPy arrays the C struct points at; the library updates them)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 device="cuda", meta_half=False):
+                 device="cuda", meta_half=False, outliers=0):
         super().__init__(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                         device=device, meta_half=meta_half)
+                         device=device, meta_half=meta_half, outliers=outliers)
         self.tq_arr = np.zeros(batch, np.int32)
         self.tr_arr = np.zeros(batch, np.int32)
         self.rc = kivi_ragged_cache(self.shape, *[t.data_ptr() for t in (
             self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
-            self.k_res, self.v_res)], _i32p(self.tq_arr), _i32p(self.tr_arr))
+            self.k_res, self.v_res)], _i32p(self.tq_arr), _i32p(self.tr_arr),
+            _ptr(self.k_outliers))
 
     @property
     def tq(self) -> np.ndarray:
@@ -235,10 +262,12 @@ class PagedKiviCache(RaggedKiviCache):
     include/kivi.h; the residual stays per sequence."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 page_tokens, num_pages=None, table=None, device="cuda", meta_half=False):
+                 page_tokens, num_pages=None, table=None, device="cuda", meta_half=False,
+                 outliers=0):
         self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                                meta_half)
+                                meta_half, outliers)
         self.meta_half = bool(meta_half)
+        self.outliers = int(outliers)
         P = page_tokens
         max_pages = capacity // P
         if num_pages is None:
@@ -262,6 +291,7 @@ class PagedKiviCache(RaggedKiviCache):
         self.v_res = torch.zeros((B, H, R, D), dtype=torch.float16, device=dev)
         assert self.k_codes.nbytes == sizes[0].value and self.k_scale.nbytes == sizes[1].value
         assert self.v_codes.nbytes == sizes[2].value and self.v_scale.nbytes == sizes[3].value
+        self.k_outliers = _outlier_store(self.shape, num_pages, P, P, num_pages, dev)
         if table is None:
             table = np.arange(B * max_pages, dtype=np.int32).reshape(B, max_pages)
         self.table_host = np.ascontiguousarray(table, np.int32).reshape(B, max_pages)
@@ -270,7 +300,8 @@ class PagedKiviCache(RaggedKiviCache):
         self.tr_arr = np.zeros(batch, np.int32)
         self.pc = kivi_paged_cache(self.shape, P, num_pages, *[t.data_ptr() for t in (
             self.k_codes, self.k_scale, self.k_zero, self.v_codes, self.v_scale, self.v_zero,
-            self.k_res, self.v_res, self.table)], _i32p(self.tq_arr), _i32p(self.tr_arr))
+            self.k_res, self.v_res, self.table)], _i32p(self.tq_arr), _i32p(self.tr_arr),
+            _ptr(self.k_outliers))
         self.workspace = None
 
     def prefill(self, k, v, ntok, tq) -> None:

@@ -6,7 +6,9 @@
 // grouped part and the full-precision residual part is combined with them.
 // Here: o = softmax(scale * q.k) . v over the tq quantized tokens (keys and
 // values dequantized in registers as code*scale + zero) and the tr residual
-// fp16 tokens, binary32 accumulation.
+// fp16 tokens, binary32 accumulation.  With key outliers (KVQuant page,
+// abstract: outliers isolated per vector), a key listed in its group's sparse
+// row takes the kept fp16 value instead of the dense one.
 //
 // One block of 256 threads per (split, b*Hkv + h).  The block owns a
 // contiguous token chunk and all r query heads of its KV head:
@@ -136,9 +138,15 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
       if (t < tq && slot(t, pl, lt)) {
         const uint32_t* row = a.k_codes + (pl * scap + lt) * W;
         const size_t m0 = (pl * (scap / G) + lt / G) * D;
+        const uint32_t* orow = a.k_out + m0 * a.n_out;   // [n_out][D] of this group
+        const uint32_t my = (uint32_t)(lt % G);
         for (int dd = 0; dd < D; dd++) {
-          const float kh = (float)code_at(row, D, bits, dd) * meta_at(a.k_scale, m0 + dd, mh) +
-                           meta_at(a.k_zero, m0 + dd, mh);
+          float kh = (float)code_at(row, D, bits, dd) * meta_at(a.k_scale, m0 + dd, mh) +
+                     meta_at(a.k_zero, m0 + dd, mh);
+          for (int j = 0; j < a.n_out; j++) {
+            const uint32_t w = orow[(size_t)j * D + dd];
+            if ((w >> 16) == my) kh = h2f((uint16_t)(w & 0xFFFFu));
+          }
 #pragma unroll
           for (int i = 0; i < RR; i++)
             if (i < r) acc[i] += sq[i * D + dd] * kh;

@@ -49,17 +49,20 @@
 
 namespace kivi {
 
-bool decode_mfma_supported(int D, int G, int r) {
-  return D == kD && G == kG && (r == 1 || r == 2 || r == 4 || r == 8);
+bool decode_mfma_supported(int D, int G, int r, int n_out) {
+  return D == kD && G == kG && (r == 1 || r == 2 || r == 4 || r == 8) && n_out >= 0 &&
+         n_out <= kMfmaMaxOutliers;
 }
 
 namespace {
-// (the binary32-metadata variant: it holds the most registers of the two)
+// (the binary32-metadata variant without outliers; every variant of one
+// (bits, r, block) shares its register budget and LDS size, hence its
+// occupancy)
 template <int BITS, int R, int NW>
 int occupancy_of() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false, false>),
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false, false, 0>),
           NW * 64, 0) !=
       hipSuccess)
     return 1;
@@ -110,13 +113,9 @@ int decode_mfma_block_waves(int r, int nw) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
-  const NoLens none;
-  switch (a.bits) {
-    case 1: return launch_bits<1, false, false>(a, none, nw, st);
-    case 2: return launch_bits<2, false, false>(a, none, nw, st);
-    case 3: return launch_bits<3, false, false>(a, none, nw, st);
-    default: return launch_bits<4, false, false>(a, none, nw, st);
-  }
+  if (a.n_out == 1) return launch_decode_mfma_o1(a, nw, st);
+  if (a.n_out == 2) return launch_decode_mfma_o2(a, nw, st);
+  return launch_family<false, false, 0>(a, NoLens{}, nw, st);
 }
 
 }  // namespace kivi

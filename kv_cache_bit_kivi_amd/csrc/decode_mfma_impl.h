@@ -1,8 +1,10 @@
 // The matrix-core decode kernel template and its launch helpers, shared by
 // the translation units that instantiate it: decode_mfma.hip (lengths
-// uniform across the batch) and decode_mfma_ragged.hip (per-sequence
-// lengths).  The method and the kernel's design are described at the top of
-// decode_mfma.hip.
+// uniform across the batch), decode_mfma_ragged.hip (per-sequence lengths),
+// decode_mfma_paged.hip (paged store), and their key-outlier variants
+// (decode_mfma_o1.hip, decode_mfma_o2.hip, decode_mfma_ragged_o.hip,
+// decode_mfma_paged_o.hip).  The method and the kernel's design are
+// described at the top of decode_mfma.hip.
 #pragma once
 
 #include <math.h>
@@ -258,7 +260,13 @@ constexpr int prefetch_depth() {
   return R >= 8 ? 2 : 1;
 }
 
-template <int BITS, int R, int NW, bool MH, bool RAG, bool PG>
+// KO: key outliers per (group, channel) (0, 1 or 2; a.n_out == KO).  Each
+// lane loads the outlier words of its key group and channels cq..cq+3 with
+// the tile's metadata, and adds q_d * (kept value - zero) for every outlier
+// into the score of its token (the dense code there is 0, so the dense score
+// already holds q_d * zero); these additions go into the wave's own LDS score
+// buffer as LDS atomics, before the MFMA scores are added on top.
+template <int BITS, int R, int NW, bool MH, bool RAG, bool PG, int KO>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
 decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
@@ -300,6 +308,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const rsrc_t r_vc = make_rsrc(a.v_codes + plane * cap * (kD * BITS / 32), (uint32_t)(cap * (kD * BITS / 32) * 4));
   const rsrc_t r_vs = make_rsrc(static_cast<const char*>(a.v_scale) + plane * vmp, (uint32_t)vmp);
   const rsrc_t r_vz = make_rsrc(static_cast<const char*>(a.v_zero) + plane * vmp, (uint32_t)vmp);
+  // key outliers: KO words per (group, channel), KO * 512 bytes per key group
+  const size_t kop = (cap / kG) * KO * kD * 4;
+  const rsrc_t r_ko = make_rsrc(a.k_out + plane * (kop / 4), (uint32_t)kop);
   const rsrc_t r_kr = make_rsrc(a.k_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
   const rsrc_t r_vr = make_rsrc(a.v_res + plane * (size_t)a.R * kD, (uint32_t)(a.R * kD * 2));
   // fused append: the new token (residual slot t_new) comes from its input row
@@ -411,12 +422,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       x7 = ld16(rvc, co + 3072);
     }
   };
-  auto load_meta = [&](int tile, MetaT& ks, MetaT& kz, MetaT& vs, MetaT& vz)
-      __attribute__((always_inline)) {
+  auto load_meta = [&](int tile, MetaT& ks, MetaT& kz, MetaT& vs, MetaT& vz, uint4& o0,
+                       uint4& o1) __attribute__((always_inline)) {
     // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 256 values
     // each, 4 per lane (converted to binary32 when the tile is computed)
     uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
-    rsrc_t rks = r_ks, rkz = r_kz, rvs = r_vs, rvz = r_vz;
+    // outlier words j of key group 2*tile + kgrp, channels cq..cq+3
+    uint32_t oo = tile < t_end ? (uint32_t)((2 * tile + kgrp) * KO) * 512 + (lane & 31) * 16 : kOut;
+    rsrc_t rks = r_ks, rkz = r_kz, rvs = r_vs, rvz = r_vz, rko = r_ko;
     if constexpr (PG) {
       size_t sp;
       uint32_t lt;
@@ -427,7 +440,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       rvs = make_rsrc(static_cast<const char*>(a.v_scale) + sp * vb, (uint32_t)vb);
       rvz = make_rsrc(static_cast<const char*>(a.v_zero) + sp * vb, (uint32_t)vb);
       mo = ok ? lt * (256 * MB) + lane * (4 * MB) : kOut;
+      if constexpr (KO > 0) {
+        const size_t ob = (size_t)(P / kG) * KO * kD * 4;
+        rko = make_rsrc(a.k_out + sp * (ob / 4), (uint32_t)ob);
+        oo = ok ? (uint32_t)((2 * lt + kgrp) * KO) * 512 + (lane & 31) * 16 : kOut;
+      }
     }
+    if constexpr (KO >= 1) o0 = ld16(rko, oo);
+    if constexpr (KO >= 2) o1 = ld16(rko, oo == kOut ? kOut : oo + 512);
     if constexpr (MH) {
       ks = ld8s(rks, mo);
       kz = ld8s(rkz, mo);
@@ -490,15 +510,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   constexpr int DEPTH = prefetch_depth<BITS, R>();
   uint4 a0, a1, a2, a3, a4, a5, a6, a7, b0, b1, b2, b3, b4, b5, b6, b7;
   MetaT a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
+  uint4 a_o0, a_o1, b_o0, b_o1;   // key-outlier words (KO > 0)
   // (the same issue order as the loop: codes A, meta A, codes B, meta B)
   load_codes(t_begin, a0, a1, a2, a3, a4, a5, a6, a7);
   __builtin_amdgcn_sched_barrier(0);
-  load_meta(t_begin, a_ks, a_kz, a_vs, a_vz);
+  load_meta(t_begin, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
   if constexpr (DEPTH == 2) {
     __builtin_amdgcn_sched_barrier(0);
     load_codes(t_begin + 1, b0, b1, b2, b3, b4, b5, b6, b7);
     __builtin_amdgcn_sched_barrier(0);
-    load_meta(t_begin + 1, b_ks, b_kz, b_vs, b_vz);
+    load_meta(t_begin + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -596,8 +617,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 
   // one tile (codes already staged in LDS): key scores -> LDS, online-softmax
   // rescale, P.V
-  auto do_tile = [&](int tile, MetaT ksm, MetaT kzm, MetaT vsm, MetaT vzm)
-      __attribute__((always_inline)) {
+  auto do_tile = [&](int tile, MetaT ksm, MetaT kzm, MetaT vsm, MetaT vzm, const uint4& o0,
+                     const uint4& o1) __attribute__((always_inline)) {
     const float4 ks4 = meta4(ksm), kz4 = meta4(kzm), vs4 = meta4(vsm), vz4 = meta4(vzm);
     const bool half_tile = tile * 64 + 64 > tq;   // only the first 32 tokens exist
     // key factors (both groups at once: lanes 0-31 group 0, 32-63 group 1)
@@ -621,9 +642,35 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       beta0[h] = lane_read(bp, 0) + lane_read(bp, 16);
       beta1[h] = lane_read(bp, 32) + lane_read(bp, 48);
     }
-    if (half_tile && lane < 32) {
+    if constexpr (KO == 0) {
+      if (half_tile && lane < 32) {
 #pragma unroll
-      for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
+        for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
+      }
+    } else {
+      // outlier corrections: the score buffer starts at 0 (-inf for the
+      // absent half of a half tile), each outlier adds q * (value - zero) of
+      // its channel at its token (position masked to the group: no word can
+      // address outside the buffer); the half tile's absent group adds none
+      const float init = (half_tile && lane >= 32) ? -INFINITY : 0.f;
+#pragma unroll
+      for (int h = 0; h < R; h++) lds_sc[h * CH + lane] = init;
+      __builtin_amdgcn_wave_barrier();
+      if (!half_tile || kgrp == 0) {
+        const uint32_t ow[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
+#pragma unroll
+        for (int j = 0; j < KO; j++)
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const uint32_t w = ow[j][e];
+            const float dv = h2f((uint16_t)(w & 0xFFFFu)) - kzv[e];
+            float* dst = lds_sc + 32 * kgrp + ((w >> 16) & 31u);
+#pragma unroll
+            for (int h = 0; h < R; h++)
+              __hip_atomic_fetch_add(dst + h * CH, sq[h][e] * dv, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_WAVEFRONT);
+          }
+      }
     }
     __builtin_amdgcn_wave_barrier();
     const int ngr = half_tile ? 1 : 2;
@@ -669,10 +716,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
             acc = mfma(af[3], cvt_word4(x.w), acc);
           }
           const int k = 16 * mb + n16;
-          const float s0 = (acc[0] + acc[1]) * qup + b0;
-          const float s1 = (acc[2] + acc[3]) * qup + b1;
-          *sc_addr(0, k) = s0;
-          *sc_addr(1, k) = s1;
+          float* p0 = sc_addr(0, k);
+          float* p1 = sc_addr(1, k);
+          float s0 = (acc[0] + acc[1]) * qup + b0;
+          float s1 = (acc[2] + acc[3]) * qup + b1;
+          if constexpr (KO > 0) {   // + the outlier corrections
+            s0 += *p0;
+            s1 += *p1;
+          }
+          *p0 = s0;
+          *p1 = s1;
           mx0 = fmaxf(mx0, s0);
           mx1 = fmaxf(mx1, s1);
         }
@@ -866,16 +919,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
       load_codes(t + 2, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz);
+      do_tile(t, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz);
+      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
       stage(b0, b1, b2, b3, b4, b5, b6, b7);
       load_codes(t + 3, b0, b1, b2, b3, b4, b5, b6, b7);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz);
+      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 3, b_ks, b_kz, b_vs, b_vz);
+      load_meta(t + 3, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
     }
   } else {
     for (int t = t_begin; t < t_end; t++) {
@@ -883,9 +936,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
       load_codes(t + 1, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz);
+      do_tile(t, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 1, a_ks, a_kz, a_vs, a_vz);
+      load_meta(t + 1, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
     }
   }
 
@@ -979,29 +1032,40 @@ constexpr int block_waves(int nw) {
   return (R >= 8 || nw < 8) ? 4 : 8;
 }
 
-template <int BITS, int R, bool MH, bool RAG, bool PG>
+template <int BITS, int R, bool MH, bool RAG, bool PG, int KO>
 hipError_t launch_m(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
   if (block_waves<R>(nw) == 8)
-    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG, PG>
+    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG, PG, KO>
         <<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a, lens);
   else
-    decode_mfma_kernel<BITS, R, 4, MH, RAG, PG><<<grid, 4 * 64, 0, st>>>(a, lens);
+    decode_mfma_kernel<BITS, R, 4, MH, RAG, PG, KO><<<grid, 4 * 64, 0, st>>>(a, lens);
   return hipGetLastError();
 }
-template <int BITS, int R, bool RAG, bool PG>
+template <int BITS, int R, bool RAG, bool PG, int KO>
 hipError_t launch_r(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
-  return a.mh ? launch_m<BITS, R, true, RAG, PG>(a, lens, nw, st)
-              : launch_m<BITS, R, false, RAG, PG>(a, lens, nw, st);
+  return a.mh ? launch_m<BITS, R, true, RAG, PG, KO>(a, lens, nw, st)
+              : launch_m<BITS, R, false, RAG, PG, KO>(a, lens, nw, st);
 }
 
-template <int BITS, bool RAG, bool PG>
+template <int BITS, bool RAG, bool PG, int KO>
 hipError_t launch_bits(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   switch (a.r) {
-    case 1: return launch_r<BITS, 1, RAG, PG>(a, lens, nw, st);
-    case 2: return launch_r<BITS, 2, RAG, PG>(a, lens, nw, st);
-    case 4: return launch_r<BITS, 4, RAG, PG>(a, lens, nw, st);
-    default: return launch_r<BITS, 8, RAG, PG>(a, lens, nw, st);
+    case 1: return launch_r<BITS, 1, RAG, PG, KO>(a, lens, nw, st);
+    case 2: return launch_r<BITS, 2, RAG, PG, KO>(a, lens, nw, st);
+    case 4: return launch_r<BITS, 4, RAG, PG, KO>(a, lens, nw, st);
+    default: return launch_r<BITS, 8, RAG, PG, KO>(a, lens, nw, st);
+  }
+}
+
+// every code width of one (lengths, store, outliers) family
+template <bool RAG, bool PG, int KO>
+hipError_t launch_family(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
+  switch (a.bits) {
+    case 1: return launch_bits<1, RAG, PG, KO>(a, lens, nw, st);
+    case 2: return launch_bits<2, RAG, PG, KO>(a, lens, nw, st);
+    case 3: return launch_bits<3, RAG, PG, KO>(a, lens, nw, st);
+    default: return launch_bits<4, RAG, PG, KO>(a, lens, nw, st);
   }
 }
 

@@ -7,12 +7,8 @@ namespace kivi {
 
 hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, int nw,
                                      hipStream_t st) {
-  switch (a.bits) {
-    case 1: return launch_bits<1, true, false>(a, lens, nw, st);
-    case 2: return launch_bits<2, true, false>(a, lens, nw, st);
-    case 3: return launch_bits<3, true, false>(a, lens, nw, st);
-    default: return launch_bits<4, true, false>(a, lens, nw, st);
-  }
+  if (a.n_out > 0) return launch_decode_mfma_ragged_o(a, lens, nw, st);
+  return launch_family<true, false, 0>(a, lens, nw, st);
 }
 
 }  // namespace kivi

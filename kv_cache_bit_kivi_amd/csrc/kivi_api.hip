@@ -22,6 +22,7 @@ int check_shape(const kivi_shape* s) {
   if (s->batch < 1 || s->num_kv_heads < 1 || s->gqa_ratio < 1) return KIVI_EINVAL;
   if (s->bits < 1 || s->bits > 4) return KIVI_EINVAL;
   if (s->meta_half != 0 && s->meta_half != 1) return KIVI_EINVAL;
+  if (s->outliers < 0 || s->outliers > 8) return KIVI_EINVAL;   // (< every group size)
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
   if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
@@ -45,6 +46,8 @@ int check_cache(const kivi_cache* c) {
   for (const void* p : ptrs)
     if (!aligned16(p)) return KIVI_EALIGN;
   const kivi_shape& s = c->shape;
+  if (s.outliers > 0 && !c->k_outliers) return KIVI_EINVAL;
+  if (s.outliers > 0 && !aligned16(c->k_outliers)) return KIVI_EALIGN;
   if (c->tq < 0 || c->tq % s.group != 0 || c->tr < 0 || c->tr > s.residual)
     return KIVI_ESHAPE;
   if (c->tq > s.capacity) return KIVI_ECAPACITY;
@@ -89,7 +92,7 @@ int max_auto_splits(const kivi_shape& s) {
 }
 
 bool use_mfma(const kivi_shape& s) {
-  return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio);
+  return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers);
 }
 
 // waves per block of the matrix-core decode kernel
@@ -149,11 +152,13 @@ struct Rg {
   int32_t* tr;
   bool paged;
   kivi::PageMap pm;   // paged: pools of pm.num_pages pages, device table [batch][max_pages]
+  uint32_t* k_out;    // key outliers (shape.outliers > 0)
 };
 
 Rg view(const kivi_ragged_cache* c) {
   return Rg{&c->shape, c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
-            c->k_res,  c->v_res,   c->tq,      c->tr,      false,      kivi::PageMap{nullptr, 0, 0, 0, 0}};
+            c->k_res,  c->v_res,   c->tq,      c->tr,      false,      kivi::PageMap{nullptr, 0, 0, 0, 0},
+            c->k_outliers};
 }
 Rg view(const kivi_paged_cache* c) {
   const int P = c->page_tokens > 0 ? c->page_tokens : 1;
@@ -162,7 +167,8 @@ Rg view(const kivi_paged_cache* c) {
   return Rg{&c->shape, c->k_codes, c->k_scale, c->k_zero, c->v_codes, c->v_scale, c->v_zero,
             c->k_res,  c->v_res,   c->tq,      c->tr,      true,
             kivi::PageMap{c->block_table, c->page_tokens, c->shape.capacity / P, c->num_pages,
-                          shift}};
+                          shift},
+            c->k_outliers};
 }
 
 // buffers present and aligned, length arrays present (shape already checked)
@@ -173,8 +179,10 @@ int check_buffers(const Rg& g) {
     if (!p) return KIVI_EINVAL;
   if (!g.tq || !g.tr) return KIVI_EINVAL;
   if (g.paged && !g.pm.table) return KIVI_EINVAL;
+  if (g.s->outliers > 0 && !g.k_out) return KIVI_EINVAL;
   for (const void* p : ptrs)
     if (!aligned16(p)) return KIVI_EALIGN;
+  if (g.s->outliers > 0 && !aligned16(g.k_out)) return KIVI_EALIGN;
   if (g.paged && (reinterpret_cast<uintptr_t>(g.pm.table) & 3u)) return KIVI_EALIGN;
   return KIVI_OK;
 }
@@ -222,11 +230,12 @@ int check_paged(const kivi_paged_cache* c) {
 
 // per-(b, h) plane extents of the contiguous cache buffers
 struct PlaneSizes {
-  size_t code_words, kmeta_bytes, vmeta_bytes, res_elems;
+  size_t code_words, kmeta_bytes, vmeta_bytes, res_elems, kout_words;
 };
 PlaneSizes plane_sizes(const kivi_shape& s) {
   const size_t cap = s.capacity, D = s.head_dim, G = s.group, mb = s.meta_half ? 2 : 4;
-  return {cap * D * s.bits / 32, (cap / G) * D * mb, cap * (D / G) * mb, (size_t)s.residual * D};
+  return {cap * D * s.bits / 32, (cap / G) * D * mb, cap * (D / G) * mb, (size_t)s.residual * D,
+          (cap / G) * (size_t)s.outliers * D};
 }
 
 // Runs `launch(list)` over the items added with `add`, kMaxSeq at a time.
@@ -262,13 +271,15 @@ int enqueue_quantize_list(const Rg& g, const uint16_t* k_src, const uint16_t* v_
   hipError_t e;
   if (g.paged) {
     e = kivi::launch_quantize_k_paged(k_src, L, g.pm, H, D, s.bits, s.group, in_stride, ntok_max,
-                                      g.k_codes, g.k_scale, g.k_zero, s.meta_half, st);
+                                      g.k_codes, g.k_scale, g.k_zero, s.meta_half, g.k_out,
+                                      s.outliers, st);
     if (e == hipSuccess)
       e = kivi::launch_quantize_v_paged(v_src, L, g.pm, H, D, s.bits, s.group, in_stride,
                                         ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
   } else {
     e = kivi::launch_quantize_k_list(k_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
-                                     ntok_max, g.k_codes, g.k_scale, g.k_zero, s.meta_half, st);
+                                     ntok_max, g.k_codes, g.k_scale, g.k_zero, s.meta_half,
+                                     g.k_out, s.outliers, st);
     if (e == hipSuccess)
       e = kivi::launch_quantize_v_list(v_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
                                        ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
@@ -393,6 +404,8 @@ int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
     a.S = S;
     a.mh = s.meta_half;
     a.scale = softmax_scale;
+    a.k_out = s.outliers > 0 ? g.k_out + cp * ps.kout_words : nullptr;
+    a.n_out = s.outliers;
     hipError_t e;
     if (use_mfma(s))
       e = g.paged ? kivi::launch_decode_mfma_paged(a, lens, mfma_waves(), st)
@@ -559,13 +572,48 @@ int kivi_cache_bytes(const kivi_shape* s, size_t* k_codes, size_t* k_meta, size_
   return KIVI_OK;
 }
 
+int kivi_outlier_bytes(const kivi_shape* s, int32_t page_tokens, int32_t num_pages,
+                       size_t* bytes) {
+  int rc = check_shape(s);
+  if (rc) return rc;
+  if (!bytes) return KIVI_EINVAL;
+  size_t slices = (size_t)s->batch * s->num_kv_heads, tokens = s->capacity;
+  if (page_tokens != 0) {
+    kivi_paged_cache c{};
+    c.shape = *s;
+    c.page_tokens = page_tokens;
+    c.num_pages = num_pages;
+    if ((rc = check_pages(&c))) return rc;
+    slices = (size_t)num_pages * s->num_kv_heads;
+    tokens = page_tokens;
+  }
+  *bytes = slices * (tokens / s->group) * (size_t)s->outliers * s->head_dim * 4;
+  return KIVI_OK;
+}
+
 int kivi_quantize_k(const kivi_shape* s, const uint16_t* k, int32_t in_tok_stride, int32_t ntok,
                     int32_t dst, uint32_t* codes, void* scale, void* zero, void* stream) {
   int rc = check_quantize(s, k, in_tok_stride, ntok, dst, codes, scale, zero);
   if (rc) return rc;
+  if (s->outliers != 0) return KIVI_EINVAL;   // kivi_quantize_k_outliers
   hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, s->meta_half, (hipStream_t)stream);
+                                         scale, zero, s->meta_half, nullptr, 0,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+}
+
+int kivi_quantize_k_outliers(const kivi_shape* s, const uint16_t* k, int32_t in_tok_stride,
+                             int32_t ntok, int32_t dst, uint32_t* codes, void* scale, void* zero,
+                             uint32_t* outliers, void* stream) {
+  int rc = check_quantize(s, k, in_tok_stride, ntok, dst, codes, scale, zero);
+  if (rc) return rc;
+  if (s->outliers < 1 || !outliers) return KIVI_EINVAL;
+  if (!aligned16(outliers)) return KIVI_EALIGN;
+  hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
+                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
+                                         scale, zero, s->meta_half, outliers, s->outliers,
+                                         (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
 }
 
@@ -593,7 +641,8 @@ int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t nt
   if (tq > 0) {
     hipError_t e = kivi::launch_quantize_k(k, s.batch, s.num_kv_heads, s.head_dim, s.bits,
                                            s.group, s.capacity, ntok, tq, 0, c->k_codes,
-                                           c->k_scale, c->k_zero, s.meta_half, st);
+                                           c->k_scale, c->k_zero, s.meta_half, c->k_outliers,
+                                           s.outliers, st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(v, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero,
@@ -625,7 +674,7 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
     hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
                                            tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
-                                           st);
+                                           c->k_outliers, s.outliers, st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, tq, c->v_codes, c->v_scale,
@@ -705,6 +754,8 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->mh = s.meta_half;
   a->scale = softmax_scale;
   a->pages = kivi::PageMap{nullptr, 0, 0, 0, 0};
+  a->k_out = s.outliers > 0 ? c->k_outliers : nullptr;
+  a->n_out = s.outliers;
   return KIVI_OK;
 }
 
@@ -754,7 +805,7 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
     hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
                                            c->tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
-                                           st);
+                                           c->k_outliers, s.outliers, st);
     if (e != hipSuccess) return KIVI_EHIP;
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, c->tq, c->v_codes,

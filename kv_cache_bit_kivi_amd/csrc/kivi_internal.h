@@ -83,6 +83,10 @@ struct DecodeArgs {
   int mh;             // metadata stored as binary16 (1) or binary32 (0)
   float scale;
   PageMap pages;      // paged launches only (table null otherwise)
+  // key outliers: n_out words per (key group, channel), [plane][cap/G][n_out][D]
+  // (page slices [slice][P/G][n_out][D]); null when n_out == 0
+  const uint32_t* k_out;
+  int n_out;
 };
 
 // Kernel parameter of the decode kernels: nothing (uniform lengths, taken
@@ -107,9 +111,12 @@ __device__ __forceinline__ int seq_plane(const LensT<RAG>& l, int i, int H) {
 
 // Launchers: validate nothing (the C ABI layer did), return hipError_t of the
 // launch.
+// Key quantizers take the key-outlier store `outl` and its row length n_out
+// (0: no isolation, outl unused).
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G,
                              int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, hipStream_t st);
+                             void* scale, void* zero, int mh, uint32_t* outl, int n_out,
+                             hipStream_t st);
 hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G,
                              int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
                              void* scale, void* zero, int mh, hipStream_t st);
@@ -126,7 +133,8 @@ hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int 
 // seq[i] of src into residual slots [b[i], b[i] + c[i]) (c[i] <= n_max).
 hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
                                   int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, hipStream_t st);
+                                  void* scale, void* zero, int mh, uint32_t* outl, int n_out,
+                                  hipStream_t st);
 hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H, int D, int bits,
                                   int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
                                   void* scale, void* zero, int mh, hipStream_t st);
@@ -139,7 +147,7 @@ hipError_t launch_copy_tokens_list(const uint16_t* k_src, const uint16_t* v_src,
 hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
                                    int H, int D, int bits, int G, int in_stride, int ntok_max,
                                    uint32_t* codes, void* scale, void* zero, int mh,
-                                   hipStream_t st);
+                                   uint32_t* outl, int n_out, hipStream_t st);
 hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const PageMap& pm,
                                    int H, int D, int bits, int G, int in_stride, int ntok_max,
                                    uint32_t* codes, void* scale, void* zero, int mh,
@@ -157,8 +165,10 @@ hipError_t launch_decode_generic_paged(const DecodeArgs& a, const SeqLens& lens,
 size_t decode_generic_lds_bytes(int r, int D);
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
 
-// Matrix-core decode kernel: head_dim 128, group 32, gqa ratio 1..8.
-bool decode_mfma_supported(int D, int G, int r);
+// Matrix-core decode kernel: head_dim 128, group 32, gqa ratio 1, 2, 4 or 8,
+// at most kMfmaMaxOutliers key outliers per group.
+constexpr int kMfmaMaxOutliers = 2;
+bool decode_mfma_supported(int D, int G, int r, int n_out);
 // nw: requested waves per block (4 or 8); the block size actually used
 // for a gqa ratio r is decode_mfma_block_waves(r, nw)
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st);
@@ -167,6 +177,14 @@ hipError_t launch_decode_mfma_ragged(const DecodeArgs& a, const SeqLens& lens, i
 hipError_t launch_decode_mfma_paged(const DecodeArgs& a, const SeqLens& lens, int nw,
                                     hipStream_t st);
 int decode_mfma_block_waves(int r, int nw);
+// The launches above for a.n_out = 1 or 2, one translation unit per
+// variant family (called by the launchers above, not by the API layer).
+hipError_t launch_decode_mfma_o1(const DecodeArgs& a, int nw, hipStream_t st);
+hipError_t launch_decode_mfma_o2(const DecodeArgs& a, int nw, hipStream_t st);
+hipError_t launch_decode_mfma_ragged_o(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                       hipStream_t st);
+hipError_t launch_decode_mfma_paged_o(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                      hipStream_t st);
 // resident blocks per compute unit of that kernel variant (occupancy query)
 int decode_mfma_blocks_per_cu(int bits, int r, int nw);
 

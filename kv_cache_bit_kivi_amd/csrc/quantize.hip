@@ -14,11 +14,21 @@
 //              code = min(rint((x - z) / s), 2^b - 1), rint = half-to-even.
 // Half-width metadata stores s and z rounded to binary16 (nearest even) after
 // the codes have been computed from the binary32 values.
+// Key outliers ("KVQuant: Towards 10 Million Context Length LLM Inference
+// with KV Cache Quantization", codewithpapers.app paper page, abstract:
+// outliers are isolated per vector so they do not stretch the quantization
+// range), n_out > 0: in each key group (one channel over G tokens) the n_out
+// entries of largest |x| (ties: the lower token) are written exactly as
+// (i << 16) | fp16 bits, in increasing token i, and left out of mn / mx; their
+// codes are 0 (the kernel stores mn in their place before encoding, which
+// encodes to 0 exactly).
 // Each block stages its fp16 tile in LDS with 16-byte loads, computes the
 // group statistics from LDS, then writes whole 32-bit code words, so any
 // number of blocks can run concurrently without read-modify-write.
 // The LIST variants work on a list of sequences with per-sequence token
 // counts and offsets (ragged batches: prefill and per-sequence flushes).
+#include <math.h>
+
 #include <type_traits>
 
 #include "kivi_internal.h"
@@ -115,7 +125,8 @@ template <int BITS, bool MH, bool LIST, bool PG>
 __global__ void __launch_bounds__(256)
 quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
                   int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero, int H, ListT<LIST> list, PageMap pm) {
+                  void* __restrict__ zero, uint32_t* __restrict__ outl, int n_out, int H,
+                  ListT<LIST> list, PageMap pm) {
   extern __shared__ __align__(16) uint8_t smem[];
   uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
   float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
@@ -144,11 +155,49 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
 
   const size_t gg = (size_t)(otok / G);
   for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float mn = h2f(tile[d]), mx = mn;
-    for (int i = 1; i < G; i++) {
-      float x = h2f(tile[i * D + d]);
-      if (x < mn) mn = x;
-      if (x > mx) mx = x;
+    float mn, mx;
+    if (n_out == 0) {
+      mn = mx = h2f(tile[d]);
+      for (int i = 1; i < G; i++) {
+        float x = h2f(tile[i * D + d]);
+        if (x < mn) mn = x;
+        if (x > mx) mx = x;
+      }
+    } else {
+      // outlier positions as a bit set over the group's G <= 128 tokens; each
+      // pass takes the first largest |x| not yet taken
+      uint64_t m0 = 0, m1 = 0;
+      auto taken = [&](int i) { return ((i < 64 ? m0 >> i : m1 >> (i - 64)) & 1u) != 0; };
+      for (int j = 0; j < n_out; j++) {
+        int best = 0;
+        float bm = -1.0f;
+        for (int i = 0; i < G; i++) {
+          const float a = fabsf(h2f(tile[i * D + d]));
+          if (a > bm && !taken(i)) {
+            bm = a;
+            best = i;
+          }
+        }
+        if (best < 64) m0 |= 1ull << best; else m1 |= 1ull << (best - 64);
+      }
+      mn = INFINITY;
+      mx = -INFINITY;
+      for (int i = 0; i < G; i++) {
+        if (taken(i)) continue;
+        float x = h2f(tile[i * D + d]);
+        if (x < mn) mn = x;
+        if (x > mx) mx = x;
+      }
+      // the sparse row, then mn in the outliers' places (code 0)
+      uint32_t* orow = outl + ((ob * (ocap / G) + gg) * n_out) * D + d;
+      const uint16_t mn_h = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
+      int j = 0;
+      for (int i = 0; i < G; i++) {
+        if (!taken(i)) continue;
+        orow[(size_t)j * D] = ((uint32_t)i << 16) | tile[i * D + d];
+        tile[i * D + d] = mn_h;
+        j++;
+      }
     }
     float s;
     group_stats<BITS>(mn, mx, &s);
@@ -291,12 +340,13 @@ void dispatch_bits(int bits, int mh, F f) {
 
 hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G, int cap,
                              int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, hipStream_t st) {
+                             void* scale, void* zero, int mh, uint32_t* outl, int n_out,
+                             hipStream_t st) {
   dim3 grid(ntok / G, B * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
-                                   NoList{}, PageMap{});
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, outl,
+                                   n_out, H, NoList{}, PageMap{});
   };
   dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, false, false>); });
   return hipGetLastError();
@@ -317,13 +367,14 @@ hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, i
 
 hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
                                   int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, hipStream_t st) {
+                                  void* scale, void* zero, int mh, uint32_t* outl, int n_out,
+                                  hipStream_t st) {
   if (list.n == 0 || ntok_max == 0) return hipSuccess;
   dim3 grid(ntok_max / G, list.n * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
-                                   PageMap{});
+    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, outl, n_out,
+                                   H, list, PageMap{});
   };
   dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, false>); });
   return hipGetLastError();
@@ -346,12 +397,13 @@ hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H,
 hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
                                    int H, int D, int bits, int G, int in_stride, int ntok_max,
                                    uint32_t* codes, void* scale, void* zero, int mh,
-                                   hipStream_t st) {
+                                   uint32_t* outl, int n_out, hipStream_t st) {
   if (list.n == 0 || ntok_max == 0) return hipSuccess;
   dim3 grid(ntok_max / G, list.n * H);
   size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
   auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
+    kernel<<<grid, 256, lds, st>>>(k, D, G, 0, in_stride, 0, codes, scale, zero, outl, n_out, H,
+                                   list, pm);
   };
   dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, true>); });
   return hipGetLastError();

@@ -11,6 +11,11 @@ summary).  Trained-model activations are not available, so:
   K = N(0, 1) with ``n_outliers`` fixed channels per KV head multiplied by 10,
   V = N(0, 1), q = N(0, 1), each drawn in binary32 and rounded to binary16
   (round to nearest even).
+Sporadic key outliers (``key_spikes`` > 0, for the per-vector outlier
+isolation of "KVQuant: Towards 10 Million Context Length LLM Inference with KV
+Cache Quantization", codewithpapers.app page, abstract): each key entry is
+independently multiplied by 20 with probability ``key_spikes`` (a seeded mask
+stream of its own), so that single entries, not whole channels, stand out.
 Every (batch, head) plane has its own PCG64 stream keyed by
 SeedSequence([seed, stream, b, h]) so any single head can be regenerated alone.
 """
@@ -22,7 +27,8 @@ from dataclasses import dataclass
 import numpy as np
 
 # stream ids of SeedSequence([seed, stream, ...])
-S_OUTLIER, S_K, S_V, S_Q, S_KNEW, S_VNEW, S_QNEW, S_LEN = range(8)
+S_OUTLIER, S_K, S_V, S_Q, S_KNEW, S_VNEW, S_QNEW, S_LEN, S_SPIKE, S_SPIKENEW = range(10)
+SPIKE_FACTOR = 20.0
 
 
 @dataclass(frozen=True)
@@ -42,6 +48,7 @@ class Workload:
     seed: int
     steps: int = 0      # streaming decode steps after the prefill
     min_context: int = 0   # > 0: ragged batch, contexts drawn in [min_context, context]
+    key_spikes: float = 0.0   # probability of a sporadic x20 key entry
 
     @property
     def gqa(self) -> int:
@@ -123,10 +130,19 @@ def outlier_channels(w: Workload, h: int) -> np.ndarray:
     return np.sort(_rng(w.seed, S_OUTLIER, h).choice(w.head_dim, w.n_outliers, replace=False))
 
 
+def _spikes(w: Workload, x: np.ndarray, *key: int) -> None:
+    """Multiply a seeded Bernoulli(key_spikes) subset of x's entries by 20."""
+    if w.key_spikes > 0:
+        m = _rng(w.seed, *key).random(x.shape) < w.key_spikes
+        x[m] *= np.float32(SPIKE_FACTOR)
+
+
 def _plane(w: Workload, stream: int, b: int, h: int, T: int, outliers: bool) -> np.ndarray:
     x = _rng(w.seed, stream, b, h).standard_normal((T, w.head_dim), dtype=np.float32)
     if outliers and w.n_outliers:
         x[:, outlier_channels(w, h)] *= np.float32(10.0)
+    if outliers:
+        _spikes(w, x, S_SPIKE, b, h)
     return x.astype(np.float16)
 
 
@@ -169,6 +185,7 @@ def new_token(w: Workload, step: int, batches=None):
         for h in range(w.kv_heads):
             if w.n_outliers:
                 k[h, outlier_channels(w, h)] *= np.float32(10.0)
+        _spikes(w, k, S_SPIKENEW, step, b)
         gv = _rng(w.seed, S_VNEW, step, b)
         ks.append(k)
         vs.append(gv.standard_normal((w.kv_heads, w.head_dim), dtype=np.float32))
@@ -178,3 +195,11 @@ def new_token(w: Workload, step: int, batches=None):
 def random_fp16(seed: int, shape, scale: float = 1.0) -> np.ndarray:
     """Generic seeded N(0, scale^2) binary16 tensor for small test cases."""
     return (_rng(seed, 99).standard_normal(shape, dtype=np.float32) * np.float32(scale)).astype(np.float16)
+
+
+def spiky_fp16(seed: int, shape, rate: float = 0.02, scale: float = 1.0) -> np.ndarray:
+    """random_fp16 with a seeded Bernoulli(rate) subset of entries multiplied
+    by 20 (sporadic single-entry outliers)."""
+    x = _rng(seed, 99).standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    x[_rng(seed, 98).random(shape) < rate] *= np.float32(SPIKE_FACTOR)
+    return x.astype(np.float16)

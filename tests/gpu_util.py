@@ -42,7 +42,7 @@ def host(t: torch.Tensor) -> np.ndarray:
 def gpu_cache_from_oracle_shape(oc, device="cuda"):
     from kv_cache_bit_kivi_amd.cache import KiviCache
     return KiviCache(oc.B, oc.H, oc.r, oc.D, oc.bits, oc.G, oc.R, oc.cap, device=device,
-                     meta_half=oc.meta_half)
+                     meta_half=oc.meta_half, outliers=oc.n_out)
 
 
 def assert_cache_equal(gc, oc, planes=None, what=""):
@@ -67,6 +67,16 @@ def assert_cache_equal(gc, oc, planes=None, what=""):
             bad = np.argwhere(g != o)
             raise AssertionError(f"{what} {gname}: {len(bad)} mismatches, first at "
                                  f"{bad[0].tolist()}: gpu={g[tuple(bad[0])]} oracle={o[tuple(bad[0])]}")
+    if oc.n_out:
+        g = gc.k_outliers
+        if planes is not None:
+            g = g[list(planes)]
+        g = host(g)
+        if not np.array_equal(g, oc.k_outl):
+            bad = np.argwhere(g != oc.k_outl)
+            raise AssertionError(f"{what} k_outliers: {len(bad)} mismatches, first at "
+                                 f"{bad[0].tolist()}: gpu={g[tuple(bad[0])]:#x} "
+                                 f"oracle={oc.k_outl[tuple(bad[0])]:#x}")
     for gname, oname in (("k_res", "k_res"), ("v_res", "v_res")):
         g = getattr(gc, gname)
         if planes is not None:

@@ -39,7 +39,7 @@ def test_strerror():
 
 def shape(**kw):
     d = dict(batch=2, num_kv_heads=4, gqa_ratio=2, head_dim=128, bits=2, group=32,
-             residual=128, capacity=512, meta_half=0)
+             residual=128, capacity=512, meta_half=0, outliers=0)
     d.update(kw)
     return kivi_shape(*[d[n] for n, _ in kivi_shape._fields_])
 
@@ -79,6 +79,7 @@ def test_cache_bytes():
     (dict(capacity=96), KIVI_ESHAPE), (dict(capacity=-64), KIVI_ESHAPE),
     (dict(group=128, capacity=192), KIVI_ESHAPE),
     (dict(meta_half=2), KIVI_EINVAL), (dict(meta_half=-1), KIVI_EINVAL),
+    (dict(outliers=-1), KIVI_EINVAL), (dict(outliers=9), KIVI_EINVAL),
 ])
 def test_shape_errors(kw, code):
     assert sizes(shape(**kw))[0] == code
@@ -112,7 +113,53 @@ def cache(**kw):
     tq = kw.pop("tq", 0)
     tr = kw.pop("tr", 0)
     ptrs = kw.pop("ptrs", [P] * 8)
-    return kivi_cache(shape(**kw), *ptrs, tq, tr)
+    k_out = kw.pop("k_out", None)
+    return kivi_cache(shape(**kw), *ptrs, tq, tr, k_out)
+
+
+# ---- key outliers ----
+
+def test_outlier_bytes():
+    n = ctypes.c_size_t()
+    s = shape(outliers=2)
+    assert _lib.kivi_outlier_bytes(ctypes.byref(s), 0, 0, ctypes.byref(n)) == KIVI_OK
+    assert n.value == 8 * (512 // 32) * 2 * 128 * 4           # planes x groups x n x D words
+    assert _lib.kivi_outlier_bytes(ctypes.byref(s), 256, 10, ctypes.byref(n)) == KIVI_OK
+    assert n.value == 10 * 4 * (256 // 32) * 2 * 128 * 4      # pages x heads x ...
+    assert _lib.kivi_outlier_bytes(ctypes.byref(shape()), 0, 0, ctypes.byref(n)) == KIVI_OK
+    assert n.value == 0
+    assert _lib.kivi_outlier_bytes(ctypes.byref(s), 96, 10, ctypes.byref(n)) == KIVI_ESHAPE
+    assert _lib.kivi_outlier_bytes(ctypes.byref(s), 0, 0, None) == KIVI_EINVAL
+    assert _lib.kivi_outlier_bytes(ctypes.byref(shape(outliers=9)), 0, 0,
+                                   ctypes.byref(n)) == KIVI_EINVAL
+
+
+def test_quantize_outlier_errors():
+    qo = _lib.kivi_quantize_k_outliers
+    s = shape(outliers=1)
+    assert qk(s) == KIVI_EINVAL                     # plain call on an outlier shape
+    assert qo(ctypes.byref(s), P, 256, 64, 0, P, P, P, None, None) == KIVI_EINVAL
+    assert qo(ctypes.byref(s), P, 256, 64, 0, P, P, P, P + 4, None) == KIVI_EALIGN
+    assert qo(ctypes.byref(shape()), P, 256, 64, 0, P, P, P, P, None) == KIVI_EINVAL
+    assert qo(ctypes.byref(s), P, 256, 48, 0, P, P, P, P, None) == KIVI_ESHAPE
+    assert qo(ctypes.byref(s), P, 256, 64, 480, P, P, P, P, None) == KIVI_ECAPACITY
+
+
+def test_outlier_cache_needs_its_store():
+    import numpy as np
+    c = cache(outliers=1, tq=64, tr=3)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_EINVAL
+    assert _lib.kivi_decode_attn(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 64, 64, None) == KIVI_EINVAL
+    assert (c.tq, c.tr) == (64, 3)
+    c = cache(outliers=1, tq=64, tr=3, k_out=P + 8)
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_EALIGN
+    r = ragged([64, 32], [3, 1], outliers=2)
+    assert _lib.kivi_ragged_append(ctypes.byref(r), P, P, None) == KIVI_EINVAL
+    assert lens(r) == ([64, 32], [3, 1])
+    g = paged([64, 32], [3, 1], outliers=2)
+    assert _lib.kivi_paged_decode_attn(ctypes.byref(g), P, 0.1, P, None, 0, 1, None) == KIVI_EINVAL
+    assert np.array_equal(g._keep[0], [64, 32])
 
 
 def test_append_errors_leave_state():
@@ -209,7 +256,7 @@ def ragged(tq, tr, ptrs=None, **kw):
     assert len(tqa) == s.batch and len(tra) == s.batch
     p32 = ctypes.POINTER(ctypes.c_int32)
     c = kivi_ragged_cache(s, *(ptrs or [P] * 8), tqa.ctypes.data_as(p32),
-                          tra.ctypes.data_as(p32))
+                          tra.ctypes.data_as(p32), None)
     c._keep = (tqa, tra)
     return c
 
@@ -302,7 +349,7 @@ def paged(tq, tr, page_tokens=128, num_pages=16, table=P, ptrs=None, **kw):
     tra = np.ascontiguousarray(tr, np.int32)
     p32 = ctypes.POINTER(ctypes.c_int32)
     c = kivi_paged_cache(s, page_tokens, num_pages, *(ptrs or [P] * 8), table,
-                         tqa.ctypes.data_as(p32), tra.ctypes.data_as(p32))
+                         tqa.ctypes.data_as(p32), tra.ctypes.data_as(p32), None)
     c._keep = (tqa, tra)
     return c
 
