@@ -35,29 +35,32 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
 
 
-def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4):
+def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4, n_out=0):
     """Algorithmic bytes of one decode call: packed K/V codes, scale and zero
-    of both (mb bytes each: 4 for binary32, 2 for binary16), fp16 residual
-    K/V, fp16 q and out."""
+    of both (mb bytes each: 4 for binary32, 2 for binary16), the key-outlier
+    words (n_out 4-byte words per key group and channel), fp16 residual K/V,
+    fp16 q and out."""
     per = (2 * tq * D * bits // 8 + (tq // G) * D * 2 * mb + tq * (D // G) * 2 * mb
-           + 4 * tr * D + 4 * r * D)
+           + (tq // G) * n_out * D * 4 + 4 * tr * D + 4 * r * D)
     return B * H * per
 
 
-def append_bytes(B, H, D, bits, G, R, flush, mb=4):
+def append_bytes(B, H, D, bits, G, R, flush, mb=4, n_out=0):
     """Algorithmic bytes of one append: read the new K/V token, write it to
     the residual; a flush reads R residual tokens of K and V and writes their
-    codes, scales and zeros."""
+    codes, scales, zeros and key-outlier words."""
     b = B * H * D * 2 * 2 * 2
     if flush:
         b += B * H * (2 * R * D * 2 + 2 * R * D * bits // 8 + (R // G) * D * 2 * mb
-                      + R * (D // G) * 2 * mb)
+                      + R * (D // G) * 2 * mb + (R // G) * n_out * D * 4)
     return b
 
 
 # the sources that define the decode kernel and its launch configuration
 DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.hip",
-                  "decode_mfma_paged.hip", "kivi_internal.h", "kivi_api.hip")
+                  "decode_mfma_paged.hip", "decode_mfma_o1.hip", "decode_mfma_o2.hip",
+                  "decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "kivi_internal.h",
+                  "kivi_api.hip")
 
 
 def kernel_source_hash() -> str:
@@ -141,7 +144,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, 
     print(json.dumps(out))
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False):
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0):
     """The C oracle (single thread) on a bounded sample of the same workload:
     whole decode steps (append with its flush, then attention for all 256
     query heads) repeated until about `min_seconds` of CPU work."""
@@ -158,7 +161,7 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False):
     ocs = []
     for b0, b1 in groups:
         oc = oracle.OracleCache(b1 - b0, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                                w.residual, cap, meta_half=meta_half)
+                                w.residual, cap, meta_half=meta_half, n_out=n_out)
         oc.prefill(k[b0:b1, :, : int(ctx[b0])], v[b0:b1, :, : int(ctx[b0])], int(tqs[b0]))
         ocs.append(oc)
     del k, v
@@ -175,9 +178,9 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False):
             t_total += time.perf_counter() - t0
             n = b1 - b0
             nbytes += append_bytes(n, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
-                                   flush, mb)
+                                   flush, mb, n_out)
             nbytes += decode_bytes(n, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
-                                   oc.tr, mb)
+                                   oc.tr, mb, n_out)
         steps += 1
         if t_total > max_seconds:
             break
@@ -206,6 +209,11 @@ def main():
                     help="storage of the quantization scales and zeros")
     ap.add_argument("--bits", type=int, default=0, choices=[0, 1, 2, 3, 4],
                     help="code width (0: the workload's own)")
+    ap.add_argument("--outliers", type=int, default=0, metavar="N",
+                    help="isolate N key outliers per key group (dense-and-sparse keys)")
+    ap.add_argument("--key-spikes", type=float, default=None, metavar="P",
+                    help="fraction of key entries multiplied by 20 (default: 0.01 with "
+                         "--outliers, else 0)")
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="paged quantized store with P-token pages (0: contiguous planes); the "
                          "block table is a seeded shuffle of the page pool")
@@ -224,7 +232,9 @@ def main():
     meta_half = args.meta == "fp16"
     mb = 2 if meta_half else 4
     # profiles are keyed by workload and metadata width
+    n_out = args.outliers
     tag = (args.workload + (f"_b{args.bits}" if args.bits else "") +
+           (f"_out{n_out}" if n_out else "") +
            (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
@@ -252,6 +262,9 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.bits:
         w = w.with_(bits=args.bits)
+    spikes = args.key_spikes if args.key_spikes is not None else (0.01 if n_out else 0.0)
+    if spikes:
+        w = w.with_(key_spikes=spikes)
     B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
                               w.residual)
     NL = args.layers
@@ -275,13 +288,14 @@ def main():
             mp = cap // args.paged
             perm = np.random.default_rng(1000 + li).permutation(B * mp).astype(np.int32)
             c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp,
-                               table=perm.reshape(B, mp), meta_half=meta_half)
+                               table=perm.reshape(B, mp), meta_half=meta_half, outliers=n_out)
             c.prefill(kd, vd, ctx0, tq0)
         elif ragged:
-            c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+            c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half,
+                                outliers=n_out)
             c.prefill(kd, vd, ctx0, tq0)
         else:
-            c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+            c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out)
             c.prefill(kd, vd, w.tq)
         caches.append(c)
     del kd, vd
@@ -408,15 +422,15 @@ def main():
     # the step's append); ragged: summed over the sequences
     per_seq = 1 if ragged else B
     dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, np.asarray(tq, np.int64),
-                                         np.asarray(tr, np.int64), mb)))
+                                         np.asarray(tr, np.int64), mb, n_out)))
                  for _, tq, tr in meta]
-    app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb)
+    app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb, n_out)
                              for f in np.atleast_1d(fl)]))
                  for fl, _, _ in meta]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
     # The timed call is the decode launch, carrying the new token's append when
     # fused (separate mode: the append launch too); windows hold no flush.
-    new_tok = append_bytes(B, H, D, bits, G, R, False, mb)
+    new_tok = append_bytes(B, H, D, bits, G, R, False, mb, n_out)
     per_call = [d + new_tok for d in dec_bytes]
     win_ms = np.array([e0.elapsed_time(e1) / len(ix) for e0, e1, ix in windows])
     win_bytes = np.array([sum(per_call[i] for i in ix) / len(ix) for _, _, ix in windows])
@@ -456,6 +470,8 @@ def main():
                                   "max": int(ctx0.max()), "per_sequence": ctx0.tolist()}),
             "bits": bits, "group": G, "residual": R,
             "scale_zero": "fp16" if meta_half else "fp32",
+            "key_outliers_per_group": n_out,
+            "key_spikes": w.key_spikes,
             "store": f"paged, {args.paged}-token pages, shuffled block table" if paged
                      else "contiguous planes",
             "layers_rotated": NL, "decode_splits": splits_used,
@@ -486,7 +502,8 @@ def main():
         "kernel_source_hash": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half,
+                                              n_out=n_out)
     print(json.dumps(result), flush=True)
 
 

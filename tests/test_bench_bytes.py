@@ -38,6 +38,20 @@ def test_decode_bytes_match_cache_sizes(meta_half, B, H, r, D, bits, G, R, cap):
     assert bench.append_bytes(B, H, D, bits, G, R, False, mb) == tok
 
 
+@pytest.mark.parametrize("n_out", [1, 2])
+def test_outlier_bytes_match_store_size(n_out):
+    """With key outliers, a decode over a full cache also reads the whole
+    outlier store, and a flush writes R/G groups of it."""
+    B, H, r, D, bits, G, R, cap = 8, 32, 1, 128, 2, 32, 128, 4096
+    s = make_shape(B, H, r, D, bits, G, R, cap, False, n_out)
+    nb = ctypes.c_size_t()
+    assert _lib.kivi_outlier_bytes(ctypes.byref(s), 0, 0, ctypes.byref(nb)) == 0
+    base = bench.decode_bytes(B, H, r, D, bits, G, cap, R, 4)
+    assert bench.decode_bytes(B, H, r, D, bits, G, cap, R, 4, n_out) == base + nb.value
+    f0 = bench.append_bytes(B, H, D, bits, G, R, True, 4)
+    assert bench.append_bytes(B, H, D, bits, G, R, True, 4, n_out) == f0 + nb.value * R // cap
+
+
 @pytest.mark.parametrize("meta_half", [False, True])
 def test_cpu_baseline_runs_its_sample(meta_half):
     """The CPU leg keeps stepping until its time budget (or step cap) is
@@ -47,6 +61,9 @@ def test_cpu_baseline_runs_its_sample(meta_half):
     r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, meta_half=meta_half)
     steps = int(r["sample"].split()[0])
     assert steps > 1
+    r = bench.cpu_baseline(w.with_(key_spikes=0.01), min_seconds=0.05, max_seconds=5.0,
+                           meta_half=meta_half, n_out=2)
+    assert int(r["sample"].split()[0]) > 1
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
 
 
