@@ -17,7 +17,8 @@
  *               papers about the method).
  *   [KVQ-abs]   "KVQuant: Towards 10 Million Context Length LLM Inference with
  *               KV Cache Quantization", codewithpapers.app paper page,
- *               abstract (per-vector dense-and-sparse quantization).
+ *               abstract (per-vector dense-and-sparse quantization; keys
+ *               quantized before the rotary positional embedding).
  *
  * What the pages fix, restated:
  *   - keys are quantized per channel: one group is one channel over a run
@@ -54,6 +55,15 @@
  *     over them alone; outlier positions get code 0 in the dense codes; a
  *     dequantized outlier position is its kept value.  No calibration: a
  *     fixed count per group, chosen from the group itself.
+ *   - pre-RoPE keys (optional, rope_theta > 0) [KVQ-abs: keys are quantized
+ *     before the rotary positional embedding]: the cache holds keys before
+ *     the embedding (quantized and residual alike); attention applies it to
+ *     each dequantized key at the key's position, its token index t in the
+ *     sequence.  The embedding is the rotate-half form: channel pairs
+ *     (i, i + D/2) for i < D/2, frequency f_i = rope_theta^(-2i/D), and
+ *     (x, y) -> (x cos(f_i t) - y sin(f_i t), x sin(f_i t) + y cos(f_i t)).
+ *     Queries arrive with the embedding already applied at their own
+ *     position, as the model computes them.
  *
  * Packed layout (the library's documented storage contract, re-implemented
  * here independently from its description).  Codes are stored in "rows" of
@@ -443,21 +453,38 @@ static double dequant_v(const uint32_t* cw, const void* sc, const void* zr, size
   return (double)c * meta_get(sc, m, meta_half) + meta_get(zr, m, meta_half);
 }
 
+/* Rotary embedding of one key vector kv[D] at position t, in place (the
+ * rotate-half form stated in the file header) [KVQ-abs]. */
+static void rope_key(double* kv, int D, int t, double theta) {
+  const int h = D / 2;
+  for (int i = 0; i < h; i++) {
+    const double f = pow(theta, -2.0 * (double)i / (double)D);
+    const double a = f * (double)t;
+    const double c = cos(a), s = sin(a);
+    const double x = kv[i], y = kv[i + h];
+    kv[i] = x * c - y * s;
+    kv[i + h] = x * s + y * c;
+  }
+}
+
 /* Decode attention over the mixed cache [KIVI-sum: scores on the grouped
  * part, then the residual part is combined with it], binary64 throughout.
  * q, out: [B][H*r][D].  Work space: 2*(tq+tr) doubles in `scratch`.  Keys
- * with isolated outliers (n_out > 0) dequantize through k_outl [KVQ-abs]. */
+ * with isolated outliers (n_out > 0) dequantize through k_outl; with
+ * rope_theta > 0 the cached keys are pre-RoPE and each is rotated at its
+ * position before the dot product [KVQ-abs]. */
 int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
                       int cap, int meta_half, const uint32_t* k_codes, const void* ks,
                       const void* kz, const uint32_t* v_codes,
                       const void* vs, const void* vz, const uint16_t* k_res,
                       const uint16_t* v_res, int tq, int tr, const uint16_t* q,
                       float softmax_scale, double* out, double* scratch,
-                      int n_out, const uint32_t* k_outl) {
+                      int n_out, const uint32_t* k_outl, double rope_theta) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (r < 1) return KIVIO_EINVAL;
   if (n_out < 0 || n_out >= G || (n_out > 0 && !k_outl)) return KIVIO_EINVAL;
+  if (!(rope_theta >= 0.0) || isinf(rope_theta) || D % 2 != 0 || D > 1024) return KIVIO_EINVAL;
   if (tq < 0 || tq % G || tq > cap || tr < 0 || tr > R || tq + tr < 1)
     return KIVIO_ESHAPE;
   const int Hq = H * r, W = words_per_row(D, bits);
@@ -477,13 +504,13 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       const uint16_t* vr = v_res + bh * (size_t)R * D;
       const uint16_t* qv = q + ((size_t)b * Hq + hq) * D;
       for (int t = 0; t < L; t++) {
+        double kvec[1024];
+        for (int d = 0; d < D; d++)
+          kvec[d] = (t < tq) ? dequant_k(kc, ks, kz, kmb, meta_half, D, bits, G, t, d, ko, n_out)
+                             : (double)kivio_half_to_float(kr[(size_t)(t - tq) * D + d]);
+        if (rope_theta > 0.0) rope_key(kvec, D, t, rope_theta);
         double dot = 0.0;
-        for (int d = 0; d < D; d++) {
-          double kv = (t < tq) ? dequant_k(kc, ks, kz, kmb, meta_half, D, bits, G, t, d,
-                                           ko, n_out)
-                               : (double)kivio_half_to_float(kr[(size_t)(t - tq) * D + d]);
-          dot += (double)kivio_half_to_float(qv[d]) * kv;
-        }
+        for (int d = 0; d < D; d++) dot += (double)kivio_half_to_float(qv[d]) * kvec[d];
         logit[t] = (double)softmax_scale * dot;
       }
       double m = logit[0];

@@ -67,7 +67,8 @@ def load():
     lib.kivio_append.restype = _int
     lib.kivio_decode_attn.argtypes = [_int] * 9 + [_u32p, _vp, _vp, _u32p, _vp,
                                                    _vp, _u16p, _u16p, _int, _int, _u16p,
-                                                   ctypes.c_float, _f64p, _f64p, _int, _u32p]
+                                                   ctypes.c_float, _f64p, _f64p, _int, _u32p,
+                                                   ctypes.c_double]
     lib.kivio_decode_attn.restype = _int
     _lib = lib
     return lib
@@ -185,6 +186,7 @@ class OracleCache:
     cap: int
     meta_half: bool = False
     n_out: int = 0          # key outliers per key group (0: none)
+    rope_theta: float = 0.0  # > 0: keys are pre-RoPE, rotated at decode (base rope_theta)
     tq: int = 0
     tr: int = 0
     k_codes: np.ndarray = field(default=None, repr=False)
@@ -262,5 +264,5 @@ def decode_attn(c: OracleCache, q, softmax_scale):
         _p(c.k_res, ctypes.c_uint16, np.uint16), _p(c.v_res, ctypes.c_uint16, np.uint16),
         c.tq, c.tr, _p(q, ctypes.c_uint16, np.uint16), float(softmax_scale),
         _p(out, ctypes.c_double, np.float64), _p(scratch, ctypes.c_double, np.float64),
-        int(c.n_out), _outl(c.k_outl)))
+        int(c.n_out), _outl(c.k_outl), float(c.rope_theta)))
     return out
