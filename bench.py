@@ -59,7 +59,8 @@ def append_bytes(B, H, D, bits, G, R, flush, mb=4, n_out=0):
 # the sources that define the decode kernel and its launch configuration
 DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.hip",
                   "decode_mfma_paged.hip", "decode_mfma_o1.hip", "decode_mfma_o2.hip",
-                  "decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "kivi_internal.h",
+                  "decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "decode_mfma_rope.hip",
+                  "decode_mfma_ragged_rope.hip", "decode_mfma_paged_rope.hip", "kivi_internal.h",
                   "kivi_api.hip")
 
 
@@ -144,7 +145,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, 
     print(json.dumps(out))
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0):
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0,
+                 rope_theta=0.0):
     """The C oracle (single thread) on a bounded sample of the same workload:
     whole decode steps (append with its flush, then attention for all 256
     query heads) repeated until about `min_seconds` of CPU work."""
@@ -161,7 +163,8 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0
     ocs = []
     for b0, b1 in groups:
         oc = oracle.OracleCache(b1 - b0, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                                w.residual, cap, meta_half=meta_half, n_out=n_out)
+                                w.residual, cap, meta_half=meta_half, n_out=n_out,
+                                rope_theta=rope_theta)
         oc.prefill(k[b0:b1, :, : int(ctx[b0])], v[b0:b1, :, : int(ctx[b0])], int(tqs[b0]))
         ocs.append(oc)
     del k, v
@@ -214,6 +217,9 @@ def main():
     ap.add_argument("--key-spikes", type=float, default=None, metavar="P",
                     help="fraction of key entries multiplied by 20 (default: 0.01 with "
                          "--outliers, else 0)")
+    ap.add_argument("--rope", type=float, default=0.0, metavar="THETA",
+                    help="pre-RoPE keys: decode applies the rotary embedding with base THETA "
+                         "(Llama-2: 10000) at each key's position")
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="paged quantized store with P-token pages (0: contiguous planes); the "
                          "block table is a seeded shuffle of the page pool")
@@ -233,8 +239,9 @@ def main():
     mb = 2 if meta_half else 4
     # profiles are keyed by workload and metadata width
     n_out = args.outliers
+    rope = float(args.rope)
     tag = (args.workload + (f"_b{args.bits}" if args.bits else "") +
-           (f"_out{n_out}" if n_out else "") +
+           (f"_out{n_out}" if n_out else "") + ("_rope" if rope > 0 else "") +
            (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
@@ -288,14 +295,16 @@ def main():
             mp = cap // args.paged
             perm = np.random.default_rng(1000 + li).permutation(B * mp).astype(np.int32)
             c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp,
-                               table=perm.reshape(B, mp), meta_half=meta_half, outliers=n_out)
+                               table=perm.reshape(B, mp), meta_half=meta_half, outliers=n_out,
+                               rope_theta=rope)
             c.prefill(kd, vd, ctx0, tq0)
         elif ragged:
             c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half,
-                                outliers=n_out)
+                                outliers=n_out, rope_theta=rope)
             c.prefill(kd, vd, ctx0, tq0)
         else:
-            c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out)
+            c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out,
+                          rope_theta=rope)
             c.prefill(kd, vd, w.tq)
         caches.append(c)
     del kd, vd
@@ -471,6 +480,7 @@ def main():
             "bits": bits, "group": G, "residual": R,
             "scale_zero": "fp16" if meta_half else "fp32",
             "key_outliers_per_group": n_out,
+            "pre_rope_keys_theta": rope,
             "key_spikes": w.key_spikes,
             "store": f"paged, {args.paged}-token pages, shuffled block table" if paged
                      else "contiguous planes",
@@ -503,7 +513,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half,
-                                              n_out=n_out)
+                                              n_out=n_out, rope_theta=rope)
     print(json.dumps(result), flush=True)
 
 

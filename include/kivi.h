@@ -32,6 +32,15 @@
  * and max taken over them alone; outlier positions carry code 0 and
  * dequantize to their kept value.  Selection uses no calibration data.
  *
+ * Pre-RoPE keys (kivi_shape.rope_theta > 0; the same KVQuant page: keys are
+ * quantized before the rotary positional embedding): the cache stores the
+ * keys it is given (quantized and residual) before the embedding, and the
+ * decode applies the embedding to every dequantized key at its position, the
+ * key's token index t in its sequence: channel pairs (i, i + D/2) for i <
+ * D/2 are rotated by the angle t * rope_theta^(-2i/D) (the rotate-half form;
+ * (x, y) -> (x cos - y sin, x sin + y cos)).  Queries are passed with the
+ * embedding already applied at their own position, as a model computes them.
+ *
  * Conventions for every function below:
  *   - All buffer pointers are DEVICE pointers (hipMalloc'd or torch CUDA
  *     tensors), owned by the caller; the library never allocates, frees,
@@ -101,7 +110,10 @@ enum kivi_status {
  *     binary32);
  *   outliers in 0..8 and < group (KIVI_EINVAL): key outliers isolated per
  *     key group (0, the zero-initialised value, = none; every cache then
- *     needs its k_outliers buffer). */
+ *     needs its k_outliers buffer);
+ *   rope_theta finite and >= 0 (KIVI_EINVAL): 0 (the zero-initialised value)
+ *     = keys used as stored; > 0 = pre-RoPE keys rotated at decode with this
+ *     base (10000 for Llama-2). */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -113,6 +125,7 @@ typedef struct {
   int32_t capacity;
   int32_t meta_half;
   int32_t outliers;
+  float rope_theta;
 } kivi_shape;
 
 /* One mixed-precision cache: device buffers (layouts above) plus the host-side
@@ -225,7 +238,11 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
  * Key outliers (shape.outliers > 0): quantized keys are dequantized through
  *   cache->k_outliers (the kept value replaces the dense one); the
  *   matrix-core kernel handles outliers <= 2, larger counts use the generic
- *   kernel. */
+ *   kernel.
+ * Pre-RoPE keys (shape.rope_theta > 0): every key is rotated at its token
+ *   index before the dot product (rule at the top of this file); the
+ *   matrix-core kernel scores keys on the vector units in that case and does
+ *   not combine it with outliers (that combination uses the generic kernel). */
 int kivi_decode_attn(const kivi_cache* cache, const uint16_t* q,
                      float softmax_scale, uint16_t* out, void* workspace,
                      size_t workspace_bytes, int32_t num_splits,

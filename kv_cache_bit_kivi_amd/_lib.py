@@ -30,7 +30,7 @@ STATUS_NAMES = {
 class kivi_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_kv_heads", "gqa_ratio", "head_dim", "bits", "group", "residual",
-        "capacity", "meta_half", "outliers")]
+        "capacity", "meta_half", "outliers")] + [("rope_theta", ctypes.c_float)]
 
 
 class kivi_cache(ctypes.Structure):

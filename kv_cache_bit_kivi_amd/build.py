@@ -31,7 +31,8 @@ EXTRA = {
     "quantize.hip": ["-ffp-contract=off"],
 }
 # (longest compiles first: the pool starts them first)
-SOURCES = ["decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "decode_mfma.hip",
+SOURCES = ["decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "decode_mfma_rope.hip",
+           "decode_mfma_ragged_rope.hip", "decode_mfma_paged_rope.hip", "decode_mfma.hip",
            "decode_mfma_ragged.hip", "decode_mfma_paged.hip", "decode_mfma_o1.hip",
            "decode_mfma_o2.hip", "kivi_api.hip", "quantize.hip", "decode_generic.hip"]
 

@@ -8,7 +8,10 @@
 // values dequantized in registers as code*scale + zero) and the tr residual
 // fp16 tokens, binary32 accumulation.  With key outliers (KVQuant page,
 // abstract: outliers isolated per vector), a key listed in its group's sparse
-// row takes the kept fp16 value instead of the dense one.
+// row takes the kept fp16 value instead of the dense one.  With pre-RoPE keys
+// (a.rope_theta > 0; same page: keys quantized before the rotary embedding)
+// every key is rotated at its token index t before the dot product: pairs
+// (i, i + D/2), angle t * rope_theta^(-2i/D) taken in binary64.
 //
 // One block of 256 threads per (split, b*Hkv + h).  The block owns a
 // contiguous token chunk and all r query heads of its KV head:
@@ -82,6 +85,10 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   float* so = sp + r * kSub;         // [kThreads/D][RR][D] pass-3 partials
   float* red = so + RR * kThreads;   // reduction scratch
   float* stat = red + 8;             // [RR] running max, [RR] running sum, [RR] rescale
+  // pre-RoPE: pair frequencies, binary64 [D/2] (8-byte aligned after stat)
+  double* th = reinterpret_cast<double*>(
+      (reinterpret_cast<uintptr_t>(stat + 3 * RR) + 7) & ~static_cast<uintptr_t>(7));
+  const bool rope = a.rope_theta > 0.f;
 
   const int split = blockIdx.x;
   const int u = seq_plane<RAG>(lens, blockIdx.y, a.H);   // b * H + h
@@ -117,6 +124,9 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
     stat[threadIdx.x] = -INFINITY;
     stat[RR + threadIdx.x] = 0.f;
   }
+  if (rope)
+    for (int i = threadIdx.x; i < D / 2; i += kThreads)
+      th[i] = exp2(-(double)(2 * i) / (double)D * log2((double)a.rope_theta));
   __syncthreads();
 
   const int nsub = kThreads / D;
@@ -135,29 +145,44 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
       for (int i = 0; i < RR; i++) acc[i] = 0.f;
       size_t pl;
       int lt;
-      if (t < tq && slot(t, pl, lt)) {
-        const uint32_t* row = a.k_codes + (pl * scap + lt) * W;
-        const size_t m0 = (pl * (scap / G) + lt / G) * D;
+      const bool quant = t < tq && slot(t, pl, lt);
+      if (quant || t >= tq) {
+        // key channel dd of token t: dequantized (outliers replaced by their
+        // kept value), or the residual fp16 value
+        const uint32_t* row = quant ? a.k_codes + (pl * scap + lt) * W : nullptr;
+        const size_t m0 = quant ? (pl * (scap / G) + lt / G) * D : 0;
         const uint32_t* orow = a.k_out + m0 * a.n_out;   // [n_out][D] of this group
-        const uint32_t my = (uint32_t)(lt % G);
-        for (int dd = 0; dd < D; dd++) {
+        const uint32_t my = quant ? (uint32_t)(lt % G) : 0u;
+        const uint16_t* rrow = quant ? nullptr : kr + (size_t)(t - tq) * D;
+        auto kval = [&](int dd) -> float {
+          if (!quant) return h2f(rrow[dd]);
           float kh = (float)code_at(row, D, bits, dd) * meta_at(a.k_scale, m0 + dd, mh) +
                      meta_at(a.k_zero, m0 + dd, mh);
           for (int j = 0; j < a.n_out; j++) {
             const uint32_t w = orow[(size_t)j * D + dd];
             if ((w >> 16) == my) kh = h2f((uint16_t)(w & 0xFFFFu));
           }
+          return kh;
+        };
+        if (rope) {
+          const int hd = D / 2;
+          for (int p = 0; p < hd; p++) {
+            const float k0 = kval(p), k1 = kval(p + hd);
+            double sn, cs;
+            sincos(th[p] * (double)t, &sn, &cs);
+            const float c = (float)cs, sf = (float)sn;
+            const float kr0 = k0 * c - k1 * sf, kr1 = k0 * sf + k1 * c;
 #pragma unroll
-          for (int i = 0; i < RR; i++)
-            if (i < r) acc[i] += sq[i * D + dd] * kh;
-        }
-      } else if (t >= tq) {
-        const uint16_t* row = kr + (size_t)(t - tq) * D;
-        for (int dd = 0; dd < D; dd++) {
-          const float kh = h2f(row[dd]);
+            for (int i = 0; i < RR; i++)
+              if (i < r) acc[i] += sq[i * D + p] * kr0 + sq[i * D + p + hd] * kr1;
+          }
+        } else {
+          for (int dd = 0; dd < D; dd++) {
+            const float kh = kval(dd);
 #pragma unroll
-          for (int i = 0; i < RR; i++)
-            if (i < r) acc[i] += sq[i * D + dd] * kh;
+            for (int i = 0; i < RR; i++)
+              if (i < r) acc[i] += sq[i * D + dd] * kh;
+          }
         }
       }
 #pragma unroll
@@ -264,7 +289,8 @@ size_t decode_generic_lds_bytes(int r, int D) {
   int rr = 1;
   while (rr < r) rr *= 2;
   const int sub = rr <= 2 ? 1024 : 2048 / rr;
-  return sizeof(float) * ((size_t)r * D + (size_t)r * sub + (size_t)rr * kThreads + 8 + 3 * rr);
+  return sizeof(float) * ((size_t)r * D + (size_t)r * sub + (size_t)rr * kThreads + 8 + 3 * rr) +
+         8 + sizeof(double) * (size_t)(D / 2);   // (+ the pre-RoPE frequencies)
 }
 
 template <bool RAG, bool PG>

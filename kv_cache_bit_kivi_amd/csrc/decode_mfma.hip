@@ -45,13 +45,27 @@
 // Codes are staged through LDS and re-read in the MFMA operand layout.  The
 // block merges its waves in LDS; one split writes fp16 output, more splits
 // write (max, sum, o) partials for the combine kernel.
+//
+// Key outliers ("KVQuant: Towards 10 Million Context Length LLM Inference
+// with KV Cache Quantization", codewithpapers.app paper page, abstract:
+// dense-and-sparse keys, outliers isolated per vector): the dense code of an
+// outlier is 0, so the MFMA score already counts q_d * z_d for it; the kernel
+// adds q_d * (kept value - z_d) per outlier at its token, a sparse correction
+// of the score tile, before the tile maximum is taken.
+//
+// Pre-RoPE keys (same page: keys quantized before the rotary positional
+// embedding): the rotation of a key depends on its position, so the key
+// product is no longer a shared-operand matrix product.  These variants score
+// keys lane-per-token on the VALU in binary32 (dequantize, rotate, dot) while
+// values keep the matrix-core path; see the ROPE parameter of
+// decode_mfma_kernel.
 #include "decode_mfma_impl.h"
 
 namespace kivi {
 
-bool decode_mfma_supported(int D, int G, int r, int n_out) {
+bool decode_mfma_supported(int D, int G, int r, int n_out, bool rope) {
   return D == kD && G == kG && (r == 1 || r == 2 || r == 4 || r == 8) && n_out >= 0 &&
-         n_out <= kMfmaMaxOutliers;
+         n_out <= kMfmaMaxOutliers && !(rope && n_out > 0);
 }
 
 namespace {
@@ -62,7 +76,7 @@ template <int BITS, int R, int NW>
 int occupancy_of() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false, false, 0>),
+          &n, reinterpret_cast<const void*>(&decode_mfma_kernel<BITS, R, NW, false, false, false, 0, false>),
           NW * 64, 0) !=
       hipSuccess)
     return 1;
@@ -113,6 +127,7 @@ int decode_mfma_block_waves(int r, int nw) {
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st) {
+  if (a.rope_theta > 0.f) return launch_decode_mfma_rope(a, nw, st);
   if (a.n_out == 1) return launch_decode_mfma_o1(a, nw, st);
   if (a.n_out == 2) return launch_decode_mfma_o2(a, nw, st);
   return launch_family<false, false, 0>(a, NoLens{}, nw, st);

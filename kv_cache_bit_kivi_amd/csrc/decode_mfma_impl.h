@@ -216,6 +216,27 @@ __device__ __forceinline__ void v_pos(int p, int& m, int& s) {
   }
 }
 
+// Code of channel d (a compile-time constant after unrolling) from the W
+// words of a token's key row, as a float (the documented row layouts: 2 and
+// 4 bits little-endian; 1 bit at beta(d % 32) of word d / 32; 3 bits as the
+// 2-bit plane, then the 1-bit plane of the high bits).
+__device__ __forceinline__ constexpr int beta_pos(int p) {
+  return 4 * ((p & 15) >> 1) + 2 * (p >> 4) + (p & 1);
+}
+template <int BITS>
+__device__ __forceinline__ float key_code(const uint32_t* w, int d) {
+  if constexpr (BITS == 2) {
+    return (float)((w[d >> 4] >> (2 * (d & 15))) & 3u);
+  } else if constexpr (BITS == 4) {
+    return (float)((w[d >> 3] >> (4 * (d & 7))) & 15u);
+  } else if constexpr (BITS == 1) {
+    return (float)((w[d >> 5] >> beta_pos(d & 31)) & 1u);
+  } else {
+    return (float)(((w[d >> 4] >> (2 * (d & 15))) & 3u) |
+                   (((w[kD / 16 + (d >> 5)] >> beta_pos(d & 31)) & 1u) << 2));
+  }
+}
+
 // value arr[2*g + hh] for lane group g without dynamic register indexing
 template <int R>
 __device__ __forceinline__ float pick(const float (&arr)[R], int g, int hh) {
@@ -250,8 +271,10 @@ struct Cfg {
 // the tile loop holds no spill; the one-head 2-bit and four-head 4-bit
 // variants spill a few registers around the loop over residual slices longer
 // than one batch, which runs only for short contexts with few splits.
-template <int BITS, int R>
-constexpr int waves_per_eu() { return R >= 8 ? 1 : ((BITS <= 2 && R == 1) ? 3 : 2); }
+template <int BITS, int R, bool ROPE = false>
+constexpr int waves_per_eu() {
+  return R >= 8 ? 1 : ((BITS <= 2 && R == 1 && !ROPE) ? 3 : 2);
+}
 
 // tiles of loads in flight per wave: one (a second register set measured no
 // faster at two waves per SIMD), two for 8 heads at one wave per SIMD
@@ -266,16 +289,31 @@ constexpr int prefetch_depth() {
 // into the score of its token (the dense code there is 0, so the dense score
 // already holds q_d * zero); these additions go into the wave's own LDS score
 // buffer as LDS atomics, before the MFMA scores are added on top.
-template <int BITS, int R, int NW, bool MH, bool RAG, bool PG, int KO>
+// ROPE: the cached keys are pre-RoPE (a.rope_theta > 0; KO == 0).  Key
+// scores are computed lane-per-token on the VALU: the key is dequantized,
+// rotated by the angle of its position inside the tile (a per-block table
+// F[pair][lane]) and dotted with the query rotated back by the tile's first
+// position (one complex factor per pair, advanced tile to tile in binary64).
+template <int BITS, int R, int NW, bool MH, bool RAG, bool PG, int KO, bool ROPE>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R>(), waves_per_eu<BITS, R>())))
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R, ROPE>(),
+                                   waves_per_eu<BITS, R, ROPE>())))
 decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   static_assert(!PG || RAG, "paged launches carry per-sequence lengths");
   using C = Cfg<BITS, R>;
   constexpr int ROWS = C::ROWS, CH = C::CH;
   constexpr int W = kD * BITS / 32;   // words per key row
   constexpr int WPC = 2 * BITS;       // words per channel per value tile
-  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES];
+  static_assert(!(ROPE && KO > 0), "pre-RoPE keys take no outlier corrections here");
+  // pre-RoPE: the block's table F[pair][lane] = (cos, sin)(theta_pair * lane);
+  // per wave the tile's scale / zero pairs [group][pair][4] (2 KB: in the A
+  // tile region, which the key product no longer uses, when it is that large,
+  // else in a region of its own) and the rotated query [pair][head] (float2,
+  // in the residual-A region: exactly its size)
+  constexpr int RT_BYTES = ROPE ? 64 * 64 * 8 : 0;
+  constexpr int RW_BYTES = (ROPE && C::A_BYTES < 2048) ? 2048 : 0;
+  static_assert(!ROPE || C::RES_BYTES == 64 * R * 8, "rotated query fills the residual-A region");
+  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
@@ -294,6 +332,27 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   char* stg = reinterpret_cast<char*>(lds_dummy) + C::DUMMY_BYTES;   // staged tile codes
   for (int i = threadIdx.x; i < C::ZERO_BYTES / 16; i += NW * 64)
     reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
+  float2* ftab = reinterpret_cast<float2*>(smem + C::ZERO_BYTES + NW * C::WAVE_BYTES);
+  char* rope_wave = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + wv * RW_BYTES;
+  // frequency of pair `lane`: rope_theta^(-2 lane / 128), binary64
+  const double rp_lb = ROPE ? log2((double)a.rope_theta) : 0.0;
+  const double rp_th = ROPE ? exp2(-(double)lane * (1.0 / 64.0) * rp_lb) : 0.0;
+  if constexpr (ROPE) {
+    // thread -> pair lane, lanes l0 .. l0 + 64/NW - 1 of the table: one
+    // binary64 sincos, then exact-enough complex steps in binary64
+    constexpr int LPT = 64 / NW;
+    const int l0 = wv * LPT;
+    double sn, c, ss, sc;
+    sincos(rp_th * (double)l0, &sn, &c);
+    sincos(rp_th, &ss, &sc);
+#pragma unroll
+    for (int k = 0; k < LPT; k++) {
+      ftab[lane * 64 + l0 + k] = float2{(float)c, (float)sn};
+      const double c2 = c * sc - sn * ss;
+      sn = sn * sc + c * ss;
+      c = c2;
+    }
+  }
   __syncthreads();
 
   // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
@@ -549,6 +608,30 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
     for (int e = 0; e < 4; e++) sqn[h][e] = sq[h][e] * qn;
 
+  // pre-RoPE: lane = pair (lane, lane + 64).  The query pair as a complex
+  // number (scaled to the log2 domain), and exp(j theta T) for the position T
+  // of this wave's next tile, advanced by exp(j theta 64) per tile.
+  float qre[R], qim[R];
+  double rp_c = 1.0, rp_s = 0.0, rp_sc = 1.0, rp_ss = 0.0;
+  if constexpr (ROPE) {
+    const uint16_t* qp = a.q + qrow0 * kD;
+#pragma unroll
+    for (int h = 0; h < R; h++) {
+      qre[h] = qs * h2f(qp[h * kD + lane]);
+      qim[h] = qs * h2f(qp[h * kD + lane + 64]);
+    }
+    sincos(rp_th * (64.0 * (double)t_begin), &rp_s, &rp_c);
+    sincos(rp_th * 64.0, &rp_ss, &rp_sc);
+  }
+  float* rp_sz = reinterpret_cast<float*>(RW_BYTES ? rope_wave : lds_a);   // [g][pair][4]
+  float2* rp_q = reinterpret_cast<float2*>(lds_res);                          // [pair][R]
+  // writes the query rotated back by angle theta_pair * T (cos, sin given)
+  auto rope_query = [&](float c, float sn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int h = 0; h < R; h++)
+      rp_q[lane * R + h] = float2{qre[h] * c + qim[h] * sn, qim[h] * c - qre[h] * sn};
+  };
+
   float m_run[R], l_acc[R], l_res[R];
   float gam[R][kNG];
   float ores[R][8];
@@ -624,6 +707,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     // key factors (both groups at once: lanes 0-31 group 0, 32-63 group 1)
     const float ksv[4] = {ks4.x, ks4.y, ks4.z, ks4.w};
     const float kzv[4] = {kz4.x, kz4.y, kz4.z, kz4.w};
+    if constexpr (!ROPE) {
     float beta0[R], beta1[R];
 #pragma unroll
     for (int h = 0; h < R; h++) {
@@ -750,6 +834,61 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       for (int h = 0; h < R; h++) mxs[h] = lane_read((h & 1) ? mx1 : mx0, 16 * (h >> 1));
       apply_max(mxs);
     }
+    } else {
+      // pre-RoPE keys.  (1) this lane's 4 channels' scale / zero, stored per
+      // pair as (s_lo, z_lo, s_hi, z_hi); (2) the query rotated back by the
+      // tile's first position (lane = pair); (3) lane = token: dequantize,
+      // rotate by the in-tile angle, dot with every head.
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int d = cq + e;
+        *reinterpret_cast<float2*>(rp_sz + (kgrp * 64 + (d & 63)) * 4 + 2 * (d >> 6)) =
+            float2{ksv[e], kzv[e]};
+      }
+      rope_query((float)rp_c, (float)rp_s);
+      {
+        const double c2 = rp_c * rp_sc - rp_s * rp_ss;
+        rp_s = rp_s * rp_sc + rp_c * rp_ss;
+        rp_c = c2;
+      }
+      __builtin_amdgcn_wave_barrier();
+      uint32_t wd[W];
+#pragma unroll
+      for (int i = 0; i < W / 4; i++) {
+        const uint4 x = *reinterpret_cast<const uint4*>(stg + lane * W * 4 + 16 * i);
+        wd[4 * i] = x.x;
+        wd[4 * i + 1] = x.y;
+        wd[4 * i + 2] = x.z;
+        wd[4 * i + 3] = x.w;
+      }
+      const float* szg = rp_sz + (lane >> 5) * 64 * 4;
+      float acc[R];
+#pragma unroll
+      for (int h = 0; h < R; h++) acc[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; i++) {
+        const float4 sz = *reinterpret_cast<const float4*>(szg + 4 * i);
+        const float k0 = fmaf(key_code<BITS>(wd, i), sz.x, sz.y);
+        const float k1 = fmaf(key_code<BITS>(wd, i + 64), sz.z, sz.w);
+        const float2 f = ftab[i * 64 + lane];
+        const float kr = f.x * k0 - f.y * k1, ki = f.y * k0 + f.x * k1;
+#pragma unroll
+        for (int h = 0; h < R; h++) {
+          const float2 pq = rp_q[i * R + h];
+          acc[h] = fmaf(pq.x, kr, fmaf(pq.y, ki, acc[h]));
+        }
+      }
+      const bool tok_ok = tile * 64 + lane < tq;
+      float mxs[R];
+#pragma unroll
+      for (int h = 0; h < R; h++) {
+        const float sc = tok_ok ? acc[h] : -INFINITY;
+        lds_sc[h * CH + lane] = sc;
+        mxs[h] = wave_max(sc);
+      }
+      apply_max(mxs);
+      __builtin_amdgcn_wave_barrier();
+    }
     // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
     const bool valid = tile * 64 + lane < tq;
     const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
@@ -815,6 +954,48 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   half8 ar[4];
   auto res_batch = [&](int t16) __attribute__((always_inline)) {
     const int n = min(16, r_end - t16);
+    if constexpr (ROPE) {
+      // the query rotated back by the batch's first position tq + t16 (one
+      // binary64 sincos per pair), then lane (token n16, quarter kg) takes
+      // its 16 pairs (channels 32 m + 8 kg + s and + 64, m = 0, 1) from the
+      // fp16 rows it holds, rotates them by the in-batch angle and reduces
+      // over the four quarters
+      {
+        double sn, c;
+        sincos(rp_th * (double)(tq + t16), &sn, &c);
+        rope_query((float)c, (float)sn);
+      }
+      __builtin_amdgcn_wave_barrier();
+      float part[R];
+#pragma unroll
+      for (int h = 0; h < R; h++) part[h] = 0.f;
+      const u32x4 klo[2] = {rk0, rk1}, khi[2] = {rk2, rk3};
+#pragma unroll
+      for (int m = 0; m < 2; m++)
+#pragma unroll
+        for (int s = 0; s < 8; s++) {
+          const int i = 32 * m + 8 * kg + s;
+          const uint32_t wl = klo[m][s >> 1], wh = khi[m][s >> 1];
+          const float k0 = h2f((uint16_t)((s & 1) ? (wl >> 16) : (wl & 0xFFFFu)));
+          const float k1 = h2f((uint16_t)((s & 1) ? (wh >> 16) : (wh & 0xFFFFu)));
+          const float2 f = ftab[i * 64 + n16];
+          const float kr = f.x * k0 - f.y * k1, ki = f.y * k0 + f.x * k1;
+#pragma unroll
+          for (int h = 0; h < R; h++) {
+            const float2 pq = rp_q[i * R + h];
+            part[h] = fmaf(pq.x, kr, fmaf(pq.y, ki, part[h]));
+          }
+        }
+#pragma unroll
+      for (int h = 0; h < R; h++) {
+        part[h] += __shfl_xor(part[h], 16);
+        part[h] += __shfl_xor(part[h], 32);
+      }
+      if (kg == 0 && n16 < n) {
+#pragma unroll
+        for (int h = 0; h < R; h++) lds_sc[h * CH + n16] = part[h];
+      }
+    } else {
     float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
     acc = mfma(ar[0], __builtin_bit_cast(half8, rk0), acc);
     acc = mfma(ar[1], __builtin_bit_cast(half8, rk1), acc);
@@ -826,6 +1007,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float* p1 = ok ? sc_addr(1, n16) : lds_dummy + n16;
       *p0 = (acc[0] + acc[1]) * qup;
       *p1 = (acc[2] + acc[3]) * qup;
+    }
     }
     __builtin_amdgcn_wave_barrier();
     rescale(n);
@@ -856,7 +1038,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // Residual key A: row (h, hi|lo), MFMA i, lane group kgr, slot s <->
   // channel 32 i + 8 kgr + s.  Lanes 0-31 write channel pairs (cq, cq+1),
   // (cq+2, cq+3) from the scaled query already in registers.
-  if (lane < 32) {
+  if (!ROPE && lane < 32) {
 #pragma unroll
     for (int e = 0; e < 2; e++) {
       const int ch = cq + 2 * e;
@@ -1032,40 +1214,46 @@ constexpr int block_waves(int nw) {
   return (R >= 8 || nw < 8) ? 4 : 8;
 }
 
-template <int BITS, int R, bool MH, bool RAG, bool PG, int KO>
+template <int BITS, int R, bool MH, bool RAG, bool PG, int KO, bool ROPE>
 hipError_t launch_m(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
-  if (block_waves<R>(nw) == 8)
-    decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG, PG, KO>
-        <<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a, lens);
-  else
-    decode_mfma_kernel<BITS, R, 4, MH, RAG, PG, KO><<<grid, 4 * 64, 0, st>>>(a, lens);
+  // (the pre-RoPE 4-bit r = 4 variant needs more LDS than 8 waves have)
+  constexpr bool kSmall = ROPE && BITS == 4 && R == 4;
+  if constexpr (kSmall) {
+    decode_mfma_kernel<BITS, R, 4, MH, RAG, PG, KO, ROPE><<<grid, 4 * 64, 0, st>>>(a, lens);
+  } else {
+    if (block_waves<R>(nw) == 8)
+      decode_mfma_kernel<BITS, R, (R < 8 ? 8 : 4), MH, RAG, PG, KO, ROPE>
+          <<<grid, (R < 8 ? 8 : 4) * 64, 0, st>>>(a, lens);
+    else
+      decode_mfma_kernel<BITS, R, 4, MH, RAG, PG, KO, ROPE><<<grid, 4 * 64, 0, st>>>(a, lens);
+  }
   return hipGetLastError();
 }
-template <int BITS, int R, bool RAG, bool PG, int KO>
+template <int BITS, int R, bool RAG, bool PG, int KO, bool ROPE>
 hipError_t launch_r(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
-  return a.mh ? launch_m<BITS, R, true, RAG, PG, KO>(a, lens, nw, st)
-              : launch_m<BITS, R, false, RAG, PG, KO>(a, lens, nw, st);
+  return a.mh ? launch_m<BITS, R, true, RAG, PG, KO, ROPE>(a, lens, nw, st)
+              : launch_m<BITS, R, false, RAG, PG, KO, ROPE>(a, lens, nw, st);
 }
 
-template <int BITS, bool RAG, bool PG, int KO>
+template <int BITS, bool RAG, bool PG, int KO, bool ROPE>
 hipError_t launch_bits(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   switch (a.r) {
-    case 1: return launch_r<BITS, 1, RAG, PG, KO>(a, lens, nw, st);
-    case 2: return launch_r<BITS, 2, RAG, PG, KO>(a, lens, nw, st);
-    case 4: return launch_r<BITS, 4, RAG, PG, KO>(a, lens, nw, st);
-    default: return launch_r<BITS, 8, RAG, PG, KO>(a, lens, nw, st);
+    case 1: return launch_r<BITS, 1, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    case 2: return launch_r<BITS, 2, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    case 4: return launch_r<BITS, 4, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    default: return launch_r<BITS, 8, RAG, PG, KO, ROPE>(a, lens, nw, st);
   }
 }
 
-// every code width of one (lengths, store, outliers) family
-template <bool RAG, bool PG, int KO>
+// every code width of one (lengths, store, outliers, pre-RoPE) family
+template <bool RAG, bool PG, int KO, bool ROPE = false>
 hipError_t launch_family(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   switch (a.bits) {
-    case 1: return launch_bits<1, RAG, PG, KO>(a, lens, nw, st);
-    case 2: return launch_bits<2, RAG, PG, KO>(a, lens, nw, st);
-    case 3: return launch_bits<3, RAG, PG, KO>(a, lens, nw, st);
-    default: return launch_bits<4, RAG, PG, KO>(a, lens, nw, st);
+    case 1: return launch_bits<1, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    case 2: return launch_bits<2, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    case 3: return launch_bits<3, RAG, PG, KO, ROPE>(a, lens, nw, st);
+    default: return launch_bits<4, RAG, PG, KO, ROPE>(a, lens, nw, st);
   }
 }
 

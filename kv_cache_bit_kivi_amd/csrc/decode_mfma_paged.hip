@@ -7,6 +7,7 @@ namespace kivi {
 
 hipError_t launch_decode_mfma_paged(const DecodeArgs& a, const SeqLens& lens, int nw,
                                     hipStream_t st) {
+  if (a.rope_theta > 0.f) return launch_decode_mfma_paged_rope(a, lens, nw, st);
   if (a.n_out > 0) return launch_decode_mfma_paged_o(a, lens, nw, st);
   return launch_family<true, true, 0>(a, lens, nw, st);
 }

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include <algorithm>
 #include <atomic>
 #include <cstdlib>
@@ -23,6 +25,7 @@ int check_shape(const kivi_shape* s) {
   if (s->bits < 1 || s->bits > 4) return KIVI_EINVAL;
   if (s->meta_half != 0 && s->meta_half != 1) return KIVI_EINVAL;
   if (s->outliers < 0 || s->outliers > 8) return KIVI_EINVAL;   // (< every group size)
+  if (!(s->rope_theta >= 0.f) || isinf(s->rope_theta)) return KIVI_EINVAL;
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
   if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
@@ -92,7 +95,8 @@ int max_auto_splits(const kivi_shape& s) {
 }
 
 bool use_mfma(const kivi_shape& s) {
-  return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers);
+  return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers,
+                                     s.rope_theta > 0.f);
 }
 
 // waves per block of the matrix-core decode kernel
@@ -406,6 +410,7 @@ int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
     a.scale = softmax_scale;
     a.k_out = s.outliers > 0 ? g.k_out + cp * ps.kout_words : nullptr;
     a.n_out = s.outliers;
+    a.rope_theta = s.rope_theta;
     hipError_t e;
     if (use_mfma(s))
       e = g.paged ? kivi::launch_decode_mfma_paged(a, lens, mfma_waves(), st)
@@ -756,6 +761,7 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->pages = kivi::PageMap{nullptr, 0, 0, 0, 0};
   a->k_out = s.outliers > 0 ? c->k_outliers : nullptr;
   a->n_out = s.outliers;
+  a->rope_theta = s.rope_theta;
   return KIVI_OK;
 }
 

@@ -87,6 +87,9 @@ struct DecodeArgs {
   // (page slices [slice][P/G][n_out][D]); null when n_out == 0
   const uint32_t* k_out;
   int n_out;
+  // > 0: the cached keys are pre-RoPE; decode rotates each key at its token
+  // index (rotate-half pairs (i, i + D/2), frequency rope_theta^(-2i/D))
+  float rope_theta;
 };
 
 // Kernel parameter of the decode kernels: nothing (uniform lengths, taken
@@ -168,7 +171,7 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t st);
 // Matrix-core decode kernel: head_dim 128, group 32, gqa ratio 1, 2, 4 or 8,
 // at most kMfmaMaxOutliers key outliers per group.
 constexpr int kMfmaMaxOutliers = 2;
-bool decode_mfma_supported(int D, int G, int r, int n_out);
+bool decode_mfma_supported(int D, int G, int r, int n_out, bool rope);
 // nw: requested waves per block (4 or 8); the block size actually used
 // for a gqa ratio r is decode_mfma_block_waves(r, nw)
 hipError_t launch_decode_mfma(const DecodeArgs& a, int nw, hipStream_t st);
@@ -185,6 +188,12 @@ hipError_t launch_decode_mfma_ragged_o(const DecodeArgs& a, const SeqLens& lens,
                                        hipStream_t st);
 hipError_t launch_decode_mfma_paged_o(const DecodeArgs& a, const SeqLens& lens, int nw,
                                       hipStream_t st);
+// ... and for pre-RoPE keys (a.rope_theta > 0, no outliers)
+hipError_t launch_decode_mfma_rope(const DecodeArgs& a, int nw, hipStream_t st);
+hipError_t launch_decode_mfma_ragged_rope(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                          hipStream_t st);
+hipError_t launch_decode_mfma_paged_rope(const DecodeArgs& a, const SeqLens& lens, int nw,
+                                         hipStream_t st);
 // resident blocks per compute unit of that kernel variant (occupancy query)
 int decode_mfma_blocks_per_cu(int bits, int r, int nw);
 
