@@ -285,10 +285,13 @@ constexpr int prefetch_depth() {
 
 // KO: key outliers per (group, channel) (0, 1 or 2; a.n_out == KO).  Each
 // lane loads the outlier words of its key group and channels cq..cq+3 with
-// the tile's metadata, and adds q_d * (kept value - zero) for every outlier
-// into the score of its token (the dense code there is 0, so the dense score
-// already holds q_d * zero); these additions go into the wave's own LDS score
-// buffer as LDS atomics, before the MFMA scores are added on top.
+// the tile's metadata.  The correction q_d * (kept value - zero) of every
+// outlier (the dense code there is 0, so the dense score already holds
+// q_d * zero) is one more matrix product per slot: the slot's positions
+// become a plane of 0/1 codes in the 2-bit key-row layout (each lane owns
+// the byte of its 4 channels in every token row, so plain byte stores build
+// it), multiplied on the matrix cores by q * (value - zero) as hi/lo rows,
+// into the same accumulators as the dense scores.
 // ROPE: the cached keys are pre-RoPE (a.rope_theta > 0; KO == 0).  Key
 // scores are computed lane-per-token on the VALU: the key is dequantized,
 // rotated by the angle of its position inside the tile (a per-block table
@@ -312,8 +315,12 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // in the residual-A region: exactly its size)
   constexpr int RT_BYTES = ROPE ? 64 * 64 * 8 : 0;
   constexpr int RW_BYTES = (ROPE && C::A_BYTES < 2048) ? 2048 : 0;
+  // outlier slot plane: 64 token rows x 32 bytes, in the staged key-code region
+  // once the key product has read it, or in a region of its own (1-bit codes)
+  constexpr int MK_BYTES = (KO > 0 && C::KC_BYTES < 2048) ? 2048 : 0;
   static_assert(!ROPE || C::RES_BYTES == 64 * R * 8, "rotated query fills the residual-A region");
-  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES];
+  __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES +
+                                     NW * (RW_BYTES + MK_BYTES)];
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
@@ -334,6 +341,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
   float2* ftab = reinterpret_cast<float2*>(smem + C::ZERO_BYTES + NW * C::WAVE_BYTES);
   char* rope_wave = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + wv * RW_BYTES;
+  char* mask_own = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES +
+                   wv * MK_BYTES;
   // frequency of pair `lane`: rope_theta^(-2 lane / 128), binary64
   const double rp_lb = ROPE ? log2((double)a.rope_theta) : 0.0;
   const double rp_th = ROPE ? exp2(-(double)lane * (1.0 / 64.0) * rp_lb) : 0.0;
@@ -402,6 +411,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     int m, s;
     k_pos<BITS>(c & 31, m, s);
     kwr[e] = (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
+  }
+  uint32_t kwr2[2];     // the same in the 2-bit operand order (outlier slot planes)
+#pragma unroll
+  for (int e = 0; e < 2; e++) {
+    const int c = cq + e;
+    int m, s;
+    k_pos<2>(c & 31, m, s);
+    kwr2[e] = (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
   }
   int vm, vs0;
   v_pos<BITS>(lane & 15, vm, vs0);
@@ -726,51 +743,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       beta0[h] = lane_read(bp, 0) + lane_read(bp, 16);
       beta1[h] = lane_read(bp, 32) + lane_read(bp, 48);
     }
-    if constexpr (KO == 0) {
-      if (half_tile && lane < 32) {
+    if (half_tile && lane < 32) {
 #pragma unroll
-        for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
-      }
-    } else {
-      // outlier corrections: the score buffer starts at 0 (-inf for the
-      // absent half of a half tile), each outlier adds q * (value - zero) of
-      // its channel at its token (position masked to the group: no word can
-      // address outside the buffer); the half tile's absent group adds none
-      const float init = (half_tile && lane >= 32) ? -INFINITY : 0.f;
-#pragma unroll
-      for (int h = 0; h < R; h++) lds_sc[h * CH + lane] = init;
-      __builtin_amdgcn_wave_barrier();
-      if (!half_tile || kgrp == 0) {
-        const uint32_t ow[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
-#pragma unroll
-        for (int j = 0; j < KO; j++)
-#pragma unroll
-          for (int e = 0; e < 4; e++) {
-            const uint32_t w = ow[j][e];
-            const float dv = h2f((uint16_t)(w & 0xFFFFu)) - kzv[e];
-            float* dst = lds_sc + 32 * kgrp + ((w >> 16) & 31u);
-#pragma unroll
-            for (int h = 0; h < R; h++)
-              __hip_atomic_fetch_add(dst + h * CH, sq[h][e] * dv, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_WAVEFRONT);
-          }
-      }
+      for (int h = 0; h < R; h++) lds_sc[h * CH + 32 + lane] = -INFINITY;
     }
     __builtin_amdgcn_wave_barrier();
     const int ngr = half_tile ? 1 : 2;
     // per-lane maxima of the scores this lane produces (heads 2kg, 2kg+1)
     float mx0 = -INFINITY, mx1 = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < 2; g++) {
-      if (g < ngr) {
-        half8 af[4];
-#pragma unroll
-        for (int m = 0; m < 4; m++)
-          af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
-        const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
-#pragma unroll
-        for (int mb2 = 0; mb2 < 2; mb2++) {
-          const int mb = 2 * g + mb2;
+    // the key product of 16-token block mb (A tile af of its key group)
+    auto key_block = [&](int mb, const half8 (&af)[4]) __attribute__((always_inline)) {
           float4v acc = float4v{0.f, 0.f, 0.f, 0.f};
           const char* krow = stg + (16 * mb + n16) * W * 4;   // token 16mb + n16
           if constexpr (BITS == 1 || BITS == 3) {
@@ -799,19 +781,111 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
             acc = mfma(af[2], cvt_word4(x.z), acc);
             acc = mfma(af[3], cvt_word4(x.w), acc);
           }
+          return acc;
+    };
+    // scores of block mb from its accumulators -> LDS, running lane maxima
+    auto put_scores = [&](int mb, const float4v& acc, float b0, float b1)
+        __attribute__((always_inline)) {
           const int k = 16 * mb + n16;
-          float* p0 = sc_addr(0, k);
-          float* p1 = sc_addr(1, k);
-          float s0 = (acc[0] + acc[1]) * qup + b0;
-          float s1 = (acc[2] + acc[3]) * qup + b1;
-          if constexpr (KO > 0) {   // + the outlier corrections
-            s0 += *p0;
-            s1 += *p1;
-          }
-          *p0 = s0;
-          *p1 = s1;
+          const float s0 = (acc[0] + acc[1]) * qup + b0;
+          const float s1 = (acc[2] + acc[3]) * qup + b1;
+          *sc_addr(0, k) = s0;
+          *sc_addr(1, k) = s1;
           mx0 = fmaxf(mx0, s0);
           mx1 = fmaxf(mx1, s1);
+    };
+    if constexpr (KO == 0) {
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        if (g < ngr) {
+          half8 af[4];
+#pragma unroll
+          for (int m = 0; m < 4; m++)
+            af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
+          const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
+#pragma unroll
+          for (int mb2 = 0; mb2 < 2; mb2++) put_scores(2 * g + mb2, key_block(2 * g + mb2, af), b0, b1);
+        }
+      }
+    } else {
+      // dense key products of all four blocks first, accumulators kept
+      float4v accs[4];
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        if (g < ngr) {
+          half8 af[4];
+#pragma unroll
+          for (int m = 0; m < 4; m++)
+            af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
+#pragma unroll
+          for (int mb2 = 0; mb2 < 2; mb2++) accs[2 * g + mb2] = key_block(2 * g + mb2, af);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      // outlier slots: (a) A' = q * (kept value - zero) / 4 in the 2-bit
+      // operand order, over the key-A region the dense product has read;
+      // (b) the slot's positions as 0/1 codes in 2-bit key rows (a lane owns
+      // byte cq/4 of each row: its 4 channels); (c) accs += A' x plane, the
+      // plane converted with scale 8 so that a set code reads as 4
+      char* mrow = MK_BYTES ? mask_own : stg;
+      const uint32_t ow[2][4] = {{o0.x, o0.y, o0.z, o0.w}, {o1.x, o1.y, o1.z, o1.w}};
+#pragma unroll
+      for (int j = 0; j < KO; j++) {
+        float dv[4];
+        uint32_t pos[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          dv[e] = 0.25f * (h2f((uint16_t)(ow[j][e] & 0xFFFFu)) - kzv[e]);
+          pos[e] = (ow[j][e] >> 16) & 31u;
+        }
+#pragma unroll
+        for (int h = 0; h < R; h++)
+#pragma unroll
+          for (int e = 0; e < 2; e++) {
+            uint32_t hi, lo;
+            split2(sqn[h][e] * dv[e], sqn[h][e + 2] * dv[e + 2], hi, lo);
+            *reinterpret_cast<uint32_t*>(lds_a + kwr2[e] + (2 * h) * 64) = hi;
+            *reinterpret_cast<uint32_t*>(lds_a + kwr2[e] + (2 * h + 1) * 64) = lo;
+          }
+        reinterpret_cast<uint4*>(mrow + lane * 32)[0] = uint4{0, 0, 0, 0};
+        reinterpret_cast<uint4*>(mrow + lane * 32)[1] = uint4{0, 0, 0, 0};
+        __builtin_amdgcn_wave_barrier();
+        if (!half_tile || kgrp == 0) {
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            uint32_t byte = 0;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; e2++) byte |= (pos[e2] == pos[e] ? 1u : 0u) << (2 * e2);
+            mrow[(32 * kgrp + pos[e]) * 32 + cq / 4] = (char)byte;
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int g = 0; g < 2; g++) {
+          if (g < ngr) {
+            half8 af[4];
+#pragma unroll
+            for (int m = 0; m < 4; m++)
+              af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
+#pragma unroll
+            for (int mb2 = 0; mb2 < 2; mb2++) {
+              const int mb = 2 * g + mb2;
+              const uint2 x = *reinterpret_cast<const uint2*>(mrow + (16 * mb + n16) * 32 + kg * 8);
+              accs[mb] = mfma(af[0], cvt_nib2(x.x & 0x33333333u, 8.0f), accs[mb]);
+              accs[mb] = mfma(af[1], cvt_nib2((x.x >> 2) & 0x33333333u, 8.0f), accs[mb]);
+              accs[mb] = mfma(af[2], cvt_nib2(x.y & 0x33333333u, 8.0f), accs[mb]);
+              accs[mb] = mfma(af[3], cvt_nib2((x.y >> 2) & 0x33333333u, 8.0f), accs[mb]);
+            }
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        if (g < ngr) {
+          const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
+#pragma unroll
+          for (int mb2 = 0; mb2 < 2; mb2++) put_scores(2 * g + mb2, accs[2 * g + mb2], b0, b1);
         }
       }
     }
@@ -865,11 +939,11 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float acc[R];
 #pragma unroll
       for (int h = 0; h < R; h++) acc[h] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 64; i++) {
+      // pair i with the codes of channels i and i + 64
+      auto pair = [&](int i, float c0, float c1) __attribute__((always_inline)) {
         const float4 sz = *reinterpret_cast<const float4*>(szg + 4 * i);
-        const float k0 = fmaf(key_code<BITS>(wd, i), sz.x, sz.y);
-        const float k1 = fmaf(key_code<BITS>(wd, i + 64), sz.z, sz.w);
+        const float k0 = fmaf(c0, sz.x, sz.y);
+        const float k1 = fmaf(c1, sz.z, sz.w);
         const float2 f = ftab[i * 64 + lane];
         const float kr = f.x * k0 - f.y * k1, ki = f.y * k0 + f.x * k1;
 #pragma unroll
@@ -877,6 +951,65 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
           const float2 pq = rp_q[i * R + h];
           acc[h] = fmaf(pq.x, kr, fmaf(pq.y, ki, acc[h]));
         }
+      };
+      if constexpr (BITS == 2) {
+        // a word holds 16 channels: its two nibble planes through the e2m1
+        // convert (scale 2) give the codes as floats, two per instruction
+        // (byte b of plane m -> positions 4b + m, 4b + 2 + m)
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          float lo[16], hi[16];
+          const uint32_t wl[2] = {wd[k], wd[4 + k]};
+#pragma unroll
+          for (int x = 0; x < 2; x++) {
+            float* o = x ? hi : lo;
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+              const uint32_t pl = (wl[x] >> (2 * m)) & 0x33333333u;
+              const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pl, 2.0f, 0);
+              const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pl, 2.0f, 1);
+              const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pl, 2.0f, 2);
+              const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(pl, 2.0f, 3);
+              o[m] = v0[0];
+              o[2 + m] = v0[1];
+              o[4 + m] = v1[0];
+              o[6 + m] = v1[1];
+              o[8 + m] = v2[0];
+              o[10 + m] = v2[1];
+              o[12 + m] = v3[0];
+              o[14 + m] = v3[1];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 16; u++) pair(16 * k + u, lo[u], hi[u]);
+        }
+      } else if constexpr (BITS == 4) {
+        // a word holds 8 channels: low and high nibbles as e4m3 bytes (scale
+        // 2^9 gives the code) -> positions 0,2 | 4,6 and 1,3 | 5,7
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+          float lo[8], hi[8];
+          const uint32_t wl[2] = {wd[k], wd[8 + k]};
+#pragma unroll
+          for (int x = 0; x < 2; x++) {
+            float* o = x ? hi : lo;
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+              const uint32_t pl = (wl[x] >> (4 * m)) & 0x0F0F0F0Fu;
+              const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pl, 512.0f, false);
+              const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(pl, 512.0f, true);
+              o[m] = v0[0];
+              o[2 + m] = v0[1];
+              o[4 + m] = v1[0];
+              o[6 + m] = v1[1];
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < 8; u++) pair(8 * k + u, lo[u], hi[u]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 64; i++) pair(i, key_code<BITS>(wd, i), key_code<BITS>(wd, i + 64));
       }
       const bool tok_ok = tile * 64 + lane < tq;
       float mxs[R];
