@@ -232,9 +232,7 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
  *   (0 = automatic); workspace: device scratch of at least
  *   kivi_decode_workspace_bytes(shape, num_splits) bytes (may be NULL when
  *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  Results are
- *   deterministic for a fixed split count (no floating-point atomics in
- *   global memory; with key outliers, each wave adds its tile's outlier score
- *   corrections into its own LDS score buffer in a fixed instruction order).
+ *   deterministic for a fixed split count (no floating-point atomics).
  * Key outliers (shape.outliers > 0): quantized keys are dequantized through
  *   cache->k_outliers (the kept value replaces the dense one); the
  *   matrix-core kernel handles outliers <= 2, larger counts use the generic

@@ -134,8 +134,7 @@ def test_decode_outliers(shp, splits):
 
 @pytest.mark.parametrize("n_out,r", [(1, 8), (2, 1), (2, 4)])
 def test_decode_outliers_deterministic(n_out, r):
-    """The outlier corrections go through LDS atomics inside one wave: two
-    identical calls still give identical bits."""
+    """Two identical calls with outlier corrections give identical bits."""
     require_gpu()
     announce(f"decode outliers deterministic n_out={n_out} r={r}")
     gc, oc, k, v, q = build(2, 4, r, 128, 2, 32, 128, 2048, 60, n_out, False, seed=5 + r)
