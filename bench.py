@@ -223,6 +223,9 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="paged quantized store with P-token pages (0: contiguous planes); the "
                          "block table is a seeded shuffle of the page pool")
+    ap.add_argument("--deterministic", action="store_true",
+                    help="deterministic caches: every decode wave keeps a fixed run of tiles "
+                         "(repeatable bits) instead of sharing the block's tiles")
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
     ap.add_argument("--window", type=int, default=16, metavar="W",
@@ -242,7 +245,8 @@ def main():
     rope = float(args.rope)
     tag = (args.workload + (f"_b{args.bits}" if args.bits else "") +
            (f"_out{n_out}" if n_out else "") + ("_rope" if rope > 0 else "") +
-           (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else ""))
+           (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else "") +
+           ("_det" if args.deterministic else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
         pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
@@ -296,15 +300,16 @@ def main():
             perm = np.random.default_rng(1000 + li).permutation(B * mp).astype(np.int32)
             c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp,
                                table=perm.reshape(B, mp), meta_half=meta_half, outliers=n_out,
-                               rope_theta=rope)
+                               rope_theta=rope, deterministic=args.deterministic)
             c.prefill(kd, vd, ctx0, tq0)
         elif ragged:
             c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half,
-                                outliers=n_out, rope_theta=rope)
+                                outliers=n_out, rope_theta=rope,
+                                deterministic=args.deterministic)
             c.prefill(kd, vd, ctx0, tq0)
         else:
             c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out,
-                          rope_theta=rope)
+                          rope_theta=rope, deterministic=args.deterministic)
             c.prefill(kd, vd, w.tq)
         caches.append(c)
     del kd, vd
@@ -481,6 +486,8 @@ def main():
             "scale_zero": "fp16" if meta_half else "fp32",
             "key_outliers_per_group": n_out,
             "pre_rope_keys_theta": rope,
+            "decode_tiles": ("fixed per-wave runs (deterministic)" if args.deterministic or rope > 0
+                             else "shared by a block's waves in load-return order"),
             "key_spikes": w.key_spikes,
             "store": f"paged, {args.paged}-token pages, shuffled block table" if paged
                      else "contiguous planes",

@@ -113,7 +113,14 @@ enum kivi_status {
  *     needs its k_outliers buffer);
  *   rope_theta finite and >= 0 (KIVI_EINVAL): 0 (the zero-initialised value)
  *     = keys used as stored; > 0 = pre-RoPE keys rotated at decode with this
- *     base (10000 for Llama-2). */
+ *     base (10000 for Llama-2);
+ *   deterministic in {0, 1} (KIVI_EINVAL): 0 (the zero-initialised value) =
+ *     the matrix-core decode lets the waves of a block take its 64-token
+ *     tiles in the order their loads return, so the binary32 sums group
+ *     differently from call to call and the output can differ in its last
+ *     bits; 1 = every wave keeps a fixed run of tiles and repeated calls
+ *     give identical bits (slower when some waves' loads return late).
+ *     Pre-RoPE keys and the generic kernel always use fixed runs. */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -126,6 +133,7 @@ typedef struct {
   int32_t meta_half;
   int32_t outliers;
   float rope_theta;
+  int32_t deterministic;
 } kivi_shape;
 
 /* One mixed-precision cache: device buffers (layouts above) plus the host-side
@@ -231,8 +239,10 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
  * num_splits: number of context chunks per (b, KV head) reduced at the end
  *   (0 = automatic); workspace: device scratch of at least
  *   kivi_decode_workspace_bytes(shape, num_splits) bytes (may be NULL when
- *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  Results are
- *   deterministic for a fixed split count (no floating-point atomics).
+ *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  With
+ *   shape.deterministic = 1 results are bit-identical between calls for a
+ *   fixed split count (no floating-point atomics anywhere); with 0 they can
+ *   differ in the last bits (tile order inside a block, above).
  * Key outliers (shape.outliers > 0): quantized keys are dequantized through
  *   cache->k_outliers (the kept value replaces the dense one); the
  *   matrix-core kernel handles outliers <= 2, larger counts use the generic

@@ -30,7 +30,8 @@ STATUS_NAMES = {
 class kivi_shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "num_kv_heads", "gqa_ratio", "head_dim", "bits", "group", "residual",
-        "capacity", "meta_half", "outliers")] + [("rope_theta", ctypes.c_float)]
+        "capacity", "meta_half", "outliers")] + [("rope_theta", ctypes.c_float),
+                                                  ("deterministic", ctypes.c_int32)]
 
 
 class kivi_cache(ctypes.Structure):

@@ -24,9 +24,10 @@ def _stream() -> int:
 
 
 def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-               meta_half=False, outliers=0, rope_theta=0.0) -> kivi_shape:
+               meta_half=False, outliers=0, rope_theta=0.0, deterministic=False) -> kivi_shape:
     return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                      int(bool(meta_half)), int(outliers), float(rope_theta))
+                      int(bool(meta_half)), int(outliers), float(rope_theta),
+                      int(bool(deterministic)))
 
 
 def _outlier_store(shape: kivi_shape, lead: int, tokens: int, page_tokens: int, num_pages: int,
@@ -48,14 +49,17 @@ class KiviCache:
     """One layer's cache: packed K/V codes, scale/zero (fp32, or fp16 when
     meta_half), fp16 residual, and with ``outliers`` > 0 the key-outlier
     store (that many kept keys per key group and channel); with
-    ``rope_theta`` > 0 the keys are pre-RoPE and decode rotates them.
+    ``rope_theta`` > 0 the keys are pre-RoPE and decode rotates them; with
+    ``deterministic`` repeated decodes give identical bits (by default the
+    waves of a block share its tiles in load-return order).
 
     Layouts are those of include/kivi.h; the host keeps (tq, tr)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 device="cuda", meta_half=False, outliers=0, rope_theta=0.0):
+                 device="cuda", meta_half=False, outliers=0, rope_theta=0.0,
+                 deterministic=False):
         self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                                meta_half, outliers, rope_theta)
+                                meta_half, outliers, rope_theta, deterministic)
         self.meta_half = bool(meta_half)
         self.outliers = int(outliers)
         mdt = torch.float16 if meta_half else torch.float32
@@ -182,10 +186,11 @@ class RaggedKiviCache(KiviCache):
     (int32 NumPy arrays the C struct points at; the library updates them)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                 device="cuda", meta_half=False, outliers=0, rope_theta=0.0):
+                 device="cuda", meta_half=False, outliers=0, rope_theta=0.0,
+                 deterministic=False):
         super().__init__(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
                          device=device, meta_half=meta_half, outliers=outliers,
-                         rope_theta=rope_theta)
+                         rope_theta=rope_theta, deterministic=deterministic)
         self.tq_arr = np.zeros(batch, np.int32)
         self.tr_arr = np.zeros(batch, np.int32)
         self.rc = kivi_ragged_cache(self.shape, *[t.data_ptr() for t in (
@@ -265,9 +270,9 @@ class PagedKiviCache(RaggedKiviCache):
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
                  page_tokens, num_pages=None, table=None, device="cuda", meta_half=False,
-                 outliers=0, rope_theta=0.0):
+                 outliers=0, rope_theta=0.0, deterministic=False):
         self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                                meta_half, outliers, rope_theta)
+                                meta_half, outliers, rope_theta, deterministic)
         self.meta_half = bool(meta_half)
         self.outliers = int(outliers)
         P = page_tokens

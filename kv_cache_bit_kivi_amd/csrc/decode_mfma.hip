@@ -33,11 +33,12 @@
 // than 2^8 (p <= 256), so the accumulators are rarely rescaled.
 // Residual keys (fp16) feed the MFMA directly; residual values use the VALU.
 //
-// Work: one block of NW waves per (b*Hkv + h, split).  Each wave owns a
-// contiguous run of 64-token value tiles plus a slice of the residual.  Per
-// tile it computes the key scores into LDS, updates the running maximum
-// (online softmax; accumulators are rescaled only when the maximum grows) and
-// accumulates P.V.  Codes and metadata arrive through raw buffer loads, 16
+// Work: one block of NW waves per (b*Hkv + h, split).  The waves take the
+// split's 64-token value tiles as their loads return (one LDS counter per
+// block; fixed contiguous runs for deterministic caches and pre-RoPE keys),
+// and each owns a slice of the residual.  Per tile a wave computes the key
+// scores into LDS, updates the running maximum (online softmax; accumulators
+// are rescaled only when the maximum grows) and accumulates P.V.  Codes and metadata arrive through raw buffer loads, 16
 // bytes per lane (8 for binary16 metadata, widened to binary32 when the tile
 // is computed), one or two tiles ahead of the compute; absent tiles and
 // tokens are loaded out of range (zeros, no memory access) instead of being

@@ -321,6 +321,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   static_assert(!ROPE || C::RES_BYTES == 64 * R * 8, "rotated query fills the residual-A region");
   __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES +
                                      NW * (RW_BYTES + MK_BYTES)];
+  // tiles the block's waves have taken beyond their first two (shared tiles)
+  __shared__ int tile_ctr;
 
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
@@ -339,6 +341,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   char* stg = reinterpret_cast<char*>(lds_dummy) + C::DUMMY_BYTES;   // staged tile codes
   for (int i = threadIdx.x; i < C::ZERO_BYTES / 16; i += NW * 64)
     reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
+  if (threadIdx.x == 0) tile_ctr = 0;
   float2* ftab = reinterpret_cast<float2*>(smem + C::ZERO_BYTES + NW * C::WAVE_BYTES);
   char* rope_wave = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + wv * RW_BYTES;
   char* mask_own = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES +
@@ -394,6 +397,29 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const int nT = (tq + 63) / 64;
   const int t_begin = (int)((int64_t)gw * nT / NWT), t_end = (int)((int64_t)(gw + 1) * nT / NWT);
   const int r_begin = (int)((int64_t)gw * tr / NWT), r_end = (int)((int64_t)(gw + 1) * tr / NWT);
+  // Shared tiles (a.share_tiles): the waves of the block take the split's
+  // tiles [sb, se) as their loads return instead of keeping fixed runs, so a
+  // wave whose loads come back late computes fewer tiles rather than holding
+  // the block back.  Wave wv starts with sb + wv and sb + NW + wv; the k-th
+  // tile taken from the block's counter is sb + 2 NW + k.  Tiles past t_lim
+  // load as zeros and are never computed; a wave's tile indices increase, so
+  // it computes every tile below t_lim that it takes.  Pre-RoPE keys advance
+  // their rotation tile by tile and always keep the fixed runs.
+  const bool share = !ROPE && a.share_tiles != 0;
+  const int sb = (int)((int64_t)split * nT / S), se = (int)((int64_t)(split + 1) * nT / S);
+  const int t_lim = share ? se : t_end;
+  const int t_first = share ? sb + wv : t_begin;
+  int t_given = share ? sb + NW + wv : t_begin + 1;   // last tile handed to this wave
+  // taking a tile is split in two so that the LDS atomic's latency hides
+  // behind a tile's compute: issue() reserves one (lane 0 holds the reply),
+  // take() returns it
+  auto issue = [&](int& pend) __attribute__((always_inline)) {
+    if (share && lane == 0)
+      pend = __hip_atomic_fetch_add(&tile_ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  auto take = [&](const int& pend) __attribute__((always_inline)) -> int {
+    return share ? sb + 2 * NW + __builtin_amdgcn_readfirstlane(pend) : ++t_given;
+  };
 
   // Lane roles.  Every global load is 16 bytes per lane over 1 KB contiguous.
   //  key factors: lane -> key group kgrp = lane/32 of the tile and channels
@@ -442,18 +468,18 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const uint32_t l16 = (uint32_t)lane * 16;
   // Paged store: the page slice of a tile (a scalar table lookup at a
   // wave-uniform index) and the tile's offset inside the slice.  Absent tiles
-  // look up an entry that exists in the sequence's table row (tile t_begin,
+  // look up an entry that exists in the sequence's table row (tile t_first,
   // clamped to the sequence's last tile, or tile 0 when it has none) and
   // load nothing.
   const int P = a.pages.page_tokens;
   const int t_last = nT > 0 ? nT - 1 : 0;
   auto page_tile = [&](int tile, size_t& sp, uint32_t& lt64) __attribute__((always_inline)) {
     const int tu =
-        __builtin_amdgcn_readfirstlane(tile < t_end ? tile : (t_begin < t_last ? t_begin : t_last));
+        __builtin_amdgcn_readfirstlane(tile < t_lim ? tile : (t_first < t_last ? t_first : t_last));
     int tok;
     const bool ok = page_slot(a.pages, b, hh, H, tu * 64, sp, tok);
     lt64 = (uint32_t)(tok / 64);
-    return ok && tile < t_end;
+    return ok && tile < t_lim;
   };
   // codes / metadata of tile `tile` of this wave, or zeros (no memory access)
   // when it is past the wave's last tile.  Codes are reloaded as soon as they
@@ -462,7 +488,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // copy waits for its load).
   auto load_codes = [&](int tile, uint4& x0, uint4& x1, uint4& x2, uint4& x3, uint4& x4,
                         uint4& x5, uint4& x6, uint4& x7) __attribute__((always_inline)) {
-    uint32_t co = tile < t_end ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
+    uint32_t co = tile < t_lim ? (uint32_t)tile * C::KC_BYTES + l16 : kOut;  // KC == VC
     rsrc_t rkc = r_kc, rvc = r_vc;
     if constexpr (PG) {
       size_t sp;
@@ -502,9 +528,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
                        uint4& o1) __attribute__((always_inline)) {
     // 2 key groups x 128 channels, or 64 tokens x 4 value groups: 256 values
     // each, 4 per lane (converted to binary32 when the tile is computed)
-    uint32_t mo = tile < t_end ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
+    uint32_t mo = tile < t_lim ? (uint32_t)tile * (256 * MB) + lane * (4 * MB) : kOut;
     // outlier words j of key group 2*tile + kgrp, channels cq..cq+3
-    uint32_t oo = tile < t_end ? (uint32_t)((2 * tile + kgrp) * KO) * 512 + (lane & 31) * 16 : kOut;
+    uint32_t oo = tile < t_lim ? (uint32_t)((2 * tile + kgrp) * KO) * 512 + (lane & 31) * 16 : kOut;
     rsrc_t rks = r_ks, rkz = r_kz, rvs = r_vs, rvz = r_vz, rko = r_ko;
     if constexpr (PG) {
       size_t sp;
@@ -588,14 +614,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   MetaT a_ks, a_kz, a_vs, a_vz, b_ks, b_kz, b_vs, b_vz;
   uint4 a_o0, a_o1, b_o0, b_o1;   // key-outlier words (KO > 0)
   // (the same issue order as the loop: codes A, meta A, codes B, meta B)
-  load_codes(t_begin, a0, a1, a2, a3, a4, a5, a6, a7);
+  load_codes(t_first, a0, a1, a2, a3, a4, a5, a6, a7);
   __builtin_amdgcn_sched_barrier(0);
-  load_meta(t_begin, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+  load_meta(t_first, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
   if constexpr (DEPTH == 2) {
     __builtin_amdgcn_sched_barrier(0);
-    load_codes(t_begin + 1, b0, b1, b2, b3, b4, b5, b6, b7);
+    load_codes(t_given, b0, b1, b2, b3, b4, b5, b6, b7);
     __builtin_amdgcn_sched_barrier(0);
-    load_meta(t_begin + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+    load_meta(t_given, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1224,57 +1250,82 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   }
 
   // ---------------- quantized tiles, DEPTH tiles of loads in flight
-  // the scheduling barriers keep "stage tile t, issue loads of t+DEPTH,
-  // compute t" in that order, so no wait for a later tile lands before the
-  // compute of tile t.  Loads past the wave's last tile read zeros; the only
-  // branch in the loop (an odd tile count under DEPTH 2) holds no load.
+  // the scheduling barriers keep "stage the current tile, issue the loads of
+  // the tile DEPTH later, compute the current tile" in that order, so no wait
+  // for a later tile lands before the current compute.  Loads of tiles past
+  // t_lim read zeros; the only branch in a loop (the second tile of an
+  // iteration that has none) holds no load.
+  // (cur: the tile in register set a; nxt: the tile loaded after it; the
+  // pending replies pa, pb are each issued a tile's compute before they are
+  // taken)
+  int pa = 0, pb = 0;
   if constexpr (DEPTH == 2) {
-    for (int t = t_begin; t < t_end; t += 2) {
+    // set a holds cur, set b holds nxt; two replies in flight
+    issue(pa);
+    issue(pb);
+    for (int cur = t_first, nxt = t_given; cur < t_lim;) {
       __builtin_amdgcn_sched_barrier(0);
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 2, a0, a1, a2, a3, a4, a5, a6, a7);
+      const int c2 = take(pa);
+      load_codes(c2, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      do_tile(cur, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      load_meta(c2, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      issue(pa);
       __builtin_amdgcn_sched_barrier(0);
       stage(b0, b1, b2, b3, b4, b5, b6, b7);
-      load_codes(t + 3, b0, b1, b2, b3, b4, b5, b6, b7);
+      const int c3 = take(pb);
+      load_codes(c3, b0, b1, b2, b3, b4, b5, b6, b7);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      if (nxt < t_lim) do_tile(nxt, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 3, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      load_meta(c3, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      issue(pb);
+      cur = c2;
+      nxt = c3;
     }
   } else if constexpr (MH) {
     // binary16 metadata (8 registers a set): the next tile's metadata is
     // issued before the current tile's compute, in a second register set,
     // instead of after it (measured 26.2 -> 25.0 us on the batch-8 Llama
     // layer; with binary32 metadata the extra set costs more than it hides)
-    for (int t = t_begin; t < t_end; t += 2) {
+    issue(pa);
+    for (int cur = t_first, nxt = t_given; cur < t_lim;) {
       __builtin_amdgcn_sched_barrier(0);
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 1, a0, a1, a2, a3, a4, a5, a6, a7);
+      load_codes(nxt, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      load_meta(nxt, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
       __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      do_tile(cur, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
+      const int c2 = take(pa);
+      issue(pa);
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 2, a0, a1, a2, a3, a4, a5, a6, a7);
+      load_codes(c2, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 2, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      load_meta(c2, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < t_end) do_tile(t + 1, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      if (nxt < t_lim) do_tile(nxt, b_ks, b_kz, b_vs, b_vz, b_o0, b_o1);
+      __builtin_amdgcn_sched_barrier(0);
+      cur = c2;
+      nxt = take(pa);
+      issue(pa);
     }
   } else {
-    for (int t = t_begin; t < t_end; t++) {
+    issue(pa);
+    for (int cur = t_first, nxt = t_given; cur < t_lim;) {
       __builtin_amdgcn_sched_barrier(0);
       stage(a0, a1, a2, a3, a4, a5, a6, a7);
-      load_codes(t + 1, a0, a1, a2, a3, a4, a5, a6, a7);
+      load_codes(nxt, a0, a1, a2, a3, a4, a5, a6, a7);
       __builtin_amdgcn_sched_barrier(0);
-      do_tile(t, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      do_tile(cur, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
       __builtin_amdgcn_sched_barrier(0);
-      load_meta(t + 1, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      load_meta(nxt, a_ks, a_kz, a_vs, a_vz, a_o0, a_o1);
+      cur = nxt;
+      nxt = take(pa);
+      issue(pa);
     }
   }
 

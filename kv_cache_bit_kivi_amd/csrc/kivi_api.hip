@@ -26,6 +26,7 @@ int check_shape(const kivi_shape* s) {
   if (s->meta_half != 0 && s->meta_half != 1) return KIVI_EINVAL;
   if (s->outliers < 0 || s->outliers > 8) return KIVI_EINVAL;   // (< every group size)
   if (!(s->rope_theta >= 0.f) || isinf(s->rope_theta)) return KIVI_EINVAL;
+  if (s->deterministic != 0 && s->deterministic != 1) return KIVI_EINVAL;
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
   if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
@@ -411,6 +412,7 @@ int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
     a.k_out = s.outliers > 0 ? g.k_out + cp * ps.kout_words : nullptr;
     a.n_out = s.outliers;
     a.rope_theta = s.rope_theta;
+    a.share_tiles = s.deterministic ? 0 : 1;
     hipError_t e;
     if (use_mfma(s))
       e = g.paged ? kivi::launch_decode_mfma_paged(a, lens, mfma_waves(), st)
@@ -762,6 +764,7 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->k_out = s.outliers > 0 ? c->k_outliers : nullptr;
   a->n_out = s.outliers;
   a->rope_theta = s.rope_theta;
+  a->share_tiles = s.deterministic ? 0 : 1;
   return KIVI_OK;
 }
 

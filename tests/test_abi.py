@@ -39,7 +39,8 @@ def test_strerror():
 
 def shape(**kw):
     d = dict(batch=2, num_kv_heads=4, gqa_ratio=2, head_dim=128, bits=2, group=32,
-             residual=128, capacity=512, meta_half=0, outliers=0, rope_theta=0.0)
+             residual=128, capacity=512, meta_half=0, outliers=0, rope_theta=0.0,
+             deterministic=0)
     d.update(kw)
     return kivi_shape(*[d[n] for n, _ in kivi_shape._fields_])
 
@@ -82,6 +83,7 @@ def test_cache_bytes():
     (dict(outliers=-1), KIVI_EINVAL), (dict(outliers=9), KIVI_EINVAL),
     (dict(rope_theta=-1.0), KIVI_EINVAL), (dict(rope_theta=float("inf")), KIVI_EINVAL),
     (dict(rope_theta=float("nan")), KIVI_EINVAL),
+    (dict(deterministic=2), KIVI_EINVAL), (dict(deterministic=-1), KIVI_EINVAL),
 ])
 def test_shape_errors(kw, code):
     assert sizes(shape(**kw))[0] == code

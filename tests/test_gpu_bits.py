@@ -2,7 +2,7 @@
 equals the separate calls bit for bit and meets the oracle, ragged and paged
 caches equal their references, and the batch-8 Llama-2-7B-shaped layer at
 full size (prefill bit-exact against the oracle, every decode row within the
-bar)."""
+bar).  Comparisons of two calls bit for bit use deterministic caches."""
 import numpy as np
 import pytest
 import torch
@@ -31,8 +31,8 @@ def test_fused_stream(bits, r, D, S):
     v = synth.random_fp16(810 + bits + r, (B, H, T, D))
     qs = synth.random_fp16(820 + bits + r, (steps, B, H * r, D))
     cap = (T + R + 63) // 64 * 64
-    sep = KiviCache(B, H, r, D, bits, G, R, cap)
-    fus = KiviCache(B, H, r, D, bits, G, R, cap)
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap)
     kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
     sep.prefill(kd, vd, tq0)
@@ -69,9 +69,10 @@ def test_ragged_and_paged(bits):
     k = synth.random_fp16(900 + bits, (B, H, T, D), scale=2.0)
     v = synth.random_fp16(910 + bits, (B, H, T, D))
     qs = synth.random_fp16(920 + bits, (steps + 1, B, H * r, D))
-    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap)
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
     table = np.random.default_rng(bits).permutation(B * (cap // P)).astype(np.int32)
-    pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, table=table.reshape(B, cap // P))
+    pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, table=table.reshape(B, cap // P),
+                        deterministic=True)
     kd, vd = dev(k), dev(v)
     rc.prefill(kd, vd, ctx, tq)
     pc.prefill(kd, vd, ctx, tq)

@@ -2,7 +2,8 @@
 kivi_append + kivi_decode_attn: identical fp16 output and identical cache
 buffers, bit for bit, at every step (through flushes, for several split
 counts, both bit widths, GQA ratios 1/2/4/8 and a shape outside the
-matrix-core kernel), and the oracle's attention within the usual bar."""
+matrix-core kernel), and the oracle's attention within the usual bar.  The
+caches are deterministic ones, so two calls can agree bit for bit."""
 import numpy as np
 import pytest
 import torch
@@ -41,8 +42,8 @@ def test_fused_equals_separate(case):
     qs = synth.random_fp16(seed + 2, (steps, B, H * r, D))
     cap = (T + R + 63) // 64 * 64
     cap = (cap + G - 1) // G * G
-    sep = KiviCache(B, H, r, D, bits, G, R, cap)
-    fus = KiviCache(B, H, r, D, bits, G, R, cap)
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
     kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
     sep.prefill(kd, vd, tq0)
     fus.prefill(kd, vd, tq0)
@@ -78,8 +79,10 @@ def test_fused_bench_workload_steps():
     announce("fused append+decode llama2_7b_b8_ctx4096")
     k, v = synth.kv(w)
     cap = w.capacity(64)
-    sep = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap)
-    fus = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap)
+    sep = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap,
+                    deterministic=True)
+    fus = KiviCache(w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, w.residual, cap,
+                    deterministic=True)
     kd, vd = dev(k), dev(v)
     sep.prefill(kd, vd, w.tq)
     fus.prefill(kd, vd, w.tq)

@@ -141,8 +141,8 @@ def test_stream16_fused(bits, r):
     v = synth.random_fp16(910 + bits + r, (B, H, T, D))
     qs = synth.random_fp16(920 + bits + r, (n, B, H * r, D))
     cap = (T + R + 63) // 64 * 64
-    sep = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True)
-    fus = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True)
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True, deterministic=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=True, deterministic=True)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=True)
     kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
     sep.prefill(kd, vd, tq0)

@@ -89,14 +89,15 @@ def test_quantize_outliers_ties(n_out):
         compare_k(x, bits, G, T, T, 0, n_out, False, f"ties bits={bits}")
 
 
-def build(B, H, r, D, bits, G, R, tq, tr, n_out, mh, seed, cls=KiviCache):
+def build(B, H, r, D, bits, G, R, tq, tr, n_out, mh, seed, cls=KiviCache, deterministic=False):
     L = tq + tr
     cap = max(64, (tq + 2 * R + 63) // 64 * 64)
     cap = (cap + G - 1) // G * G
     k = synth.spiky_fp16(seed, (B, H, L, D), rate=0.02, scale=2.0)
     v = synth.random_fp16(seed + 1, (B, H, L, D))
     q = synth.random_fp16(seed + 2, (B, H * r, D))
-    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=mh, outliers=n_out)
+    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=mh, outliers=n_out,
+                   deterministic=deterministic)
     gc.prefill(dev(k), dev(v), tq)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=mh, n_out=n_out)
     oc.prefill(k, v, tq)
@@ -137,7 +138,8 @@ def test_decode_outliers_deterministic(n_out, r):
     """Two identical calls with outlier corrections give identical bits."""
     require_gpu()
     announce(f"decode outliers deterministic n_out={n_out} r={r}")
-    gc, oc, k, v, q = build(2, 4, r, 128, 2, 32, 128, 2048, 60, n_out, False, seed=5 + r)
+    gc, oc, k, v, q = build(2, 4, r, 128, 2, 32, 128, 2048, 60, n_out, False, seed=5 + r,
+                            deterministic=True)
     qd = dev(q)
     a = host(gc.decode(qd, SCALE))
     for _ in range(3):
@@ -160,8 +162,8 @@ def test_stream_outliers_fused(bits, n_out, r):
     v = synth.random_fp16(seed + 1, (B, H, T, D))
     qs = synth.random_fp16(seed + 2, (n, B, H * r, D))
     cap = (T + R + 63) // 64 * 64
-    sep = KiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out)
-    fus = KiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out)
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out, deterministic=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out, deterministic=True)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, n_out=n_out)
     kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
     sep.prefill(kd, vd, tq0)
@@ -254,9 +256,9 @@ def test_paged_outliers():
     T = max(ctx) + steps
     k = synth.spiky_fp16(31, (B, H, T, D), rate=0.03, scale=2.0)
     v = synth.random_fp16(32, (B, H, T, D))
-    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out)
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, outliers=n_out, deterministic=True)
     pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, num_pages=B * mp + 4, table=table,
-                        outliers=n_out)
+                        outliers=n_out, deterministic=True)
     rc.prefill(dev(k), dev(v), ctx, tq)
     pc.prefill(dev(k), dev(v), ctx, tq)
     for i in range(steps):

@@ -5,7 +5,8 @@ bit (through prefill, staggered flushes and fused steps).  The table is a
 shuffled page order with spare pages that must stay untouched and, in one
 case, -1 entries past every sequence's reach that must never be needed.  The
 ragged cache itself is checked against the oracle in test_gpu_ragged.py; one
-case here also checks the paged output against the oracle directly."""
+case here also checks the paged output against the oracle directly.  The
+caches compared bit for bit are deterministic ones."""
 import numpy as np
 import pytest
 import torch
@@ -58,9 +59,9 @@ def run_pair(B, H, r, D, bits, G, R, P, ctx, steps, seed, meta_half=False, split
     k[..., 3] *= np.float16(10)
     v = synth.random_fp16(seed + 1, (B, H, T, D))
     qs = synth.random_fp16(seed + 2, (steps + 1, B, H * r, D))
-    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, deterministic=True)
     pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, num_pages=B * mp + spare, table=table,
-                        meta_half=meta_half)
+                        meta_half=meta_half, deterministic=True)
     kd, vd = dev(k), dev(v)
     rc.prefill(kd, vd, ctx, tq)
     pc.prefill(kd, vd, ctx, tq)

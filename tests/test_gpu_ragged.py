@@ -7,7 +7,8 @@ usual row bar.  Covered: ragged prefill (including empty and residual-only
 sequences), decode over split counts larger than a short sequence, both
 kernel paths, both bit widths, GQA ratios, binary16 metadata, staggered
 flushes with the fused step equal to the separate calls, more sequences than
-one launch takes, and equal lengths matching the uniform cache exactly."""
+one launch takes, and equal lengths matching the uniform cache exactly (those
+comparisons of two calls bit for bit use deterministic caches)."""
 import numpy as np
 import pytest
 import torch
@@ -91,9 +92,9 @@ def test_ragged_prefill_decode(case, splits):
     q = synth.random_fp16(7 + B, (B, H * r, D))
     out = host(gc.decode(dev(q), SCALE, num_splits=splits))
     check_decode(gc, ocs, q, out, f"decode S={splits}")
-    # deterministic for a fixed split count
+    # shared tiles: a second call may group the sums differently, within the bar
     again = host(gc.decode(dev(q), SCALE, num_splits=splits))
-    assert np.array_equal(out.view(np.uint16), again.view(np.uint16))
+    check_decode(gc, ocs, q, again, f"decode again S={splits}")
 
 
 @pytest.mark.parametrize("bits,meta_half,r", [(2, False, 1), (4, True, 2), (2, False, 4)])
@@ -114,8 +115,8 @@ def test_ragged_stream_fused(bits, meta_half, r):
     k[..., 2] *= np.float16(10)
     v = synth.random_fp16(310 + bits, (B, H, T, D))
     qs = synth.random_fp16(320 + bits, (steps, B, H * r, D))
-    sep = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
-    fus = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+    sep = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, deterministic=True)
+    fus = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, deterministic=True)
     kd, vd = dev(k), dev(v)
     sep.prefill(kd, vd, ntok, tq)
     fus.prefill(kd, vd, ntok, tq)
@@ -182,8 +183,8 @@ def test_ragged_equal_lengths_match_uniform(D, r, S):
     k = synth.random_fp16(61, (B, H, tq + tr, D), scale=2.0)
     v = synth.random_fp16(62, (B, H, tq + tr, D))
     q = dev(synth.random_fp16(63, (B, H * r, D)))
-    uc = KiviCache(B, H, r, D, bits, G, R, cap)
-    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap)
+    uc = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
     kd, vd = dev(k), dev(v)
     uc.prefill(kd, vd, tq)
     rc.prefill(kd, vd, [tq + tr] * B, [tq] * B)
