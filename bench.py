@@ -486,7 +486,7 @@ def main():
             "scale_zero": "fp16" if meta_half else "fp32",
             "key_outliers_per_group": n_out,
             "pre_rope_keys_theta": rope,
-            "decode_tiles": ("fixed per-wave runs (deterministic)" if args.deterministic or rope > 0
+            "decode_tiles": ("fixed per-wave runs (deterministic)" if args.deterministic
                              else "shared by a block's waves in load-return order"),
             "key_spikes": w.key_spikes,
             "store": f"paged, {args.paged}-token pages, shuffled block table" if paged

@@ -96,6 +96,9 @@ enum kivi_status {
   KIVI_EHIP = 7          /* a HIP launch or runtime call failed             */
 };
 
+/* Largest split count a decode call accepts (num_splits arguments). */
+#define KIVI_MAX_SPLITS 4096
+
 /* Static configuration of one cache (one attention layer).
  * Constraints (KIVI_ESHAPE unless noted):
  *   batch, num_kv_heads, gqa_ratio >= 1 (KIVI_EINVAL);
@@ -120,7 +123,7 @@ enum kivi_status {
  *     differently from call to call and the output can differ in its last
  *     bits; 1 = every wave keeps a fixed run of tiles and repeated calls
  *     give identical bits (slower when some waves' loads return late).
- *     Pre-RoPE keys and the generic kernel always use fixed runs. */
+ *     The generic kernel always uses fixed runs. */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -226,7 +229,8 @@ int kivi_decode_auto_splits(const kivi_cache* cache);
 
 /* Workspace bytes kivi_decode_attn needs for `num_splits` splits of the
  * context; num_splits == 0 returns a bound valid for the automatic split
- * count at every context length of this shape.  Host arithmetic only. */
+ * count at every context length of this shape; 0 for an invalid shape or a
+ * num_splits outside 0..KIVI_MAX_SPLITS.  Host arithmetic only. */
 size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
                                    int32_t num_splits);
 
@@ -237,7 +241,8 @@ size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
  *   tr residual tokens (no mask), accumulated in binary32, written as fp16
  *   (round to nearest even).  q, out: fp16 [B][Hkv*r][D].
  * num_splits: number of context chunks per (b, KV head) reduced at the end
- *   (0 = automatic); workspace: device scratch of at least
+ *   (0 = automatic; at most KIVI_MAX_SPLITS and at most tq + tr, else
+ *   KIVI_ESHAPE); workspace: device scratch of at least
  *   kivi_decode_workspace_bytes(shape, num_splits) bytes (may be NULL when
  *   that is 0).  Requires tq + tr >= 1 (KIVI_ESHAPE).  With
  *   shape.deterministic = 1 results are bit-identical between calls for a
@@ -325,7 +330,8 @@ int kivi_ragged_decode_auto_splits(const kivi_ragged_cache* cache);
 
 /* Decode attention for every sequence at its own lengths (the operation of
  * kivi_decode_attn).  Every sequence must hold at least one token
- * (KIVI_ESHAPE).  num_splits (0 = automatic) applies to every sequence; a
+ * (KIVI_ESHAPE).  num_splits (0 = automatic, at most KIVI_MAX_SPLITS, else
+ * KIVI_ESHAPE) applies to every sequence; a
  * split past a short sequence's end contributes nothing.  The workspace is
  * sized by kivi_decode_workspace_bytes(&cache->shape, num_splits). */
 int kivi_ragged_decode_attn(const kivi_ragged_cache* cache, const uint16_t* q,

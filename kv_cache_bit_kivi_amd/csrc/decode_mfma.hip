@@ -35,7 +35,7 @@
 //
 // Work: one block of NW waves per (b*Hkv + h, split).  The waves take the
 // split's 64-token value tiles as their loads return (one LDS counter per
-// block; fixed contiguous runs for deterministic caches and pre-RoPE keys),
+// block; fixed contiguous runs for deterministic caches),
 // and each owns a slice of the residual.  Per tile a wave computes the key
 // scores into LDS, updates the running maximum (online softmax; accumulators
 // are rescaled only when the maximum grows) and accumulates P.V.  Codes and metadata arrive through raw buffer loads, 16

@@ -247,6 +247,26 @@ __device__ __forceinline__ float pick(const float (&arr)[R], int g, int hh) {
   return v;
 }
 
+// floor(g * n / parts) for 0 <= g <= parts < 2^16 and n >= 0, exactly, in
+// 32-bit arithmetic (g (n mod parts) < 2^32).  This keeps the wave-uniform
+// prologue short: a 64-bit division expands to about a hundred scalar
+// instructions, and the waves of a compute unit share one scalar unit.  (The
+// C ABI caps the split count at 4096, so S * NW < 2^16.)
+__device__ __forceinline__ int part_bound(int g, int n, int parts) {
+  const uint32_t p = (uint32_t)parts, q = (uint32_t)n / p, r = (uint32_t)n - q * p;
+  return (int)((uint32_t)g * q + ((uint32_t)g * r) / p);
+}
+
+// Block barrier that publishes LDS writes but, unlike __syncthreads, does
+// not wait for the wave's outstanding global loads (lgkmcnt(0) only; the
+// signal fences keep the compiler from moving memory accesses across it)
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // vmcnt 63, expcnt 7, lgkmcnt 0
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int BITS, int R>
 struct Cfg {
   static constexpr int ROWS = 2 * R;                    // A rows: (head, hi|lo)
@@ -273,7 +293,7 @@ struct Cfg {
 // than one batch, which runs only for short contexts with few splits.
 template <int BITS, int R, bool ROPE = false>
 constexpr int waves_per_eu() {
-  return R >= 8 ? 1 : ((BITS <= 2 && R == 1 && !ROPE) ? 3 : 2);
+  return (R >= 8 || (ROPE && R >= 2)) ? 1 : ((BITS <= 2 && R == 1 && !ROPE) ? 3 : 2);
 }
 
 // tiles of loads in flight per wave: one (a second register set measured no
@@ -314,7 +334,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // else in a region of its own) and the rotated query [pair][head] (float2,
   // in the residual-A region: exactly its size)
   constexpr int RT_BYTES = ROPE ? 64 * 64 * 8 : 0;
-  constexpr int RW_BYTES = (ROPE && C::A_BYTES < 2048) ? 2048 : 0;
+  // (one head: 1 KB more for the per-pair constant terms of the folded form)
+  constexpr int RW_BYTES = (ROPE && C::A_BYTES < 2048) ? (R == 1 ? 3072 : 2048) : 0;
   // outlier slot plane: 64 token rows x 32 bytes, in the staged key-code region
   // once the key product has read it, or in a region of its own (1-bit codes)
   constexpr int MK_BYTES = (KO > 0 && C::KC_BYTES < 2048) ? 2048 : 0;
@@ -327,8 +348,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int n16 = lane & 15, kg = lane >> 4;
   const int S = a.S, H = a.H;
-  const int u = seq_plane<RAG>(lens, blockIdx.x / S, H), split = blockIdx.x % S;
-  const int b = u / H, hh = u % H;
+  const int bs = (int)(blockIdx.x / (uint32_t)S);
+  const int u = seq_plane<RAG>(lens, bs, H), split = (int)blockIdx.x - bs * S;
+  const int b = (int)((uint32_t)u / (uint32_t)H), hh = u - b * H;
   const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
 
   char* zero = smem;
@@ -342,30 +364,12 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   for (int i = threadIdx.x; i < C::ZERO_BYTES / 16; i += NW * 64)
     reinterpret_cast<uint4*>(zero)[i] = uint4{0, 0, 0, 0};
   if (threadIdx.x == 0) tile_ctr = 0;
+  // (pre-RoPE launches publish these with the table, after the first loads)
+  if constexpr (!ROPE) __syncthreads();
   float2* ftab = reinterpret_cast<float2*>(smem + C::ZERO_BYTES + NW * C::WAVE_BYTES);
   char* rope_wave = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + wv * RW_BYTES;
   char* mask_own = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES +
                    wv * MK_BYTES;
-  // frequency of pair `lane`: rope_theta^(-2 lane / 128), binary64
-  const double rp_lb = ROPE ? log2((double)a.rope_theta) : 0.0;
-  const double rp_th = ROPE ? exp2(-(double)lane * (1.0 / 64.0) * rp_lb) : 0.0;
-  if constexpr (ROPE) {
-    // thread -> pair lane, lanes l0 .. l0 + 64/NW - 1 of the table: one
-    // binary64 sincos, then exact-enough complex steps in binary64
-    constexpr int LPT = 64 / NW;
-    const int l0 = wv * LPT;
-    double sn, c, ss, sc;
-    sincos(rp_th * (double)l0, &sn, &c);
-    sincos(rp_th, &ss, &sc);
-#pragma unroll
-    for (int k = 0; k < LPT; k++) {
-      ftab[lane * 64 + l0 + k] = float2{(float)c, (float)sn};
-      const double c2 = c * sc - sn * ss;
-      sn = sn * sc + c * ss;
-      c = c2;
-    }
-  }
-  __syncthreads();
 
   // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
   const size_t plane = (size_t)u, cap = (size_t)a.cap;
@@ -389,24 +393,23 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   const int t_new = fused ? tr - 1 : -1;
   const rsrc_t r_kn = make_rsrc(fused ? a.k_new + plane * kD : a.k_res, fused ? kD * 2 : 0);
   const rsrc_t r_vn = make_rsrc(fused ? a.v_new + plane * kD : a.v_res, fused ? kD * 2 : 0);
-  const size_t qrow0 = (size_t)b * H * R + (size_t)(u % H) * R;
+  const size_t qrow0 = (size_t)b * H * R + (size_t)hh * R;
   const rsrc_t r_q = make_rsrc(a.q + qrow0 * kD, (uint32_t)(R * kD * 2));
 
   // this wave's share: value tiles [t_begin, t_end) and residual [r_begin, r_end)
   const int NWT = S * NW, gw = split * NW + wv;
   const int nT = (tq + 63) / 64;
-  const int t_begin = (int)((int64_t)gw * nT / NWT), t_end = (int)((int64_t)(gw + 1) * nT / NWT);
-  const int r_begin = (int)((int64_t)gw * tr / NWT), r_end = (int)((int64_t)(gw + 1) * tr / NWT);
+  const int t_begin = part_bound(gw, nT, NWT), t_end = part_bound(gw + 1, nT, NWT);
+  const int r_begin = part_bound(gw, tr, NWT), r_end = part_bound(gw + 1, tr, NWT);
   // Shared tiles (a.share_tiles): the waves of the block take the split's
   // tiles [sb, se) as their loads return instead of keeping fixed runs, so a
   // wave whose loads come back late computes fewer tiles rather than holding
   // the block back.  Wave wv starts with sb + wv and sb + NW + wv; the k-th
   // tile taken from the block's counter is sb + 2 NW + k.  Tiles past t_lim
   // load as zeros and are never computed; a wave's tile indices increase, so
-  // it computes every tile below t_lim that it takes.  Pre-RoPE keys advance
-  // their rotation tile by tile and always keep the fixed runs.
-  const bool share = !ROPE && a.share_tiles != 0;
-  const int sb = (int)((int64_t)split * nT / S), se = (int)((int64_t)(split + 1) * nT / S);
+  // it computes every tile below t_lim that it takes.
+  const bool share = a.share_tiles != 0;
+  const int sb = part_bound(split, nT, S), se = part_bound(split + 1, nT, S);
   const int t_lim = share ? se : t_end;
   const int t_first = share ? sb + wv : t_begin;
   int t_given = share ? sb + NW + wv : t_begin + 1;   // last tile handed to this wave
@@ -625,6 +628,29 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   }
   __builtin_amdgcn_sched_barrier(0);
 
+  // pre-RoPE: the block's table, built while the first loads are in flight
+  // (the barrier after it waits for LDS only, not for those loads)
+  // frequency of pair `lane`: rope_theta^(-2 lane / 128), binary64
+  const double rp_lb = ROPE ? log2((double)a.rope_theta) : 0.0;
+  const double rp_th = ROPE ? exp2(-(double)lane * (1.0 / 64.0) * rp_lb) : 0.0;
+  if constexpr (ROPE) {
+    // thread -> pair lane, lanes l0 .. l0 + 64/NW - 1 of the table: one
+    // binary64 sincos, then exact-enough complex steps in binary64
+    constexpr int LPT = 64 / NW;
+    const int l0 = wv * LPT;
+    double sn, c, ss, sc;
+    sincos(rp_th * (double)l0, &sn, &c);
+    sincos(rp_th, &ss, &sc);
+#pragma unroll
+    for (int k = 0; k < LPT; k++) {
+      ftab[lane * 64 + l0 + k] = float2{(float)c, (float)sn};
+      const double c2 = c * sc - sn * ss;
+      sn = sn * sc + c * ss;
+      c = c2;
+    }
+    lds_barrier();
+  }
+
   // scaled query (log2 domain) of channels cq..cq+3, and its power-of-two
   // normalisation qn so that |q * qn| < 1 (then |q' * qn| < 65536 / 1.5)
   const float qs = a.scale * kLog2e;
@@ -652,10 +678,10 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     for (int e = 0; e < 4; e++) sqn[h][e] = sq[h][e] * qn;
 
   // pre-RoPE: lane = pair (lane, lane + 64).  The query pair as a complex
-  // number (scaled to the log2 domain), and exp(j theta T) for the position T
-  // of this wave's next tile, advanced by exp(j theta 64) per tile.
+  // number (scaled to the log2 domain); each tile rotates it back by its
+  // first position T (one binary64 sincos per lane and tile, so the tiles
+  // can come in any order).
   float qre[R], qim[R];
-  double rp_c = 1.0, rp_s = 0.0, rp_sc = 1.0, rp_ss = 0.0;
   if constexpr (ROPE) {
     const uint16_t* qp = a.q + qrow0 * kD;
 #pragma unroll
@@ -663,8 +689,6 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       qre[h] = qs * h2f(qp[h * kD + lane]);
       qim[h] = qs * h2f(qp[h * kD + lane + 64]);
     }
-    sincos(rp_th * (64.0 * (double)t_begin), &rp_s, &rp_c);
-    sincos(rp_th * 64.0, &rp_ss, &rp_sc);
   }
   float* rp_sz = reinterpret_cast<float*>(RW_BYTES ? rope_wave : lds_a);   // [g][pair][4]
   float2* rp_q = reinterpret_cast<float2*>(lds_res);                          // [pair][R]
@@ -945,13 +969,39 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         *reinterpret_cast<float2*>(rp_sz + (kgrp * 64 + (d & 63)) * 4 + 2 * (d >> 6)) =
             float2{ksv[e], kzv[e]};
       }
-      rope_query((float)rp_c, (float)rp_s);
+      // one head: the query rotated back by the tile's position, P = (pr, pim),
+      // stays in this lane (= pair); several heads share the rotated key
+      float pr = 0.f, pim = 0.f;
       {
-        const double c2 = rp_c * rp_sc - rp_s * rp_ss;
-        rp_s = rp_s * rp_sc + rp_c * rp_ss;
-        rp_c = c2;
+        double tsn, tc;
+        sincos(rp_th * (64.0 * (double)tile), &tsn, &tc);
+        const float c = (float)tc, sn = (float)tsn;
+        if constexpr (R == 1) {
+          pr = qre[0] * c + qim[0] * sn;
+          pim = qim[0] * c - qre[0] * sn;
+        } else {
+          rope_query(c, sn);
+        }
       }
       __builtin_amdgcn_wave_barrier();
+      // One head, folded form: with k0 = c0 s0 + z0, k1 = c1 s1 + z1 and the
+      // in-tile angle (cos, sin), the pair adds cos * X + sin * Y where
+      //   X = P_r k0 + P_i k1 = c0 (P_r s0) + c1 (P_i s1) + (P_r z0 + P_i z1)
+      //   Y = P_i k0 - P_r k1 = c0 (P_i s0) - c1 (P_r s1) + (P_i z0 - P_r z1),
+      // i.e. 6 FMAs per pair and token instead of 8.  Lane = pair computes the
+      // six coefficients of both key groups; the four code factors replace its
+      // (s, z) entries in place, the two constants go to their own 1 KB.
+      float4* rp_co = reinterpret_cast<float4*>(rp_sz);                   // [g][pair]
+      float2* rp_ce = reinterpret_cast<float2*>(rope_wave + 2048);        // [g][pair]
+      if constexpr (R == 1) {
+#pragma unroll
+        for (int g = 0; g < 2; g++) {
+          const float4 sz = rp_co[g * 64 + lane];   // (s0, z0, s1, z1) of pair `lane`
+          rp_co[g * 64 + lane] = float4{pr * sz.x, pim * sz.z, pim * sz.x, -(pr * sz.z)};
+          rp_ce[g * 64 + lane] = float2{pr * sz.y + pim * sz.w, pim * sz.y - pr * sz.w};
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
       uint32_t wd[W];
 #pragma unroll
       for (int i = 0; i < W / 4; i++) {
@@ -967,6 +1017,15 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       for (int h = 0; h < R; h++) acc[h] = 0.f;
       // pair i with the codes of channels i and i + 64
       auto pair = [&](int i, float c0, float c1) __attribute__((always_inline)) {
+        if constexpr (R == 1) {
+          const float4 co = rp_co[(lane >> 5) * 64 + i];
+          const float2 ce = rp_ce[(lane >> 5) * 64 + i];
+          const float X = fmaf(c0, co.x, fmaf(c1, co.y, ce.x));
+          const float Y = fmaf(c0, co.z, fmaf(c1, co.w, ce.y));
+          const float2 f = ftab[i * 64 + lane];
+          acc[0] = fmaf(f.x, X, fmaf(f.y, Y, acc[0]));
+          return;
+        }
         const float4 sz = *reinterpret_cast<const float4*>(szg + 4 * i);
         const float k0 = fmaf(c0, sz.x, sz.y);
         const float k1 = fmaf(c1, sz.z, sz.w);
@@ -978,6 +1037,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
           acc[h] = fmaf(pq.x, kr, fmaf(pq.y, ki, acc[h]));
         }
       };
+      float4 pf_co[8];
+      float2 pf_ce[8], pf_f[8];
+      if constexpr (R == 1 && BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+          pf_co[i] = rp_co[(lane >> 5) * 64 + i];
+          pf_ce[i] = rp_ce[(lane >> 5) * 64 + i];
+          pf_f[i] = ftab[i * 64 + lane];
+        }
+      }
       if constexpr (BITS == 2) {
         // a word holds 16 channels: its two nibble planes through the e2m1
         // convert (scale 2) give the codes as floats, two per instruction
@@ -1006,8 +1075,26 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
               o[14 + m] = v3[1];
             }
           }
+          if constexpr (R == 1) {
+#pragma unroll
+            for (int u = 0; u < 16; u++) {
+              const int i = 16 * k + u;
+              const float4 co = pf_co[i & 7];
+              const float2 ce = pf_ce[i & 7];
+              const float2 f = pf_f[i & 7];
+              if (i + 8 < 64) {
+                pf_co[i & 7] = rp_co[(lane >> 5) * 64 + i + 8];
+                pf_ce[i & 7] = rp_ce[(lane >> 5) * 64 + i + 8];
+                pf_f[i & 7] = ftab[(i + 8) * 64 + lane];
+              }
+              const float X = fmaf(lo[u], co.x, fmaf(hi[u], co.y, ce.x));
+              const float Y = fmaf(lo[u], co.z, fmaf(hi[u], co.w, ce.y));
+              acc[0] = fmaf(f.x, X, fmaf(f.y, Y, acc[0]));
+            }
+          } else {
 #pragma unroll
           for (int u = 0; u < 16; u++) pair(16 * k + u, lo[u], hi[u]);
+          }
         }
       } else if constexpr (BITS == 4) {
         // a word holds 8 channels: low and high nibbles as e4m3 bytes (scale
@@ -1422,8 +1509,10 @@ constexpr int block_waves(int nw) {
 template <int BITS, int R, bool MH, bool RAG, bool PG, int KO, bool ROPE>
 hipError_t launch_m(const DecodeArgs& a, const LensT<RAG>& lens, int nw, hipStream_t st) {
   const dim3 grid(a.B * a.H * a.S);
-  // (the pre-RoPE 4-bit r = 4 variant needs more LDS than 8 waves have)
-  constexpr bool kSmall = ROPE && BITS == 4 && R == 4;
+  // (pre-RoPE keys with several heads per KV head run 4-wave blocks at the
+  // one-wave register budget: at two waves per SIMD their rotated keys and
+  // per-head sums spilled to scratch)
+  constexpr bool kSmall = ROPE && R >= 2;
   if constexpr (kSmall) {
     decode_mfma_kernel<BITS, R, 4, MH, RAG, PG, KO, ROPE><<<grid, 4 * 64, 0, st>>>(a, lens);
   } else {

@@ -330,6 +330,7 @@ int plan_ragged_decode(const Rg& g, std::vector<int> tq, std::vector<int> tr, co
   if (!q || !out) return KIVI_EINVAL;
   if (!aligned16(q) || !aligned16(out)) return KIVI_EALIGN;
   if (num_splits < 0) return KIVI_EINVAL;
+  if (num_splits > KIVI_MAX_SPLITS) return KIVI_ESHAPE;
   const kivi_shape& s = *g.s;
   int max_tq = 0, max_tr = 0;
   for (int b = 0; b < s.batch; b++) {
@@ -707,7 +708,7 @@ int kivi_decode_auto_splits(const kivi_cache* c) {
 }
 
 size_t kivi_decode_workspace_bytes(const kivi_shape* s, int32_t num_splits) {
-  if (check_shape(s) != KIVI_OK || num_splits < 0) return 0;
+  if (check_shape(s) != KIVI_OK || num_splits < 0 || num_splits > KIVI_MAX_SPLITS) return 0;
   return ws_bytes(*s, num_splits == 0 ? max_auto_splits(*s) : num_splits);
 }
 
@@ -722,7 +723,7 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   const kivi_shape& s = c->shape;
   const int L = tq + tr;
   if (L < 1) return KIVI_ESHAPE;
-  if (num_splits > 0 && num_splits > L) return KIVI_ESHAPE;
+  if (num_splits > 0 && (num_splits > L || num_splits > KIVI_MAX_SPLITS)) return KIVI_ESHAPE;
   int S = num_splits;
   if (S == 0) {
     const int cus = device_cu_count();

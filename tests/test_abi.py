@@ -212,6 +212,11 @@ def test_decode_errors():
     assert dec(ctypes.byref(c), P, 0.1, P, P + 4, need, 4, None) == KIVI_EALIGN
     c = cache(tq=64, tr=200)
     assert dec(ctypes.byref(c), P, 0.1, P, None, 0, 1, None) == KIVI_ESHAPE
+    # at most KIVI_MAX_SPLITS = 4096 splits, even with more tokens than that
+    c = cache(tq=4224, tr=100, capacity=4352)
+    need = _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4096)
+    assert need > 0 and _lib.kivi_decode_workspace_bytes(ctypes.byref(c.shape), 4097) == 0
+    assert dec(ctypes.byref(c), P, 0.1, P, P, 1 << 40, 4097, None) == KIVI_ESHAPE
 
 
 def test_workspace_bytes():

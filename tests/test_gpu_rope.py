@@ -8,7 +8,8 @@ Bar: the quantized store bit-exact (it does not depend on the embedding);
 attention within the row bar on the matrix-core kernel's pre-RoPE variant
 (lane-per-token key scores) and on the generic kernel, over split counts,
 positions up to 64K, ragged and paged stores, the fused step and the
-full-size Llama-2-7B-shaped layer."""
+full-size Llama-2-7B-shaped layer.  Comparisons of two calls bit for bit use
+deterministic caches."""
 import numpy as np
 import pytest
 import torch
@@ -31,14 +32,15 @@ def keys(seed, shape):
     return k
 
 
-def build(B, H, r, D, bits, G, R, tq, tr, theta, mh, seed, n_out=0):
+def build(B, H, r, D, bits, G, R, tq, tr, theta, mh, seed, n_out=0, deterministic=False):
     L = tq + tr
     cap = max(64, (tq + 2 * R + 63) // 64 * 64)
     cap = (cap + G - 1) // G * G
     k = keys(seed, (B, H, L, D))
     v = synth.random_fp16(seed + 1, (B, H, L, D))
     q = synth.random_fp16(seed + 2, (B, H * r, D))
-    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=mh, outliers=n_out, rope_theta=theta)
+    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=mh, outliers=n_out, rope_theta=theta,
+                   deterministic=deterministic)
     gc.prefill(dev(k), dev(v), tq)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=mh, n_out=n_out,
                             rope_theta=theta)
@@ -90,14 +92,22 @@ def test_decode_rope_long_positions(splits):
     assert row_rel_err(out, ref) <= ATTN_TOL
 
 
-def test_decode_rope_deterministic():
+@pytest.mark.parametrize("r", [1, 2])
+def test_decode_rope_deterministic(r):
+    """A deterministic cache repeats its bits; the default (shared tiles)
+    stays within the bar on every call."""
     require_gpu()
-    announce("decode rope deterministic")
-    gc, oc, k, v, q = build(2, 4, 2, 128, 2, 32, 128, 2048, 60, 10000.0, False, seed=5)
+    announce(f"decode rope deterministic r={r}")
+    gc, oc, k, v, q = build(2, 4, r, 128, 2, 32, 128, 2048, 60, 10000.0, False, seed=5,
+                            deterministic=True)
     qd = dev(q)
     a = host(gc.decode(qd, SCALE))
     for _ in range(3):
         assert np.array_equal(a.view(np.uint16), host(gc.decode(qd, SCALE)).view(np.uint16))
+    gs, _, _, _, _ = build(2, 4, r, 128, 2, 32, 128, 2048, 60, 10000.0, False, seed=5)
+    ref = oc.decode(q, SCALE)
+    for _ in range(3):
+        assert row_rel_err(host(gs.decode(qd, SCALE)).astype(np.float64), ref) <= ATTN_TOL
 
 
 @pytest.mark.parametrize("bits,r", [(2, 1), (4, 4), (1, 2), (3, 8)])
@@ -115,8 +125,8 @@ def test_stream_rope_fused(bits, r):
     v = synth.random_fp16(seed + 1, (B, H, T, D))
     qs = synth.random_fp16(seed + 2, (n, B, H * r, D))
     cap = (T + R + 63) // 64 * 64
-    sep = KiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0)
-    fus = KiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0)
+    sep = KiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0, deterministic=True)
+    fus = KiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0, deterministic=True)
     oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0)
     kd, vd = dev(k[:, :, : tq0 + tr0]), dev(v[:, :, : tq0 + tr0])
     sep.prefill(kd, vd, tq0)
@@ -182,9 +192,9 @@ def test_paged_rope():
     T = max(ctx) + steps
     k = keys(61, (B, H, T, D))
     v = synth.random_fp16(62, (B, H, T, D))
-    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0)
+    rc = RaggedKiviCache(B, H, r, D, bits, G, R, cap, rope_theta=10000.0, deterministic=True)
     pc = PagedKiviCache(B, H, r, D, bits, G, R, cap, P, num_pages=B * mp + 3,
-                        table=table.reshape(B, mp), rope_theta=10000.0)
+                        table=table.reshape(B, mp), rope_theta=10000.0, deterministic=True)
     rc.prefill(dev(k), dev(v), ctx, tq)
     pc.prefill(dev(k), dev(v), ctx, tq)
     for i in range(steps):
