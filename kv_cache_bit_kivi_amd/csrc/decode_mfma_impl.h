@@ -1037,6 +1037,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
           acc[h] = fmaf(pq.x, kr, fmaf(pq.y, ki, acc[h]));
         }
       };
+      // one head, 2-bit codes: the coefficients and table entries of pair
+      // i + 8 are read while pair i is computed (an 8-deep ring), so that
+      // the compiler does not wait for each LDS read right before its use
       float4 pf_co[8];
       float2 pf_ce[8], pf_f[8];
       if constexpr (R == 1 && BITS == 2) {
