@@ -1338,6 +1338,19 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     res_batch(t16);
     if (fused) write_new(t16);
   }
+  // From here on the residual's sums only rescale: reduce them across lanes
+  // now, while the first tile's loads are in flight, rather than after the
+  // last tile (value partials: over the token groups in lanes c8, c8 + 16,
+  // c8 + 32, c8 + 48; the probability sum over the whole wave)
+#pragma unroll
+  for (int h = 0; h < R; h++) {
+    l_res[h] = wave_sum(l_res[h]);
+#pragma unroll
+    for (int e = 0; e < 8; e++) {
+      ores[h][e] += __shfl_xor(ores[h][e], 16);
+      ores[h][e] += __shfl_xor(ores[h][e], 32);
+    }
+  }
 
   // ---------------- quantized tiles, DEPTH tiles of loads in flight
   // the scheduling barriers keep "stage the current tile, issue the loads of
@@ -1430,10 +1443,10 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       *o1 = cv[nb][2] + cv[nb][3];
     }
   }
-  // residual P.V partials: lanes c8, c8+16, c8+32, c8+48 (the 4 token groups)
-  // hold channels 8*c8..8*c8+7; sum them across lanes, then lane (tg, c8) adds
-  // channels 8*c8+2*tg, 8*c8+2*tg+1 (value group c8/4) together with the Gamma
-  // term of that group
+  // residual P.V sums (already reduced over the token groups: every lane
+  // c8 + 16 k holds channels 8*c8..8*c8+7): lane (tg, c8) adds channels
+  // 8*c8+2*tg, 8*c8+2*tg+1 (value group c8/4) together with the Gamma term of
+  // that group
   __builtin_amdgcn_wave_barrier();
   {
     const int tg = lane >> 4, c8 = lane & 15, grp = c8 >> 2;
@@ -1442,7 +1455,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float g[kNG];
 #pragma unroll
       for (int j = 0; j < kNG; j++) g[j] = wave_sum(gam[h][j]);
-      const float lsum = wave_sum(l_acc[h]) + wave_sum(l_res[h]);
+      const float lsum = wave_sum(l_acc[h]) + l_res[h];
       float gj = g[0];
 #pragma unroll
       for (int j = 1; j < kNG; j++)
@@ -1450,11 +1463,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e++) {
-        float x = ores[h][e];
-        x += __shfl_xor(x, 16);
-        x += __shfl_xor(x, 32);
-        if (e == 2 * tg) rs0 = x;
-        if (e == 2 * tg + 1) rs1 = x;
+        if (e == 2 * tg) rs0 = ores[h][e];
+        if (e == 2 * tg + 1) rs1 = ores[h][e];
       }
       float2* op = reinterpret_cast<float2*>(lds_o + h * kD + 8 * c8 + 2 * tg);
       float2 o2 = *op;

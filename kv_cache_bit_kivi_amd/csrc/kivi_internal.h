@@ -91,7 +91,7 @@ struct DecodeArgs {
   // index (rotate-half pairs (i, i + D/2), frequency rope_theta^(-2i/D))
   float rope_theta;
   // 1: the waves of a block share its tiles in load-return order (matrix-core
-  // kernel, keys used as stored); 0: fixed per-wave runs (reproducible)
+  // kernel); 0: fixed per-wave runs (reproducible)
   int share_tiles;
 };
 
