@@ -285,15 +285,17 @@ struct Cfg {
   static_assert(WAVE_BYTES % 16 == 0 && A_BYTES % 16 == 0, "b128 LDS accesses need 16-byte alignment");
 };
 
-// register budget of the occupancy target: one wave per SIMD for 8 heads, the
-// three-wave budget for one head at 2 bits (measured fastest), two waves
-// otherwise.  Blocks of 8 waves still place two per SIMD.  At these budgets
-// the tile loop holds no spill; the one-head 2-bit and four-head 4-bit
-// variants spill a few registers around the loop over residual slices longer
-// than one batch, which runs only for short contexts with few splits.
-template <int BITS, int R, bool ROPE = false>
+// register budget of the occupancy target: one wave per SIMD for 8 heads and
+// for pre-RoPE keys with several heads, the three-wave budget for one head at
+// 2 bits without outliers (measured fastest), two waves otherwise (the
+// outlier variants spilled 68-80 bytes per lane at the three-wave budget).
+// Blocks of 8 waves still place two per SIMD.  At these budgets the one-head
+// 2-bit and four-head 4-bit variants spill a few registers around the loop
+// over residual slices longer than one batch, which runs only for short
+// contexts with few splits.
+template <int BITS, int R, bool ROPE = false, int KO = 0>
 constexpr int waves_per_eu() {
-  return (R >= 8 || (ROPE && R >= 2)) ? 1 : ((BITS <= 2 && R == 1 && !ROPE) ? 3 : 2);
+  return (R >= 8 || (ROPE && R >= 2)) ? 1 : ((BITS <= 2 && R == 1 && !ROPE && KO == 0) ? 3 : 2);
 }
 
 // tiles of loads in flight per wave: one (a second register set measured no
@@ -319,8 +321,8 @@ constexpr int prefetch_depth() {
 // position (one complex factor per pair, advanced tile to tile in binary64).
 template <int BITS, int R, int NW, bool MH, bool RAG, bool PG, int KO, bool ROPE>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R, ROPE>(),
-                                   waves_per_eu<BITS, R, ROPE>())))
+__attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R, ROPE, KO>(),
+                                   waves_per_eu<BITS, R, ROPE, KO>())))
 decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   static_assert(!PG || RAG, "paged launches carry per-sequence lengths");
   using C = Cfg<BITS, R>;
