@@ -286,16 +286,14 @@ struct Cfg {
 };
 
 // register budget of the occupancy target: one wave per SIMD for 8 heads and
-// for pre-RoPE keys with several heads, the three-wave budget for one head at
-// 2 bits without outliers (measured fastest), two waves otherwise (the
-// outlier variants spilled 68-80 bytes per lane at the three-wave budget).
-// Blocks of 8 waves still place two per SIMD.  At these budgets the one-head
-// 2-bit and four-head 4-bit variants spill a few registers around the loop
-// over residual slices longer than one batch, which runs only for short
-// contexts with few splits.
+// for pre-RoPE keys with several heads, two waves otherwise (blocks of 8 waves
+// place two per SIMD).  The three-wave budget spilled 56 bytes per lane in the
+// one-head 2-bit variant (27.5 against 27.2 us on the batch-8 Llama layer at
+// two waves) and 68-80 bytes with outliers.  The four-head variants still
+// spill 16-68 bytes per lane at two waves.
 template <int BITS, int R, bool ROPE = false, int KO = 0>
 constexpr int waves_per_eu() {
-  return (R >= 8 || (ROPE && R >= 2)) ? 1 : ((BITS <= 2 && R == 1 && !ROPE && KO == 0) ? 3 : 2);
+  return (R >= 8 || (ROPE && R >= 2)) ? 1 : 2;
 }
 
 // tiles of loads in flight per wave: one (a second register set measured no
