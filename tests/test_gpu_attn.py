@@ -103,6 +103,21 @@ def test_decode_deterministic_and_guarded(deterministic):
         assert np.all(g[:1024] == 0x7BAD) and np.all(g[1024 + n:] == 0x7BAD)
 
 
+@pytest.mark.parametrize("deterministic", [False, True])
+def test_decode_max_splits(deterministic):
+    """num_splits at its cap (4096 splits of an 8K context: 32768 waves, most
+    without a tile): the wave shares' 32-bit arithmetic at its widest, and the
+    combine over 4096 partials, one and four heads."""
+    require_gpu()
+    for r in (1, 4):
+        announce(f"decode max splits r={r} deterministic={deterministic}")
+        gc, oc, q = build_pair(1, 1, r, 128, 2, 32, 128, 8128, 100, seed=31 + r,
+                               deterministic=deterministic)
+        ref = oc.decode(q, 0.0883883461356163)
+        out = host(gc.decode(dev(q), 0.0883883461356163, num_splits=4096)).astype(np.float64)
+        assert row_rel_err(out, ref) <= ATTN_TOL
+
+
 def test_split_count_invariance():
     require_gpu()
     announce("split invariance")
