@@ -8,10 +8,12 @@ context 4096 at the start of the timed region): append the new token's K/V
 decode attention for every query head, as one kivi_append_decode_attn call
 (the append is folded into the decode launch; `--separate` times
 kivi_append + kivi_decode_attn instead).  Steps rotate over `--layers`
-independent layer caches (8 by default, 1.2 GB in total) so that no step finds
-its cache resident in the 256 MB Infinity Cache left by the previous step;
-each layer starts with a full residual, so with 1024 steps every layer flushes
-once per 128 appends, the method's own rate.
+independent layer caches, by default the model's 32 layers (4.6 GB in total;
+fewer for larger layers, within 16 GB), as a decode step of the whole model
+visits them, so that no step finds its cache resident in the 256 MB Infinity
+Cache left by the previous step.  By default 128 steps per layer are timed
+(4096); each layer starts with a full residual, so every layer flushes once
+per 128 appends, the method's own rate.
 
 Prints one JSON line: whole-step algorithmic HBM GB/s (value), query-heads/s,
 the roofline of the dominant kernel (decode attention with the folded append,
@@ -203,10 +205,13 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (default: 128 per rotated layer cache)")
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="llama2_7b_b8_ctx4096")
-    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--layers", type=int, default=0,
+                    help="layer caches the steps rotate over (default: 32, Llama-2-7B's layer "
+                         "count, or fewer so that they stay within 16 GB)")
     ap.add_argument("--splits", type=int, default=0, help="decode split count (0 = automatic)")
     ap.add_argument("--meta", choices=["fp32", "fp16"], default="fp32",
                     help="storage of the quantization scales and zeros")
@@ -278,6 +283,11 @@ def main():
         w = w.with_(key_spikes=spikes)
     B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
                               w.residual)
+    if args.layers <= 0:
+        layer_bytes = decode_bytes(B, H, r, D, bits, G, int(w.context), R, mb, n_out)
+        args.layers = int(max(2, min(32, 16e9 // layer_bytes)))
+    if args.steps <= 0:
+        args.steps = 128 * args.layers
     NL = args.layers
     total_steps = args.warmup + args.steps
     per_layer_appends = (total_steps + NL - 1) // NL
