@@ -2,24 +2,29 @@
 """Benchmark of the quantized-KV decode hot path on one MI355X.
 
 A step is one decode step of one attention layer of the Llama-2-7B-shaped
-workload (batch 8, 32 heads, head_dim 128, 2-bit codes, G = 32, R = 128,
-context 4096 at the start of the timed region): append the new token's K/V
-(quantizing the full residual into the grouped part when it is full), then
-decode attention for every query head, as one kivi_append_decode_attn call
-(the append is folded into the decode launch; `--separate` times
-kivi_append + kivi_decode_attn instead).  Steps rotate over `--layers`
-independent layer caches, by default the model's 32 layers (4.6 GB in total;
-fewer for larger layers, within 16 GB), as a decode step of the whole model
-visits them, so that no step finds its cache resident in the 256 MB Infinity
-Cache left by the previous step.  By default 128 steps per layer are timed
-(4096); each layer starts with a full residual, so every layer flushes once
-per 128 appends, the method's own rate.
+workload (batch 8, 32 heads, head_dim 128, 2-bit codes, G = 32, R = 128):
+append the new token's K/V (quantizing the full residual into the grouped
+part first when it is full), then decode attention for every query head, as
+one kivi_append_decode_attn call (the append is folded into the decode
+launch; `--separate` times kivi_append + kivi_decode_attn instead).
+
+Steps rotate over `--layers` independent layer caches, by default the
+model's 32 layers (4.6 GB in total; fewer for larger layers, within 16 GB),
+as a decode step of the whole model visits them, so that no step finds its
+cache resident in the 256 MB Infinity Cache left by the previous step.  Each
+layer cache starts one token short of the workload's context (3968 quantized
++ 127 residual tokens), so a layer's first step decodes exactly the
+workload's call (3968 + 128 tokens); every later visit appends one more
+token and the full residual is flushed once per 128 visits of a layer, the
+method's own rate (streaming workloads start at their prefill instead).
 
 Prints one JSON line: whole-step algorithmic HBM GB/s (value), query-heads/s,
 the roofline of the dominant kernel (decode attention with the folded append,
-timed with HIP events on the launch stream around windows of `--window`
-consecutive calls inside the timed region, windows holding a flush left out)
-and the CPU oracle timed on a bounded sample.
+timed with HIP events on the launch stream around windows of up to
+`--window` consecutive calls inside the timed region; windows of steps that
+flush are timed apart and reported under `flush_steps`), the codec's
+throughput on the layer prefills, and the CPU oracle timed on a bounded
+sample, on one core and on the host's cores.
 """
 from __future__ import annotations
 
@@ -35,6 +40,12 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
+# GPU work before the timed region: at least this many steps, whatever
+# --warmup says (the shader clock needs a few hundred launches of load to
+# settle; fewer make the first timed windows slow)
+MIN_WARMUP_STEPS = 512
+# worker processes of the multi-core CPU leg: the host's cores, at most 16
+MAX_CPU_WORKERS = 16
 
 
 def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4, n_out=0):
@@ -58,7 +69,72 @@ def append_bytes(B, H, D, bits, G, R, flush, mb=4, n_out=0):
     return b
 
 
-# the sources that define the decode kernel and its launch configuration
+def prefill_bytes(H, D, bits, G, tq, tr, mb=4, n_out=0):
+    """Algorithmic bytes of a prefill, summed over sequences (tq, tr: arrays
+    or ints per sequence): read tq fp16 tokens of K and V and write their
+    codes, scales, zeros and outlier words; copy tr fp16 tokens of K and V
+    into the residual (read and write)."""
+    import numpy as np
+    tq = np.asarray(tq, np.int64)
+    tr = np.asarray(tr, np.int64)
+    per = (2 * tq * D * 2 + 2 * tq * D * bits // 8 + (tq // G) * D * 2 * mb
+           + tq * (D // G) * 2 * mb + (tq // G) * n_out * D * 4 + 2 * tr * D * 2 * 2)
+    return int(H * np.sum(per))
+
+
+def plan_steps(steps, layers, tq_start, tr_start, R, window):
+    """Host replay of the cache lengths over the timed steps.
+
+    Step i visits layer i % layers; each layer starts at (tq_start, tr_start)
+    (ints, or per-sequence arrays for ragged batches) and every step appends
+    one token per sequence with the lazy flush of the library: a sequence
+    whose residual holds R tokens is quantized into the grouped part first.
+
+    Returns (steps_info, windows).  steps_info[i] = (layer, flush, tq, tr):
+    the sequences that flush at step i (bool array) and the lengths the
+    step's decode reads.  windows: runs of consecutive steps of one kind
+    (flushing or not), at most `window` steps each, as (flushes, [steps]);
+    together they cover every step exactly once, in order.
+    """
+    import numpy as np
+    if steps < 1 or layers < 1 or window < 1:
+        raise ValueError("steps, layers and window must be positive")
+    tq0 = np.atleast_1d(np.asarray(tq_start, np.int64))
+    tr0 = np.atleast_1d(np.asarray(tr_start, np.int64))
+    if np.any(tr0 < 0) or np.any(tr0 > R):
+        raise ValueError("residual length outside [0, R]")
+    tqs = [tq0.copy() for _ in range(layers)]
+    trs = [tr0.copy() for _ in range(layers)]
+    info = []
+    for i in range(steps):
+        li = i % layers
+        fl = trs[li] == R
+        tqs[li] = tqs[li] + np.where(fl, R, 0)
+        trs[li] = np.where(fl, 0, trs[li]) + 1
+        info.append((li, fl, tqs[li].copy(), trs[li].copy()))
+    windows = []
+    for i, (_, fl, _, _) in enumerate(info):
+        kind = bool(np.any(fl))
+        if windows and windows[-1][0] == kind and len(windows[-1][1]) < window:
+            windows[-1][1].append(i)
+        else:
+            windows.append((kind, [i]))
+    return info, windows
+
+
+def start_lengths(w):
+    """(tq, tr) arrays every layer cache starts the timed steps at: one token
+    short of the workload's context, so the first step decodes the
+    workload's own call; a streaming workload starts at its prefill; a cache
+    with an empty residual (everything quantized) starts as it is."""
+    import numpy as np
+    tq = w.tqs().astype(np.int64)
+    tr = w.contexts().astype(np.int64) - tq
+    if w.steps == 0:
+        tr = np.where(tr > 0, tr - 1, tr)
+    return tq, tr
+
+
 DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.hip",
                   "decode_mfma_paged.hip", "decode_mfma_o1.hip", "decode_mfma_o2.hip",
                   "decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "decode_mfma_rope.hip",
@@ -67,6 +143,7 @@ DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.h
 
 
 def kernel_source_hash() -> str:
+    """Hash of the sources that define the decode kernel and its launch."""
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
         h.update(name.encode())
@@ -147,67 +224,150 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, 
     print(json.dumps(out))
 
 
-def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0,
-                 rope_theta=0.0):
-    """The C oracle (single thread) on a bounded sample of the same workload:
-    whole decode steps (append with its flush, then attention for all 256
-    query heads) repeated until about `min_seconds` of CPU work."""
+# ---------------------------------------------------------------- CPU leg
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_units(w, units, steps, kw):
+    """The oracle on (batch, KV-head) units, each a one-sequence, one-head
+    cache: prefill (not timed), then `steps` whole decode steps (append with
+    its flush, then attention for the unit's query heads).  Returns (start,
+    end, bytes, steps) with perf_counter times (system-wide monotonic)."""
     import numpy as np
 
     import oracle
     from kv_cache_bit_kivi_amd import synth
 
-    k, v = synth.kv(w)
-    cap = w.capacity(64)
-    # one oracle cache per sequence for a ragged batch, one for the whole batch otherwise
-    groups = ([(b, b + 1) for b in range(w.batch)] if w.ragged else [(0, w.batch)])
+    r = w.gqa
     ctx, tqs = w.contexts(), w.tqs()
-    ocs = []
-    for b0, b1 in groups:
-        oc = oracle.OracleCache(b1 - b0, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                                w.residual, cap, meta_half=meta_half, n_out=n_out,
-                                rope_theta=rope_theta)
-        oc.prefill(k[b0:b1, :, : int(ctx[b0])], v[b0:b1, :, : int(ctx[b0])], int(tqs[b0]))
-        ocs.append(oc)
-    del k, v
-    mb = 2 if meta_half else 4
-    nbytes, steps, t_total = 0, 0, 0.0
-    while t_total < min_seconds and steps < 64:
-        kn, vn = synth.new_token(w, steps + 1)
-        q = synth.query(w, steps + 1)
-        for (b0, b1), oc in zip(groups, ocs):
+    tq_s, tr_s = start_lengths(w)
+    cap = w.capacity(steps + 64)
+    caches = []
+    for b, h in units:
+        L = int(ctx[b])
+        k = synth.k_plane(w, b, h, L)[None, None]
+        v = synth.v_plane(w, b, h, L)[None, None]
+        oc = oracle.OracleCache(1, 1, r, w.head_dim, w.bits, w.group, w.residual, cap, **kw)
+        oc.prefill(k, v, int(tqs[b]))
+        oc.tq, oc.tr = int(tq_s[b]), int(tr_s[b])
+        caches.append(oc)
+    # the step's inputs are generated before its timed part
+    mb = 2 if kw.get("meta_half") else 4
+    n_out = kw.get("n_out", 0)
+    t_busy, nbytes = 0.0, 0
+    t0 = time.perf_counter()
+    for s in range(1, steps + 1):
+        kn, vn = synth.new_token(w, s)
+        q = synth.query(w, s)
+        ins = [(np.ascontiguousarray(kn[b:b + 1, h:h + 1]), np.ascontiguousarray(vn[b:b + 1, h:h + 1]),
+                np.ascontiguousarray(q[b:b + 1, h * r:(h + 1) * r])) for b, h in units]
+        t1 = time.perf_counter()
+        for oc, (kk, vv, qq) in zip(caches, ins):
             flush = oc.tr == w.residual
-            t0 = time.perf_counter()
-            oc.append(np.ascontiguousarray(kn[b0:b1]), np.ascontiguousarray(vn[b0:b1]))
-            oc.decode(np.ascontiguousarray(q[b0:b1]), w.softmax_scale)
-            t_total += time.perf_counter() - t0
-            n = b1 - b0
-            nbytes += append_bytes(n, w.kv_heads, w.head_dim, w.bits, w.group, w.residual,
-                                   flush, mb, n_out)
-            nbytes += decode_bytes(n, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group, oc.tq,
-                                   oc.tr, mb, n_out)
-        steps += 1
-        if t_total > max_seconds:
+            oc.append(kk, vv)
+            oc.decode(qq, w.softmax_scale)
+            nbytes += append_bytes(1, 1, w.head_dim, w.bits, w.group, w.residual, flush, mb,
+                                   n_out)
+            nbytes += decode_bytes(1, 1, r, w.head_dim, w.bits, w.group, oc.tq, oc.tr, mb,
+                                   n_out)
+        t_busy += time.perf_counter() - t1
+    return t0, time.perf_counter(), t_busy, nbytes
+
+
+def _cpu_worker(args):
+    w, units, steps, kw = args
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    return _cpu_units(w, units, steps, kw)
+
+
+def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0,
+                 rope_theta=0.0, workers=None, pool=None):
+    """The C oracle (single-threaded code) on a bounded sample of the same
+    workload: whole decode steps over every (batch, KV-head) unit.
+
+    One core: the units run in this process, step after step, until about
+    `min_seconds` of oracle time.  Host cores: the same units fanned out over
+    `workers` processes (default: the host's cores, at most 16), each running
+    the single-threaded oracle on its share for the same kind of steps; the
+    rate is the bytes of all units over the wall time from the first start to
+    the last finish."""
+    kw = dict(meta_half=meta_half, n_out=n_out, rope_theta=rope_theta)
+    units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
+    # one core: grow the step count until the sample is long enough
+    steps, spent = 1, 0.0
+    while True:
+        _, _, busy, nbytes = _cpu_units(w, units, steps, kw)
+        spent += busy
+        if busy >= min_seconds or steps >= 64 or spent > max_seconds:
             break
-    return {
-        "value": round(nbytes / t_total / 1e9, 4),
+        steps = min(64, max(steps + 1, int(steps * min_seconds / max(busy, 1e-3)) + 1))
+    one = {"value": round(nbytes / busy / 1e9, 4), "seconds_per_step": round(busy / steps, 4),
+           "steps": steps, "query_heads_per_s": round(steps * w.batch * w.q_heads / busy, 2)}
+    res = {
+        "value": one["value"],
         "unit": "GB/s",
         "cores": 1,
         "kind": "oracle",
         "sample": f"{steps} whole decode steps of the same workload (one layer: append incl. "
                   f"flush, then attention for all {w.batch * w.q_heads} query heads), "
-                  f"{t_total:.1f} s single-threaded",
-        "seconds_per_step": round(t_total / steps, 4),
-        "query_heads_per_s": round(steps * w.batch * w.q_heads / t_total, 2),
+                  f"{busy:.1f} s single-threaded",
+        "one_core": one,
+        "cpu_model": cpu_model(),
+        "host_cores_visible": len(os.sched_getaffinity(0)),
     }
+    n = workers if workers is not None else min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS)
+    n = max(1, min(n, len(units)))
+    if n > 1:
+        # as many steps as fit about min_seconds on n cores
+        msteps = int(min(256, max(steps, min_seconds * n / max(one["seconds_per_step"], 1e-6))))
+        shares = [units[i::n] for i in range(n)]
+        jobs = [(w, s, msteps, kw) for s in shares]
+        if pool is not None:
+            outs = pool.map(_cpu_worker, jobs)
+        else:
+            import multiprocessing as mp
+            with mp.get_context("fork").Pool(n) as p:
+                outs = p.map(_cpu_worker, jobs)
+        # timed part of each worker: its steps, after its own prefill
+        t_first = min(o[1] - o[2] for o in outs)
+        t_last = max(o[1] for o in outs)
+        wall = t_last - t_first
+        nb = sum(o[3] for o in outs)
+        res.update({
+            "value": round(nb / wall / 1e9, 4),
+            "cores": n,
+            "sample": f"{msteps} whole decode steps of the same workload (one layer: append "
+                      f"incl. flush, then attention for all {w.batch * w.q_heads} query heads), "
+                      f"its {len(units)} (batch, KV-head) units over {n} processes, "
+                      f"{wall:.1f} s wall; one core: {steps} steps, {busy:.1f} s",
+            "seconds_per_step": round(wall / msteps, 4),
+            "query_heads_per_s": round(msteps * w.batch * w.q_heads / wall, 2),
+        })
+    else:
+        res.update({"seconds_per_step": one["seconds_per_step"],
+                    "query_heads_per_s": one["query_heads_per_s"]})
+    return res
 
+
+# ---------------------------------------------------------------- GPU leg
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=0,
-                    help="timed steps (default: 128 per rotated layer cache)")
-    ap.add_argument("--warmup", type=int, default=64)
+                    help="timed steps (default: 128 per rotated layer cache; streaming "
+                         "workloads: their own step count per layer)")
+    ap.add_argument("--warmup", type=int, default=64,
+                    help=f"untimed steps before the timed region (at least {MIN_WARMUP_STEPS} "
+                         "are run, see warmup_effective)")
     ap.add_argument("--workload", default="llama2_7b_b8_ctx4096")
     ap.add_argument("--layers", type=int, default=0,
                     help="layer caches the steps rotate over (default: 32, Llama-2-7B's layer "
@@ -234,9 +394,13 @@ def main():
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
     ap.add_argument("--window", type=int, default=16, metavar="W",
-                    help="HIP events bracket windows of W consecutive timed steps")
+                    help="HIP events bracket windows of up to W consecutive timed steps")
+    ap.add_argument("--window-trace", metavar="PATH",
+                    help="also write every window's (first step, steps, flushes, us per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-workers", type=int, default=None,
+                    help="processes of the multi-core CPU leg (default: host cores, at most 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (PMC calibration)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB", "CMD"),
@@ -262,11 +426,32 @@ def main():
               "(the kernels shard across GPUs by (batch, KV head) with no exchange, but this "
               "build measures one GPU only).", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 0 or args.warmup < 0:
+        print("--steps and --warmup must not be negative", file=sys.stderr)
+        sys.exit(2)
 
     import numpy as np
-    import torch
 
     from kv_cache_bit_kivi_amd import synth
+
+    w = synth.WORKLOADS[args.workload]
+    if args.bits:
+        w = w.with_(bits=args.bits)
+    spikes = args.key_spikes if args.key_spikes is not None else (0.01 if n_out else 0.0)
+    if spikes:
+        w = w.with_(key_spikes=spikes)
+
+    # The multi-core CPU leg's worker processes are forked now, before this
+    # process touches the GPU, and wait for their work until the GPU leg ends.
+    pool = None
+    n_workers = (args.cpu_workers if args.cpu_workers is not None
+                 else min(len(os.sched_getaffinity(0)), MAX_CPU_WORKERS))
+    if not args.no_cpu_baseline and n_workers > 1:
+        import multiprocessing as mp
+        pool = mp.get_context("fork").Pool(n_workers)
+
+    import torch
+
     from kv_cache_bit_kivi_amd._lib import lib
     from kv_cache_bit_kivi_amd.cache import KiviCache, PagedKiviCache, RaggedKiviCache
 
@@ -275,56 +460,61 @@ def main():
         sys.exit(1)
     lib()  # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
-    w = synth.WORKLOADS[args.workload]
-    if args.bits:
-        w = w.with_(bits=args.bits)
-    spikes = args.key_spikes if args.key_spikes is not None else (0.01 if n_out else 0.0)
-    if spikes:
-        w = w.with_(key_spikes=spikes)
     B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
                               w.residual)
     if args.layers <= 0:
         layer_bytes = decode_bytes(B, H, r, D, bits, G, int(w.context), R, mb, n_out)
         args.layers = int(max(2, min(32, 16e9 // layer_bytes)))
-    if args.steps <= 0:
-        args.steps = 128 * args.layers
     NL = args.layers
-    total_steps = args.warmup + args.steps
-    per_layer_appends = (total_steps + NL - 1) // NL
-    cap = w.capacity(per_layer_appends + R)
+    if args.steps == 0:
+        args.steps = (w.steps or 128) * NL
+    warm = max(args.warmup, MIN_WARMUP_STEPS)
+    tq_s, tr_s = start_lengths(w)
+    # capacity for every flush of the warm-up or of the timed steps (the
+    # lengths are set back to the start after the warm-up)
+    per_layer = (max(warm, args.steps) + NL - 1) // NL
+    cap = w.capacity(per_layer + R)
 
     paged = args.paged > 0
     ragged = w.ragged or paged      # (the paged calls carry per-sequence lengths)
-    ctx0 = w.contexts().astype(np.int32)          # per-sequence lengths at the start
+    ctx0 = w.contexts().astype(np.int32)          # per-sequence lengths at the prefill
     tq0 = w.tqs().astype(np.int32)
-    tr0 = ctx0 - tq0
     k, v = synth.kv(w)
     kd, vd = torch.from_numpy(k).cuda(), torch.from_numpy(v).cuda()
     del k, v
     caches = []
     if paged:
         cap = (cap + args.paged - 1) // args.paged * args.paged
+    # each layer's prefill is timed with events: the codec's throughput
+    cur = torch.cuda.current_stream()
+    pf_ev = []
     for li in range(NL):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if paged:
-            mp = cap // args.paged
-            perm = np.random.default_rng(1000 + li).permutation(B * mp).astype(np.int32)
-            c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp,
-                               table=perm.reshape(B, mp), meta_half=meta_half, outliers=n_out,
+            mp_ = cap // args.paged
+            perm = np.random.default_rng(1000 + li).permutation(B * mp_).astype(np.int32)
+            c = PagedKiviCache(B, H, r, D, bits, G, R, cap, args.paged, num_pages=B * mp_,
+                               table=perm.reshape(B, mp_), meta_half=meta_half, outliers=n_out,
                                rope_theta=rope, deterministic=args.deterministic)
+            e0.record(cur)
             c.prefill(kd, vd, ctx0, tq0)
         elif ragged:
             c = RaggedKiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half,
                                 outliers=n_out, rope_theta=rope,
                                 deterministic=args.deterministic)
+            e0.record(cur)
             c.prefill(kd, vd, ctx0, tq0)
         else:
             c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out,
                           rope_theta=rope, deterministic=args.deterministic)
+            e0.record(cur)
             c.prefill(kd, vd, w.tq)
+        e1.record(cur)
+        pf_ev.append((e0, e1))
         caches.append(c)
     del kd, vd
     # distinct synthetic tokens / queries for every step, resident on the GPU
-    n_tok = min(total_steps, 256)
+    n_tok = min(max(warm, args.steps), 256)
     knew, vnew, qs = [], [], []
     for s in range(n_tok):
         kn, vn = synth.new_token(w, s + 1)
@@ -343,6 +533,7 @@ def main():
     for c in caches:
         c.workspace_for(args.splits)
     torch.cuda.synchronize()
+    pf_us = np.array([a.elapsed_time(b) * 1e3 for a, b in pf_ev])
 
     # The step loop calls the C ABI directly with pointers bound once, so the
     # host enqueues faster than the GPU drains and the events bracket queued
@@ -350,7 +541,6 @@ def main():
     import ctypes
 
     L = lib()
-    cur = torch.cuda.current_stream()
     stream = cur.cuda_stream
     kptr = [t.data_ptr() for t in knew]
     vptr = [t.data_ptr() for t in vnew]
@@ -367,28 +557,26 @@ def main():
         crefs = [ctypes.byref(c.rc) for c in caches]
         append_fn, decode_fn = L.kivi_ragged_append, L.kivi_ragged_decode_attn
         fused_fn = L.kivi_ragged_append_decode_attn
-    if ragged:
-
-        def flushes(li):          # sequences whose residual is full (flush on this append)
-            return caches[li].tr_arr == R
-
-        def lengths(li):
-            return caches[li].tq_arr.copy(), caches[li].tr_arr.copy()
     else:
         crefs = [ctypes.byref(c.c) for c in caches]
         append_fn, decode_fn = L.kivi_append, L.kivi_decode_attn
         fused_fn = L.kivi_append_decode_attn
 
-        def flushes(li):
-            return caches[li].c.tr == R
+    def lengths(li):
+        if ragged:
+            return caches[li].tq_arr.astype(np.int64), caches[li].tr_arr.astype(np.int64)
+        return np.array([caches[li].c.tq], np.int64), np.array([caches[li].c.tr], np.int64)
 
-        def lengths(li):
-            return caches[li].c.tq, caches[li].c.tr
+    def set_start():
+        for c in caches:
+            if ragged:
+                c.set_lengths(tq_s, tr_s)
+            else:
+                c.set_lengths(int(tq_s[0]), int(tr_s[0]))
 
     def step(i):
         li = i % NL
         j = i % n_tok
-        fl = flushes(li)
         if args.separate:
             rc = append_fn(crefs[li], kptr[j], vptr[j], stream)
             if rc:
@@ -400,70 +588,72 @@ def main():
                           wsp[li][1], args.splits, stream)
         if rc:
             raise RuntimeError(f"decode step failed: {rc}")
-        return (fl, *lengths(li))
 
-    for i in range(args.warmup):
+    set_start()
+    for i in range(warm):
         step(i)
     torch.cuda.synchronize()
-    for c in caches:       # back to the workload's starting lengths
-        if ragged:
-            c.set_lengths(tq0, tr0)
-        else:
-            c.set_lengths(w.tq, w.tr)
+    set_start()         # back to the start lengths
     splits_used = caches[0].auto_splits() if args.splits == 0 else args.splits
 
     # HIP events on the launch stream bracket windows of up to W consecutive
-    # steps that flush nothing (an event is a packet on that stream:
-    # bracketing every launch would add its own dispatch latency to each
-    # measured launch and slow the loop).  Whether a step flushes is known on
-    # the host before its call, so a window closes before any flush step.
+    # steps of one kind (flushing or not).  An event is a packet on that
+    # stream: bracketing every launch would add its own dispatch latency to
+    # each measured launch and slow the loop.  Whether a step flushes is known
+    # on the host before its call (plan_steps replays the lengths).
     W = max(1, args.window)
-    pool = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 2)]
-    windows, open_w, pi = [], None, 0
-    meta = []
+    info, windows = plan_steps(args.steps, NL, tq_s if ragged else tq_s[:1],
+                               tr_s if ragged else tr_s[:1], R, W)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in windows]
+    opens = {ix[0]: k for k, (_, ix) in enumerate(windows)}
+    closes = {ix[-1]: k for k, (_, ix) in enumerate(windows)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        fl = bool(np.any(flushes(i % NL)))
-        if open_w is not None and (fl or len(open_w[2]) == W):
-            open_w[1].record(cur)
-            windows.append(open_w)
-            open_w = None
-        if not fl and open_w is None:
-            open_w = (pool[pi], pool[pi + 1], [])
-            pi += 2
-            open_w[0].record(cur)
-        meta.append(step(i))
-        if open_w is not None:
-            open_w[2].append(i)
-    if open_w is not None:
-        open_w[1].record(cur)
-        windows.append(open_w)
+        k = opens.get(i)
+        if k is not None:
+            ev[k][0].record(cur)
+        step(i)
+        k = closes.get(i)
+        if k is not None:
+            ev[k][1].record(cur)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the library's host lengths must have followed the plan
+    for li in range(NL):
+        last = max(i for i in range(args.steps) if i % NL == li) if args.steps > li else None
+        if last is not None:
+            tq_l, tr_l = lengths(li)
+            assert np.array_equal(tq_l, info[last][2]) and np.array_equal(tr_l, info[last][3]), \
+                "cache lengths differ from the step plan"
 
     # algorithmic bytes of every step, at the lengths the decode reads (after
     # the step's append); ragged: summed over the sequences
     per_seq = 1 if ragged else B
-    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, np.asarray(tq, np.int64),
-                                         np.asarray(tr, np.int64), mb, n_out)))
-                 for _, tq, tr in meta]
+    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, tq, tr, mb, n_out)))
+                 for _, _, tq, tr in info]
     app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb, n_out)
-                             for f in np.atleast_1d(fl)]))
-                 for fl, _, _ in meta]
+                             for f in fl]))
+                 for _, fl, _, _ in info]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
-    # The timed call is the decode launch, carrying the new token's append when
-    # fused (separate mode: the append launch too); windows hold no flush.
+    n_flush = int(sum(int(np.sum(fl)) for _, fl, _, _ in info))
+    # The dominant kernel is the decode launch, carrying the new token's
+    # append when fused (separate mode: the append launch too).
     new_tok = append_bytes(B, H, D, bits, G, R, False, mb, n_out)
     per_call = [d + new_tok for d in dec_bytes]
-    win_ms = np.array([e0.elapsed_time(e1) / len(ix) for e0, e1, ix in windows])
-    win_bytes = np.array([sum(per_call[i] for i in ix) / len(ix) for _, _, ix in windows])
-    if not len(win_ms):
-        raise SystemExit("every timed step flushes: raise --steps")
-    n_launch = sum(len(ix) for _, _, ix in windows)
-    w_time = float(sum(t * len(ix) for t, (_, _, ix) in zip(win_ms, windows)))   # ms
-    w_bytes = float(sum(b * len(ix) for b, (_, _, ix) in zip(win_bytes, windows)))
-    n_flush = sum(int(np.sum(fl)) for fl, _, _ in meta)
+    win_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(len(windows))]
+    plain = [k for k, (fl, _) in enumerate(windows) if not fl]
+    flushing = [k for k, (fl, _) in enumerate(windows) if fl]
+    sel = plain if plain else list(range(len(windows)))
+    n_launch = sum(len(windows[k][1]) for k in sel)
+    w_time = float(sum(win_ms[k] for k in sel))                              # ms
+    w_bytes = float(sum(per_call[i] for k in sel for i in windows[k][1]))
+    per_launch_us = np.array([win_ms[k] / len(windows[k][1]) * 1e3 for k in sel])
+    if args.window_trace:
+        with open(args.window_trace, "w") as f:
+            for k, (fl, ix) in enumerate(windows):
+                f.write(f"{ix[0]} {len(ix)} {int(fl)} {win_ms[k] / len(ix) * 1e3:.3f}\n")
 
     value = total_bytes / elapsed / 1e9
     achieved = w_bytes / (w_time * 1e-3) / 1e9
@@ -473,6 +663,9 @@ def main():
                  else f"kivi_{kind}_append_decode_attn")
     else:
         calls = "kivi_append + kivi_decode_attn" if args.separate else "kivi_append_decode_attn"
+    pf_bytes = prefill_bytes(H, D, bits, G, tq0.astype(np.int64),
+                             (ctx0 - tq0).astype(np.int64), mb, n_out)
+    pf_med = float(np.median(pf_us[1:] if len(pf_us) > 1 else pf_us))
 
     result = {
         "metric": METRIC,
@@ -481,17 +674,25 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_effective": warm,
         "ms_per_step": round(elapsed / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16 io, f16/bf16 mfma (hi+lo factors), f32 acc",
+        "arithmetic": ("codes, scales and zeros stored exactly (codec in IEEE binary32); fp16 "
+                       "queries, residual and output; dot products on the matrix cores with the "
+                       "codes as exact f16/bf16 operands and each factor split into hi + lo "
+                       "halves (>= 16 significant bits), accumulated in binary32; softmax in "
+                       "binary32"),
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": B, "q_heads": H * r, "kv_heads": H, "head_dim": D,
-            "context_at_start": (w.context if not ragged else
-                                 {"min": int(ctx0.min()), "mean": round(float(ctx0.mean()), 1),
-                                  "max": int(ctx0.max()), "per_sequence": ctx0.tolist()}),
+            "context_at_first_step": (int(tq_s[0] + tr_s[0] + 1) if not ragged else
+                                      {"min": int((tq_s + tr_s).min() + 1),
+                                       "max": int((tq_s + tr_s).max() + 1)}),
+            "start_lengths_tq_tr": ([int(tq_s[0]), int(tr_s[0])] if not ragged else
+                                    [tq_s.tolist(), tr_s.tolist()]),
             "bits": bits, "group": G, "residual": R,
             "scale_zero": "fp16" if meta_half else "fp32",
             "key_outliers_per_group": n_out,
@@ -512,7 +713,8 @@ def main():
             "kernel": (f"{calls} (append and decode launches)" if args.separate
                        else f"kivi decode attention with the append folded in ({calls}: one "
                        "decode launch per step)") +
-                      f"; HIP events around runs of up to {W} consecutive steps without a flush",
+                      f"; HIP events around runs of up to {W} consecutive steps" +
+                      (" without a flush" if plain else " (every step flushes)"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -521,16 +723,44 @@ def main():
             "bytes_per_launch": int(w_bytes / n_launch),
             "launches_averaged": int(n_launch),
             "window_launches": W,
-            "windows": len(windows),
+            "windows": len(sel),
             "avg_launch_us": round(w_time / n_launch * 1e3, 3),
-            "window_p10_us": round(float(np.percentile(win_ms, 10)) * 1e3, 3),
-            "window_p90_us": round(float(np.percentile(win_ms, 90)) * 1e3, 3),
+            "window_p10_us": round(float(np.percentile(per_launch_us, 10)), 3),
+            "window_p90_us": round(float(np.percentile(per_launch_us, 90)), 3),
+        },
+        "flush_steps": ({
+            "steps": int(sum(len(windows[k][1]) for k in flushing)),
+            "avg_step_us": round(sum(win_ms[k] for k in flushing) * 1e3 /
+                                 sum(len(windows[k][1]) for k in flushing), 3),
+            "algorithmic_bytes_per_step": int(np.mean([dec_bytes[i] + app_bytes[i]
+                                                       for k in flushing
+                                                       for i in windows[k][1]])),
+            "note": "steps whose append flushes the full residual first, timed in windows of "
+                    "their own; left out of the roofline, included in value",
+        } if flushing else None),
+        "prefill_quantize": {
+            "kernels": "kivi_prefill: quantize keys and values of the quantized part, copy the "
+                       "residual (one layer)",
+            "median_us": round(pf_med, 2),
+            "algorithmic_bytes": pf_bytes,
+            "gbps": round(pf_bytes / (pf_med * 1e-6) / 1e9, 1),
+            "frac": round(pf_bytes / (pf_med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "layers_timed": int(len(pf_us) - 1 if len(pf_us) > 1 else 1),
         },
         "kernel_source_hash": kernel_source_hash(),
     }
+    if w.steps:
+        # streaming workloads: the layer's whole run of steps (flushes included)
+        result["per_layer_run"] = {"steps": w.steps,
+                                   "ms": round(elapsed * 1e3 * w.steps / args.steps, 3)}
+    del caches, knew, vnew, qs, outs
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half,
-                                              n_out=n_out, rope_theta=rope)
+                                              n_out=n_out, rope_theta=rope,
+                                              workers=n_workers, pool=pool)
+    if pool is not None:
+        pool.close()
+        pool.join()
     print(json.dumps(result), flush=True)
 
 

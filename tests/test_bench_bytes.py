@@ -58,13 +58,15 @@ def test_cpu_baseline_runs_its_sample(meta_half):
     reached, for both metadata widths."""
     from kv_cache_bit_kivi_amd import synth
     w = synth.WORKLOADS["single_head_512"]
-    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, meta_half=meta_half)
+    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, meta_half=meta_half,
+                           workers=1)
     steps = int(r["sample"].split()[0])
-    assert steps > 1
+    assert steps > 1 and r["one_core"]["steps"] == steps
     r = bench.cpu_baseline(w.with_(key_spikes=0.01), min_seconds=0.05, max_seconds=5.0,
-                           meta_half=meta_half, n_out=2)
+                           meta_half=meta_half, n_out=2, workers=1)
     assert int(r["sample"].split()[0]) > 1
     assert r["kind"] == "oracle" and r["cores"] == 1 and r["value"] > 0
+    assert r["cpu_model"] and r["host_cores_visible"] >= 1
 
 
 def test_ragged_workload_lengths():
@@ -87,5 +89,16 @@ def test_cpu_baseline_ragged_sample():
     from kv_cache_bit_kivi_amd import synth
     w = synth.WORKLOADS["ragged_b16_ctx512_8192"].with_(batch=3, q_heads=2, kv_heads=2,
                                                         context=384, min_context=40)
-    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0)
+    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, workers=1)
     assert int(r["sample"].split()[0]) > 1 and r["value"] > 0
+
+
+def test_cpu_baseline_multi_core():
+    """The multi-core leg fans the (batch, KV-head) units over worker
+    processes and moves the same bytes per step as one core does."""
+    from kv_cache_bit_kivi_amd import synth
+    w = synth.WORKLOADS["single_head_512"].with_(batch=2, q_heads=4, kv_heads=2, context=256,
+                                                 tq=224)
+    r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, workers=3)
+    assert r["cores"] == 3 and r["value"] > 0 and r["one_core"]["value"] > 0
+    assert "over 3 processes" in r["sample"]
