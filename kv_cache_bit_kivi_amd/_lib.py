@@ -125,6 +125,13 @@ def lib():
         if not os.path.exists(LIB_PATH):
             raise ImportError(
                 f"{LIB_PATH} not found: build it with `python -m kv_cache_bit_kivi_amd.build`")
+        # The caller's device memory and streams come from PyTorch, so the
+        # library must run on PyTorch's HIP runtime.  PyTorch loads its own
+        # copy of libamdhip64 by the unversioned name; loaded first, the
+        # library's own dependency (by its versioned soname) would pull in a
+        # second HIP runtime that sees no device.  Importing torch first makes
+        # the dynamic linker bind the library to torch's copy.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in PROTOTYPES.items():
             fn = getattr(L, name)

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <vector>
 
@@ -18,6 +19,15 @@ namespace {
 using kivi::DecodeArgs;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// KIVI_EHIP for a failed HIP call; with the environment variable KIVI_DEBUG
+// set, the HIP error's name goes to stderr first (the status code alone does
+// not say which HIP error it was)
+int hip_fail(hipError_t e, const char* where) {
+  static const bool verbose = getenv("KIVI_DEBUG") != nullptr;
+  if (verbose) fprintf(stderr, "kivi: %s: %s\n", where, hipGetErrorName(e));
+  return KIVI_EHIP;
+}
 
 int check_shape(const kivi_shape* s) {
   if (!s) return KIVI_EINVAL;
@@ -289,7 +299,7 @@ int enqueue_quantize_list(const Rg& g, const uint16_t* k_src, const uint16_t* v_
       e = kivi::launch_quantize_v_list(v_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
                                        ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
   }
-  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
 // Quantizes the full residual of every sequence whose residual holds R tokens
@@ -312,7 +322,7 @@ int enqueue_ragged_token_copy(const Rg& g, const uint16_t* k_new, const uint16_t
   auto cp = batcher([&](const kivi::SeqList& L) {
     hipError_t e = kivi::launch_copy_tokens_list(k_new, v_new, 1, g.k_res, g.v_res, s.residual, L,
                                                  1, s.num_kv_heads, s.head_dim, st);
-    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+    return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
   });
   for (int b = 0; b < s.batch; b++) cp.add(b, 0, slot[b], 1);
   return cp.flush();
@@ -421,8 +431,11 @@ int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
     else
       e = g.paged ? kivi::launch_decode_generic_paged(a, lens, st)
                   : kivi::launch_decode_generic_ragged(a, lens, st);
-    if (e != hipSuccess) return KIVI_EHIP;
-    if (S > 1 && kivi::launch_combine(a, st) != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
+    if (S > 1) {
+      e = kivi::launch_combine(a, st);
+      if (e != hipSuccess) return hip_fail(e, __func__);
+    }
   }
   return KIVI_OK;
 }
@@ -474,7 +487,7 @@ int do_prefill(const Rg& g, const uint16_t* k, const uint16_t* v, int32_t in_tok
     hipError_t e = kivi::launch_copy_tokens_list(k, v, in_tok_stride, g.k_res, g.v_res,
                                                  s.residual, L, max_n, s.num_kv_heads,
                                                  s.head_dim, st);
-    return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+    return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
   });
   for (int b = 0; b < s.batch; b++)
     if (ntok[b] > tq[b]) cp.add(b, tq[b], 0, ntok[b] - tq[b]);
@@ -608,7 +621,7 @@ int kivi_quantize_k(const kivi_shape* s, const uint16_t* k, int32_t in_tok_strid
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
                                          scale, zero, s->meta_half, nullptr, 0,
                                          (hipStream_t)stream);
-  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
 int kivi_quantize_k_outliers(const kivi_shape* s, const uint16_t* k, int32_t in_tok_stride,
@@ -622,7 +635,7 @@ int kivi_quantize_k_outliers(const kivi_shape* s, const uint16_t* k, int32_t in_
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
                                          scale, zero, s->meta_half, outliers, s->outliers,
                                          (hipStream_t)stream);
-  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
 int kivi_quantize_v(const kivi_shape* s, const uint16_t* v, int32_t in_tok_stride, int32_t ntok,
@@ -632,7 +645,7 @@ int kivi_quantize_v(const kivi_shape* s, const uint16_t* v, int32_t in_tok_strid
   hipError_t e = kivi::launch_quantize_v(v, s->batch, s->num_kv_heads, s->head_dim, s->bits,
                                          s->group, s->capacity, in_tok_stride, ntok, dst, codes,
                                          scale, zero, s->meta_half, (hipStream_t)stream);
-  return e == hipSuccess ? KIVI_OK : KIVI_EHIP;
+  return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
 int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t ntok, int32_t tq,
@@ -651,16 +664,16 @@ int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t nt
                                            s.group, s.capacity, ntok, tq, 0, c->k_codes,
                                            c->k_scale, c->k_zero, s.meta_half, c->k_outliers,
                                            s.outliers, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
     e = kivi::launch_quantize_v(v, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero,
                                 s.meta_half, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
   }
   if (ntok > tq) {
     hipError_t e = kivi::launch_copy_tokens(k, v, ntok, tq, c->k_res, c->v_res, s.residual, 0,
                                             ntok - tq, s.batch, s.num_kv_heads, s.head_dim, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
   }
   c->tq = tq;
   c->tr = ntok - tq;
@@ -683,17 +696,17 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
                                            tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
                                            c->k_outliers, s.outliers, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, tq, c->v_codes, c->v_scale,
                                 c->v_zero, s.meta_half, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
     tq += s.residual;
     tr = 0;
   }
   hipError_t e = kivi::launch_copy_tokens(k_new, v_new, 1, 0, c->k_res, c->v_res, s.residual,
                                           tr, 1, s.batch, s.num_kv_heads, s.head_dim, st);
-  if (e != hipSuccess) return KIVI_EHIP;
+  if (e != hipSuccess) return hip_fail(e, __func__);
   c->tq = tq;
   c->tr = tr + 1;
   return KIVI_OK;
@@ -772,10 +785,10 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
 static int enqueue_decode(const kivi_shape& s, const DecodeArgs& a, hipStream_t st) {
   hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
                              : kivi::launch_decode_generic(a, st);
-  if (e != hipSuccess) return KIVI_EHIP;
+  if (e != hipSuccess) return hip_fail(e, __func__);
   if (a.S > 1) {
     e = kivi::launch_combine(a, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
   }
   return KIVI_OK;
 }
@@ -816,11 +829,11 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
                                            s.bits, s.group, s.capacity, s.residual, s.residual,
                                            c->tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
                                            c->k_outliers, s.outliers, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
     e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
                                 s.capacity, s.residual, s.residual, c->tq, c->v_codes,
                                 c->v_scale, c->v_zero, s.meta_half, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
   }
   if (use_mfma(s)) {
     // the decode kernel reads the new token from its input rows and writes it
@@ -831,7 +844,7 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
     hipError_t e = kivi::launch_copy_tokens(k_new, v_new, 1, 0, c->k_res, c->v_res,
                                             s.residual, slot, 1, s.batch, s.num_kv_heads,
                                             s.head_dim, st);
-    if (e != hipSuccess) return KIVI_EHIP;
+    if (e != hipSuccess) return hip_fail(e, __func__);
   }
   rc = enqueue_decode(s, a, st);
   if (rc) return rc;

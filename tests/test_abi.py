@@ -401,3 +401,20 @@ def test_paged_errors_leave_state():
     c = paged([64, 32], [3, 1], ptrs=[P] * 7 + [0])
     assert ap(ctypes.byref(c), P, P, None) == KIVI_EINVAL
     assert lens(c) == ([64, 32], [3, 1])
+
+
+def test_one_hip_runtime_in_process():
+    """Loading the library first (before torch) must not map a second HIP
+    runtime next to PyTorch's: a fresh interpreter loads it through the
+    binding, then imports torch, and exactly one libamdhip64 is mapped."""
+    import subprocess
+    import sys
+    code = ("from kv_cache_bit_kivi_amd import _lib; _lib.lib(); import torch; "
+            "paths = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}; "
+            "print(len(paths), sorted(paths))")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True,
+                         timeout=600)
+    assert out.returncode == 0, out.stderr
+    n = int(out.stdout.split()[0])
+    assert n == 1, out.stdout
