@@ -278,6 +278,29 @@ int kivi_append_decode_attn(kivi_cache* cache, const uint16_t* k_new,
                             void* workspace, size_t workspace_bytes,
                             int32_t num_splits, void* stream);
 
+/* Bytes of the library's own device scratch array used by
+ * kivi_decode_attn_noalloc (one copy per GPU, held until the process ends). */
+#define KIVI_SCRATCH_BYTES (8u << 20)
+
+/* kivi_decode_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same validation and results, bit for bit, as
+ * kivi_decode_attn with the same split count, but the split-K partials live
+ * in a device array of the library (KIVI_SCRATCH_BYTES per GPU) instead of a
+ * caller workspace.  The call allocates nothing.  A split count whose
+ * partials, kivi_decode_workspace_bytes(&cache->shape, num_splits), exceed
+ * KIVI_SCRATCH_BYTES is refused with KIVI_EWORKSPACE before any HIP call
+ * (num_splits == 0: the automatic count, checked after the compute-unit
+ * query).  The first call on a device looks up that device's copy of the
+ * array (a HIP symbol query; KIVI_EHIP if it fails).  Every call on one GPU
+ * shares its array and leaves its last partials there; nothing in it needs
+ * clearing (each call writes every partial it reads).  Calls that can
+ * overlap on one GPU (other streams, other host threads) race on the array
+ * and must be ordered by the caller. */
+int kivi_decode_attn_noalloc(const kivi_cache* cache, const uint16_t* q,
+                             float softmax_scale, uint16_t* out,
+                             int32_t num_splits, void* stream);
+
 /* ---- Ragged batches: a different length for every sequence ------------
  * In a serving batch every sequence has its own context length, so the
  * quantized and residual token counts differ per sequence (study.space

@@ -91,6 +91,7 @@ PROTOTYPES = {
     "kivi_decode_attn": (ctypes.c_int, [_CP, _vp, ctypes.c_float, _vp, _vp, _sz, _i32, _vp]),
     "kivi_append_decode_attn": (ctypes.c_int, [_CP, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _sz,
                                                _i32, _vp]),
+    "kivi_decode_attn_noalloc": (ctypes.c_int, [_CP, _vp, ctypes.c_float, _vp, _i32, _vp]),
     "kivi_ragged_prefill": (ctypes.c_int, [_RP, _vp, _vp, _i32, _I32P, _I32P, _vp]),
     "kivi_ragged_append": (ctypes.c_int, [_RP, _vp, _vp, _vp]),
     "kivi_ragged_decode_auto_splits": (ctypes.c_int, [_RP]),
@@ -165,6 +166,7 @@ kivi_decode_auto_splits = _fn("kivi_decode_auto_splits")
 kivi_decode_workspace_bytes = _fn("kivi_decode_workspace_bytes")
 kivi_decode_attn = _fn("kivi_decode_attn")
 kivi_append_decode_attn = _fn("kivi_append_decode_attn")
+kivi_decode_attn_noalloc = _fn("kivi_decode_attn_noalloc")
 kivi_ragged_prefill = _fn("kivi_ragged_prefill")
 kivi_ragged_append = _fn("kivi_ragged_append")
 kivi_ragged_decode_auto_splits = _fn("kivi_ragged_decode_auto_splits")

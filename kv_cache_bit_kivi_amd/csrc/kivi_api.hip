@@ -853,6 +853,54 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
   return KIVI_OK;
 }
 
+// ---- decode without a caller workspace ----------------------------------------
+// The split-K partials of kivi_decode_attn_noalloc live in this file-scope
+// device array: every GPU the library runs on holds its own copy until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address is taken
+// once per device with hipGetSymbolAddress and kept per device.
+static __device__ __align__(256) float scratch[KIVI_SCRATCH_BYTES / sizeof(float)];
+
+static std::atomic<void*> g_scratch_ptr[64];
+
+// device address of this device's copy of `scratch`, or nullptr on a HIP error
+static void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* q = nullptr;
+  if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+  g_scratch_ptr[dev].store(q, std::memory_order_release);
+  return q;
+}
+
+int kivi_decode_attn_noalloc(const kivi_cache* c, const uint16_t* q, float softmax_scale,
+                             uint16_t* out, int32_t num_splits, void* stream) {
+  int rc = check_cache(c);
+  if (rc) return rc;
+  if (num_splits < 0) return KIVI_EINVAL;
+  const int L = c->tq + c->tr;
+  if (L < 1) return KIVI_ESHAPE;
+  if (num_splits > 0 && (num_splits > L || num_splits > KIVI_MAX_SPLITS)) return KIVI_ESHAPE;
+  // the split count's partials must fit the array (checked before any HIP
+  // call when num_splits is given)
+  int S = num_splits;
+  if (S == 0) {
+    const int cus = device_cu_count();
+    if (cus < 0) return KIVI_EHIP;
+    S = auto_splits(c->shape, c->tq, c->tr, cus);
+  }
+  if (ws_bytes(c->shape, S) > (size_t)KIVI_SCRATCH_BYTES) return KIVI_EWORKSPACE;
+  void* ws = S > 1 ? scratch_address() : nullptr;
+  if (S > 1 && !ws) return KIVI_EHIP;
+  DecodeArgs a;
+  rc = prepare_decode(c, c->tq, c->tr, q, softmax_scale, out, ws, S > 1 ? KIVI_SCRATCH_BYTES : 0,
+                      S, &a);
+  if (rc) return rc;
+  return enqueue_decode(c->shape, a, (hipStream_t)stream);
+}
+
 // ---- ragged batches ---------------------------------------------------------
 
 int kivi_ragged_prefill(kivi_ragged_cache* c, const uint16_t* k, const uint16_t* v,
