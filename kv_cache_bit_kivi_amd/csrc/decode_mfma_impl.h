@@ -316,7 +316,8 @@ constexpr int prefetch_depth() {
 // scores are computed lane-per-token on the VALU: the key is dequantized,
 // rotated by the angle of its position inside the tile (a per-block table
 // F[pair][lane]) and dotted with the query rotated back by the tile's first
-// position (one complex factor per pair, advanced tile to tile in binary64).
+// position (one binary64 sincos per pair and tile, so tiles can come in any
+// order).
 template <int BITS, int R, int NW, bool MH, bool RAG, bool PG, int KO, bool ROPE>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(waves_per_eu<BITS, R, ROPE, KO>(),
@@ -721,9 +722,10 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     return h < R ? lds_sc + h * CH + k : lds_dummy + n16;
   };
 
-  // new maximum over the ntok scores in LDS -> rescale every running quantity
-  // new running maximum of each head -> rescale every running quantity
-  auto apply_max = [&](const float (&mxs)[R]) __attribute__((always_inline)) {
+  // new running maximum of each head -> rescale every running quantity (the
+  // residual's value sums only while the residual is processed: afterwards
+  // they wait in LDS and are rescaled once at the end)
+  auto apply_max = [&](const float (&mxs)[R], bool in_res) __attribute__((always_inline)) {
     float alpha[R];
     bool any = false;
 #pragma unroll
@@ -741,11 +743,13 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
       for (int h = 0; h < R; h++) {
         l_acc[h] *= alpha[h];
-        l_res[h] *= alpha[h];
 #pragma unroll
         for (int j = 0; j < kNG; j++) gam[h][j] *= alpha[h];
+        if (in_res) {
+          l_res[h] *= alpha[h];
 #pragma unroll
-        for (int e = 0; e < 8; e++) ores[h][e] *= alpha[h];
+          for (int e = 0; e < 8; e++) ores[h][e] *= alpha[h];
+        }
       }
       const float a0 = pick<R>(alpha, kg, 0), a1 = pick<R>(alpha, kg, 1);
 #pragma unroll
@@ -762,7 +766,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     float mxs[R];
 #pragma unroll
     for (int h = 0; h < R; h++) mxs[h] = wave_max(lane < ntok ? lds_sc[h * CH + lane] : -INFINITY);
-    apply_max(mxs);
+    apply_max(mxs, true);
   };
 
   // one tile (codes already staged in LDS): key scores -> LDS, online-softmax
@@ -785,13 +789,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h) * 64) = hi;
         *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h + 1) * 64) = lo;
       }
-      float bp = sq[h][0] * kzv[0] + sq[h][1] * kzv[1] + sq[h][2] * kzv[2] + sq[h][3] * kzv[3];
+      // (on the normalised query, scaled back by qup: a power of two)
+      float bp = sqn[h][0] * kzv[0] + sqn[h][1] * kzv[1] + sqn[h][2] * kzv[2] + sqn[h][3] * kzv[3];
       bp += dpp<0x128>(bp);
       bp += dpp<0x124>(bp);
       bp += dpp<0x122>(bp);
       bp += dpp<0x121>(bp);
-      beta0[h] = lane_read(bp, 0) + lane_read(bp, 16);
-      beta1[h] = lane_read(bp, 32) + lane_read(bp, 48);
+      beta0[h] = (lane_read(bp, 0) + lane_read(bp, 16)) * qup;
+      beta1[h] = (lane_read(bp, 32) + lane_read(bp, 48)) * qup;
     }
     if (half_tile && lane < 32) {
 #pragma unroll
@@ -956,7 +961,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float mxs[R];
 #pragma unroll
       for (int h = 0; h < R; h++) mxs[h] = lane_read((h & 1) ? mx1 : mx0, 16 * (h >> 1));
-      apply_max(mxs);
+      apply_max(mxs, false);
     }
     } else {
       // pre-RoPE keys.  (1) this lane's 4 channels' scale / zero, stored per
@@ -1135,7 +1140,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         lds_sc[h * CH + lane] = sc;
         mxs[h] = wave_max(sc);
       }
-      apply_max(mxs);
+      apply_max(mxs, false);
       __builtin_amdgcn_wave_barrier();
     }
     // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
@@ -1351,6 +1356,26 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       ores[h][e] += __shfl_xor(ores[h][e], 32);
     }
   }
+  // ... and park them in this wave's output slot until the end, with the
+  // running maximum they are referred to (the registers are free for the
+  // tile loop): lane (tg, c8) keeps channels 8*c8 + 2*tg, 8*c8 + 2*tg + 1
+  {
+    const int tg = lane >> 4, c8 = lane & 15;
+#pragma unroll
+    for (int h = 0; h < R; h++) {
+      float rs0 = 0.f, rs1 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        if (e == 2 * tg) rs0 = ores[h][e];
+        if (e == 2 * tg + 1) rs1 = ores[h][e];
+      }
+      *reinterpret_cast<float2*>(lds_o + h * kD + 8 * c8 + 2 * tg) = float2{rs0, rs1};
+      if (lane == 0) {
+        lds_o[R * kD + h] = m_run[h];
+        lds_o[R * kD + R + h] = l_res[h];
+      }
+    }
+  }
 
   // ---------------- quantized tiles, DEPTH tiles of loads in flight
   // the scheduling barriers keep "stage the current tile, issue the loads of
@@ -1433,6 +1458,22 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   }
 
   // ---------------- wave result -> LDS: o[h][d], m[h], l[h]
+  // the residual's parked sums, read before the slot is overwritten, and the
+  // factor 2^(m_res - m_run) that brings them to the final reference (the
+  // product of the tile loop's rescale factors; 0 for an empty residual)
+  float2 rpart[R];
+  float rfac[R], lres[R];
+  {
+    const int tg = lane >> 4, c8 = lane & 15;
+#pragma unroll
+    for (int h = 0; h < R; h++) {
+      rpart[h] = *reinterpret_cast<const float2*>(lds_o + h * kD + 8 * c8 + 2 * tg);
+      const float mr = lds_o[R * kD + h];
+      lres[h] = lds_o[R * kD + R + h];
+      rfac[h] = mr == -INFINITY ? 0.f : fast_exp2(mr - m_run[h]);
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
   {
     const int h0 = 2 * kg, h1 = 2 * kg + 1;
 #pragma unroll
@@ -1443,10 +1484,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       *o1 = cv[nb][2] + cv[nb][3];
     }
   }
-  // residual P.V sums (already reduced over the token groups: every lane
-  // c8 + 16 k holds channels 8*c8..8*c8+7): lane (tg, c8) adds channels
-  // 8*c8+2*tg, 8*c8+2*tg+1 (value group c8/4) together with the Gamma term of
-  // that group
+  // residual P.V sums: lane (tg, c8) adds channels 8*c8+2*tg, 8*c8+2*tg+1
+  // (value group c8/4) together with the Gamma term of that group
   __builtin_amdgcn_wave_barrier();
   {
     const int tg = lane >> 4, c8 = lane & 15, grp = c8 >> 2;
@@ -1455,21 +1494,15 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       float g[kNG];
 #pragma unroll
       for (int j = 0; j < kNG; j++) g[j] = wave_sum(gam[h][j]);
-      const float lsum = wave_sum(l_acc[h]) + l_res[h];
+      const float lsum = wave_sum(l_acc[h]) + lres[h] * rfac[h];
       float gj = g[0];
 #pragma unroll
       for (int j = 1; j < kNG; j++)
         if (grp == j) gj = g[j];
-      float rs0 = 0.f, rs1 = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; e++) {
-        if (e == 2 * tg) rs0 = ores[h][e];
-        if (e == 2 * tg + 1) rs1 = ores[h][e];
-      }
       float2* op = reinterpret_cast<float2*>(lds_o + h * kD + 8 * c8 + 2 * tg);
       float2 o2 = *op;
-      o2.x += gj + rs0;
-      o2.y += gj + rs1;
+      o2.x += gj + rpart[h].x * rfac[h];
+      o2.y += gj + rpart[h].y * rfac[h];
       *op = o2;
       if (lane == 0) {
         lds_o[R * kD + h] = m_run[h];
