@@ -149,6 +149,48 @@ size_t ws_bytes(const kivi_shape& s, int S) {
   return rows * (size_t)S * (size_t)(s.head_dim + 2) * sizeof(float);
 }
 
+// A codec job writing into a cache's grouped store (sources, counts and the
+// residual of a copy set by the caller).
+kivi::QuantJob store_job(const kivi_shape& s, uint32_t* k_codes, void* k_scale, void* k_zero,
+                         uint32_t* v_codes, void* v_scale, void* v_zero, uint32_t* k_out) {
+  kivi::QuantJob j{};
+  j.k_codes = k_codes;
+  j.k_scale = k_scale;
+  j.k_zero = k_zero;
+  j.v_codes = v_codes;
+  j.v_scale = v_scale;
+  j.v_zero = v_zero;
+  j.k_out = s.outliers > 0 ? k_out : nullptr;
+  j.n_out = s.outliers;
+  j.H = s.num_kv_heads;
+  j.D = s.head_dim;
+  j.G = s.group;
+  j.cap = s.capacity;
+  j.R = s.residual;
+  return j;
+}
+kivi::QuantJob cache_job(const kivi_cache* c) {
+  kivi::QuantJob j = store_job(c->shape, c->k_codes, c->k_scale, c->k_zero, c->v_codes,
+                               c->v_scale, c->v_zero, c->k_outliers);
+  j.k_res = c->k_res;
+  j.v_res = c->v_res;
+  return j;
+}
+// the flush of a full residual into tokens [tq, tq + R): keys and values in
+// one launch
+hipError_t launch_flush(const kivi_cache* c, int tq, hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  kivi::QuantJob j = cache_job(c);
+  j.k = c->k_res;
+  j.v = c->v_res;
+  j.in_stride = s.residual;
+  j.do_k = j.do_v = 1;
+  j.nq = s.residual;
+  j.dst_off = tq;
+  j.ncopy = 0;
+  return kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st);
+}
+
 // ---- ragged batches and the paged store -------------------------------------
 // Both carry per-sequence host lengths; the paged store also a page map.  The
 // calls below work on this common view.
@@ -277,28 +319,27 @@ struct ListBatcher {
 template <class F>
 ListBatcher<F> batcher(F f) { return ListBatcher<F>(f); }
 
-// Quantize list items of src ([batch][H][in_stride][D]) into the grouped store
-// (contiguous planes, or the pages of the table), K from k_src, V from v_src.
+// One codec launch over list items of src ([batch][H][in_stride][D]) into the
+// grouped store (contiguous planes, or the pages of the table): item i
+// quantizes a[i] tokens of K and V of sequence seq[i] into its tokens
+// [b[i], b[i] + a[i]) and copies the next c[i] tokens into its residual.
 int enqueue_quantize_list(const Rg& g, const uint16_t* k_src, const uint16_t* v_src,
-                          int in_stride, int ntok_max, const kivi::SeqList& L, hipStream_t st) {
+                          int in_stride, int ntok_max, int ncopy_max, const kivi::SeqList& L,
+                          hipStream_t st) {
   const kivi_shape& s = *g.s;
-  const int H = s.num_kv_heads, D = s.head_dim;
-  hipError_t e;
-  if (g.paged) {
-    e = kivi::launch_quantize_k_paged(k_src, L, g.pm, H, D, s.bits, s.group, in_stride, ntok_max,
-                                      g.k_codes, g.k_scale, g.k_zero, s.meta_half, g.k_out,
-                                      s.outliers, st);
-    if (e == hipSuccess)
-      e = kivi::launch_quantize_v_paged(v_src, L, g.pm, H, D, s.bits, s.group, in_stride,
-                                        ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
-  } else {
-    e = kivi::launch_quantize_k_list(k_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
-                                     ntok_max, g.k_codes, g.k_scale, g.k_zero, s.meta_half,
-                                     g.k_out, s.outliers, st);
-    if (e == hipSuccess)
-      e = kivi::launch_quantize_v_list(v_src, L, H, D, s.bits, s.group, s.capacity, in_stride,
-                                       ntok_max, g.v_codes, g.v_scale, g.v_zero, s.meta_half, st);
-  }
+  kivi::QuantJob j = store_job(s, g.k_codes, g.k_scale, g.k_zero, g.v_codes, g.v_scale,
+                               g.v_zero, g.k_out);
+  j.k = k_src;
+  j.v = v_src;
+  j.in_stride = in_stride;
+  j.do_k = j.do_v = 1;
+  j.nq = ntok_max;
+  j.k_res = g.k_res;
+  j.v_res = g.v_res;
+  hipError_t e = g.paged ? kivi::launch_quantize_kv_paged(j, L, g.pm, s.bits, s.meta_half,
+                                                          ncopy_max, st)
+                         : kivi::launch_quantize_kv_list(j, L, s.bits, s.meta_half, ncopy_max,
+                                                         st);
   return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
@@ -308,7 +349,7 @@ int enqueue_ragged_flush(const Rg& g, hipStream_t st) {
   const kivi_shape& s = *g.s;
   const int R = s.residual;
   auto fl = batcher([&](const kivi::SeqList& L) {
-    return enqueue_quantize_list(g, g.k_res, g.v_res, R, R, L, st);
+    return enqueue_quantize_list(g, g.k_res, g.v_res, R, R, 0, L, st);
   });
   for (int b = 0; b < s.batch; b++)
     if (g.tr[b] == R) fl.add(b, R, g.tq[b], 0);
@@ -476,22 +517,14 @@ int do_prefill(const Rg& g, const uint16_t* k, const uint16_t* v, int32_t in_tok
     max_tq = std::max(max_tq, (int)tq[b]);
     max_n = std::max(max_n, (int)(ntok[b] - tq[b]));
   }
+  // one launch: each sequence's prefix quantized, its tail copied
   auto qz = batcher([&](const kivi::SeqList& L) {
-    return enqueue_quantize_list(g, k, v, in_tok_stride, max_tq, L, st);
+    return enqueue_quantize_list(g, k, v, in_tok_stride, max_tq, max_n, L, st);
   });
   for (int b = 0; b < s.batch; b++)
-    if (tq[b] > 0) qz.add(b, tq[b], 0, 0);
+    if (ntok[b] > 0) qz.add(b, tq[b], 0, ntok[b] - tq[b]);
   int rc = qz.flush();
   if (rc) return rc;
-  auto cp = batcher([&](const kivi::SeqList& L) {
-    hipError_t e = kivi::launch_copy_tokens_list(k, v, in_tok_stride, g.k_res, g.v_res,
-                                                 s.residual, L, max_n, s.num_kv_heads,
-                                                 s.head_dim, st);
-    return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
-  });
-  for (int b = 0; b < s.batch; b++)
-    if (ntok[b] > tq[b]) cp.add(b, tq[b], 0, ntok[b] - tq[b]);
-  if ((rc = cp.flush())) return rc;
   for (int b = 0; b < s.batch; b++) {
     g.tq[b] = tq[b];
     g.tr[b] = ntok[b] - tq[b];
@@ -617,10 +650,14 @@ int kivi_quantize_k(const kivi_shape* s, const uint16_t* k, int32_t in_tok_strid
   int rc = check_quantize(s, k, in_tok_stride, ntok, dst, codes, scale, zero);
   if (rc) return rc;
   if (s->outliers != 0) return KIVI_EINVAL;   // kivi_quantize_k_outliers
-  hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
-                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, s->meta_half, nullptr, 0,
-                                         (hipStream_t)stream);
+  kivi::QuantJob j = store_job(*s, codes, scale, zero, nullptr, nullptr, nullptr, nullptr);
+  j.k = k;
+  j.in_stride = in_tok_stride;
+  j.do_k = 1;
+  j.nq = ntok;
+  j.dst_off = dst;
+  hipError_t e = kivi::launch_quantize_kv(j, s->bits, s->meta_half, s->batch,
+                                          (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
@@ -631,10 +668,14 @@ int kivi_quantize_k_outliers(const kivi_shape* s, const uint16_t* k, int32_t in_
   if (rc) return rc;
   if (s->outliers < 1 || !outliers) return KIVI_EINVAL;
   if (!aligned16(outliers)) return KIVI_EALIGN;
-  hipError_t e = kivi::launch_quantize_k(k, s->batch, s->num_kv_heads, s->head_dim, s->bits,
-                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, s->meta_half, outliers, s->outliers,
-                                         (hipStream_t)stream);
+  kivi::QuantJob j = store_job(*s, codes, scale, zero, nullptr, nullptr, nullptr, outliers);
+  j.k = k;
+  j.in_stride = in_tok_stride;
+  j.do_k = 1;
+  j.nq = ntok;
+  j.dst_off = dst;
+  hipError_t e = kivi::launch_quantize_kv(j, s->bits, s->meta_half, s->batch,
+                                          (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
@@ -642,9 +683,14 @@ int kivi_quantize_v(const kivi_shape* s, const uint16_t* v, int32_t in_tok_strid
                     int32_t dst, uint32_t* codes, void* scale, void* zero, void* stream) {
   int rc = check_quantize(s, v, in_tok_stride, ntok, dst, codes, scale, zero);
   if (rc) return rc;
-  hipError_t e = kivi::launch_quantize_v(v, s->batch, s->num_kv_heads, s->head_dim, s->bits,
-                                         s->group, s->capacity, in_tok_stride, ntok, dst, codes,
-                                         scale, zero, s->meta_half, (hipStream_t)stream);
+  kivi::QuantJob j = store_job(*s, nullptr, nullptr, nullptr, codes, scale, zero, nullptr);
+  j.v = v;
+  j.in_stride = in_tok_stride;
+  j.do_v = 1;
+  j.nq = ntok;
+  j.dst_off = dst;
+  hipError_t e = kivi::launch_quantize_kv(j, s->bits, s->meta_half, s->batch,
+                                          (hipStream_t)stream);
   return e == hipSuccess ? KIVI_OK : hip_fail(e, __func__);
 }
 
@@ -658,23 +704,17 @@ int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t nt
   if (ntok < 1 || tq < 0 || tq % s.group != 0 || ntok - tq < 0 || ntok - tq > s.residual)
     return KIVI_ESHAPE;
   if (tq > s.capacity) return KIVI_ECAPACITY;
-  hipStream_t st = (hipStream_t)stream;
-  if (tq > 0) {
-    hipError_t e = kivi::launch_quantize_k(k, s.batch, s.num_kv_heads, s.head_dim, s.bits,
-                                           s.group, s.capacity, ntok, tq, 0, c->k_codes,
-                                           c->k_scale, c->k_zero, s.meta_half, c->k_outliers,
-                                           s.outliers, st);
-    if (e != hipSuccess) return hip_fail(e, __func__);
-    e = kivi::launch_quantize_v(v, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
-                                s.capacity, ntok, tq, 0, c->v_codes, c->v_scale, c->v_zero,
-                                s.meta_half, st);
-    if (e != hipSuccess) return hip_fail(e, __func__);
-  }
-  if (ntok > tq) {
-    hipError_t e = kivi::launch_copy_tokens(k, v, ntok, tq, c->k_res, c->v_res, s.residual, 0,
-                                            ntok - tq, s.batch, s.num_kv_heads, s.head_dim, st);
-    if (e != hipSuccess) return hip_fail(e, __func__);
-  }
+  // one launch: tokens [0, tq) quantized, [tq, ntok) copied into the residual
+  kivi::QuantJob j = cache_job(c);
+  j.k = k;
+  j.v = v;
+  j.in_stride = ntok;
+  j.do_k = j.do_v = 1;
+  j.nq = tq;
+  j.dst_off = 0;
+  j.ncopy = ntok - tq;
+  hipError_t e = kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, __func__);
   c->tq = tq;
   c->tr = ntok - tq;
   return KIVI_OK;
@@ -692,14 +732,7 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
     if ((int64_t)tq + s.residual > s.capacity) return KIVI_ECAPACITY;
     // flush: the full residual becomes the next quantized tokens; the copy
     // below is enqueued after, so slot 0 is read before it is overwritten
-    hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
-                                           s.bits, s.group, s.capacity, s.residual, s.residual,
-                                           tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
-                                           c->k_outliers, s.outliers, st);
-    if (e != hipSuccess) return hip_fail(e, __func__);
-    e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
-                                s.capacity, s.residual, s.residual, tq, c->v_codes, c->v_scale,
-                                c->v_zero, s.meta_half, st);
+    hipError_t e = launch_flush(c, tq, st);
     if (e != hipSuccess) return hip_fail(e, __func__);
     tq += s.residual;
     tr = 0;
@@ -825,14 +858,7 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
   if (rc) return rc;
   hipStream_t st = (hipStream_t)stream;
   if (flush) {
-    hipError_t e = kivi::launch_quantize_k(c->k_res, s.batch, s.num_kv_heads, s.head_dim,
-                                           s.bits, s.group, s.capacity, s.residual, s.residual,
-                                           c->tq, c->k_codes, c->k_scale, c->k_zero, s.meta_half,
-                                           c->k_outliers, s.outliers, st);
-    if (e != hipSuccess) return hip_fail(e, __func__);
-    e = kivi::launch_quantize_v(c->v_res, s.batch, s.num_kv_heads, s.head_dim, s.bits, s.group,
-                                s.capacity, s.residual, s.residual, c->tq, c->v_codes,
-                                c->v_scale, c->v_zero, s.meta_half, st);
+    hipError_t e = launch_flush(c, c->tq, st);
     if (e != hipSuccess) return hip_fail(e, __func__);
   }
   if (use_mfma(s)) {

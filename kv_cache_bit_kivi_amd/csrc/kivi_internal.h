@@ -117,47 +117,51 @@ __device__ __forceinline__ int seq_plane(const LensT<RAG>& l, int i, int H) {
 
 // Launchers: validate nothing (the C ABI layer did), return hipError_t of the
 // launch.
-// Key quantizers take the key-outlier store `outl` and its row length n_out
-// (0: no isolation, outl unused).
-hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G,
-                             int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, uint32_t* outl, int n_out,
-                             hipStream_t st);
-hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G,
-                             int cap, int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, hipStream_t st);
+
+// One launch of the codec (a prefill, a flush, or a quantize call): keys
+// and/or values of `nq` source tokens ([*][H][in_stride][D], tokens
+// [0, nq)) into destination tokens [dst_off, dst_off + nq) of the grouped
+// store, and a copy of source tokens [nq, nq + ncopy) into residual slots
+// [0, ncopy).  nq is a multiple of G (and of 32 for values).  Key outliers:
+// n_out words per key group and channel into k_out (0: no isolation).
+// List launches take nq, dst_off and ncopy per item (a[i], b[i], c[i]) and
+// use the job's nq as the largest item's count.
+struct QuantJob {
+  const uint16_t* k;
+  const uint16_t* v;
+  int in_stride;
+  int do_k, do_v;
+  int nq, dst_off, ncopy;
+  uint16_t* k_res;
+  uint16_t* v_res;
+  int R;
+  uint32_t* k_codes;
+  void* k_scale;      // float, or binary16 bits when metadata is half width
+  void* k_zero;
+  uint32_t* v_codes;
+  void* v_scale;
+  void* v_zero;
+  uint32_t* k_out;
+  int n_out;
+  int H, D, G, cap;
+};
+hipError_t launch_quantize_kv(const QuantJob& j, int bits, int mh, int B, hipStream_t st);
+// per-sequence items (the paged form writes quantized tokens into the page
+// slices the table names; pm.page_tokens is the slice capacity, j.cap unused)
+hipError_t launch_quantize_kv_list(const QuantJob& j, const SeqList& list, int bits, int mh,
+                                   int ncopy_max, hipStream_t st);
+hipError_t launch_quantize_kv_paged(const QuantJob& j, const SeqList& list, const PageMap& pm,
+                                    int bits, int mh, int ncopy_max, hipStream_t st);
 // Copies tokens [t0, t0 + n) of src ([B][H][src_stride][D]) into slots
 // [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once.
 hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
                               int t0, uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
                               int slot0, int n, int B, int H, int D, hipStream_t st);
-
-// Per-sequence variants.  Quantize: item i quantizes tokens [0, a[i]) of
-// sequence seq[i] of src ([*][H][in_stride][D]) into cache tokens
-// [b[i], b[i] + a[i]) of that sequence (a[i], b[i] multiples of G, a[i] <=
-// ntok_max).  Copy: item i copies tokens [a[i], a[i] + c[i]) of sequence
+// Per-sequence copy: item i copies tokens [a[i], a[i] + c[i]) of sequence
 // seq[i] of src into residual slots [b[i], b[i] + c[i]) (c[i] <= n_max).
-hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
-                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, uint32_t* outl, int n_out,
-                                  hipStream_t st);
-hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H, int D, int bits,
-                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, hipStream_t st);
 hipError_t launch_copy_tokens_list(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
                                    uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
                                    const SeqList& list, int n_max, int H, int D, hipStream_t st);
-// The same quantize lists writing into a paged store: destination token
-// b[i] + j of sequence seq[i] goes to its page slice (pm.page_tokens is the
-// slice capacity, `cap` unused).
-hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
-                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
-                                   uint32_t* codes, void* scale, void* zero, int mh,
-                                   uint32_t* outl, int n_out, hipStream_t st);
-hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const PageMap& pm,
-                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
-                                   uint32_t* codes, void* scale, void* zero, int mh,
-                                   hipStream_t st);
 
 // Generic decode kernel (any supported shape) + split combine.  The ragged
 // variants take the launch's per-sequence lengths (a.tq / a.tr unused) and

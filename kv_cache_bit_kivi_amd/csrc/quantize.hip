@@ -1,4 +1,4 @@
-// Quantize kernels: per-channel keys, per-token values, and token copies.
+// Codec kernels: per-channel keys, per-token values, residual copies.
 //
 // Method: "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache"
 // (mlsanity paper page, Abstract): keys are quantized per channel, values per
@@ -6,8 +6,7 @@
 // consecutive tokens and new tokens are appended along the token axis.
 //
 // Codec, per group of G values, b in {1, 2, 3, 4} bits (bit-exact contract,
-// IEEE binary32, built with
-// -ffp-contract=off and correctly rounded division):
+// IEEE binary32, built with -ffp-contract=off and correctly rounded division):
 //   mn, mx   : strict-comparison scan in index order (first extremum wins);
 //   mx == mn : scale 0, zero mn, codes 0 (the group dequantizes exactly);
 //   else     : range = mx - mn; s = range / (2^b - 1); z = mn;
@@ -22,11 +21,25 @@
 // (i << 16) | fp16 bits, in increasing token i, and left out of mn / mx; their
 // codes are 0 (the kernel stores mn in their place before encoding, which
 // encodes to 0 exactly).
-// Each block stages its fp16 tile in LDS with 16-byte loads, computes the
-// group statistics from LDS, then writes whole 32-bit code words, so any
-// number of blocks can run concurrently without read-modify-write.
-// The LIST variants work on a list of sequences with per-sequence token
-// counts and offsets (ragged batches: prefill and per-sequence flushes).
+//
+// One launch does a whole prefill or flush: its blocks are key groups (G
+// tokens x D channels of one plane), value chunks (32 tokens x D channels)
+// and residual-copy chunks, told apart by blockIdx.x.  A quantizing block
+// stages its fp16 tile in LDS with 16-byte loads, computes the group
+// statistics with several threads per group (partial extremes combined in
+// index order), writes every code as a byte into an LDS code tile, and then
+// packs whole 32-bit code words from it, so blocks never share a word.
+//
+// Encoding without a division per element: with r = rcp(s) (v_rcp_f32,
+// within one ulp of 1/s) the quotient q = fl(u * r) is within 1.5 * 2^-23 of
+// u / s relatively, and the reference's correctly rounded quotient
+// v = fl(u / s) within 2^-24; for |u / s| < 16 (at most 2^b - 1 + 2^-20 here)
+// |q - v| < 2^-18.  When q lies more than kTieBand = 2^-12 from every
+// half-integer, v lies on the same side of the same half-integers, so
+// rint(v) = rint(q); otherwise the element takes the reference's own steps
+// (the correctly rounded division).  u and s are normal binary32 numbers
+// (differences of binary16 values, s >= 2^-24 / 15), so no denormal case
+// arises.  The codes are therefore bit-identical to the reference's.
 #include <math.h>
 
 #include <type_traits>
@@ -36,30 +49,52 @@
 namespace kivi {
 namespace {
 
+constexpr int kThreads = 256;
+// the shape whose launches are compiled with constant sizes (head_dim 128,
+// group 32); every other shape takes them at run time
+constexpr int kFixD = 128, kFixG = 32;
+constexpr float kTieBand = 1.0f / 4096.0f;
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
 template <int BITS>
-__device__ __forceinline__ void group_stats(float mn, float mx, float* s_out) {
+__device__ __forceinline__ float group_scale(float mn, float mx) {
   constexpr float qmax = (float)((1 << BITS) - 1);
-  if (mx == mn) {
-    *s_out = 0.0f;
-  } else {
-    float range = mx - mn;
-    *s_out = range / qmax;
-  }
+  if (mx == mn) return 0.0f;
+  float range = mx - mn;
+  return range / qmax;
 }
 
+// code = min(rint(fl((x - z) / s)), 2^b - 1) (the reference's steps with a
+// correctly rounded division; 0 when s == 0) for four values of one group,
+// from the reciprocal r = rcp(s) (0 when s == 0): see the top of this file
+// for why the result is the same.  One branch covers the rare case that any
+// of the four lies near a half-integer: then all four take the correctly
+// rounded division, which the others would agree with anyway.
+// The clamp to 2^b - 1 is only needed on the exact path: there q stays below
+// (2^b - 1)(1 + 2^-20) (u <= mx - mn and s >= fl(mx - mn) / (2^b - 1) within
+// 2^-23), so a q that passes the band test rounds to at most 2^b - 1.
 template <int BITS>
-__device__ __forceinline__ uint32_t encode(float x, float s, float z) {
+__device__ __forceinline__ void encode4(const float (&x)[4], float s, float z, float r,
+                                        uint32_t (&c)[4]) {
   constexpr float qmax = (float)((1 << BITS) - 1);
-  if (s == 0.0f) return 0u;
-  float u = x - z;
-  float v = u / s;
-  float c = rintf(v);
-  if (c > qmax) c = qmax;
-  return (uint32_t)c;
+  float u[4], cf[4], dev[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    u[e] = x[e] - z;
+    const float q = u[e] * r;
+    cf[e] = rintf(q);
+    dev[e] = fabsf(q - cf[e]);
+  }
+  // (one compare for all four: the largest distance from an integer)
+  if (fmaxf(fmaxf(dev[0], dev[1]), fmaxf(dev[2], dev[3])) > 0.5f - kTieBand) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) cf[e] = fminf(rintf(u[e] / s), qmax);   // (s != 0 here)
+  }
+#pragma unroll
+  for (int e = 0; e < 4; e++) c[e] = (uint32_t)cf[e];
 }
 
 // metadata store: binary32, or binary16 rounded to nearest even
@@ -71,6 +106,23 @@ __device__ __forceinline__ void put_meta(void* p, size_t i, float x) {
     static_cast<float*>(p)[i] = x;
 }
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ h2v as_h2(uint32_t w) { return __builtin_bit_cast(h2v, w); }
+
+// Group extremes.  The reference scans in index order with strict
+// comparisons, so of equal values the first one stays; that differs from
+// min / max instructions only for +0 / -0, so the kernels take extremes with
+// packed binary16 min / max (binary16 comparisons order exactly as binary32
+// ones) and replace a zero extreme by the first zero in index order:
+// first_zero returns the first of n values p[0], p[stride], ... that is zero.
+__device__ __forceinline__ float first_zero(const uint16_t* p, int stride, int n) {
+  for (int i = 0; i < n; i++) {
+    const float x = h2f(p[i * stride]);
+    if (x == 0.0f) return x;
+  }
+  return 0.0f;
+}
+
 // Packed layout of a row of n codes (a key row: one token's D channels; a
 // value row: one channel's 64 tokens of a tile), n*BITS/32 words:
 //   2, 4 bits: position p at word p/E, bit BITS*(p%E), E = 32/BITS;
@@ -79,29 +131,61 @@ __device__ __forceinline__ void put_meta(void* p, size_t i, float x) {
 //              bits at word n/16 + p/32, bit beta(p%32).
 // beta keeps the nibble bit-planes of a one-bit word on the code positions
 // of a two-bit word's planes (the decode's operand conversion relies on it).
-__device__ __forceinline__ int beta(int p) { return 4 * ((p & 15) >> 1) + 2 * (p >> 4) + (p & 1); }
+__device__ __forceinline__ constexpr int beta(int p) {
+  return 4 * ((p & 15) >> 1) + 2 * (p >> 4) + (p & 1);
+}
 
-// Word k (0 .. n*BITS/32 - 1) of a row from its codes: code(p) gives the code
-// of position p of the row.
-template <int BITS, class F>
-__device__ __forceinline__ uint32_t pack_word(int n, int k, F code) {
+// n consecutive dwords of LDS from a 4-byte aligned address
+template <int N>
+__device__ __forceinline__ void ld_dwords(const uint8_t* p, uint32_t* w) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < N; i++) w[i] = q[i];
+}
+
+// Word k of a row of n codes held one per byte in LDS (row[p] = code of
+// position p, the row 4-byte aligned; only the bytes the word covers are
+// read).
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_bytes(const uint8_t* row, int n, int k) {
+  auto byte = [](const uint32_t* w, int e) -> uint32_t { return (w[e >> 2] >> (8 * (e & 3))) & 0xFFu; };
+  uint32_t wd[8];
   uint32_t w = 0;
-  if constexpr (BITS == 1) {
+  if constexpr (BITS == 2) {
+    // four codes (< 4) in the bytes of y -> their 8-bit group: y | y >> 6
+    // puts c0 | c1 << 2 in byte 0 and c2 | c3 << 2 in byte 2
+    uint32_t x[4];
+    ld_dwords<4>(row + 16 * k, x);
+    auto sq = [](uint32_t y) -> uint32_t {
+      const uint32_t t = y | (y >> 6);
+      return (t & 0xFu) | ((t >> 12) & 0xF0u);
+    };
+    w = sq(x[0]) | (sq(x[1]) << 8) | (sq(x[2]) << 16) | (sq(x[3]) << 24);
+  } else if constexpr (BITS == 4) {
+    // two codes (< 16) per 16-bit half: y | y >> 4 puts c0 | c1 << 4 in
+    // byte 0 and c2 | c3 << 4 in byte 2
+    uint32_t x[2];
+    ld_dwords<2>(row + 8 * k, x);
+    auto sq = [](uint32_t y) -> uint32_t {
+      const uint32_t t = y | (y >> 4);
+      return (t & 0xFFu) | ((t >> 8) & 0xFF00u);
+    };
+    w = sq(x[0]) | (sq(x[1]) << 16);
+  } else if constexpr (BITS == 1) {
+    ld_dwords<8>(row + 32 * k, wd);
 #pragma unroll
-    for (int q = 0; q < 32; q++) w |= code(32 * k + q) << beta(q);
-  } else if constexpr (BITS == 3) {
-    if (k < n / 16) {
-#pragma unroll
-      for (int q = 0; q < 16; q++) w |= (code(16 * k + q) & 3u) << (2 * q);
-    } else {
-      const int kh = k - n / 16;
-#pragma unroll
-      for (int q = 0; q < 32; q++) w |= (code(32 * kh + q) >> 2) << beta(q);
-    }
+    for (int q = 0; q < 32; q++) w |= byte(wd, q) << beta(q);
   } else {
-    constexpr int E = 32 / BITS;
+    if (k < n / 16) {   // two-bit plane of the low bits
+      ld_dwords<4>(row + 16 * k, wd);
 #pragma unroll
-    for (int e = 0; e < E; e++) w |= code(E * k + e) << (BITS * e);
+      for (int e = 0; e < 16; e++) w |= (byte(wd, e) & 3u) << (2 * e);
+    } else {            // one-bit plane of the high bit
+      const int kh = k - n / 16;
+      ld_dwords<8>(row + 32 * kh, wd);
+#pragma unroll
+      for (int q = 0; q < 32; q++) w |= (byte(wd, q) >> 2) << beta(q);
+    }
   }
   return w;
 }
@@ -117,58 +201,52 @@ __device__ __forceinline__ void copy16_nt(void* dst, const void* src) {
       __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src));
 }
 
-// One block per (group of G source tokens, b*H + h), or per (group, item*H +
-// h) over a sequence list (blocks past the item's token count exit).  PG: the
-// destination is the page slice the block table names for the group's
-// tokens (a group never straddles a page; a page outside the pool is skipped).
-template <int BITS, bool MH, bool LIST, bool PG>
-__global__ void __launch_bounds__(256)
-quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_stride,
-                  int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero, uint32_t* __restrict__ outl, int n_out, int H,
-                  ListT<LIST> list, PageMap pm) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [G][D]
-  float* s_sc = reinterpret_cast<float*>(tile + G * D);      // [D]
-  float* s_zr = s_sc + D;                                    // [D]
-  const int g = blockIdx.x;
-  size_t bh = blockIdx.y;
-  int seq = 0;
-  if constexpr (LIST) {
-    const int item = blockIdx.y / H;
-    if (g * G >= list.a[item]) return;   // the whole block: uniform
-    seq = list.seq[item];
-    bh = (size_t)seq * H + blockIdx.y % H;
-    dst_off = list.b[item];
-  }
-  // destination: tokens [otok, otok + G) of plane ob, a plane of ocap tokens
-  size_t ob = bh;
-  int otok = dst_off + g * G, ocap = cap;
-  if constexpr (PG) {
-    if (!page_slot(pm, seq, (int)(bh % H), H, otok, ob, otok)) return;   // uniform
-    ocap = pm.page_tokens;
-  }
-  const uint4* src = reinterpret_cast<const uint4*>(k + (bh * in_stride + (size_t)g * G) * D);
-  for (int i = threadIdx.x; i < G * D / 8; i += blockDim.x)
-    copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
-  __syncthreads();
+// LDS bytes of a key group block and of a value chunk block
+__host__ __device__ constexpr int key_parts(int D) { return kThreads / D; }
+__host__ __device__ constexpr int val_pairs(int D, int G) { return 32 * (D / G); }
+__host__ __device__ constexpr int val_parts(int D, int G) { return kThreads / val_pairs(D, G); }
+size_t key_lds_bytes(int D, int G) {
+  return (size_t)G * D * 2 + (size_t)G * D + 3 * (size_t)D * 4 +
+         2 * (size_t)(2 * key_parts(D)) * D * 4;
+}
+// value tiles: rows of D + kVPad binary16 values and code rows of kCRow
+// bytes, so that the lanes of one token (and of one channel) spread over the
+// LDS banks (unpadded, their rows are multiples of the bank count apart)
+constexpr int kVPad = 8, kCRow = 36;
+size_t val_lds_bytes(int D, int G) {
+  const size_t pr = val_pairs(D, G);
+  return 32 * (size_t)(D + kVPad) * 2 + (size_t)kCRow * D + 3 * pr * 4 +
+         2 * pr * val_parts(D, G) * 4;
+}
 
+// A key group, its G x D fp16 tile already staged at the start of smem ->
+// tokens [otok, otok + G) of destination plane ob (capacity ocap).
+// Threads: channel d = th % D, part h = th / D (tokens [h*G/P, (h+1)*G/P)).
+template <int BITS, bool MH, bool KO, bool FIX>
+__device__ void key_group(const QuantJob& j, uint8_t* smem, size_t ob, int otok, int ocap) {
+  const int D = FIX ? kFixD : j.D, G = FIX ? kFixG : j.G, W = D * BITS / 32, P = key_parts(D),
+            per = G / P;
+  const int th = threadIdx.x, d = th % D, h = th / D;
+  // statistics: channel pair cp = th % (D/2), part hs of PS = 2P parts
+  const int PS = 2 * P, pers = G / PS, cp = th % (D / 2), hs = th / (D / 2);
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                 // [G][D]
+  uint8_t* cb = smem + (size_t)G * D * 2;                              // codes [G][D]
+  float* s_sc = reinterpret_cast<float*>(cb + (size_t)G * D);         // [D]
+  float* s_zr = s_sc + D;
+  float* s_rc = s_zr + D;
+  float* p_mn = s_rc + D;                                              // [PS][D]
+  float* p_mx = p_mn + PS * D;
   const size_t gg = (size_t)(otok / G);
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float mn, mx;
-    if (n_out == 0) {
-      mn = mx = h2f(tile[d]);
-      for (int i = 1; i < G; i++) {
-        float x = h2f(tile[i * D + d]);
-        if (x < mn) mn = x;
-        if (x > mx) mx = x;
-      }
-    } else {
-      // outlier positions as a bit set over the group's G <= 128 tokens; each
-      // pass takes the first largest |x| not yet taken
+  const size_t mrow = (ob * (ocap / G) + gg) * D;
+  if constexpr (KO) {
+    // outlier selection needs the whole group: one thread per channel.  The
+    // positions form a bit set over the group's G <= 128 tokens; each pass
+    // takes the first largest |x| not yet taken.
+    if (h == 0) {
+      const int n_out = j.n_out;
       uint64_t m0 = 0, m1 = 0;
       auto taken = [&](int i) { return ((i < 64 ? m0 >> i : m1 >> (i - 64)) & 1u) != 0; };
-      for (int j = 0; j < n_out; j++) {
+      for (int q = 0; q < n_out; q++) {
         int best = 0;
         float bm = -1.0f;
         for (int i = 0; i < G; i++) {
@@ -180,108 +258,174 @@ quantize_k_kernel(const uint16_t* __restrict__ k, int D, int G, int cap, int in_
         }
         if (best < 64) m0 |= 1ull << best; else m1 |= 1ull << (best - 64);
       }
-      mn = INFINITY;
-      mx = -INFINITY;
+      float mn = INFINITY, mx = -INFINITY;
       for (int i = 0; i < G; i++) {
         if (taken(i)) continue;
-        float x = h2f(tile[i * D + d]);
+        const float x = h2f(tile[i * D + d]);
         if (x < mn) mn = x;
         if (x > mx) mx = x;
       }
       // the sparse row, then mn in the outliers' places (code 0)
-      uint32_t* orow = outl + ((ob * (ocap / G) + gg) * n_out) * D + d;
+      uint32_t* orow = j.k_out + ((ob * (ocap / G) + gg) * n_out) * D + d;
       const uint16_t mn_h = __builtin_bit_cast(uint16_t, (_Float16)mn);   // exact
-      int j = 0;
+      int q = 0;
       for (int i = 0; i < G; i++) {
         if (!taken(i)) continue;
-        orow[(size_t)j * D] = ((uint32_t)i << 16) | tile[i * D + d];
+        orow[(size_t)q * D] = ((uint32_t)i << 16) | tile[i * D + d];
         tile[i * D + d] = mn_h;
-        j++;
+        q++;
+      }
+      const float s = group_scale<BITS>(mn, mx);
+      s_sc[d] = s;
+      s_zr[d] = mn;
+      s_rc[d] = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+      put_meta<MH>(j.k_scale, mrow + d, s);
+      put_meta<MH>(j.k_zero, mrow + d, mn);
+    }
+  } else {
+    // channels 2cp, 2cp + 1 over tokens [hs*pers, (hs+1)*pers), packed
+    const uint16_t* col = tile + (size_t)hs * pers * D + 2 * cp;
+    h2v mn2 = as_h2(*reinterpret_cast<const uint32_t*>(col)), mx2 = mn2;
+    for (int i = 1; i < pers; i++) {
+      const h2v x = as_h2(*reinterpret_cast<const uint32_t*>(col + (size_t)i * D));
+      mn2 = __builtin_elementwise_min(mn2, x);
+      mx2 = __builtin_elementwise_max(mx2, x);
+    }
+    float mn[2] = {(float)mn2.x, (float)mn2.y}, mx[2] = {(float)mx2.x, (float)mx2.y};
+#pragma unroll
+    for (int e = 0; e < 2; e++) {
+      if (mn[e] == 0.0f || mx[e] == 0.0f) {
+        const float z0 = first_zero(col + e, D, pers);
+        if (mn[e] == 0.0f) mn[e] = z0;
+        if (mx[e] == 0.0f) mx[e] = z0;
+      }
+      p_mn[hs * D + 2 * cp + e] = mn[e];
+      p_mx[hs * D + 2 * cp + e] = mx[e];
+    }
+    __syncthreads();
+    if (hs == 0) {
+#pragma unroll
+      for (int e = 0; e < 2; e++) {
+        const int dd = 2 * cp + e;
+        // parts in index order, strict comparisons: the earlier part keeps ties
+        for (int q = 1; q < PS; q++) {
+          const float a = p_mn[q * D + dd], b = p_mx[q * D + dd];
+          if (a < mn[e]) mn[e] = a;
+          if (b > mx[e]) mx[e] = b;
+        }
+        const float s = group_scale<BITS>(mn[e], mx[e]);
+        s_sc[dd] = s;
+        s_zr[dd] = mn[e];
+        s_rc[dd] = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+        put_meta<MH>(j.k_scale, mrow + dd, s);
+        put_meta<MH>(j.k_zero, mrow + dd, mn[e]);
       }
     }
-    float s;
-    group_stats<BITS>(mn, mx, &s);
-    s_sc[d] = s;
-    s_zr[d] = mn;
-    size_t m = (ob * (ocap / G) + gg) * D + d;
-    put_meta<MH>(scale, m, s);
-    put_meta<MH>(zero, m, mn);
   }
   __syncthreads();
-
-  const int W = D * BITS / 32;   // words per key row
-  uint32_t* dst = codes + (ob * ocap + otok) * W;
-  for (int it = threadIdx.x; it < G * W; it += blockDim.x) {
+  {
+    // four tokens at a time (per is a multiple of 4): loads, codes, stores
+    const float s = s_sc[d], z = s_zr[d], r = s_rc[d];
+    for (int i = h * per; i < (h + 1) * per; i += 4) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; e++) x[e] = h2f(tile[(i + e) * D + d]);
+      uint32_t c[4];
+      encode4<BITS>(x, s, z, r, c);
+#pragma unroll
+      for (int e = 0; e < 4; e++) cb[(i + e) * D + d] = (uint8_t)c[e];
+    }
+  }
+  __syncthreads();
+  uint32_t* dst = j.k_codes + (ob * ocap + otok) * W;
+  for (int it = th; it < G * W; it += kThreads) {
     const int i = it / W, w = it % W;
-    dst[it] = pack_word<BITS>(D, w, [&](int d) {
-      return encode<BITS>(h2f(tile[i * D + d]), s_sc[d], s_zr[d]);
-    });
+    dst[it] = pack_bytes<BITS>(cb + (size_t)i * D, D, w);
   }
 }
 
-// One block per (32 source tokens, b*H + h) (or per item, as above).  Value
-// codes are stored in 64-token tiles, channel-major: word ((t/64)*D + d)*(64/E)
-// + (t%64)/E.
-template <int BITS, bool MH, bool LIST, bool PG>
-__global__ void __launch_bounds__(256)
-quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_stride,
-                  int dst_off, uint32_t* __restrict__ codes, void* __restrict__ scale,
-                  void* __restrict__ zero, int H, ListT<LIST> list, PageMap pm) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);       // [32][D]
-  const int NG = D / G;
-  float* s_sc = reinterpret_cast<float*>(tile + 32 * D);     // [32][NG]
-  float* s_zr = s_sc + 32 * NG;
-  const int blk = blockIdx.x;
-  size_t bh = blockIdx.y;
-  int seq = 0;
-  if constexpr (LIST) {
-    const int item = blockIdx.y / H;
-    if (blk * 32 >= list.a[item]) return;   // the whole block: uniform
-    seq = list.seq[item];
-    bh = (size_t)seq * H + blockIdx.y % H;
-    dst_off = list.b[item];
-  }
-  // destination: tokens [t_base, t_base + 32) of plane ob (ocap tokens)
-  size_t ob = bh;
-  int t_base = dst_off + blk * 32, ocap = cap;
-  if constexpr (PG) {
-    if (!page_slot(pm, seq, (int)(bh % H), H, t_base, ob, t_base)) return;   // uniform
-    ocap = pm.page_tokens;
-  }
-  const uint4* src = reinterpret_cast<const uint4*>(v + (bh * in_stride + (size_t)blk * 32) * D);
-  for (int i = threadIdx.x; i < 32 * D / 8; i += blockDim.x)
-    copy16_nt(reinterpret_cast<uint4*>(tile) + i, src + i);
-  __syncthreads();
-
-  for (int it = threadIdx.x; it < 32 * NG; it += blockDim.x) {
-    const int t = it / NG, j = it % NG;
-    const uint16_t* row = tile + t * D + j * G;
-    float mn = h2f(row[0]), mx = mn;
-    for (int i = 1; i < G; i++) {
-      float x = h2f(row[i]);
-      if (x < mn) mn = x;
-      if (x > mx) mx = x;
+// A value chunk, its 32 x D fp16 tile already staged at the start of smem ->
+// tokens [t_base, t_base + 32) of destination plane ob (capacity ocap), one
+// half of a 64-token tile.  Value
+// codes are stored in 64-token tiles, channel-major: word
+// ((t/64)*D + d)*(64/E) + (t%64)/E.  Threads: part h = th % P of the
+// (token t, channel group jg) pair th / P (channels [jg*G + h*G/P, +G/P)).
+template <int BITS, bool MH, bool FIX>
+__device__ void value_chunk(const QuantJob& j, uint8_t* smem, size_t ob, int t_base, int ocap) {
+  const int D = FIX ? kFixD : j.D, G = FIX ? kFixG : j.G, NG = D / G, NP = val_pairs(D, G),
+            P = val_parts(D, G), per = G / P;
+  const int th = threadIdx.x, h = th % P, pr = th / P, t = pr / NG, jg = pr % NG;
+  const int VT = D + kVPad;                                            // tile row stride
+  uint16_t* tile = reinterpret_cast<uint16_t*>(smem);                 // [32][VT]
+  uint8_t* cbT = smem + 32 * (size_t)VT * 2;                           // codes [D][kCRow]
+  float* s_sc = reinterpret_cast<float*>(cbT + (size_t)kCRow * D);    // [pairs]
+  float* s_zr = s_sc + NP;
+  float* s_rc = s_zr + NP;
+  float* p_mn = s_rc + NP;                                             // [pairs][P]
+  float* p_mx = p_mn + NP * P;
+  const int c0 = jg * G + h * per;
+  float mn, mx;
+  {
+    // channels [c0, c0 + per) of token t, four at a time (per is a multiple
+    // of 4), packed
+    const uint16_t* row = tile + t * VT + c0;
+    const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+    h2v mn2 = __builtin_elementwise_min(as_h2(x0.x), as_h2(x0.y));
+    h2v mx2 = __builtin_elementwise_max(as_h2(x0.x), as_h2(x0.y));
+    for (int c = 4; c < per; c += 4) {
+      const uint2 x = *reinterpret_cast<const uint2*>(row + c);
+      mn2 = __builtin_elementwise_min(mn2, __builtin_elementwise_min(as_h2(x.x), as_h2(x.y)));
+      mx2 = __builtin_elementwise_max(mx2, __builtin_elementwise_max(as_h2(x.x), as_h2(x.y)));
     }
-    float s;
-    group_stats<BITS>(mn, mx, &s);
-    s_sc[it] = s;
-    s_zr[it] = mn;
-    size_t m = (ob * ocap + t_base + t) * NG + j;
-    put_meta<MH>(scale, m, s);
-    put_meta<MH>(zero, m, mn);
+    mn = fminf((float)mn2.x, (float)mn2.y);
+    mx = fmaxf((float)mx2.x, (float)mx2.y);
+    if (mn == 0.0f || mx == 0.0f) {
+      const float z0 = first_zero(row, 1, per);
+      if (mn == 0.0f) mn = z0;
+      if (mx == 0.0f) mx = z0;
+    }
+  }
+  p_mn[pr * P + h] = mn;
+  p_mx[pr * P + h] = mx;
+  __syncthreads();
+  if (h == 0) {
+    for (int q = 1; q < P; q++) {
+      const float a = p_mn[pr * P + q], b = p_mx[pr * P + q];
+      if (a < mn) mn = a;
+      if (b > mx) mx = b;
+    }
+    const float s = group_scale<BITS>(mn, mx);
+    s_sc[pr] = s;
+    s_zr[pr] = mn;
+    s_rc[pr] = s == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(s);
+    const size_t m = (ob * ocap + t_base + t) * NG + jg;
+    put_meta<MH>(j.v_scale, m, s);
+    put_meta<MH>(j.v_zero, m, mn);
+  }
+  __syncthreads();
+  {
+    // four channels at a time (per is a multiple of 4): one 8-byte load
+    const float s = s_sc[pr], z = s_zr[pr], r = s_rc[pr];
+    for (int c = c0; c < c0 + per; c += 4) {
+      const uint2 x2 = *reinterpret_cast<const uint2*>(tile + t * VT + c);
+      const float x[4] = {h2f((uint16_t)(x2.x & 0xFFFFu)), h2f((uint16_t)(x2.x >> 16)),
+                          h2f((uint16_t)(x2.y & 0xFFFFu)), h2f((uint16_t)(x2.y >> 16))};
+      uint32_t q[4];
+      encode4<BITS>(x, s, z, r, q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) cbT[(c + e) * kCRow + t] = (uint8_t)q[e];
+    }
   }
   __syncthreads();
 
   constexpr int WPC = 2 * BITS;   // words per channel per 64-token tile
-  uint32_t* plane = codes + ob * ((size_t)ocap * D * BITS / 32);
+  uint32_t* plane = j.v_codes + ob * ((size_t)ocap * D * BITS / 32);
   const size_t tile_idx = (size_t)(t_base / 64);
   const int half = (t_base % 64) / 32;   // this block's half of the tile
   // the words of a channel's tile row that hold only this half's tokens: of
   // the 2*BITS words, those whose positions all lie in [32*half, 32*half+32)
-  for (int it = threadIdx.x; it < D * BITS; it += blockDim.x) {
+  for (int it = th; it < D * BITS; it += kThreads) {
     const int d = it / BITS, k = it % BITS;
-    const int j = d / G;
     int rw;   // row word index
     if constexpr (BITS == 1) {
       rw = half;
@@ -290,11 +434,146 @@ quantize_v_kernel(const uint16_t* __restrict__ v, int D, int G, int cap, int in_
     } else {
       rw = half * BITS + k;
     }
-    plane[(tile_idx * D + d) * WPC + rw] = pack_word<BITS>(64, rw, [&](int p) {
-      const int t = p - 32 * half;   // token of this block
-      return encode<BITS>(h2f(tile[t * D + d]), s_sc[t * NG + j], s_zr[t * NG + j]);
-    });
+    // (this half's 32 code bytes are positions 32*half .. 32*half + 31 of
+    // the channel's tile row: word k of this half reads them from offset 0)
+    uint32_t w;
+    const uint8_t* row = cbT + (size_t)d * kCRow;
+    if constexpr (BITS == 1) {
+      w = pack_bytes<1>(row, 32, 0);
+    } else if constexpr (BITS == 3) {
+      w = k < 2 ? pack_bytes<3>(row, 32, k) : pack_bytes<3>(row, 32, 2);
+    } else {
+      w = pack_bytes<BITS>(row, 32, k);
+    }
+    plane[(tile_idx * D + d) * WPC + rw] = w;
   }
+}
+
+// Items (key groups or value chunks) per block: a block walks up to kItems
+// consecutive items of one plane, holding the next item's tile in registers
+// (up to kMaxPf 16-byte units per thread) while it computes the current one
+// from LDS, so the tile loads overlap the computation.  Larger tiles are
+// loaded at the start of their item instead.
+constexpr int kItems = 8;
+constexpr int kMaxPf = 4;
+struct Prefetch {
+  u32x4_t r[kMaxPf];
+};
+__device__ __forceinline__ void pf_load(Prefetch& p, const uint16_t* src, int n16) {
+#pragma unroll
+  for (int v = 0; v < kMaxPf; v++) {
+    const int i = (int)threadIdx.x + v * kThreads;
+    if (i < n16) p.r[v] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src) + i);
+  }
+}
+// (the tile in LDS has rows of 2^sh 16-byte units plus `pad` units)
+__device__ __forceinline__ int padded(int i, int sh, int pad) { return i + (i >> sh) * pad; }
+__device__ __forceinline__ void pf_store(const Prefetch& p, uint8_t* smem, int n16, int sh,
+                                         int pad) {
+#pragma unroll
+  for (int v = 0; v < kMaxPf; v++) {
+    const int i = (int)threadIdx.x + v * kThreads;
+    if (i < n16) reinterpret_cast<u32x4_t*>(smem)[padded(i, sh, pad)] = p.r[v];
+  }
+}
+__device__ __forceinline__ void stage_direct(uint8_t* smem, const uint16_t* src, int n16, int sh,
+                                             int pad) {
+  for (int i = threadIdx.x; i < n16; i += kThreads)
+    copy16_nt(reinterpret_cast<uint4*>(smem) + padded(i, sh, pad),
+              reinterpret_cast<const uint4*>(src) + i);
+}
+
+// One launch of the codec (blockIdx.y: plane, or list item * H + head):
+//   blockIdx.x < nkb           : key groups  (do_k), kItems per block
+//   nkb <= blockIdx.x < nkb+nvb: value chunks (do_v), kItems per block
+//   above                      : residual copy chunk of 256 x 16 bytes
+// Uniform launches quantize source tokens [0, nq) into destination tokens
+// [dst_off, dst_off + nq) and copy source tokens [nq, nq + ncopy) into
+// residual slots [0, ncopy); list item i does the same with nq = a[i],
+// dst_off = b[i], ncopy = c[i] for sequence seq[i] (blocks past an item's
+// counts exit).  PG: the destination is the page slice the block table names
+// for the group's tokens (a group never straddles a page; a page outside the
+// pool is skipped).
+template <int BITS, bool MH, bool LIST, bool PG, bool KO, bool FIX>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 5)))
+quantize_kv_kernel(QuantJob j, ListT<LIST> list, PageMap pm) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int H = j.H, D = FIX ? kFixD : j.D, G = FIX ? kFixG : j.G;
+  size_t bh = blockIdx.y;
+  int seq = 0, nq = j.nq, dst_off = j.dst_off, ncopy = j.ncopy;
+  if constexpr (LIST) {
+    const int item = blockIdx.y / H;
+    seq = list.seq[item];
+    bh = (size_t)seq * H + blockIdx.y % H;
+    nq = list.a[item];
+    dst_off = list.b[item];
+    ncopy = list.c[item];
+  }
+  // (j.nq: the largest item's count)
+  const int nkb = j.do_k ? (j.nq / G + kItems - 1) / kItems : 0;
+  const int nvb = j.do_v ? (j.nq / 32 + kItems - 1) / kItems : 0;
+  int bx = blockIdx.x;
+  // items [i0, i1) of `tok` tokens each from source tokens i0*tok, ...: the
+  // block loop, `run(i)` computing item i from the staged tile (the branch
+  // on the page slot inside it is uniform, so every barrier is reached by
+  // the whole block)
+  // (row units 2^sh: D / 8 is a power of two)
+  const int sh = 31 - __builtin_clz(D / 8);
+  auto walk = [&](const uint16_t* src, int tok, int pad, int n_items, auto run) {
+    const int i0 = bx * kItems, i1 = min(i0 + kItems, n_items);
+    if (i0 >= i1) return;   // the whole block: uniform
+    const int n16 = tok * D / 8;
+    const bool pf = n16 <= kMaxPf * kThreads;
+    auto item_src = [&](int i) { return src + (bh * j.in_stride + (size_t)i * tok) * D; };
+    Prefetch p;
+    if (pf) pf_load(p, item_src(i0), n16);
+    for (int i = i0; i < i1; i++) {
+      __syncthreads();   // the previous item's LDS reads are done
+      if (pf) {
+        pf_store(p, smem, n16, sh, pad);
+        if (i + 1 < i1) pf_load(p, item_src(i + 1), n16);
+      } else {
+        stage_direct(smem, item_src(i), n16, sh, pad);
+      }
+      __syncthreads();
+      run(i);
+    }
+  };
+  if (bx < nkb) {
+    walk(j.k, G, 0, nq / G, [&](int g) {
+      size_t ob = bh;
+      int otok = dst_off + g * G, ocap = j.cap;
+      if constexpr (PG) {
+        if (!page_slot(pm, seq, (int)(bh % H), H, otok, ob, otok)) return;   // uniform
+        ocap = pm.page_tokens;
+      }
+      key_group<BITS, MH, KO, FIX>(j, smem, ob, otok, ocap);
+    });
+    return;
+  }
+  bx -= nkb;
+  if (bx < nvb) {
+    walk(j.v, 32, kVPad / 8, nq / 32, [&](int c) {
+      size_t ob = bh;
+      int t_base = dst_off + c * 32, ocap = j.cap;
+      if constexpr (PG) {
+        if (!page_slot(pm, seq, (int)(bh % H), H, t_base, ob, t_base)) return;   // uniform
+        ocap = pm.page_tokens;
+      }
+      value_chunk<BITS, MH, FIX>(j, smem, ob, t_base, ocap);
+    });
+    return;
+  }
+  bx -= nvb;
+  // residual copy: source tokens [nq, nq + ncopy) -> slots [0, ncopy)
+  const int per_tok = D / 8;
+  const int i = bx * kThreads + (int)threadIdx.x;
+  if (i >= ncopy * per_tok) return;
+  const int t = i / per_tok, c = i % per_tok;
+  const size_t so = ((bh * j.in_stride + nq + t) * D) / 8 + c;
+  const size_t dd = ((bh * j.R + t) * D) / 8 + c;
+  copy16_nt(reinterpret_cast<uint4*>(j.k_res) + dd, reinterpret_cast<const uint4*>(j.k) + so);
+  copy16_nt(reinterpret_cast<uint4*>(j.v_res) + dd, reinterpret_cast<const uint4*>(j.v) + so);
 }
 
 template <bool LIST>
@@ -322,11 +601,14 @@ copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restric
   }
 }
 
-// f(bits, metadata-half) with both as compile-time constants
+// f(bits, metadata-half, outliers) with all three as compile-time constants
 template <class F>
-void dispatch_bits(int bits, int mh, F f) {
+void dispatch(int bits, int mh, bool ko, F f) {
+  auto with_ko = [&](auto B, auto M) {
+    if (ko) f(B, M, std::true_type{}); else f(B, M, std::false_type{});
+  };
   auto with_mh = [&](auto B) {
-    if (mh) f(B, std::true_type{}); else f(B, std::false_type{});
+    if (mh) with_ko(B, std::true_type{}); else with_ko(B, std::false_type{});
   };
   switch (bits) {
     case 1: with_mh(std::integral_constant<int, 1>{}); break;
@@ -336,91 +618,53 @@ void dispatch_bits(int bits, int mh, F f) {
   }
 }
 
+// grid x extent and LDS bytes of a job
+void job_shape(const QuantJob& j, int ncopy_max, int& gx, size_t& lds) {
+  const int nkb = j.do_k ? (j.nq / j.G + kItems - 1) / kItems : 0;
+  const int nvb = j.do_v ? (j.nq / 32 + kItems - 1) / kItems : 0;
+  const int ncb = (ncopy_max * (j.D / 8) + kThreads - 1) / kThreads;
+  gx = nkb + nvb + ncb;
+  lds = 0;
+  if (nkb) lds = key_lds_bytes(j.D, j.G);
+  if (nvb) lds = lds > val_lds_bytes(j.D, j.G) ? lds : val_lds_bytes(j.D, j.G);
+}
+
+template <bool LIST, bool PG>
+hipError_t launch_job(const QuantJob& j, int bits, int mh, int gy, int ncopy_max,
+                      const ListT<LIST>& list, const PageMap& pm, hipStream_t st) {
+  int gx;
+  size_t lds;
+  job_shape(j, ncopy_max, gx, lds);
+  if (gx == 0 || gy == 0) return hipSuccess;
+  const dim3 grid(gx, gy);
+  const bool fix = j.D == kFixD && j.G == kFixG;
+  dispatch(bits, mh, j.n_out > 0, [&](auto B, auto M, auto K) {
+    if (fix)
+      quantize_kv_kernel<B.value, M.value, LIST, PG, K.value, true>
+          <<<grid, kThreads, lds, st>>>(j, list, pm);
+    else
+      quantize_kv_kernel<B.value, M.value, LIST, PG, K.value, false>
+          <<<grid, kThreads, lds, st>>>(j, list, pm);
+  });
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_quantize_k(const uint16_t* k, int B, int H, int D, int bits, int G, int cap,
-                             int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, uint32_t* outl, int n_out,
-                             hipStream_t st) {
-  dim3 grid(ntok / G, B * H);
-  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, dst_off, codes, scale, zero, outl,
-                                   n_out, H, NoList{}, PageMap{});
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, false, false>); });
-  return hipGetLastError();
+hipError_t launch_quantize_kv(const QuantJob& j, int bits, int mh, int B, hipStream_t st) {
+  return launch_job<false, false>(j, bits, mh, B * j.H, j.ncopy, NoList{}, PageMap{}, st);
 }
 
-hipError_t launch_quantize_v(const uint16_t* v, int B, int H, int D, int bits, int G, int cap,
-                             int in_stride, int ntok, int dst_off, uint32_t* codes,
-                             void* scale, void* zero, int mh, hipStream_t st) {
-  dim3 grid(ntok / 32, B * H);
-  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, dst_off, codes, scale, zero, H,
-                                   NoList{}, PageMap{});
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, false, false>); });
-  return hipGetLastError();
+hipError_t launch_quantize_kv_list(const QuantJob& j, const SeqList& list, int bits, int mh,
+                                   int ncopy_max, hipStream_t st) {
+  if (list.n == 0) return hipSuccess;
+  return launch_job<true, false>(j, bits, mh, list.n * j.H, ncopy_max, list, PageMap{}, st);
 }
 
-hipError_t launch_quantize_k_list(const uint16_t* k, const SeqList& list, int H, int D, int bits,
-                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, uint32_t* outl, int n_out,
-                                  hipStream_t st) {
-  if (list.n == 0 || ntok_max == 0) return hipSuccess;
-  dim3 grid(ntok_max / G, list.n * H);
-  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, cap, in_stride, 0, codes, scale, zero, outl, n_out,
-                                   H, list, PageMap{});
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, false>); });
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_v_list(const uint16_t* v, const SeqList& list, int H, int D, int bits,
-                                  int G, int cap, int in_stride, int ntok_max, uint32_t* codes,
-                                  void* scale, void* zero, int mh, hipStream_t st) {
-  if (list.n == 0 || ntok_max == 0) return hipSuccess;
-  dim3 grid(ntok_max / 32, list.n * H);
-  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(v, D, G, cap, in_stride, 0, codes, scale, zero, H, list,
-                                   PageMap{});
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, true, false>); });
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_k_paged(const uint16_t* k, const SeqList& list, const PageMap& pm,
-                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
-                                   uint32_t* codes, void* scale, void* zero, int mh,
-                                   uint32_t* outl, int n_out, hipStream_t st) {
-  if (list.n == 0 || ntok_max == 0) return hipSuccess;
-  dim3 grid(ntok_max / G, list.n * H);
-  size_t lds = (size_t)G * D * 2 + 2 * D * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(k, D, G, 0, in_stride, 0, codes, scale, zero, outl, n_out, H,
-                                   list, pm);
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_k_kernel<B.value, M.value, true, true>); });
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_v_paged(const uint16_t* v, const SeqList& list, const PageMap& pm,
-                                   int H, int D, int bits, int G, int in_stride, int ntok_max,
-                                   uint32_t* codes, void* scale, void* zero, int mh,
-                                   hipStream_t st) {
-  if (list.n == 0 || ntok_max == 0) return hipSuccess;
-  dim3 grid(ntok_max / 32, list.n * H);
-  size_t lds = (size_t)32 * D * 2 + 2 * 32 * (D / G) * sizeof(float);
-  auto go = [&](auto kernel) {
-    kernel<<<grid, 256, lds, st>>>(v, D, G, 0, in_stride, 0, codes, scale, zero, H, list, pm);
-  };
-  dispatch_bits(bits, mh, [&](auto B, auto M) { go(quantize_v_kernel<B.value, M.value, true, true>); });
-  return hipGetLastError();
+hipError_t launch_quantize_kv_paged(const QuantJob& j, const SeqList& list, const PageMap& pm,
+                                    int bits, int mh, int ncopy_max, hipStream_t st) {
+  if (list.n == 0) return hipSuccess;
+  return launch_job<true, true>(j, bits, mh, list.n * j.H, ncopy_max, list, pm, st);
 }
 
 hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
