@@ -41,8 +41,8 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
 # GPU work before the timed region: at least this many steps, whatever
-# --warmup says (the shader clock needs a few hundred launches of load to
-# settle; fewer make the first timed windows slow)
+# --warmup says, so that every layer cache (32 by default) has been visited
+# several times, its first flush included, before the timed region
 MIN_WARMUP_STEPS = 512
 # worker processes of the multi-core CPU leg: the host's cores, at most 16
 MAX_CPU_WORKERS = 16
@@ -604,17 +604,29 @@ def main():
     W = max(1, args.window)
     info, windows = plan_steps(args.steps, NL, tq_s if ragged else tq_s[:1],
                                tr_s if ragged else tr_s[:1], R, W)
+    # The first step runs on an idle queue: between an event recorded before
+    # it and its kernel lies the host's enqueue latency (tens of microseconds
+    # measured), so the first window opens after the first step's launch (it
+    # then marks that kernel's end) and step 0 stays out of the roofline (it
+    # still counts in `value`).
+    if len(windows[0][1]) > 1 or len(windows) == 1:
+        windows[0] = (windows[0][0], windows[0][1][1:] or windows[0][1])
+    else:
+        windows = windows[1:]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in windows]
-    opens = {ix[0]: k for k, (_, ix) in enumerate(windows)}
+    # window k opens after the launch of the step before its first step
+    opens = {ix[0] - 1: k for k, (_, ix) in enumerate(windows) if ix[0] > 0}
     closes = {ix[-1]: k for k, (_, ix) in enumerate(windows)}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    if windows[0][1][0] == 0:        # a one-step run: its only step is timed as it is
+        ev[0][0].record(cur)
     for i in range(args.steps):
+        step(i)
         k = opens.get(i)
         if k is not None:
             ev[k][0].record(cur)
-        step(i)
         k = closes.get(i)
         if k is not None:
             ev[k][1].record(cur)
@@ -713,7 +725,8 @@ def main():
             "kernel": (f"{calls} (append and decode launches)" if args.separate
                        else f"kivi decode attention with the append folded in ({calls}: one "
                        "decode launch per step)") +
-                      f"; HIP events around runs of up to {W} consecutive steps" +
+                      f"; HIP events around runs of up to {W} consecutive steps (the first "
+                      "step of the timed region left out: it starts on an idle queue)" +
                       (" without a flush" if plain else " (every step flushes)"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,

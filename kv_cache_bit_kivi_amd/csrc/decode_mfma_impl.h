@@ -287,10 +287,9 @@ struct Cfg {
 
 // register budget of the occupancy target: one wave per SIMD for 8 heads and
 // for pre-RoPE keys with several heads, two waves otherwise (blocks of 8 waves
-// place two per SIMD).  The three-wave budget spilled 56 bytes per lane in the
-// one-head 2-bit variant (27.5 against 27.2 us on the batch-8 Llama layer at
-// two waves) and 68-80 bytes with outliers.  The four-head variants still
-// spill 16-68 bytes per lane at two waves.
+// place two per SIMD).  Three waves per SIMD (12-wave blocks) fit the one-head
+// 2-bit variant without spills (158 registers) but measured slower (28.1
+// against 27.1 us on the batch-8 Llama layer).
 template <int BITS, int R, bool ROPE = false, int KO = 0>
 constexpr int waves_per_eu() {
   return (R >= 8 || (ROPE && R >= 2)) ? 1 : 2;
@@ -712,9 +711,15 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
     for (int e = 0; e < 8; e++) ores[h][e] = 0.f;
   }
-  float4v cv[8];
+  // P.V partial outputs of the rows this lane holds (heads 2kg, 2kg+1): each
+  // tile's products are summed (hi + lo rows) into these, so the product
+  // accumulators are free between tiles (one head: 8 registers, not 32)
+  constexpr int OH = R >= 2 ? 2 : 1;
+  float oacc[8][OH];
 #pragma unroll
-  for (int nb = 0; nb < 8; nb++) cv[nb] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 8; nb++)
+#pragma unroll
+    for (int e = 0; e < OH; e++) oacc[nb][e] = 0.f;
 
   // score slot of head 2*kg + hh for token index k (absent heads go to a sink)
   auto sc_addr = [&](int hh, int k) __attribute__((always_inline)) -> float* {
@@ -754,10 +759,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       const float a0 = pick<R>(alpha, kg, 0), a1 = pick<R>(alpha, kg, 1);
 #pragma unroll
       for (int nb = 0; nb < 8; nb++) {
-        cv[nb][0] *= a0;
-        cv[nb][1] *= a0;
-        cv[nb][2] *= a1;
-        cv[nb][3] *= a1;
+        oacc[nb][0] *= a0;
+        if constexpr (OH == 2) oacc[nb][OH - 1] *= a1;
       }
     }
   };
@@ -1176,6 +1179,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
       for (int nbj = 0; nbj < 2; nbj++) {
         const int nb = 2 * j + nbj;
+        float4v cvn = float4v{0.f, 0.f, 0.f, 0.f};   // this block's products
         const char* vrow = vstg + (16 * nb + n16) * WPC * 4;   // channel 16nb + n16
         if constexpr (BITS == 1 || BITS == 3) {
           // one-bit plane: word kg/2 holds this lane group's 16 tokens in
@@ -1184,20 +1188,22 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
               vrow + (BITS == 3 ? 16 : 0) + (kg >> 1) * 4);
           const float sc = BITS == 3 ? 8.0f : 2.0f;
           const uint32_t xs = x >> (2 * (kg & 1));
-          cv[nb] = mfma_bf(av0, cvt_nib2_bf(xs & 0x11111111u, sc), cv[nb]);
-          cv[nb] = mfma_bf(av1, cvt_nib2_bf((xs >> 1) & 0x11111111u, sc), cv[nb]);
+          cvn = mfma_bf(av0, cvt_nib2_bf(xs & 0x11111111u, sc), cvn);
+          cvn = mfma_bf(av1, cvt_nib2_bf((xs >> 1) & 0x11111111u, sc), cvn);
         }
         if constexpr (BITS == 2 || BITS == 3) {
           // two-bit plane: word kg
           const uint32_t x = *reinterpret_cast<const uint32_t*>(vrow + kg * 4);
-          cv[nb] = mfma_bf(av0, cvt_nib2_bf(x & 0x33333333u), cv[nb]);
-          cv[nb] = mfma_bf(av1, cvt_nib2_bf((x >> 2) & 0x33333333u), cv[nb]);
+          cvn = mfma_bf(av0, cvt_nib2_bf(x & 0x33333333u), cvn);
+          cvn = mfma_bf(av1, cvt_nib2_bf((x >> 2) & 0x33333333u), cvn);
         }
         if constexpr (BITS == 4) {
           const uint2 x = *reinterpret_cast<const uint2*>(vstg + (16 * nb + n16) * WPC * 4 + kg * 8);
-          cv[nb] = mfma_bf(av0, cvt_word4_bf(x.x), cv[nb]);
-          cv[nb] = mfma_bf(av1, cvt_word4_bf(x.y), cv[nb]);
+          cvn = mfma_bf(av0, cvt_word4_bf(x.x), cvn);
+          cvn = mfma_bf(av1, cvt_word4_bf(x.y), cvn);
         }
+        oacc[nb][0] += cvn[0] + cvn[1];
+        if constexpr (OH == 2) oacc[nb][OH - 1] += cvn[2] + cvn[3];
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -1480,8 +1486,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     for (int nb = 0; nb < 8; nb++) {
       float* o0 = h0 < R ? lds_o + h0 * kD + 16 * nb + n16 : lds_dummy + n16;
       float* o1 = h1 < R ? lds_o + h1 * kD + 16 * nb + n16 : lds_dummy + n16;
-      *o0 = cv[nb][0] + cv[nb][1];
-      *o1 = cv[nb][2] + cv[nb][3];
+      *o0 = oacc[nb][0];
+      *o1 = OH == 2 ? oacc[nb][OH - 1] : 0.f;
     }
   }
   // residual P.V sums: lane (tg, c8) adds channels 8*c8+2*tg, 8*c8+2*tg+1
