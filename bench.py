@@ -44,6 +44,9 @@ METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-he
 # --warmup says, so that every layer cache (32 by default) has been visited
 # several times, its first flush included, before the timed region
 MIN_WARMUP_STEPS = 512
+LAT_REPS = 64
+LAT_SPIN_CYCLES = 2_000_000
+PF_SPIN_CYCLES = 20_000_000
 # worker processes of the multi-core CPU leg: the host's cores, at most 16
 MAX_CPU_WORKERS = 16
 
@@ -403,6 +406,8 @@ def main():
                     help="processes of the multi-core CPU leg (default: host cores, at most 16)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run a plain device copy of MIB MiB (PMC calibration)")
+    ap.add_argument("--latency-reps", type=int, default=LAT_REPS,
+                    help="prefill + step pairs timed for latency_us (0: skip)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_MIB", "CMD"),
                     help="write the calibrated traffic summary from two PMC runs and exit")
     args = ap.parse_args()
@@ -485,9 +490,12 @@ def main():
     caches = []
     if paged:
         cap = (cap + args.paged - 1) // args.paged * args.paged
-    # each layer's prefill is timed with events: the codec's throughput
+    # each layer's prefill is timed with events: the codec's throughput.  A
+    # spin kernel first, so the layers' allocations and prefills queue up
+    # behind it and each event pair brackets device work, not host calls.
     cur = torch.cuda.current_stream()
     pf_ev = []
+    torch.cuda._sleep(PF_SPIN_CYCLES)
     for li in range(NL):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         if paged:
@@ -512,7 +520,6 @@ def main():
         e1.record(cur)
         pf_ev.append((e0, e1))
         caches.append(c)
-    del kd, vd
     # distinct synthetic tokens / queries for every step, resident on the GPU
     n_tok = min(max(warm, args.steps), 256)
     knew, vnew, qs = [], [], []
@@ -640,6 +647,40 @@ def main():
             assert np.array_equal(tq_l, info[last][2]) and np.array_equal(tr_l, info[last][3]), \
                 "cache lengths differ from the step plan"
 
+    # Latency of a fresh cache's first decode: a prefill of layer 0 followed by
+    # one fused step, LAT_REPS pairs enqueued behind a short spin kernel so the
+    # events see back-to-back device work, not the host's enqueue time; and
+    # one pair timed on the host from an idle queue to its synchronisation.
+    c0 = caches[0]
+
+    def prefill0():
+        if ragged:
+            c0.prefill(kd, vd, ctx0, tq0)
+        else:
+            c0.prefill(kd, vd, w.tq)
+
+    pair_us = host_pair_us = None
+    if args.latency_reps > 0:
+        for _ in range(4):
+            prefill0()
+            step(0)
+        torch.cuda.synchronize()
+        t_h = time.perf_counter()
+        prefill0()
+        step(0)
+        torch.cuda.synchronize()
+        host_pair_us = (time.perf_counter() - t_h) * 1e6
+        la, lb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(LAT_SPIN_CYCLES)
+        la.record(cur)
+        for _ in range(args.latency_reps):
+            prefill0()
+            step(0)
+        lb.record(cur)
+        torch.cuda.synchronize()
+        pair_us = la.elapsed_time(lb) * 1e3 / args.latency_reps
+    del kd, vd
+
     # algorithmic bytes of every step, at the lengths the decode reads (after
     # the step's append); ragged: summed over the sequences
     per_seq = 1 if ragged else B
@@ -762,6 +803,16 @@ def main():
         },
         "kernel_source_hash": kernel_source_hash(),
     }
+    # one layer's prefill (quantize the grouped part, copy the residual)
+    # followed by one fused step: the latency of a fresh cache's first decode
+    if pair_us is not None:
+        result["latency_us"] = {
+            "prefill_plus_step": round(pair_us, 2),
+            "host_call_to_sync": round(host_pair_us, 2),
+            "note": (f"device time of a prefill and one {calls} step on layer 0, "
+                     f"{args.latency_reps} pairs back to back behind a spin kernel (host "
+                     f"enqueue hidden); host_call_to_sync: one pair from an idle queue, "
+                     f"host clock")}
     if w.steps:
         # streaming workloads: the layer's whole run of steps (flushes included)
         result["per_layer_run"] = {"steps": w.steps,

@@ -453,8 +453,12 @@ __device__ void value_chunk(const QuantJob& j, uint8_t* smem, size_t ob, int t_b
 // consecutive items of one plane, holding the next item's tile in registers
 // (up to kMaxPf 16-byte units per thread) while it computes the current one
 // from LDS, so the tile loads overlap the computation.  Larger tiles are
-// loaded at the start of their item instead.
+// loaded at the start of their item instead.  A job too small to give
+// kFillBlocks blocks at kItems per block takes fewer items per block (down
+// to one), so a short prefill or flush spreads over the compute units
+// instead of running a few long chains.
 constexpr int kItems = 8;
+constexpr long kFillBlocks = 2048;
 constexpr int kMaxPf = 4;
 struct Prefetch {
   u32x4_t r[kMaxPf];
@@ -484,8 +488,8 @@ __device__ __forceinline__ void stage_direct(uint8_t* smem, const uint16_t* src,
 }
 
 // One launch of the codec (blockIdx.y: plane, or list item * H + head):
-//   blockIdx.x < nkb           : key groups  (do_k), kItems per block
-//   nkb <= blockIdx.x < nkb+nvb: value chunks (do_v), kItems per block
+//   blockIdx.x < nkb           : key groups  (do_k), ipb per block
+//   nkb <= blockIdx.x < nkb+nvb: value chunks (do_v), ipb per block
 //   above                      : residual copy chunk of 256 x 16 bytes
 // Uniform launches quantize source tokens [0, nq) into destination tokens
 // [dst_off, dst_off + nq) and copy source tokens [nq, nq + ncopy) into
@@ -496,7 +500,7 @@ __device__ __forceinline__ void stage_direct(uint8_t* smem, const uint16_t* src,
 // pool is skipped).
 template <int BITS, bool MH, bool LIST, bool PG, bool KO, bool FIX>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(5, 5)))
-quantize_kv_kernel(QuantJob j, ListT<LIST> list, PageMap pm) {
+quantize_kv_kernel(QuantJob j, ListT<LIST> list, PageMap pm, int ipb) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int H = j.H, D = FIX ? kFixD : j.D, G = FIX ? kFixG : j.G;
   size_t bh = blockIdx.y;
@@ -510,8 +514,8 @@ quantize_kv_kernel(QuantJob j, ListT<LIST> list, PageMap pm) {
     ncopy = list.c[item];
   }
   // (j.nq: the largest item's count)
-  const int nkb = j.do_k ? (j.nq / G + kItems - 1) / kItems : 0;
-  const int nvb = j.do_v ? (j.nq / 32 + kItems - 1) / kItems : 0;
+  const int nkb = j.do_k ? (j.nq / G + ipb - 1) / ipb : 0;
+  const int nvb = j.do_v ? (j.nq / 32 + ipb - 1) / ipb : 0;
   int bx = blockIdx.x;
   // items [i0, i1) of `tok` tokens each from source tokens i0*tok, ...: the
   // block loop, `run(i)` computing item i from the staged tile (the branch
@@ -520,7 +524,7 @@ quantize_kv_kernel(QuantJob j, ListT<LIST> list, PageMap pm) {
   // (row units 2^sh: D / 8 is a power of two)
   const int sh = 31 - __builtin_clz(D / 8);
   auto walk = [&](const uint16_t* src, int tok, int pad, int n_items, auto run) {
-    const int i0 = bx * kItems, i1 = min(i0 + kItems, n_items);
+    const int i0 = bx * ipb, i1 = min(i0 + ipb, n_items);
     if (i0 >= i1) return;   // the whole block: uniform
     const int n16 = tok * D / 8;
     const bool pf = n16 <= kMaxPf * kThreads;
@@ -618,10 +622,17 @@ void dispatch(int bits, int mh, bool ko, F f) {
   }
 }
 
-// grid x extent and LDS bytes of a job
-void job_shape(const QuantJob& j, int ncopy_max, int& gx, size_t& lds) {
-  const int nkb = j.do_k ? (j.nq / j.G + kItems - 1) / kItems : 0;
-  const int nvb = j.do_v ? (j.nq / 32 + kItems - 1) / kItems : 0;
+// item blocks of a job at n items per block
+int item_blocks(const QuantJob& j, int n) {
+  return (j.do_k ? (j.nq / j.G + n - 1) / n : 0) + (j.do_v ? (j.nq / 32 + n - 1) / n : 0);
+}
+
+// items per block, grid x extent and LDS bytes of a job (gy planes or items)
+void job_shape(const QuantJob& j, int gy, int ncopy_max, int& ipb, int& gx, size_t& lds) {
+  ipb = kItems;
+  while (ipb > 1 && (long)item_blocks(j, ipb) * gy < kFillBlocks) ipb /= 2;
+  const int nkb = j.do_k ? (j.nq / j.G + ipb - 1) / ipb : 0;
+  const int nvb = j.do_v ? (j.nq / 32 + ipb - 1) / ipb : 0;
   const int ncb = (ncopy_max * (j.D / 8) + kThreads - 1) / kThreads;
   gx = nkb + nvb + ncb;
   lds = 0;
@@ -632,19 +643,19 @@ void job_shape(const QuantJob& j, int ncopy_max, int& gx, size_t& lds) {
 template <bool LIST, bool PG>
 hipError_t launch_job(const QuantJob& j, int bits, int mh, int gy, int ncopy_max,
                       const ListT<LIST>& list, const PageMap& pm, hipStream_t st) {
-  int gx;
+  int ipb, gx;
   size_t lds;
-  job_shape(j, ncopy_max, gx, lds);
+  job_shape(j, gy, ncopy_max, ipb, gx, lds);
   if (gx == 0 || gy == 0) return hipSuccess;
   const dim3 grid(gx, gy);
   const bool fix = j.D == kFixD && j.G == kFixG;
   dispatch(bits, mh, j.n_out > 0, [&](auto B, auto M, auto K) {
     if (fix)
       quantize_kv_kernel<B.value, M.value, LIST, PG, K.value, true>
-          <<<grid, kThreads, lds, st>>>(j, list, pm);
+          <<<grid, kThreads, lds, st>>>(j, list, pm, ipb);
     else
       quantize_kv_kernel<B.value, M.value, LIST, PG, K.value, false>
-          <<<grid, kThreads, lds, st>>>(j, list, pm);
+          <<<grid, kThreads, lds, st>>>(j, list, pm, ipb);
   });
   return hipGetLastError();
 }
