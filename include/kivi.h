@@ -376,10 +376,12 @@ int kivi_ragged_append_decode_attn(kivi_ragged_cache* cache,
 /* ---- Paged quantized store --------------------------------------------
  * A server keeps many sequences of unpredictable length, so the quantized
  * part of each sequence lives in fixed-size pages drawn from shared pools, as
- * in paged attention (mlsanity KIVI page, Key facts and Abstract: KIVI plugs
- * into a serving stack; scholarfeed "KIVI" quote page: the quantized tokens
- * and the fixed-length full-precision residual are kept apart, so they are
- * managed apart here too).  A page holds P = page_tokens consecutive tokens of
+ * in paged attention.  The scholarfeed "KIVI" quote page notes that a paged
+ * pool of uniform-precision blocks does not fit a cache that mixes quantized
+ * tokens with a fixed-length full-precision residual, and names separate
+ * page tables as one way out: here the quantized tokens are paged (one block
+ * table) and the residual keeps a fixed-length pool of its own per sequence,
+ * so each pool holds one precision.  A page holds P = page_tokens consecutive tokens of
  * one sequence for every KV head; page p, head h is a "slice" with exactly the
  * layout of a kivi_cache plane of capacity P:
  *   k_codes : uint32 [num_pages][Hkv][P][D/E]
