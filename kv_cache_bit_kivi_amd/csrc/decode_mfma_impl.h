@@ -302,6 +302,20 @@ constexpr int prefetch_depth() {
   return R >= 8 ? 2 : 1;
 }
 
+// Binary32 metadata: issue the next tile's scales and zeros before the
+// current tile's compute, in a second register set (as binary16 metadata
+// always does), or after it.  Measured on one box, same binary otherwise:
+// before is faster with several heads per KV head (Mistral-shaped r = 4
+// layer 57.8-58.1 against 59.9-61.4 us) and for ragged batches (51.9-52.3
+// against 52.5-52.9 us), after is faster for one head with uniform lengths
+// (batch-8 Llama layer 27.0-27.1 against 27.8-27.9 us) and for the paged
+// store (27.7-28.0 against 28.9 us with 256-token pages).  Outlier and
+// pre-RoPE variants keep the order they were tuned with.
+template <int R, bool MH, bool RAG, bool PG, int KO, bool ROPE>
+constexpr bool early_meta() {
+  return MH || (KO == 0 && !ROPE && !PG && R <= 4 && (R >= 2 || RAG));
+}
+
 // KO: key outliers per (group, channel) (0, 1 or 2; a.n_out == KO).  Each
 // lane loads the outlier words of its key group and channels cq..cq+3 with
 // the tile's metadata.  The correction q_d * (kept value - zero) of every
@@ -1419,11 +1433,10 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       cur = c2;
       nxt = c3;
     }
-  } else if constexpr (MH) {
-    // binary16 metadata (8 registers a set): the next tile's metadata is
-    // issued before the current tile's compute, in a second register set,
-    // instead of after it (measured 26.2 -> 25.0 us on the batch-8 Llama
-    // layer; with binary32 metadata the extra set costs more than it hides)
+  } else if constexpr (early_meta<R, MH, RAG, PG, KO, ROPE>()) {
+    // the next tile's metadata is issued before the current tile's compute,
+    // in a second register set, instead of after it (binary16 metadata: 26.2
+    // -> 25.0 us on the batch-8 Llama layer; binary32: see early_meta)
     issue(pa);
     for (int cur = t_first, nxt = t_given; cur < t_lim;) {
       __builtin_amdgcn_sched_barrier(0);
