@@ -16,4 +16,5 @@ from .oracle import (  # noqa: F401
     outlier_shape,
     quantize_k,
     quantize_v,
+    quantize_v_token,
 )

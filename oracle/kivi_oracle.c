@@ -65,6 +65,18 @@
  *     Queries arrive with the embedding already applied at their own
  *     position, as the model computes them.
  *
+ *   - value sliding window (optional residual policy, v_window = 1)
+ *     [KIVI-quo: a fixed-length buffer of recent full-precision tokens;
+ *     KIVI-abs: values are quantized per token, so a single value token can
+ *     be quantized on its own, while a key group needs G tokens]: the
+ *     full-precision values are the R newest tokens.  When a token arrives
+ *     and the cache holds L >= R tokens, the value of token L - R leaves the
+ *     window and is quantized by itself (its per-token groups, as any
+ *     value); keys keep the lazy flush of the whole key residual.  After any
+ *     append, values [0, max(0, L - R)) are quantized and the rest are full
+ *     precision; keys [0, tq) are quantized, tq >= L - R.  The window keeps
+ *     value token t in slot t mod R of the value residual buffer.
+ *
  * Packed layout (the library's documented storage contract, re-implemented
  * here independently from its description).  Codes are stored in "rows" of
  * n positions: a key row is one token's n = D channels, a value row is one
@@ -200,6 +212,19 @@ static void row_clear(uint32_t* row, int n, int bits, int p) {
     row[n / 16 + p / 32] = 0;
   } else {
     row[p / (32 / bits)] = 0;
+  }
+}
+
+/* clear the bits of position p of the row (the other positions keep theirs) */
+static void row_unset(uint32_t* row, int n, int bits, int p) {
+  if (bits == 3) {
+    row[p / 16] &= ~(3u << (2 * (p % 16)));
+    row[n / 16 + p / 32] &= ~(1u << beta(p % 32));
+  } else if (bits == 1) {
+    row[p / 32] &= ~(1u << beta(p % 32));
+  } else {
+    const int E = 32 / bits;
+    row[p / E] &= ~(((1u << bits) - 1u) << (bits * (p % E)));
   }
 }
 
@@ -389,6 +414,44 @@ int kivio_quantize_v(int B, int H, int D, int bits, int G, int cap, int meta_hal
   return KIVIO_OK;
 }
 
+/* Value quantization of one token per (b, h) [KIVI-abs: per token]: source
+ * row `slot` of v ([B][H][in_stride][D]) becomes cache token t; the same
+ * per-token groups as kivio_quantize_v, at any token position (the bits of
+ * position t % 64 in the shared value rows are replaced, the other tokens'
+ * bits are kept). */
+int kivio_quantize_v_token(int B, int H, int D, int bits, int G, int cap, int meta_half,
+                           const uint16_t* v, int in_stride, int slot, int t,
+                           uint32_t* codes, void* scale, void* zero) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (slot < 0 || slot >= in_stride || t < 0) return KIVIO_ESHAPE;
+  if (t >= cap) return KIVIO_ECAPACITY;
+  const int NG = D / G;
+  const size_t plane_words = (size_t)cap * D * bits / 32;
+  float xs[1024];
+  uint8_t cs[1024];
+  if (G > 1024) return KIVIO_ESHAPE;
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < H; h++) {
+      const uint16_t* src = v + (((size_t)b * H + h) * (size_t)in_stride + slot) * D;
+      uint32_t* cw = codes + ((size_t)b * H + h) * plane_words;
+      const size_t mbase = ((size_t)b * H + h) * (size_t)cap * NG;
+      for (int j = 0; j < NG; j++) {
+        for (int i = 0; i < G; i++) xs[i] = kivio_half_to_float(src[j * G + i]);
+        float s, z;
+        quantize_group(xs, G, bits, NULL, cs, &s, &z);
+        meta_put(scale, mbase + (size_t)t * NG + j, s, meta_half);
+        meta_put(zero, mbase + (size_t)t * NG + j, z, meta_half);
+        for (int i = 0; i < G; i++) {
+          uint32_t* row = cw + v_row(D, bits, t, j * G + i);
+          row_unset(row, 64, bits, t % 64);
+          row_put(row, 64, bits, t % 64, cs[i]);
+        }
+      }
+    }
+  return KIVIO_OK;
+}
+
 /* Streaming append of one decode token per (b, h) [KIVI-sum: the residual
  * part is kept in full precision and new tokens are appended; KIVI-quo: a
  * fixed-length residual of recent tokens].  Reading: when a token arrives
@@ -424,6 +487,50 @@ int kivio_append(int B, int H, int D, int bits, int G, int R, int cap, int meta_
         size_t dst = (((size_t)b * H + h) * R + r) * D + d;
         k_res[dst] = k_new[src];
         v_res[dst] = v_new[src];
+      }
+  *tq = q;
+  *tr = r + 1;
+  return KIVIO_OK;
+}
+
+/* kivio_append under the value sliding window (the v_window reading in the
+ * file header): the keys take exactly kivio_append's steps; v_res is the
+ * window (value token t in slot t mod R).  With L = tq + tr tokens cached,
+ * L >= R sends value token L - R (slot (L - R) mod R = L mod R) to the
+ * value store first; the new value then takes slot L mod R.  *tq, *tr are
+ * updated only on success, and nothing is written on an error. */
+int kivio_append_vw(int B, int H, int D, int bits, int G, int R, int cap, int meta_half,
+                    uint32_t* k_codes, void* ks, void* kz, uint32_t* v_codes,
+                    void* vs, void* vz, uint16_t* k_res, uint16_t* v_res,
+                    const uint16_t* k_new, const uint16_t* v_new, int* tq,
+                    int* tr, int n_out, uint32_t* k_outl) {
+  int rc = check_common(B, H, D, bits, G, cap);
+  if (rc) return rc;
+  if (R < G || R % G) return KIVIO_ESHAPE;
+  if (n_out < 0 || n_out >= G || (n_out > 0 && !k_outl)) return KIVIO_EINVAL;
+  int q = *tq, r = *tr;
+  if (q < 0 || q % G || r < 0 || r > R) return KIVIO_ESHAPE;
+  const int L = q + r;
+  if (r == R && q + R > cap) return KIVIO_ECAPACITY;
+  if (L >= R && L - R >= cap) return KIVIO_ECAPACITY;
+  if (r == R) {
+    rc = kivio_quantize_k(B, H, D, bits, G, cap, meta_half, k_res, R, R, q, k_codes, ks, kz,
+                          n_out, k_outl);
+    if (rc) return rc;
+    q += R;
+    r = 0;
+  }
+  if (L >= R) {
+    rc = kivio_quantize_v_token(B, H, D, bits, G, cap, meta_half, v_res, R, L % R, L - R,
+                                v_codes, vs, vz);
+    if (rc) return rc;
+  }
+  for (int b = 0; b < B; b++)
+    for (int h = 0; h < H; h++)
+      for (int d = 0; d < D; d++) {
+        size_t src = ((size_t)b * H + h) * D + d;
+        k_res[(((size_t)b * H + h) * R + r) * D + d] = k_new[src];
+        v_res[(((size_t)b * H + h) * R + L % R) * D + d] = v_new[src];
       }
   *tq = q;
   *tr = r + 1;
@@ -473,6 +580,15 @@ static void rope_key(double* kv, int D, int t, double theta) {
  * with isolated outliers (n_out > 0) dequantize through k_outl; with
  * rope_theta > 0 the cached keys are pre-RoPE and each is rotated at its
  * position before the dot product [KVQ-abs]. */
+int kivio_decode_attn_vw(int B, int H, int r, int D, int bits, int G, int R,
+                         int cap, int meta_half, const uint32_t* k_codes, const void* ks,
+                         const void* kz, const uint32_t* v_codes,
+                         const void* vs, const void* vz, const uint16_t* k_res,
+                         const uint16_t* v_res, int tq, int tr, const uint16_t* q,
+                         float softmax_scale, double* out, double* scratch,
+                         int n_out, const uint32_t* k_outl, double rope_theta,
+                         int v_window);
+
 int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
                       int cap, int meta_half, const uint32_t* k_codes, const void* ks,
                       const void* kz, const uint32_t* v_codes,
@@ -480,6 +596,22 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
                       const uint16_t* v_res, int tq, int tr, const uint16_t* q,
                       float softmax_scale, double* out, double* scratch,
                       int n_out, const uint32_t* k_outl, double rope_theta) {
+  return kivio_decode_attn_vw(B, H, r, D, bits, G, R, cap, meta_half, k_codes, ks, kz,
+                              v_codes, vs, vz, k_res, v_res, tq, tr, q, softmax_scale, out,
+                              scratch, n_out, k_outl, rope_theta, 0);
+}
+
+/* The same attention with the value residual read as the sliding window when
+ * v_window = 1: values [0, max(0, L - R)) dequantized, value token t >= that
+ * from slot t mod R of v_res. */
+int kivio_decode_attn_vw(int B, int H, int r, int D, int bits, int G, int R,
+                         int cap, int meta_half, const uint32_t* k_codes, const void* ks,
+                         const void* kz, const uint32_t* v_codes,
+                         const void* vs, const void* vz, const uint16_t* k_res,
+                         const uint16_t* v_res, int tq, int tr, const uint16_t* q,
+                         float softmax_scale, double* out, double* scratch,
+                         int n_out, const uint32_t* k_outl, double rope_theta,
+                         int v_window) {
   int rc = check_common(B, H, D, bits, G, cap);
   if (rc) return rc;
   if (r < 1) return KIVIO_EINVAL;
@@ -487,8 +619,10 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
   if (!(rope_theta >= 0.0) || isinf(rope_theta) || D % 2 != 0 || D > 1024) return KIVIO_EINVAL;
   if (tq < 0 || tq % G || tq > cap || tr < 0 || tr > R || tq + tr < 1)
     return KIVIO_ESHAPE;
+  if (v_window != 0 && v_window != 1) return KIVIO_EINVAL;
   const int Hq = H * r, W = words_per_row(D, bits);
   const int L = tq + tr;
+  const int tv = v_window ? (L > R ? L - R : 0) : tq;   /* quantized value tokens */
   double* logit = scratch;
   double* p = scratch + L;
   for (int b = 0; b < B; b++)
@@ -525,8 +659,9 @@ int kivio_decode_attn(int B, int H, int r, int D, int bits, int G, int R,
       for (int d = 0; d < D; d++) {
         double acc = 0.0;
         for (int t = 0; t < L; t++) {
-          double vv = (t < tq) ? dequant_v(vc, vs, vz, vmb, meta_half, D, bits, G, t, d)
-                               : (double)kivio_half_to_float(vr[(size_t)(t - tq) * D + d]);
+          const size_t slot = v_window ? (size_t)(t % R) : (size_t)(t - tq);
+          double vv = (t < tv) ? dequant_v(vc, vs, vz, vmb, meta_half, D, bits, G, t, d)
+                               : (double)kivio_half_to_float(vr[slot * D + d]);
           acc += p[t] * vv;
         }
         o[d] = acc / l;

@@ -65,11 +65,18 @@ def load():
                                              _u16p, _u16p, _u16p, _u16p, _i32p, _i32p,
                                              _int, _u32p]
     lib.kivio_append.restype = _int
+    lib.kivio_append_vw.argtypes = lib.kivio_append.argtypes
+    lib.kivio_append_vw.restype = _int
+    lib.kivio_quantize_v_token.argtypes = [_int] * 7 + [_u16p, _int, _int, _int, _u32p, _vp,
+                                                        _vp]
+    lib.kivio_quantize_v_token.restype = _int
     lib.kivio_decode_attn.argtypes = [_int] * 9 + [_u32p, _vp, _vp, _u32p, _vp,
                                                    _vp, _u16p, _u16p, _int, _int, _u16p,
                                                    ctypes.c_float, _f64p, _f64p, _int, _u32p,
                                                    ctypes.c_double]
     lib.kivio_decode_attn.restype = _int
+    lib.kivio_decode_attn_vw.argtypes = lib.kivio_decode_attn.argtypes + [_int]
+    lib.kivio_decode_attn_vw.restype = _int
     _lib = lib
     return lib
 
@@ -173,6 +180,16 @@ def quantize_v(v, bits, G, cap, ntok=None, dst_off=0, codes=None, scale=None, ze
     return codes, scale, zero
 
 
+def quantize_v_token(v, slot, t, bits, G, cap, codes, scale, zero, meta_half=False):
+    """Quantize source row ``slot`` of v[B][H][S][D] (binary16) as cache token
+    t of the value store (codes, scale, zero updated in place)."""
+    v = _h(v)
+    B, H, S, D = v.shape
+    _check(load().kivio_quantize_v_token(
+        B, H, D, bits, G, cap, int(meta_half), _p(v, ctypes.c_uint16, np.uint16), S, slot, t,
+        _p(codes, ctypes.c_uint32, np.uint32), _m(scale, meta_half), _m(zero, meta_half)))
+
+
 @dataclass
 class OracleCache:
     """Host-side mixed-precision cache driven by the C oracle."""
@@ -187,6 +204,7 @@ class OracleCache:
     meta_half: bool = False
     n_out: int = 0          # key outliers per key group (0: none)
     rope_theta: float = 0.0  # > 0: keys are pre-RoPE, rotated at decode (base rope_theta)
+    v_window: bool = False   # values: a sliding window of the R newest tokens (v_res slot t % R)
     tq: int = 0
     tr: int = 0
     k_codes: np.ndarray = field(default=None, repr=False)
@@ -223,10 +241,21 @@ class OracleCache:
         if tq:
             quantize_k(k, self.bits, self.G, self.cap, tq, 0, self.k_codes, self.ks, self.kz,
                        self.meta_half, self.n_out, self.k_outl)
-            quantize_v(v, self.bits, self.G, self.cap, tq, 0, self.v_codes, self.vs, self.vz,
-                       self.meta_half)
         self.k_res[:, :, : T - tq] = k[:, :, tq:]
-        self.v_res[:, :, : T - tq] = v[:, :, tq:]
+        if self.v_window:
+            # values [0, T - R) quantized one token at a time, the rest in the
+            # window at slot t % R
+            tv = max(0, T - self.R)
+            for t in range(tv):
+                quantize_v_token(v, t, t, self.bits, self.G, self.cap, self.v_codes, self.vs,
+                                 self.vz, self.meta_half)
+            for t in range(tv, T):
+                self.v_res[:, :, t % self.R] = v[:, :, t]
+        else:
+            if tq:
+                quantize_v(v, self.bits, self.G, self.cap, tq, 0, self.v_codes, self.vs,
+                           self.vz, self.meta_half)
+            self.v_res[:, :, : T - tq] = v[:, :, tq:]
         self.tq, self.tr = tq, T - tq
 
     def append(self, k_new, v_new):
@@ -235,7 +264,8 @@ class OracleCache:
         tr = ctypes.c_int(self.tr)
         before = self.tq
         mh = self.meta_half
-        _check(load().kivio_append(
+        fn = load().kivio_append_vw if self.v_window else load().kivio_append
+        _check(fn(
             self.B, self.H, self.D, self.bits, self.G, self.R, self.cap, int(mh),
             _p(self.k_codes, ctypes.c_uint32, np.uint32), _m(self.ks, mh), _m(self.kz, mh),
             _p(self.v_codes, ctypes.c_uint32, np.uint32), _m(self.vs, mh), _m(self.vz, mh),
@@ -245,6 +275,11 @@ class OracleCache:
         self.tq, self.tr = tq.value, tr.value
         if self.tq != before:
             self.flushes += 1
+
+    @property
+    def tv(self) -> int:
+        """Quantized value tokens (tq without the value window)."""
+        return max(0, self.tq + self.tr - self.R) if self.v_window else self.tq
 
     def decode(self, q, softmax_scale):
         return decode_attn(self, q, softmax_scale)
@@ -257,12 +292,12 @@ def decode_attn(c: OracleCache, q, softmax_scale):
     out = np.zeros((c.B, c.H * c.r, c.D), np.float64)
     scratch = np.zeros(2 * max(1, c.tq + c.tr), np.float64)
     mh = c.meta_half
-    _check(load().kivio_decode_attn(
+    _check(load().kivio_decode_attn_vw(
         c.B, c.H, c.r, c.D, c.bits, c.G, c.R, c.cap, int(mh),
         _p(c.k_codes, ctypes.c_uint32, np.uint32), _m(c.ks, mh), _m(c.kz, mh),
         _p(c.v_codes, ctypes.c_uint32, np.uint32), _m(c.vs, mh), _m(c.vz, mh),
         _p(c.k_res, ctypes.c_uint16, np.uint16), _p(c.v_res, ctypes.c_uint16, np.uint16),
         c.tq, c.tr, _p(q, ctypes.c_uint16, np.uint16), float(softmax_scale),
         _p(out, ctypes.c_double, np.float64), _p(scratch, ctypes.c_double, np.float64),
-        int(c.n_out), _outl(c.k_outl), float(c.rope_theta)))
+        int(c.n_out), _outl(c.k_outl), float(c.rope_theta), int(c.v_window)))
     return out
