@@ -51,37 +51,52 @@ PF_SPIN_CYCLES = 20_000_000
 MAX_CPU_WORKERS = 16
 
 
-def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4, n_out=0):
+def decode_bytes(B, H, r, D, bits, G, tq, tr, mb=4, n_out=0, v_window=False, R=0):
     """Algorithmic bytes of one decode call: packed K/V codes, scale and zero
     of both (mb bytes each: 4 for binary32, 2 for binary16), the key-outlier
     words (n_out 4-byte words per key group and channel), fp16 residual K/V,
-    fp16 q and out."""
-    per = (2 * tq * D * bits // 8 + (tq // G) * D * 2 * mb + tq * (D // G) * 2 * mb
-           + (tq // G) * n_out * D * 4 + 4 * tr * D + 4 * r * D)
+    fp16 q and out.  With the value window the values are quantized up to
+    max(0, tq + tr - R) and the rest are read from the fp16 window."""
+    import numpy as np
+    tv = np.maximum(tq + tr - R, 0) if v_window else tq
+    per = (tq * D * bits // 8 + tv * D * bits // 8 + (tq // G) * D * 2 * mb
+           + tv * (D // G) * 2 * mb + (tq // G) * n_out * D * 4 + 2 * tr * D
+           + 2 * (tq + tr - tv) * D + 4 * r * D)
     return B * H * per
 
 
-def append_bytes(B, H, D, bits, G, R, flush, mb=4, n_out=0):
+def append_bytes(B, H, D, bits, G, R, flush, mb=4, n_out=0, v_window=False, v_leave=False):
     """Algorithmic bytes of one append: read the new K/V token, write it to
     the residual; a flush reads R residual tokens of K and V and writes their
-    codes, scales, zeros and key-outlier words."""
+    codes, scales, zeros and key-outlier words.  With the value window a
+    flush covers the keys only, and a value leaving the window (v_leave) is
+    read from it and written as codes, scales and zeros."""
     b = B * H * D * 2 * 2 * 2
-    if flush:
+    if flush and not v_window:
         b += B * H * (2 * R * D * 2 + 2 * R * D * bits // 8 + (R // G) * D * 2 * mb
                       + R * (D // G) * 2 * mb + (R // G) * n_out * D * 4)
+    if flush and v_window:
+        b += B * H * (R * D * 2 + R * D * bits // 8 + (R // G) * D * 2 * mb
+                      + (R // G) * n_out * D * 4)
+    if v_window and v_leave:
+        b += B * H * (D * 2 + D * bits // 8 + (D // G) * 2 * mb)
     return b
 
 
-def prefill_bytes(H, D, bits, G, tq, tr, mb=4, n_out=0):
+def prefill_bytes(H, D, bits, G, tq, tr, mb=4, n_out=0, v_window=False, R=0):
     """Algorithmic bytes of a prefill, summed over sequences (tq, tr: arrays
     or ints per sequence): read tq fp16 tokens of K and V and write their
     codes, scales, zeros and outlier words; copy tr fp16 tokens of K and V
-    into the residual (read and write)."""
+    into the residual (read and write).  With the value window the values
+    are quantized up to max(0, tq + tr - R) and the rest copied."""
     import numpy as np
     tq = np.asarray(tq, np.int64)
     tr = np.asarray(tr, np.int64)
-    per = (2 * tq * D * 2 + 2 * tq * D * bits // 8 + (tq // G) * D * 2 * mb
-           + tq * (D // G) * 2 * mb + (tq // G) * n_out * D * 4 + 2 * tr * D * 2 * 2)
+    tv = np.maximum(tq + tr - R, 0) if v_window else tq
+    per = (tq * D * 2 + tq * D * bits // 8 + (tq // G) * D * 2 * mb
+           + (tq // G) * n_out * D * 4 + tr * D * 2 * 2
+           + tv * D * 2 + tv * D * bits // 8 + tv * (D // G) * 2 * mb
+           + (tq + tr - tv) * D * 2 * 2)
     return int(H * np.sum(per))
 
 
@@ -273,14 +288,16 @@ def _cpu_units(w, units, steps, kw):
         ins = [(np.ascontiguousarray(kn[b:b + 1, h:h + 1]), np.ascontiguousarray(vn[b:b + 1, h:h + 1]),
                 np.ascontiguousarray(q[b:b + 1, h * r:(h + 1) * r])) for b, h in units]
         t1 = time.perf_counter()
+        vw = bool(kw.get("v_window"))
         for oc, (kk, vv, qq) in zip(caches, ins):
             flush = oc.tr == w.residual
+            leave = oc.tq + oc.tr >= w.residual
             oc.append(kk, vv)
             oc.decode(qq, w.softmax_scale)
             nbytes += append_bytes(1, 1, w.head_dim, w.bits, w.group, w.residual, flush, mb,
-                                   n_out)
-            nbytes += decode_bytes(1, 1, r, w.head_dim, w.bits, w.group, oc.tq, oc.tr, mb,
-                                   n_out)
+                                   n_out, vw, leave)
+            nbytes += int(decode_bytes(1, 1, r, w.head_dim, w.bits, w.group, oc.tq, oc.tr, mb,
+                                       n_out, vw, w.residual))
         t_busy += time.perf_counter() - t1
     return t0, time.perf_counter(), t_busy, nbytes
 
@@ -292,7 +309,7 @@ def _cpu_worker(args):
 
 
 def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0,
-                 rope_theta=0.0, workers=None, pool=None):
+                 rope_theta=0.0, workers=None, pool=None, v_window=False):
     """The C oracle (single-threaded code) on a bounded sample of the same
     workload: whole decode steps over every (batch, KV-head) unit.
 
@@ -303,6 +320,8 @@ def cpu_baseline(w, min_seconds=10.0, max_seconds=30.0, meta_half=False, n_out=0
     rate is the bytes of all units over the wall time from the first start to
     the last finish."""
     kw = dict(meta_half=meta_half, n_out=n_out, rope_theta=rope_theta)
+    if v_window:
+        kw["v_window"] = True
     units = [(b, h) for b in range(w.batch) for h in range(w.kv_heads)]
     # one core: grow the step count until the sample is long enough
     steps, spent = 1, 0.0
@@ -391,6 +410,9 @@ def main():
     ap.add_argument("--paged", type=int, default=0, metavar="P",
                     help="paged quantized store with P-token pages (0: contiguous planes); the "
                          "block table is a seeded shuffle of the page pool")
+    ap.add_argument("--v-window", action="store_true",
+                    help="values keep a sliding window of the R newest tokens (uniform caches; "
+                         "generic decode kernel)")
     ap.add_argument("--deterministic", action="store_true",
                     help="deterministic caches: every decode wave keeps a fixed run of tiles "
                          "(repeatable bits) instead of sharing the block's tiles")
@@ -420,7 +442,7 @@ def main():
     tag = (args.workload + (f"_b{args.bits}" if args.bits else "") +
            (f"_out{n_out}" if n_out else "") + ("_rope" if rope > 0 else "") +
            (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else "") +
-           ("_det" if args.deterministic else ""))
+           ("_det" if args.deterministic else "") + ("_vwin" if args.v_window else ""))
     if args.pmc_summary:
         fcsv, wcsv, mib, cmd = args.pmc_summary
         pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
@@ -482,6 +504,10 @@ def main():
 
     paged = args.paged > 0
     ragged = w.ragged or paged      # (the paged calls carry per-sequence lengths)
+    if args.v_window and ragged:
+        print("--v-window needs a uniform workload (ragged and paged caches refuse it)",
+              file=sys.stderr)
+        sys.exit(2)
     ctx0 = w.contexts().astype(np.int32)          # per-sequence lengths at the prefill
     tq0 = w.tqs().astype(np.int32)
     k, v = synth.kv(w)
@@ -514,7 +540,8 @@ def main():
             c.prefill(kd, vd, ctx0, tq0)
         else:
             c = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half, outliers=n_out,
-                          rope_theta=rope, deterministic=args.deterministic)
+                          rope_theta=rope, deterministic=args.deterministic,
+                          v_window=args.v_window)
             e0.record(cur)
             c.prefill(kd, vd, w.tq)
         e1.record(cur)
@@ -684,17 +711,23 @@ def main():
     # algorithmic bytes of every step, at the lengths the decode reads (after
     # the step's append); ragged: summed over the sequences
     per_seq = 1 if ragged else B
-    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, tq, tr, mb, n_out)))
+    vw = args.v_window
+    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, tq, tr, mb, n_out, vw, R)))
                  for _, _, tq, tr in info]
-    app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb, n_out)
+    # (a value leaves the window when the cache held R tokens before the append)
+    app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb, n_out, vw,
+                                          bool(np.all(tq + tr - 1 >= R)))
                              for f in fl]))
-                 for _, fl, _, _ in info]
+                 for _, fl, tq, tr in info]
     total_bytes = sum(dec_bytes) + sum(app_bytes)
     n_flush = int(sum(int(np.sum(fl)) for _, fl, _, _ in info))
     # The dominant kernel is the decode launch, carrying the new token's
-    # append when fused (separate mode: the append launch too).
+    # append when fused (separate mode: the append launch too).  With the
+    # value window a step is the window append's launches and the generic
+    # decode: the windows time whole steps.
     new_tok = append_bytes(B, H, D, bits, G, R, False, mb, n_out)
-    per_call = [d + new_tok for d in dec_bytes]
+    per_call = ([d + a for d, a in zip(dec_bytes, app_bytes)] if vw
+                else [d + new_tok for d in dec_bytes])
     win_ms = [ev[k][0].elapsed_time(ev[k][1]) for k in range(len(windows))]
     plain = [k for k, (fl, _) in enumerate(windows) if not fl]
     flushing = [k for k, (fl, _) in enumerate(windows) if fl]
@@ -717,7 +750,7 @@ def main():
     else:
         calls = "kivi_append + kivi_decode_attn" if args.separate else "kivi_append_decode_attn"
     pf_bytes = prefill_bytes(H, D, bits, G, tq0.astype(np.int64),
-                             (ctx0 - tq0).astype(np.int64), mb, n_out)
+                             (ctx0 - tq0).astype(np.int64), mb, n_out, vw, R)
     pf_med = float(np.median(pf_us[1:] if len(pf_us) > 1 else pf_us))
 
     result = {
@@ -750,6 +783,7 @@ def main():
             "scale_zero": "fp16" if meta_half else "fp32",
             "key_outliers_per_group": n_out,
             "pre_rope_keys_theta": rope,
+            "value_window": bool(vw),
             "decode_tiles": ("fixed per-wave runs (deterministic)" if args.deterministic
                              else "shared by a block's waves in load-return order"),
             "key_spikes": w.key_spikes,
@@ -764,6 +798,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": (f"{calls} (append and decode launches)" if args.separate
+                       else f"{calls} with the value window: the window append's launches "
+                       "and the generic decode kernel, timed as whole steps" if vw
                        else f"kivi decode attention with the append folded in ({calls}: one "
                        "decode launch per step)") +
                       f"; HIP events around runs of up to {W} consecutive steps (the first "
@@ -821,7 +857,8 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, meta_half=meta_half,
                                               n_out=n_out, rope_theta=rope,
-                                              workers=n_workers, pool=pool)
+                                              workers=n_workers, pool=pool,
+                                              v_window=args.v_window)
     if pool is not None:
         pool.close()
         pool.join()

@@ -123,7 +123,22 @@ enum kivi_status {
  *     differently from call to call and the output can differ in its last
  *     bits; 1 = every wave keeps a fixed run of tiles and repeated calls
  *     give identical bits (slower when some waves' loads return late).
- *     The generic kernel always uses fixed runs. */
+ *     The generic kernel always uses fixed runs;
+ *   v_window in {0, 1} (KIVI_EINVAL): the residual policy for values.  0 (the
+ *     zero-initialised value) = values follow the keys: a token arriving at
+ *     a full residual flushes all residual tokens, keys and values.  1 = a
+ *     sliding window of values (scholarfeed "KIVI" quote page: a fixed-length
+ *     buffer of recent full-precision tokens; "KIVI...", Abstract: values are
+ *     quantized per token, so one value token can be quantized on its own):
+ *     the R newest values stay fp16, value token t in slot t mod R of v_res,
+ *     and a value leaving the window is quantized by itself; keys keep the
+ *     lazy flush.  With L = tq + tr cached tokens, values [0, max(0, L - R))
+ *     are quantized.  Uniform caches only (KIVI_EUNSUPPORTED for ragged and
+ *     paged caches).  Decode: the whole 64-token tiles below L - R (keys
+ *     and values quantized) on the matrix-core kernel where it takes the
+ *     shape, in num_splits splits, and the other tokens on the generic
+ *     kernel as one more split-K partial; shapes the matrix-core kernel does
+ *     not take run on the generic kernel alone. */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
@@ -137,11 +152,14 @@ typedef struct {
   int32_t outliers;
   float rope_theta;
   int32_t deterministic;
+  int32_t v_window;
 } kivi_shape;
 
 /* One mixed-precision cache: device buffers (layouts above) plus the host-side
  * lengths: tq quantized tokens (a multiple of group, <= capacity) and tr
- * residual tokens (0 <= tr <= residual), equal for every sequence. */
+ * residual tokens (0 <= tr <= residual), equal for every sequence.  With
+ * shape.v_window = 1, tq and tr count keys; the values are quantized up to
+ * max(0, tq + tr - residual) and v_res holds the rest as the window. */
 typedef struct {
   kivi_shape shape;
   uint32_t* k_codes;
@@ -230,7 +248,9 @@ int kivi_decode_auto_splits(const kivi_cache* cache);
 /* Workspace bytes kivi_decode_attn needs for `num_splits` splits of the
  * context; num_splits == 0 returns a bound valid for the automatic split
  * count at every context length of this shape; 0 for an invalid shape or a
- * num_splits outside 0..KIVI_MAX_SPLITS.  Host arithmetic only. */
+ * num_splits outside 0..KIVI_MAX_SPLITS.  With shape->v_window the bound
+ * covers one more partial (the window's tail, below).  Host arithmetic
+ * only. */
 size_t kivi_decode_workspace_bytes(const kivi_shape* shape,
                                    int32_t num_splits);
 

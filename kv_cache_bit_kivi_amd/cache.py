@@ -24,10 +24,11 @@ def _stream() -> int:
 
 
 def make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-               meta_half=False, outliers=0, rope_theta=0.0, deterministic=False) -> kivi_shape:
+               meta_half=False, outliers=0, rope_theta=0.0, deterministic=False,
+               v_window=False) -> kivi_shape:
     return kivi_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
                       int(bool(meta_half)), int(outliers), float(rope_theta),
-                      int(bool(deterministic)))
+                      int(bool(deterministic)), int(bool(v_window)))
 
 
 def _outlier_store(shape: kivi_shape, lead: int, tokens: int, page_tokens: int, num_pages: int,
@@ -51,15 +52,18 @@ class KiviCache:
     store (that many kept keys per key group and channel); with
     ``rope_theta`` > 0 the keys are pre-RoPE and decode rotates them; with
     ``deterministic`` repeated decodes give identical bits (by default the
-    waves of a block share its tiles in load-return order).
+    waves of a block share its tiles in load-return order); with
+    ``v_window`` the values keep a sliding window of the ``residual`` newest
+    tokens in full precision (v_res slot t % residual) and are quantized one
+    token at a time as they leave it.
 
     Layouts are those of include/kivi.h; the host keeps (tq, tr)."""
 
     def __init__(self, batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
                  device="cuda", meta_half=False, outliers=0, rope_theta=0.0,
-                 deterministic=False):
+                 deterministic=False, v_window=False):
         self.shape = make_shape(batch, kv_heads, gqa, head_dim, bits, group, residual, capacity,
-                                meta_half, outliers, rope_theta, deterministic)
+                                meta_half, outliers, rope_theta, deterministic, v_window)
         self.meta_half = bool(meta_half)
         self.outliers = int(outliers)
         mdt = torch.float16 if meta_half else torch.float32

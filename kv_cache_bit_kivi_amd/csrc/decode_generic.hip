@@ -11,7 +11,10 @@
 // row takes the kept fp16 value instead of the dense one.  With pre-RoPE keys
 // (a.rope_theta > 0; same page: keys quantized before the rotary embedding)
 // every key is rotated at its token index t before the dot product: pairs
-// (i, i + D/2), angle t * rope_theta^(-2i/D) taken in binary64.
+// (i, i + D/2), angle t * rope_theta^(-2i/D) taken in binary64.  With the
+// value window (a.vwin; scholarfeed "KIVI" quote page: a fixed-length buffer
+// of recent full-precision tokens) the values of the R newest tokens come
+// from v_res slot t % R and the older ones are dequantized.
 //
 // One block of 256 threads per (split, b*Hkv + h).  The block owns a
 // contiguous token chunk and all r query heads of its KV head:
@@ -95,8 +98,10 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
   const int b = u / a.H, h = u % a.H;
   const int tq = seq_tq<RAG>(a, lens, b), tr = seq_tr<RAG>(a, lens, b);
   const int L = tq + tr;
+  // quantized values: tq, or with the value window all but the R newest
+  const int tv = a.vwin ? (L > a.R ? L - a.R : 0) : tq;
   if constexpr (RAG) chunk = (L + a.S - 1) / a.S;   // per sequence
-  const int t0 = split * chunk;
+  const int t0 = a.t_begin + split * chunk;
   const int t1 = min(L, t0 + chunk);
   const int W = D * bits / 32, WPC = 2 * bits, NG = D / G;   // words per key / value row
 
@@ -223,7 +228,7 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
         float vh = 0.f;
         size_t pl;
         int lt;
-        if (t < tq) {
+        if (t < tv) {
           if (slot(t, pl, lt)) {
             const uint32_t* row =
                 a.v_codes + pl * scap * D * bits / 32 + ((size_t)(lt / 64) * D + d) * WPC;
@@ -232,7 +237,7 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
                  meta_at(a.v_zero, mi, mh);
           }
         } else {
-          vh = h2f(vr[(size_t)(t - tq) * D + d]);
+          vh = h2f(vr[(size_t)(a.vwin ? t % a.R : t - tq) * D + d]);
         }
 #pragma unroll
         for (int i = 0; i < RR; i++)
@@ -252,15 +257,16 @@ decode_generic_kernel(DecodeArgs a, int chunk, LensT<RAG> lens) {
     float acc = 0.f;
     for (int s = 0; s < nsub; s++) acc += so[(s * RR + i) * D + dd];
     const size_t row = qrow0 + i;
-    if (a.S == 1) {
+    if (a.ws_stride == 1) {
       a.out[row * D + dd] = f2h(acc / stat[RR + i]);
     } else {
-      const size_t rows = (size_t)a.B * a.H * r;
+      const size_t rows = (size_t)a.B * a.H * r, WS = a.ws_stride;
+      const size_t slot = (size_t)a.ws_slot0 + split;
       if (dd == 0) {
-        a.ws[row * a.S + split] = empty ? -INFINITY : stat[i];
-        a.ws[rows * a.S + row * a.S + split] = empty ? 0.f : stat[RR + i];
+        a.ws[row * WS + slot] = empty ? -INFINITY : stat[i];
+        a.ws[rows * WS + row * WS + slot] = empty ? 0.f : stat[RR + i];
       }
-      a.ws[2 * rows * a.S + (row * a.S + split) * D + dd] = empty ? 0.f : acc;
+      a.ws[2 * rows * WS + (row * WS + slot) * D + dd] = empty ? 0.f : acc;
     }
   }
 }
@@ -295,7 +301,7 @@ size_t decode_generic_lds_bytes(int r, int D) {
 
 template <bool RAG, bool PG>
 static hipError_t launch_generic(const DecodeArgs& a, const LensT<RAG>& lens, hipStream_t st) {
-  const int L = a.tq + a.tr;
+  const int L = a.tq + a.tr - a.t_begin;   // tokens of the launch's range
   const int chunk = (L + a.S - 1) / a.S;   // (per sequence in the kernel when ragged)
   dim3 grid(a.S, a.B * a.H);
   const size_t lds = decode_generic_lds_bytes(a.r, a.D);
@@ -326,7 +332,7 @@ hipError_t launch_decode_generic_paged(const DecodeArgs& a, const SeqLens& lens,
 
 hipError_t launch_combine(const DecodeArgs& a, hipStream_t st) {
   const int rows = a.B * a.H * a.r;
-  combine_kernel<<<rows, 128, 0, st>>>(a.ws, a.out, rows, a.S, a.D);
+  combine_kernel<<<rows, 128, 0, st>>>(a.ws, a.out, rows, a.ws_stride, a.D);
   return hipGetLastError();
 }
 

@@ -1553,15 +1553,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       }
     }
     const size_t row = qrow0 + h;
-    if (S == 1) {
+    if (a.ws_stride == 1) {
       a.out[row * kD + d] = f2h(O / L);
     } else {
-      const size_t rows = (size_t)a.B * H * R;
+      const size_t rows = (size_t)a.B * H * R, WS = a.ws_stride;
+      const size_t slot = (size_t)a.ws_slot0 + split;
       if (d == 0) {
-        a.ws[row * S + split] = M * kLn2;          // natural-log units for the combine
-        a.ws[rows * S + row * S + split] = L;
+        a.ws[row * WS + slot] = M * kLn2;          // natural-log units for the combine
+        a.ws[rows * WS + row * WS + slot] = L;
       }
-      a.ws[2 * rows * S + (row * S + split) * kD + d] = O;
+      a.ws[2 * rows * WS + (row * WS + slot) * kD + d] = O;
     }
   }
 }

@@ -37,6 +37,7 @@ int check_shape(const kivi_shape* s) {
   if (s->outliers < 0 || s->outliers > 8) return KIVI_EINVAL;   // (< every group size)
   if (!(s->rope_theta >= 0.f) || isinf(s->rope_theta)) return KIVI_EINVAL;
   if (s->deterministic != 0 && s->deterministic != 1) return KIVI_EINVAL;
+  if (s->v_window != 0 && s->v_window != 1) return KIVI_EINVAL;
   const int D = s->head_dim, G = s->group;
   if (!(D == 32 || D == 64 || D == 128 || D == 256)) return KIVI_EUNSUPPORTED;
   if (!(G == 32 || G == 64 || G == 128)) return KIVI_EUNSUPPORTED;
@@ -105,8 +106,16 @@ int max_auto_splits(const kivi_shape& s) {
   return units >= 2048 ? 1 : (2048 + units - 1) / units;
 }
 
-bool use_mfma(const kivi_shape& s) {
+// the matrix-core kernel takes the shape (its whole-tile part with the value
+// window)
+bool mfma_shape(const kivi_shape& s) {
   return kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers,
+                                     s.rope_theta > 0.f);
+}
+// the matrix-core kernel runs the whole decode (with the value window, the
+// generic kernel takes the tokens whose values are in the window)
+bool use_mfma(const kivi_shape& s) {
+  return !s.v_window && kivi::decode_mfma_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers,
                                      s.rope_theta > 0.f);
 }
 
@@ -120,11 +129,11 @@ int mfma_waves() {
   return nw;
 }
 
-int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
+int auto_splits_for(const kivi_shape& s, int tq, int tr, int cus, bool mfma) {
   const int units = s.batch * s.num_kv_heads;
   const int L = tq + tr;
   int S;
-  if (use_mfma(s)) {
+  if (mfma) {
     // one round of blocks: as many splits as fill the resident block slots,
     // keeping at least two 64-token tiles per wave
     const int nw = kivi::decode_mfma_block_waves(s.gqa_ratio, mfma_waves());
@@ -141,6 +150,36 @@ int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
   if (S < 1) S = 1;
   const int cap = max_auto_splits(s);
   return S > cap ? cap : S;
+}
+int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
+  return auto_splits_for(s, tq, tr, cus, use_mfma(s));
+}
+
+// The decode's plan at lengths (tq, tr): S_run splits of the main launch and
+// S_ws partial slots per query row (1: the launch writes fp16 output).  With
+// the value window, t_tiles whole 64-token tiles below max(0, L - R) (their
+// keys and values quantized) go to the matrix-core kernel in S_run splits
+// and the rest of the tokens (R to R + 63 of them) to the generic kernel as
+// kMaxTailSplits more partials; t_tiles = 0 when the matrix-core kernel does
+// not take the shape or no whole tile is there.  The device count is needed
+// (KIVI_EHIP without one) only for an automatic split count.
+// (One tail split: on the batch-8 Llama layer a step took 130 us with one and
+// 169 us with up to eight of about 16 tokens each.)
+constexpr int kMaxTailSplits = 1;
+int tail_splits(int) { return kMaxTailSplits; }
+int decode_plan(const kivi_shape& s, int tq, int tr, int num_splits, int* S_run, int* S_ws,
+                int* t_tiles) {
+  const int L = tq + tr, tv = L > s.residual ? L - s.residual : 0;
+  *t_tiles = s.v_window && mfma_shape(s) ? tv / 64 * 64 : 0;
+  int S = num_splits;
+  if (S == 0) {
+    const int cus = device_cu_count();
+    if (cus < 0) return KIVI_EHIP;
+    S = *t_tiles > 0 ? auto_splits_for(s, *t_tiles, 0, cus, true) : auto_splits(s, tq, tr, cus);
+  }
+  *S_run = S;
+  *S_ws = *t_tiles > 0 ? S + tail_splits(L - *t_tiles) : S;
+  return KIVI_OK;
 }
 
 size_t ws_bytes(const kivi_shape& s, int S) {
@@ -191,6 +230,117 @@ hipError_t launch_flush(const kivi_cache* c, int tq, hipStream_t st) {
   return kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st);
 }
 
+// ---- value window (shape.v_window) ------------------------------------------
+// Values keep the R newest tokens in v_res (token t in slot t % R); a value
+// leaving the window is quantized by itself; keys follow the lazy flush.
+
+// copies tokens [t0, t0 + n) of one tensor src ([B][H][stride][D]) into the
+// window slots t % R of dst
+hipError_t copy_window(const kivi_shape& s, const uint16_t* src, int stride, int t0, int n,
+                       uint16_t* dst, hipStream_t st) {
+  const int R = s.residual;
+  while (n > 0) {
+    const int slot = t0 % R, m = n < R - slot ? n : R - slot;
+    hipError_t e = kivi::launch_copy_tokens(nullptr, src, stride, t0, nullptr, dst, R, slot, m,
+                                            s.batch, s.num_kv_heads, s.head_dim, st);
+    if (e != hipSuccess) return e;
+    t0 += m;
+    n -= m;
+  }
+  return hipSuccess;
+}
+
+// prefill: keys as without the window; values [0, ntok - R) quantized (whole
+// 32-token chunks by the codec launch, the rest one token at a time), the
+// newest min(ntok, R) values into the window
+hipError_t prefill_window(const kivi_cache* c, const uint16_t* k, const uint16_t* v, int ntok,
+                          int tq, hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  const int tv = ntok > s.residual ? ntok - s.residual : 0, tv32 = tv / 32 * 32;
+  hipError_t e = hipSuccess;
+  if (tq > 0) {
+    kivi::QuantJob j = cache_job(c);
+    j.k = k;
+    j.v = v;
+    j.in_stride = ntok;
+    j.do_k = 1;
+    j.do_v = 0;
+    j.nq = tq;
+    j.dst_off = 0;
+    j.ncopy = 0;
+    if ((e = kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st)) != hipSuccess)
+      return e;
+  }
+  if (tv32 > 0) {
+    kivi::QuantJob j = cache_job(c);
+    j.k = k;
+    j.v = v;
+    j.in_stride = ntok;
+    j.do_k = 0;
+    j.do_v = 1;
+    j.nq = tv32;
+    j.dst_off = 0;
+    j.ncopy = 0;
+    if ((e = kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st)) != hipSuccess)
+      return e;
+  }
+  if ((e = kivi::launch_quantize_v_tokens(cache_job(c), s.bits, s.meta_half, s.batch, v, ntok,
+                                          tv32, tv32, tv - tv32, st)) != hipSuccess)
+    return e;
+  if (ntok > tq &&
+      (e = kivi::launch_copy_tokens(k, nullptr, ntok, tq, c->k_res, nullptr, s.residual, 0,
+                                    ntok - tq, s.batch, s.num_kv_heads, s.head_dim, st)) !=
+          hipSuccess)
+    return e;
+  return copy_window(s, v, ntok, tv, ntok - tv, c->v_res, st);
+}
+
+// lengths after a window append (the capacity checked), without any HIP call
+int window_append_lengths(const kivi_cache* c, int* tq, int* tr) {
+  const kivi_shape& s = c->shape;
+  const int R = s.residual, L = c->tq + c->tr;
+  const bool flush = c->tr == R;
+  if (flush && (int64_t)c->tq + R > s.capacity) return KIVI_ECAPACITY;
+  if (L >= R && L - R >= s.capacity) return KIVI_ECAPACITY;
+  *tq = c->tq + (flush ? R : 0);
+  *tr = (flush ? 0 : c->tr) + 1;
+  return KIVI_OK;
+}
+
+// enqueues a window append (lengths already checked): the key flush when the
+// key residual is full, the value leaving the window (token L - R, slot
+// L % R) into the value store, then the new key and value
+hipError_t append_window(const kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new,
+                         hipStream_t st) {
+  const kivi_shape& s = c->shape;
+  const int R = s.residual, L = c->tq + c->tr;
+  const bool flush = c->tr == R;
+  hipError_t e = hipSuccess;
+  if (flush) {
+    kivi::QuantJob j = cache_job(c);
+    j.k = c->k_res;
+    j.v = c->v_res;
+    j.in_stride = R;
+    j.do_k = 1;
+    j.do_v = 0;
+    j.nq = R;
+    j.dst_off = c->tq;
+    j.ncopy = 0;
+    if ((e = kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st)) != hipSuccess)
+      return e;
+  }
+  if (L >= R &&
+      (e = kivi::launch_quantize_v_tokens(cache_job(c), s.bits, s.meta_half, s.batch, c->v_res,
+                                          R, L % R, L - R, 1, st)) != hipSuccess)
+    return e;
+  if ((e = kivi::launch_copy_tokens(k_new, nullptr, 1, 0, c->k_res, nullptr, R,
+                                    flush ? 0 : c->tr, 1, s.batch, s.num_kv_heads, s.head_dim,
+                                    st)) != hipSuccess)
+    return e;
+  return kivi::launch_copy_tokens(nullptr, v_new, 1, 0, nullptr, c->v_res, R, L % R, 1,
+                                  s.batch, s.num_kv_heads, s.head_dim, st);
+}
+
 // ---- ragged batches and the paged store -------------------------------------
 // Both carry per-sequence host lengths; the paged store also a page map.  The
 // calls below work on this common view.
@@ -230,6 +380,7 @@ Rg view(const kivi_paged_cache* c) {
 
 // buffers present and aligned, length arrays present (shape already checked)
 int check_buffers(const Rg& g) {
+  if (g.s->v_window) return KIVI_EUNSUPPORTED;   // (uniform caches only)
   const void* ptrs[] = {g.k_codes, g.k_scale, g.k_zero, g.v_codes,
                         g.v_scale, g.v_zero,  g.k_res,  g.v_res};
   for (const void* p : ptrs)
@@ -465,6 +616,10 @@ int enqueue_ragged_decode(const Rg& g, const RaggedPlan& p, const uint16_t* q,
     a.n_out = s.outliers;
     a.rope_theta = s.rope_theta;
     a.share_tiles = s.deterministic ? 0 : 1;
+    a.vwin = 0;
+    a.t_begin = 0;
+    a.ws_stride = S;
+    a.ws_slot0 = 0;
     hipError_t e;
     if (use_mfma(s))
       e = g.paged ? kivi::launch_decode_mfma_paged(a, lens, mfma_waves(), st)
@@ -704,6 +859,14 @@ int kivi_prefill(kivi_cache* c, const uint16_t* k, const uint16_t* v, int32_t nt
   if (ntok < 1 || tq < 0 || tq % s.group != 0 || ntok - tq < 0 || ntok - tq > s.residual)
     return KIVI_ESHAPE;
   if (tq > s.capacity) return KIVI_ECAPACITY;
+  if (s.v_window) {
+    if (ntok > s.capacity + s.residual) return KIVI_ECAPACITY;
+    hipError_t e = prefill_window(c, k, v, ntok, tq, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, __func__);
+    c->tq = tq;
+    c->tr = ntok - tq;
+    return KIVI_OK;
+  }
   // one launch: tokens [0, tq) quantized, [tq, ntok) copied into the residual
   kivi::QuantJob j = cache_job(c);
   j.k = k;
@@ -728,6 +891,14 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
   const kivi_shape& s = c->shape;
   hipStream_t st = (hipStream_t)stream;
   int tq = c->tq, tr = c->tr;
+  if (s.v_window) {
+    if ((rc = window_append_lengths(c, &tq, &tr))) return rc;
+    hipError_t e = append_window(c, k_new, v_new, st);
+    if (e != hipSuccess) return hip_fail(e, __func__);
+    c->tq = tq;
+    c->tr = tr;
+    return KIVI_OK;
+  }
   if (tr == s.residual) {
     if ((int64_t)tq + s.residual > s.capacity) return KIVI_ECAPACITY;
     // flush: the full residual becomes the next quantized tokens; the copy
@@ -748,14 +919,16 @@ int kivi_append(kivi_cache* c, const uint16_t* k_new, const uint16_t* v_new, voi
 int kivi_decode_auto_splits(const kivi_cache* c) {
   int rc = check_cache(c);
   if (rc) return -rc;
-  const int cus = device_cu_count();
-  if (cus < 0) return cus;
-  return auto_splits(c->shape, c->tq, c->tr, cus);
+  int S = 0, S_ws = 0, t_tiles = 0;
+  if ((rc = decode_plan(c->shape, c->tq, c->tr, 0, &S, &S_ws, &t_tiles))) return -rc;
+  return S;
 }
 
 size_t kivi_decode_workspace_bytes(const kivi_shape* s, int32_t num_splits) {
   if (check_shape(s) != KIVI_OK || num_splits < 0 || num_splits > KIVI_MAX_SPLITS) return 0;
-  return ws_bytes(*s, num_splits == 0 ? max_auto_splits(*s) : num_splits);
+  const int S = num_splits == 0 ? max_auto_splits(*s) : num_splits;
+  // (the value window may need kMaxTailSplits more partial slots: its tail)
+  return ws_bytes(*s, s->v_window ? S + kMaxTailSplits : S);
 }
 
 // Checks a decode at lengths (tq, tr) and fills the launch arguments; no HIP
@@ -770,14 +943,11 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   const int L = tq + tr;
   if (L < 1) return KIVI_ESHAPE;
   if (num_splits > 0 && (num_splits > L || num_splits > KIVI_MAX_SPLITS)) return KIVI_ESHAPE;
-  int S = num_splits;
-  if (S == 0) {
-    const int cus = device_cu_count();
-    if (cus < 0) return KIVI_EHIP;
-    S = auto_splits(s, tq, tr, cus);
-  }
-  if (S > 1) {
-    if (workspace_bytes < ws_bytes(s, S)) return KIVI_EWORKSPACE;
+  int S = 0, S_ws = 0, t_tiles = 0;
+  int rc = decode_plan(s, tq, tr, num_splits, &S, &S_ws, &t_tiles);
+  if (rc) return rc;
+  if (S_ws > 1) {
+    if (workspace_bytes < ws_bytes(s, S_ws)) return KIVI_EWORKSPACE;
     if (!workspace) return KIVI_EINVAL;
     if (!aligned16(workspace)) return KIVI_EALIGN;
   }
@@ -812,14 +982,37 @@ static int prepare_decode(const kivi_cache* c, int tq, int tr, const uint16_t* q
   a->n_out = s.outliers;
   a->rope_theta = s.rope_theta;
   a->share_tiles = s.deterministic ? 0 : 1;
+  a->vwin = s.v_window;
+  a->t_begin = t_tiles;      // (the value window's whole-tile part, when any)
+  a->ws_stride = S_ws;
+  a->ws_slot0 = 0;
   return KIVI_OK;
 }
 
 static int enqueue_decode(const kivi_shape& s, const DecodeArgs& a, hipStream_t st) {
-  hipError_t e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
-                             : kivi::launch_decode_generic(a, st);
-  if (e != hipSuccess) return hip_fail(e, __func__);
-  if (a.S > 1) {
+  hipError_t e;
+  if (s.v_window && a.t_begin > 0) {
+    // value window: whole tiles [0, t_begin) on the matrix cores (keys and
+    // values quantized, no residual) in slots [0, S), the tail [t_begin, L)
+    // on the generic kernel in slots [S, ws_stride), then the combine over
+    // all ws_stride slots
+    DecodeArgs m = a;
+    m.tq = a.t_begin;
+    m.tr = 0;
+    m.vwin = 0;
+    m.t_begin = 0;
+    if ((e = kivi::launch_decode_mfma(m, mfma_waves(), st)) != hipSuccess)
+      return hip_fail(e, __func__);
+    DecodeArgs g = a;
+    g.S = a.ws_stride - a.S;
+    g.ws_slot0 = a.S;
+    if ((e = kivi::launch_decode_generic(g, st)) != hipSuccess) return hip_fail(e, __func__);
+  } else {
+    e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)
+                    : kivi::launch_decode_generic(a, st);
+    if (e != hipSuccess) return hip_fail(e, __func__);
+  }
+  if (a.ws_stride > 1) {
     e = kivi::launch_combine(a, st);
     if (e != hipSuccess) return hip_fail(e, __func__);
   }
@@ -847,6 +1040,22 @@ int kivi_append_decode_attn(kivi_cache* c, const uint16_t* k_new, const uint16_t
   if (!k_new || !v_new) return KIVI_EINVAL;
   if (!aligned16(k_new) || !aligned16(v_new)) return KIVI_EALIGN;
   const kivi_shape& s = c->shape;
+  if (s.v_window) {
+    // the window append's launches, then the decode at the new lengths
+    int tq2 = 0, tr2 = 0;
+    if ((rc = window_append_lengths(c, &tq2, &tr2))) return rc;
+    DecodeArgs a;
+    rc = prepare_decode(c, tq2, tr2, q, softmax_scale, out, workspace, workspace_bytes,
+                        num_splits, &a);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = append_window(c, k_new, v_new, st);
+    if (e != hipSuccess) return hip_fail(e, __func__);
+    if ((rc = enqueue_decode(s, a, st))) return rc;
+    c->tq = tq2;
+    c->tr = tr2;
+    return KIVI_OK;
+  }
   // lengths after the append (a full residual is flushed first)
   const bool flush = c->tr == s.residual;
   if (flush && (int64_t)c->tq + s.residual > s.capacity) return KIVI_ECAPACITY;
@@ -911,18 +1120,14 @@ int kivi_decode_attn_noalloc(const kivi_cache* c, const uint16_t* q, float softm
   if (num_splits > 0 && (num_splits > L || num_splits > KIVI_MAX_SPLITS)) return KIVI_ESHAPE;
   // the split count's partials must fit the array (checked before any HIP
   // call when num_splits is given)
-  int S = num_splits;
-  if (S == 0) {
-    const int cus = device_cu_count();
-    if (cus < 0) return KIVI_EHIP;
-    S = auto_splits(c->shape, c->tq, c->tr, cus);
-  }
-  if (ws_bytes(c->shape, S) > (size_t)KIVI_SCRATCH_BYTES) return KIVI_EWORKSPACE;
-  void* ws = S > 1 ? scratch_address() : nullptr;
-  if (S > 1 && !ws) return KIVI_EHIP;
+  int S = 0, S_ws = 0, t_tiles = 0;
+  if ((rc = decode_plan(c->shape, c->tq, c->tr, num_splits, &S, &S_ws, &t_tiles))) return rc;
+  if (ws_bytes(c->shape, S_ws) > (size_t)KIVI_SCRATCH_BYTES) return KIVI_EWORKSPACE;
+  void* ws = S_ws > 1 ? scratch_address() : nullptr;
+  if (S_ws > 1 && !ws) return KIVI_EHIP;
   DecodeArgs a;
-  rc = prepare_decode(c, c->tq, c->tr, q, softmax_scale, out, ws, S > 1 ? KIVI_SCRATCH_BYTES : 0,
-                      S, &a);
+  rc = prepare_decode(c, c->tq, c->tr, q, softmax_scale, out, ws,
+                      S_ws > 1 ? KIVI_SCRATCH_BYTES : 0, S, &a);
   if (rc) return rc;
   return enqueue_decode(c->shape, a, (hipStream_t)stream);
 }

@@ -93,6 +93,14 @@ struct DecodeArgs {
   // 1: the waves of a block share its tiles in load-return order (matrix-core
   // kernel); 0: fixed per-wave runs (reproducible)
   int share_tiles;
+  // 1: value sliding window (generic kernel): values [0, max(0, L - R))
+  // quantized, value token t >= that in v_res slot t % R
+  int vwin;
+  // generic kernel: first token of the launch's range [t_begin, tq + tr)
+  int t_begin;
+  // split partials: ws_stride slots per query row, this launch's splits at
+  // slots ws_slot0 .. ws_slot0 + S - 1 (ws_stride == 1: fp16 output instead)
+  int ws_stride, ws_slot0;
 };
 
 // Kernel parameter of the decode kernels: nothing (uniform lengths, taken
@@ -152,8 +160,15 @@ hipError_t launch_quantize_kv_list(const QuantJob& j, const SeqList& list, int b
                                    int ncopy_max, hipStream_t st);
 hipError_t launch_quantize_kv_paged(const QuantJob& j, const SeqList& list, const PageMap& pm,
                                     int bits, int mh, int ncopy_max, hipStream_t st);
+// Value window: quantizes cache tokens [t0, t0 + n) of every (b, h) from
+// source rows [src_row, src_row + n) of src ([B][H][src_stride][D]) into the
+// value store of j (per-token groups; other tokens' code bits kept).
+hipError_t launch_quantize_v_tokens(const QuantJob& j, int bits, int mh, int B,
+                                    const uint16_t* src, int src_stride, int src_row, int t0,
+                                    int n, hipStream_t st);
 // Copies tokens [t0, t0 + n) of src ([B][H][src_stride][D]) into slots
-// [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once.
+// [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once
+// (a null source skips that tensor).
 hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int src_stride,
                               int t0, uint16_t* k_dst, uint16_t* v_dst, int dst_stride,
                               int slot0, int n, int B, int H, int D, hipStream_t st);

@@ -600,8 +600,70 @@ copy_tokens_kernel(const uint16_t* __restrict__ k_src, const uint16_t* __restric
     const int t = i / per_tok, c = i % per_tok;
     const size_t so = ((bh * src_stride + t0 + t) * D) / 8 + c;
     const size_t dd = ((bh * dst_stride + slot0 + t) * D) / 8 + c;
-    copy16_nt(reinterpret_cast<uint4*>(k_dst) + dd, reinterpret_cast<const uint4*>(k_src) + so);
-    copy16_nt(reinterpret_cast<uint4*>(v_dst) + dd, reinterpret_cast<const uint4*>(v_src) + so);
+    if (k_src)
+      copy16_nt(reinterpret_cast<uint4*>(k_dst) + dd, reinterpret_cast<const uint4*>(k_src) + so);
+    if (v_src)
+      copy16_nt(reinterpret_cast<uint4*>(v_dst) + dd, reinterpret_cast<const uint4*>(v_src) + so);
+  }
+}
+
+// Value quantization of single tokens (the value window): block (b, h) takes
+// cache tokens t0 .. t0 + n - 1 in order, one thread per channel; token
+// t0 + i comes from source row src_row + i of the plane's [src_stride][D]
+// rows.  The steps are the codec's (S1) with the correctly rounded division
+// and a strict in-order min / max scan; a token replaces the bits of its
+// position in the shared 64-token value rows and keeps the other tokens'
+// bits.  Each thread writes only its own channel's rows, in token order.
+template <int BITS>
+__device__ __forceinline__ void set_code(uint32_t* row, int p, uint32_t c) {
+  if constexpr (BITS == 3) {
+    row[p >> 4] = (row[p >> 4] & ~(3u << (2 * (p & 15)))) | ((c & 3u) << (2 * (p & 15)));
+    const int w = 4 + (p >> 5), b = beta(p & 31);   // (64-position rows: the hi plane at word 4)
+    row[w] = (row[w] & ~(1u << b)) | ((c >> 2) << b);
+  } else if constexpr (BITS == 1) {
+    const int b = beta(p & 31);
+    row[p >> 5] = (row[p >> 5] & ~(1u << b)) | (c << b);
+  } else {
+    constexpr int E = 32 / BITS;
+    constexpr uint32_t M = (1u << BITS) - 1u;
+    const int sh = BITS * (p % E);
+    row[p / E] = (row[p / E] & ~(M << sh)) | (c << sh);
+  }
+}
+
+template <int BITS, bool MH>
+__global__ void __launch_bounds__(256)
+quantize_v_tokens_kernel(QuantJob j, const uint16_t* __restrict__ src, int src_stride,
+                         int src_row, int t0, int n) {
+  __shared__ float xs[256];
+  __shared__ float gs[8], gz[8];   // (D / G <= 8)
+  const int D = j.D, G = j.G, NG = D / G, d = threadIdx.x;
+  const size_t bh = blockIdx.x;
+  constexpr float qmax = (float)((1 << BITS) - 1);
+  uint32_t* plane = j.v_codes + bh * ((size_t)j.cap * D * BITS / 32);
+  for (int i = 0; i < n; i++) {
+    const int t = t0 + i;
+    const float x = h2f(src[(bh * src_stride + src_row + i) * D + d]);
+    xs[d] = x;
+    __syncthreads();
+    if (d < NG) {
+      float mn = xs[d * G], mx = mn;
+      for (int e = 1; e < G; e++) {
+        const float y = xs[d * G + e];
+        if (y < mn) mn = y;
+        if (y > mx) mx = y;
+      }
+      const float sc = group_scale<BITS>(mn, mx);
+      gs[d] = sc;
+      gz[d] = mn;
+      put_meta<MH>(j.v_scale, (bh * j.cap + t) * NG + d, sc);
+      put_meta<MH>(j.v_zero, (bh * j.cap + t) * NG + d, mn);
+    }
+    __syncthreads();
+    const float sc = gs[d / G], z = gz[d / G];
+    const uint32_t c = sc == 0.0f ? 0u : (uint32_t)fminf(rintf((x - z) / sc), qmax);
+    set_code<BITS>(plane + ((size_t)(t / 64) * D + d) * (2 * BITS), t % 64, c);
+    __syncthreads();   // (xs and gs are rewritten by the next token)
   }
 }
 
@@ -685,6 +747,18 @@ hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int 
   dim3 grid((items + 255) / 256, B * H);
   copy_tokens_kernel<false><<<grid, 256, 0, st>>>(k_src, v_src, src_stride, t0, k_dst, v_dst,
                                                   dst_stride, slot0, n, D, H, NoList{});
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v_tokens(const QuantJob& j, int bits, int mh, int B,
+                                    const uint16_t* src, int src_stride, int src_row, int t0,
+                                    int n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(B * j.H);
+  dispatch(bits, mh, false, [&](auto Bt, auto M, auto) {
+    quantize_v_tokens_kernel<Bt.value, M.value>
+        <<<grid, j.D, 0, st>>>(j, src, src_stride, src_row, t0, n);
+  });
   return hipGetLastError();
 }
 

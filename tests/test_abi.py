@@ -40,7 +40,7 @@ def test_strerror():
 def shape(**kw):
     d = dict(batch=2, num_kv_heads=4, gqa_ratio=2, head_dim=128, bits=2, group=32,
              residual=128, capacity=512, meta_half=0, outliers=0, rope_theta=0.0,
-             deterministic=0)
+             deterministic=0, v_window=0)
     d.update(kw)
     return kivi_shape(*[d[n] for n, _ in kivi_shape._fields_])
 
@@ -84,6 +84,7 @@ def test_cache_bytes():
     (dict(rope_theta=-1.0), KIVI_EINVAL), (dict(rope_theta=float("inf")), KIVI_EINVAL),
     (dict(rope_theta=float("nan")), KIVI_EINVAL),
     (dict(deterministic=2), KIVI_EINVAL), (dict(deterministic=-1), KIVI_EINVAL),
+    (dict(v_window=2), KIVI_EINVAL), (dict(v_window=-1), KIVI_EINVAL),
 ])
 def test_shape_errors(kw, code):
     assert sizes(shape(**kw))[0] == code
@@ -418,3 +419,41 @@ def test_one_hip_runtime_in_process():
     assert out.returncode == 0, out.stderr
     n = int(out.stdout.split()[0])
     assert n == 1, out.stdout
+
+
+# ---- value window ----
+
+def test_window_errors_leave_state():
+    """The window append and the fused step refuse a key flush or a value
+    past the capacity, and bad arguments, before any HIP call; ragged and
+    paged caches refuse the window."""
+    import numpy as np
+    ad = _lib.kivi_append_decode_attn
+    c = cache(tq=416, tr=128, v_window=1)      # key flush to 544 > 512
+    assert _lib.kivi_append(ctypes.byref(c), P, P, None) == KIVI_ECAPACITY
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, None, 0, 1, None) == KIVI_ECAPACITY
+    assert (c.tq, c.tr) == (416, 128)
+    c = cache(tq=64, tr=3, v_window=1)
+    assert _lib.kivi_append(ctypes.byref(c), None, P, None) == KIVI_EINVAL
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P + 2, None, 0, 1, None) == KIVI_EALIGN
+    # the query covers the window's extra partial slot (its tail) ...
+    ws = _lib.kivi_decode_workspace_bytes
+    assert ws(ctypes.byref(c.shape), 4) == ws(ctypes.byref(shape()), 5)
+    # (automatic: at most 2048 / 8 = 256 splits for 2 x 4 (b, h) units, + 1)
+    assert ws(ctypes.byref(c.shape), 0) == ws(ctypes.byref(shape()), 0) // 256 * 257
+    # ... and a workspace short of this decode's own 4 slots is refused
+    need = ws(ctypes.byref(shape()), 4)
+    assert ad(ctypes.byref(c), P, P, P, 0.1, P, P, need - 1, 4, None) == KIVI_EWORKSPACE
+    assert (c.tq, c.tr) == (64, 3)
+    assert _lib.kivi_prefill(ctypes.byref(c), P, P, 300, 128, None) == KIVI_ESHAPE
+    assert (c.tq, c.tr) == (64, 3)
+    r = ragged([64, 32], [3, 1], v_window=1)
+    assert _lib.kivi_ragged_append(ctypes.byref(r), P, P, None) == KIVI_EUNSUPPORTED
+    p32 = ctypes.POINTER(ctypes.c_int32)
+    assert _lib.kivi_ragged_prefill(ctypes.byref(r), P, P, 256, r._keep[0].ctypes.data_as(p32),
+                                    r._keep[1].ctypes.data_as(p32), None) == KIVI_EUNSUPPORTED
+    assert lens(r) == ([64, 32], [3, 1])
+    g = paged([64, 32], [3, 1], v_window=1)
+    assert _lib.kivi_paged_decode_attn(ctypes.byref(g), P, 0.1, P, None, 0, 1,
+                                       None) == KIVI_EUNSUPPORTED
+    assert np.array_equal(g._keep[0], [64, 32])

@@ -102,3 +102,28 @@ def test_cpu_baseline_multi_core():
     r = bench.cpu_baseline(w, min_seconds=0.05, max_seconds=5.0, workers=3)
     assert r["cores"] == 3 and r["value"] > 0 and r["one_core"]["value"] > 0
     assert "over 3 processes" in r["sample"]
+
+
+def test_window_bytes():
+    """With the value window, the tokens [L - R, tq) have quantized keys and
+    fp16 values: the decode reads 2 D value bytes each instead of their
+    codes, scales and zeros; everything else is unchanged.  The append adds
+    the leaving value, and its flush covers the keys only."""
+    B, H, r, D, bits, G, R = 2, 4, 1, 128, 2, 32, 128
+    for mb in (4, 2):
+        for tq, tr in ((3968, 127), (4096, 1), (0, 60), (64, 100)):
+            tv = max(0, tq + tr - R)
+            diff = int(bench.decode_bytes(B, H, r, D, bits, G, tq, tr, mb, 0, True, R)) - \
+                bench.decode_bytes(B, H, r, D, bits, G, tq, tr, mb)
+            assert diff == B * H * (tq - tv) * (2 * D - D * bits // 8 - (D // G) * 2 * mb)
+        base = bench.append_bytes(B, H, D, bits, G, R, False, mb)
+        leave = bench.append_bytes(B, H, D, bits, G, R, False, mb, 0, True, True)
+        assert leave - base == B * H * (2 * D + D * bits // 8 + (D // G) * 2 * mb)
+        full = bench.append_bytes(B, H, D, bits, G, R, True, mb)
+        keys = bench.append_bytes(B, H, D, bits, G, R, True, mb, 0, True, False)
+        assert full - keys == B * H * (R * D * 2 + R * D * bits // 8 + R * (D // G) * 2 * mb)
+    # prefill: the window keeps the R newest values, so max(0, T - R) are quantized
+    assert bench.prefill_bytes(H, D, bits, G, 3968, 128, 4, 0, True, R) == \
+        bench.prefill_bytes(H, D, bits, G, 3968, 128, 4)
+    assert bench.prefill_bytes(H, D, bits, G, 64, 100, 4, 0, True, R) < \
+        bench.prefill_bytes(H, D, bits, G, 64, 100, 4) + H * 64 * D * 4
