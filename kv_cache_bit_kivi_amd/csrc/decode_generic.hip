@@ -25,6 +25,8 @@
 // (max, sum, unnormalised o) partial and the combine kernel merges them.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kivi_internal.h"
 
 namespace kivi {
@@ -289,7 +291,175 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   }
 }
 
+// ---- value window tail ---------------------------------------------------
+// Tokens [a.t_begin, tq + tr) of one (b, h) plane for the matrix-core shape
+// (D = 128, G = 32) without key outliers or pre-RoPE keys: keys from the
+// codes (t < tq) or the key residual, values from the codes (t < L - R) or
+// the window (slot t % R).  Lane l holds channels 2l and 2l + 1; wave w takes
+// every NWV-th token (16 waves, 8 for eight heads: the merge buffer stays at
+// 32 KB), scores by a butterfly sum over the lanes and an
+// online softmax per head; the waves' states merge in LDS with the split-K
+// partials [0, a.ws_slot0) that the matrix-core launch before it wrote
+// (natural-log maxima), and the block writes the fp16 output.
+
+// code at position p of a packed row of n codes, b = BITS (the layouts of
+// code_at, with the width known at compile time)
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at_t(const uint32_t* row, int n, int p) {
+  if constexpr (BITS == 3) {
+    const int q = p & 31;
+    const int bt = 4 * ((q & 15) >> 1) + 2 * (q >> 4) + (q & 1);
+    return ((row[p >> 4] >> (2 * (p & 15))) & 3u) | (((row[(n >> 4) + (p >> 5)] >> bt) & 1u) << 2);
+  } else if constexpr (BITS == 1) {
+    const int q = p & 31;
+    const int bt = 4 * ((q & 15) >> 1) + 2 * (q >> 4) + (q & 1);
+    return (row[p >> 5] >> bt) & 1u;
+  } else {
+    constexpr int E = 32 / BITS;
+    return (row[p / E] >> (BITS * (p % E))) & ((1u << BITS) - 1u);
+  }
+}
+
+__device__ __forceinline__ float lane_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+template <int RR>
+constexpr int tail_waves() { return RR >= 8 ? 8 : 16; }
+
+template <int BITS, bool MH, int RR, int NWV = tail_waves<RR>()>
+__global__ void __launch_bounds__(NWV * 64) window_tail_kernel(DecodeArgs a) {
+  constexpr int D = 128, G = 32, NG = D / G, W = D * BITS / 32, WPC = 2 * BITS;
+  __shared__ float s_m[NWV][RR], s_l[NWV][RR];
+  __shared__ float s_o[NWV][RR][D];
+  const int u = blockIdx.x;                  // b * H + h
+  const int b = u / a.H, h = u % a.H, r = a.r;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, c0 = 2 * lane;
+  const int tq = a.tq, L = a.tq + a.tr, R = a.R;
+  const int tv = L > R ? L - R : 0;
+  const size_t qrow0 = (size_t)b * a.H * r + (size_t)h * r;
+  float q0[RR], q1[RR], m[RR], l[RR], o0[RR], o1[RR];
+#pragma unroll
+  for (int i = 0; i < RR; i++) {
+    const bool on = i < r;
+    q0[i] = on ? a.scale * h2f(a.q[(qrow0 + i) * D + c0]) : 0.f;
+    q1[i] = on ? a.scale * h2f(a.q[(qrow0 + i) * D + c0 + 1]) : 0.f;
+    m[i] = -INFINITY;
+    l[i] = o0[i] = o1[i] = 0.f;
+  }
+  const size_t cap = a.cap;
+  const uint32_t* kc = a.k_codes + (size_t)u * cap * W;
+  const uint32_t* vc = a.v_codes + (size_t)u * cap * D * BITS / 32;
+  const uint16_t* kr = a.k_res + (size_t)u * R * D;
+  const uint16_t* vr = a.v_res + (size_t)u * R * D;
+#pragma unroll 2
+  for (int t = a.t_begin + wv; t < L; t += NWV) {
+    float k0, k1, v0, v1;
+    if (t < tq) {
+      const uint32_t* row = kc + (size_t)t * W;
+      const size_t mi = ((size_t)u * (cap / G) + t / G) * D + c0;
+      k0 = (float)code_at_t<BITS>(row, D, c0) * meta_at(a.k_scale, mi, MH) +
+           meta_at(a.k_zero, mi, MH);
+      k1 = (float)code_at_t<BITS>(row, D, c0 + 1) * meta_at(a.k_scale, mi + 1, MH) +
+           meta_at(a.k_zero, mi + 1, MH);
+    } else {
+      k0 = h2f(kr[(size_t)(t - tq) * D + c0]);
+      k1 = h2f(kr[(size_t)(t - tq) * D + c0 + 1]);
+    }
+    if (t < tv) {
+      const uint32_t* row0 = vc + ((size_t)(t / 64) * D + c0) * WPC;
+      const size_t mi = ((size_t)u * cap + t) * NG + c0 / G;
+      const float sc = meta_at(a.v_scale, mi, MH), z = meta_at(a.v_zero, mi, MH);
+      v0 = (float)code_at_t<BITS>(row0, 64, t % 64) * sc + z;
+      v1 = (float)code_at_t<BITS>(row0 + WPC, 64, t % 64) * sc + z;
+    } else {
+      v0 = h2f(vr[(size_t)(t % R) * D + c0]);
+      v1 = h2f(vr[(size_t)(t % R) * D + c0 + 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < RR; i++) {
+      if (i >= r) continue;
+      const float sc = lane_sum(q0[i] * k0 + q1[i] * k1);
+      const float mn = fmaxf(m[i], sc);
+      const float alpha = __expf(m[i] - mn);   // (0 while m is -inf)
+      const float p = __expf(sc - mn);
+      l[i] = l[i] * alpha + p;
+      o0[i] = o0[i] * alpha + p * v0;
+      o1[i] = o1[i] * alpha + p * v1;
+      m[i] = mn;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < RR; i++) {
+    if (lane == 0) {
+      s_m[wv][i] = m[i];
+      s_l[wv][i] = l[i];
+    }
+    s_o[wv][i][c0] = o0[i];
+    s_o[wv][i][c0 + 1] = o1[i];
+  }
+  __syncthreads();
+  const size_t rows = (size_t)a.B * a.H * r, WS = a.ws_stride;
+  const int S0 = a.ws_slot0;   // the matrix-core partials
+  for (int idx = threadIdx.x; idx < r * D; idx += NWV * 64) {
+    const int i = idx / D, d = idx % D;
+    const size_t row = qrow0 + i;
+    const float* pm = a.ws + row * WS;
+    const float* pl = a.ws + rows * WS + row * WS;
+    const float* po = a.ws + 2 * rows * WS + row * WS * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NWV; w++) M = fmaxf(M, s_m[w][i]);
+    for (int sp = 0; sp < S0; sp++) M = fmaxf(M, pm[sp]);
+    float O = 0.f, Ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; w++) {
+      const float f = __expf(s_m[w][i] - M);
+      O += s_o[w][i][d] * f;
+      Ls += s_l[w][i] * f;
+    }
+    for (int sp = 0; sp < S0; sp++) {
+      const float f = __expf(pm[sp] - M);
+      O += po[(size_t)sp * D + d] * f;
+      Ls += pl[sp] * f;
+    }
+    a.out[row * D + d] = f2h(O / Ls);
+  }
+}
+
 }  // namespace
+
+bool window_tail_supported(int D, int G, int r, int outliers, bool rope) {
+  return D == 128 && G == 32 && r >= 1 && r <= 8 && outliers == 0 && !rope;
+}
+
+hipError_t launch_window_tail(const DecodeArgs& a, hipStream_t st) {
+  const dim3 grid(a.B * a.H);
+  auto go = [&](auto B, auto M) {
+    constexpr int BITS = decltype(B)::value;
+    constexpr bool MH = decltype(M)::value;
+    if (a.r == 1)
+      window_tail_kernel<BITS, MH, 1><<<grid, tail_waves<1>() * 64, 0, st>>>(a);
+    else if (a.r == 2)
+      window_tail_kernel<BITS, MH, 2><<<grid, tail_waves<2>() * 64, 0, st>>>(a);
+    else if (a.r <= 4)
+      window_tail_kernel<BITS, MH, 4><<<grid, tail_waves<4>() * 64, 0, st>>>(a);
+    else
+      window_tail_kernel<BITS, MH, 8><<<grid, tail_waves<8>() * 64, 0, st>>>(a);
+  };
+  auto with_mh = [&](auto B) {
+    if (a.mh) go(B, std::true_type{}); else go(B, std::false_type{});
+  };
+  switch (a.bits) {
+    case 1: with_mh(std::integral_constant<int, 1>{}); break;
+    case 2: with_mh(std::integral_constant<int, 2>{}); break;
+    case 3: with_mh(std::integral_constant<int, 3>{}); break;
+    default: with_mh(std::integral_constant<int, 4>{}); break;
+  }
+  return hipGetLastError();
+}
 
 size_t decode_generic_lds_bytes(int r, int D) {
   int rr = 1;

@@ -163,8 +163,9 @@ int auto_splits(const kivi_shape& s, int tq, int tr, int cus) {
 // kMaxTailSplits more partials; t_tiles = 0 when the matrix-core kernel does
 // not take the shape or no whole tile is there.  The device count is needed
 // (KIVI_EHIP without one) only for an automatic split count.
-// (One tail split: on the batch-8 Llama layer a step took 130 us with one and
-// 169 us with up to eight of about 16 tokens each.)
+// (One tail partial: its kernel takes the whole tail in one block per plane;
+// on the generic kernel a step of the batch-8 Llama layer took 130 us with
+// one and 169 us with up to eight splits of about 16 tokens each.)
 constexpr int kMaxTailSplits = 1;
 int tail_splits(int) { return kMaxTailSplits; }
 int decode_plan(const kivi_shape& s, int tq, int tr, int num_splits, int* S_run, int* S_ws,
@@ -329,16 +330,11 @@ hipError_t append_window(const kivi_cache* c, const uint16_t* k_new, const uint1
     if ((e = kivi::launch_quantize_kv(j, s.bits, s.meta_half, s.batch, st)) != hipSuccess)
       return e;
   }
-  if (L >= R &&
-      (e = kivi::launch_quantize_v_tokens(cache_job(c), s.bits, s.meta_half, s.batch, c->v_res,
-                                          R, L % R, L - R, 1, st)) != hipSuccess)
-    return e;
-  if ((e = kivi::launch_copy_tokens(k_new, nullptr, 1, 0, c->k_res, nullptr, R,
-                                    flush ? 0 : c->tr, 1, s.batch, s.num_kv_heads, s.head_dim,
-                                    st)) != hipSuccess)
-    return e;
-  return kivi::launch_copy_tokens(nullptr, v_new, 1, 0, nullptr, c->v_res, R, L % R, 1,
-                                  s.batch, s.num_kv_heads, s.head_dim, st);
+  // one launch: the leaving value (if any) quantized from its window slot,
+  // then the new key and value written into their slots
+  return kivi::launch_quantize_v_tokens(cache_job(c), s.bits, s.meta_half, s.batch, c->v_res,
+                                        R, L % R, L - R, L >= R ? 1 : 0, st, k_new,
+                                        flush ? 0 : c->tr, v_new, L % R);
 }
 
 // ---- ragged batches and the paged store -------------------------------------
@@ -1006,6 +1002,12 @@ static int enqueue_decode(const kivi_shape& s, const DecodeArgs& a, hipStream_t 
     DecodeArgs g = a;
     g.S = a.ws_stride - a.S;
     g.ws_slot0 = a.S;
+    if (kivi::window_tail_supported(s.head_dim, s.group, s.gqa_ratio, s.outliers,
+                                    s.rope_theta > 0.f)) {
+      // (the tail kernel merges every partial and writes the output itself)
+      if ((e = kivi::launch_window_tail(g, st)) != hipSuccess) return hip_fail(e, __func__);
+      return KIVI_OK;
+    }
     if ((e = kivi::launch_decode_generic(g, st)) != hipSuccess) return hip_fail(e, __func__);
   } else {
     e = use_mfma(s) ? kivi::launch_decode_mfma(a, mfma_waves(), st)

@@ -160,12 +160,24 @@ hipError_t launch_quantize_kv_list(const QuantJob& j, const SeqList& list, int b
                                    int ncopy_max, hipStream_t st);
 hipError_t launch_quantize_kv_paged(const QuantJob& j, const SeqList& list, const PageMap& pm,
                                     int bits, int mh, int ncopy_max, hipStream_t st);
+// Value window tail (decode tokens [a.t_begin, L) into split-K slot
+// a.ws_slot0) for the shapes the dedicated kernel takes: D 128, G 32, no key
+// outliers, no pre-RoPE keys, gqa ratio <= 8.
+bool window_tail_supported(int D, int G, int r, int outliers, bool rope);
+// (final: the kernel also merges split-K slots [0, a.ws_slot0), which the
+// matrix-core launch before it wrote, with its own and writes the fp16
+// output; no combine launch follows)
+hipError_t launch_window_tail(const DecodeArgs& a, hipStream_t st);
 // Value window: quantizes cache tokens [t0, t0 + n) of every (b, h) from
 // source rows [src_row, src_row + n) of src ([B][H][src_stride][D]) into the
-// value store of j (per-token groups; other tokens' code bits kept).
+// value store of j (per-token groups; other tokens' code bits kept); with
+// k_new (append: n <= 1), then writes the new token ([B][H][D] rows) into
+// key-residual slot k_slot and window slot v_slot of j.k_res, j.v_res.
 hipError_t launch_quantize_v_tokens(const QuantJob& j, int bits, int mh, int B,
                                     const uint16_t* src, int src_stride, int src_row, int t0,
-                                    int n, hipStream_t st);
+                                    int n, hipStream_t st, const uint16_t* k_new = nullptr,
+                                    int k_slot = 0, const uint16_t* v_new = nullptr,
+                                    int v_slot = 0);
 // Copies tokens [t0, t0 + n) of src ([B][H][src_stride][D]) into slots
 // [slot0, slot0 + n) of dst ([B][H][dst_stride][D]), for K and V at once
 // (a null source skips that tensor).

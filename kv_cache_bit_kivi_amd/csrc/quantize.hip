@@ -631,10 +631,14 @@ __device__ __forceinline__ void set_code(uint32_t* row, int p, uint32_t c) {
   }
 }
 
+// (The window append fuses the new token's copies into the same launch:
+// after its token, thread d writes channel d of k_new into key-residual slot
+// k_slot and of v_new into window slot v_slot, which it has already read.)
 template <int BITS, bool MH>
 __global__ void __launch_bounds__(256)
 quantize_v_tokens_kernel(QuantJob j, const uint16_t* __restrict__ src, int src_stride,
-                         int src_row, int t0, int n) {
+                         int src_row, int t0, int n, const uint16_t* __restrict__ k_new,
+                         int k_slot, const uint16_t* __restrict__ v_new, int v_slot) {
   __shared__ float xs[256];
   __shared__ float gs[8], gz[8];   // (D / G <= 8)
   const int D = j.D, G = j.G, NG = D / G, d = threadIdx.x;
@@ -664,6 +668,10 @@ quantize_v_tokens_kernel(QuantJob j, const uint16_t* __restrict__ src, int src_s
     const uint32_t c = sc == 0.0f ? 0u : (uint32_t)fminf(rintf((x - z) / sc), qmax);
     set_code<BITS>(plane + ((size_t)(t / 64) * D + d) * (2 * BITS), t % 64, c);
     __syncthreads();   // (xs and gs are rewritten by the next token)
+  }
+  if (k_new) {
+    j.k_res[(bh * j.R + k_slot) * D + d] = k_new[bh * D + d];
+    j.v_res[(bh * j.R + v_slot) * D + d] = v_new[bh * D + d];
   }
 }
 
@@ -752,12 +760,13 @@ hipError_t launch_copy_tokens(const uint16_t* k_src, const uint16_t* v_src, int 
 
 hipError_t launch_quantize_v_tokens(const QuantJob& j, int bits, int mh, int B,
                                     const uint16_t* src, int src_stride, int src_row, int t0,
-                                    int n, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
+                                    int n, hipStream_t st, const uint16_t* k_new, int k_slot,
+                                    const uint16_t* v_new, int v_slot) {
+  if (n <= 0 && !k_new) return hipSuccess;
   const dim3 grid(B * j.H);
   dispatch(bits, mh, false, [&](auto Bt, auto M, auto) {
-    quantize_v_tokens_kernel<Bt.value, M.value>
-        <<<grid, j.D, 0, st>>>(j, src, src_stride, src_row, t0, n);
+    quantize_v_tokens_kernel<Bt.value, M.value><<<grid, j.D, 0, st>>>(
+        j, src, src_stride, src_row, t0, n, k_new, k_slot, v_new, v_slot);
   });
   return hipGetLastError();
 }
