@@ -136,9 +136,10 @@ enum kivi_status {
  *     are quantized.  Uniform caches only (KIVI_EUNSUPPORTED for ragged and
  *     paged caches).  Decode: the whole 64-token tiles below L - R (keys
  *     and values quantized) on the matrix-core kernel where it takes the
- *     shape, in num_splits splits, and the other tokens on the generic
- *     kernel as one more split-K partial; shapes the matrix-core kernel does
- *     not take run on the generic kernel alone. */
+ *     shape, in num_splits splits, and the other tokens as one more split-K
+ *     partial (a dedicated kernel without key outliers or pre-RoPE keys,
+ *     else the generic kernel); shapes the matrix-core kernel does not take
+ *     run on the generic kernel alone. */
 typedef struct {
   int32_t batch;
   int32_t num_kv_heads;
