@@ -52,18 +52,24 @@ def test_noalloc_equals_workspace_decode():
     require_gpu()
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
-    # (B, H, r, D, bits, G, R, tq, tr, splits): a long matrix-core case, then a
-    # smaller one; a generic-kernel case (D = 64); the automatic split count
-    cases = [(4, 8, 2, 128, 2, 32, 128, 2944, 77, 5), (2, 4, 1, 128, 4, 32, 64, 640, 9, 3),
-             (3, 2, 1, 64, 2, 32, 32, 448, 20, 4), (1, 2, 1, 128, 2, 32, 128, 16256, 100, 0)]
-    for i, (B, H, r, D, bits, G, R, tq, tr, S) in enumerate(cases):
-        announce(f"noalloc vs workspace decode {(B, H, r, D, bits, G, R, tq, tr, S)}")
+    # (B, H, r, D, bits, G, R, tq, tr, splits, value window): a long matrix-core
+    # case, then a smaller one; a generic-kernel case (D = 64); the automatic
+    # split count; value windows (matrix cores + the tail kernel, whose
+    # partials go through the array; the generic kernel alone)
+    cases = [(4, 8, 2, 128, 2, 32, 128, 2944, 77, 5, False),
+             (2, 4, 1, 128, 4, 32, 64, 640, 9, 3, False),
+             (3, 2, 1, 64, 2, 32, 32, 448, 20, 4, False),
+             (1, 2, 1, 128, 2, 32, 128, 16256, 100, 0, False),
+             (2, 4, 2, 128, 2, 32, 128, 960, 100, 3, True),
+             (2, 4, 2, 64, 2, 32, 64, 256, 40, 0, True)]
+    for i, (B, H, r, D, bits, G, R, tq, tr, S, vw) in enumerate(cases):
+        announce(f"noalloc vs workspace decode {(B, H, r, D, bits, G, R, tq, tr, S, vw)}")
         T = tq + tr
         cap = (T + 63) // 64 * 64
         k = synth.random_fp16(500 + i, (B, H, T, D), scale=2.0)
         v = synth.random_fp16(600 + i, (B, H, T, D))
         q = dev(synth.random_fp16(700 + i, (B, H * r, D)))
-        gc = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True)
+        gc = KiviCache(B, H, r, D, bits, G, R, cap, deterministic=True, v_window=vw)
         gc.prefill(dev(k), dev(v), tq)
         splits = S if S else gc.auto_splits()
         if S == 0:
