@@ -295,9 +295,9 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 // Tokens [a.t_begin, tq + tr) of one (b, h) plane for the matrix-core shape
 // (D = 128, G = 32) without key outliers or pre-RoPE keys: keys from the
 // codes (t < tq) or the key residual, values from the codes (t < L - R) or
-// the window (slot t % R).  Lane l holds channels 2l and 2l + 1; wave w takes
-// every NWV-th token (16 waves, 8 for eight heads: the merge buffer stays at
-// 32 KB), scores by a butterfly sum over the lanes and an
+// the window (slot t % R).  Each half wave takes its own token stream (every
+// 2 NWV-th token; 16 waves, 8 for eight heads: the merge buffer stays at
+// 32 KB), lane = 4 channels, scores by a butterfly sum over the half and an
 // online softmax per head; the waves' states merge in LDS with the split-K
 // partials [0, a.ws_slot0) that the matrix-core launch before it wrote
 // (natural-log maxima), and the block writes the fp16 output.
@@ -320,9 +320,10 @@ __device__ __forceinline__ uint32_t code_at_t(const uint32_t* row, int n, int p)
   }
 }
 
-__device__ __forceinline__ float lane_sum(float v) {
+// sum over the 32 lanes of a half wave (every lane of the half gets it)
+__device__ __forceinline__ float half_sum(float v) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  for (int off = 16; off > 0; off >>= 1) v += __shfl_xor(v, off, 32);
   return v;
 }
 
@@ -336,69 +337,84 @@ __global__ void __launch_bounds__(NWV * 64) window_tail_kernel(DecodeArgs a) {
   __shared__ float s_o[NWV][RR][D];
   const int u = blockIdx.x;                  // b * H + h
   const int b = u / a.H, h = u % a.H, r = a.r;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, c0 = 2 * lane;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int hf = lane >> 5, c0 = 4 * (lane & 31);   // half wave, its lane's 4 channels
   const int tq = a.tq, L = a.tq + a.tr, R = a.R;
   const int tv = L > R ? L - R : 0;
   const size_t qrow0 = (size_t)b * a.H * r + (size_t)h * r;
-  float q0[RR], q1[RR], m[RR], l[RR], o0[RR], o1[RR];
+  float q[RR][4], m[RR], l[RR], o[RR][4];
 #pragma unroll
   for (int i = 0; i < RR; i++) {
-    const bool on = i < r;
-    q0[i] = on ? a.scale * h2f(a.q[(qrow0 + i) * D + c0]) : 0.f;
-    q1[i] = on ? a.scale * h2f(a.q[(qrow0 + i) * D + c0 + 1]) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      q[i][e] = i < r ? a.scale * h2f(a.q[(qrow0 + i) * D + c0 + e]) : 0.f;
+      o[i][e] = 0.f;
+    }
     m[i] = -INFINITY;
-    l[i] = o0[i] = o1[i] = 0.f;
+    l[i] = 0.f;
   }
   const size_t cap = a.cap;
   const uint32_t* kc = a.k_codes + (size_t)u * cap * W;
   const uint32_t* vc = a.v_codes + (size_t)u * cap * D * BITS / 32;
   const uint16_t* kr = a.k_res + (size_t)u * R * D;
   const uint16_t* vr = a.v_res + (size_t)u * R * D;
+  // token stream 2 wv + hf: every 2 NWV-th token
 #pragma unroll 2
-  for (int t = a.t_begin + wv; t < L; t += NWV) {
-    float k0, k1, v0, v1;
+  for (int t = a.t_begin + 2 * wv + hf; t < L; t += 2 * NWV) {
+    float k[4], v[4];
     if (t < tq) {
       const uint32_t* row = kc + (size_t)t * W;
       const size_t mi = ((size_t)u * (cap / G) + t / G) * D + c0;
-      k0 = (float)code_at_t<BITS>(row, D, c0) * meta_at(a.k_scale, mi, MH) +
-           meta_at(a.k_zero, mi, MH);
-      k1 = (float)code_at_t<BITS>(row, D, c0 + 1) * meta_at(a.k_scale, mi + 1, MH) +
-           meta_at(a.k_zero, mi + 1, MH);
+#pragma unroll
+      for (int e = 0; e < 4; e++)
+        k[e] = (float)code_at_t<BITS>(row, D, c0 + e) * meta_at(a.k_scale, mi + e, MH) +
+               meta_at(a.k_zero, mi + e, MH);
     } else {
-      k0 = h2f(kr[(size_t)(t - tq) * D + c0]);
-      k1 = h2f(kr[(size_t)(t - tq) * D + c0 + 1]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) k[e] = h2f(kr[(size_t)(t - tq) * D + c0 + e]);
     }
     if (t < tv) {
       const uint32_t* row0 = vc + ((size_t)(t / 64) * D + c0) * WPC;
       const size_t mi = ((size_t)u * cap + t) * NG + c0 / G;
       const float sc = meta_at(a.v_scale, mi, MH), z = meta_at(a.v_zero, mi, MH);
-      v0 = (float)code_at_t<BITS>(row0, 64, t % 64) * sc + z;
-      v1 = (float)code_at_t<BITS>(row0 + WPC, 64, t % 64) * sc + z;
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = (float)code_at_t<BITS>(row0 + e * WPC, 64, t % 64) * sc + z;
     } else {
-      v0 = h2f(vr[(size_t)(t % R) * D + c0]);
-      v1 = h2f(vr[(size_t)(t % R) * D + c0 + 1]);
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[e] = h2f(vr[(size_t)(t % R) * D + c0 + e]);
     }
 #pragma unroll
     for (int i = 0; i < RR; i++) {
       if (i >= r) continue;
-      const float sc = lane_sum(q0[i] * k0 + q1[i] * k1);
+      const float sc = half_sum(q[i][0] * k[0] + q[i][1] * k[1] + q[i][2] * k[2] + q[i][3] * k[3]);
       const float mn = fmaxf(m[i], sc);
       const float alpha = __expf(m[i] - mn);   // (0 while m is -inf)
       const float p = __expf(sc - mn);
       l[i] = l[i] * alpha + p;
-      o0[i] = o0[i] * alpha + p * v0;
-      o1[i] = o1[i] * alpha + p * v1;
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[i][e] = o[i][e] * alpha + p * v[e];
       m[i] = mn;
     }
   }
+  // the two halves' streams -> one state per wave (lane and lane ^ 32 hold
+  // the same channels)
 #pragma unroll
   for (int i = 0; i < RR; i++) {
+    const float m2 = __shfl_xor(m[i], 32, 64), l2 = __shfl_xor(l[i], 32, 64);
+    const float mn = fmaxf(m[i], m2);
+    const float f1 = mn == -INFINITY ? 0.f : __expf(m[i] - mn);
+    const float f2 = mn == -INFINITY ? 0.f : __expf(m2 - mn);
+    float oo[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) oo[e] = o[i][e] * f1 + __shfl_xor(o[i][e], 32, 64) * f2;
     if (lane == 0) {
-      s_m[wv][i] = m[i];
-      s_l[wv][i] = l[i];
+      s_m[wv][i] = mn;
+      s_l[wv][i] = l[i] * f1 + l2 * f2;
     }
-    s_o[wv][i][c0] = o0[i];
-    s_o[wv][i][c0 + 1] = o1[i];
+    if (hf == 0) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) s_o[wv][i][c0 + e] = oo[e];
+    }
   }
   __syncthreads();
   const size_t rows = (size_t)a.B * a.H * r, WS = a.ws_stride;
