@@ -446,6 +446,14 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   //  value factors: lane -> token lane of the tile, its own 16-byte scale /
   //    zero load (4 value groups);
   //  codes: staged through LDS and re-read in the MFMA operand layout.
+  //  One head per KV head (stored keys, no outliers): one key A operand
+  //    serves both key groups (rows (group, hi|lo)) and one value A operand
+  //    all four value groups (rows (group, hi|lo)), each output lane taking
+  //    the rows of its own group, so each is read from LDS once per tile
+  //    (otherwise the rows are (head, hi|lo) and each group has its own).
+  constexpr bool SHA = R == 1 && KO == 0 && !ROPE;
+  constexpr int KROWS = SHA ? 4 : ROWS;   // rows of the key A operand
+  constexpr int VROWS = SHA ? 8 : ROWS;   // rows of the value A operand
   const int kgrp = lane >> 5, cq = 4 * (lane & 31);
   uint32_t kwr[2];      // A offsets of channel pairs (cq, cq+2), (cq+1, cq+3)
 #pragma unroll
@@ -453,7 +461,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     const int c = cq + e;
     int m, s;
     k_pos<BITS>(c & 31, m, s);
-    kwr[e] = (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
+    kwr[e] = SHA ? (uint32_t)(((m * KROWS) * 4 + (c >> 5)) * 16 + 2 * s + (2 * kgrp) * 64)
+                 : (uint32_t)(kgrp * (4 * ROWS * 64) + ((m * ROWS) * 4 + (c >> 5)) * 16 + 2 * s);
   }
   uint32_t kwr2[2];     // the same in the 2-bit operand order (outlier slot planes)
 #pragma unroll
@@ -465,10 +474,12 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   }
   int vm, vs0;
   v_pos<BITS>(lane & 15, vm, vs0);
-  const uint32_t vwr = (uint32_t)(((vm * ROWS) * 4 + kg) * 16 + 2 * vs0);
-  // A read base: lanes of absent rows read the all-zero region instead
+  const uint32_t vwr = (uint32_t)(((vm * VROWS) * 4 + kg) * 16 + 2 * vs0);
+  // A read bases: lanes of absent rows read the all-zero region instead
   const bool row_ok = n16 < ROWS;
   const char* a_rd = row_ok ? lds_a + (n16 * 4 + kg) * 16 : zero + kg * 16;
+  const char* a_rdk = n16 < KROWS ? lds_a + (n16 * 4 + kg) * 16 : zero + kg * 16;
+  const char* a_rdv = n16 < VROWS ? lds_a + (n16 * 4 + kg) * 16 : zero + kg * 16;
   const char* res_rd = row_ok ? lds_res + (n16 * 4 + kg) * 16 : zero + kg * 16;
 
   // Issue order matters: vector-memory loads complete in order, so the query
@@ -866,7 +877,31 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
           mx0 = fmaxf(mx0, s0);
           mx1 = fmaxf(mx1, s1);
     };
-    if constexpr (KO == 0) {
+    // the matrix-core sections run at raised wave priority: with two waves
+    // per SIMD, the wave in its product keeps the matrix cores fed while the
+    // other one's vector work fills the gaps (batch-8 Llama layer 27.55 ->
+    // 27.32 us)
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (SHA) {
+      // rows (group g, hi|lo): block mb of group g takes rows 2g, 2g + 1
+      half8 af[4];
+#pragma unroll
+      for (int m = 0; m < 4; m++)
+        af[m] = *reinterpret_cast<const half8*>(a_rdk + m * KROWS * 64);
+#pragma unroll
+      for (int g = 0; g < 2; g++) {
+        if (g < ngr) {
+#pragma unroll
+          for (int mb2 = 0; mb2 < 2; mb2++) {
+            const int mb = 2 * g + mb2, k = 16 * mb + n16;
+            const float4v acc = key_block(mb, af);
+            const float s0 = (acc[2 * g] + acc[2 * g + 1]) * qup + (g ? beta1[0] : beta0[0]);
+            *sc_addr(0, k) = s0;
+            mx0 = fmaxf(mx0, s0);
+          }
+        }
+      }
+    } else if constexpr (KO == 0) {
 #pragma unroll
       for (int g = 0; g < 2; g++) {
         if (g < ngr) {
@@ -961,6 +996,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_wave_barrier();
     // tile maximum per head straight from the MFMA output: reduce over the 16
     // token lanes of each row (heads 2kg, 2kg+1 live in lane row kg)
@@ -1176,6 +1212,15 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
       for (int jj = 0; jj < kNG; jj += 2) {
         uint32_t hi, lo;
         split2_bf(valid ? p * vsv[jj] : 0.f, valid ? p * vsv[jj + 1] : 0.f, hi, lo);
+        if constexpr (SHA) {
+          // rows 2j (hi), 2j + 1 (lo) of group j
+          char* d = lds_a + vwr + (uint32_t)(2 * jj * 64);
+          *reinterpret_cast<uint16_t*>(d) = (uint16_t)hi;
+          *reinterpret_cast<uint16_t*>(d + 64) = (uint16_t)lo;
+          *reinterpret_cast<uint16_t*>(d + 128) = (uint16_t)(hi >> 16);
+          *reinterpret_cast<uint16_t*>(d + 192) = (uint16_t)(lo >> 16);
+          continue;
+        }
         char* d0 = lds_a + vwr + (uint32_t)(jj * 2 * ROWS * 64);
         char* d1 = d0 + 2 * ROWS * 64;
         *reinterpret_cast<uint16_t*>(d0 + (2 * h) * 64) = (uint16_t)hi;
@@ -1186,10 +1231,18 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     }
     __builtin_amdgcn_wave_barrier();
     const char* vstg = stg + C::KC_BYTES;
+    bf16x8 sav0, sav1;   // the shared value A operand (both token halves)
+    if constexpr (!ROPE) __builtin_amdgcn_s_setprio(1);
+    if constexpr (SHA) {
+      sav0 = *reinterpret_cast<const bf16x8*>(a_rdv);
+      sav1 = *reinterpret_cast<const bf16x8*>(a_rdv + VROWS * 64);
+    }
 #pragma unroll
     for (int j = 0; j < kNG; j++) {
-      const bf16x8 av0 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 0) * ROWS * 64);
-      const bf16x8 av1 = *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 1) * ROWS * 64);
+      const bf16x8 av0 =
+          SHA ? sav0 : *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 0) * ROWS * 64);
+      const bf16x8 av1 =
+          SHA ? sav1 : *reinterpret_cast<const bf16x8*>(a_rd + (j * 2 + 1) * ROWS * 64);
 #pragma unroll
       for (int nbj = 0; nbj < 2; nbj++) {
         const int nb = 2 * j + nbj;
@@ -1216,10 +1269,16 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
           cvn = mfma_bf(av0, cvt_word4_bf(x.x), cvn);
           cvn = mfma_bf(av1, cvt_word4_bf(x.y), cvn);
         }
-        oacc[nb][0] += cvn[0] + cvn[1];
-        if constexpr (OH == 2) oacc[nb][OH - 1] += cvn[2] + cvn[3];
+        if constexpr (SHA) {
+          // group j's rows 2j, 2j + 1 sit in lane row j / 2
+          oacc[nb][0] += cvn[2 * (j & 1)] + cvn[2 * (j & 1) + 1];
+        } else {
+          oacc[nb][0] += cvn[0] + cvn[1];
+          if constexpr (OH == 2) oacc[nb][OH - 1] += cvn[2] + cvn[3];
+        }
       }
     }
+    if constexpr (!ROPE) __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_wave_barrier();
   };
 
@@ -1497,7 +1556,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     const int h0 = 2 * kg, h1 = 2 * kg + 1;
 #pragma unroll
     for (int nb = 0; nb < 8; nb++) {
-      float* o0 = h0 < R ? lds_o + h0 * kD + 16 * nb + n16 : lds_dummy + n16;
+      // (shared value operand: channel 16 nb + n16 of the head is in lane row nb / 4)
+      float* o0 = (SHA ? kg == (nb >> 2) : h0 < R) ? lds_o + (SHA ? 0 : h0 * kD) + 16 * nb + n16
+                                                    : lds_dummy + n16;
       float* o1 = h1 < R ? lds_o + h1 * kD + 16 * nb + n16 : lds_dummy + n16;
       *o0 = oacc[nb][0];
       *o1 = OH == 2 ? oacc[nb][OH - 1] : 0.f;
