@@ -60,7 +60,11 @@
  *             at bits [bits*(d%E), +bits).
  *   k_scale, k_zero : meta [B][Hkv][cap/G][D]    (one pair per channel per
  *             group of G tokens); meta = float, or binary16 bits (uint16)
- *             when meta_half.
+ *             when meta_half.  A key zero is the minimum of binary16 inputs
+ *             and so a binary16 value; the decode relies on it (with several
+ *             query heads per KV head it takes the zeros as binary16 matrix
+ *             operands), so planes filled other than by this library's codec
+ *             must keep that property.
  *   v_codes : uint32 [B][Hkv][cap/64][D][64/E]; 64-token tiles, channel-major
  *             inside a tile: token t, channel d is in tile t/64, word
  *             (t%64)/E of channel d, bits [bits*((t%64)%E), +bits).

@@ -354,8 +354,15 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   // once the key product has read it, or in a region of its own (1-bit codes)
   constexpr int MK_BYTES = (KO > 0 && C::KC_BYTES < 2048) ? 2048 : 0;
   static_assert(!ROPE || C::RES_BYTES == 64 * R * 8, "rotated query fills the residual-A region");
+  // several heads per KV head, stored keys: the zero term beta of every head
+  // and key group is one more matrix product per tile (the scaled query rows
+  // of the residual key product times the tile's key zeros), so the per-head
+  // cross-lane sums leave the vector units; per wave the tile's key zeros as
+  // binary16 [group][channel] (512 bytes)
+  constexpr bool BMF = R >= 2 && !ROPE;
+  constexpr int KZ_BYTES = BMF ? 2 * kD * 2 : 0;
   __shared__ __align__(16) char smem[C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES +
-                                     NW * (RW_BYTES + MK_BYTES)];
+                                     NW * (RW_BYTES + MK_BYTES + KZ_BYTES)];
   // tiles the block's waves have taken beyond their first two (shared tiles)
   __shared__ int tile_ctr;
 
@@ -384,6 +391,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
   char* rope_wave = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + wv * RW_BYTES;
   char* mask_own = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES + NW * RW_BYTES +
                    wv * MK_BYTES;
+  char* kz_own = smem + C::ZERO_BYTES + NW * C::WAVE_BYTES + RT_BYTES +
+                 NW * (RW_BYTES + MK_BYTES) + wv * KZ_BYTES;
 
   // per-(b, h) planes as buffer resources (uniform base, 32-bit lane offsets)
   const size_t plane = (size_t)u, cap = (size_t)a.cap;
@@ -817,14 +826,24 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
         *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h) * 64) = hi;
         *reinterpret_cast<uint32_t*>(lds_a + kwr[e] + (2 * h + 1) * 64) = lo;
       }
-      // (on the normalised query, scaled back by qup: a power of two)
-      float bp = sqn[h][0] * kzv[0] + sqn[h][1] * kzv[1] + sqn[h][2] * kzv[2] + sqn[h][3] * kzv[3];
-      bp += dpp<0x128>(bp);
-      bp += dpp<0x124>(bp);
-      bp += dpp<0x122>(bp);
-      bp += dpp<0x121>(bp);
-      beta0[h] = (lane_read(bp, 0) + lane_read(bp, 16)) * qup;
-      beta1[h] = (lane_read(bp, 32) + lane_read(bp, 48)) * qup;
+      if constexpr (!BMF) {
+        // (on the normalised query, scaled back by qup: a power of two)
+        float bp = sqn[h][0] * kzv[0] + sqn[h][1] * kzv[1] + sqn[h][2] * kzv[2] + sqn[h][3] * kzv[3];
+        bp += dpp<0x128>(bp);
+        bp += dpp<0x124>(bp);
+        bp += dpp<0x122>(bp);
+        bp += dpp<0x121>(bp);
+        beta0[h] = (lane_read(bp, 0) + lane_read(bp, 16)) * qup;
+        beta1[h] = (lane_read(bp, 32) + lane_read(bp, 48)) * qup;
+      }
+    }
+    if constexpr (BMF) {
+      // this lane's four key zeros as binary16: exact, a zero is the minimum
+      // of binary16 inputs (the group's, or of its dense rest)
+      const hrtz2 z01 = __builtin_amdgcn_cvt_pkrtz(kzv[0], kzv[1]);
+      const hrtz2 z23 = __builtin_amdgcn_cvt_pkrtz(kzv[2], kzv[3]);
+      *reinterpret_cast<uint2*>(kz_own + (kgrp * kD + cq) * 2) =
+          uint2{__builtin_bit_cast(uint32_t, z01), __builtin_bit_cast(uint32_t, z23)};
     }
     if (half_tile && lane < 32) {
 #pragma unroll
@@ -882,6 +901,34 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     // other one's vector work fills the gaps (batch-8 Llama layer 27.55 ->
     // 27.32 us)
     __builtin_amdgcn_s_setprio(1);
+    // zero terms of the heads in this lane's output rows (2kg, 2kg + 1) for
+    // key group g: beta[g][hh]
+    float bta[2][2];
+    if constexpr (BMF) {
+      // A = the scaled query rows (head, hi|lo) of the residual key product,
+      // B = the key zeros, column n -> key group n & 1 (only columns 0 and 1
+      // are used; a column's products depend on that column alone)
+      float4v bacc = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const half8 aq = *reinterpret_cast<const half8*>(res_rd + i * ROWS * 64);
+        const half8 bz =
+            *reinterpret_cast<const half8*>(kz_own + ((n16 & 1) * kD + 32 * i + 8 * kg) * 2);
+        bacc = mfma(aq, bz, bacc);
+      }
+      // rows 2hh, 2hh + 1 of lane row kg are head 2kg + hh (hi, lo); the
+      // columns of groups 0 and 1 are broadcast over the row (row_newbcast)
+      const float s0 = (bacc[0] + bacc[1]) * qup, s1 = (bacc[2] + bacc[3]) * qup;
+      bta[0][0] = dpp<0x150>(s0);
+      bta[0][1] = dpp<0x150>(s1);
+      bta[1][0] = dpp<0x151>(s0);
+      bta[1][1] = dpp<0x151>(s1);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; g++)
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) bta[g][hh] = pick<R>(g ? beta1 : beta0, kg, hh);
+    }
     if constexpr (SHA) {
       // rows (group g, hi|lo): block mb of group g takes rows 2g, 2g + 1
       half8 af[4];
@@ -909,9 +956,9 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
           for (int m = 0; m < 4; m++)
             af[m] = *reinterpret_cast<const half8*>(a_rd + g * (4 * ROWS * 64) + m * ROWS * 64);
-          const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
 #pragma unroll
-          for (int mb2 = 0; mb2 < 2; mb2++) put_scores(2 * g + mb2, key_block(2 * g + mb2, af), b0, b1);
+          for (int mb2 = 0; mb2 < 2; mb2++)
+            put_scores(2 * g + mb2, key_block(2 * g + mb2, af), bta[g][0], bta[g][1]);
         }
       }
     } else {
@@ -990,9 +1037,8 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
       for (int g = 0; g < 2; g++) {
         if (g < ngr) {
-          const float b0 = pick<R>(g ? beta1 : beta0, kg, 0), b1 = pick<R>(g ? beta1 : beta0, kg, 1);
 #pragma unroll
-          for (int mb2 = 0; mb2 < 2; mb2++) put_scores(2 * g + mb2, accs[2 * g + mb2], b0, b1);
+          for (int mb2 = 0; mb2 < 2; mb2++) put_scores(2 * g + mb2, accs[2 * g + mb2], bta[g][0], bta[g][1]);
         }
       }
     }
@@ -1198,7 +1244,12 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
     }
     // P.V: value factors of token lane, 4 groups, hi/lo halves to LDS
     const bool valid = tile * 64 + lane < tq;
-    const float vsv[4] = {vs4.x, vs4.y, vs4.z, vs4.w};
+    // (absent tokens of a half tile: p = 0 and factors 0, so every product of
+    // theirs is 0 whatever their unwritten scale / zero held; several heads
+    // mask the factors once, one head each product, which compiles shorter)
+    constexpr bool VM1 = R >= 2;
+    const float vsv[4] = {VM1 && !valid ? 0.f : vs4.x, VM1 && !valid ? 0.f : vs4.y,
+                          VM1 && !valid ? 0.f : vs4.z, VM1 && !valid ? 0.f : vs4.w};
     const float vzv[4] = {valid ? vz4.x : 0.f, valid ? vz4.y : 0.f, valid ? vz4.z : 0.f,
                           valid ? vz4.w : 0.f};
 #pragma unroll
@@ -1211,7 +1262,7 @@ decode_mfma_kernel(DecodeArgs a, LensT<RAG> lens) {
 #pragma unroll
       for (int jj = 0; jj < kNG; jj += 2) {
         uint32_t hi, lo;
-        split2_bf(valid ? p * vsv[jj] : 0.f, valid ? p * vsv[jj + 1] : 0.f, hi, lo);
+        split2_bf(VM1 || valid ? p * vsv[jj] : 0.f, VM1 || valid ? p * vsv[jj + 1] : 0.f, hi, lo);
         if constexpr (SHA) {
           // rows 2j (hi), 2j + 1 (lo) of group j
           char* d = lds_a + vwr + (uint32_t)(2 * jj * 64);
