@@ -42,8 +42,13 @@ PEAK_HBM_GBS = 8000.0
 METRIC = "quantized-KV decode attention: achieved HBM GB/s (% of peak), query-heads/s"
 # GPU work before the timed region: at least this many steps, whatever
 # --warmup says, so that every layer cache (32 by default) has been visited
-# several times, its first flush included, before the timed region
-MIN_WARMUP_STEPS = 512
+# many times, its first flush included, before the timed region.  A burst of
+# flushes (codec launches) slows the decode launches that follow it by up to
+# 15% for a few hundred launches while the shader clock recovers (kernel
+# traces of the batch-8 Llama and Mistral-shaped runs); the warm-up ends
+# about 2000 launches after its burst, so a short timed region sees the
+# steady clock that most launches of a long run see.
+MIN_WARMUP_STEPS = 2048
 LAT_REPS = 64
 LAT_SPIN_CYCLES = 2_000_000
 PF_SPIN_CYCLES = 20_000_000
@@ -418,8 +423,10 @@ def main():
                          "(repeatable bits) instead of sharing the block's tiles")
     ap.add_argument("--separate", action="store_true",
                     help="kivi_append then kivi_decode_attn (two calls) instead of the fused call")
-    ap.add_argument("--window", type=int, default=16, metavar="W",
-                    help="HIP events bracket windows of up to W consecutive timed steps")
+    ap.add_argument("--window", type=int, default=256, metavar="W",
+                    help="HIP events bracket windows of up to W consecutive timed steps (an "
+                         "event delays the next launch by several microseconds, so windows "
+                         "are long)")
     ap.add_argument("--window-trace", metavar="PATH",
                     help="also write every window's (first step, steps, flushes, us per step)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
