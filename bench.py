@@ -166,11 +166,13 @@ DECODE_SOURCES = ("decode_mfma_impl.h", "decode_mfma.hip", "decode_mfma_ragged.h
 
 
 def kernel_source_hash() -> str:
-    """Hash of the sources that define the decode kernel and its launch."""
+    """Hash of the sources that define the decode kernel and its launch, and
+    of the build script (its per-source compiler flags)."""
     h = hashlib.sha256()
     for name in DECODE_SOURCES:
         h.update(name.encode())
         h.update(open(os.path.join(ROOT, "kv_cache_bit_kivi_amd", "csrc", name), "rb").read())
+    h.update(open(os.path.join(ROOT, "kv_cache_bit_kivi_amd", "build.py"), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -659,6 +661,13 @@ def main():
         windows = windows[1:]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in windows]
+    # torch creates an event's HIP event at its first record: record each one
+    # once here, so that no event is created inside the timed region (a
+    # creation there held the launch after the first window event back by
+    # some 80 us in a kernel trace)
+    for e0, e1 in ev:
+        e0.record(cur)
+        e1.record(cur)
     # window k opens after the launch of the step before its first step
     opens = {ix[0] - 1: k for k, (_, ix) in enumerate(windows) if ix[0] > 0}
     closes = {ix[-1]: k for k, (_, ix) in enumerate(windows)}
