@@ -183,21 +183,26 @@ COPY_KERNEL_HINT = "bitwise_not"
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 PMC summary,
-    only if it was taken on the current kernel sources."""
+    """(HBM bytes per decode launch, their ratio to the algorithmic bytes of
+    the same dispatches) from the committed rocprofv3 PMC summary, only if it
+    was taken on the current kernel sources; else (None, None).  The PMC run
+    is the workload's default run (warm-up and timed steps), so its launches
+    read at their own lengths: the ratio, not the byte count, carries over to
+    another run of the workload."""
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
-        return None
+        return None, None
     if d.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return d.get("hbm_bytes_per_launch")
+        return None, None
+    return d.get("hbm_bytes_per_launch"), d.get("traffic_over_algorithmic")
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, command: str):
+def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, command: str,
+                alg_mean: float, alg_dispatches: int):
     """Calibrated HBM traffic of the decode kernel from two rocprofv3 --pmc
     runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch).  Each counter is
     scaled by bytes / counter of the plain copy kernel that the same run
@@ -240,6 +245,11 @@ def pmc_summary(fetch_csv: str, write_csv: str, copy_bytes: int, workload: str, 
         "hbm_read_bytes_per_launch": int(read_b),
         "hbm_write_bytes_per_launch": int(write_b),
         "hbm_bytes_per_launch": int(read_b + write_b),
+        # the algorithmic bytes of the same dispatches (warm-up and timed
+        # steps, at the lengths each one read), for the comparison
+        "algorithmic_bytes_per_dispatch": int(alg_mean),
+        "algorithmic_dispatches": alg_dispatches,
+        "traffic_over_algorithmic": round((read_b + write_b) / alg_mean, 4),
         "kernel_source_hash": kernel_source_hash(),
     }
     path = os.path.join(ROOT, "profiles", f"decode_{workload}_pmc.json")
@@ -452,12 +462,7 @@ def main():
            (f"_out{n_out}" if n_out else "") + ("_rope" if rope > 0 else "") +
            (f"_paged{args.paged}" if args.paged else "") + ("_meta16" if meta_half else "") +
            ("_det" if args.deterministic else "") + ("_vwin" if args.v_window else ""))
-    if args.pmc_summary:
-        fcsv, wcsv, mib, cmd = args.pmc_summary
-        pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd)
-        return
-
-    if args.gpus != 1:
+    if args.gpus != 1 and not args.pmc_summary:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
               "(the kernels shard across GPUs by (batch, KV head) with no exchange, but this "
               "build measures one GPU only).", file=sys.stderr)
@@ -476,6 +481,40 @@ def main():
     spikes = args.key_spikes if args.key_spikes is not None else (0.01 if n_out else 0.0)
     if spikes:
         w = w.with_(key_spikes=spikes)
+
+    B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
+                              w.residual)
+    if args.layers <= 0:
+        layer_bytes = decode_bytes(B, H, r, D, bits, G, int(w.context), R, mb, n_out)
+        args.layers = int(max(2, min(32, 16e9 // layer_bytes)))
+    NL = args.layers
+    if args.steps == 0:
+        args.steps = (w.steps or 128) * NL
+    warm = max(args.warmup, MIN_WARMUP_STEPS)
+    tq_s, tr_s = start_lengths(w)
+    paged = args.paged > 0
+    ragged = w.ragged or paged      # (the paged calls carry per-sequence lengths)
+    W = max(1, args.window)
+    per_seq = 1 if ragged else B
+    vw = args.v_window
+
+    def dec_bytes_of(info):
+        # algorithmic bytes of each planned step's decode, at the lengths it
+        # reads (after the step's append); ragged: summed over the sequences
+        return [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, tq, tr, mb, n_out, vw, R)))
+                for _, _, tq, tr in info]
+
+    if args.pmc_summary:
+        # the counters average every decode dispatch of the profiled run: the
+        # warm-up's and the timed steps' (no latency pairs in PMC runs), each
+        # with the new token folded in
+        new_tok = append_bytes(B, H, D, bits, G, R, False, mb, n_out)
+        plans = [plan_steps(n, NL, tq_s if ragged else tq_s[:1], tr_s if ragged else tr_s[:1],
+                            R, W)[0] for n in (warm, args.steps)]
+        allb = [d + new_tok for info in plans for d in dec_bytes_of(info)]
+        fcsv, wcsv, mib, cmd = args.pmc_summary
+        pmc_summary(fcsv, wcsv, int(mib) << 20, tag, cmd, sum(allb) / len(allb), len(allb))
+        return
 
     # The multi-core CPU leg's worker processes are forked now, before this
     # process touches the GPU, and wait for their work until the GPU leg ends.
@@ -496,23 +535,11 @@ def main():
         sys.exit(1)
     lib()  # fails loudly if the HIP library is missing
     torch.cuda.set_device(0)
-    B, H, r, D, bits, G, R = (w.batch, w.kv_heads, w.gqa, w.head_dim, w.bits, w.group,
-                              w.residual)
-    if args.layers <= 0:
-        layer_bytes = decode_bytes(B, H, r, D, bits, G, int(w.context), R, mb, n_out)
-        args.layers = int(max(2, min(32, 16e9 // layer_bytes)))
-    NL = args.layers
-    if args.steps == 0:
-        args.steps = (w.steps or 128) * NL
-    warm = max(args.warmup, MIN_WARMUP_STEPS)
-    tq_s, tr_s = start_lengths(w)
     # capacity for every flush of the warm-up or of the timed steps (the
     # lengths are set back to the start after the warm-up)
     per_layer = (max(warm, args.steps) + NL - 1) // NL
     cap = w.capacity(per_layer + R)
 
-    paged = args.paged > 0
-    ragged = w.ragged or paged      # (the paged calls carry per-sequence lengths)
     if args.v_window and ragged:
         print("--v-window needs a uniform workload (ragged and paged caches refuse it)",
               file=sys.stderr)
@@ -647,7 +674,6 @@ def main():
     # stream: bracketing every launch would add its own dispatch latency to
     # each measured launch and slow the loop.  Whether a step flushes is known
     # on the host before its call (plan_steps replays the lengths).
-    W = max(1, args.window)
     info, windows = plan_steps(args.steps, NL, tq_s if ragged else tq_s[:1],
                                tr_s if ragged else tr_s[:1], R, W)
     # The first step runs on an idle queue: between an event recorded before
@@ -727,12 +753,8 @@ def main():
         pair_us = la.elapsed_time(lb) * 1e3 / args.latency_reps
     del kd, vd
 
-    # algorithmic bytes of every step, at the lengths the decode reads (after
-    # the step's append); ragged: summed over the sequences
-    per_seq = 1 if ragged else B
-    vw = args.v_window
-    dec_bytes = [int(np.sum(decode_bytes(per_seq, H, r, D, bits, G, tq, tr, mb, n_out, vw, R)))
-                 for _, _, tq, tr in info]
+    # algorithmic bytes of every step, at the lengths the decode reads
+    dec_bytes = dec_bytes_of(info)
     # (a value leaves the window when the cache held R tokens before the append)
     app_bytes = [int(np.sum([append_bytes(per_seq, H, D, bits, G, R, bool(f), mb, n_out, vw,
                                           bool(np.all(tq + tr - 1 >= R)))
@@ -761,6 +783,7 @@ def main():
                 f.write(f"{ix[0]} {len(ix)} {int(fl)} {win_ms[k] / len(ix) * 1e3:.3f}\n")
 
     value = total_bytes / elapsed / 1e9
+    traffic_b, traffic_r = measured_traffic(tag)
     achieved = w_bytes / (w_time * 1e-3) / 1e9
     if ragged:
         kind = "paged" if paged else "ragged"
@@ -828,7 +851,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(tag),
+            "traffic": traffic_b,
+            "traffic_over_algorithmic": traffic_r,
             "bytes_per_launch": int(w_bytes / n_launch),
             "launches_averaged": int(n_launch),
             "window_launches": W,
