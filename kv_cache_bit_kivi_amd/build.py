@@ -26,13 +26,19 @@ COMMON = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 # per-source extra flags: the codec is a bit-exact contract (no contraction;
-# division stays the correctly rounded default); the uniform-cache decode
-# kernels are scheduled for instruction-level parallelism (their tile loop is
-# a latency-bound chain: batch-8 Llama layer 26.39 -> 26.26 us, Mistral-shaped
-# 57.5-58.0 -> 57.1-57.3 us against the default scheduler, same box)
+# division stays the correctly rounded default); the matrix-core decode
+# kernels with stored keys are scheduled for instruction-level parallelism
+# (their tile loop is a latency-bound chain; against the default scheduler,
+# same box: batch-8 Llama layer 26.39 -> 26.26 us, Mistral-shaped 57.5-58.0 ->
+# 57.1-57.3 us, ragged batch 51.3 -> 51.0 us, one and two key outliers per
+# group 31.0 -> 30.6 us and 37.9-38.3 -> 37.5-37.7 us, paged store 27.44-27.51
+# -> 27.40-27.43 us); the pre-RoPE units keep the default (no gain measured)
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
 EXTRA = {
     "quantize.hip": ["-ffp-contract=off"],
-    "decode_mfma.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    **{f: _ILP for f in ("decode_mfma.hip", "decode_mfma_ragged.hip", "decode_mfma_paged.hip",
+                         "decode_mfma_o1.hip", "decode_mfma_o2.hip", "decode_mfma_ragged_o.hip",
+                         "decode_mfma_paged_o.hip")},
 }
 # (longest compiles first: the pool starts them first)
 SOURCES = ["decode_mfma_ragged_o.hip", "decode_mfma_paged_o.hip", "decode_mfma_rope.hip",
