@@ -676,15 +676,19 @@ def main():
     # on the host before its call (plan_steps replays the lengths).
     info, windows = plan_steps(args.steps, NL, tq_s if ragged else tq_s[:1],
                                tr_s if ragged else tr_s[:1], R, W)
-    # The first step runs on an idle queue: between an event recorded before
-    # it and its kernel lies the host's enqueue latency (tens of microseconds
-    # measured), so the first window opens after the first step's launch (it
-    # then marks that kernel's end) and step 0 stays out of the roofline (it
-    # still counts in `value`).
-    if len(windows[0][1]) > 1 or len(windows) == 1:
-        windows[0] = (windows[0][0], windows[0][1][1:] or windows[0][1])
-    else:
-        windows = windows[1:]
+    # The first steps run while the host's enqueue still trails the device:
+    # the first starts on an idle queue (between an event recorded before it
+    # and its kernel lies the host's enqueue latency, tens of microseconds),
+    # and in kernel traces the second still waited 5.6 us (18.6 us under the
+    # tracer) after the window's start event, the later ones none.  So the
+    # first window opens after the second step's launch (it then marks that
+    # kernel's end) and steps 0 and 1 stay out of the roofline (they still
+    # count in `value`); a run of one or two steps keeps what it has.
+    for _ in range(2):
+        if len(windows[0][1]) > 1:
+            windows[0] = (windows[0][0], windows[0][1][1:])
+        elif len(windows) > 1:
+            windows = windows[1:]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in windows]
     # torch creates an event's HIP event at its first record: record each one
@@ -845,7 +849,8 @@ def main():
                        else f"kivi decode attention with the append folded in ({calls}: one "
                        "decode launch per step)") +
                       f"; HIP events around runs of up to {W} consecutive steps (the first "
-                      "step of the timed region left out: it starts on an idle queue)" +
+                      "two steps of the timed region left out: the host's enqueue still trails "
+                      "the device there)" +
                       (" without a flush" if plain else " (every step flushes)"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
