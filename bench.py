@@ -676,14 +676,15 @@ def main():
     # on the host before its call (plan_steps replays the lengths).
     info, windows = plan_steps(args.steps, NL, tq_s if ragged else tq_s[:1],
                                tr_s if ragged else tr_s[:1], R, W)
-    # The first steps run while the host's enqueue still trails the device:
-    # the first starts on an idle queue (between an event recorded before it
-    # and its kernel lies the host's enqueue latency, tens of microseconds),
-    # and in kernel traces the second still waited 5.6 us (18.6 us under the
-    # tracer) after the window's start event, the later ones none.  So the
-    # first window opens after the second step's launch (it then marks that
-    # kernel's end) and steps 0 and 1 stay out of the roofline (they still
-    # count in `value`); a run of one or two steps keeps what it has.
+    # The first steps run while the host's enqueue may still trail the
+    # device: the first starts on an idle queue (between an event recorded
+    # before it and its kernel lies the host's enqueue latency, tens of
+    # microseconds), and under the kernel tracer the launch after it waited
+    # 18.6 us behind the window's start event, against 5.6 us (the event's
+    # own cost) when the event follows the second step.  So the first window
+    # opens after the second step's launch (it then marks that kernel's end)
+    # and steps 0 and 1 stay out of the roofline (they still count in
+    # `value`); a run of one or two steps keeps what it has.
     for _ in range(2):
         if len(windows[0][1]) > 1:
             windows[0] = (windows[0][0], windows[0][1][1:])
