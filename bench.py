@@ -145,6 +145,23 @@ def plan_steps(steps, layers, tq_start, tr_start, R, window):
     return info, windows
 
 
+# timed steps left out of the roofline windows at the start of the timed
+# region (see timed_windows' caller)
+LEAD_STEPS = 2
+
+
+def timed_windows(windows, lead):
+    """The windows of plan_steps without the first `lead` steps, as long as a
+    window remains (a run of at most `lead` steps keeps its last step)."""
+    windows = [(fl, list(ix)) for fl, ix in windows]
+    for _ in range(lead):
+        if len(windows[0][1]) > 1:
+            windows[0] = (windows[0][0], windows[0][1][1:])
+        elif len(windows) > 1:
+            windows = windows[1:]
+    return windows
+
+
 def start_lengths(w):
     """(tq, tr) arrays every layer cache starts the timed steps at: one token
     short of the workload's context, so the first step decodes the
@@ -685,11 +702,7 @@ def main():
     # opens after the second step's launch (it then marks that kernel's end)
     # and steps 0 and 1 stay out of the roofline (they still count in
     # `value`); a run of one or two steps keeps what it has.
-    for _ in range(2):
-        if len(windows[0][1]) > 1:
-            windows[0] = (windows[0][0], windows[0][1][1:])
-        elif len(windows) > 1:
-            windows = windows[1:]
+    windows = timed_windows(windows, LEAD_STEPS)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in windows]
     # torch creates an event's HIP event at its first record: record each one

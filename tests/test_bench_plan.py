@@ -99,3 +99,29 @@ def test_prefill_bytes():
     per = (2 * 3968 * 128 * 2 + 2 * 3968 * 128 * 2 // 8 + 124 * 128 * 8 + 3968 * 4 * 8
            + 2 * 128 * 128 * 4)
     assert b == 8 * 32 * per
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 20, 4096])
+def test_timed_windows_skip_the_lead_steps(steps):
+    w = synth.WORKLOADS["llama2_7b_b8_ctx4096"]
+    tq, tr = bench.start_lengths(w)
+    _, windows = bench.plan_steps(steps, 32, tq[:1], tr[:1], R, 256)
+    tw = bench.timed_windows(windows, bench.LEAD_STEPS)
+    timed = [i for _, ix in tw for i in ix]
+    if steps <= bench.LEAD_STEPS:
+        assert timed == [steps - 1]               # the last step stays timed
+    else:
+        assert timed == list(range(bench.LEAD_STEPS, steps))
+    if steps == 20:
+        assert len(tw) == 1 and len(tw[0][1]) == 18
+    for fl, ix in tw:                             # still one kind per window, consecutive
+        assert ix == list(range(ix[0], ix[-1] + 1))
+
+
+def test_timed_windows_drop_a_leading_flush_window():
+    w = synth.WORKLOADS["stream_b64_2bit"]
+    tq, tr = bench.start_lengths(w)
+    info, windows = bench.plan_steps(8, 1, tq[:1], tr[:1], R, 256)
+    assert windows[0] == (True, [0])               # the first append flushes
+    tw = bench.timed_windows(windows, 2)
+    assert tw[0] == (False, list(range(2, 8)))
