@@ -343,3 +343,33 @@ def test_error_codes(oracle_lib):
         oracle.quantize_k(x, 2, 32, cap=64, ntok=48)
     with pytest.raises(oracle.oracle.OracleError, match="ECAPACITY"):
         oracle.quantize_k(x, 2, 32, cap=64, ntok=64, dst_off=32)
+
+
+@pytest.mark.parametrize("meta_half", [False, True])
+@pytest.mark.parametrize("n_out", [0, 1, 2])
+@pytest.mark.parametrize("bits", [1, 2, 4])
+def test_key_zeros_are_binary16_values(oracle_lib, bits, n_out, meta_half):
+    """A key zero is the minimum of binary16 inputs (the group's, or of the
+    entries left after its outliers), so it is a binary16 value exactly: the
+    matrix-core decode takes the zeros as binary16 operands for several heads
+    per KV head.  Spiky inputs, a constant group and a group of signed zeros
+    included; with outliers the zero is the minimum of the dense rest."""
+    G, T, D = 32, 128, 128
+    x = synth.spiky_fp16(40 + bits, (1, 2, T, D), rate=0.03, scale=2.0)
+    x[0, 0, 0:G, 3] = np.float16(0.7)                       # constant group
+    x[0, 0, G:2 * G, 5] = np.float16(-0.0)
+    x[0, 0, G + 7, 5] = np.float16(0.0)                     # signed zeros
+    out = oracle.quantize_k(x, bits, G, cap=T, meta_half=meta_half, n_out=n_out)
+    z = out[2]
+    zf = (z.view(np.float16).astype(np.float64) if meta_half else z.astype(np.float64)).reshape(-1)
+    assert np.array_equal(zf, zf.astype(np.float16).astype(np.float64))
+    xs = _groups_keys(x, G)                                  # [groups][G], same order
+    if n_out == 0:
+        assert np.array_equal(zf, xs.min(1))
+    else:
+        # the n_out entries of largest magnitude (lower token first) leave the range
+        order = np.argsort(-np.abs(xs), axis=1, kind="stable")[:, :n_out]
+        mask = np.ones_like(xs, dtype=bool)
+        np.put_along_axis(mask, order, False, axis=1)
+        dense_min = np.where(mask, xs, np.inf).min(1)
+        assert np.array_equal(zf, dense_min)
