@@ -204,3 +204,30 @@ def test_small_value_scales(v_scale, q_scale, bits, r):
     out = host(gc.decode(dev(q), 0.0883883461356163)).astype(np.float64)
     err = row_rel_err(out, ref)
     assert err <= ATTN_TOL, err
+
+
+@pytest.mark.parametrize("meta_half", [False, True])
+@pytest.mark.parametrize("r", [1, 2, 4, 8])
+def test_decode_large_key_zeros(r, meta_half):
+    """Keys around +-3000 (channel offsets), so every key zero is a large
+    binary16 value and the zero term carries most of each score: the
+    several-heads kernels take the zeros as binary16 matrix operands, one head
+    sums them on the vector units; both within the bar of the oracle."""
+    require_gpu()
+    announce(f"decode large key zeros r={r} meta_half={meta_half}")
+    B, H, D, bits, G, R, tq, tr = 2, 2, 128, 2, 32, 128, 1984, 40
+    L = tq + tr
+    rng_k = synth.random_fp16(71 + r, (B, H, L, D), scale=40.0).astype(np.float32)
+    off = np.where(np.arange(D) % 2 == 0, 3000.0, -2500.0).astype(np.float32)
+    k = (rng_k + off).astype(np.float16)
+    v = synth.random_fp16(72 + r, (B, H, L, D), scale=1.0)
+    q = synth.random_fp16(73 + r, (B, H * r, D), scale=0.01)
+    cap = (tq + R + 63) // 64 * 64
+    gc = KiviCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+    gc.prefill(dev(k), dev(v), tq)
+    oc = oracle.OracleCache(B, H, r, D, bits, G, R, cap, meta_half=meta_half)
+    oc.prefill(k, v, tq)
+    ref = oc.decode(q, 0.0883883461356163)
+    for S in (0, 3):
+        out = host(gc.decode(dev(q), 0.0883883461356163, num_splits=S)).astype(np.float64)
+        assert row_rel_err(out, ref) <= ATTN_TOL, (S, row_rel_err(out, ref))
